@@ -1,0 +1,144 @@
+"""Pins of the oracle's P-EAGLE drafter-batch expansion and hidden fill.
+
+"P-EAGLE: parallel speculative decoding in vLLM" page: section "Triton Kernel"
+lists what one pass produces (shifted copy of ids and positions, the bonus
+token, MASK-filled parallel-drafting slots, rejected-token mask, masked-token
+mask, new-token indices, hidden-state mapping); section "Hidden State 管理"
+prints the two statements that fill the hidden rows; section "并行草稿生成的挑战"
+says positions advance per request and start indices are recomputed.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _run(inp, with_hidden=True):
+    return oracle.expand(
+        inp.in_token_ids.numpy(), inp.in_positions.numpy(), inp.in_start.numpy(),
+        inp.accepted.numpy(), inp.bonus.numpy(), inp.K, inp.mask_id,
+        workloads.bf16_bits(inp.target_hidden) if with_hidden else None,
+        workloads.bf16_bits(inp.mask_hidden) if with_hidden else None)
+
+
+def test_hand_worked_example():
+    with open(os.path.join(GOLDEN, "expand_worked_example.json")) as f:
+        ex = json.load(f)
+    r = oracle.expand(ex["in_token_ids"], ex["in_positions"], ex["in_start"], ex["accepted"],
+                      ex["bonus"], ex["K"], ex["mask_id"])
+    e = ex["expected"]
+    assert r.n_bad == 0
+    for key in ("out_start", "out_token_ids", "out_positions", "rejected_mask", "masked_mask",
+                "hidden_map"):
+        assert list(getattr(r, key)) == e[key], key
+    assert r.new_token_indices.tolist() == e["new_token_indices"]
+
+
+def check_invariants(inp, r):
+    """Facts fixed by the page, independent of the slot order inside a window."""
+    B, K = inp.B, inp.K
+    st = inp.in_start.numpy().astype(np.int64)
+    n = np.diff(st)
+    acc = inp.accepted.numpy()
+    N_out = inp.N_in + B * (K - 1)
+    # start indices: exclusive scan of the expanded request sizes n_b + K - 1
+    want_start = np.concatenate([[0], np.cumsum(n + K - 1)])
+    np.testing.assert_array_equal(r.out_start, want_start)
+    masked = r.masked_mask.astype(bool)
+    rejected = r.rejected_mask.astype(bool)
+    assert set(np.unique(r.masked_mask)) <= {0, 1} and set(np.unique(r.rejected_mask)) <= {0, 1}
+    assert not (masked & rejected).any()
+    # the mapping is injective, and its image with the masked slots partitions the output
+    hm = r.hidden_map
+    assert len(np.unique(hm)) == inp.N_in
+    cover = np.zeros(N_out, np.int64)
+    np.add.at(cover, hm, 1)
+    cover[masked] += 1
+    assert (cover == 1).all()
+    ids = inp.in_token_ids.numpy()
+    pos = inp.in_positions.numpy()
+    bonus = inp.bonus.numpy()
+    for b in range(B):
+        o0, o1 = r.out_start[b], r.out_start[b + 1]
+        sl = slice(o0, o1)
+        valid = ~masked[sl] & ~rejected[sl]
+        # per request: a+1 valid (accepted drafts + bonus), n-1-a rejected, K-1 MASK
+        assert valid.sum() == acc[b] + 1
+        assert rejected[sl].sum() == n[b] - 1 - acc[b]
+        assert masked[sl].sum() == K - 1
+        assert (r.out_token_ids[sl][masked[sl]] == inp.mask_id).all()
+        # every input row of the request maps into its own window
+        assert ((hm[st[b]:st[b + 1]] >= o0) & (hm[st[b]:st[b + 1]] < o1)).all()
+        # drafter inputs: the slot holding input hidden row j carries position pos_j + 1
+        np.testing.assert_array_equal(r.out_positions[hm[st[b]:st[b + 1]]], pos[st[b]:st[b + 1]] + 1)
+        # valid + MASK slots have strictly increasing, consecutive positions
+        keep = valid | masked[sl]
+        vp = r.out_positions[sl][keep]
+        assert (np.diff(vp) == 1).all()
+        assert vp[0] == pos[st[b]] + 1
+        # the valid tokens are the accepted drafts followed by the bonus
+        vt = r.out_token_ids[sl][valid]
+        assert list(vt[:-1]) == list(ids[st[b] + 1:st[b] + 1 + acc[b]])
+        assert vt[-1] == bonus[b]
+        # new-token indices: the bonus slot then the K-1 MASK slots
+        nti = r.new_token_indices[b]
+        assert r.out_token_ids[nti[0]] == bonus[b] and valid[nti[0] - o0]
+        assert masked[nti[1:]].all() and (np.diff(nti) > 0).all()
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_invariants_at_full_size(seed):
+    inp = workloads.expand_inputs(B=512, K=8, H=64, seed=seed)
+    r = _run(inp, with_hidden=False)
+    assert r.n_bad == 0
+    check_invariants(inp, r)
+
+
+def test_invariants_ragged_requests():
+    rng = np.random.default_rng(3)
+    n = rng.integers(1, 12, 97)
+    inp = workloads.expand_inputs(B=97, K=5, H=16, seed=3, n_per_request=n)
+    r = _run(inp, with_hidden=False)
+    assert r.n_bad == 0
+    check_invariants(inp, r)
+
+
+@pytest.mark.parametrize("K", [1, 2, 8])
+def test_hidden_fill_matches_page_statements(K):
+    """The page's two statements run in torch on the CPU against the oracle's
+    hidden rows: bit-equal, and every output row written exactly once."""
+    inp = workloads.expand_inputs(B=37, K=K, H=48, seed=K)
+    r = _run(inp)
+    N_out = inp.N_out
+    hidden_states = torch.full((N_out, inp.H), float("nan"), dtype=torch.bfloat16)
+    out_hidden_state_mapping = torch.from_numpy(r.hidden_map.astype(np.int64))
+    hidden_states[out_hidden_state_mapping] = inp.target_hidden
+    mask = torch.from_numpy(r.masked_mask.astype(bool))
+    torch.where(mask.unsqueeze(1), inp.mask_hidden, hidden_states, out=hidden_states)
+    want = workloads.bf16_bits(hidden_states)
+    np.testing.assert_array_equal(r.out_hidden, want)
+    assert not np.isnan(hidden_states.float().numpy()).any()
+
+
+def test_invalid_requests_write_nothing():
+    inp = workloads.expand_inputs(B=4, K=3, H=8, seed=9)
+    acc = inp.accepted.clone()
+    acc[2] = 4  # n = 4 => a must be <= 3
+    r = oracle.expand(inp.in_token_ids.numpy(), inp.in_positions.numpy(), inp.in_start.numpy(),
+                      acc.numpy(), inp.bonus.numpy(), 3, inp.mask_id)
+    assert r.n_bad == 1
+    o0, o1 = r.out_start[2], r.out_start[3]
+    assert (r.out_token_ids[o0:o1] == -7).all()
+    assert (r.new_token_indices[2] == -7).all()
+    with pytest.raises(ValueError):
+        st = inp.in_start.numpy().copy()
+        st[-1] += 1  # in_start[B] != N_in
+        oracle.expand(inp.in_token_ids.numpy(), inp.in_positions.numpy(), st, inp.accepted.numpy(),
+                      inp.bonus.numpy(), 3, inp.mask_id)

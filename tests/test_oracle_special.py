@@ -1,0 +1,173 @@
+"""Special cases whose outcome the pages or textbook facts fix exactly."""
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from stats_helpers import chi2_pvalue, draw_categorical, softmax_rows
+
+
+def test_identical_distributions_accept_everything():
+    """Explainer page, section "核心思想": two models with the same (uniform
+    1..100) distribution defeat naive 'accept if equal' (1 in 100), while the
+    modified rule accepts every draft when p == q."""
+    B, K, V = 2000, 5, 100
+    t = np.zeros((1, K + 1, V), np.float32)  # uniform over 100 tokens
+    rng = np.random.default_rng(0)
+    x = rng.integers(0, V, (B, K)).astype(np.int32)
+    r = oracle.verify(t, t, x, np.ones(B, np.float32), seed=1)
+    assert (r.accepted == K).all()
+    assert (r.tokens[:, :K] == x).all()
+    # random identical rows at two temperatures
+    tl = (2 * rng.standard_normal((1, K + 1, 300))).astype(np.float32)
+    for T in (0.6, 1.0):
+        x = draw_categorical(softmax_rows(tl[0, :K], T), B, rng)
+        r = oracle.verify(tl, tl, x, np.full(B, T, np.float32), seed=2)
+        assert (r.accepted == K).all()
+
+
+def test_disjoint_supports_reject_at_once_and_resample_from_p():
+    B, K, V = 200_000, 3, 20
+    rng = np.random.default_rng(1)
+    tl = np.full((1, K + 1, V), -np.inf, np.float32)
+    dl = np.full((1, K + 1, V), -np.inf, np.float32)
+    tl[0, :, :10] = rng.standard_normal((K + 1, 10))
+    dl[0, :, 10:] = rng.standard_normal((K + 1, 10))
+    x = draw_categorical(softmax_rows(dl[0, :K]), B, rng)
+    r = oracle.verify(tl, dl, x, np.ones(B, np.float32), seed=3, debug=False, trace=False)
+    assert (r.accepted == 0).all()
+    assert (r.tokens[:, 0] < 10).all() and (r.tokens[:, 1:] == -1).all()
+    counts = np.bincount(r.tokens[:, 0], minlength=V)
+    assert chi2_pvalue(counts, softmax_rows(tl[0, 0])) >= 1e-4
+
+
+def test_one_hot_target_is_deterministic():
+    """p = delta_c: a draft equal to c is accepted (t = 1), any other is
+    rejected and the residual max(0, delta_c - q) is concentrated on c."""
+    B, K, V = 5000, 4, 50
+    rng = np.random.default_rng(2)
+    c = rng.integers(0, V, K + 1)
+    tl = np.full((1, K + 1, V), -np.inf, np.float32)
+    tl[0, np.arange(K + 1), c] = 0.0
+    dl = rng.standard_normal((1, K + 1, V)).astype(np.float32)
+    x = rng.integers(0, V, (B, K)).astype(np.int32)
+    x[: B // 2] = c[:K]  # half the requests draft exactly c
+    r = oracle.verify(tl, dl, x, np.ones(B, np.float32), seed=4)
+    match = x == c[:K]
+    a_want = np.where(match.all(1), K, np.argmin(match, axis=1))
+    np.testing.assert_array_equal(r.accepted, a_want)
+    for i in range(B):
+        a = a_want[i]
+        assert list(r.tokens[i, :a + 1]) == list(c[:a + 1])
+
+
+def test_greedy_ties_go_to_lowest_index():
+    K, V = 2, 16
+    t = np.zeros((1, K + 1, V), np.float32)
+    t[0, 0, [3, 7]] = 5.0       # tie at row 0
+    t[0, 1, [2, 9]] = 4.0       # tie at row 1
+    t[0, 2, [11, 12]] = 1.0     # tie at the bonus row
+    d = np.zeros_like(t)
+    x = np.array([[7, 2], [3, 9], [3, 2]], np.int32)
+    r = oracle.verify(t, d, x, np.zeros(3, np.float32))
+    np.testing.assert_array_equal(r.accepted, [0, 1, 2])
+    assert list(r.tokens[0]) == [3, -1, -1]
+    assert list(r.tokens[1]) == [3, 2, -1]
+    assert list(r.tokens[2]) == [3, 2, 11]
+    # bf16 logits: equal bit patterns tie, the lowest index wins
+    tb = workloads.bf16_bits(__import__("torch").tensor(t).bfloat16())
+    r2 = oracle.verify(tb, workloads.bf16_bits(__import__("torch").tensor(d).bfloat16()), x,
+                       np.zeros(3, np.float32))
+    np.testing.assert_array_equal(r2.tokens, r.tokens)
+
+
+def test_greedy_matches_argmax_definition():
+    rng = np.random.default_rng(5)
+    B, K, V = 64, 5, 333
+    t = rng.standard_normal((B, K + 1, V)).astype(np.float32)
+    g = np.argmax(t, axis=2)
+    x = g[:, :K].copy()
+    flip = rng.random((B, K)) < 0.3
+    x[flip] = (x[flip] + 1) % V
+    r = oracle.verify(t, t, x.astype(np.int32), np.zeros(B, np.float32))
+    for b in range(B):
+        bad = np.flatnonzero(flip[b])
+        a = bad[0] if len(bad) else K
+        assert r.accepted[b] == a
+        assert list(r.tokens[b, :a]) == list(x[b, :a])
+        assert r.tokens[b, a] == g[b, a]
+
+
+def test_single_token_vocabulary_and_single_draft():
+    r = oracle.verify(np.zeros((3, 3, 1), np.float32), np.zeros((3, 3, 1), np.float32),
+                      np.zeros((3, 2), np.int32), np.array([1.0, 0.0, 0.5], np.float32))
+    assert (r.accepted == 2).all() and (r.tokens == 0).all()
+    rng = np.random.default_rng(6)
+    B = 100_000
+    tl = rng.standard_normal((1, 2, 8)).astype(np.float32)
+    dl = rng.standard_normal((1, 2, 8)).astype(np.float32)
+    x = draw_categorical(softmax_rows(dl[0, :1]), B, rng)
+    r = oracle.verify(tl, dl, x, np.ones(B, np.float32), debug=False, trace=False)
+    assert set(np.unique(r.accepted)) <= {0, 1}
+    assert chi2_pvalue(np.bincount(r.tokens[:, 0], minlength=8), softmax_rows(tl[0, 0])) >= 1e-4
+
+
+def test_invalid_requests_are_flagged():
+    rng = np.random.default_rng(7)
+    B, K, V = 5, 3, 10
+    t = rng.standard_normal((B, K + 1, V)).astype(np.float32)
+    x = rng.integers(0, V, (B, K)).astype(np.int32)
+    T = np.ones(B, np.float32)
+    x[1, 2] = V          # token out of range
+    x[2, 0] = -1         # negative token
+    T[3] = -1.0          # negative temperature
+    t[4, 1, :] = -np.inf  # a row with no finite maximum (sampled request)
+    r = oracle.verify(t, t, x, T)
+    assert r.n_bad == 4
+    assert r.accepted[0] == K
+    for b in range(1, 5):
+        assert r.accepted[b] == -1 and (r.tokens[b] == -1).all()
+
+
+def test_request_base_reproduces_a_shard():
+    """A subset of requests run with request_base = its first index gives
+    exactly the rows of the full run (counter keyed on the request)."""
+    inp = workloads.verify_tiny(seed=0)
+    tl = workloads.logits_numpy(inp.target)
+    dl = workloads.logits_numpy(inp.draft)
+    x = inp.draft_tokens.numpy()
+    T = inp.temperature.numpy()
+    full = oracle.verify(tl, dl, x, T, seed=11, step=3)
+    part = oracle.verify(tl[2:], dl[2:], x[2:], T[2:], seed=11, step=3, request_base=2)
+    np.testing.assert_array_equal(full.tokens[2:], part.tokens)
+    np.testing.assert_array_equal(full.accepted[2:], part.accepted)
+    again = oracle.verify(tl, dl, x, T, seed=11, step=3)
+    np.testing.assert_array_equal(full.tokens, again.tokens)
+    other = oracle.verify(tl, dl, x, T, seed=11, step=4)
+    assert (other.trace[:, 0, 0] != full.trace[:, 0, 0]).any()
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_softmax_matches_library_and_debug_probs(dtype):
+    import torch
+    rng = np.random.default_rng(8)
+    B, K, V = 6, 3, 257
+    t32 = (3 * rng.standard_normal((B, K + 1, V))).astype(np.float32)
+    d32 = (t32 + rng.standard_normal((B, K + 1, V))).astype(np.float32)
+    t32[0, 0, :5] = -np.inf
+    if dtype == "bf16":
+        tt, dt = torch.tensor(t32).bfloat16(), torch.tensor(d32).bfloat16()
+        tl, dl = workloads.bf16_bits(tt), workloads.bf16_bits(dt)
+        tv, dv = tt.float().numpy(), dt.float().numpy()
+    else:
+        tl, dl, tv, dv = t32, d32, t32, d32
+    T = np.array([1.0, 0.6, 1.3, 0.25, 2.0, 1.0], np.float32)
+    x = rng.integers(5, V, (B, K)).astype(np.int32)
+    r = oracle.verify(tl, dl, x, T)
+    for b in range(B):
+        for k in range(K):
+            p = softmax_rows(tv[b, k], float(T[b]))
+            q = softmax_rows(dv[b, k], float(T[b]))
+            np.testing.assert_allclose(oracle.softmax(tl[b, k], float(T[b])), p, rtol=1e-13, atol=1e-300)
+            assert r.debug_probs[b, k, 0] == np.float32(p[x[b, k]])
+            assert r.debug_probs[b, k, 1] == np.float32(q[x[b, k]])
