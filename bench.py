@@ -1,0 +1,198 @@
+"""Benchmark of one speculative-decoding hot-path step on one MI355X.
+
+A step = one verification of the headline batch (B=256 requests, K=8 drafts,
+V=151936 bf16 logits, temperatures drawn from {0, 0.6, 1}, mixture drafts)
+followed by the P-EAGLE expansion of the same batch (hidden width 2880, the
+bonus read from the verification's output tokens), both through the C ABI on
+torch's current stream.  Inputs are generated once on the GPU and stay resident
+in HBM; each timed step uses a new Philox step counter.
+
+Prints one JSON line: verified draft positions per second (B*K per step),
+the roofline of the dominant kernel (the row-statistics pass of verification)
+timed with HIP events on the launch stream, and the CPU oracle timed on the
+host's cores over whole steps of the same batch.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="approximate CPU-seconds of oracle work for the CPU baseline")
+    return ap.parse_args()
+
+
+def algorithmic_verify_bytes(B, K, V, es, temps):
+    """Bytes the parallel formulation must read once: every target row 0..K,
+    and draft rows 0..K-1 of sampled (T > 0) requests; plus draft tokens and
+    temperatures in, accepted counts and output tokens out."""
+    n_sampled = int((temps > 0).sum())
+    logits = B * (K + 1) * V * es + n_sampled * K * V * es
+    return logits + B * K * 4 + B * 4 + B * 4 + B * (K + 1) * 4
+
+
+def algorithmic_expand_bytes(B, K, H, n_in):
+    n_out = n_in + B * (K - 1)
+    hidden = n_in * H * 2 + H * 2 + n_out * H * 2
+    meta_in = n_in * (4 + 8) + (B + 1) * 4 + B * 4 + B * 4
+    meta_out = n_out * (4 + 8 + 1 + 1) + B * K * 4 + n_in * 4 + (B + 1) * 4
+    return hidden + meta_in + meta_out
+
+
+def cpu_baseline(inp, seed, cpu_seconds):
+    """The oracle, as it stands, over whole steps of the headline batch on all
+    host threads it is given (OMP_NUM_THREADS, else every core)."""
+    import numpy as np
+    import oracle
+    import workloads
+    tl = workloads.logits_numpy(inp.target)
+    dl = workloads.logits_numpy(inp.draft)
+    x = inp.draft_tokens.cpu().numpy()
+    T = inp.temperature.cpu().numpy()
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    steps = 0
+    wall = 0.0
+    cpu0 = time.process_time()
+    while True:
+        t0 = time.perf_counter()
+        oracle.verify(tl, dl, x, T, seed=seed, step=steps, debug=False, trace=False, nthreads=threads)
+        wall += time.perf_counter() - t0
+        steps += 1
+        if time.process_time() - cpu0 >= cpu_seconds or steps >= 50:
+            break
+    B, K = x.shape
+    return {"value": steps * B * K / wall, "unit": "positions/s", "cores": threads, "kind": "oracle",
+            "sample": "%d whole step(s) of the headline batch (B=%d, K=%d, V=%d), %.1f CPU-s"
+                      % (steps, B, K, tl.shape[-1], time.process_time() - cpu0)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (request sharding is "
+              "described in the design notes); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import rejection_sampling_verify_03_amd as sv
+    import workloads
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    inp = workloads.verify_headline(seed=args.seed, device=dev)
+    B, K, V = inp.B, inp.K, inp.V
+    H = workloads.HIDDEN_GPT_OSS_20B
+    # the verify batch feeding the expansion: per request [last token, x_0..x_{K-1}]
+    g = torch.Generator(device=dev).manual_seed(args.seed + 1)
+    last = torch.randint(0, V, (B, 1), generator=g, device=dev, dtype=torch.int32)
+    in_ids = torch.cat([last, inp.draft_tokens], dim=1).reshape(-1).contiguous()
+    off = torch.randint(0, 16384, (B, 1), generator=g, device=dev, dtype=torch.int64)
+    in_pos = (off + torch.arange(K + 1, device=dev)).reshape(-1).contiguous()
+    in_start = (torch.arange(B + 1, device=dev, dtype=torch.int32) * (K + 1)).contiguous()
+    hidden = torch.randn(B * (K + 1), H, generator=g, device=dev).to(torch.bfloat16)
+    mask_hidden = torch.randn(H, generator=g, device=dev).to(torch.bfloat16)
+    mask_id = workloads.GPT_OSS_VOCAB
+
+    accepted = torch.empty(B, dtype=torch.int32, device=dev)
+    tokens = torch.empty(B, K + 1, dtype=torch.int32, device=dev)
+    ws = sv.make_workspace(B, K, V, dev)
+    out = sv.expand_outputs(B, K, B * (K + 1), H, dev)
+    stream = torch.cuda.current_stream()
+    sptr = stream.cuda_stream
+    ex_args = sv.expand_args(in_ids, in_pos, in_start, accepted, None, K, mask_id, hidden, mask_hidden, out,
+                             verify_tokens=tokens)
+
+    n_events = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(n_events)]
+    for e4 in ev:  # create the underlying HIP events
+        for e in e4:
+            e.record(stream)
+    torch.cuda.synchronize()
+
+    def step(i, events=None):
+        va = sv.verify_args(inp.target, inp.draft, inp.draft_tokens, inp.temperature, accepted, tokens, None,
+                            ws, seed=args.seed, step=i,
+                            phase_event=events[1].cuda_event if events else None)
+        if events:
+            events[0].record(stream)
+        rc = sv.spec_verify_launch(va, sptr)
+        if rc != sv.SPEC_OK:
+            raise sv.SpecError(rc)
+        if events:
+            events[2].record(stream)
+        rc = sv.spec_expand_launch(ex_args, sptr)
+        if rc != sv.SPEC_OK:
+            raise sv.SpecError(rc)
+        if events:
+            events[3].record(stream)
+
+    for i in range(args.warmup):
+        step(1_000_000 + i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i, ev[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+    k1 = np.array([e[0].elapsed_time(e[1]) for e in ev])
+    k2 = np.array([e[1].elapsed_time(e[2]) for e in ev])
+    ke = np.array([e[2].elapsed_time(e[3]) for e in ev])
+
+    temps = inp.temperature.cpu().numpy()
+    vbytes = algorithmic_verify_bytes(B, K, V, 2, temps)
+    logit_bytes = vbytes - (B * K * 4 + B * 4 + B * 4 + B * (K + 1) * 4)
+    ebytes = algorithmic_expand_bytes(B, K, H, B * (K + 1))
+    k1_ms = float(k1.mean())
+    achieved = logit_bytes / (k1_ms * 1e-3) / 1e9
+    acc_np = accepted.cpu().numpy()
+    positions_per_s = B * K / (ms_per_step * 1e-3)
+    line = {
+        "metric": "verified draft positions/sec + achieved HBM GB/s at B=256,K=8,V=151936 bf16",
+        "value": positions_per_s,
+        "unit": "positions/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "headline verify B=256 K=8 V=151936 bf16, T in {0,0.6,1}, mixture drafts "
+                               "+ P-EAGLE expand H=2880 chained on the verify outputs",
+                   "B": B, "K": K, "V": V, "H": H, "sampled_requests": int((temps > 0).sum())},
+        "roofline": {"kernel": "verify_rowstats", "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "algorithmic_bytes": logit_bytes},
+        "kernels_ms": {"verify_rowstats": k1_ms, "verify_sample": float(k2.mean()),
+                       "expand": float(ke.mean()),
+                       "verify_rowstats_p10_p90": [float(np.percentile(k1, 10)), float(np.percentile(k1, 90))]},
+        "verify_GBps_algorithmic": vbytes / ((k1.mean() + k2.mean()) * 1e-3) / 1e9,
+        "expand_GBps_algorithmic": ebytes / (ke.mean() * 1e-3) / 1e9,
+        "emitted_tokens_per_s": float((acc_np + 1).sum()) / (ms_per_step * 1e-3),
+        "mean_accepted": float(acc_np.mean()),
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(inp, args.seed, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,187 @@
+/*
+ * spec_verify.h -- C ABI of the MI355X (gfx950) speculative-decoding hot path:
+ * batched modified-rejection-sampling verification and the P-EAGLE
+ * parallel-drafting batch expansion with its hidden-state gather.
+ *
+ * Conventions for every entry point
+ *  - Pointers marked "device" are HIP device pointers; the library never
+ *    dereferences them on the host.  Pointers to the argument structs are host
+ *    pointers, read only during the call.
+ *  - The caller owns all memory and keeps it alive until the stream has passed
+ *    the launch.  The library allocates nothing, keeps no per-call state and
+ *    performs no host-device synchronisation inside *_launch; work is enqueued
+ *    asynchronously on `stream` (a hipStream_t; 0 = the null stream).
+ *  - Argument errors are returned synchronously as a negative spec_status
+ *    before anything is enqueued.  Data errors only the device can see are
+ *    reported per request in the outputs (documented per call).
+ *  - Strides are in elements.  Vectorised 16-byte loads are used when the
+ *    logits/hidden base pointers and row strides are 16-byte aligned; other
+ *    layouts take a scalar path with identical results.
+ */
+#ifndef SPEC_VERIFY_H
+#define SPEC_VERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t* hipStream_t;
+
+typedef enum {
+  SPEC_OK = 0,
+  SPEC_EINVAL = -1,     /* null pointer, size or stride out of range */
+  SPEC_EDTYPE = -2,     /* unknown logits dtype */
+  SPEC_EALIGN = -3,     /* workspace not 16-byte aligned */
+  SPEC_EWORKSPACE = -4, /* workspace smaller than spec_verify_workspace_bytes() */
+  SPEC_ELAUNCH = -5     /* the HIP runtime refused a launch */
+} spec_status;
+
+typedef enum { SPEC_F32 = 0, SPEC_BF16 = 1 } spec_dtype;
+
+/* Largest number of drafts per request (one 64-lane wavefront ballot). */
+#define SPEC_MAX_K 63
+
+/* ------------------------------------------------------------- verification
+ *
+ * Defined by the explainer page on speculative decoding, section "修正拒绝采样"
+ * (accept draft token x with probability min(1, p(x)/q(x)); on rejection
+ * resample from normalize(max(0, p - q)); the emitted law is p) and section
+ * "核心思想" (the target scores K+1 positions at once; stop at the first
+ * rejection; all K accepted yields K+1 tokens, the last sampled from p), with
+ * the greedy limit of the same page: temperature 0 accepts iff the draft is
+ * the target argmax and emits the target argmax where it stops.
+ *
+ * For request b with temperature T_b > 0, p_k = softmax(target[b,k,:] / T_b)
+ * and q_k = softmax(draft[b,k,:] / T_b).  Uniforms: Philox4x32-10 with counter
+ * {b + request_base, k, step, 0} and key {seed & 0xffffffff, seed >> 32};
+ * word 0 -> u_k for the accept test at row k, word 1 -> u'_k for the sampling
+ * draw at row k; a word w maps to (w >> 8) * 2^-24.  Accept iff
+ * u_k < min(1, p_k(x_k) / q_k(x_k)) (q_k(x_k) = 0: accept iff p_k(x_k) > 0).
+ * a_b = number of leading accepts.  If a_b < K the emitted token is the
+ * smallest v with r(v) > 0 and u'_{a} * R < sum_{i<=v} r(i), r = max(0, p_a -
+ * q_a), R = sum r (if R == 0, r = p_a); if a_b == K it is drawn the same way
+ * from r = p_K.  Argmax ties (T = 0) go to the lowest index.
+ *
+ * Layouts: target [B, K+1, V] and draft [B, >=K, V] with the given request and
+ * row strides (request stride 0 shares one set of rows across all requests);
+ * draft row K is never read, and draft rows are not read at all for T_b = 0.
+ *
+ * Preconditions on the data (not checked): logits are not NaN or +inf and
+ * |logit| / T_b < 2^100; every row of a sampled request has a finite maximum
+ * (violations are detected where they make a row's normaliser non-finite or
+ * zero, and reported as a data error).
+ */
+typedef struct {
+  int32_t B;                   /* requests, >= 0 */
+  int32_t K;                   /* drafts per request, 1..SPEC_MAX_K */
+  int32_t V;                   /* vocabulary size, >= 1 */
+  int32_t dtype;               /* spec_dtype of both logits tensors */
+  const void* target_logits;   /* device [B, K+1, V] */
+  int64_t t_req_stride;        /* elements between requests (0 = shared), else >= (K+1)*t_row_stride */
+  int64_t t_row_stride;        /* elements between rows, >= V */
+  const void* draft_logits;    /* device [B, >=K, V] */
+  int64_t d_req_stride;        /* 0 = shared, else >= K*d_row_stride */
+  int64_t d_row_stride;        /* >= V */
+  const int32_t* draft_tokens; /* device [B, K], the K draft tokens of each request */
+  const float* temperature;    /* device [B]; 0 = greedy */
+  uint64_t seed;               /* Philox key */
+  uint32_t step;               /* Philox counter word 2 (decode step) */
+  uint32_t request_base;       /* added to the request index in the counter */
+  int32_t* accepted_counts;    /* device out [B]: a_b in 0..K; -1 = invalid request data */
+  int32_t* output_tokens;      /* device out [B, K+1]: x_0..x_{a-1}, the emitted token, then -1 */
+  float* debug_probs;          /* device out [B, K, 2] or NULL: p_k(x_k), q_k(x_k) (0 for T = 0) */
+  void* workspace;             /* device scratch, spec_verify_workspace_bytes(B, K, V) bytes */
+  size_t workspace_bytes;
+  void* phase_event;           /* hipEvent_t or NULL: recorded on `stream` between the row-statistics
+                                  kernel and the sampling kernel (for timing them apart) */
+} spec_verify_args;
+
+/* Bytes of device workspace a verification of this shape needs. */
+size_t spec_verify_workspace_bytes(int32_t B, int32_t K, int32_t V);
+
+/* Zero-fill a workspace (enqueued on `stream`, a fill kernel, no memset
+ * node).  A workspace serves one (B, K, V) shape: initialise it before its
+ * first use and again before using it for another shape.  Every verification
+ * that runs to completion leaves its arrival counters at zero, so one
+ * initialisation suffices for any number of calls of that shape.  Misuse
+ * (no initialisation, a shape change) gives wrong outputs but never an
+ * out-of-bounds access.  Calls that overlap on one workspace race. */
+int spec_verify_workspace_init(void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Enqueue one verification step.  A request whose data is invalid (a draft
+ * token outside [0, V), a temperature that is negative, NaN or infinite, or a
+ * row of a sampled request without a finite normaliser) gets
+ * accepted_counts = -1, output_tokens all -1 and debug_probs 0. */
+int spec_verify_launch(const spec_verify_args* args, hipStream_t stream);
+
+/* ---------------------------------------------------------------- expansion
+ *
+ * Defined by the "P-EAGLE: parallel speculative decoding in vLLM" page:
+ * section "并行草稿生成的挑战" (the drafter batch appends K-1 MASK slots per
+ * request, [token, MASK, ...]; ids, hidden states and positions are expanded,
+ * positions advance per request, start indices are recomputed), section
+ * "Triton Kernel" (one pass copies the old ids and positions into shifted
+ * slots, inserts each request's bonus token, fills the MASK slots and emits
+ * the rejected-token mask, the masked-token mask, the new-token indices and
+ * the hidden-state mapping), section "Hidden State 管理" (target hidden rows go
+ * to their mapped slots, MASK slots take the learned placeholder row) and
+ * section "核心方法" step 2 (a drafter input pairs the hidden state of a
+ * position with the token of the next position).
+ *
+ * Layout (per request b, n_b = in_start[b+1] - in_start[b], a = a_b):
+ *   out_start[b] = o_b = in_start[b] + b*(K-1); request b owns slots
+ *   [o_b, o_b + n_b + K - 1); N_out = N_in + B*(K-1).
+ *   slot o_b+j, j < n_b: hidden row in_start[b]+j (hidden_map), token = the
+ *     bonus if j == a else in_token_ids[in_start[b] + min(j+1, n_b-1)],
+ *     position in_positions[in_start[b]+j] + 1, rejected iff j > a;
+ *   slot o_b+n_b-1+m, m = 1..K-1: MASK id, position
+ *     in_positions[in_start[b]+a] + 1 + m, masked, hidden = mask_hidden;
+ *   new_token_indices[b] = {o_b + a, o_b + n_b, ..., o_b + n_b + K - 2}.
+ * A request with n_b < 1, a window outside [0, N_in] or a outside
+ * [0, n_b - 1] (or above K when the bonus comes from verify_output_tokens)
+ * writes only new_token_indices[b, :] = -1.  If in_start[0] != 0
+ * or in_start[B] != N_in every request does so and out_start is not written.
+ * A decreasing in_start is outside the contract (results unspecified, all
+ * accesses stay in bounds).
+ */
+typedef struct {
+  int32_t B;                      /* requests, >= 0 */
+  int32_t K;                      /* drafts per request, >= 1 */
+  int32_t H;                      /* hidden width (bf16 elements), >= 0 */
+  int32_t N_in;                   /* input slots, = in_start[B] */
+  const int32_t* in_token_ids;    /* device [N_in] */
+  const int64_t* in_positions;    /* device [N_in] */
+  const int32_t* in_start;        /* device [B+1] */
+  const int32_t* accepted_counts; /* device [B] */
+  const int32_t* bonus_tokens;    /* device [B], or NULL when verify_output_tokens is given */
+  const int32_t* verify_output_tokens; /* device [B, K+1] or NULL: output_tokens of a verification
+                                  with the same B and K; the bonus of request b is then
+                                  verify_output_tokens[b*(K+1) + a_b], which needs a_b <= K */
+  int32_t mask_token_id;
+  const uint16_t* target_hidden;  /* device bf16 bits [N_in, H] with row stride below */
+  int64_t hidden_row_stride;      /* elements, >= H */
+  const uint16_t* mask_hidden;    /* device bf16 bits [H] */
+  int32_t* out_token_ids;         /* device out [N_out] */
+  int64_t* out_positions;         /* device out [N_out] */
+  uint8_t* rejected_mask;         /* device out [N_out] */
+  uint8_t* masked_mask;           /* device out [N_out] */
+  int32_t* new_token_indices;     /* device out [B, K] */
+  int32_t* hidden_map;            /* device out [N_in] */
+  int32_t* out_start;             /* device out [B+1] */
+  uint16_t* out_hidden;           /* device out bf16 bits [N_out, H], or NULL to skip the gather */
+} spec_expand_args;
+
+/* Enqueue one expansion (metadata and, if out_hidden != NULL, the hidden-row
+ * gather) as a single kernel. */
+int spec_expand_launch(const spec_expand_args* args, hipStream_t stream);
+
+/* Human-readable name of a spec_status value (static storage). */
+const char* spec_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SPEC_VERIFY_H */

@@ -45,10 +45,20 @@ static int expand_args_ok(const oracle_expand_args* a) {
   return 1;
 }
 
+static void mark_invalid(const oracle_expand_args* a, int b) {
+  for (int m = 0; m < a->K; ++m) a->new_token_indices[(int64_t)b * a->K + m] = -1;
+}
+
 int oracle_expand(const oracle_expand_args* a) {
   if (!expand_args_ok(a)) return -1;
   const int B = a->B, K = a->K;
-  if (a->in_start[0] != 0 || a->in_start[B] != a->N_in) return -2;
+  if (B == 0) return 0; /* nothing to expand, nothing written */
+  if (a->in_start[0] != 0 || a->in_start[B] != a->N_in) {
+    /* the start indices do not describe the N_in input rows: every request is
+     * invalid and only its new-token indices are written (all -1) */
+    for (int b = 0; b < B; ++b) mark_invalid(a, b);
+    return B;
+  }
 
   for (int b = 0; b <= B; ++b) a->out_start[b] = a->in_start[b] + b * (K - 1);
 
@@ -59,6 +69,7 @@ int oracle_expand(const oracle_expand_args* a) {
     const int acc = a->accepted[b];
     const int o = a->out_start[b];
     if (n < 1 || s < 0 || a->in_start[b + 1] > a->N_in || acc < 0 || acc > n - 1) {
+      mark_invalid(a, b);
       ++bad;
       continue;
     }

@@ -122,8 +122,11 @@ typedef struct {
   uint16_t* out_hidden;              /* nullable [N_out, H] */
 } oracle_expand_args;
 
-/* Returns the number of requests with invalid data (n_b < 1, accepted out of
- * range); such a request writes nothing.  -1 on bad arguments. */
+/* Returns the number of requests with invalid data (n_b < 1, a window
+ * outside [0, N_in], accepted out of range); such a request writes only its
+ * new-token indices, all -1.  If in_start[0] != 0 or in_start[B] != N_in every
+ * request is invalid in that way and out_start is not written.  -1 on bad
+ * arguments.  A decreasing in_start is outside the contract. */
 int oracle_expand(const oracle_expand_args* a);
 
 #ifdef __cplusplus

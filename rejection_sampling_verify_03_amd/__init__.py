@@ -1,0 +1,276 @@
+"""Python binding of ``libspecverify.so``: the C ABI in ``include/spec_verify.h``.
+
+Argument marshalling only.  Every step of verification and expansion runs in
+the library's HIP kernels; torch supplies device memory and the stream.  There
+is no fallback: if the library has not been built (``build.py``) importing the
+binding raises.
+
+Same names as the C ABI: ``spec_verify_workspace_bytes``,
+``spec_verify_workspace_init``, ``spec_verify_launch``, ``spec_expand_launch``,
+``spec_status_string``; plus two convenience wrappers, ``verify`` and
+``expand``, that allocate the outputs and call the launchers on torch's current
+stream.
+"""
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libspecverify.so")
+
+SPEC_OK, SPEC_EINVAL, SPEC_EDTYPE, SPEC_EALIGN, SPEC_EWORKSPACE, SPEC_ELAUNCH = 0, -1, -2, -3, -4, -5
+SPEC_F32, SPEC_BF16 = 0, 1
+SPEC_MAX_K = 63
+
+EXPORTED = ("spec_verify_workspace_bytes", "spec_verify_workspace_init", "spec_verify_launch",
+            "spec_expand_launch", "spec_status_string")
+
+
+class SpecVerifyArgs(ctypes.Structure):
+    _fields_ = [
+        ("B", ctypes.c_int32), ("K", ctypes.c_int32), ("V", ctypes.c_int32), ("dtype", ctypes.c_int32),
+        ("target_logits", ctypes.c_void_p), ("t_req_stride", ctypes.c_int64), ("t_row_stride", ctypes.c_int64),
+        ("draft_logits", ctypes.c_void_p), ("d_req_stride", ctypes.c_int64), ("d_row_stride", ctypes.c_int64),
+        ("draft_tokens", ctypes.c_void_p), ("temperature", ctypes.c_void_p),
+        ("seed", ctypes.c_uint64), ("step", ctypes.c_uint32), ("request_base", ctypes.c_uint32),
+        ("accepted_counts", ctypes.c_void_p), ("output_tokens", ctypes.c_void_p),
+        ("debug_probs", ctypes.c_void_p), ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
+        ("phase_event", ctypes.c_void_p),
+    ]
+
+
+class SpecExpandArgs(ctypes.Structure):
+    _fields_ = [
+        ("B", ctypes.c_int32), ("K", ctypes.c_int32), ("H", ctypes.c_int32), ("N_in", ctypes.c_int32),
+        ("in_token_ids", ctypes.c_void_p), ("in_positions", ctypes.c_void_p), ("in_start", ctypes.c_void_p),
+        ("accepted_counts", ctypes.c_void_p), ("bonus_tokens", ctypes.c_void_p),
+        ("verify_output_tokens", ctypes.c_void_p),
+        ("mask_token_id", ctypes.c_int32),
+        ("target_hidden", ctypes.c_void_p), ("hidden_row_stride", ctypes.c_int64),
+        ("mask_hidden", ctypes.c_void_p),
+        ("out_token_ids", ctypes.c_void_p), ("out_positions", ctypes.c_void_p),
+        ("rejected_mask", ctypes.c_void_p), ("masked_mask", ctypes.c_void_p),
+        ("new_token_indices", ctypes.c_void_p), ("hidden_map", ctypes.c_void_p),
+        ("out_start", ctypes.c_void_p), ("out_hidden", ctypes.c_void_p),
+    ]
+
+
+def _load():
+    # torch ships its own HIP runtime under the same SONAME as the system one;
+    # loading torch first makes this library bind to that single runtime
+    # instead of pulling in a second copy.
+    import torch  # noqa: F401
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            "libspecverify.so is not built (expected at %s); run rejection_sampling_verify_03_amd/build.py "
+            "or __graft_entry__.build()" % LIB_PATH)
+    L = ctypes.CDLL(LIB_PATH)
+    L.spec_verify_workspace_bytes.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32]
+    L.spec_verify_workspace_bytes.restype = ctypes.c_size_t
+    L.spec_verify_workspace_init.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    L.spec_verify_workspace_init.restype = ctypes.c_int
+    L.spec_verify_launch.argtypes = [ctypes.POINTER(SpecVerifyArgs), ctypes.c_void_p]
+    L.spec_verify_launch.restype = ctypes.c_int
+    L.spec_expand_launch.argtypes = [ctypes.POINTER(SpecExpandArgs), ctypes.c_void_p]
+    L.spec_expand_launch.restype = ctypes.c_int
+    L.spec_status_string.argtypes = [ctypes.c_int]
+    L.spec_status_string.restype = ctypes.c_char_p
+    return L
+
+
+lib = _load()
+
+
+class SpecError(RuntimeError):
+    def __init__(self, status):
+        super().__init__(spec_status_string(status))
+        self.status = status
+
+
+# ----------------------------------------------------------------- raw C ABI
+def spec_verify_workspace_bytes(B, K, V):
+    return int(lib.spec_verify_workspace_bytes(int(B), int(K), int(V)))
+
+
+def spec_verify_workspace_init(workspace_ptr, workspace_bytes, stream_ptr):
+    return int(lib.spec_verify_workspace_init(workspace_ptr, int(workspace_bytes), stream_ptr))
+
+
+def spec_verify_launch(args, stream_ptr):
+    """args: a SpecVerifyArgs; stream_ptr: hipStream_t as an int (0 = null stream)."""
+    return int(lib.spec_verify_launch(ctypes.byref(args), stream_ptr))
+
+
+def spec_expand_launch(args, stream_ptr):
+    return int(lib.spec_expand_launch(ctypes.byref(args), stream_ptr))
+
+
+def spec_status_string(status):
+    return lib.spec_status_string(int(status)).decode()
+
+
+# ------------------------------------------------------- torch conveniences
+def _torch():
+    import torch
+    return torch
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream_ptr(stream=None):
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _logit_dtype(t):
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return SPEC_BF16
+    if t.dtype == torch.float32:
+        return SPEC_F32
+    raise TypeError("logits must be bfloat16 or float32, got %s" % t.dtype)
+
+
+def _check_dev(*ts):
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise ValueError("all tensors must be on the GPU")
+
+
+def make_workspace(B, K, V, device="cuda"):
+    """A zero-filled workspace for verifications of this shape (zeroed by
+    torch; the library keeps its counters at zero after every call)."""
+    torch = _torch()
+    n = spec_verify_workspace_bytes(B, K, V)
+    return torch.zeros(max(n, 16), dtype=torch.uint8, device=device)
+
+
+def verify_args(target, draft, draft_tokens, temperature, accepted, tokens, debug, workspace,
+                seed=0, step=0, request_base=0, phase_event=None):
+    """Fill a SpecVerifyArgs from tensors (no copies).
+
+    target [B or broadcast, K+1, V] and draft [B or broadcast, >=K, V] with a
+    unit innermost stride; a request stride of 0 (expanded tensor) shares rows.
+    """
+    _check_dev(target, draft, draft_tokens, temperature, accepted, tokens, debug, workspace)
+    B, K = draft_tokens.shape
+    V = target.shape[-1]
+    if target.stride(-1) != 1 or draft.stride(-1) != 1:
+        raise ValueError("logits rows must be contiguous")
+    if draft_tokens.dtype != _torch().int32 or not draft_tokens.is_contiguous():
+        raise ValueError("draft_tokens must be contiguous int32 [B, K]")
+    if temperature.dtype != _torch().float32 or not temperature.is_contiguous():
+        raise ValueError("temperature must be contiguous float32 [B]")
+    a = SpecVerifyArgs()
+    a.B, a.K, a.V, a.dtype = B, K, V, _logit_dtype(target)
+    if draft.dtype != target.dtype:
+        raise TypeError("target and draft logits must share a dtype")
+    a.target_logits = target.data_ptr()
+    a.t_req_stride = target.stride(0) if target.shape[0] == B and B > 1 else 0
+    a.t_row_stride = target.stride(1)
+    a.draft_logits = draft.data_ptr()
+    a.d_req_stride = draft.stride(0) if draft.shape[0] == B and B > 1 else 0
+    a.d_row_stride = draft.stride(1)
+    a.draft_tokens = draft_tokens.data_ptr()
+    a.temperature = temperature.data_ptr()
+    a.seed, a.step, a.request_base = int(seed) & (2 ** 64 - 1), int(step) & 0xFFFFFFFF, int(request_base)
+    a.accepted_counts = accepted.data_ptr()
+    a.output_tokens = tokens.data_ptr()
+    a.debug_probs = debug.data_ptr() if debug is not None else None
+    a.workspace = workspace.data_ptr()
+    a.workspace_bytes = workspace.numel() * workspace.element_size()
+    a.phase_event = phase_event
+    return a
+
+
+def verify(target, draft, draft_tokens, temperature, seed=0, step=0, request_base=0, debug=False,
+           workspace=None, stream=None):
+    """One verification step on torch's current stream.  Returns
+    (accepted_counts [B] int32, output_tokens [B, K+1] int32, debug_probs
+    [B, K, 2] float32 or None)."""
+    torch = _torch()
+    B, K = draft_tokens.shape
+    V = target.shape[-1]
+    dev = target.device
+    accepted = torch.empty(B, dtype=torch.int32, device=dev)
+    tokens = torch.empty(B, K + 1, dtype=torch.int32, device=dev)
+    dbg = torch.empty(B, K, 2, dtype=torch.float32, device=dev) if debug else None
+    ws = workspace if workspace is not None else make_workspace(B, K, V, dev)
+    a = verify_args(target, draft, draft_tokens, temperature, accepted, tokens, dbg, ws, seed, step,
+                    request_base)
+    rc = spec_verify_launch(a, _stream_ptr(stream))
+    if rc != SPEC_OK:
+        raise SpecError(rc)
+    return accepted, tokens, dbg
+
+
+class ExpandOutputs:
+    def __init__(self, **kw):
+        self.__dict__.update(kw)
+
+
+def expand_outputs(B, K, N_in, H, device, with_hidden=True):
+    torch = _torch()
+    N_out = N_in + B * (K - 1)
+    return ExpandOutputs(
+        out_token_ids=torch.empty(N_out, dtype=torch.int32, device=device),
+        out_positions=torch.empty(N_out, dtype=torch.int64, device=device),
+        rejected_mask=torch.empty(N_out, dtype=torch.uint8, device=device),
+        masked_mask=torch.empty(N_out, dtype=torch.uint8, device=device),
+        new_token_indices=torch.empty(B, K, dtype=torch.int32, device=device),
+        hidden_map=torch.empty(N_in, dtype=torch.int32, device=device),
+        out_start=torch.empty(B + 1, dtype=torch.int32, device=device),
+        out_hidden=torch.empty(N_out, H, dtype=torch.bfloat16, device=device) if with_hidden else None)
+
+
+def expand_args(in_token_ids, in_positions, in_start, accepted, bonus, K, mask_id, target_hidden,
+                mask_hidden, out, verify_tokens=None):
+    """bonus: [B] int32, or None with verify_tokens = the [B, K+1] output
+    tokens of a verification (the bonus is then read at the accepted count)."""
+    torch = _torch()
+    _check_dev(in_token_ids, in_positions, in_start, accepted, bonus, target_hidden, mask_hidden)
+    for t, dt in ((in_token_ids, torch.int32), (in_positions, torch.int64), (in_start, torch.int32),
+                  (accepted, torch.int32), (bonus, torch.int32), (verify_tokens, torch.int32)):
+        if t is not None and (t.dtype != dt or not t.is_contiguous()):
+            raise ValueError("expected contiguous %s" % dt)
+    a = SpecExpandArgs()
+    B = accepted.shape[0]
+    a.B, a.K, a.N_in, a.mask_token_id = B, int(K), in_token_ids.shape[0], int(mask_id)
+    a.in_token_ids, a.in_positions, a.in_start = (in_token_ids.data_ptr(), in_positions.data_ptr(),
+                                                   in_start.data_ptr())
+    a.accepted_counts = accepted.data_ptr()
+    a.bonus_tokens = bonus.data_ptr() if bonus is not None else None
+    a.verify_output_tokens = verify_tokens.data_ptr() if verify_tokens is not None else None
+    if out.out_hidden is not None:
+        if target_hidden.dtype != torch.bfloat16 or target_hidden.stride(-1) != 1:
+            raise ValueError("target_hidden must be bfloat16 with contiguous rows")
+        a.H = target_hidden.shape[1]
+        a.target_hidden = target_hidden.data_ptr()
+        a.hidden_row_stride = target_hidden.stride(0)
+        a.mask_hidden = mask_hidden.contiguous().data_ptr()
+        a.out_hidden = out.out_hidden.data_ptr()
+    else:
+        a.H, a.target_hidden, a.hidden_row_stride, a.mask_hidden, a.out_hidden = 0, None, 0, None, None
+    a.out_token_ids, a.out_positions = out.out_token_ids.data_ptr(), out.out_positions.data_ptr()
+    a.rejected_mask, a.masked_mask = out.rejected_mask.data_ptr(), out.masked_mask.data_ptr()
+    a.new_token_indices, a.hidden_map = out.new_token_indices.data_ptr(), out.hidden_map.data_ptr()
+    a.out_start = out.out_start.data_ptr()
+    return a
+
+
+def expand(in_token_ids, in_positions, in_start, accepted, bonus, K, mask_id, target_hidden=None,
+           mask_hidden=None, stream=None, out=None, verify_tokens=None):
+    """One expansion on torch's current stream; returns an ExpandOutputs."""
+    B = accepted.shape[0]
+    H = target_hidden.shape[1] if target_hidden is not None else 0
+    if out is None:
+        out = expand_outputs(B, K, in_token_ids.shape[0], H, accepted.device,
+                             with_hidden=target_hidden is not None)
+    a = expand_args(in_token_ids, in_positions, in_start, accepted, bonus, K, mask_id, target_hidden,
+                    mask_hidden, out, verify_tokens)
+    rc = spec_expand_launch(a, _stream_ptr(stream))
+    if rc != SPEC_OK:
+        raise SpecError(rc)
+    return out

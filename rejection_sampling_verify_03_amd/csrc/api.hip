@@ -1,0 +1,160 @@
+// api.hip -- the C ABI: host-side argument validation, workspace sizing and
+// kernel launches.  Every check here runs before anything is enqueued, and no
+// entry point synchronises the stream or allocates memory.
+#include <stdint.h>
+
+#include "spec_verify.h"
+#include "verify_kernels.hpp"
+#include "verify_layout.hpp"
+
+using namespace specv;
+
+namespace {
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+int verify_check(const spec_verify_args* a) {
+  if (!a) return SPEC_EINVAL;
+  if (a->B < 0 || a->K < 1 || a->K > SPEC_MAX_K || a->V < 1) return SPEC_EINVAL;
+  if (a->dtype != SPEC_F32 && a->dtype != SPEC_BF16) return SPEC_EDTYPE;
+  if (a->B == 0) return SPEC_OK;
+  if (!a->target_logits || !a->draft_logits || !a->draft_tokens || !a->temperature ||
+      !a->accepted_counts || !a->output_tokens || !a->workspace)
+    return SPEC_EINVAL;
+  if (a->t_row_stride < a->V || a->d_row_stride < a->V) return SPEC_EINVAL;
+  if (a->t_req_stride != 0 && a->t_req_stride < (int64_t)(a->K + 1) * a->t_row_stride) return SPEC_EINVAL;
+  if (a->d_req_stride != 0 && a->d_req_stride < (int64_t)a->K * a->d_row_stride) return SPEC_EINVAL;
+  const Layout L = make_layout(a->B, a->K, a->V);
+  if ((int64_t)a->B * L.R * L.C > INT32_MAX) return SPEC_EINVAL;
+  if (!aligned16(a->workspace)) return SPEC_EALIGN;
+  if (a->workspace_bytes < L.total) return SPEC_EWORKSPACE;
+  return SPEC_OK;
+}
+
+int expand_check(const spec_expand_args* a) {
+  if (!a) return SPEC_EINVAL;
+  if (a->B < 0 || a->K < 1 || a->H < 0 || a->N_in < 0) return SPEC_EINVAL;
+  if ((int64_t)a->N_in + (int64_t)a->B * (a->K - 1) > INT32_MAX) return SPEC_EINVAL;
+  if (a->B == 0) return SPEC_OK;
+  if (!a->bonus_tokens == !a->verify_output_tokens) return SPEC_EINVAL;  // exactly one bonus source
+  if (!a->in_start || !a->accepted_counts || !a->out_token_ids ||
+      !a->out_positions || !a->rejected_mask || !a->masked_mask || !a->new_token_indices || !a->out_start)
+    return SPEC_EINVAL;
+  if (a->N_in > 0 && (!a->in_token_ids || !a->in_positions || !a->hidden_map)) return SPEC_EINVAL;
+  if (a->out_hidden) {
+    if (a->H > 0 && (!a->mask_hidden || (a->N_in > 0 && !a->target_hidden))) return SPEC_EINVAL;
+    if (a->hidden_row_stride < a->H) return SPEC_EINVAL;
+  }
+  return SPEC_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t spec_verify_workspace_bytes(int32_t B, int32_t K, int32_t V) {
+  if (B < 0 || K < 1 || K > SPEC_MAX_K || V < 1) return 0;
+  return make_layout(B, K, V).total;
+}
+
+int spec_verify_workspace_init(void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (workspace_bytes == 0) return SPEC_OK;
+  if (!workspace) return SPEC_EINVAL;
+  if (!aligned16(workspace)) return SPEC_EALIGN;
+  return launch_fill_zero(workspace, workspace_bytes, stream) == hipSuccess ? SPEC_OK : SPEC_ELAUNCH;
+}
+
+int spec_verify_launch(const spec_verify_args* a, hipStream_t stream) {
+  const int rc = verify_check(a);
+  if (rc != SPEC_OK || a->B == 0) return rc;
+  const Layout L = make_layout(a->B, a->K, a->V);
+  const int es = a->dtype == SPEC_BF16 ? 2 : 4;
+  VerifyParams P;
+  P.B = a->B;
+  P.K = a->K;
+  P.V = a->V;
+  P.R = L.R;
+  P.C = L.C;
+  P.chunk = L.chunk;
+  P.nseg = L.nseg;
+  P.target = static_cast<const char*>(a->target_logits);
+  P.t_req = a->t_req_stride;
+  P.t_row = a->t_row_stride;
+  P.draft = static_cast<const char*>(a->draft_logits);
+  P.d_req = a->d_req_stride;
+  P.d_row = a->d_row_stride;
+  P.tokens = a->draft_tokens;
+  P.temperature = a->temperature;
+  P.seed = a->seed;
+  P.step = a->step;
+  P.request_base = a->request_base;
+  P.accepted = a->accepted_counts;
+  P.out_tokens = a->output_tokens;
+  P.debug = a->debug_probs;
+  char* ws = static_cast<char*>(a->workspace);
+  P.rowp = reinterpret_cast<RowPartial*>(ws + L.off_rowp);
+  P.desc = reinterpret_cast<ReqDesc*>(ws + L.off_desc);
+  P.seg = reinterpret_cast<double*>(ws + L.off_seg);
+  P.cnt1 = reinterpret_cast<uint32_t*>(ws + L.off_cnt1);
+  P.cnt2 = reinterpret_cast<uint32_t*>(ws + L.off_cnt2);
+  const bool vec = aligned16(a->target_logits) && aligned16(a->draft_logits) &&
+                   (a->t_row_stride * es) % 16 == 0 && (a->t_req_stride * es) % 16 == 0 &&
+                   (a->d_row_stride * es) % 16 == 0 && (a->d_req_stride * es) % 16 == 0;
+  return launch_verify(P, a->dtype, vec, static_cast<hipEvent_t>(a->phase_event), stream) == hipSuccess
+             ? SPEC_OK
+             : SPEC_ELAUNCH;
+}
+
+int spec_expand_launch(const spec_expand_args* a, hipStream_t stream) {
+  const int rc = expand_check(a);
+  if (rc != SPEC_OK || a->B == 0) return rc;
+  ExpandParams P;
+  P.B = a->B;
+  P.K = a->K;
+  P.H = a->H;
+  P.N_in = a->N_in;
+  P.mask_id = a->mask_token_id;
+  // ~4 output rows per workgroup on average; a request's window is shared by G
+  // workgroups row-interleaved
+  const int64_t n_out = (int64_t)a->N_in + (int64_t)a->B * (a->K - 1);
+  const int64_t avg_window = (n_out + a->B - 1) / a->B;
+  int64_t G = (avg_window + 3) / 4;
+  if (G < 1) G = 1;
+  if (G > 64) G = 64;
+  if ((int64_t)a->B * G > INT32_MAX) G = 1;
+  P.G = (int32_t)G;
+  P.ids = a->in_token_ids;
+  P.pos = a->in_positions;
+  P.in_start = a->in_start;
+  P.acc = a->accepted_counts;
+  P.bonus = a->bonus_tokens;
+  P.vtok = a->verify_output_tokens;
+  P.th = a->target_hidden;
+  P.th_stride = a->hidden_row_stride;
+  P.mh = a->mask_hidden;
+  P.out_ids = a->out_token_ids;
+  P.out_pos = a->out_positions;
+  P.rej = a->rejected_mask;
+  P.msk = a->masked_mask;
+  P.nti = a->new_token_indices;
+  P.hmap = a->hidden_map;
+  P.out_start = a->out_start;
+  P.out_h = (a->H > 0) ? a->out_hidden : nullptr;
+  const bool vec = (a->H % 8) == 0 && (a->hidden_row_stride % 8) == 0 && aligned16(a->target_hidden) &&
+                   aligned16(a->mask_hidden) && aligned16(a->out_hidden);
+  return launch_expand(P, vec, stream) == hipSuccess ? SPEC_OK : SPEC_ELAUNCH;
+}
+
+const char* spec_status_string(int status) {
+  switch (status) {
+    case SPEC_OK: return "SPEC_OK";
+    case SPEC_EINVAL: return "SPEC_EINVAL: invalid argument (null pointer, size or stride out of range)";
+    case SPEC_EDTYPE: return "SPEC_EDTYPE: unknown logits dtype";
+    case SPEC_EALIGN: return "SPEC_EALIGN: workspace not 16-byte aligned";
+    case SPEC_EWORKSPACE: return "SPEC_EWORKSPACE: workspace too small";
+    case SPEC_ELAUNCH: return "SPEC_ELAUNCH: kernel launch failed";
+    default: return "unknown spec_status";
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,155 @@
+// device_common.hpp -- gfx950 device helpers shared by the verification and
+// expansion kernels: the Philox4x32-10 stream, 8-element logit groups, and
+// 64-lane wavefront / 256-thread workgroup reductions.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace specv {
+
+constexpr int kWG = 256;           // threads per workgroup (4 wave64)
+constexpr int kWaves = kWG / 64;
+
+// ---------------------------------------------------------------- Philox --
+// Philox4x32-10 (Salmon et al., "Parallel Random Numbers: As Easy as 1, 2, 3",
+// SC'11): per round the two multipliers give 64-bit products of counter
+// words 0 and 2, whose halves are recombined with words 1, 3 and the round
+// key; the key advances by the Weyl increments after every round.
+struct Philox4 {
+  uint32_t w[4];
+};
+
+__device__ __forceinline__ Philox4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3,
+                                                  uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int i = 0; i < 10; ++i) {
+    const uint32_t a0 = 0xD2511F53u * c0, b0 = __umulhi(0xD2511F53u, c0);
+    const uint32_t a2 = 0xCD9E8D57u * c2, b2 = __umulhi(0xCD9E8D57u, c2);
+    const uint32_t n0 = b2 ^ c1 ^ k0;
+    const uint32_t n2 = b0 ^ c3 ^ k1;
+    c0 = n0;
+    c1 = a2;
+    c2 = n2;
+    c3 = a0;
+    k0 += 0x9E3779B9u;
+    k1 += 0xBB67AE85u;
+  }
+  return Philox4{{c0, c1, c2, c3}};
+}
+
+// 24 high bits of a word as a uniform in [0, 1); exact in float and double.
+__device__ __forceinline__ double unit_uniform(uint32_t w) { return (double)(w >> 8) * 0x1p-24; }
+
+// ---------------------------------------------------------- logit groups --
+// A group is 8 consecutive logits widened to fp32: one 16-byte load for bf16,
+// two for fp32 (VEC), or 8 scalar loads when the row is not 16-byte aligned.
+template <int ES, bool VEC>
+__device__ __forceinline__ void load_group(const char* __restrict__ row, int64_t e0, float x[8]) {
+  if constexpr (ES == 2) {
+    if constexpr (VEC) {
+      const uint4 v = *reinterpret_cast<const uint4*>(row + e0 * 2);
+      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        x[2 * i] = __uint_as_float(w[i] << 16);
+        x[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+      }
+    } else {
+      const uint16_t* r = reinterpret_cast<const uint16_t*>(row) + e0;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) x[i] = __uint_as_float((uint32_t)r[i] << 16);
+    }
+  } else {
+    if constexpr (VEC) {
+      const float4 a = *reinterpret_cast<const float4*>(row + e0 * 4);
+      const float4 b = *reinterpret_cast<const float4*>(row + e0 * 4 + 16);
+      x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+      x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+    } else {
+      const float* r = reinterpret_cast<const float*>(row) + e0;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) x[i] = r[i];
+    }
+  }
+}
+
+template <int ES>
+__device__ __forceinline__ float load_one(const char* __restrict__ row, int64_t e) {
+  if constexpr (ES == 2)
+    return __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(row)[e] << 16);
+  else
+    return reinterpret_cast<const float*>(row)[e];
+}
+
+// ------------------------------------------------------ scaled exponentials --
+// Logits enter as t = x * s - M with s = log2(e) / T split into s_hi (fp32,
+// rounded toward zero) + s_lo (>= FLT_MIN, so -inf logits stay -inf and give 0)
+// and M an integer-valued reference, so exp2(t) <= 1 for the row maximum.
+__device__ __forceinline__ float scaled_exp2(float x, float s_hi, float s_lo, float negM) {
+  return __builtin_amdgcn_exp2f(__builtin_fmaf(x, s_hi, __builtin_fmaf(x, s_lo, negM)));
+}
+
+// ---------------------------------------------------------- reductions --
+// (M, S) pairs stand for S * 2^M with M integer-valued; merging is exact in
+// the exponent (ldexp) and rounds only in the double add.
+struct MS {
+  float m;
+  double s;
+};
+
+__device__ __forceinline__ MS ms_merge(MS a, MS b) {
+  const float m = fmaxf(a.m, b.m);
+  MS r;
+  r.m = m;
+  const int da = a.m < m ? (int)fmaxf(a.m - m, -2000.f) : 0;
+  const int db = b.m < m ? (int)fmaxf(b.m - m, -2000.f) : 0;
+  r.s = ldexp(a.s, da) + ldexp(b.s, db);
+  return r;
+}
+
+__device__ __forceinline__ double shfl_xor_d(double v, int lane_mask) {
+  return __shfl_xor(v, lane_mask, 64);
+}
+
+// Butterfly over the 64 lanes; every lane ends with the same value.
+__device__ __forceinline__ MS wave_merge_ms(MS v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    MS o;
+    o.m = __shfl_xor(v.m, off, 64);
+    o.s = shfl_xor_d(v.s, off);
+    v = ms_merge(v, o);
+  }
+  return v;
+}
+
+__device__ __forceinline__ double wave_sum_d(double v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += shfl_xor_d(v, off);
+  return v;
+}
+
+// (value, index) with larger value first, lower index on ties.
+struct VI {
+  float v;
+  int i;
+};
+
+__device__ __forceinline__ VI vi_pick(VI a, VI b) {
+  const bool take_b = (b.v > a.v) || (b.v == a.v && b.i < a.i);
+  return take_b ? b : a;
+}
+
+__device__ __forceinline__ VI wave_argmax(VI v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    VI o;
+    o.v = __shfl_xor(v.v, off, 64);
+    o.i = __shfl_xor(v.i, off, 64);
+    v = vi_pick(v, o);
+  }
+  return v;
+}
+
+}  // namespace specv

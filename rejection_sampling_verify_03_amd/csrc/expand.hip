@@ -1,0 +1,114 @@
+// expand.hip -- P-EAGLE parallel-drafting batch expansion and hidden-state
+// gather on gfx950, as one kernel.
+//
+// "P-EAGLE: parallel speculative decoding in vLLM" page: the drafter batch
+// appends K-1 MASK slots per request ("并行草稿生成的挑战"); one pass copies the
+// old token ids and positions into shifted slots, inserts the bonus token,
+// fills the MASK slots and emits the rejected / masked masks, the new-token
+// indices and the hidden-state mapping ("Triton Kernel"); the hidden rows are
+// the mapped target rows, the MASK slots take the learned placeholder
+// ("Hidden State 管理").  The page writes the hidden rows as a scatter through
+// the mapping followed by a masked overwrite; here every output row is
+// written exactly once as a gather, which gives the same rows because the
+// mapping is injective and, with the MASK slots, covers the output.
+//
+// Request b owns the fixed window of n_b + K - 1 slots starting at
+// in_start[b] + b*(K-1), so no scan is needed; G workgroups share a request's
+// window row-interleaved, each writing the metadata of its rows and copying
+// its hidden rows with 16-byte loads and stores.
+#include "device_common.hpp"
+#include "verify_kernels.hpp"
+
+namespace specv {
+
+constexpr int kCopyUnroll = 4;
+
+template <bool VEC>
+__global__ __launch_bounds__(kWG) void expand_kernel(ExpandParams P) {
+  const int b = blockIdx.x / P.G;
+  const int g = blockIdx.x % P.G;
+  const int K = P.K;
+  const int tid = threadIdx.x;
+  const bool gvalid = P.in_start[0] == 0 && P.in_start[P.B] == P.N_in;
+  const int s = P.in_start[b];
+  const int s1 = P.in_start[b + 1];
+  const int n = s1 - s;
+  const int a = P.acc[b];
+  const int o = s + b * (K - 1);
+  const int a_max = P.vtok ? min(n - 1, K) : n - 1;
+  if (gvalid && g == 0 && tid == 0) {
+    P.out_start[b] = o;
+    if (b == P.B - 1) P.out_start[P.B] = P.N_in + P.B * (K - 1);
+  }
+  const bool valid = gvalid && n >= 1 && s >= 0 && s1 <= P.N_in && a >= 0 && a <= a_max;
+  if (!valid) {
+    if (g == 0)
+      for (int m = tid; m < K; m += kWG) P.nti[(int64_t)b * K + m] = -1;
+    return;
+  }
+  const int Wb = n + K - 1;  // slots of this request's window
+  const int bonus = P.vtok ? P.vtok[(int64_t)b * (K + 1) + a] : P.bonus[b];
+
+  // metadata: one thread per slot r of this workgroup's rows g, g+G, ...
+  for (int r = g + P.G * tid; r < Wb; r += P.G * kWG) {
+    const int slot = o + r;
+    if (r < n) {
+      P.hmap[s + r] = slot;
+      P.out_ids[slot] = (r == a) ? bonus : P.ids[s + min(r + 1, n - 1)];
+      P.out_pos[slot] = P.pos[s + r] + 1;
+      P.rej[slot] = (uint8_t)(r > a);
+      P.msk[slot] = 0;
+      if (r == a) P.nti[(int64_t)b * K] = slot;
+    } else {
+      const int m = r - n + 1;  // 1..K-1
+      P.out_ids[slot] = P.mask_id;
+      P.out_pos[slot] = P.pos[s + a] + 1 + m;
+      P.rej[slot] = 0;
+      P.msk[slot] = 1;
+      P.nti[(int64_t)b * K + m] = slot;
+    }
+  }
+
+  if (P.out_h == nullptr || g >= Wb) return;
+  const int nr = (Wb - g + P.G - 1) / P.G;  // rows of this workgroup
+  if constexpr (VEC) {
+    const int ncols = P.H >> 3;  // 16-byte cells per row
+    const int cells = nr * ncols;
+    for (int c0 = tid; c0 < cells; c0 += kWG * kCopyUnroll) {
+      uint4 v[kCopyUnroll];
+      uint4* dst[kCopyUnroll];
+#pragma unroll
+      for (int u = 0; u < kCopyUnroll; ++u) {
+        const int c = c0 + u * kWG;
+        dst[u] = nullptr;
+        if (c < cells) {
+          const int rl = c / ncols, col = c - rl * ncols;
+          const int r = g + P.G * rl;
+          const uint16_t* src = r < n ? P.th + (int64_t)(s + r) * P.th_stride : P.mh;
+          v[u] = reinterpret_cast<const uint4*>(src)[col];
+          dst[u] = reinterpret_cast<uint4*>(P.out_h + (int64_t)(o + r) * P.H) + col;
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < kCopyUnroll; ++u)
+        if (dst[u]) *dst[u] = v[u];
+    }
+  } else {
+    const int cells = nr * P.H;
+    for (int c = tid; c < cells; c += kWG) {
+      const int rl = c / P.H, col = c - rl * P.H;
+      const int r = g + P.G * rl;
+      const uint16_t* src = r < n ? P.th + (int64_t)(s + r) * P.th_stride : P.mh;
+      P.out_h[(int64_t)(o + r) * P.H + col] = src[col];
+    }
+  }
+}
+
+hipError_t launch_expand(const ExpandParams& P, bool vec, hipStream_t stream) {
+  const int64_t grid = (int64_t)P.B * P.G;
+  if (vec) hipLaunchKernelGGL(expand_kernel<true>, dim3((unsigned)grid), dim3(kWG), 0, stream, P);
+  else hipLaunchKernelGGL(expand_kernel<false>, dim3((unsigned)grid), dim3(kWG), 0, stream, P);
+  return hipGetLastError();
+}
+
+}  // namespace specv

@@ -1,0 +1,58 @@
+// verify_kernels.hpp -- kernel parameter blocks and launchers behind the C ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "spec_verify.h"
+#include "verify_layout.hpp"
+
+namespace specv {
+
+struct VerifyParams {
+  int32_t B, K, V, R, C, chunk, nseg;
+  const char* target;
+  int64_t t_req, t_row;
+  const char* draft;
+  int64_t d_req, d_row;
+  const int32_t* tokens;
+  const float* temperature;
+  uint64_t seed;
+  uint32_t step, request_base;
+  int32_t* accepted;
+  int32_t* out_tokens;
+  float* debug;
+  RowPartial* rowp;
+  ReqDesc* desc;
+  double* seg;
+  uint32_t* cnt1;
+  uint32_t* cnt2;
+};
+
+struct ExpandParams {
+  int32_t B, K, H, N_in, G, mask_id;
+  const int32_t* ids;
+  const int64_t* pos;
+  const int32_t* in_start;
+  const int32_t* acc;
+  const int32_t* bonus;
+  const int32_t* vtok;  // verification output tokens [B, K+1] (bonus source) or null
+  const uint16_t* th;
+  int64_t th_stride;
+  const uint16_t* mh;
+  int32_t* out_ids;
+  int64_t* out_pos;
+  uint8_t* rej;
+  uint8_t* msk;
+  int32_t* nti;
+  int32_t* hmap;
+  int32_t* out_start;
+  uint16_t* out_h;
+};
+
+hipError_t launch_verify(const VerifyParams& P, int dtype, bool vec, hipEvent_t phase_event,
+                         hipStream_t stream);
+hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t stream);
+hipError_t launch_expand(const ExpandParams& P, bool vec, hipStream_t stream);
+
+}  // namespace specv

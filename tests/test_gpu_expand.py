@@ -1,0 +1,146 @@
+"""GPU P-EAGLE expansion through the C ABI against the CPU oracle: every output
+bit-exact (token ids, positions, masks, new-token indices, hidden map, start
+indices and the gathered hidden rows)."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def sv():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import rejection_sampling_verify_03_amd as m
+    return m
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def to_dev(e):
+    for k in ("in_token_ids", "in_positions", "in_start", "accepted", "bonus", "target_hidden", "mask_hidden"):
+        setattr(e, k, getattr(e, k).cuda())
+    return e
+
+
+def run_both(sv, e, with_hidden=True, accepted=None, in_start=None, hidden=None):
+    acc = e.accepted if accepted is None else accepted
+    st = e.in_start if in_start is None else in_start
+    th = (e.target_hidden if hidden is None else hidden) if with_hidden else None
+    out = sv.expand(e.in_token_ids, e.in_positions, st, acc, e.bonus, e.K, e.mask_id, th,
+                    e.mask_hidden if with_hidden else None)
+    torch.cuda.synchronize()
+    ref = oracle.expand(e.in_token_ids.cpu().numpy(), e.in_positions.cpu().numpy(), st.cpu().numpy(),
+                        acc.cpu().numpy(), e.bonus.cpu().numpy(), e.K, e.mask_id,
+                        workloads.bf16_bits(th) if with_hidden else None,
+                        workloads.bf16_bits(e.mask_hidden) if with_hidden else None)
+    return out, ref
+
+
+def assert_same(out, ref, with_hidden=True, valid_rows=None):
+    nti = out.new_token_indices.cpu().numpy()
+    np.testing.assert_array_equal(nti, ref.new_token_indices)
+    ok_req = (ref.new_token_indices[:, 0] >= 0)
+    if (ref.out_start != -7).all():
+        np.testing.assert_array_equal(out.out_start.cpu().numpy(), ref.out_start)
+    # slots of valid requests (invalid ones are not written by either side)
+    mask = ref.out_token_ids != -7
+    for name in ("out_token_ids", "out_positions", "rejected_mask", "masked_mask"):
+        np.testing.assert_array_equal(getattr(out, name).cpu().numpy()[mask], getattr(ref, name)[mask], name)
+    hm_mask = ref.hidden_map != -7
+    np.testing.assert_array_equal(out.hidden_map.cpu().numpy()[hm_mask], ref.hidden_map[hm_mask])
+    if with_hidden:
+        got = workloads.bf16_bits(out.out_hidden)
+        np.testing.assert_array_equal(got[mask], ref.out_hidden[mask])
+    return ok_req
+
+
+def test_full_size_expand(sv):
+    """B=512, K=8, H=2880 (the GPT-OSS-20B hidden width), ragged accepted
+    counts, positions from offsets in [0, 16384)."""
+    say("case: expand B512 K8 H2880")
+    for seed in (0, 1):
+        e = workloads.expand_inputs(B=512, K=8, seed=seed, device="cuda")
+        out, ref = run_both(sv, e)
+        assert ref.n_bad == 0
+        assert_same(out, ref)
+
+
+@pytest.mark.parametrize("K,H", [(1, 64), (2, 2880), (5, 100), (8, 7), (63, 16)])
+def test_shapes_and_scalar_path(sv, K, H):
+    """K = 1 (no MASK slots), H not a multiple of 8 (2-byte copy path)."""
+    say("case: expand K%d H%d" % (K, H))
+    e = workloads.expand_inputs(B=37, K=K, H=H, seed=K + H, device="cuda")
+    out, ref = run_both(sv, e)
+    assert_same(out, ref)
+
+
+def test_ragged_requests_and_strided_hidden(sv):
+    say("case: expand ragged")
+    rng = np.random.default_rng(5)
+    n = rng.integers(1, 40, 300)
+    e = workloads.expand_inputs(B=300, K=6, H=256, seed=5, device="cuda", n_per_request=n)
+    out, ref = run_both(sv, e)
+    assert_same(out, ref)
+    # hidden rows inside a wider buffer (row stride > H)
+    wide = torch.zeros(e.N_in, 320, dtype=torch.bfloat16, device="cuda")
+    wide[:, :256] = e.target_hidden
+    out2, ref2 = run_both(sv, e, hidden=wide[:, :256])
+    assert_same(out2, ref2)
+
+
+def test_metadata_only(sv):
+    say("case: expand without hidden rows")
+    e = workloads.expand_inputs(B=64, K=4, H=8, seed=3, device="cuda")
+    out, ref = run_both(sv, e, with_hidden=False)
+    assert out.out_hidden is None
+    assert_same(out, ref, with_hidden=False)
+
+
+def test_invalid_requests(sv):
+    say("case: expand invalid data")
+    e = workloads.expand_inputs(B=6, K=3, H=16, seed=9, device="cuda")
+    acc = e.accepted.clone()
+    acc[2] = 4   # n = 4: a must be <= 3
+    acc[4] = -1
+    out, ref = run_both(sv, e, accepted=acc)
+    assert ref.n_bad == 2
+    assert_same(out, ref)
+    # an empty request (n_b = 0)
+    st = torch.tensor([0, 4, 4, 8, 12, 16, 24], dtype=torch.int32, device="cuda")
+    out, ref = run_both(sv, e, in_start=st, accepted=torch.tensor([1, 0, 2, 3, 0, 7], dtype=torch.int32,
+                                                                  device="cuda"))
+    assert ref.n_bad == 1
+    assert_same(out, ref)
+    # start indices not covering the input: every request invalid
+    st = e.in_start.clone()
+    st[-1] -= 1
+    out, ref = run_both(sv, e, in_start=st)
+    assert ref.n_bad == 6
+    assert (out.new_token_indices.cpu().numpy() == -1).all()
+
+
+def test_chained_after_verify(sv):
+    """The bonus read straight from a verification's output tokens."""
+    say("case: verify -> expand chained")
+    vin = workloads.verify_tiny(seed=2, device="cuda")
+    acc, tok, _ = sv.verify(vin.target, vin.draft, vin.draft_tokens, vin.temperature, seed=4)
+    B, K = vin.B, vin.K
+    e = workloads.expand_inputs(B=B, K=K, H=64, seed=2, device="cuda", accepted=acc.cpu())
+    out = sv.expand(e.in_token_ids, e.in_positions, e.in_start, acc, None, K, e.mask_id, e.target_hidden,
+                    e.mask_hidden, verify_tokens=tok)
+    torch.cuda.synchronize()
+    a = acc.cpu().numpy()
+    bonus = tok.cpu().numpy()[np.arange(B), a]
+    ref = oracle.expand(e.in_token_ids.cpu().numpy(), e.in_positions.cpu().numpy(), e.in_start.cpu().numpy(),
+                        a, bonus, K, e.mask_id, workloads.bf16_bits(e.target_hidden),
+                        workloads.bf16_bits(e.mask_hidden))
+    assert_same(out, ref)

@@ -1,0 +1,310 @@
+"""GPU verification through the C ABI against the CPU oracle.
+
+Element-by-element parity at sizes the oracle finishes in seconds (several
+chunks per row, ragged tails, vector and scalar load paths, shared and padded
+rows, every special case), then the full-size workloads in the launch
+configuration the benchmark times, checked on sampled requests the oracle
+computes one by one.  The bar is the one in ``parity.py``.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from parity import Report, compare
+from stats_helpers import binom_z, chi2_pvalue, draw_categorical, softmax_rows
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def sv():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import rejection_sampling_verify_03_amd as m
+    return m
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def host(inp):
+    return (workloads.logits_numpy(inp.target), workloads.logits_numpy(inp.draft),
+            inp.draft_tokens.cpu().numpy(), inp.temperature.cpu().numpy())
+
+
+def run(sv, target, draft, x, T, seed=0, step=0, request_base=0, debug=True, ws=None):
+    acc, tok, dbg = sv.verify(target, draft, x, T, seed=seed, step=step, request_base=request_base,
+                              debug=debug, workspace=ws)
+    torch.cuda.synchronize()
+    return acc.cpu().numpy(), tok.cpu().numpy(), None if dbg is None else dbg.cpu().numpy()
+
+
+def to_dev(inp):
+    inp.target = inp.target.cuda()
+    inp.draft = inp.draft.cuda()
+    inp.draft_tokens = inp.draft_tokens.cuda()
+    inp.temperature = inp.temperature.cuda()
+    return inp
+
+
+def check(sv, inp, seeds=(0,), steps=(0,), debug=True):
+    tl, dl, x, T = host(inp)
+    rep = Report()
+    for seed in seeds:
+        for step in steps:
+            acc, tok, dbg = run(sv, inp.target, inp.draft, inp.draft_tokens, inp.temperature, seed, step,
+                                debug=debug)
+            compare(tl, dl, x, T, acc, tok, dbg, seed=seed, step=step, report=rep)
+    say(inp.name, rep.summary())
+    assert rep.ok(), rep.failures[:5]
+    return rep
+
+
+def test_tiny_fp32_many_steps(sv):
+    say("case: tiny B4 K4 V1024 fp32, 64 steps")
+    inp = to_dev(workloads.verify_tiny(seed=0))
+    rep = check(sv, inp, seeds=(0, 1), steps=range(32))
+    assert rep.exact >= rep.requests - 2
+
+
+@pytest.mark.parametrize("dtype,V", [(torch.bfloat16, 70001), (torch.float32, 33000),
+                                     (torch.bfloat16, 2 * 32768 + 512)])
+def test_multi_chunk_mixed_temperatures(sv, dtype, V):
+    say("case: B12 K5 V%d %s mixed T" % (V, dtype))
+    inp = workloads.mixture_inputs("mixed B12 K5 V%d" % V, 12, 5, V, dtype, 3, "cuda",
+                                   temps=(0.0, 0.6, 1.0), lam_lo=0.05, lam_hi=0.6)
+    check(sv, inp, seeds=(0, 5), steps=(0, 1))
+
+
+@pytest.mark.parametrize("dtype,V", [(torch.float32, 1023), (torch.bfloat16, 20003), (torch.bfloat16, 9)])
+def test_scalar_load_path(sv, dtype, V):
+    """Rows whose byte length is not a multiple of 16 take the scalar path."""
+    say("case: scalar path V%d %s" % (V, dtype))
+    inp = workloads.noisy_draft_inputs("scalar V%d" % V, 6, 4, V, dtype, 1, "cuda", "gauss",
+                                       target_std=2.0, draft_noise=0.5)
+    check(sv, inp, seeds=(0,), steps=range(4))
+
+
+def test_padded_rows_and_views(sv):
+    """Logits inside larger buffers: row stride > V (padded), and only the
+    first K draft rows present."""
+    say("case: padded rows")
+    B, K, V = 8, 4, 5000
+    base = workloads.mixture_inputs("pad", B, K, V, torch.bfloat16, 4, "cuda", temps=(0.6, 1.0),
+                                    lam_lo=0.1, lam_hi=0.5)
+    tpad = torch.full((B, K + 1, V + 64), -30.0, dtype=torch.bfloat16, device="cuda")
+    tpad[:, :, :V] = base.target
+    dpad = torch.full((B, K, V + 128), -30.0, dtype=torch.bfloat16, device="cuda")
+    dpad[:, :, :V] = base.draft[:, :K]
+    tl, dl, x, T = host(base)
+    acc, tok, dbg = run(sv, tpad[:, :, :V], dpad[:, :, :V], base.draft_tokens, base.temperature, 9, 2)
+    rep = compare(tl, dl, x, T, acc, tok, dbg, seed=9, step=2)
+    say(rep.summary())
+    assert rep.ok(), rep.failures[:5]
+
+
+def test_shared_rows_broadcast(sv):
+    """Request stride 0: every request reads the same rows."""
+    say("case: shared rows")
+    K, V, B = 3, 700, 512
+    rng = np.random.default_rng(0)
+    tl = (1.5 * rng.standard_normal((1, K + 1, V))).astype(np.float32)
+    dl = (tl + rng.standard_normal((1, K + 1, V))).astype(np.float32)
+    x = draw_categorical(softmax_rows(dl[0, :K]), B, rng)
+    T = np.ones(B, np.float32)
+    t = torch.from_numpy(tl).cuda().expand(B, K + 1, V)
+    d = torch.from_numpy(dl).cuda().expand(B, K + 1, V)
+    acc, tok, dbg = run(sv, t, d, torch.from_numpy(x).cuda(), torch.from_numpy(T).cuda(), 3)
+    rep = compare(tl, dl, x, T, acc, tok, dbg, seed=3)
+    say(rep.summary())
+    assert rep.ok(), rep.failures[:5]
+
+
+def test_special_cases(sv):
+    say("case: special cases")
+    rng = np.random.default_rng(1)
+    # identical distributions => everything accepted
+    B, K, V = 64, 5, 100
+    t = torch.zeros(B, K + 1, V, device="cuda")
+    x = torch.from_numpy(rng.integers(0, V, (B, K)).astype(np.int32)).cuda()
+    acc, tok, _ = run(sv, t, t, x, torch.ones(B, device="cuda"))
+    assert (acc == K).all() and (tok[:, :K] == x.cpu().numpy()).all()
+    tl = (2 * rng.standard_normal((B, K + 1, 3000))).astype(np.float32)
+    tt = torch.from_numpy(tl).cuda().bfloat16()
+    acc, _, _ = run(sv, tt, tt, torch.from_numpy(rng.integers(0, 3000, (B, K)).astype(np.int32)).cuda(),
+                    torch.full((B,), 0.6, device="cuda"))
+    assert (acc == K).all()
+    # disjoint supports => reject at once, resample inside p's support
+    tl = np.full((B, K + 1, 40), -np.inf, np.float32)
+    dl = np.full((B, K + 1, 40), -np.inf, np.float32)
+    tl[:, :, :20] = rng.standard_normal((B, K + 1, 20))
+    dl[:, :, 20:] = rng.standard_normal((B, K + 1, 20))
+    x = rng.integers(20, 40, (B, K)).astype(np.int32)
+    T = np.ones(B, np.float32)
+    acc, tok, dbg = run(sv, torch.from_numpy(tl).cuda(), torch.from_numpy(dl).cuda(),
+                        torch.from_numpy(x).cuda(), torch.from_numpy(T).cuda(), 5)
+    assert (acc == 0).all() and (tok[:, 0] < 20).all()
+    rep = compare(tl, dl, x, T, acc, tok, dbg, seed=5)
+    assert rep.ok(), rep.failures[:5]
+    # one-hot targets => deterministic output
+    c = rng.integers(0, 50, (B, K + 1))
+    tl = np.full((B, K + 1, 50), -np.inf, np.float32)
+    for b in range(B):
+        tl[b, np.arange(K + 1), c[b]] = 0.0
+    dl = rng.standard_normal((B, K + 1, 50)).astype(np.float32)
+    x = rng.integers(0, 50, (B, K)).astype(np.int32)
+    x[: B // 2] = c[: B // 2, :K]
+    acc, tok, dbg = run(sv, torch.from_numpy(tl).cuda(), torch.from_numpy(dl).cuda(),
+                        torch.from_numpy(x).cuda(), torch.ones(B, device="cuda"), 6)
+    for b in range(B):
+        assert list(tok[b, :acc[b] + 1]) == list(c[b, :acc[b] + 1])
+    # greedy with ties: lowest index
+    t = torch.zeros(3, 3, 16, device="cuda")
+    t[:, 0, 3] = t[:, 0, 7] = 5.0
+    t[:, 1, 2] = t[:, 1, 9] = 4.0
+    t[:, 2, 11] = t[:, 2, 12] = 1.0
+    x = torch.tensor([[7, 2], [3, 9], [3, 2]], dtype=torch.int32, device="cuda")
+    acc, tok, dbg = run(sv, t, t, x, torch.zeros(3, device="cuda"))
+    assert list(acc) == [0, 1, 2]
+    assert tok.tolist() == [[3, -1, -1], [3, 2, -1], [3, 2, 11]]
+    assert (dbg == 0).all()
+    # bf16 greedy ties across chunk boundaries (V spans 3 chunks)
+    V = 3 * 32768
+    t = torch.zeros(2, 2, V, device="cuda", dtype=torch.bfloat16)
+    t[:, 0, [40000, 70000, 90000]] = 3.0
+    t[:, 1, [5, 98000]] = 2.0
+    acc, tok, _ = run(sv, t, t, torch.tensor([[40000], [70000]], dtype=torch.int32, device="cuda"),
+                      torch.zeros(2, device="cuda"))
+    assert list(acc) == [1, 0] and tok.tolist() == [[40000, 5], [40000, -1]]
+    # all -inf greedy row => index 0, as the oracle's argmax
+    t = torch.full((1, 2, 300), -float("inf"), device="cuda")
+    acc, tok, _ = run(sv, t, t, torch.tensor([[0]], dtype=torch.int32, device="cuda"),
+                      torch.zeros(1, device="cuda"))
+    assert acc[0] == 1 and tok[0].tolist() == [0, 0]
+    # V = 1 and K = 1
+    acc, tok, _ = run(sv, torch.zeros(3, 3, 1, device="cuda"), torch.zeros(3, 3, 1, device="cuda"),
+                      torch.zeros(3, 2, dtype=torch.int32, device="cuda"),
+                      torch.tensor([1.0, 0.0, 0.5], device="cuda"))
+    assert (acc == 2).all() and (tok == 0).all()
+    inp = workloads.noisy_draft_inputs("K1", 16, 1, 999, torch.float32, 7, "cuda", "gauss")
+    check(sv, inp, steps=range(3))
+    # K = 63, the largest ballot
+    inp = workloads.noisy_draft_inputs("K63", 3, 63, 256, torch.float32, 8, "cuda", "gauss",
+                                       target_std=0.3, draft_noise=0.05)
+    check(sv, inp, steps=range(2))
+
+
+def test_invalid_requests(sv):
+    say("case: invalid request data")
+    inp = workloads.noisy_draft_inputs("bad", 6, 3, 64, torch.float32, 2, "cuda", "gauss")
+    x = inp.draft_tokens.clone()
+    T = inp.temperature.clone()
+    t = inp.target.clone()
+    x[1, 2] = 64
+    x[2, 0] = -5
+    T[3] = -1.0
+    T[4] = float("nan")
+    t[5, 1, :] = -float("inf")
+    acc, tok, dbg = run(sv, t, inp.draft, x, T)
+    assert acc[0] >= 0
+    for b in range(1, 6):
+        assert acc[b] == -1 and (tok[b] == -1).all() and (dbg[b] == 0).all(), b
+    tl = workloads.logits_numpy(t)
+    dl = workloads.logits_numpy(inp.draft)
+    rep = compare(tl, dl, x.cpu().numpy(), T.cpu().numpy(), acc, tok, dbg)
+    assert rep.ok(), rep.failures
+
+
+def test_determinism_and_workspace_reuse(sv):
+    say("case: determinism / workspace reuse")
+    big = workloads.mixture_inputs("reuse", 16, 6, 40000, torch.bfloat16, 11, "cuda", temps=(0.0, 1.0),
+                                   lam_lo=0.1, lam_hi=0.5)
+    small = workloads.verify_tiny(seed=3, device="cuda")
+    ws = sv.make_workspace(16, 6, 40000)
+    assert sv.spec_verify_workspace_bytes(4, 4, 1024) <= ws.numel()
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def reinit():
+        assert sv.spec_verify_workspace_init(ws.data_ptr(), ws.numel(), stream) == sv.SPEC_OK
+
+    r1 = run(sv, big.target, big.draft, big.draft_tokens, big.temperature, 1, 0, ws=ws)
+    r1b = run(sv, big.target, big.draft, big.draft_tokens, big.temperature, 1, 0, ws=ws)
+    reinit()  # a workspace serves one shape
+    r2 = run(sv, small.target, small.draft, small.draft_tokens, small.temperature, 1, 0, ws=ws)
+    reinit()
+    r3 = run(sv, big.target, big.draft, big.draft_tokens, big.temperature, 1, 0, ws=ws)
+    r4 = run(sv, small.target, small.draft, small.draft_tokens, small.temperature, 1, 0)
+    for a, b in zip(r1, r1b):
+        assert np.array_equal(a, b)
+    for a, b in zip(r1, r3):
+        assert np.array_equal(a, b)
+    for a, b in zip(r2, r4):
+        assert np.array_equal(a, b)
+
+
+def test_output_law_through_the_gpu(sv):
+    """The distribution-preservation theorem on the GPU outputs: 10^6
+    requests sharing rows (V = 64, K = 3); tokens at each reached position
+    follow p_k, acceptance counts are binomial."""
+    say("case: chi-square through the GPU, 1e6 requests")
+    K, V, N = 3, 64, 1_000_000
+    rng = np.random.default_rng(64)
+    tl = (1.5 * rng.standard_normal((1, K + 1, V))).astype(np.float32)
+    dl = (tl + rng.standard_normal((1, K + 1, V))).astype(np.float32)
+    p, q = softmax_rows(tl[0]), softmax_rows(dl[0])
+    x = draw_categorical(q[:K], N, rng)
+    t = torch.from_numpy(tl).cuda().expand(N, K + 1, V)
+    d = torch.from_numpy(dl).cuda().expand(N, K + 1, V)
+    acc, tok, _ = run(sv, t, d, torch.from_numpy(x).cuda(), torch.ones(N, device="cuda"), seed=77,
+                      debug=False)
+    pv, zs = [], []
+    for k in range(K + 1):
+        reach = acc >= k
+        pv.append(chi2_pvalue(np.bincount(tok[reach, k], minlength=V), p[k]))
+        if k < K:
+            zs.append(binom_z(int((acc[reach] > k).sum()), int(reach.sum()), float(np.minimum(p[k], q[k]).sum())))
+    say("p-values", pv, "z", zs)
+    assert min(pv) >= 1e-4 and max(abs(z) for z in zs) < 5
+
+
+def test_gptoss_vocab_full_parity(sv):
+    """B=64, K=5, V=201088 bf16 Zipf rows, draft = target + N(0, 0.7): every
+    request against the oracle."""
+    say("case: gpt-oss vocab B64 K5 V201088, full parity")
+    inp = workloads.verify_gptoss(seed=0, device="cuda")
+    rep = check(sv, inp, seeds=(0,), steps=(0, 1))
+    assert rep.exact >= rep.requests - 4
+
+
+def _sampled_parity(sv, inp, idx, seed, step, acc, tok, dbg, rep):
+    for b in idx:
+        tl = workloads.logits_numpy(inp.target[b:b + 1])
+        dl = workloads.logits_numpy(inp.draft[b:b + 1])
+        x = inp.draft_tokens[b:b + 1].cpu().numpy()
+        T = inp.temperature[b:b + 1].cpu().numpy()
+        compare(tl, dl, x, T, acc[b:b + 1], tok[b:b + 1], dbg[b:b + 1], seed=seed, step=step,
+                request_base=b, report=rep)
+
+
+def test_headline_full_size_sampled(sv):
+    """B=256, K=8, V=151936 bf16, temperatures {0, 0.6, 1}, mixture drafts:
+    the whole batch in one launch (as benchmarked), 40 requests checked
+    against the oracle one by one, and run-to-run bit-identical."""
+    say("case: headline B256 K8 V151936, sampled parity")
+    inp = workloads.verify_headline(seed=0, device="cuda")
+    acc, tok, dbg = run(sv, inp.target, inp.draft, inp.draft_tokens, inp.temperature, 0, 0)
+    acc2, tok2, dbg2 = run(sv, inp.target, inp.draft, inp.draft_tokens, inp.temperature, 0, 0)
+    assert np.array_equal(acc, acc2) and np.array_equal(tok, tok2) and np.array_equal(dbg, dbg2)
+    rng = np.random.default_rng(0)
+    idx = sorted(set([0, 1, 255] + list(rng.choice(256, 37, replace=False))))
+    rep = Report()
+    _sampled_parity(sv, inp, idx, 0, 0, acc, tok, dbg, rep)
+    say(rep.summary())
+    assert rep.ok(), rep.failures[:5]
+    T = inp.temperature.cpu().numpy()
+    say("accepted mean by T:", {float(t): float(acc[T == t].mean()) for t in np.unique(T)})
+    assert (acc >= 0).all() and (acc <= 8).all()

@@ -136,9 +136,17 @@ def test_invalid_requests_write_nothing():
     assert r.n_bad == 1
     o0, o1 = r.out_start[2], r.out_start[3]
     assert (r.out_token_ids[o0:o1] == -7).all()
-    assert (r.new_token_indices[2] == -7).all()
-    with pytest.raises(ValueError):
-        st = inp.in_start.numpy().copy()
-        st[-1] += 1  # in_start[B] != N_in
-        oracle.expand(inp.in_token_ids.numpy(), inp.in_positions.numpy(), st, inp.accepted.numpy(),
+    assert (r.new_token_indices[2] == -1).all()
+    assert (r.new_token_indices[[0, 1, 3]] >= 0).all()
+    # an empty request (n_b = 0) is invalid, its neighbours are not
+    st = np.array([0, 4, 4, 8, 12], np.int32)
+    r = oracle.expand(inp.in_token_ids.numpy()[:12], inp.in_positions.numpy()[:12], st,
+                      [1, 0, 2, 3], inp.bonus.numpy(), 3, inp.mask_id)
+    assert r.n_bad == 1 and (r.new_token_indices[1] == -1).all()
+    assert (r.new_token_indices[[0, 2, 3]] >= 0).all()
+    # start indices that do not cover the input rows invalidate every request
+    st = inp.in_start.numpy().copy()
+    st[-1] -= 1  # in_start[B] != N_in
+    r = oracle.expand(inp.in_token_ids.numpy(), inp.in_positions.numpy(), st, inp.accepted.numpy(),
                       inp.bonus.numpy(), 3, inp.mask_id)
+    assert r.n_bad == 4 and (r.new_token_indices == -1).all() and (r.out_start == -7).all()
