@@ -93,23 +93,17 @@ typedef struct {
   int32_t* accepted_counts;    /* device out [B]: a_b in 0..K; -1 = invalid request data */
   int32_t* output_tokens;      /* device out [B, K+1]: x_0..x_{a-1}, the emitted token, then -1 */
   float* debug_probs;          /* device out [B, K, 2] or NULL: p_k(x_k), q_k(x_k) (0 for T = 0) */
-  void* workspace;             /* device scratch, spec_verify_workspace_bytes(B, K, V) bytes */
+  void* workspace;             /* device scratch, >= spec_verify_workspace_bytes(B, K, V) bytes, 16-B aligned */
   size_t workspace_bytes;
-  void* phase_event;           /* hipEvent_t or NULL: recorded on `stream` between the row-statistics
-                                  kernel and the sampling kernel (for timing them apart) */
+  void* phase_event;           /* hipEvent_t or NULL: recorded on `stream` right after the
+                                  row-statistics kernel (to time it apart from the rest) */
 } spec_verify_args;
 
-/* Bytes of device workspace a verification of this shape needs. */
+/* Bytes of device workspace a verification of this shape needs (0 for an
+ * invalid shape).  The workspace carries nothing from one call to the next:
+ * it needs no initialisation and may be reused for any shape it is large
+ * enough for.  Calls that overlap on one workspace race. */
 size_t spec_verify_workspace_bytes(int32_t B, int32_t K, int32_t V);
-
-/* Zero-fill a workspace (enqueued on `stream`, a fill kernel, no memset
- * node).  A workspace serves one (B, K, V) shape: initialise it before its
- * first use and again before using it for another shape.  Every verification
- * that runs to completion leaves its arrival counters at zero, so one
- * initialisation suffices for any number of calls of that shape.  Misuse
- * (no initialisation, a shape change) gives wrong outputs but never an
- * out-of-bounds access.  Calls that overlap on one workspace race. */
-int spec_verify_workspace_init(void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Enqueue one verification step.  A request whose data is invalid (a draft
  * token outside [0, V), a temperature that is negative, NaN or infinite, or a

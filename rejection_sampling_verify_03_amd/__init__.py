@@ -6,8 +6,7 @@ is no fallback: if the library has not been built (``build.py``) importing the
 binding raises.
 
 Same names as the C ABI: ``spec_verify_workspace_bytes``,
-``spec_verify_workspace_init``, ``spec_verify_launch``, ``spec_expand_launch``,
-``spec_status_string``; plus two convenience wrappers, ``verify`` and
+``spec_verify_launch``, ``spec_expand_launch``, ``spec_status_string``; plus two convenience wrappers, ``verify`` and
 ``expand``, that allocate the outputs and call the launchers on torch's current
 stream.
 """
@@ -21,8 +20,8 @@ SPEC_OK, SPEC_EINVAL, SPEC_EDTYPE, SPEC_EALIGN, SPEC_EWORKSPACE, SPEC_ELAUNCH = 
 SPEC_F32, SPEC_BF16 = 0, 1
 SPEC_MAX_K = 63
 
-EXPORTED = ("spec_verify_workspace_bytes", "spec_verify_workspace_init", "spec_verify_launch",
-            "spec_expand_launch", "spec_status_string")
+EXPORTED = ("spec_verify_workspace_bytes", "spec_verify_launch", "spec_expand_launch",
+            "spec_status_string")
 
 
 class SpecVerifyArgs(ctypes.Structure):
@@ -66,8 +65,6 @@ def _load():
     L = ctypes.CDLL(LIB_PATH)
     L.spec_verify_workspace_bytes.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32]
     L.spec_verify_workspace_bytes.restype = ctypes.c_size_t
-    L.spec_verify_workspace_init.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
-    L.spec_verify_workspace_init.restype = ctypes.c_int
     L.spec_verify_launch.argtypes = [ctypes.POINTER(SpecVerifyArgs), ctypes.c_void_p]
     L.spec_verify_launch.restype = ctypes.c_int
     L.spec_expand_launch.argtypes = [ctypes.POINTER(SpecExpandArgs), ctypes.c_void_p]
@@ -89,10 +86,6 @@ class SpecError(RuntimeError):
 # ----------------------------------------------------------------- raw C ABI
 def spec_verify_workspace_bytes(B, K, V):
     return int(lib.spec_verify_workspace_bytes(int(B), int(K), int(V)))
-
-
-def spec_verify_workspace_init(workspace_ptr, workspace_bytes, stream_ptr):
-    return int(lib.spec_verify_workspace_init(workspace_ptr, int(workspace_bytes), stream_ptr))
 
 
 def spec_verify_launch(args, stream_ptr):
@@ -140,11 +133,11 @@ def _check_dev(*ts):
 
 
 def make_workspace(B, K, V, device="cuda"):
-    """A zero-filled workspace for verifications of this shape (zeroed by
-    torch; the library keeps its counters at zero after every call)."""
+    """A workspace large enough for verifications of this shape (no
+    initialisation needed; torch's allocations are 256-byte aligned)."""
     torch = _torch()
     n = spec_verify_workspace_bytes(B, K, V)
-    return torch.zeros(max(n, 16), dtype=torch.uint8, device=device)
+    return torch.empty(max(n, 16), dtype=torch.uint8, device=device)
 
 
 def verify_args(target, draft, draft_tokens, temperature, accepted, tokens, debug, workspace,

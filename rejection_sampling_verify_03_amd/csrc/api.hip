@@ -57,13 +57,6 @@ size_t spec_verify_workspace_bytes(int32_t B, int32_t K, int32_t V) {
   return make_layout(B, K, V).total;
 }
 
-int spec_verify_workspace_init(void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  if (workspace_bytes == 0) return SPEC_OK;
-  if (!workspace) return SPEC_EINVAL;
-  if (!aligned16(workspace)) return SPEC_EALIGN;
-  return launch_fill_zero(workspace, workspace_bytes, stream) == hipSuccess ? SPEC_OK : SPEC_ELAUNCH;
-}
-
 int spec_verify_launch(const spec_verify_args* a, hipStream_t stream) {
   const int rc = verify_check(a);
   if (rc != SPEC_OK || a->B == 0) return rc;
@@ -95,8 +88,6 @@ int spec_verify_launch(const spec_verify_args* a, hipStream_t stream) {
   P.rowp = reinterpret_cast<RowPartial*>(ws + L.off_rowp);
   P.desc = reinterpret_cast<ReqDesc*>(ws + L.off_desc);
   P.seg = reinterpret_cast<double*>(ws + L.off_seg);
-  P.cnt1 = reinterpret_cast<uint32_t*>(ws + L.off_cnt1);
-  P.cnt2 = reinterpret_cast<uint32_t*>(ws + L.off_cnt2);
   const bool vec = aligned16(a->target_logits) && aligned16(a->draft_logits) &&
                    (a->t_row_stride * es) % 16 == 0 && (a->t_req_stride * es) % 16 == 0 &&
                    (a->d_row_stride * es) % 16 == 0 && (a->d_req_stride * es) % 16 == 0;

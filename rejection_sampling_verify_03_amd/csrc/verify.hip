@@ -7,7 +7,9 @@
 // sampled from p_K.  Temperature 0 is the greedy limit (accept iff x_k is the
 // target argmax, emit the target argmax where the request stops).
 //
-// Two kernels, no host round trip and no spin-waits:
+// Three kernels in stream order, no host round trip, and no communication
+// between workgroups of one kernel (kernel boundaries make each kernel's
+// writes visible to the next, so no atomics and no cache-maintenance fences):
 //
 //  verify_rowstats  one workgroup per (request, row, chunk of ~32K logits)
 //      streams every row the parallel formulation needs exactly once (target
@@ -15,18 +17,20 @@
 //      loads, and reduces the chunk to S * 2^M = sum_v 2^(x_v * s - M)
 //      (s = log2(e) / T, M an integer-valued reference raised by exact
 //      power-of-two rescaling) or, for greedy requests, to (max, lowest
-//      argmax).  The last workgroup of a request (atomic arrival counter)
-//      merges the chunks in order, evaluates the K accept tests in parallel
-//      (one lane per position, Philox uniforms, double-precision p(x), q(x)),
-//      finds a_b as the count of trailing ones of a wavefront ballot and
-//      writes the accepted prefix plus what the sampling pass needs.
+//      argmax).
 //
-//  verify_sample    one workgroup per (request, chunk) re-reads only the
-//      sampling row(s) of sampled requests (p_a and q_a, or p_K for the bonus)
-//      and writes sums of the residual weights max(0, p - q) and of p over
-//      512-element segments; the last workgroup of the request scans the
-//      segment sums for the inverse-CDF crossing of u' * R, recomputes the
-//      weights of that one segment, and finds the token with a wavefront scan.
+//  verify_decide    one workgroup per (request, chunk): merges the request's
+//      chunk partials in order, evaluates the K accept tests in parallel (one
+//      lane per position, Philox uniforms, double-precision p(x), q(x)) and
+//      finds a_b as the count of trailing ones of a wavefront ballot -- every
+//      workgroup of the request derives the same decision; the chunk-0
+//      workgroup writes the outputs -- then re-reads its chunk of the sampling
+//      row(s) (p_a and q_a, or p_K for the bonus) and writes sums of the
+//      residual weights max(0, p - q) and of p over 512-element segments.
+//
+//  verify_sample    one workgroup per sampled request scans the segment sums
+//      for the inverse-CDF crossing of u' * R, recomputes the weights of that
+//      one segment and finds the token with a wavefront scan.
 #include <float.h>
 #include <limits.h>
 
@@ -178,15 +182,25 @@ __device__ __forceinline__ VI block_argmax(VI v) {
 }
 
 // ------------------------------------------------------------- decision
-// Run by the last workgroup to finish a request's rows.
+struct Decision {
+  int a;     // accepted drafts, -1 for invalid request data
+  int mode;  // kModeNone / kModeResidual / kModeBonus
+  float s_hi, s_lo;
+  double mp, sp, mq, sq, u;
+};
+
+// The decision of request b, computed by the whole workgroup into `D`
+// (shared).  With `write`, the outputs of the request are written too.
 template <int ES>
-__device__ void decide(const VerifyParams& P, int b, float T, bool greedy) {
+__device__ void decide(const VerifyParams& P, int b, bool write, Decision& D) {
   __shared__ float sh_m[2 * SPEC_MAX_K + 1];
   __shared__ double sh_s[2 * SPEC_MAX_K + 1];
   __shared__ int sh_g[SPEC_MAX_K + 1];
   __shared__ int sh_bad;
   const int K = P.K;
   const int tid = threadIdx.x;
+  const float T = P.temperature[b];
+  const bool greedy = (T == 0.0f);
   if (tid == 0) sh_bad = temperature_valid(T) ? 0 : 1;
   __syncthreads();
   int x = 0;
@@ -235,41 +249,55 @@ __device__ void decide(const VerifyParams& P, int b, float T, bool greedy) {
         dq = (float)q;
       }
     }
-    if (P.debug && tid < K) {
-      P.debug[((int64_t)b * K + tid) * 2 + 0] = dp;
-      P.debug[((int64_t)b * K + tid) * 2 + 1] = dq;
-    }
     const uint64_t mask = __ballot(acc);
     const int a = bad ? -1 : (int)__builtin_ctzll(~mask);  // lanes >= K never accept, so a <= K
-    int32_t* out = P.out_tokens + (int64_t)b * (K + 1);
-    for (int j = tid; j <= K; j += 64) {
-      int tok;
-      if (bad || j > a) tok = -1;
-      else if (j < a) tok = P.tokens[(int64_t)b * K + j];
-      else tok = greedy ? sh_g[a] : -1;  // sampled: written by the sampling pass
-      if (!(j == a && !greedy && !bad)) out[j] = tok;
+    if (write) {
+      if (P.debug && tid < K) {
+        P.debug[((int64_t)b * K + tid) * 2 + 0] = dp;
+        P.debug[((int64_t)b * K + tid) * 2 + 1] = dq;
+      }
+      int32_t* out = P.out_tokens + (int64_t)b * (K + 1);
+      for (int j = tid; j <= K; j += 64) {  // K <= 63: one pass
+        int tok;
+        if (bad || j > a) tok = -1;
+        else if (j < a) tok = P.tokens[(int64_t)b * K + j];
+        else tok = greedy ? sh_g[a] : -1;  // sampled: written by the sampling kernel
+        if (!(j == a && !greedy && !bad)) out[j] = tok;
+      }
+      if (tid == 0) P.accepted[b] = a;
     }
     if (tid == 0) {
-      P.accepted[b] = a;
-      ReqDesc d;
-      d.mode = (bad || greedy) ? kModeNone : (a < K ? kModeResidual : kModeBonus);
-      d.a = a;
-      d.s_hi = s_hi;
-      d.s_lo = s_lo;
-      d.mp = d.sp = d.mq = d.sq = d.u = d.pad = 0.0;
-      if (d.mode != kModeNone) {
-        d.mp = (double)sh_m[a];
-        d.sp = sh_s[a];
+      D.a = a;
+      D.mode = (bad || greedy) ? kModeNone : (a < K ? kModeResidual : kModeBonus);
+      D.s_hi = s_hi;
+      D.s_lo = s_lo;
+      D.mp = D.sp = D.mq = D.sq = D.u = 0.0;
+      if (D.mode != kModeNone) {
+        D.mp = (double)sh_m[a];
+        D.sp = sh_s[a];
         if (a < K) {
-          d.mq = (double)sh_m[K + 1 + a];
-          d.sq = sh_s[K + 1 + a];
+          D.mq = (double)sh_m[K + 1 + a];
+          D.sq = sh_s[K + 1 + a];
         }
-        d.u = unit_uniform(philox4x32_10(req, (uint32_t)a, P.step, 0u, k0, k1).w[1]);
+        D.u = unit_uniform(philox4x32_10(req, (uint32_t)a, P.step, 0u, k0, k1).w[1]);
       }
-      P.desc[b] = d;
-      P.cnt1[b] = 0u;  // every arrival of this call has been counted
+      if (write) {
+        ReqDesc d;
+        d.mode = D.mode;
+        d.a = D.a;
+        d.s_hi = D.s_hi;
+        d.s_lo = D.s_lo;
+        d.mp = D.mp;
+        d.sp = D.sp;
+        d.mq = D.mq;
+        d.sq = D.sq;
+        d.u = D.u;
+        d.pad = 0.0;
+        P.desc[b] = d;
+      }
     }
   }
+  __syncthreads();
 }
 
 template <int ES, bool VEC>
@@ -297,18 +325,7 @@ __global__ __launch_bounds__(kWG) void verify_rowstats_kernel(VerifyParams P) {
     part.idx = 0;
     part.s = v.s;
   }
-  __shared__ int s_last;
-  if (threadIdx.x == 0) {
-    P.rowp[((int64_t)b * P.R + r) * P.C + c] = part;
-    __threadfence();
-    const uint32_t need = (uint32_t)((greedy ? P.K + 1 : P.R) * P.C);
-    s_last = (atomicAdd(&P.cnt1[b], 1u) + 1u == need);
-    __threadfence();
-  }
-  __syncthreads();
-  if (!s_last) return;
-  __threadfence();
-  decide<ES>(P, b, T, greedy);
+  if (threadIdx.x == 0) P.rowp[((int64_t)b * P.R + r) * P.C + c] = part;
 }
 
 // ------------------------------------------------------- sampling pass
@@ -593,41 +610,43 @@ __device__ void sample(const VerifyParams& P, int b, const ReqDesc& d, const dou
     if (tid == 0) sh_pick = y;
   }
   __syncthreads();
-  if (tid == 0) {
-    P.out_tokens[(int64_t)b * (P.K + 1) + d.a] = sh_pick;
-    P.cnt2[b] = 0u;
-  }
+  if (tid == 0) P.out_tokens[(int64_t)b * (P.K + 1) + d.a] = sh_pick;
+}
+
+template <int ES, bool VEC>
+__global__ __launch_bounds__(kWG) void verify_decide_kernel(VerifyParams P) {
+  const int c = blockIdx.x % P.C;
+  const int b = blockIdx.x / P.C;
+  __shared__ Decision D;
+  decide<ES>(P, b, c == 0, D);
+  if (D.mode == kModeNone) return;
+  ReqDesc d;
+  d.mode = D.mode;
+  d.a = D.a;
+  d.s_hi = D.s_hi;
+  d.s_lo = D.s_lo;
+  d.mp = D.mp;
+  d.sp = D.sp;
+  d.mq = D.mq;
+  d.sq = D.sq;
+  d.u = D.u;
+  double* seg = P.seg + (int64_t)b * P.nseg * 2;
+  if (D.mode == kModeResidual) residual_chunk<ES, VEC, true>(P, b, c, d, seg);
+  else residual_chunk<ES, VEC, false>(P, b, c, d, seg);
 }
 
 template <int ES, bool VEC>
 __global__ __launch_bounds__(kWG) void verify_sample_kernel(VerifyParams P) {
-  const int c = blockIdx.x % P.C;
-  const int b = blockIdx.x / P.C;
+  const int b = blockIdx.x;
   const ReqDesc d = P.desc[b];
-  // greedy / invalid requests have nothing to sample; a descriptor that is not
-  // a sampling row of this shape (a workspace used without re-initialisation
-  // for another shape) is never followed
   if (d.mode == kModeResidual) {
     if (d.a < 0 || d.a >= P.K) return;
   } else if (d.mode == kModeBonus) {
     if (d.a != P.K) return;
   } else {
-    return;
+    return;  // greedy or invalid: nothing to sample
   }
-  double* seg = P.seg + (int64_t)b * P.nseg * 2;
-  if (d.mode == kModeResidual) residual_chunk<ES, VEC, true>(P, b, c, d, seg);
-  else residual_chunk<ES, VEC, false>(P, b, c, d, seg);
-  __shared__ int s_last;
-  __threadfence();
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    s_last = (atomicAdd(&P.cnt2[b], 1u) + 1u == (uint32_t)P.C);
-    __threadfence();
-  }
-  __syncthreads();
-  if (!s_last) return;
-  __threadfence();
-  sample<ES, VEC>(P, b, d, seg);
+  sample<ES, VEC>(P, b, d, P.seg + (int64_t)b * P.nseg * 2);
 }
 
 // --------------------------------------------------------------- launch
@@ -642,7 +661,10 @@ static hipError_t launch_typed(const VerifyParams& P, hipEvent_t phase_event, hi
     e = hipEventRecord(phase_event, stream);
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL((verify_sample_kernel<ES, VEC>), dim3((unsigned)g2), dim3(kWG), 0, stream, P);
+  hipLaunchKernelGGL((verify_decide_kernel<ES, VEC>), dim3((unsigned)g2), dim3(kWG), 0, stream, P);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((verify_sample_kernel<ES, VEC>), dim3((unsigned)P.B), dim3(kWG), 0, stream, P);
   return hipGetLastError();
 }
 
@@ -651,20 +673,6 @@ hipError_t launch_verify(const VerifyParams& P, int dtype, bool vec, hipEvent_t 
   if (dtype == SPEC_BF16)
     return vec ? launch_typed<2, true>(P, phase_event, stream) : launch_typed<2, false>(P, phase_event, stream);
   return vec ? launch_typed<4, true>(P, phase_event, stream) : launch_typed<4, false>(P, phase_event, stream);
-}
-
-__global__ void fill_zero_kernel(uint32_t* p, size_t n) {
-  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
-    p[i] = 0u;
-}
-
-hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t stream) {
-  const size_t n = bytes / 4;
-  if (n == 0) return hipSuccess;
-  size_t blocks = (n + kWG - 1) / kWG;
-  if (blocks > 4096) blocks = 4096;
-  hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)blocks), dim3(kWG), 0, stream, (uint32_t*)p, n);
-  return hipGetLastError();
 }
 
 }  // namespace specv

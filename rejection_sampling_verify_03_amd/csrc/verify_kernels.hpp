@@ -25,8 +25,6 @@ struct VerifyParams {
   RowPartial* rowp;
   ReqDesc* desc;
   double* seg;
-  uint32_t* cnt1;
-  uint32_t* cnt2;
 };
 
 struct ExpandParams {
@@ -52,7 +50,6 @@ struct ExpandParams {
 
 hipError_t launch_verify(const VerifyParams& P, int dtype, bool vec, hipEvent_t phase_event,
                          hipStream_t stream);
-hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t stream);
 hipError_t launch_expand(const ExpandParams& P, bool vec, hipStream_t stream);
 
 }  // namespace specv

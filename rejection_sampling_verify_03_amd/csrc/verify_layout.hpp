@@ -37,7 +37,7 @@ enum { kModeNone = 0, kModeResidual = 1, kModeBonus = 2 };
 
 struct Layout {
   int32_t R, C, chunk, nseg;
-  size_t off_rowp, off_desc, off_seg, off_cnt1, off_cnt2, total;
+  size_t off_rowp, off_desc, off_seg, total;
 };
 
 __host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -59,10 +59,6 @@ __host__ __device__ inline Layout make_layout(int32_t B, int32_t K, int32_t V) {
   off = align256(off + (size_t)B * sizeof(ReqDesc));
   L.off_seg = off;
   off = align256(off + (size_t)B * L.nseg * 2 * sizeof(double));
-  L.off_cnt1 = off;
-  off = align256(off + (size_t)B * sizeof(uint32_t));
-  L.off_cnt2 = off;
-  off = align256(off + (size_t)B * sizeof(uint32_t));
   L.total = off;
   return L;
 }

@@ -111,9 +111,6 @@ def test_verify_argument_errors(sv):
     a.B = 0
     assert launch(a) == sv.SPEC_OK
     assert sv.lib.spec_verify_launch(None, None) == sv.SPEC_EINVAL
-    assert sv.spec_verify_workspace_init(None, 0, None) == sv.SPEC_OK
-    assert sv.spec_verify_workspace_init(None, 64, None) == sv.SPEC_EINVAL
-    assert sv.spec_verify_workspace_init(0x10004, 64, None) == sv.SPEC_EALIGN
 
 
 def test_expand_argument_errors(sv):

@@ -226,16 +226,10 @@ def test_determinism_and_workspace_reuse(sv):
     small = workloads.verify_tiny(seed=3, device="cuda")
     ws = sv.make_workspace(16, 6, 40000)
     assert sv.spec_verify_workspace_bytes(4, 4, 1024) <= ws.numel()
-    stream = torch.cuda.current_stream().cuda_stream
-
-    def reinit():
-        assert sv.spec_verify_workspace_init(ws.data_ptr(), ws.numel(), stream) == sv.SPEC_OK
-
+    ws.fill_(0xA5)  # stale contents are never read
     r1 = run(sv, big.target, big.draft, big.draft_tokens, big.temperature, 1, 0, ws=ws)
     r1b = run(sv, big.target, big.draft, big.draft_tokens, big.temperature, 1, 0, ws=ws)
-    reinit()  # a workspace serves one shape
     r2 = run(sv, small.target, small.draft, small.draft_tokens, small.temperature, 1, 0, ws=ws)
-    reinit()
     r3 = run(sv, big.target, big.draft, big.draft_tokens, big.temperature, 1, 0, ws=ws)
     r4 = run(sv, small.target, small.draft, small.draft_tokens, small.temperature, 1, 0)
     for a, b in zip(r1, r1b):
