@@ -11,6 +11,8 @@ using namespace specv;
 
 namespace {
 
+constexpr int64_t kExpandRowsPerWG = 4;
+
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 int verify_check(const spec_verify_args* a) {
@@ -25,7 +27,7 @@ int verify_check(const spec_verify_args* a) {
   if (a->t_req_stride != 0 && a->t_req_stride < (int64_t)(a->K + 1) * a->t_row_stride) return SPEC_EINVAL;
   if (a->d_req_stride != 0 && a->d_req_stride < (int64_t)a->K * a->d_row_stride) return SPEC_EINVAL;
   const Layout L = make_layout(a->B, a->K, a->V);
-  if ((int64_t)a->B * L.R * L.C > INT32_MAX) return SPEC_EINVAL;
+  if ((int64_t)a->B * L.R * L.C1 > INT32_MAX || (int64_t)a->B * L.C2 > INT32_MAX) return SPEC_EINVAL;
   if (!aligned16(a->workspace)) return SPEC_EALIGN;
   if (a->workspace_bytes < L.total) return SPEC_EWORKSPACE;
   return SPEC_OK;
@@ -67,8 +69,10 @@ int spec_verify_launch(const spec_verify_args* a, hipStream_t stream) {
   P.K = a->K;
   P.V = a->V;
   P.R = L.R;
-  P.C = L.C;
-  P.chunk = L.chunk;
+  P.C1 = L.C1;
+  P.chunk1 = L.chunk1;
+  P.C2 = L.C2;
+  P.chunk2 = L.chunk2;
   P.nseg = L.nseg;
   P.target = static_cast<const char*>(a->target_logits);
   P.t_req = a->t_req_stride;
@@ -105,11 +109,11 @@ int spec_expand_launch(const spec_expand_args* a, hipStream_t stream) {
   P.H = a->H;
   P.N_in = a->N_in;
   P.mask_id = a->mask_token_id;
-  // ~4 output rows per workgroup on average; a request's window is shared by G
-  // workgroups row-interleaved
+  // about kExpandRowsPerWG output rows per workgroup on average; a request's
+  // window is shared by G workgroups row-interleaved
   const int64_t n_out = (int64_t)a->N_in + (int64_t)a->B * (a->K - 1);
   const int64_t avg_window = (n_out + a->B - 1) / a->B;
-  int64_t G = (avg_window + 3) / 4;
+  int64_t G = (avg_window + kExpandRowsPerWG - 1) / kExpandRowsPerWG;
   if (G < 1) G = 1;
   if (G > 64) G = 64;
   if ((int64_t)a->B * G > INT32_MAX) G = 1;

@@ -42,13 +42,17 @@ __device__ __forceinline__ Philox4 philox4x32_10(uint32_t c0, uint32_t c1, uint3
 __device__ __forceinline__ double unit_uniform(uint32_t w) { return (double)(w >> 8) * 0x1p-24; }
 
 // ---------------------------------------------------------- logit groups --
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
 // A group is 8 consecutive logits widened to fp32: one 16-byte load for bf16,
 // two for fp32 (VEC), or 8 scalar loads when the row is not 16-byte aligned.
 template <int ES, bool VEC>
 __device__ __forceinline__ void load_group(const char* __restrict__ row, int64_t e0, float x[8]) {
   if constexpr (ES == 2) {
     if constexpr (VEC) {
-      const uint4 v = *reinterpret_cast<const uint4*>(row + e0 * 2);
+      // streamed once: a non-temporal load keeps it from displacing reusable lines
+      const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(row + e0 * 2));
       const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -62,8 +66,8 @@ __device__ __forceinline__ void load_group(const char* __restrict__ row, int64_t
     }
   } else {
     if constexpr (VEC) {
-      const float4 a = *reinterpret_cast<const float4*>(row + e0 * 4);
-      const float4 b = *reinterpret_cast<const float4*>(row + e0 * 4 + 16);
+      const f32x4 a = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(row + e0 * 4));
+      const f32x4 b = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(row + e0 * 4 + 16));
       x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
       x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
     } else {
@@ -72,6 +76,72 @@ __device__ __forceinline__ void load_group(const char* __restrict__ row, int64_t
       for (int i = 0; i < 8; ++i) x[i] = r[i];
     }
   }
+}
+
+// The same 8 logits kept as loaded (two bf16 per dword, or fp32), so that many
+// groups can be in flight in few registers; widened by unpack_group.
+template <int ES, bool VEC>
+struct RawGroup;
+template <>
+struct RawGroup<2, true> {
+  u32x4 v;
+};
+template <>
+struct RawGroup<4, true> {
+  f32x4 a, b;
+};
+template <int ES>
+struct RawGroup<ES, false> {
+  float x[8];
+};
+
+template <int ES, bool VEC>
+__device__ __forceinline__ RawGroup<ES, VEC> load_raw(const char* __restrict__ row, int64_t e0) {
+  RawGroup<ES, VEC> r;
+  if constexpr (!VEC) {
+    load_group<ES, false>(row, e0, r.x);
+  } else if constexpr (ES == 2) {
+    r.v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(row + e0 * 2));
+  } else {
+    r.a = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(row + e0 * 4));
+    r.b = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(row + e0 * 4 + 16));
+  }
+  return r;
+}
+
+template <int ES, bool VEC>
+__device__ __forceinline__ void unpack_group(const RawGroup<ES, VEC>& r, float x[8]) {
+  if constexpr (!VEC) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) x[i] = r.x[i];
+  } else if constexpr (ES == 2) {
+    const uint32_t w[4] = {r.v.x, r.v.y, r.v.z, r.v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x[2 * i] = __uint_as_float(w[i] << 16);
+      x[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+  } else {
+    x[0] = r.a.x; x[1] = r.a.y; x[2] = r.a.z; x[3] = r.a.w;
+    x[4] = r.b.x; x[5] = r.b.y; x[6] = r.b.z; x[7] = r.b.w;
+  }
+}
+
+// A group whose 8 logits are all -inf (padding past a row end).
+template <int ES, bool VEC>
+__device__ __forceinline__ RawGroup<ES, VEC> neg_inf_group() {
+  RawGroup<ES, VEC> r;
+  if constexpr (!VEC) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) r.x[i] = -INFINITY;
+  } else if constexpr (ES == 2) {
+    const uint32_t ni = 0xff80ff80u;  // two bf16 -inf
+    r.v = u32x4{ni, ni, ni, ni};
+  } else {
+    r.a = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+    r.b = r.a;
+  }
+  return r;
 }
 
 template <int ES>

@@ -21,7 +21,7 @@
 
 namespace specv {
 
-constexpr int kCopyUnroll = 4;
+constexpr int kCopyBatch = 8;  // 16-byte cells per lane loaded before any is stored
 
 template <bool VEC>
 __global__ __launch_bounds__(kWG) void expand_kernel(ExpandParams P) {
@@ -47,9 +47,47 @@ __global__ __launch_bounds__(kWG) void expand_kernel(ExpandParams P) {
     return;
   }
   const int Wb = n + K - 1;  // slots of this request's window
-  const int bonus = P.vtok ? P.vtok[(int64_t)b * (K + 1) + a] : P.bonus[b];
+
+  // hidden rows g, g+G, ... of the window: slot o+r takes input row s+r
+  // (r < n) or the MASK placeholder; loads of a batch are all issued before
+  // its stores, and the output is written once (non-temporal stores)
+  if (P.out_h != nullptr && g < Wb) {
+    const int nr = (Wb - g + P.G - 1) / P.G;
+    if constexpr (VEC) {
+      const int ncols = P.H >> 3;
+      const int cells = nr * ncols;
+      for (int c0 = tid; c0 < cells; c0 += kWG * kCopyBatch) {
+        u32x4 v[kCopyBatch];
+        int64_t dst[kCopyBatch];
+#pragma unroll
+        for (int u = 0; u < kCopyBatch; ++u) {
+          const int c = c0 + u * kWG;
+          dst[u] = -1;
+          if (c < cells) {
+            const int rl = c / ncols, col = c - rl * ncols;
+            const int r = g + P.G * rl;
+            const uint16_t* src = r < n ? P.th + (int64_t)(s + r) * P.th_stride : P.mh;
+            v[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src) + col);
+            dst[u] = (int64_t)(o + r) * ncols + col;
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < kCopyBatch; ++u)
+          if (dst[u] >= 0) __builtin_nontemporal_store(v[u], reinterpret_cast<u32x4*>(P.out_h) + dst[u]);
+      }
+    } else {
+      const int cells = nr * P.H;
+      for (int c = tid; c < cells; c += kWG) {
+        const int rl = c / P.H, col = c - rl * P.H;
+        const int r = g + P.G * rl;
+        const uint16_t* src = r < n ? P.th + (int64_t)(s + r) * P.th_stride : P.mh;
+        P.out_h[(int64_t)(o + r) * P.H + col] = src[col];
+      }
+    }
+  }
 
   // metadata: one thread per slot r of this workgroup's rows g, g+G, ...
+  const int bonus = P.vtok ? P.vtok[(int64_t)b * (K + 1) + a] : P.bonus[b];
   for (int r = g + P.G * tid; r < Wb; r += P.G * kWG) {
     const int slot = o + r;
     if (r < n) {
@@ -66,40 +104,6 @@ __global__ __launch_bounds__(kWG) void expand_kernel(ExpandParams P) {
       P.rej[slot] = 0;
       P.msk[slot] = 1;
       P.nti[(int64_t)b * K + m] = slot;
-    }
-  }
-
-  if (P.out_h == nullptr || g >= Wb) return;
-  const int nr = (Wb - g + P.G - 1) / P.G;  // rows of this workgroup
-  if constexpr (VEC) {
-    const int ncols = P.H >> 3;  // 16-byte cells per row
-    const int cells = nr * ncols;
-    for (int c0 = tid; c0 < cells; c0 += kWG * kCopyUnroll) {
-      uint4 v[kCopyUnroll];
-      uint4* dst[kCopyUnroll];
-#pragma unroll
-      for (int u = 0; u < kCopyUnroll; ++u) {
-        const int c = c0 + u * kWG;
-        dst[u] = nullptr;
-        if (c < cells) {
-          const int rl = c / ncols, col = c - rl * ncols;
-          const int r = g + P.G * rl;
-          const uint16_t* src = r < n ? P.th + (int64_t)(s + r) * P.th_stride : P.mh;
-          v[u] = reinterpret_cast<const uint4*>(src)[col];
-          dst[u] = reinterpret_cast<uint4*>(P.out_h + (int64_t)(o + r) * P.H) + col;
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < kCopyUnroll; ++u)
-        if (dst[u]) *dst[u] = v[u];
-    }
-  } else {
-    const int cells = nr * P.H;
-    for (int c = tid; c < cells; c += kWG) {
-      const int rl = c / P.H, col = c - rl * P.H;
-      const int r = g + P.G * rl;
-      const uint16_t* src = r < n ? P.th + (int64_t)(s + r) * P.th_stride : P.mh;
-      P.out_h[(int64_t)(o + r) * P.H + col] = src[col];
     }
   }
 }

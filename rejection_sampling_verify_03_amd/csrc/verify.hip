@@ -8,29 +8,31 @@
 // target argmax, emit the target argmax where the request stops).
 //
 // Three kernels in stream order, no host round trip, and no communication
-// between workgroups of one kernel (kernel boundaries make each kernel's
-// writes visible to the next, so no atomics and no cache-maintenance fences):
+// between workgroups of one kernel (each kernel boundary makes the previous
+// kernel's writes visible, so no atomics and no cache-maintenance fences):
 //
-//  verify_rowstats  one workgroup per (request, row, chunk of ~32K logits)
-//      streams every row the parallel formulation needs exactly once (target
-//      rows 0..K and, for sampled requests, draft rows 0..K-1) with 16-byte
-//      loads, and reduces the chunk to S * 2^M = sum_v 2^(x_v * s - M)
-//      (s = log2(e) / T, M an integer-valued reference raised by exact
-//      power-of-two rescaling) or, for greedy requests, to (max, lowest
-//      argmax).
+//  verify_rowstats  one 256-thread workgroup per (request, row, chunk of ~32K
+//      logits) streams every row the parallel formulation needs exactly once
+//      (target rows 0..K and, for sampled requests, draft rows 0..K-1) with
+//      non-temporal 16-byte loads, and reduces the chunk to
+//      S * 2^M = sum_v 2^(x_v * s - M) (s = log2(e) / T, M an integer-valued
+//      reference raised by exact power-of-two rescaling) or, for greedy
+//      requests, to (max, lowest argmax).
 //
-//  verify_decide    one workgroup per (request, chunk): merges the request's
-//      chunk partials in order, evaluates the K accept tests in parallel (one
-//      lane per position, Philox uniforms, double-precision p(x), q(x)) and
-//      finds a_b as the count of trailing ones of a wavefront ballot -- every
-//      workgroup of the request derives the same decision; the chunk-0
-//      workgroup writes the outputs -- then re-reads its chunk of the sampling
-//      row(s) (p_a and q_a, or p_K for the bonus) and writes sums of the
-//      residual weights max(0, p - q) and of p over 512-element segments.
+//  verify_decide    one workgroup per (request, chunk of ~32K logits): merges
+//      the request's row partials in order and evaluates the K accept tests
+//      in parallel (one lane per position, Philox uniforms, double-precision
+//      p(x), q(x)); a_b is the count of trailing ones of a wavefront ballot.
+//      Every workgroup of a request derives the same decision; the chunk-0
+//      one writes the outputs and a decision record.  Each then streams its
+//      chunk of the sampling row(s) (p_a and q_a, or p_K for the bonus) into
+//      sums of the residual weights max(0, p - q) and of p over 4096-logit
+//      segments, one segment per wave.
 //
-//  verify_sample    one workgroup per sampled request scans the segment sums
-//      for the inverse-CDF crossing of u' * R, recomputes the weights of that
-//      one segment and finds the token with a wavefront scan.
+//  verify_draw      one 512-thread workgroup per sampled request scans the
+//      segment sums for the inverse-CDF crossing of u' * R, recomputes the
+//      weights of that one segment (one 512-logit block per wave) and finds
+//      the token with a wavefront scan.
 #include <float.h>
 #include <limits.h>
 
@@ -81,7 +83,7 @@ __device__ __forceinline__ float sum8_exp(const float x[8], float s_hi, float s_
 template <int ES, bool VEC>
 __device__ __forceinline__ MS chunk_stats(const char* __restrict__ row, int e0, int e1, float s_hi,
                                           float s_lo) {
-  constexpr int U = (ES == 2) ? 4 : 2;  // 64 bytes in flight per lane per iteration
+  constexpr int U = (ES == 2) ? 8 : 4;  // 128 bytes in flight per lane per iteration
   const int nfull = (e1 - e0) >> 3;
   float M = -INFINITY;
   double S = 0.0;
@@ -124,7 +126,7 @@ __device__ __forceinline__ MS chunk_stats(const char* __restrict__ row, int e0, 
 
 template <int ES, bool VEC>
 __device__ __forceinline__ VI chunk_argmax(const char* __restrict__ row, int e0, int e1) {
-  constexpr int U = (ES == 2) ? 4 : 2;
+  constexpr int U = (ES == 2) ? 8 : 4;
   const int nfull = (e1 - e0) >> 3;
   VI best{-INFINITY, INT_MAX};
   int g = threadIdx.x;
@@ -182,17 +184,11 @@ __device__ __forceinline__ VI block_argmax(VI v) {
 }
 
 // ------------------------------------------------------------- decision
-struct Decision {
-  int a;     // accepted drafts, -1 for invalid request data
-  int mode;  // kModeNone / kModeResidual / kModeBonus
-  float s_hi, s_lo;
-  double mp, sp, mq, sq, u;
-};
-
 // The decision of request b, computed by the whole workgroup into `D`
-// (shared).  With `write`, the outputs of the request are written too.
+// (shared).  With `write`, the request's outputs (all but the token the draw
+// samples) and its decision record are written too.
 template <int ES>
-__device__ void decide(const VerifyParams& P, int b, bool write, Decision& D) {
+__device__ void decide(const VerifyParams& P, int b, bool write, ReqDesc& D) {
   __shared__ float sh_m[2 * SPEC_MAX_K + 1];
   __shared__ double sh_s[2 * SPEC_MAX_K + 1];
   __shared__ int sh_g[SPEC_MAX_K + 1];
@@ -204,20 +200,26 @@ __device__ void decide(const VerifyParams& P, int b, bool write, Decision& D) {
   if (tid == 0) sh_bad = temperature_valid(T) ? 0 : 1;
   __syncthreads();
   int x = 0;
+  float zt_f = 0.f, zq_f = 0.f;
   if (tid < K) {
     x = P.tokens[(int64_t)b * K + tid];
     if (x < 0 || x >= P.V) atomicOr(&sh_bad, 1);
+    if (!greedy) {  // gathered logits, loaded while the partials below are in flight
+      const int xc = min(max(x, 0), P.V - 1);  // a bad token makes the request invalid anyway
+      zt_f = load_one<ES>(row_ptr<ES>(P, b, tid), xc);
+      zq_f = load_one<ES>(row_ptr<ES>(P, b, K + 1 + tid), xc);
+    }
   }
   const int nrows = greedy ? K + 1 : P.R;
   if (tid < nrows) {
-    const RowPartial* rp = P.rowp + ((int64_t)b * P.R + tid) * P.C;
+    const RowPartial* rp = P.rowp + ((int64_t)b * P.R + tid) * P.C1;
     if (greedy) {
       VI best{rp[0].m, rp[0].idx};
-      for (int c = 1; c < P.C; ++c) best = vi_pick(best, VI{rp[c].m, rp[c].idx});
+      for (int c = 1; c < P.C1; ++c) best = vi_pick(best, VI{rp[c].m, rp[c].idx});
       sh_g[tid] = best.i;
     } else {
       MS acc{rp[0].m, rp[0].s};
-      for (int c = 1; c < P.C; ++c) acc = ms_merge(acc, MS{rp[c].m, rp[c].s});
+      for (int c = 1; c < P.C1; ++c) acc = ms_merge(acc, MS{rp[c].m, rp[c].s});
       sh_m[tid] = acc.m;
       sh_s[tid] = acc.s;
       if (!(acc.s > 0.0 && acc.s <= DBL_MAX && fabsf(acc.m) <= FLT_MAX)) atomicOr(&sh_bad, 1);
@@ -238,8 +240,8 @@ __device__ void decide(const VerifyParams& P, int b, bool write, Decision& D) {
         acc = (x == sh_g[tid]);
       } else {
         const double s_eff = (double)s_hi + (double)s_lo;
-        const double zt = (double)load_one<ES>(row_ptr<ES>(P, b, tid), x);
-        const double zq = (double)load_one<ES>(row_ptr<ES>(P, b, K + 1 + tid), x);
+        const double zt = (double)zt_f;
+        const double zq = (double)zq_f;
         const double p = exp2(zt * s_eff - (double)sh_m[tid]) / sh_s[tid];
         const double q = exp2(zq * s_eff - (double)sh_m[K + 1 + tid]) / sh_s[K + 1 + tid];
         const double thr = q > 0.0 ? fmin(1.0, p / q) : (p > 0.0 ? 1.0 : 0.0);
@@ -261,40 +263,29 @@ __device__ void decide(const VerifyParams& P, int b, bool write, Decision& D) {
         int tok;
         if (bad || j > a) tok = -1;
         else if (j < a) tok = P.tokens[(int64_t)b * K + j];
-        else tok = greedy ? sh_g[a] : -1;  // sampled: written by the sampling kernel
+        else tok = greedy ? sh_g[a] : -1;  // sampled: written by the draw
         if (!(j == a && !greedy && !bad)) out[j] = tok;
       }
       if (tid == 0) P.accepted[b] = a;
     }
     if (tid == 0) {
-      D.a = a;
-      D.mode = (bad || greedy) ? kModeNone : (a < K ? kModeResidual : kModeBonus);
-      D.s_hi = s_hi;
-      D.s_lo = s_lo;
-      D.mp = D.sp = D.mq = D.sq = D.u = 0.0;
-      if (D.mode != kModeNone) {
-        D.mp = (double)sh_m[a];
-        D.sp = sh_s[a];
+      ReqDesc d;
+      d.a = a;
+      d.mode = (bad || greedy) ? kModeNone : (a < K ? kModeResidual : kModeBonus);
+      d.s_hi = s_hi;
+      d.s_lo = s_lo;
+      d.mp = d.sp = d.mq = d.sq = d.u = d.pad = 0.0;
+      if (d.mode != kModeNone) {
+        d.mp = (double)sh_m[a];
+        d.sp = sh_s[a];
         if (a < K) {
-          D.mq = (double)sh_m[K + 1 + a];
-          D.sq = sh_s[K + 1 + a];
+          d.mq = (double)sh_m[K + 1 + a];
+          d.sq = sh_s[K + 1 + a];
         }
-        D.u = unit_uniform(philox4x32_10(req, (uint32_t)a, P.step, 0u, k0, k1).w[1]);
+        d.u = unit_uniform(philox4x32_10(req, (uint32_t)a, P.step, 0u, k0, k1).w[1]);
       }
-      if (write) {
-        ReqDesc d;
-        d.mode = D.mode;
-        d.a = D.a;
-        d.s_hi = D.s_hi;
-        d.s_lo = D.s_lo;
-        d.mp = D.mp;
-        d.sp = D.sp;
-        d.mq = D.mq;
-        d.sq = D.sq;
-        d.u = D.u;
-        d.pad = 0.0;
-        P.desc[b] = d;
-      }
+      D = d;
+      if (write) P.desc[b] = d;
     }
   }
   __syncthreads();
@@ -302,15 +293,15 @@ __device__ void decide(const VerifyParams& P, int b, bool write, Decision& D) {
 
 template <int ES, bool VEC>
 __global__ __launch_bounds__(kWG) void verify_rowstats_kernel(VerifyParams P) {
-  const int c = blockIdx.x % P.C;
-  const int r = (blockIdx.x / P.C) % P.R;
-  const int b = blockIdx.x / (P.C * P.R);
+  const int c = blockIdx.x % P.C1;
+  const int r = (blockIdx.x / P.C1) % P.R;
+  const int b = blockIdx.x / (P.C1 * P.R);
   const float T = P.temperature[b];
   const bool greedy = (T == 0.0f);
   if (greedy && r > P.K) return;  // greedy requests read no draft rows
   const char* row = row_ptr<ES>(P, b, r);
-  const int e0 = c * P.chunk;
-  const int e1 = min(P.V, e0 + P.chunk);
+  const int e0 = c * P.chunk1;
+  const int e1 = min(P.V, e0 + P.chunk1);
   RowPartial part;
   if (greedy) {
     const VI v = block_argmax(chunk_argmax<ES, VEC>(row, e0, e1));
@@ -325,26 +316,20 @@ __global__ __launch_bounds__(kWG) void verify_rowstats_kernel(VerifyParams P) {
     part.idx = 0;
     part.s = v.s;
   }
-  if (threadIdx.x == 0) P.rowp[((int64_t)b * P.R + r) * P.C + c] = part;
+  if (threadIdx.x == 0) P.rowp[((int64_t)b * P.R + r) * P.C1 + c] = part;
 }
 
-// ------------------------------------------------------- sampling pass
-// Sampling weight of one logit pair: p(v) (bonus) or max(0, p(v) - q(v)).
+// ------------------------------------------------------------ sampling weights
+// The draw samples from r = max(0, p - q) (or from p for the bonus).  With
+// e_p = 2^(x_p s - M_p), e_q = 2^(x_q s - M_q) and the normalisers S_p, S_q,
+// r = max(0, e_p - e_q * c) / S_p with c = S_p / S_q.  The weights are kept in
+// units of 1 / S_p (a common factor that cancels in the inverse CDF) and
+// computed in fp32 with c split as c_hi + c_lo: each fma rounds once,
+// relative to the result, so the residual keeps ~1e-7 relative accuracy even
+// where p and q nearly cancel.
 struct WeightCtx {
-  float s_hi, s_lo, negMp, negMq;
-  double ip, iq;
+  float s_hi, s_lo, negMp, negMq, c_hi, c_lo;
 };
-
-__device__ __forceinline__ void pair_weights(const WeightCtx& w, float xp, float xq, bool res, double& r,
-                                             double& pv) {
-  pv = (double)scaled_exp2(xp, w.s_hi, w.s_lo, w.negMp) * w.ip;
-  if (res) {
-    const double qv = (double)scaled_exp2(xq, w.s_hi, w.s_lo, w.negMq) * w.iq;
-    r = fmax(pv - qv, 0.0);
-  } else {
-    r = pv;
-  }
-}
 
 __device__ __forceinline__ WeightCtx make_ctx(const ReqDesc& d) {
   WeightCtx w;
@@ -352,9 +337,19 @@ __device__ __forceinline__ WeightCtx make_ctx(const ReqDesc& d) {
   w.s_lo = d.s_lo;
   w.negMp = -(float)d.mp;
   w.negMq = -(float)d.mq;
-  w.ip = 1.0 / d.sp;
-  w.iq = d.mode == kModeResidual ? 1.0 / d.sq : 0.0;
+  const double c = d.mode == kModeResidual ? d.sp / d.sq : 0.0;
+  w.c_hi = (float)c;
+  w.c_lo = (float)(c - (double)w.c_hi);
   return w;
+}
+
+// Weight of one logit pair: residual (res) or p, in units of 1 / S_p.
+__device__ __forceinline__ float pair_weight(const WeightCtx& w, float xp, float xq, bool res, float& ep) {
+  ep = scaled_exp2(xp, w.s_hi, w.s_lo, w.negMp);
+  if (!res) return ep;
+  const float eq = scaled_exp2(xq, w.s_hi, w.s_lo, w.negMq);
+  const float t = __builtin_fmaf(-eq, w.c_lo, __builtin_fmaf(-eq, w.c_hi, ep));
+  return fmaxf(t, 0.0f);
 }
 
 // 8 consecutive logits from e0 on, -inf past the row end e1.
@@ -368,165 +363,184 @@ __device__ __forceinline__ void load_group_bounded(const char* row, int e0, int 
   }
 }
 
-// Sums of the sampling weights over one tile (256 groups = 4 segments of 512
-// logits, one per wave) -> the segment sums of the residual and of p.
-template <int U>
-__device__ __forceinline__ void tile_segment_sums(const WeightCtx& w, bool res, const float (&xp)[U][8],
-                                                  const float (&xq)[U][8], int seg0, int e1,
-                                                  double* __restrict__ seg) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+// A group of 8 logits from e0 on, -inf past the row end V (scalar loads for a
+// group that straddles the end).
+template <int ES, bool VEC>
+__device__ __forceinline__ RawGroup<ES, VEC> load_raw_bounded(const char* row, int e0, int V) {
+  if (e0 + 8 <= V) return load_raw<ES, VEC>(row, e0);
+  float x[8];
 #pragma unroll
-  for (int u = 0; u < U; ++u) {
-    double rs = 0.0, ps = 0.0;
+  for (int i = 0; i < 8; ++i) x[i] = (e0 + i < V) ? load_one<ES>(row, e0 + i) : -INFINITY;
+  RawGroup<ES, VEC> r;
+  if constexpr (!VEC) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      double r, pv;
-      pair_weights(w, xp[u][i], xq[u][i], res, r, pv);
-      rs += r;
-      ps += pv;
-    }
-    rs = wave_sum_d(rs);
-    ps = wave_sum_d(ps);
-    const int s_idx = seg0 + u * kWaves + wave;
-    if (lane == 0 && s_idx * kSeg < e1) {
-      seg[2 * s_idx + 0] = rs;
-      seg[2 * s_idx + 1] = ps;
-    }
+    for (int i = 0; i < 8; ++i) r.x[i] = x[i];
+  } else if constexpr (ES == 2) {
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      w[i] = (__float_as_uint(x[2 * i]) >> 16) | (__float_as_uint(x[2 * i + 1]) & 0xffff0000u);
+    r.v = u32x4{w[0], w[1], w[2], w[3]};
+  } else {
+    r.a = f32x4{x[0], x[1], x[2], x[3]};
+    r.b = f32x4{x[4], x[5], x[6], x[7]};
   }
+  return r;
 }
 
+// One wave sums the weights of segment [s0, s0 + kSeg) (clipped to V): lane l
+// takes groups l, l+64, ... so that every load of the wave is one contiguous
+// kilobyte, and a whole part of the segment (both rows) is loaded before any
+// of it is used.  Returns (residual sum, p sum) in every lane.
 template <int ES, bool VEC, bool RES>
-__device__ __forceinline__ void residual_chunk(const VerifyParams& P, int b, int c, const ReqDesc& d,
-                                               double* __restrict__ seg) {
-  constexpr int U = (ES == 2) ? 2 : 1;
-  const char* prow = row_ptr<ES>(P, b, d.a);
-  const char* qrow = RES ? row_ptr<ES>(P, b, P.K + 1 + d.a) : prow;
-  const WeightCtx w = make_ctx(d);
-  const int e0 = c * P.chunk;
-  const int e1 = min(P.V, e0 + P.chunk);
-  const int nfull = (e1 - e0) >> 3;
-  const int ngroups = (e1 - e0 + 7) >> 3;
-  const int tid = threadIdx.x;
-  int tile = 0;
-  for (; (tile + U) * kWG <= nfull; tile += U) {  // tiles of full groups only
-    float xp[U][8], xq[U][8];
+__device__ __forceinline__ void segment_sums(const char* prow, const char* qrow, const WeightCtx& w, int s0,
+                                             int V, double& rsum, double& psum) {
+  constexpr int H = (ES == 2 && VEC) ? kSegGroups : kSegGroups / 2;  // groups per part
+  constexpr int NH = kSegGroups / H;
+  const int lane = threadIdx.x & 63;
+  const bool full = s0 + kSeg <= V;
+  rsum = 0.0;
+  psum = 0.0;
+#pragma unroll 1
+  for (int h = 0; h < NH; ++h) {
+    RawGroup<ES, VEC> rp[H], rq[H];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int gg = (tile + u) * kWG + tid;
-      load_group<ES, VEC>(prow, (int64_t)e0 + 8 * gg, xp[u]);
-      if (RES) load_group<ES, VEC>(qrow, (int64_t)e0 + 8 * gg, xq[u]);
-      else {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) xq[u][i] = 0.f;
+    for (int g = 0; g < H; ++g) {
+      const int e = s0 + ((h * H + g) * 64 + lane) * 8;
+      if (full) {
+        rp[g] = load_raw<ES, VEC>(prow, e);
+        if (RES) rq[g] = load_raw<ES, VEC>(qrow, e);
+      } else if (e < V) {
+        rp[g] = load_raw_bounded<ES, VEC>(prow, e, V);
+        if (RES) rq[g] = load_raw_bounded<ES, VEC>(qrow, e, V);
+      } else {
+        rp[g] = neg_inf_group<ES, VEC>();
+        if (RES) rq[g] = neg_inf_group<ES, VEC>();
       }
     }
-    tile_segment_sums<U>(w, RES, xp, xq, e0 / kSeg + tile * kWaves, e1, seg);
+#pragma unroll
+    for (int g = 0; g < H; ++g) {
+      float xp[8], xq[8];
+      unpack_group<ES, VEC>(rp[g], xp);
+      if (RES) unpack_group<ES, VEC>(rq[g], xq);
+      float r8 = 0.f, p8 = 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        float ep;
+        r8 += pair_weight(w, xp[i], RES ? xq[i] : 0.f, RES, ep);
+        p8 += ep;
+      }
+      rsum += (double)r8;
+      psum += (double)p8;
+    }
   }
-  for (; tile * kWG < ngroups; ++tile) {  // the last, partly filled tiles
-    float xp[1][8], xq[1][8];
-    const int gg = tile * kWG + tid;
-    if (gg < ngroups) {
-      load_group_bounded<ES, VEC>(prow, e0 + 8 * gg, e1, xp[0]);
-      if (RES) load_group_bounded<ES, VEC>(qrow, e0 + 8 * gg, e1, xq[0]);
-    } else {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) xp[0][i] = -INFINITY;
+  rsum = wave_sum_d(rsum);
+  psum = wave_sum_d(psum);
+}
+
+template <int ES, bool VEC>
+__global__ __launch_bounds__(kWG) void verify_decide_kernel(VerifyParams P) {
+  const int c = blockIdx.x % P.C2;
+  const int b = blockIdx.x / P.C2;
+  __shared__ ReqDesc D;
+  decide<ES>(P, b, c == 0, D);
+  if (D.mode == kModeNone) return;
+  const bool res = D.mode == kModeResidual;
+  const char* prow = row_ptr<ES>(P, b, D.a);
+  const char* qrow = res ? row_ptr<ES>(P, b, P.K + 1 + D.a) : prow;
+  const WeightCtx w = make_ctx(D);
+  double* seg = P.seg + (int64_t)b * P.nseg * 2;
+  const int e0 = c * P.chunk2;
+  const int e1 = min(P.V, e0 + P.chunk2);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int s0 = e0 + wave * kSeg; s0 < e1; s0 += kWaves * kSeg) {
+    double rs, ps;
+    if (res) segment_sums<ES, VEC, true>(prow, qrow, w, s0, P.V, rs, ps);
+    else segment_sums<ES, VEC, false>(prow, qrow, w, s0, P.V, rs, ps);
+    if (lane == 0) {
+      seg[2 * (s0 / kSeg) + 0] = rs;
+      seg[2 * (s0 / kSeg) + 1] = ps;
     }
-    if (!RES || gg >= ngroups) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) xq[0][i] = RES ? -INFINITY : 0.f;
-    }
-    tile_segment_sums<1>(w, RES, xp, xq, e0 / kSeg + tile * kWaves, e1, seg);
   }
 }
 
-// Inclusive / exclusive scan of one double per thread over the workgroup, in
-// a fixed order; `total` is the workgroup sum.  All threads must call it.
-__device__ __forceinline__ void block_scan_d(double v, double& incl, double& excl, double& total) {
-  __shared__ double wt[kWaves];
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  double x = v;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const double y = __shfl_up(x, off, 64);
-    if (lane >= off) x += y;
-  }
-  double xe = __shfl_up(x, 1, 64);
-  if (lane == 0) xe = 0.0;
-  if (lane == 63) wt[w] = x;
-  __syncthreads();
-  double base = 0.0, tot = 0.0;
-#pragma unroll
-  for (int i = 0; i < kWaves; ++i) {
-    if (i < w) base += wt[i];
-    tot += wt[i];
-  }
-  incl = base + x;
-  excl = base + xe;
-  total = tot;
-  __syncthreads();
-}
+// --------------------------------------------------------------------- draw
+constexpr int kWGD = 512;  // draw workgroup: 8 waves, one 512-logit block each
+static_assert(kWGD / 64 * 512 == kSeg, "a draw wave per 512-logit block of a segment");
 
-// Lowest thread index whose predicate holds, or -1.  All threads must call it.
+template <int NT>
 __device__ __forceinline__ int block_first_true(bool pred) {
-  __shared__ int first[kWaves];
+  constexpr int W = NT / 64;
+  __shared__ int first[W];
   const uint64_t m = __ballot(pred);
   const int w = threadIdx.x >> 6;
   if ((threadIdx.x & 63) == 0) first[w] = m ? (int)__builtin_ctzll(m) + 64 * w : -1;
   __syncthreads();
   int r = -1;
 #pragma unroll
-  for (int i = kWaves - 1; i >= 0; --i)
+  for (int i = W - 1; i >= 0; --i)
     if (first[i] >= 0) r = first[i];
   __syncthreads();
   return r;
 }
 
+template <int NT>
 __device__ __forceinline__ int block_max_int(int v) {
-  __shared__ int mx[kWaves];
+  constexpr int W = NT / 64;
+  __shared__ int mx[W];
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) v = max(v, __shfl_xor(v, off, 64));
   if ((threadIdx.x & 63) == 0) mx[threadIdx.x >> 6] = v;
   __syncthreads();
   int r = mx[0];
 #pragma unroll
-  for (int i = 1; i < kWaves; ++i) r = max(r, mx[i]);
+  for (int i = 1; i < W; ++i) r = max(r, mx[i]);
   __syncthreads();
   return r;
 }
 
-// Within segment j (run by wave 0): the first element whose cumulative weight
-// (starting from `base`) exceeds `target`, or with `last_positive`, the last
-// element of positive weight.
+// Inside segment j: the first logit whose cumulative weight (from `base`)
+// exceeds `target`, or with `last_positive` the last logit of positive weight.
+// Wave w recomputes the weights of block w (512 logits); the crossing block
+// is found from the block totals in order, then the crossing lane and logit.
 template <int ES, bool VEC>
-__device__ int search_segment(const VerifyParams& P, int b, const ReqDesc& d, bool res, int j,
-                              double base, double target, bool last_positive) {
-  const int lane = threadIdx.x & 63;
+__device__ int draw_in_segment(const VerifyParams& P, int b, const ReqDesc& d, bool res, int j, double base,
+                               double target, bool last_positive) {
+  constexpr int W = kWGD / 64;
+  __shared__ double blk_tot[W];
+  __shared__ int blk_last[W];
+  __shared__ int sh_w, sh_mode;
+  __shared__ double sh_base;
+  __shared__ int sh_pick;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const bool resmode = d.mode == kModeResidual;
   const char* prow = row_ptr<ES>(P, b, d.a);
-  const char* qrow = d.mode == kModeResidual ? row_ptr<ES>(P, b, P.K + 1 + d.a) : prow;
+  const char* qrow = resmode ? row_ptr<ES>(P, b, P.K + 1 + d.a) : prow;
   const WeightCtx w = make_ctx(d);
-  const int e0 = j * kSeg + 8 * lane;
-  const int e1 = P.V;
+  const int e0 = j * kSeg + wave * 512 + 8 * lane;
   float xp[8], xq[8];
-  if (e0 < e1) {
-    load_group_bounded<ES, VEC>(prow, e0, e1, xp);
-    load_group_bounded<ES, VEC>(qrow, e0, e1, xq);
+  if (e0 < P.V) {
+    load_group_bounded<ES, VEC>(prow, e0, P.V, xp);
+    if (resmode) load_group_bounded<ES, VEC>(qrow, e0, P.V, xq);
   } else {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) xp[i] = xq[i] = -INFINITY;
+    for (int i = 0; i < 8; ++i) xp[i] = -INFINITY;
+  }
+  if (!resmode || e0 >= P.V) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) xq[i] = resmode ? -INFINITY : 0.f;
   }
   double wt[8];
   double ls = 0.0;
   int lastpos = -1;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    double r, pv;
-    pair_weights(w, xp[i], xq[i], d.mode == kModeResidual, r, pv);
-    wt[i] = res ? r : pv;
+    float ep;
+    const float r = pair_weight(w, xp[i], xq[i], resmode, ep);
+    wt[i] = (double)(res ? r : ep);
     ls += wt[i];
     if (wt[i] > 0.0) lastpos = e0 + i;
   }
-  // inclusive / exclusive wave scan of the lane sums
   double x = ls;
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) {
@@ -535,13 +549,44 @@ __device__ int search_segment(const VerifyParams& P, int b, const ReqDesc& d, bo
   }
   double xe = __shfl_up(x, 1, 64);
   if (lane == 0) xe = 0.0;
-  int pick = -1;
-  if (!last_positive) {
-    const uint64_t m = __ballot(base + x > target);
-    if (m) {
-      const int L = (int)__builtin_ctzll(m);
+  const double wtotal = __shfl(x, 63, 64);
+  int wl = lastpos;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) wl = max(wl, __shfl_xor(wl, off, 64));
+  if (lane == 0) {
+    blk_tot[wave] = wtotal;
+    blk_last[wave] = wl;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int wsel = -1, mode = 1;  // 0: search the block, 1: its last positive logit
+    double acc = base;
+    if (!last_positive) {
+      for (int i = 0; i < W; ++i) {
+        if (acc + blk_tot[i] > target) {
+          wsel = i;
+          mode = 0;
+          break;
+        }
+        acc += blk_tot[i];
+      }
+    }
+    if (wsel < 0)
+      for (int i = 0; i < W; ++i)
+        if (blk_last[i] >= 0) wsel = i;
+    sh_w = wsel;
+    sh_mode = mode;
+    sh_base = acc;
+    sh_pick = -1;
+  }
+  __syncthreads();
+  if (wave == sh_w) {
+    int pick = -1;
+    if (sh_mode == 0) {
+      const uint64_t m = __ballot(sh_base + x > target);
+      const int L = m ? (int)__builtin_ctzll(m) : 63;
       if (lane == L) {
-        double run = base + xe;
+        double run = sh_base + xe;
         for (int i = 0; i < 8; ++i) {
           run += wt[i];
           if (wt[i] > 0.0 && target < run) {
@@ -552,93 +597,71 @@ __device__ int search_segment(const VerifyParams& P, int b, const ReqDesc& d, bo
         if (pick < 0) pick = lastpos;  // cumulative rounding: stay inside this lane
       }
       for (int off = 32; off >= 1; off >>= 1) pick = max(pick, __shfl_xor(pick, off, 64));
-      return pick;
+      if (pick < 0) pick = blk_last[wave];
+    } else {
+      pick = blk_last[wave];
     }
-  }
-  // the last element of positive weight in the segment
-  pick = lastpos;
-  for (int off = 32; off >= 1; off >>= 1) pick = max(pick, __shfl_xor(pick, off, 64));
-  return pick;
-}
-
-template <int ES, bool VEC>
-__device__ void sample(const VerifyParams& P, int b, const ReqDesc& d, const double* __restrict__ seg) {
-  __shared__ int sh_pick;
-  __shared__ double sh_base;
-  const int tid = threadIdx.x;
-  const int nseg = P.nseg;
-  // totals of both weight kinds, as a fixed-order batched scan over segments
-  double carry_r = 0.0, carry_p = 0.0;
-  for (int j0 = 0; j0 < nseg; j0 += kWG) {
-    const int j = j0 + tid;
-    const double vr = j < nseg ? seg[2 * j + 0] : 0.0;
-    const double vp = j < nseg ? seg[2 * j + 1] : 0.0;
-    double i1, e1, t1, i2, e2, t2;
-    block_scan_d(vr, i1, e1, t1);
-    block_scan_d(vp, i2, e2, t2);
-    carry_r += t1;
-    carry_p += t2;
-  }
-  const bool res = d.mode == kModeResidual && carry_r > 0.0;
-  const int wsel = res ? 0 : 1;
-  const double W = res ? carry_r : carry_p;
-  const double target = d.u * W;
-  // first segment whose cumulative weight exceeds target
-  double carry = 0.0;
-  int found = -1, lastpos = -1;
-  double base = 0.0;
-  for (int j0 = 0; j0 < nseg && found < 0; j0 += kWG) {
-    const int j = j0 + tid;
-    const double v = j < nseg ? seg[2 * j + wsel] : 0.0;
-    double incl, excl, tot;
-    block_scan_d(v, incl, excl, tot);
-    const int f = block_first_true(j < nseg && carry + incl > target);
-    lastpos = max(lastpos, block_max_int(v > 0.0 ? j : -1));
-    if (f >= 0 && tid == f) sh_base = carry + excl;
-    __syncthreads();
-    if (f >= 0) {
-      found = j0 + f;
-      base = sh_base;
-    }
-    carry += tot;
-    __syncthreads();
-  }
-  if (tid < 64) {
-    int y = -1;  // no positive weight anywhere: only reachable outside the data contract
-    if (found >= 0) y = search_segment<ES, VEC>(P, b, d, res, found, base, target, false);
-    else if (lastpos >= 0) y = search_segment<ES, VEC>(P, b, d, res, lastpos, 0.0, 0.0, true);
-    if (tid == 0) sh_pick = y;
+    if (lane == 0) sh_pick = pick;
   }
   __syncthreads();
-  if (tid == 0) P.out_tokens[(int64_t)b * (P.K + 1) + d.a] = sh_pick;
+  return sh_pick;
+}
+
+// Inclusive and exclusive scans of two doubles per thread over the workgroup in
+// one pass (fixed order); totals of both.  All threads must call it.
+template <int NT>
+__device__ __forceinline__ void block_scan_d2(double v0, double v1, double& incl0, double& excl0, double& tot0,
+                                              double& incl1, double& excl1, double& tot1) {
+  constexpr int W = NT / 64;
+  __shared__ double wt[2][W];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  double x0 = v0, x1 = v1;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const double y0 = __shfl_up(x0, off, 64);
+    const double y1 = __shfl_up(x1, off, 64);
+    if (lane >= off) {
+      x0 += y0;
+      x1 += y1;
+    }
+  }
+  double e0 = __shfl_up(x0, 1, 64), e1 = __shfl_up(x1, 1, 64);
+  if (lane == 0) e0 = e1 = 0.0;
+  if (lane == 63) {
+    wt[0][w] = x0;
+    wt[1][w] = x1;
+  }
+  __syncthreads();
+  double b0 = 0.0, b1 = 0.0, t0 = 0.0, t1 = 0.0;
+#pragma unroll
+  for (int i = 0; i < W; ++i) {
+    if (i < w) {
+      b0 += wt[0][i];
+      b1 += wt[1][i];
+    }
+    t0 += wt[0][i];
+    t1 += wt[1][i];
+  }
+  incl0 = b0 + x0;
+  excl0 = b0 + e0;
+  tot0 = t0;
+  incl1 = b1 + x1;
+  excl1 = b1 + e1;
+  tot1 = t1;
+  __syncthreads();
 }
 
 template <int ES, bool VEC>
-__global__ __launch_bounds__(kWG) void verify_decide_kernel(VerifyParams P) {
-  const int c = blockIdx.x % P.C;
-  const int b = blockIdx.x / P.C;
-  __shared__ Decision D;
-  decide<ES>(P, b, c == 0, D);
-  if (D.mode == kModeNone) return;
-  ReqDesc d;
-  d.mode = D.mode;
-  d.a = D.a;
-  d.s_hi = D.s_hi;
-  d.s_lo = D.s_lo;
-  d.mp = D.mp;
-  d.sp = D.sp;
-  d.mq = D.mq;
-  d.sq = D.sq;
-  d.u = D.u;
-  double* seg = P.seg + (int64_t)b * P.nseg * 2;
-  if (D.mode == kModeResidual) residual_chunk<ES, VEC, true>(P, b, c, d, seg);
-  else residual_chunk<ES, VEC, false>(P, b, c, d, seg);
-}
-
-template <int ES, bool VEC>
-__global__ __launch_bounds__(kWG) void verify_sample_kernel(VerifyParams P) {
+__global__ __launch_bounds__(kWGD) void verify_draw_kernel(VerifyParams P) {
   const int b = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int nseg = P.nseg;
+  const double* seg = P.seg + (int64_t)b * P.nseg * 2;
+  // the decision record and the first block of segment sums are loaded together
   const ReqDesc d = P.desc[b];
+  const bool in0 = tid < nseg;
+  const double r0 = in0 ? seg[2 * tid + 0] : 0.0;
+  const double p0 = in0 ? seg[2 * tid + 1] : 0.0;
   if (d.mode == kModeResidual) {
     if (d.a < 0 || d.a >= P.K) return;
   } else if (d.mode == kModeBonus) {
@@ -646,14 +669,68 @@ __global__ __launch_bounds__(kWG) void verify_sample_kernel(VerifyParams P) {
   } else {
     return;  // greedy or invalid: nothing to sample
   }
-  sample<ES, VEC>(P, b, d, P.seg + (int64_t)b * P.nseg * 2);
+  __shared__ double sh_base;
+  int found = -1, lastpos = -1;
+  double base = 0.0, target;
+  bool res;
+  if (nseg <= kWGD) {
+    // one pass: scans of both weight kinds, then the crossing of u' * W
+    double ir, er, tr, ip, ep, tp;
+    block_scan_d2<kWGD>(r0, p0, ir, er, tr, ip, ep, tp);
+    res = d.mode == kModeResidual && tr > 0.0;  // else the weights fall back to p
+    target = d.u * (res ? tr : tp);
+    const double incl = res ? ir : ip, excl = res ? er : ep, v = res ? r0 : p0;
+    const int f = block_first_true<kWGD>(in0 && incl > target);
+    lastpos = block_max_int<kWGD>(v > 0.0 ? tid : -1);
+    if (f >= 0 && tid == f) sh_base = excl;
+    __syncthreads();
+    if (f >= 0) {
+      found = f;
+      base = sh_base;
+    }
+  } else {
+    // totals of both weight kinds, a fixed-order batched scan over the segments
+    double carry_r = 0.0, carry_p = 0.0;
+    for (int j0 = 0; j0 < nseg; j0 += kWGD) {
+      const int j = j0 + tid;
+      double i1, e1, t1, i2, e2, t2;
+      block_scan_d2<kWGD>(j < nseg ? seg[2 * j + 0] : 0.0, j < nseg ? seg[2 * j + 1] : 0.0, i1, e1, t1, i2, e2,
+                          t2);
+      carry_r += t1;
+      carry_p += t2;
+    }
+    res = d.mode == kModeResidual && carry_r > 0.0;
+    const int wsel = res ? 0 : 1;
+    target = d.u * (res ? carry_r : carry_p);
+    double carry = 0.0;
+    for (int j0 = 0; j0 < nseg && found < 0; j0 += kWGD) {
+      const int j = j0 + tid;
+      const double v = j < nseg ? seg[2 * j + wsel] : 0.0;
+      double incl, excl, tot, i2, e2, t2;
+      block_scan_d2<kWGD>(v, 0.0, incl, excl, tot, i2, e2, t2);
+      const int f = block_first_true<kWGD>(j < nseg && carry + incl > target);
+      lastpos = max(lastpos, block_max_int<kWGD>(v > 0.0 ? j : -1));
+      if (f >= 0 && tid == f) sh_base = carry + excl;
+      __syncthreads();
+      if (f >= 0) {
+        found = j0 + f;
+        base = sh_base;
+      }
+      carry += tot;
+      __syncthreads();
+    }
+  }
+  int y = -1;  // no positive weight anywhere: only reachable outside the data contract
+  if (found >= 0) y = draw_in_segment<ES, VEC>(P, b, d, res, found, base, target, false);
+  else if (lastpos >= 0) y = draw_in_segment<ES, VEC>(P, b, d, res, lastpos, 0.0, 0.0, true);
+  if (tid == 0) P.out_tokens[(int64_t)b * (P.K + 1) + d.a] = y;
 }
 
 // --------------------------------------------------------------- launch
 template <int ES, bool VEC>
 static hipError_t launch_typed(const VerifyParams& P, hipEvent_t phase_event, hipStream_t stream) {
-  const int64_t g1 = (int64_t)P.B * P.R * P.C;
-  const int64_t g2 = (int64_t)P.B * P.C;
+  const int64_t g1 = (int64_t)P.B * P.R * P.C1;
+  const int64_t g2 = (int64_t)P.B * P.C2;
   hipLaunchKernelGGL((verify_rowstats_kernel<ES, VEC>), dim3((unsigned)g1), dim3(kWG), 0, stream, P);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -664,7 +741,7 @@ static hipError_t launch_typed(const VerifyParams& P, hipEvent_t phase_event, hi
   hipLaunchKernelGGL((verify_decide_kernel<ES, VEC>), dim3((unsigned)g2), dim3(kWG), 0, stream, P);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((verify_sample_kernel<ES, VEC>), dim3((unsigned)P.B), dim3(kWG), 0, stream, P);
+  hipLaunchKernelGGL((verify_draw_kernel<ES, VEC>), dim3((unsigned)P.B), dim3(kWGD), 0, stream, P);
   return hipGetLastError();
 }
 

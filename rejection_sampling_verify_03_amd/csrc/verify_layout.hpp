@@ -7,13 +7,18 @@
 
 namespace specv {
 
-// A row of V logits is cut into C chunks of `chunk` elements (a multiple of
-// the 512-element segment, so segment sums of the sampling pass tile a row
-// exactly); one workgroup streams one chunk.  ~32K elements per chunk keeps
-// each workgroup's stream long enough to hide its start-up and gives
-// thousands of workgroups at the workload sizes of interest.
-constexpr int kChunkTarget = 32768;
-constexpr int kSeg = 512;  // elements per segment = one wave64 x 8 elements
+// Segments: the sampling pass sums its weights over runs of kSeg consecutive
+// logits, one run per wave64 (8 groups of 8 logits per lane), and the draw
+// then searches a single segment.
+constexpr int kSegGroups = 8;
+constexpr int kSeg = 64 * 8 * kSegGroups;  // 4096 logits
+
+// Row pass: one 256-thread workgroup streams ~32K logits of one row, long
+// enough to hide its start-up, still thousands of workgroups per batch.
+constexpr int kRowChunkTarget = 32768;
+// Sampling pass: ~32K logits (8 segments, 2 per wave) per workgroup spreads
+// the 1-2 sampling rows of a request over several compute units.
+constexpr int kSampleChunkTarget = 32768;
 
 struct RowPartial {  // one chunk of one row
   float m;           // integer-valued reference exponent (sampled) or max logit (greedy)
@@ -21,7 +26,7 @@ struct RowPartial {  // one chunk of one row
   double s;          // sum of 2^(x*s - m) over the chunk (sampled)
 };
 
-struct ReqDesc {  // decision of one request, consumed by the sampling pass
+struct ReqDesc {  // decision of one request, read by the draw
   int32_t mode;   // kModeNone / kModeResidual / kModeBonus
   int32_t a;      // accepted drafts = the sampling row
   float s_hi, s_lo;
@@ -30,31 +35,41 @@ struct ReqDesc {  // decision of one request, consumed by the sampling pass
   double u;       // the sampling uniform of row a
   double pad;
 };
+
 static_assert(sizeof(RowPartial) == 16, "RowPartial layout");
 static_assert(sizeof(ReqDesc) == 64, "ReqDesc layout");
 
 enum { kModeNone = 0, kModeResidual = 1, kModeBonus = 2 };
 
 struct Layout {
-  int32_t R, C, chunk, nseg;
+  int32_t R;           // rows per request the row pass may read: K+1 target + K draft
+  int32_t C1, chunk1;  // row-pass chunks per row and their length
+  int32_t C2, chunk2;  // sampling-pass chunks per row and their length
+  int32_t nseg;        // segments per row
   size_t off_rowp, off_desc, off_seg, total;
 };
 
 __host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// Cut V into chunks of about `target` logits, each a multiple of kSeg.
+__host__ __device__ inline void chunking(int32_t V, int32_t target, int32_t& C, int32_t& chunk) {
+  int64_t n = ((int64_t)V + target - 1) / target;
+  if (n < 1) n = 1;
+  int64_t per = ((int64_t)V + n - 1) / n;
+  per = (per + kSeg - 1) / kSeg * kSeg;
+  chunk = (int32_t)per;
+  C = (int32_t)(((int64_t)V + per - 1) / per);
+}
+
 __host__ __device__ inline Layout make_layout(int32_t B, int32_t K, int32_t V) {
   Layout L;
   L.R = 2 * K + 1;
-  int64_t C = ((int64_t)V + kChunkTarget - 1) / kChunkTarget;
-  if (C < 1) C = 1;
-  int64_t per = ((int64_t)V + C - 1) / C;
-  per = (per + kSeg - 1) / kSeg * kSeg;
-  L.chunk = (int32_t)per;
-  L.C = (int32_t)(((int64_t)V + per - 1) / per);
+  chunking(V, kRowChunkTarget, L.C1, L.chunk1);
+  chunking(V, kSampleChunkTarget, L.C2, L.chunk2);
   L.nseg = (int32_t)(((int64_t)V + kSeg - 1) / kSeg);
   size_t off = 0;
   L.off_rowp = off;
-  off = align256(off + (size_t)B * L.R * L.C * sizeof(RowPartial));
+  off = align256(off + (size_t)B * L.R * L.C1 * sizeof(RowPartial));
   L.off_desc = off;
   off = align256(off + (size_t)B * sizeof(ReqDesc));
   L.off_seg = off;
