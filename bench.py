@@ -33,6 +33,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="approximate CPU-seconds of oracle work for the CPU baseline")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="after the timed steps, copy 1 GiB device to device once (a plain copy kernel of known "
+                         "size, to scale hardware byte counters)")
     return ap.parse_args()
 
 
@@ -51,6 +54,31 @@ def algorithmic_expand_bytes(B, K, H, n_in):
     meta_in = n_in * (4 + 8) + (B + 1) * 4 + B * 4 + B * 4
     meta_out = n_out * (4 + 8 + 1 + 1) + B * K * 4 + n_in * 4 + (B + 1) * 4
     return hidden + meta_in + meta_out
+
+
+ROWPASS_SOURCES = ["rejection_sampling_verify_03_amd/csrc/verify.hip", "rejection_sampling_verify_03_amd/csrc/device_common.hpp",
+                   "rejection_sampling_verify_03_amd/csrc/verify_layout.hpp",
+                   "rejection_sampling_verify_03_amd/csrc/verify_kernels.hpp"]
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "verify_rowstats_traffic.md")
+
+
+def measured_traffic():
+    """HBM bytes per launch of the row pass from the committed counter summary,
+    or None when the row-pass sources changed since those counters were taken."""
+    import hashlib
+    import re
+    h = hashlib.sha256()
+    for f in ROWPASS_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    try:
+        text = open(TRAFFIC_SUMMARY).read()
+    except OSError:
+        return None
+    m = re.search(r"traffic_bytes_per_launch: (\d+) source_sha256: ([0-9a-f]+)", text)
+    if not m or m.group(2) != h.hexdigest()[:16]:
+        return None
+    return int(m.group(1))
 
 
 def cpu_baseline(inp, seed, cpu_seconds):
@@ -154,6 +182,13 @@ def main():
     k2 = np.array([e[1].elapsed_time(e[2]) for e in ev])
     ke = np.array([e[2].elapsed_time(e[3]) for e in ev])
 
+    if args.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
     temps = inp.temperature.cpu().numpy()
     vbytes = algorithmic_verify_bytes(B, K, V, 2, temps)
     logit_bytes = vbytes - (B * K * 4 + B * 4 + B * 4 + B * (K + 1) * 4)
@@ -179,7 +214,7 @@ def main():
                                "+ P-EAGLE expand H=2880 chained on the verify outputs",
                    "B": B, "K": K, "V": V, "H": H, "sampled_requests": int((temps > 0).sum())},
         "roofline": {"kernel": "verify_rowstats", "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(),
                      "algorithmic_bytes": logit_bytes},
         "kernels_ms": {"verify_rowstats": k1_ms, "verify_decide_and_draw": float(k2.mean()),
                        "expand": float(ke.mean()),
