@@ -49,17 +49,20 @@ def zipf_logits(rows, V, g, device, slope=1.1, noise=0.3, batch=256):
     return out
 
 
-def gumbel_argmax(logits_f32, g, batch=256):
-    """One draw per row from softmax(logits) by the Gumbel-max trick; -inf
-    logits are never drawn."""
-    rows, V = logits_f32.shape
-    out = torch.empty(rows, dtype=torch.int64, device=logits_f32.device)
-    tiny = torch.finfo(torch.float32).tiny
+def gumbel_argmax(logits, g, batch=128):
+    """One draw per row from softmax(logits) by the Gumbel-max trick, in
+    float64: with float32 uniforms the largest Gumbel values -- the ones that
+    pick the winner among ~1e5 tokens -- sit on a coarse grid (the uniforms'
+    2^-24 spacing next to 1) and over-weight the likeliest tokens.  -inf logits
+    are never drawn."""
+    rows, V = logits.shape
+    out = torch.empty(rows, dtype=torch.int64, device=logits.device)
+    tiny = torch.finfo(torch.float64).tiny
     for r0 in range(0, rows, batch):
         r1 = min(rows, r0 + batch)
-        u = torch.rand(r1 - r0, V, generator=g, device=logits_f32.device).clamp_min_(tiny)
+        u = torch.rand(r1 - r0, V, generator=g, device=logits.device, dtype=torch.float64).clamp_min_(tiny)
         gumbel = -torch.log(-torch.log(u))
-        out[r0:r1] = torch.argmax(logits_f32[r0:r1] + gumbel, dim=1)
+        out[r0:r1] = torch.argmax(logits[r0:r1].double() + gumbel, dim=1)
     return out
 
 
