@@ -7,10 +7,17 @@ bonus read from the verification's output tokens), both through the C ABI on
 torch's current stream.  Inputs are generated once on the GPU and stay resident
 in HBM; each timed step uses a new Philox step counter.
 
+By default the verification reads its rows in early-exit phases (rows of a
+phase only for requests whose earlier drafts were all accepted), cut by the
+library's planner from the acceptance curve of one-pass warmup steps; the
+outputs are identical to one pass (--early-exit off).
+
 Prints one JSON line: verified draft positions per second (B*K per step),
-the roofline of the dominant kernel (the row-statistics pass of verification)
-timed with HIP events on the launch stream, and the CPU oracle timed on the
-host's cores over whole steps of the same batch.
+the roofline of the dominant stage (the row statistics of verification: its
+row-pass kernels and, with phases, the decisions between them), timed with
+HIP events on the launch stream against the logit bytes the timed steps
+read, and the CPU oracle timed on the host's cores over whole steps of the
+same batch.
 """
 import argparse
 import json
@@ -33,6 +40,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="approximate CPU-seconds of oracle work for the CPU baseline")
+    ap.add_argument("--early-exit", choices=("plan", "off"), default="plan",
+                    help="plan: read rows in phases planned from the acceptance of the warmup steps; "
+                         "off: one pass over every row")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the timed steps, copy 1 GiB device to device once (a plain copy kernel of known "
                          "size, to scale hardware byte counters)")
@@ -46,6 +56,33 @@ def algorithmic_verify_bytes(B, K, V, es, temps):
     n_sampled = int((temps > 0).sum())
     logits = B * (K + 1) * V * es + n_sampled * K * V * es
     return logits + B * K * 4 + B * 4 + B * 4 + B * (K + 1) * 4
+
+
+def phased_logit_bytes(acc, temps, mask, K, V, es):
+    """Logit bytes the row stage reads under the phase cut `mask` (0 = one
+    pass) for one step with accepted counts `acc`: a request reads the rows of
+    every phase up to the one holding its stopping position (all of them when
+    its data is invalid only under one pass)."""
+    starts = [0] + [k for k in range(1, K + 1) if (mask >> k) & 1]
+    ends = starts[1:] + [K + 1]
+    total = 0
+    for a, t in zip(acc, temps):
+        a = K if a < 0 else int(a)
+        for s, e in zip(starts, ends):
+            if s > a:
+                break
+            total += (e - s) + ((min(e, K) - s) if t > 0 else 0)
+    return total * V * es
+
+
+def sequential_logit_bytes(acc, temps, K, V, es):
+    """The method's own minimum: rows 0..a of the target and, for sampled
+    requests, draft rows 0..min(a, K-1)."""
+    rows = sum((int(a) + 1) + (min(int(a) + 1, K) if t > 0 else 0) for a, t in zip(acc, temps) if a >= 0)
+    return rows * V * es
+
+
+PHASE_BOUNDARY_US = 8.0  # one extra phase: the phase-decision kernel and two launch gaps (measured)
 
 
 def algorithmic_expand_bytes(B, K, H, n_in):
@@ -152,10 +189,12 @@ def main():
             e.record(stream)
     torch.cuda.synchronize()
 
+    plan = {"mask": 0}
+
     def step(i, events=None):
         va = sv.verify_args(inp.target, inp.draft, inp.draft_tokens, inp.temperature, accepted, tokens, None,
                             ws, seed=args.seed, step=i,
-                            phase_event=events[1].cuda_event if events else None)
+                            phase_event=events[1].cuda_event if events else None, phase_starts=plan["mask"])
         if events:
             events[0].record(stream)
         rc = sv.spec_verify_launch(va, sptr)
@@ -169,6 +208,23 @@ def main():
         if events:
             events[3].record(stream)
 
+    temps = inp.temperature.cpu().numpy()
+    sampled_fraction = float((temps > 0).mean())
+    if args.early_exit == "plan":
+        # one-pass warmup steps give the acceptance curve and the time to read one row of every request;
+        # the phase plan follows from them, as a serving loop would plan from its recent steps
+        n0 = max(args.warmup // 2, 2)
+        accs, k1w = [], []
+        for i in range(n0):
+            step(1_000_000 + i, ev[i])
+            torch.cuda.synchronize()
+            accs.extend(accepted.cpu().tolist())
+            k1w.append(ev[i][0].elapsed_time(ev[i][1]))
+        surv = sv.survival_from_accepted(accs, K)
+        row_us = 1e3 * float(np.median(k1w)) / ((K + 1) + sampled_fraction * K)
+        plan["mask"] = sv.spec_verify_plan_phases(K, surv, sampled_fraction, PHASE_BOUNDARY_US / row_us)
+        plan["survival"] = [round(v, 4) for v in surv]
+        plan["phase_cost_rows"] = round(PHASE_BOUNDARY_US / row_us, 4)
     for i in range(args.warmup):
         step(1_000_000 + i)
     torch.cuda.synchronize()
@@ -189,13 +245,20 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    temps = inp.temperature.cpu().numpy()
+    # the timed steps again, untimed (outputs depend only on seed and step), for the rows each one read
+    mask = plan["mask"]
+    acc_steps = []
+    for i in range(args.steps):
+        step(i)
+        acc_steps.append(accepted.cpu().numpy().copy())
+    read_bytes = float(np.mean([phased_logit_bytes(a, temps, mask, K, V, 2) for a in acc_steps]))
+    seq_bytes = float(np.mean([sequential_logit_bytes(a, temps, K, V, 2) for a in acc_steps]))
     vbytes = algorithmic_verify_bytes(B, K, V, 2, temps)
-    logit_bytes = vbytes - (B * K * 4 + B * 4 + B * 4 + B * (K + 1) * 4)
+    one_pass_bytes = vbytes - (B * K * 4 + B * 4 + B * 4 + B * (K + 1) * 4)
     ebytes = algorithmic_expand_bytes(B, K, H, B * (K + 1))
     k1_ms = float(k1.mean())
-    achieved = logit_bytes / (k1_ms * 1e-3) / 1e9
-    acc_np = accepted.cpu().numpy()
+    achieved = read_bytes / (k1_ms * 1e-3) / 1e9
+    acc_np = np.concatenate(acc_steps)
     positions_per_s = B * K / (ms_per_step * 1e-3)
     line = {
         "metric": "verified draft positions/sec + achieved HBM GB/s at B=256,K=8,V=151936 bf16",
@@ -214,14 +277,18 @@ def main():
                                "+ P-EAGLE expand H=2880 chained on the verify outputs",
                    "B": B, "K": K, "V": V, "H": H, "sampled_requests": int((temps > 0).sum())},
         "roofline": {"kernel": "verify_rowstats", "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(),
-                     "algorithmic_bytes": logit_bytes},
-        "kernels_ms": {"verify_rowstats": k1_ms, "verify_decide_and_draw": float(k2.mean()),
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": measured_traffic() if mask == 0 else None,
+                     "algorithmic_bytes": read_bytes, "one_pass_bytes": one_pass_bytes,
+                     "sequential_min_bytes": seq_bytes},
+        "early_exit": {"phase_starts": mask, "phases": [0] + [k for k in range(1, K + 1) if (mask >> k) & 1],
+                       **{k: v for k, v in plan.items() if k != "mask"}},
+        "kernels_ms": {"verify_row_stage": k1_ms, "verify_decide_and_draw": float(k2.mean()),
                        "expand": float(ke.mean()),
-                       "verify_rowstats_p10_p90": [float(np.percentile(k1, 10)), float(np.percentile(k1, 90))]},
-        "verify_GBps_algorithmic": vbytes / ((k1.mean() + k2.mean()) * 1e-3) / 1e9,
+                       "verify_row_stage_p10_p90": [float(np.percentile(k1, 10)), float(np.percentile(k1, 90))]},
+        "verify_GBps_algorithmic": (read_bytes + vbytes - one_pass_bytes) / ((k1.mean() + k2.mean()) * 1e-3) / 1e9,
         "expand_GBps_algorithmic": ebytes / (ke.mean() * 1e-3) / 1e9,
-        "emitted_tokens_per_s": float((acc_np + 1).sum()) / (ms_per_step * 1e-3),
+        "emitted_tokens_per_s": float((acc_np + 1).sum()) / args.steps / (ms_per_step * 1e-3),
         "mean_accepted": float(acc_np.mean()),
     }
     if not args.no_cpu_baseline:

@@ -96,8 +96,33 @@ typedef struct {
   void* workspace;             /* device scratch, >= spec_verify_workspace_bytes(B, K, V) bytes, 16-B aligned */
   size_t workspace_bytes;
   void* phase_event;           /* hipEvent_t or NULL: recorded on `stream` right after the
-                                  row-statistics kernel (to time it apart from the rest) */
+                                  row-statistics stage (to time it apart from the rest) */
+  uint64_t phase_starts;       /* early exit: bit k (1 <= k <= K) starts a new phase at draft
+                                  position k; 0 = one pass over every row (see below) */
 } spec_verify_args;
+
+/* Early exit (same explainer page, section "核心思想": a request stops at
+ * its first rejection, so the rows after it are never needed).  With
+ * phase_starts != 0 the positions 0..K are cut into phases at the set bits;
+ * the rows of a phase (target rows k and, for sampled requests, draft rows k
+ * of its positions) are read only for requests whose drafts before the phase
+ * were all accepted, and a small kernel between phases runs the phase's
+ * accept tests.  accepted_counts and output_tokens are identical to the
+ * one-pass result.  Differences: debug_probs of positions in phases after
+ * the one where a request stopped are 0 (their rows are never read), and a
+ * row without a finite normaliser in such a phase is not detected. */
+
+/* A phase plan for phase_starts: minimises the expected rows read plus
+ * phase_cost per extra phase, over every way of cutting 0..K into phases,
+ * when a request reaches position k (all drafts before k accepted) with
+ * probability survival[k] (host array [K+1], survival[0] = 1; e.g. measured
+ * on recent steps).  Rows are counted per request: one target row per
+ * position 0..K plus sampled_fraction draft rows per position 0..K-1; phase_cost
+ * is the time of one phase boundary in units of the time to read one row for
+ * every request.  Returns 0 (one pass) when that is best or an argument is out
+ * of range (K outside 1..SPEC_MAX_K, NULL survival, negative or non-finite
+ * inputs). */
+uint64_t spec_verify_plan_phases(int32_t K, const double* survival, double sampled_fraction, double phase_cost);
 
 /* Bytes of device workspace a verification of this shape needs (0 for an
  * invalid shape).  The workspace carries nothing from one call to the next:

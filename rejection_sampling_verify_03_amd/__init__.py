@@ -20,8 +20,8 @@ SPEC_OK, SPEC_EINVAL, SPEC_EDTYPE, SPEC_EALIGN, SPEC_EWORKSPACE, SPEC_ELAUNCH = 
 SPEC_F32, SPEC_BF16 = 0, 1
 SPEC_MAX_K = 63
 
-EXPORTED = ("spec_verify_workspace_bytes", "spec_verify_launch", "spec_expand_launch",
-            "spec_status_string")
+EXPORTED = ("spec_verify_workspace_bytes", "spec_verify_plan_phases", "spec_verify_launch",
+            "spec_expand_launch", "spec_status_string")
 
 
 class SpecVerifyArgs(ctypes.Structure):
@@ -33,7 +33,7 @@ class SpecVerifyArgs(ctypes.Structure):
         ("seed", ctypes.c_uint64), ("step", ctypes.c_uint32), ("request_base", ctypes.c_uint32),
         ("accepted_counts", ctypes.c_void_p), ("output_tokens", ctypes.c_void_p),
         ("debug_probs", ctypes.c_void_p), ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
-        ("phase_event", ctypes.c_void_p),
+        ("phase_event", ctypes.c_void_p), ("phase_starts", ctypes.c_uint64),
     ]
 
 
@@ -65,6 +65,9 @@ def _load():
     L = ctypes.CDLL(LIB_PATH)
     L.spec_verify_workspace_bytes.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32]
     L.spec_verify_workspace_bytes.restype = ctypes.c_size_t
+    L.spec_verify_plan_phases.argtypes = [ctypes.c_int32, ctypes.POINTER(ctypes.c_double), ctypes.c_double,
+                                          ctypes.c_double]
+    L.spec_verify_plan_phases.restype = ctypes.c_uint64
     L.spec_verify_launch.argtypes = [ctypes.POINTER(SpecVerifyArgs), ctypes.c_void_p]
     L.spec_verify_launch.restype = ctypes.c_int
     L.spec_expand_launch.argtypes = [ctypes.POINTER(SpecExpandArgs), ctypes.c_void_p]
@@ -86,6 +89,21 @@ class SpecError(RuntimeError):
 # ----------------------------------------------------------------- raw C ABI
 def spec_verify_workspace_bytes(B, K, V):
     return int(lib.spec_verify_workspace_bytes(int(B), int(K), int(V)))
+
+
+def spec_verify_plan_phases(K, survival, sampled_fraction, phase_cost):
+    """survival: K+1 floats, survival[k] = probability that a request reaches
+    draft position k.  Returns the phase_starts bit mask (0 = one pass)."""
+    arr = (ctypes.c_double * (int(K) + 1))(*[float(v) for v in survival])
+    return int(lib.spec_verify_plan_phases(int(K), arr, float(sampled_fraction), float(phase_cost)))
+
+
+def survival_from_accepted(accepted, K):
+    """survival[k] = fraction of valid requests whose first k drafts were
+    accepted, from a batch of accepted counts (any iterable of ints)."""
+    a = [int(v) for v in accepted if int(v) >= 0]
+    n = max(len(a), 1)
+    return [sum(1 for v in a if v >= k) / n for k in range(int(K) + 1)]
 
 
 def spec_verify_launch(args, stream_ptr):
@@ -141,7 +159,7 @@ def make_workspace(B, K, V, device="cuda"):
 
 
 def verify_args(target, draft, draft_tokens, temperature, accepted, tokens, debug, workspace,
-                seed=0, step=0, request_base=0, phase_event=None):
+                seed=0, step=0, request_base=0, phase_event=None, phase_starts=0):
     """Fill a SpecVerifyArgs from tensors (no copies).
 
     target [B or broadcast, K+1, V] and draft [B or broadcast, >=K, V] with a
@@ -175,11 +193,12 @@ def verify_args(target, draft, draft_tokens, temperature, accepted, tokens, debu
     a.workspace = workspace.data_ptr()
     a.workspace_bytes = workspace.numel() * workspace.element_size()
     a.phase_event = phase_event
+    a.phase_starts = int(phase_starts)
     return a
 
 
 def verify(target, draft, draft_tokens, temperature, seed=0, step=0, request_base=0, debug=False,
-           workspace=None, stream=None):
+           workspace=None, stream=None, phase_starts=0):
     """One verification step on torch's current stream.  Returns
     (accepted_counts [B] int32, output_tokens [B, K+1] int32, debug_probs
     [B, K, 2] float32 or None)."""
@@ -192,7 +211,7 @@ def verify(target, draft, draft_tokens, temperature, seed=0, step=0, request_bas
     dbg = torch.empty(B, K, 2, dtype=torch.float32, device=dev) if debug else None
     ws = workspace if workspace is not None else make_workspace(B, K, V, dev)
     a = verify_args(target, draft, draft_tokens, temperature, accepted, tokens, dbg, ws, seed, step,
-                    request_base)
+                    request_base, phase_starts=phase_starts)
     rc = spec_verify_launch(a, _stream_ptr(stream))
     if rc != SPEC_OK:
         raise SpecError(rc)

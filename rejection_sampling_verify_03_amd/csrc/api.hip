@@ -29,6 +29,8 @@ int verify_check(const spec_verify_args* a) {
   const Layout L = make_layout(a->B, a->K, a->V);
   if ((int64_t)a->B * L.R * L.C1 > INT32_MAX || (int64_t)a->B * L.C2 > INT32_MAX) return SPEC_EINVAL;
   if (!aligned16(a->workspace)) return SPEC_EALIGN;
+  if (a->phase_starts & 1u) return SPEC_EINVAL;  // position 0 always starts the first phase
+  if (a->K < 63 && (a->phase_starts >> (a->K + 1)) != 0) return SPEC_EINVAL;
   if (a->workspace_bytes < L.total) return SPEC_EWORKSPACE;
   return SPEC_OK;
 }
@@ -53,6 +55,31 @@ int expand_check(const spec_expand_args* a) {
 }  // namespace
 
 extern "C" {
+
+uint64_t spec_verify_plan_phases(int32_t K, const double* survival, double sampled_fraction, double phase_cost) {
+  if (K < 1 || K > SPEC_MAX_K || !survival) return 0;
+  if (!(sampled_fraction >= 0.0 && sampled_fraction <= 1.0) || !(phase_cost >= 0.0 && phase_cost < 1e300)) return 0;
+  for (int k = 0; k <= K; ++k)
+    if (!(survival[k] >= 0.0 && survival[k] <= 1.0)) return 0;
+  // best[s]: least expected cost of positions s..K when a phase starts at s
+  double best[SPEC_MAX_K + 2];
+  int next[SPEC_MAX_K + 2];
+  best[K + 1] = 0.0;
+  for (int s = K; s >= 0; --s) {
+    best[s] = -1.0;
+    for (int e = K + 1; e > s; --e) {
+      const double rows = (double)(e - s) + sampled_fraction * (double)((e < K ? e : K) - s);
+      const double c = survival[s] * rows + (e <= K ? phase_cost : 0.0) + best[e];
+      if (best[s] < 0.0 || c < best[s]) {  // ties keep the longer phase, found first
+        best[s] = c;
+        next[s] = e;
+      }
+    }
+  }
+  uint64_t mask = 0;
+  for (int s = next[0]; s <= K; s = next[s]) mask |= (uint64_t)1 << s;
+  return mask;
+}
 
 size_t spec_verify_workspace_bytes(int32_t B, int32_t K, int32_t V) {
   if (B < 0 || K < 1 || K > SPEC_MAX_K || V < 1) return 0;
@@ -95,7 +122,11 @@ int spec_verify_launch(const spec_verify_args* a, hipStream_t stream) {
   const bool vec = aligned16(a->target_logits) && aligned16(a->draft_logits) &&
                    (a->t_row_stride * es) % 16 == 0 && (a->t_req_stride * es) % 16 == 0 &&
                    (a->d_row_stride * es) % 16 == 0 && (a->d_req_stride * es) % 16 == 0;
-  return launch_verify(P, a->dtype, vec, static_cast<hipEvent_t>(a->phase_event), stream) == hipSuccess
+  P.state = reinterpret_cast<int32_t*>(ws + L.off_state);
+  P.ph_lo = P.ph_nt = P.ph_nd = P.ph_check = 0;
+  P.last_lo = P.phased = 0;
+  return launch_verify(P, a->dtype, vec, a->phase_starts, static_cast<hipEvent_t>(a->phase_event), stream) ==
+                 hipSuccess
              ? SPEC_OK
              : SPEC_ELAUNCH;
 }

@@ -33,6 +33,13 @@
 //      segment sums for the inverse-CDF crossing of u' * R, recomputes the
 //      weights of that one segment (one 512-logit block per wave) and finds
 //      the token with a wavefront scan.
+//
+// Early exit (a request stops at its first rejection, same page, section
+// "核心思想"): the caller may cut the positions 0..K into phases.  The row
+// pass then runs once per phase over the phase's rows, skipping requests that
+// already stopped, and verify_phase runs the phase's accept tests in between
+// (one workgroup per request), leaving a per-request state for the next
+// phase and for the final decision.
 #include <float.h>
 #include <limits.h>
 
@@ -184,86 +191,137 @@ __device__ __forceinline__ VI block_argmax(VI v) {
 }
 
 // ------------------------------------------------------------- decision
-// The decision of request b, computed by the whole workgroup into `D`
-// (shared).  With `write`, the request's outputs (all but the token the draw
-// samples) and its decision record are written too.
+// The accept tests of request b over draft positions [lo, hi) (positions
+// before lo passed in earlier phases), computed by the whole workgroup.
+// Merges the statistics of target rows [lo, thi) and, for a sampled request,
+// draft rows [lo, min(thi, K)) into `sh`; thi >= hi.  With known >= 0 no test
+// runs and a = known (its rows lo = known, thi = known + 1 are merged for the
+// draw).  Returns, in every thread, a in [lo, hi] (hi: every test in range
+// passed) or -1 for invalid data.  Every draft token and the temperature are
+// checked whatever the range, so invalid tokens are caught by the first
+// decision of a request.  With `debug`, writes p_k(x_k), q_k(x_k) of every
+// tested position, zero for the positions from hi on when the request stopped
+// before hi (their rows are never read) and zero everywhere for invalid data.
+struct DecideShared {
+  float m[2 * SPEC_MAX_K + 1];
+  double s[2 * SPEC_MAX_K + 1];
+  int g[SPEC_MAX_K + 1];
+  int bad;
+  int a;
+};
+
 template <int ES>
-__device__ void decide(const VerifyParams& P, int b, bool write, ReqDesc& D) {
-  __shared__ float sh_m[2 * SPEC_MAX_K + 1];
-  __shared__ double sh_s[2 * SPEC_MAX_K + 1];
-  __shared__ int sh_g[SPEC_MAX_K + 1];
-  __shared__ int sh_bad;
+__device__ int decide_tests(const VerifyParams& P, int b, int lo, int hi, int thi, int known, bool invalid,
+                            bool debug, DecideShared& sh) {
   const int K = P.K;
   const int tid = threadIdx.x;
   const float T = P.temperature[b];
   const bool greedy = (T == 0.0f);
-  if (tid == 0) sh_bad = temperature_valid(T) ? 0 : 1;
+  const bool test = known < 0;
+  if (tid == 0) sh.bad = (invalid || !temperature_valid(T)) ? 1 : 0;
   __syncthreads();
   int x = 0;
   float zt_f = 0.f, zq_f = 0.f;
   if (tid < K) {
     x = P.tokens[(int64_t)b * K + tid];
-    if (x < 0 || x >= P.V) atomicOr(&sh_bad, 1);
-    if (!greedy) {  // gathered logits, loaded while the partials below are in flight
-      const int xc = min(max(x, 0), P.V - 1);  // a bad token makes the request invalid anyway
+    if (x < 0 || x >= P.V) atomicOr(&sh.bad, 1);
+    if (!greedy && test && tid >= lo && tid < hi) {  // gathered logits, in flight with the partials below
+      const int xc = min(max(x, 0), P.V - 1);        // a bad token makes the request invalid anyway
       zt_f = load_one<ES>(row_ptr<ES>(P, b, tid), xc);
       zq_f = load_one<ES>(row_ptr<ES>(P, b, K + 1 + tid), xc);
     }
   }
-  const int nrows = greedy ? K + 1 : P.R;
-  if (tid < nrows) {
-    const RowPartial* rp = P.rowp + ((int64_t)b * P.R + tid) * P.C1;
+  const int nt = thi - lo;
+  const int nrows = nt + (greedy ? 0 : min(thi, K) - lo);
+  if (tid < nrows && !invalid) {
+    const int r = tid < nt ? lo + tid : K + 1 + lo + (tid - nt);
+    const RowPartial* rp = P.rowp + ((int64_t)b * P.R + r) * P.C1;
     if (greedy) {
       VI best{rp[0].m, rp[0].idx};
       for (int c = 1; c < P.C1; ++c) best = vi_pick(best, VI{rp[c].m, rp[c].idx});
-      sh_g[tid] = best.i;
+      sh.g[r] = best.i;
     } else {
       MS acc{rp[0].m, rp[0].s};
       for (int c = 1; c < P.C1; ++c) acc = ms_merge(acc, MS{rp[c].m, rp[c].s});
-      sh_m[tid] = acc.m;
-      sh_s[tid] = acc.s;
-      if (!(acc.s > 0.0 && acc.s <= DBL_MAX && fabsf(acc.m) <= FLT_MAX)) atomicOr(&sh_bad, 1);
+      sh.m[r] = acc.m;
+      sh.s[r] = acc.s;
+      if (!(acc.s > 0.0 && acc.s <= DBL_MAX && fabsf(acc.m) <= FLT_MAX)) atomicOr(&sh.bad, 1);
     }
   }
   __syncthreads();
-  const bool bad = sh_bad != 0;
-  float s_hi = 0.f, s_lo = 0.f;
-  if (!greedy && !bad) temperature_scale(T, s_hi, s_lo);
-  const uint32_t k0 = (uint32_t)(P.seed & 0xffffffffu), k1 = (uint32_t)(P.seed >> 32);
-  const uint32_t req = (uint32_t)b + P.request_base;
-
+  const bool bad = sh.bad != 0;
   if (tid < 64) {  // wave 0: one lane per draft position
-    bool acc = false;
+    bool acc = tid < lo;
     float dp = 0.f, dq = 0.f;
-    if (tid < K && !bad) {
+    if (test && tid >= lo && tid < hi && !bad) {
       if (greedy) {
-        acc = (x == sh_g[tid]);
+        acc = (x == sh.g[tid]);
       } else {
+        float s_hi, s_lo;
+        temperature_scale(T, s_hi, s_lo);
         const double s_eff = (double)s_hi + (double)s_lo;
-        const double zt = (double)zt_f;
-        const double zq = (double)zq_f;
-        const double p = exp2(zt * s_eff - (double)sh_m[tid]) / sh_s[tid];
-        const double q = exp2(zq * s_eff - (double)sh_m[K + 1 + tid]) / sh_s[K + 1 + tid];
+        const double p = exp2((double)zt_f * s_eff - (double)sh.m[tid]) / sh.s[tid];
+        const double q = exp2((double)zq_f * s_eff - (double)sh.m[K + 1 + tid]) / sh.s[K + 1 + tid];
         const double thr = q > 0.0 ? fmin(1.0, p / q) : (p > 0.0 ? 1.0 : 0.0);
-        const Philox4 r = philox4x32_10(req, (uint32_t)tid, P.step, 0u, k0, k1);
-        acc = unit_uniform(r.w[0]) < thr;
+        const uint32_t k0 = (uint32_t)(P.seed & 0xffffffffu), k1 = (uint32_t)(P.seed >> 32);
+        const Philox4 rr = philox4x32_10((uint32_t)b + P.request_base, (uint32_t)tid, P.step, 0u, k0, k1);
+        acc = unit_uniform(rr.w[0]) < thr;
         dp = (float)p;
         dq = (float)q;
       }
     }
     const uint64_t mask = __ballot(acc);
-    const int a = bad ? -1 : (int)__builtin_ctzll(~mask);  // lanes >= K never accept, so a <= K
-    if (write) {
-      if (P.debug && tid < K) {
-        P.debug[((int64_t)b * K + tid) * 2 + 0] = dp;
-        P.debug[((int64_t)b * K + tid) * 2 + 1] = dq;
+    const int a = bad ? -1 : (test ? (int)__builtin_ctzll(~mask) : known);  // lanes >= hi fail: a <= hi
+    if (debug && P.debug && tid < K) {
+      float* d = P.debug + ((int64_t)b * K + tid) * 2;
+      if (bad || (tid >= hi && a < hi)) {
+        d[0] = 0.f;
+        d[1] = 0.f;
+      } else if (test && tid >= lo && tid < hi) {
+        d[0] = dp;
+        d[1] = dq;
       }
+    }
+    if (tid == 0) sh.a = a;
+  }
+  __syncthreads();
+  return sh.a;
+}
+
+// The decision of request b at the sampling stage, computed by the whole
+// workgroup into `D` (shared).  With `write`, the request's outputs (all but
+// the token the draw samples), its debug rows and its decision record are
+// written too.
+template <int ES>
+__device__ void decide(const VerifyParams& P, int b, bool write, ReqDesc& D) {
+  __shared__ DecideShared sh;
+  const int K = P.K;
+  const int tid = threadIdx.x;
+  int lo = 0, known = -1;
+  bool invalid = false;
+  if (P.phased) {  // rows were read in phases: the request may have stopped earlier
+    const int st = P.state[b];
+    invalid = st == kStateInvalid;
+    if (st >= 0) {
+      known = st;
+      lo = st;
+    } else {
+      lo = P.last_lo;
+    }
+  }
+  const int thi = known >= 0 ? known + 1 : K + 1;
+  const int a = decide_tests<ES>(P, b, lo, K, thi, known, invalid, write, sh);
+  const float T = P.temperature[b];
+  const bool greedy = (T == 0.0f);
+  const bool bad = a < 0;
+  if (tid < 64) {
+    if (write) {
       int32_t* out = P.out_tokens + (int64_t)b * (K + 1);
       for (int j = tid; j <= K; j += 64) {  // K <= 63: one pass
         int tok;
         if (bad || j > a) tok = -1;
         else if (j < a) tok = P.tokens[(int64_t)b * K + j];
-        else tok = greedy ? sh_g[a] : -1;  // sampled: written by the draw
+        else tok = greedy ? sh.g[a] : -1;  // sampled: written by the draw
         if (!(j == a && !greedy && !bad)) out[j] = tok;
       }
       if (tid == 0) P.accepted[b] = a;
@@ -272,17 +330,18 @@ __device__ void decide(const VerifyParams& P, int b, bool write, ReqDesc& D) {
       ReqDesc d;
       d.a = a;
       d.mode = (bad || greedy) ? kModeNone : (a < K ? kModeResidual : kModeBonus);
-      d.s_hi = s_hi;
-      d.s_lo = s_lo;
+      d.s_hi = d.s_lo = 0.f;
       d.mp = d.sp = d.mq = d.sq = d.u = d.pad = 0.0;
       if (d.mode != kModeNone) {
-        d.mp = (double)sh_m[a];
-        d.sp = sh_s[a];
+        temperature_scale(T, d.s_hi, d.s_lo);
+        d.mp = (double)sh.m[a];
+        d.sp = sh.s[a];
         if (a < K) {
-          d.mq = (double)sh_m[K + 1 + a];
-          d.sq = sh_s[K + 1 + a];
+          d.mq = (double)sh.m[K + 1 + a];
+          d.sq = sh.s[K + 1 + a];
         }
-        d.u = unit_uniform(philox4x32_10(req, (uint32_t)a, P.step, 0u, k0, k1).w[1]);
+        const uint32_t k0 = (uint32_t)(P.seed & 0xffffffffu), k1 = (uint32_t)(P.seed >> 32);
+        d.u = unit_uniform(philox4x32_10((uint32_t)b + P.request_base, (uint32_t)a, P.step, 0u, k0, k1).w[1]);
       }
       D = d;
       if (write) P.desc[b] = d;
@@ -291,14 +350,30 @@ __device__ void decide(const VerifyParams& P, int b, bool write, ReqDesc& D) {
   __syncthreads();
 }
 
+// Between early-exit phases: the accept tests of the phase's positions
+// [ph_lo, ph_lo + ph_nd) for every request still alive; one workgroup per
+// request updates its state.
+template <int ES>
+__global__ __launch_bounds__(kWG) void verify_phase_kernel(VerifyParams P) {
+  __shared__ DecideShared sh;
+  const int b = blockIdx.x;
+  if (P.ph_check && P.state[b] != kStateAlive) return;
+  const int lo = P.ph_lo, hi = P.ph_lo + P.ph_nd;
+  const int a = decide_tests<ES>(P, b, lo, hi, hi, -1, false, true, sh);
+  if (threadIdx.x == 0) P.state[b] = a < 0 ? kStateInvalid : (a < hi ? a : kStateAlive);
+}
+
 template <int ES, bool VEC>
 __global__ __launch_bounds__(kWG) void verify_rowstats_kernel(VerifyParams P) {
+  const int nr = P.ph_nt + P.ph_nd;
   const int c = blockIdx.x % P.C1;
-  const int r = (blockIdx.x / P.C1) % P.R;
-  const int b = blockIdx.x / (P.C1 * P.R);
+  const int lr = (blockIdx.x / P.C1) % nr;
+  const int b = blockIdx.x / (P.C1 * nr);
+  const int r = lr < P.ph_nt ? P.ph_lo + lr : P.K + 1 + P.ph_lo + (lr - P.ph_nt);
   const float T = P.temperature[b];
   const bool greedy = (T == 0.0f);
   if (greedy && r > P.K) return;  // greedy requests read no draft rows
+  if (P.ph_check && P.state[b] != kStateAlive) return;  // stopped in an earlier phase
   const char* row = row_ptr<ES>(P, b, r);
   const int e0 = c * P.chunk1;
   const int e1 = min(P.V, e0 + P.chunk1);
@@ -728,28 +803,49 @@ __global__ __launch_bounds__(kWGD) void verify_draw_kernel(VerifyParams P) {
 
 // --------------------------------------------------------------- launch
 template <int ES, bool VEC>
-static hipError_t launch_typed(const VerifyParams& P, hipEvent_t phase_event, hipStream_t stream) {
-  const int64_t g1 = (int64_t)P.B * P.R * P.C1;
-  const int64_t g2 = (int64_t)P.B * P.C2;
-  hipLaunchKernelGGL((verify_rowstats_kernel<ES, VEC>), dim3((unsigned)g1), dim3(kWG), 0, stream, P);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+static hipError_t launch_typed(VerifyParams P, uint64_t phase_starts, hipEvent_t phase_event,
+                               hipStream_t stream) {
+  const int K = P.K;
+  int lo = 0;
+  for (int j = 0; lo <= K; ++j) {  // phases [lo, hi), the last one ends past target row K
+    int hi = lo + 1;
+    while (hi <= K && !((phase_starts >> hi) & 1u)) ++hi;
+    P.ph_lo = lo;
+    P.ph_nt = hi - lo;
+    P.ph_nd = min(hi, K) - lo;
+    P.ph_check = j > 0;
+    const int64_t g1 = (int64_t)P.B * (P.ph_nt + P.ph_nd) * P.C1;
+    hipLaunchKernelGGL((verify_rowstats_kernel<ES, VEC>), dim3((unsigned)g1), dim3(kWG), 0, stream, P);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if (hi <= K) {
+      hipLaunchKernelGGL((verify_phase_kernel<ES>), dim3((unsigned)P.B), dim3(kWG), 0, stream, P);
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+    P.last_lo = lo;
+    P.phased = j > 0;
+    lo = hi;
+  }
   if (phase_event) {
-    e = hipEventRecord(phase_event, stream);
+    const hipError_t e = hipEventRecord(phase_event, stream);
     if (e != hipSuccess) return e;
   }
+  const int64_t g2 = (int64_t)P.B * P.C2;
   hipLaunchKernelGGL((verify_decide_kernel<ES, VEC>), dim3((unsigned)g2), dim3(kWG), 0, stream, P);
-  e = hipGetLastError();
+  hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((verify_draw_kernel<ES, VEC>), dim3((unsigned)P.B), dim3(kWGD), 0, stream, P);
   return hipGetLastError();
 }
 
-hipError_t launch_verify(const VerifyParams& P, int dtype, bool vec, hipEvent_t phase_event,
-                         hipStream_t stream) {
+hipError_t launch_verify(const VerifyParams& P, int dtype, bool vec, uint64_t phase_starts,
+                         hipEvent_t phase_event, hipStream_t stream) {
   if (dtype == SPEC_BF16)
-    return vec ? launch_typed<2, true>(P, phase_event, stream) : launch_typed<2, false>(P, phase_event, stream);
-  return vec ? launch_typed<4, true>(P, phase_event, stream) : launch_typed<4, false>(P, phase_event, stream);
+    return vec ? launch_typed<2, true>(P, phase_starts, phase_event, stream)
+               : launch_typed<2, false>(P, phase_starts, phase_event, stream);
+  return vec ? launch_typed<4, true>(P, phase_starts, phase_event, stream)
+             : launch_typed<4, false>(P, phase_starts, phase_event, stream);
 }
 
 }  // namespace specv

@@ -25,6 +25,12 @@ struct VerifyParams {
   RowPartial* rowp;
   ReqDesc* desc;
   double* seg;
+  int32_t* state;  // per-request state between early-exit phases
+  // rows of one early-exit phase: target rows [ph_lo, ph_lo + ph_nt), draft
+  // rows [ph_lo, ph_lo + ph_nd); ph_check: skip requests no longer alive
+  int32_t ph_lo, ph_nt, ph_nd, ph_check;
+  // start of the last phase when the rows were read in several phases, else 0
+  int32_t last_lo, phased;
 };
 
 struct ExpandParams {
@@ -48,8 +54,10 @@ struct ExpandParams {
   uint16_t* out_h;
 };
 
-hipError_t launch_verify(const VerifyParams& P, int dtype, bool vec, hipEvent_t phase_event,
-                         hipStream_t stream);
+// phase_starts: bit k (1 <= k <= K) starts an early-exit phase at draft
+// position k; 0 reads every row in one pass.
+hipError_t launch_verify(const VerifyParams& P, int dtype, bool vec, uint64_t phase_starts,
+                         hipEvent_t phase_event, hipStream_t stream);
 hipError_t launch_expand(const ExpandParams& P, bool vec, hipStream_t stream);
 
 }  // namespace specv

@@ -41,12 +41,18 @@ static_assert(sizeof(ReqDesc) == 64, "ReqDesc layout");
 
 enum { kModeNone = 0, kModeResidual = 1, kModeBonus = 2 };
 
+// Request state between the phases of an early-exit verification: >= 0 the
+// request stopped at that draft position, kStateInvalid its data is invalid,
+// kStateAlive every accept test so far passed.
+constexpr int32_t kStateInvalid = -1;
+constexpr int32_t kStateAlive = -2;
+
 struct Layout {
   int32_t R;           // rows per request the row pass may read: K+1 target + K draft
   int32_t C1, chunk1;  // row-pass chunks per row and their length
   int32_t C2, chunk2;  // sampling-pass chunks per row and their length
   int32_t nseg;        // segments per row
-  size_t off_rowp, off_desc, off_seg, total;
+  size_t off_rowp, off_desc, off_seg, off_state, total;
 };
 
 __host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -74,6 +80,8 @@ __host__ __device__ inline Layout make_layout(int32_t B, int32_t K, int32_t V) {
   off = align256(off + (size_t)B * sizeof(ReqDesc));
   L.off_seg = off;
   off = align256(off + (size_t)B * L.nseg * 2 * sizeof(double));
+  L.off_state = off;
+  off = align256(off + (size_t)B * sizeof(int32_t));
   L.total = off;
   return L;
 }

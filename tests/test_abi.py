@@ -102,6 +102,12 @@ def test_verify_argument_errors(sv):
         a = _valid_verify_args(sv)
         setattr(a, field, value)
         assert launch(a) == want, (field, value)
+    # early-exit phases: bit 0 or a bit above K is rejected (K = 3 here); bits 1..K pass validation
+    for mask, want in [(1, sv.SPEC_EINVAL), (1 << 4, sv.SPEC_EINVAL), (1 << 63, sv.SPEC_EINVAL),
+                       ((1 << 1) | (1 << 3), sv.SPEC_EWORKSPACE)]:
+        a = _valid_verify_args(sv)
+        a.phase_starts = mask
+        assert launch(a) == want, mask
     # request stride 0 (shared rows) is accepted by validation
     a = _valid_verify_args(sv)
     a.t_req_stride = a.d_req_stride = 0

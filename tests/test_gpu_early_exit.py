@@ -1,0 +1,169 @@
+"""Early-exit verification on the GPU (rows read in phases, only for requests
+still alive) through the C ABI.
+
+For every case and phase plan the accepted counts and output tokens must be
+bit-identical to the one-pass launch on the same inputs, the debug
+probabilities must equal the one-pass ones on every position whose phase was
+read and be 0 past the phase where the request stopped, and the outputs must
+meet the oracle bar of ``parity.py``.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from parity import Report, compare
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def sv():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import rejection_sampling_verify_03_amd as m
+    return m
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def phase_end(a, mask, K):
+    """End (exclusive) of the phase holding position a under the cut `mask`."""
+    e = a + 1
+    while e <= K and not (mask >> e) & 1:
+        e += 1
+    return e
+
+
+def all_masks(K):
+    return [m << 1 for m in range(1 << K)]
+
+
+def one_vs_phased(sv, inp, mask, seed=0, step=0, x=None, T=None, target=None):
+    x = inp.draft_tokens if x is None else x
+    T = inp.temperature if T is None else T
+    target = inp.target if target is None else target
+    K = x.shape[1]
+    a1, t1, d1 = sv.verify(target, inp.draft, x, T, seed=seed, step=step, debug=True)
+    a2, t2, d2 = sv.verify(target, inp.draft, x, T, seed=seed, step=step, debug=True, phase_starts=mask)
+    torch.cuda.synchronize()
+    a1, t1, d1 = a1.cpu().numpy(), t1.cpu().numpy(), d1.cpu().numpy()
+    a2, t2, d2 = a2.cpu().numpy(), t2.cpu().numpy(), d2.cpu().numpy()
+    assert np.array_equal(a1, a2), ("accepted differ", bin(mask))
+    assert np.array_equal(t1, t2), ("tokens differ", bin(mask))
+    for b in range(len(a1)):
+        if a1[b] < 0:
+            assert (d2[b] == 0).all()
+            continue
+        e = min(phase_end(int(a1[b]), mask, K), K)
+        assert np.array_equal(d1[b, :e], d2[b, :e]), (b, bin(mask))
+        assert (d2[b, e:] == 0).all(), (b, bin(mask))
+    return a2, t2
+
+
+def oracle_check(inp, acc, tok, seed, step, idx=None):
+    rep = Report()
+    if idx is None:
+        compare(workloads.logits_numpy(inp.target), workloads.logits_numpy(inp.draft),
+                inp.draft_tokens.cpu().numpy(), inp.temperature.cpu().numpy(), acc, tok, None,
+                seed=seed, step=step, report=rep)
+    else:
+        for b in idx:
+            compare(workloads.logits_numpy(inp.target[b:b + 1]), workloads.logits_numpy(inp.draft[b:b + 1]),
+                    inp.draft_tokens[b:b + 1].cpu().numpy(), inp.temperature[b:b + 1].cpu().numpy(),
+                    acc[b:b + 1], tok[b:b + 1], None, seed=seed, step=step, request_base=int(b), report=rep)
+    say("  ", rep.summary())
+    assert rep.ok(), rep.failures[:5]
+
+
+def test_every_plan_tiny(sv):
+    """B=4, K=4, V=1024 fp32: all 16 cuts of the positions, 8 steps each."""
+    say("case: early exit, every plan, B4 K4 V1024 fp32")
+    inp = workloads.verify_tiny(seed=0, device="cuda")
+    for mask in all_masks(inp.K):
+        for step in range(8):
+            acc, tok = one_vs_phased(sv, inp, mask, seed=1, step=step)
+            if mask == 0b11110 and step < 2:
+                oracle_check(inp, acc, tok, 1, step)
+
+
+@pytest.mark.parametrize("dtype,V", [(torch.bfloat16, 70001), (torch.float32, 33000)])
+def test_plans_multi_chunk_mixed_temperatures(sv, dtype, V):
+    say("case: early exit B12 K5 V%d %s mixed T" % (V, dtype))
+    inp = workloads.mixture_inputs("mixed B12 K5 V%d" % V, 12, 5, V, dtype, 3, "cuda",
+                                   temps=(0.0, 0.6, 1.0), lam_lo=0.05, lam_hi=0.6)
+    for mask in [1 << 1, 1 << 3, 1 << 5, 0b111110, 0b101010]:
+        for step in range(2):
+            acc, tok = one_vs_phased(sv, inp, mask, seed=5, step=step)
+            oracle_check(inp, acc, tok, 5, step)
+
+
+def test_plans_scalar_path_and_K63(sv):
+    say("case: early exit, scalar path and K=63")
+    inp = workloads.noisy_draft_inputs("scalar V20003", 6, 4, 20003, torch.bfloat16, 1, "cuda", "gauss",
+                                       target_std=2.0, draft_noise=0.5)
+    for mask in [0b11110, 0b00100]:
+        acc, tok = one_vs_phased(sv, inp, mask, step=3)
+        oracle_check(inp, acc, tok, 0, 3)
+    inp = workloads.noisy_draft_inputs("K63", 3, 63, 256, torch.float32, 8, "cuda", "gauss",
+                                       target_std=0.3, draft_noise=0.05)
+    rng = np.random.default_rng(63)
+    some = rng.choice(np.arange(1, 64), 9, replace=False)
+    masks = [(1 << 64) - 2, 1 << 1, 1 << 63, int(sum(1 << int(k) for k in some))]
+    for mask in masks:
+        for step in range(2):
+            acc, tok = one_vs_phased(sv, inp, mask, step=step)
+    oracle_check(inp, acc, tok, 0, 1)
+
+
+def test_invalid_requests_phased(sv):
+    """Invalid tokens anywhere and invalid temperatures are caught by the first
+    decision; a row without a finite normaliser in a phase that is read is
+    caught there."""
+    say("case: early exit, invalid request data")
+    inp = workloads.noisy_draft_inputs("bad", 6, 3, 64, torch.float32, 2, "cuda", "gauss")
+    x = inp.draft_tokens.clone()
+    T = inp.temperature.clone()
+    t = inp.target.clone()
+    x[1, 2] = 64
+    x[2, 0] = -5
+    T[3] = -1.0
+    T[4] = float("nan")
+    t[5, 0, :] = -float("inf")
+    for mask in [0b0010, 0b1110, 0b1000]:
+        acc, tok = one_vs_phased(sv, inp, mask, x=x, T=T, target=t)
+        assert acc[0] >= 0
+        for b in range(1, 6):
+            assert acc[b] == -1 and (tok[b] == -1).all(), (b, bin(mask))
+
+
+def test_headline_planned(sv):
+    """B=256, K=8, V=151936 bf16 as benchmarked: the plan from the measured
+    survival curve of one step, then 3 steps bit-identical to one pass and 24
+    requests against the oracle."""
+    say("case: early exit, headline B256 K8 V151936 with a measured plan")
+    inp = workloads.verify_headline(seed=0, device="cuda")
+    K = inp.K
+    acc, _, _ = sv.verify(inp.target, inp.draft, inp.draft_tokens, inp.temperature, seed=0, step=100)
+    surv = sv.survival_from_accepted(acc.cpu().numpy(), K)
+    f = float((inp.temperature > 0).float().mean())
+    mask = sv.spec_verify_plan_phases(K, surv, f, 0.7)
+    say("  survival", [round(s, 3) for s in surv], "plan", bin(mask))
+    assert mask != 0
+    for step in range(3):
+        acc, tok = one_vs_phased(sv, inp, mask, step=step)
+    rng = np.random.default_rng(2)
+    oracle_check(inp, acc, tok, 0, 2, idx=sorted(rng.choice(inp.B, 24, replace=False)))
+
+
+def test_gptoss_vocab_planned_full_parity(sv):
+    """B=64, K=5, V=201088 bf16: every position its own phase, every request
+    against the oracle."""
+    say("case: early exit, gpt-oss vocab B64 K5 V201088, full parity")
+    inp = workloads.verify_gptoss(seed=0, device="cuda")
+    acc, tok = one_vs_phased(sv, inp, 0b111110, step=0)
+    oracle_check(inp, acc, tok, 0, 0)
