@@ -27,7 +27,7 @@ int verify_check(const spec_verify_args* a) {
   if (a->t_req_stride != 0 && a->t_req_stride < (int64_t)(a->K + 1) * a->t_row_stride) return SPEC_EINVAL;
   if (a->d_req_stride != 0 && a->d_req_stride < (int64_t)a->K * a->d_row_stride) return SPEC_EINVAL;
   const Layout L = make_layout(a->B, a->K, a->V);
-  if ((int64_t)a->B * L.R * L.C1 > INT32_MAX || (int64_t)a->B * L.C2 > INT32_MAX) return SPEC_EINVAL;
+  if ((int64_t)a->B * L.R * L.C1 > INT32_MAX || (int64_t)a->B * L.nseg > INT32_MAX) return SPEC_EINVAL;
   if (!aligned16(a->workspace)) return SPEC_EALIGN;
   if (a->phase_starts & 1u) return SPEC_EINVAL;  // position 0 always starts the first phase
   if (a->K < 63 && (a->phase_starts >> (a->K + 1)) != 0) return SPEC_EINVAL;
@@ -98,8 +98,6 @@ int spec_verify_launch(const spec_verify_args* a, hipStream_t stream) {
   P.R = L.R;
   P.C1 = L.C1;
   P.chunk1 = L.chunk1;
-  P.C2 = L.C2;
-  P.chunk2 = L.chunk2;
   P.nseg = L.nseg;
   P.target = static_cast<const char*>(a->target_logits);
   P.t_req = a->t_req_stride;

@@ -144,6 +144,20 @@ __device__ __forceinline__ RawGroup<ES, VEC> neg_inf_group() {
   return r;
 }
 
+// One logit as stored (bf16 bits zero-extended, or fp32 bits), and its value.
+template <int ES>
+__device__ __forceinline__ uint32_t load_bits(const char* __restrict__ row, int64_t e) {
+  if constexpr (ES == 2)
+    return (uint32_t)reinterpret_cast<const uint16_t*>(row)[e];
+  else
+    return reinterpret_cast<const uint32_t*>(row)[e];
+}
+
+template <int ES>
+__device__ __forceinline__ float bits_to_logit(uint32_t w) {
+  return __uint_as_float(ES == 2 ? w << 16 : w);
+}
+
 template <int ES>
 __device__ __forceinline__ float load_one(const char* __restrict__ row, int64_t e) {
   if constexpr (ES == 2)

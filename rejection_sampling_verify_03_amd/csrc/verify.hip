@@ -7,7 +7,7 @@
 // sampled from p_K.  Temperature 0 is the greedy limit (accept iff x_k is the
 // target argmax, emit the target argmax where the request stops).
 //
-// Three kernels in stream order, no host round trip, and no communication
+// Four kernels in stream order, no host round trip, and no communication
 // between workgroups of one kernel (each kernel boundary makes the previous
 // kernel's writes visible, so no atomics and no cache-maintenance fences):
 //
@@ -17,17 +17,18 @@
 //      non-temporal 16-byte loads, and reduces the chunk to
 //      S * 2^M = sum_v 2^(x_v * s - M) (s = log2(e) / T, M an integer-valued
 //      reference raised by exact power-of-two rescaling) or, for greedy
-//      requests, to (max, lowest argmax).
+//      requests, to (max, lowest argmax).  The chunk holding a position's
+//      draft token also records the logit there.
 //
-//  verify_decide    one workgroup per (request, chunk of ~32K logits): merges
-//      the request's row partials in order and evaluates the K accept tests
-//      in parallel (one lane per position, Philox uniforms, double-precision
-//      p(x), q(x)); a_b is the count of trailing ones of a wavefront ballot.
-//      Every workgroup of a request derives the same decision; the chunk-0
-//      one writes the outputs and a decision record.  Each then streams its
-//      chunk of the sampling row(s) (p_a and q_a, or p_K for the bonus) into
-//      sums of the residual weights max(0, p - q) and of p over 4096-logit
-//      segments, one segment per wave.
+//  verify_decide    one workgroup per request merges its row partials in
+//      chunk order and evaluates the K accept tests in parallel (one lane per
+//      position, Philox uniforms, double-precision p(x), q(x)); a_b is the
+//      count of trailing ones of a wavefront ballot.  Writes the outputs but
+//      the sampled token, and a decision record.
+//
+//  verify_segsum    one wave64 workgroup per (request, 4096-logit segment)
+//      sums the residual weights max(0, p - q) and the weights of p over its
+//      segment of the sampling row(s) (p_a and q_a, or p_K for the bonus).
 //
 //  verify_draw      one 512-thread workgroup per sampled request scans the
 //      segment sums for the inverse-CDF crossing of u' * R, recomputes the
@@ -199,57 +200,98 @@ __device__ __forceinline__ VI block_argmax(VI v) {
 // draw).  Returns, in every thread, a in [lo, hi] (hi: every test in range
 // passed) or -1 for invalid data.  Every draft token and the temperature are
 // checked whatever the range, so invalid tokens are caught by the first
-// decision of a request.  With `debug`, writes p_k(x_k), q_k(x_k) of every
+// decision of a request.  With check_state, a request whose state is not
+// alive returns kNotAlive and writes nothing.  With `debug`, writes p_k(x_k), q_k(x_k) of every
 // tested position, zero for the positions from hi on when the request stopped
 // before hi (their rows are never read) and zero everywhere for invalid data.
 struct DecideShared {
   float m[2 * SPEC_MAX_K + 1];
   double s[2 * SPEC_MAX_K + 1];
+  float z[2 * SPEC_MAX_K + 1];  // logit of the row at its position's draft token
   int g[SPEC_MAX_K + 1];
-  int bad;
   int a;
 };
 
+// Merge the chunk partials of one row in chunk order, the first batch of 8
+// given (loaded by the caller with everything else), later batches loaded 8 at
+// a time.  Sampled rows also return the logit at x recorded by the chunk that
+// holds x (x outside [0, V) leaves z = 0; such a request is invalid).
+constexpr int kPartBatch = 8;
+
+__device__ __forceinline__ void load_partials(const RowPartial* __restrict__ rp, int c0, int C1,
+                                              RowPartial q[kPartBatch]) {
+#pragma unroll
+  for (int i = 0; i < kPartBatch; ++i)
+    if (c0 + i < C1) q[i] = rp[c0 + i];
+}
+
+template <int ES, bool GREEDY>
+__device__ __forceinline__ void merge_row(const VerifyParams& P, const RowPartial* __restrict__ rp,
+                                          RowPartial q[kPartBatch], int x, MS& ms, VI& vi, float& z) {
+  const int cx = (x >= 0 && x < P.V) ? x / P.chunk1 : -1;
+  z = 0.f;
+  for (int c0 = 0; c0 < P.C1; c0 += kPartBatch) {
+    if (c0 > 0) load_partials(rp, c0, P.C1, q);
+#pragma unroll
+    for (int i = 0; i < kPartBatch; ++i) {
+      const int c = c0 + i;
+      if (c >= P.C1) break;
+      if (GREEDY) {
+        const VI v{q[i].m, q[i].idx};
+        vi = c == 0 ? v : vi_pick(vi, v);
+      } else {
+        const MS v{q[i].m, q[i].s};
+        ms = c == 0 ? v : ms_merge(ms, v);
+        if (c == cx) z = bits_to_logit<ES>((uint32_t)q[i].idx);
+      }
+    }
+  }
+}
+
+constexpr int kNotAlive = -3;  // decide_tests: the request stopped in an earlier phase
+
 template <int ES>
 __device__ int decide_tests(const VerifyParams& P, int b, int lo, int hi, int thi, int known, bool invalid,
-                            bool debug, DecideShared& sh) {
+                            bool debug, bool check_state, DecideShared& sh) {
   const int K = P.K;
   const int tid = threadIdx.x;
-  const float T = P.temperature[b];
-  const bool greedy = (T == 0.0f);
   const bool test = known < 0;
-  if (tid == 0) sh.bad = (invalid || !temperature_valid(T)) ? 1 : 0;
-  __syncthreads();
-  int x = 0;
-  float zt_f = 0.f, zq_f = 0.f;
-  if (tid < K) {
-    x = P.tokens[(int64_t)b * K + tid];
-    if (x < 0 || x >= P.V) atomicOr(&sh.bad, 1);
-    if (!greedy && test && tid >= lo && tid < hi) {  // gathered logits, in flight with the partials below
-      const int xc = min(max(x, 0), P.V - 1);        // a bad token makes the request invalid anyway
-      zt_f = load_one<ES>(row_ptr<ES>(P, b, tid), xc);
-      zq_f = load_one<ES>(row_ptr<ES>(P, b, K + 1 + tid), xc);
-    }
-  }
+  // Every load of the prologue is issued before any result is used: the
+  // state (stale and ignored without check_state), the temperature, the
+  // tokens, and the first partials of every row the request may need (draft
+  // rows too, ignored for a greedy request).
+  const int st = P.state[b];
+  const float T = P.temperature[b];
+  const int x = P.tokens[(int64_t)b * K + min(tid, K - 1)];
   const int nt = thi - lo;
-  const int nrows = nt + (greedy ? 0 : min(thi, K) - lo);
-  if (tid < nrows && !invalid) {
-    const int r = tid < nt ? lo + tid : K + 1 + lo + (tid - nt);
-    const RowPartial* rp = P.rowp + ((int64_t)b * P.R + r) * P.C1;
+  const int nd = min(thi, K) - lo;
+  const bool row_thread = tid < nt + nd && !invalid;
+  const int r = tid < nt ? lo + tid : K + 1 + lo + (tid - nt);
+  const int k = tid < nt ? r : r - K - 1;  // position of the row
+  const RowPartial* rp = P.rowp + ((int64_t)b * P.R + (row_thread ? r : 0)) * P.C1;
+  const int xr = P.tokens[(int64_t)b * K + min(k, K - 1)];
+  RowPartial q[kPartBatch];
+  if (row_thread) load_partials(rp, 0, P.C1, q);
+
+  const bool greedy = (T == 0.0f);
+  bool mybad = invalid || !temperature_valid(T) || (tid < K && (x < 0 || x >= P.V));
+  if (row_thread && (!greedy || tid < nt)) {
+    MS ms{0.f, 0.0};
+    VI vi{0.f, 0};
+    float z;
     if (greedy) {
-      VI best{rp[0].m, rp[0].idx};
-      for (int c = 1; c < P.C1; ++c) best = vi_pick(best, VI{rp[c].m, rp[c].idx});
-      sh.g[r] = best.i;
+      merge_row<ES, true>(P, rp, q, -1, ms, vi, z);
+      sh.g[r] = vi.i;
     } else {
-      MS acc{rp[0].m, rp[0].s};
-      for (int c = 1; c < P.C1; ++c) acc = ms_merge(acc, MS{rp[c].m, rp[c].s});
-      sh.m[r] = acc.m;
-      sh.s[r] = acc.s;
-      if (!(acc.s > 0.0 && acc.s <= DBL_MAX && fabsf(acc.m) <= FLT_MAX)) atomicOr(&sh.bad, 1);
+      merge_row<ES, false>(P, rp, q, k < K ? xr : -1, ms, vi, z);
+      sh.m[r] = ms.m;
+      sh.s[r] = ms.s;
+      sh.z[r] = z;
+      mybad |= !(ms.s > 0.0 && ms.s <= DBL_MAX && fabsf(ms.m) <= FLT_MAX);
     }
   }
-  __syncthreads();
-  const bool bad = sh.bad != 0;
+  const bool bad = __syncthreads_or(mybad) != 0;
+  if (check_state && st != kStateAlive) return kNotAlive;  // its partials here were never written
   if (tid < 64) {  // wave 0: one lane per draft position
     bool acc = tid < lo;
     float dp = 0.f, dq = 0.f;
@@ -260,8 +302,8 @@ __device__ int decide_tests(const VerifyParams& P, int b, int lo, int hi, int th
         float s_hi, s_lo;
         temperature_scale(T, s_hi, s_lo);
         const double s_eff = (double)s_hi + (double)s_lo;
-        const double p = exp2((double)zt_f * s_eff - (double)sh.m[tid]) / sh.s[tid];
-        const double q = exp2((double)zq_f * s_eff - (double)sh.m[K + 1 + tid]) / sh.s[K + 1 + tid];
+        const double p = exp2((double)sh.z[tid] * s_eff - (double)sh.m[tid]) / sh.s[tid];
+        const double q = exp2((double)sh.z[K + 1 + tid] * s_eff - (double)sh.m[K + 1 + tid]) / sh.s[K + 1 + tid];
         const double thr = q > 0.0 ? fmin(1.0, p / q) : (p > 0.0 ? 1.0 : 0.0);
         const uint32_t k0 = (uint32_t)(P.seed & 0xffffffffu), k1 = (uint32_t)(P.seed >> 32);
         const Philox4 rr = philox4x32_10((uint32_t)b + P.request_base, (uint32_t)tid, P.step, 0u, k0, k1);
@@ -310,7 +352,7 @@ __device__ void decide(const VerifyParams& P, int b, bool write, ReqDesc& D) {
     }
   }
   const int thi = known >= 0 ? known + 1 : K + 1;
-  const int a = decide_tests<ES>(P, b, lo, K, thi, known, invalid, write, sh);
+  const int a = decide_tests<ES>(P, b, lo, K, thi, known, invalid, write, false, sh);
   const float T = P.temperature[b];
   const bool greedy = (T == 0.0f);
   const bool bad = a < 0;
@@ -357,9 +399,9 @@ template <int ES>
 __global__ __launch_bounds__(kWG) void verify_phase_kernel(VerifyParams P) {
   __shared__ DecideShared sh;
   const int b = blockIdx.x;
-  if (P.ph_check && P.state[b] != kStateAlive) return;
   const int lo = P.ph_lo, hi = P.ph_lo + P.ph_nd;
-  const int a = decide_tests<ES>(P, b, lo, hi, hi, -1, false, true, sh);
+  const int a = decide_tests<ES>(P, b, lo, hi, hi, -1, false, true, P.ph_check != 0, sh);
+  if (a == kNotAlive) return;
   if (threadIdx.x == 0) P.state[b] = a < 0 ? kStateInvalid : (a < hi ? a : kStateAlive);
 }
 
@@ -370,10 +412,21 @@ __global__ __launch_bounds__(kWG) void verify_rowstats_kernel(VerifyParams P) {
   const int lr = (blockIdx.x / P.C1) % nr;
   const int b = blockIdx.x / (P.C1 * nr);
   const int r = lr < P.ph_nt ? P.ph_lo + lr : P.K + 1 + P.ph_lo + (lr - P.ph_nt);
+  const int k = lr < P.ph_nt ? r : r - P.K - 1;  // position of the row
+  // three independent loads, unconditional and all feeding one branch so that
+  // they are issued together (the state of a first phase is stale and
+  // ignored; position K has no token)
   const float T = P.temperature[b];
+  const int st = P.state[b];
+  const int xt = P.tokens[(int64_t)b * P.K + min(k, P.K - 1)];
   const bool greedy = (T == 0.0f);
-  if (greedy && r > P.K) return;  // greedy requests read no draft rows
-  if (P.ph_check && P.state[b] != kStateAlive) return;  // stopped in an earlier phase
+  // skip: draft rows of greedy requests (never read), requests that stopped in
+  // an earlier phase, and rows of a request whose draft token at this
+  // position is out of range (the request is invalid; no statistic is used)
+  const bool skip = (greedy & (r > P.K)) | ((P.ph_check != 0) & (st != kStateAlive)) |
+                    ((k < P.K) & ((uint32_t)xt >= (uint32_t)P.V));
+  if (skip) return;
+  const int x = k < P.K ? xt : -1;
   const char* row = row_ptr<ES>(P, b, r);
   const int e0 = c * P.chunk1;
   const int e1 = min(P.V, e0 + P.chunk1);
@@ -384,11 +437,16 @@ __global__ __launch_bounds__(kWG) void verify_rowstats_kernel(VerifyParams P) {
     part.idx = v.i;
     part.s = 0.0;
   } else {
+    // the logit at the position's draft token, recorded by the chunk holding
+    // it: loaded unconditionally (clamped into the chunk) and kept as loaded,
+    // so that nothing waits for it before the stream below
+    const bool has_x = x >= e0 && x < e1;
+    const uint32_t zbits = load_bits<ES>(row, min(max(x, e0), e1 - 1));
     float s_hi, s_lo;
     temperature_scale(T, s_hi, s_lo);
     const MS v = block_merge_ms(chunk_stats<ES, VEC>(row, e0, e1, s_hi, s_lo));
     part.m = v.m;
-    part.idx = 0;
+    part.idx = has_x ? (int32_t)zbits : 0;
     part.s = v.s;
   }
   if (threadIdx.x == 0) P.rowp[((int64_t)b * P.R + r) * P.C1 + c] = part;
@@ -513,29 +571,40 @@ __device__ __forceinline__ void segment_sums(const char* prow, const char* qrow,
   psum = wave_sum_d(psum);
 }
 
-template <int ES, bool VEC>
+// The final decision of every request: outputs (all but the token the draw
+// samples), debug rows and the decision record; one workgroup per request.
+template <int ES>
 __global__ __launch_bounds__(kWG) void verify_decide_kernel(VerifyParams P) {
-  const int c = blockIdx.x % P.C2;
-  const int b = blockIdx.x / P.C2;
   __shared__ ReqDesc D;
-  decide<ES>(P, b, c == 0, D);
-  if (D.mode == kModeNone) return;
-  const bool res = D.mode == kModeResidual;
-  const char* prow = row_ptr<ES>(P, b, D.a);
-  const char* qrow = res ? row_ptr<ES>(P, b, P.K + 1 + D.a) : prow;
-  const WeightCtx w = make_ctx(D);
-  double* seg = P.seg + (int64_t)b * P.nseg * 2;
-  const int e0 = c * P.chunk2;
-  const int e1 = min(P.V, e0 + P.chunk2);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  for (int s0 = e0 + wave * kSeg; s0 < e1; s0 += kWaves * kSeg) {
-    double rs, ps;
-    if (res) segment_sums<ES, VEC, true>(prow, qrow, w, s0, P.V, rs, ps);
-    else segment_sums<ES, VEC, false>(prow, qrow, w, s0, P.V, rs, ps);
-    if (lane == 0) {
-      seg[2 * (s0 / kSeg) + 0] = rs;
-      seg[2 * (s0 / kSeg) + 1] = ps;
-    }
+  decide<ES>(P, blockIdx.x, true, D);
+}
+
+// A decision record that calls for a draw (anything else samples nothing).
+__device__ __forceinline__ bool desc_samples(const ReqDesc& d, int K) {
+  return (d.mode == kModeResidual && d.a >= 0 && d.a < K) || (d.mode == kModeBonus && d.a == K);
+}
+
+// The sums of one 4096-logit segment of one request's sampling row(s): one
+// wave64 workgroup per (request, segment), so that the hardware dispatcher
+// balances the sampled requests' segments over the compute units (the
+// requests that sample nothing exit after reading their decision record).
+template <int ES, bool VEC>
+__global__ __launch_bounds__(64) void verify_segsum_kernel(VerifyParams P) {
+  const int j = blockIdx.x % P.nseg;
+  const int b = blockIdx.x / P.nseg;
+  const ReqDesc d = P.desc[b];
+  if (!desc_samples(d, P.K)) return;
+  const bool res = d.mode == kModeResidual;
+  const char* prow = row_ptr<ES>(P, b, d.a);
+  const char* qrow = res ? row_ptr<ES>(P, b, P.K + 1 + d.a) : prow;
+  const WeightCtx w = make_ctx(d);
+  double rs, ps;
+  if (res) segment_sums<ES, VEC, true>(prow, qrow, w, j * kSeg, P.V, rs, ps);
+  else segment_sums<ES, VEC, false>(prow, qrow, w, j * kSeg, P.V, rs, ps);
+  if (threadIdx.x == 0) {
+    double* seg = P.seg + ((int64_t)b * P.nseg + j) * 2;
+    seg[0] = rs;
+    seg[1] = ps;
   }
 }
 
@@ -737,13 +806,7 @@ __global__ __launch_bounds__(kWGD) void verify_draw_kernel(VerifyParams P) {
   const bool in0 = tid < nseg;
   const double r0 = in0 ? seg[2 * tid + 0] : 0.0;
   const double p0 = in0 ? seg[2 * tid + 1] : 0.0;
-  if (d.mode == kModeResidual) {
-    if (d.a < 0 || d.a >= P.K) return;
-  } else if (d.mode == kModeBonus) {
-    if (d.a != P.K) return;
-  } else {
-    return;  // greedy or invalid: nothing to sample
-  }
+  if (!desc_samples(d, P.K)) return;  // greedy or invalid: nothing to sample
   __shared__ double sh_base;
   int found = -1, lastpos = -1;
   double base = 0.0, target;
@@ -831,9 +894,12 @@ static hipError_t launch_typed(VerifyParams P, uint64_t phase_starts, hipEvent_t
     const hipError_t e = hipEventRecord(phase_event, stream);
     if (e != hipSuccess) return e;
   }
-  const int64_t g2 = (int64_t)P.B * P.C2;
-  hipLaunchKernelGGL((verify_decide_kernel<ES, VEC>), dim3((unsigned)g2), dim3(kWG), 0, stream, P);
+  hipLaunchKernelGGL((verify_decide_kernel<ES>), dim3((unsigned)P.B), dim3(kWG), 0, stream, P);
   hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t g2 = (int64_t)P.B * P.nseg;
+  hipLaunchKernelGGL((verify_segsum_kernel<ES, VEC>), dim3((unsigned)g2), dim3(64), 0, stream, P);
+  e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((verify_draw_kernel<ES, VEC>), dim3((unsigned)P.B), dim3(kWGD), 0, stream, P);
   return hipGetLastError();

@@ -10,7 +10,7 @@
 namespace specv {
 
 struct VerifyParams {
-  int32_t B, K, V, R, C1, chunk1, C2, chunk2, nseg;
+  int32_t B, K, V, R, C1, chunk1, nseg;
   const char* target;
   int64_t t_req, t_row;
   const char* draft;

@@ -16,13 +16,12 @@ constexpr int kSeg = 64 * 8 * kSegGroups;  // 4096 logits
 // Row pass: one 256-thread workgroup streams ~32K logits of one row, long
 // enough to hide its start-up, still thousands of workgroups per batch.
 constexpr int kRowChunkTarget = 32768;
-// Sampling pass: ~32K logits (8 segments, 2 per wave) per workgroup spreads
-// the 1-2 sampling rows of a request over several compute units.
-constexpr int kSampleChunkTarget = 32768;
 
 struct RowPartial {  // one chunk of one row
   float m;           // integer-valued reference exponent (sampled) or max logit (greedy)
-  int32_t idx;       // argmax index (greedy)
+  int32_t idx;       // argmax index (greedy); sampled rows of draft positions: the logit at
+                     // the position's draft token as stored (bf16 bits zero-extended, or
+                     // fp32 bits) if this chunk holds it, else 0
   double s;          // sum of 2^(x*s - m) over the chunk (sampled)
 };
 
@@ -50,7 +49,6 @@ constexpr int32_t kStateAlive = -2;
 struct Layout {
   int32_t R;           // rows per request the row pass may read: K+1 target + K draft
   int32_t C1, chunk1;  // row-pass chunks per row and their length
-  int32_t C2, chunk2;  // sampling-pass chunks per row and their length
   int32_t nseg;        // segments per row
   size_t off_rowp, off_desc, off_seg, off_state, total;
 };
@@ -71,7 +69,6 @@ __host__ __device__ inline Layout make_layout(int32_t B, int32_t K, int32_t V) {
   Layout L;
   L.R = 2 * K + 1;
   chunking(V, kRowChunkTarget, L.C1, L.chunk1);
-  chunking(V, kSampleChunkTarget, L.C2, L.chunk2);
   L.nseg = (int32_t)(((int64_t)V + kSeg - 1) / kSeg);
   size_t off = 0;
   L.off_rowp = off;
