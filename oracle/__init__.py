@@ -57,6 +57,8 @@ class ExpandArgs(ctypes.Structure):
         ("rejected_mask", ctypes.c_void_p), ("masked_mask", ctypes.c_void_p),
         ("new_token_indices", ctypes.c_void_p), ("hidden_map", ctypes.c_void_p),
         ("out_start", ctypes.c_void_p), ("out_hidden", ctypes.c_void_p),
+        ("block_table", ctypes.c_void_p), ("bt_row_stride", ctypes.c_int64),
+        ("max_blocks", ctypes.c_int32), ("block_size", ctypes.c_int32), ("slot_mapping", ctypes.c_void_p),
     ]
 
 
@@ -258,10 +260,12 @@ class ExpandResult:
 
 
 def expand(in_token_ids, in_positions, in_start, accepted, bonus, K, mask_id,
-           target_hidden=None, mask_hidden=None, hidden_fill=None):
+           target_hidden=None, mask_hidden=None, hidden_fill=None, block_table=None, block_size=0):
     """Run the oracle expansion.  target_hidden: [N_in, H] uint16 (bf16 bits);
     mask_hidden: [H] uint16.  Output rows never written keep ``hidden_fill``
-    (default 0xFFFF) so tests can check that every row was written once."""
+    (default 0xFFFF) so tests can check that every row was written once.
+    block_table: [B, max_blocks] int32 with block_size > 0 adds the KV-cache
+    slot mapping (``slot_mapping``, -7 where unwritten)."""
     ids = _c(in_token_ids, np.int32)
     pos = _c(in_positions, np.int64)
     st = _c(in_start, np.int32)
@@ -274,7 +278,7 @@ def expand(in_token_ids, in_positions, in_start, accepted, bonus, K, mask_id,
         out_token_ids=np.full(N_out, -7, np.int32), out_positions=np.full(N_out, -7, np.int64),
         rejected_mask=np.full(N_out, 7, np.uint8), masked_mask=np.full(N_out, 7, np.uint8),
         new_token_indices=np.full((B, K), -7, np.int32), hidden_map=np.full(N_in, -7, np.int32),
-        out_start=np.full(B + 1, -7, np.int32), out_hidden=None, n_bad=0)
+        out_start=np.full(B + 1, -7, np.int32), out_hidden=None, n_bad=0, slot_mapping=None)
     a = ExpandArgs()
     a.B, a.K, a.N_in, a.mask_id = B, int(K), N_in, int(mask_id)
     a.in_token_ids, a.in_positions, a.in_start, a.accepted, a.bonus = (
@@ -291,6 +295,14 @@ def expand(in_token_ids, in_positions, in_start, accepted, bonus, K, mask_id,
         a.out_hidden = _ptr(r.out_hidden)
     else:
         a.H, a.target_hidden, a.hidden_row_stride, a.mask_hidden, a.out_hidden = 0, None, 0, None, None
+    if block_table is not None:
+        bt = _c(block_table, np.int32)
+        keep.append(bt)
+        r.slot_mapping = np.full(N_out, -7, np.int64)
+        a.block_table, a.bt_row_stride, a.max_blocks, a.block_size = _ptr(bt), bt.shape[1], bt.shape[1], int(block_size)
+        a.slot_mapping = _ptr(r.slot_mapping)
+    else:
+        a.block_table, a.bt_row_stride, a.max_blocks, a.block_size, a.slot_mapping = None, 0, 0, 0, None
     a.out_token_ids, a.out_positions = _ptr(r.out_token_ids), _ptr(r.out_positions)
     a.rejected_mask, a.masked_mask = _ptr(r.rejected_mask), _ptr(r.masked_mask)
     a.new_token_indices, a.hidden_map, a.out_start = (

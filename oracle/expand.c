@@ -16,7 +16,8 @@
  *    sample draft tokens, and the hidden-state mapping.
  *  - "Hidden State 管理": the hidden rows are filled by two statements,
  *    hidden[mapping] = target_hidden, then the masked rows take the learned
- *    placeholder; rejected tokens get the padding slot in the KV mapping.
+ *    placeholder; valid tokens get their normal KV-cache slot and rejected
+ *    tokens the padding slot -1, so that no cache entry is written for them.
  *  - "核心方法" step 2: the drafter input at a position pairs the token of the
  *    next position with the hidden state of this one (inputs shifted by one).
  *
@@ -27,7 +28,9 @@
  * otherwise, clamped at the last input token), at position in_positions[j]+1;
  * slots j > a_b are the rejected ones; the K - 1 MASK slots follow at
  * positions in_positions[a_b] + 1 + m, m = 1..K-1; new-token indices are the
- * bonus slot then the MASK slots.
+ * bonus slot then the MASK slots.  The "normal" slot is the paged-cache one:
+ * logical block pos / block_size of the request through its block table, at
+ * offset pos % block_size; a position without a block maps to -1 as well.
  */
 #include "spec_oracle.h"
 
@@ -42,7 +45,20 @@ static int expand_args_ok(const oracle_expand_args* a) {
     return 0;
   if (a->out_hidden && (!a->target_hidden || !a->mask_hidden || a->hidden_row_stride < a->H))
     return 0;
+  if (a->slot_mapping && (!a->block_table || a->block_size < 1 || a->max_blocks < 0 ||
+                          a->bt_row_stride < a->max_blocks))
+    return 0;
   return 1;
+}
+
+/* KV-cache slot of an output slot at position pos of request b. */
+static int64_t cache_slot(const oracle_expand_args* a, int b, int64_t pos, int rejected) {
+  if (rejected || pos < 0) return -1; /* PADDING_SLOT_ID */
+  const int64_t block = pos / a->block_size;
+  if (block >= a->max_blocks) return -1;
+  const int32_t phys = a->block_table[(int64_t)b * a->bt_row_stride + block];
+  if (phys < 0) return -1;
+  return (int64_t)phys * a->block_size + pos % a->block_size;
 }
 
 static void mark_invalid(const oracle_expand_args* a, int b) {
@@ -80,6 +96,7 @@ int oracle_expand(const oracle_expand_args* a) {
       a->out_positions[o + j] = a->in_positions[s + j] + 1;
       a->rejected_mask[o + j] = (uint8_t)(j > acc);
       a->masked_mask[o + j] = 0;
+      if (a->slot_mapping) a->slot_mapping[o + j] = cache_slot(a, b, a->out_positions[o + j], j > acc);
     }
     for (int m = 1; m <= K - 1; ++m) {
       const int slot = o + n - 1 + m;
@@ -87,6 +104,7 @@ int oracle_expand(const oracle_expand_args* a) {
       a->out_positions[slot] = a->in_positions[s + acc] + 1 + m;
       a->rejected_mask[slot] = 0;
       a->masked_mask[slot] = 1;
+      if (a->slot_mapping) a->slot_mapping[slot] = cache_slot(a, b, a->out_positions[slot], 0);
     }
     a->new_token_indices[(int64_t)b * K + 0] = o + acc;
     for (int m = 1; m <= K - 1; ++m) a->new_token_indices[(int64_t)b * K + m] = o + n - 1 + m;

@@ -120,9 +120,24 @@ typedef struct {
   int32_t* hidden_map;               /* [N_in] */
   int32_t* out_start;                /* [B+1] */
   uint16_t* out_hidden;              /* nullable [N_out, H] */
+  /* KV-cache slot mapping (nullable slot_mapping skips it): paged cache of
+   * block_size slots per block, block_table[b, i] = physical block of the
+   * request's logical block i (i < max_blocks; row stride bt_row_stride) */
+  const int32_t* block_table;
+  int64_t bt_row_stride;
+  int32_t max_blocks;
+  int32_t block_size;
+  int64_t* slot_mapping;             /* nullable [N_out] */
 } oracle_expand_args;
 
-/* Returns the number of requests with invalid data (n_b < 1, a window
+/* Slot mapping ("P-EAGLE" page, section "Hidden State 管理": valid tokens get
+ * their normal KV-cache slot, rejected ones PADDING_SLOT_ID = -1 so that
+ * nothing is written to the cache for them): an output slot at position pos of
+ * request b maps to block_table[b, pos / block_size] * block_size +
+ * pos % block_size, or -1 when it is rejected or its position has no block
+ * (pos < 0, pos / block_size >= max_blocks, or a negative table entry).
+ *
+ * Returns the number of requests with invalid data (n_b < 1, a window
  * outside [0, N_in], accepted out of range); such a request writes only its
  * new-token indices, all -1.  If in_start[0] != 0 or in_start[B] != N_in every
  * request is invalid in that way and out_start is not written.  -1 on bad

@@ -20,25 +20,73 @@ import workloads
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
 
-def _run(inp, with_hidden=True):
+def _run(inp, with_hidden=True, block_table=None, block_size=0):
     return oracle.expand(
         inp.in_token_ids.numpy(), inp.in_positions.numpy(), inp.in_start.numpy(),
         inp.accepted.numpy(), inp.bonus.numpy(), inp.K, inp.mask_id,
         workloads.bf16_bits(inp.target_hidden) if with_hidden else None,
-        workloads.bf16_bits(inp.mask_hidden) if with_hidden else None)
+        workloads.bf16_bits(inp.mask_hidden) if with_hidden else None,
+        block_table=None if block_table is None else block_table.numpy(), block_size=block_size)
 
 
 def test_hand_worked_example():
     with open(os.path.join(GOLDEN, "expand_worked_example.json")) as f:
         ex = json.load(f)
     r = oracle.expand(ex["in_token_ids"], ex["in_positions"], ex["in_start"], ex["accepted"],
-                      ex["bonus"], ex["K"], ex["mask_id"])
+                      ex["bonus"], ex["K"], ex["mask_id"], block_table=ex["block_table"],
+                      block_size=ex["block_size"])
     e = ex["expected"]
     assert r.n_bad == 0
     for key in ("out_start", "out_token_ids", "out_positions", "rejected_mask", "masked_mask",
-                "hidden_map"):
+                "hidden_map", "slot_mapping"):
         assert list(getattr(r, key)) == e[key], key
     assert r.new_token_indices.tolist() == e["new_token_indices"]
+    # without a block table nothing else changes
+    r2 = oracle.expand(ex["in_token_ids"], ex["in_positions"], ex["in_start"], ex["accepted"],
+                       ex["bonus"], ex["K"], ex["mask_id"])
+    assert r2.slot_mapping is None and list(r2.out_token_ids) == e["out_token_ids"]
+
+
+def test_hand_worked_slot_edge_cases():
+    """Positions past the block table or in a block marked -1 get no slot."""
+    with open(os.path.join(GOLDEN, "expand_worked_example.json")) as f:
+        cases = json.load(f)["slot_edge_cases"]
+    for c in cases:
+        r = oracle.expand(c["in_token_ids"], c["in_positions"], c["in_start"], c["accepted"], c["bonus"],
+                          c["K"], c["mask_id"], block_table=c["block_table"], block_size=c["block_size"])
+        assert list(r.slot_mapping) == c["expected_slot_mapping"], c["why"]
+
+
+@pytest.mark.parametrize("block_size", [1, 16])
+def test_slot_mapping_invariants(block_size):
+    """Rejected slots and only they get -1 when every position has a block;
+    every other slot lies in the block the table gives for its position, at
+    the position's offset, and no two slots of the batch share a cache slot
+    unless they share a request and a position."""
+    inp = workloads.expand_inputs(B=64, K=6, H=8, seed=5, max_offset=300)
+    max_blocks = (300 + 2 * 6 + 2) // block_size + 1
+    bt = workloads.block_tables(64, max_blocks, seed=6)
+    r = _run(inp, with_hidden=False, block_table=bt, block_size=block_size)
+    sm = r.slot_mapping
+    rej = r.rejected_mask.astype(bool)
+    assert ((sm == -1) == rej).all()
+    btn = bt.numpy()
+    owner = np.repeat(np.arange(64), np.diff(r.out_start))
+    pos = r.out_positions
+    v = ~rej
+    np.testing.assert_array_equal(sm[v] // block_size, btn[owner[v], pos[v] // block_size])
+    np.testing.assert_array_equal(sm[v] % block_size, pos[v] % block_size)
+    keys = set()
+    for s_, b_, p_ in zip(sm[v], owner[v], pos[v]):
+        keys.add((int(s_), int(b_), int(p_)))
+    assert len({k[0] for k in keys}) == len({(k[1], k[2]) for k in keys})
+    # blocks marked -1 leave their positions without a slot, and nothing else changes
+    bt2 = workloads.block_tables(64, max_blocks, seed=6, unmapped_fraction=0.3)
+    r2 = _run(inp, with_hidden=False, block_table=bt2, block_size=block_size)
+    blk = pos // block_size
+    hole = bt2.numpy()[owner, blk] != btn[owner, blk]
+    np.testing.assert_array_equal(r2.slot_mapping[hole], -1)
+    np.testing.assert_array_equal(r2.slot_mapping[~hole], sm[~hole])
 
 
 def check_invariants(inp, r):

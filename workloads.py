@@ -253,6 +253,18 @@ def expand_inputs(B=512, K=8, H=HIDDEN_GPT_OSS_20B, vocab=GPT_OSS_VOCAB, seed=0,
         target_hidden=hidden, mask_hidden=mask_hidden)
 
 
+def block_tables(B, max_blocks, seed, device="cpu", unmapped_fraction=0.0):
+    """A synthetic paged-KV block table [B, max_blocks] int32: every entry a
+    distinct physical block (a random permutation of 0..B*max_blocks-1), and
+    a ``unmapped_fraction`` of entries set to -1 (no block)."""
+    g = _gen(seed, device)
+    perm = torch.randperm(B * max_blocks, generator=g, device=device).to(torch.int32).reshape(B, max_blocks)
+    if unmapped_fraction > 0:
+        drop = torch.rand(B, max_blocks, generator=g, device=device) < unmapped_fraction
+        perm = torch.where(drop, torch.full_like(perm, -1), perm)
+    return perm.contiguous()
+
+
 def bf16_bits(t):
     """uint16 numpy view of a bfloat16 tensor (copied to the CPU)."""
     import numpy as np
