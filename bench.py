@@ -3,8 +3,9 @@
 A step = one verification of the headline batch (B=256 requests, K=8 drafts,
 V=151936 bf16 logits, temperatures drawn from {0, 0.6, 1}, mixture drafts)
 followed by the P-EAGLE expansion of the same batch (hidden width 2880, the
-bonus read from the verification's output tokens), both through the C ABI on
-torch's current stream.  Inputs are generated once on the GPU and stay resident
+bonus read from the verification's output tokens, KV-cache slot mapping
+through a 16-slot-per-block table), both through the C ABI on torch's current
+stream.  Inputs are generated once on the GPU and stay resident
 in HBM; each timed step uses a new Philox step counter.
 
 By default the verification reads its rows in early-exit phases (rows of a
@@ -92,11 +93,15 @@ PLAN_STEPS = 8  # one-pass steps whose accepted counts give the survival curve
 
 
 def algorithmic_expand_bytes(B, K, H, n_in):
+    """Hidden rows read and written once, metadata in and out, and the slot
+    mapping (one block-table entry read and one int64 slot written per output
+    slot)."""
     n_out = n_in + B * (K - 1)
     hidden = n_in * H * 2 + H * 2 + n_out * H * 2
     meta_in = n_in * (4 + 8) + (B + 1) * 4 + B * 4 + B * 4
     meta_out = n_out * (4 + 8 + 1 + 1) + B * K * 4 + n_in * 4 + (B + 1) * 4
-    return hidden + meta_in + meta_out
+    slots = n_out * (4 + 8)
+    return hidden + meta_in + meta_out + slots
 
 
 ROWPASS_SOURCES = ["rejection_sampling_verify_03_amd/csrc/verify.hip", "rejection_sampling_verify_03_amd/csrc/device_common.hpp",
@@ -188,11 +193,14 @@ def main():
     accepted = torch.empty(B, dtype=torch.int32, device=dev)
     tokens = torch.empty(B, K + 1, dtype=torch.int32, device=dev)
     ws = sv.make_workspace(B, K, V, dev)
-    out = sv.expand_outputs(B, K, B * (K + 1), H, dev)
+    out = sv.expand_outputs(B, K, B * (K + 1), H, dev, with_slots=True)
+    # paged KV cache of 16-slot blocks covering every position of the batch
+    block_size = 16
+    block_table = workloads.block_tables(B, (16384 + 2 * K + 2) // block_size + 1, seed=args.seed + 2, device=dev)
     stream = torch.cuda.current_stream()
     sptr = stream.cuda_stream
     ex_args = sv.expand_args(in_ids, in_pos, in_start, accepted, None, K, mask_id, hidden, mask_hidden, out,
-                             verify_tokens=tokens)
+                             verify_tokens=tokens, block_table=block_table, block_size=block_size)
 
     n_events = args.steps
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(n_events)]
@@ -284,7 +292,7 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": "headline verify B=256 K=8 V=151936 bf16, T in {0,0.6,1}, mixture drafts "
-                               "+ P-EAGLE expand H=2880 chained on the verify outputs",
+                               "+ P-EAGLE expand H=2880 with KV slot mapping, chained on the verify outputs",
                    "B": B, "K": K, "V": V, "H": H, "sampled_requests": int((temps > 0).sum())},
         "roofline": {"kernel": "verify_rowstats", "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,

@@ -159,6 +159,13 @@ int spec_verify_launch(const spec_verify_args* args, hipStream_t stream);
  *   slot o_b+n_b-1+m, m = 1..K-1: MASK id, position
  *     in_positions[in_start[b]+a] + 1 + m, masked, hidden = mask_hidden;
  *   new_token_indices[b] = {o_b + a, o_b + n_b, ..., o_b + n_b + K - 2}.
+ * KV-cache slot mapping (same page, section "Hidden State 管理": valid tokens
+ * get their normal slot, rejected tokens PADDING_SLOT_ID = -1 so that nothing
+ * is written to the cache for them): slot o_b+j at position pos maps to
+ *   block_table[b, pos / block_size] * block_size + pos % block_size,
+ * or -1 when the slot is rejected or pos has no block (pos < 0,
+ * pos / block_size >= max_blocks, or a negative table entry).  MASK slots are
+ * drafter positions and get their slot.
  * A request with n_b < 1, a window outside [0, N_in] or a outside
  * [0, n_b - 1] (or above K when the bonus comes from verify_output_tokens)
  * writes only new_token_indices[b, :] = -1.  If in_start[0] != 0
@@ -191,6 +198,12 @@ typedef struct {
   int32_t* hidden_map;            /* device out [N_in] */
   int32_t* out_start;             /* device out [B+1] */
   uint16_t* out_hidden;           /* device out bf16 bits [N_out, H], or NULL to skip the gather */
+  /* KV-cache slot mapping (all four inputs ignored when slot_mapping is NULL) */
+  const int32_t* block_table;     /* device [B, >= max_blocks] physical block ids (< 0: none) */
+  int64_t bt_row_stride;          /* elements between requests' rows, >= max_blocks */
+  int32_t max_blocks;             /* logical blocks per request in the table, >= 0 */
+  int32_t block_size;             /* cache slots per block, >= 1 */
+  int64_t* slot_mapping;          /* device out [N_out], or NULL */
 } spec_expand_args;
 
 /* Enqueue one expansion (metadata and, if out_hidden != NULL, the hidden-row

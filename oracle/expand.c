@@ -45,7 +45,7 @@ static int expand_args_ok(const oracle_expand_args* a) {
     return 0;
   if (a->out_hidden && (!a->target_hidden || !a->mask_hidden || a->hidden_row_stride < a->H))
     return 0;
-  if (a->slot_mapping && (!a->block_table || a->block_size < 1 || a->max_blocks < 0 ||
+  if (a->slot_mapping && ((!a->block_table && a->max_blocks > 0) || a->block_size < 1 || a->max_blocks < 0 ||
                           a->bt_row_stride < a->max_blocks))
     return 0;
   return 1;

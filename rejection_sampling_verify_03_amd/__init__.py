@@ -50,6 +50,8 @@ class SpecExpandArgs(ctypes.Structure):
         ("rejected_mask", ctypes.c_void_p), ("masked_mask", ctypes.c_void_p),
         ("new_token_indices", ctypes.c_void_p), ("hidden_map", ctypes.c_void_p),
         ("out_start", ctypes.c_void_p), ("out_hidden", ctypes.c_void_p),
+        ("block_table", ctypes.c_void_p), ("bt_row_stride", ctypes.c_int64),
+        ("max_blocks", ctypes.c_int32), ("block_size", ctypes.c_int32), ("slot_mapping", ctypes.c_void_p),
     ]
 
 
@@ -223,10 +225,11 @@ class ExpandOutputs:
         self.__dict__.update(kw)
 
 
-def expand_outputs(B, K, N_in, H, device, with_hidden=True):
+def expand_outputs(B, K, N_in, H, device, with_hidden=True, with_slots=False):
     torch = _torch()
     N_out = N_in + B * (K - 1)
     return ExpandOutputs(
+        slot_mapping=torch.empty(N_out, dtype=torch.int64, device=device) if with_slots else None,
         out_token_ids=torch.empty(N_out, dtype=torch.int32, device=device),
         out_positions=torch.empty(N_out, dtype=torch.int64, device=device),
         rejected_mask=torch.empty(N_out, dtype=torch.uint8, device=device),
@@ -238,9 +241,11 @@ def expand_outputs(B, K, N_in, H, device, with_hidden=True):
 
 
 def expand_args(in_token_ids, in_positions, in_start, accepted, bonus, K, mask_id, target_hidden,
-                mask_hidden, out, verify_tokens=None):
+                mask_hidden, out, verify_tokens=None, block_table=None, block_size=0):
     """bonus: [B] int32, or None with verify_tokens = the [B, K+1] output
-    tokens of a verification (the bonus is then read at the accepted count)."""
+    tokens of a verification (the bonus is then read at the accepted count).
+    block_table: [B, max_blocks] int32 (row stride free, unit column stride)
+    with block_size, when out.slot_mapping is given."""
     torch = _torch()
     _check_dev(in_token_ids, in_positions, in_start, accepted, bonus, target_hidden, mask_hidden)
     for t, dt in ((in_token_ids, torch.int32), (in_positions, torch.int64), (in_start, torch.int32),
@@ -265,6 +270,17 @@ def expand_args(in_token_ids, in_positions, in_start, accepted, bonus, K, mask_i
         a.out_hidden = out.out_hidden.data_ptr()
     else:
         a.H, a.target_hidden, a.hidden_row_stride, a.mask_hidden, a.out_hidden = 0, None, 0, None, None
+    if getattr(out, "slot_mapping", None) is not None:
+        if block_table is None or block_table.dtype != torch.int32 or block_table.stride(-1) != 1:
+            raise ValueError("slot mapping needs an int32 block table with unit column stride")
+        _check_dev(block_table)
+        a.block_table = block_table.data_ptr()
+        a.bt_row_stride = block_table.stride(0)
+        a.max_blocks = block_table.shape[1]
+        a.block_size = int(block_size)
+        a.slot_mapping = out.slot_mapping.data_ptr()
+    else:
+        a.block_table, a.bt_row_stride, a.max_blocks, a.block_size, a.slot_mapping = None, 0, 0, 0, None
     a.out_token_ids, a.out_positions = out.out_token_ids.data_ptr(), out.out_positions.data_ptr()
     a.rejected_mask, a.masked_mask = out.rejected_mask.data_ptr(), out.masked_mask.data_ptr()
     a.new_token_indices, a.hidden_map = out.new_token_indices.data_ptr(), out.hidden_map.data_ptr()
@@ -273,15 +289,16 @@ def expand_args(in_token_ids, in_positions, in_start, accepted, bonus, K, mask_i
 
 
 def expand(in_token_ids, in_positions, in_start, accepted, bonus, K, mask_id, target_hidden=None,
-           mask_hidden=None, stream=None, out=None, verify_tokens=None):
-    """One expansion on torch's current stream; returns an ExpandOutputs."""
+           mask_hidden=None, stream=None, out=None, verify_tokens=None, block_table=None, block_size=0):
+    """One expansion on torch's current stream; returns an ExpandOutputs
+    (with slot_mapping when a block table is given)."""
     B = accepted.shape[0]
     H = target_hidden.shape[1] if target_hidden is not None else 0
     if out is None:
         out = expand_outputs(B, K, in_token_ids.shape[0], H, accepted.device,
-                             with_hidden=target_hidden is not None)
+                             with_hidden=target_hidden is not None, with_slots=block_table is not None)
     a = expand_args(in_token_ids, in_positions, in_start, accepted, bonus, K, mask_id, target_hidden,
-                    mask_hidden, out, verify_tokens)
+                    mask_hidden, out, verify_tokens, block_table=block_table, block_size=block_size)
     rc = spec_expand_launch(a, _stream_ptr(stream))
     if rc != SPEC_OK:
         raise SpecError(rc)

@@ -49,6 +49,10 @@ int expand_check(const spec_expand_args* a) {
     if (a->H > 0 && (!a->mask_hidden || (a->N_in > 0 && !a->target_hidden))) return SPEC_EINVAL;
     if (a->hidden_row_stride < a->H) return SPEC_EINVAL;
   }
+  if (a->slot_mapping) {
+    if (a->block_size < 1 || a->max_blocks < 0 || a->bt_row_stride < a->max_blocks) return SPEC_EINVAL;
+    if (a->max_blocks > 0 && !a->block_table) return SPEC_EINVAL;
+  }
   return SPEC_OK;
 }
 
@@ -164,6 +168,11 @@ int spec_expand_launch(const spec_expand_args* a, hipStream_t stream) {
   P.hmap = a->hidden_map;
   P.out_start = a->out_start;
   P.out_h = (a->H > 0) ? a->out_hidden : nullptr;
+  P.slots = a->slot_mapping;
+  P.bt = a->block_table;
+  P.bt_stride = a->bt_row_stride;
+  P.max_blocks = a->slot_mapping ? a->max_blocks : 0;
+  P.block_size = a->slot_mapping ? a->block_size : 1;
   const bool vec = (a->H % 8) == 0 && (a->hidden_row_stride % 8) == 0 && aligned16(a->target_hidden) &&
                    aligned16(a->mask_hidden) && aligned16(a->out_hidden);
   return launch_expand(P, vec, stream) == hipSuccess ? SPEC_OK : SPEC_ELAUNCH;

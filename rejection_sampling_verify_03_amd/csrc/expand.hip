@@ -12,6 +12,11 @@
 // written exactly once as a gather, which gives the same rows because the
 // mapping is injective and, with the MASK slots, covers the output.
 //
+// With a block table, each output slot also gets its KV-cache slot in the
+// paged cache (block_table[b, pos / block_size] * block_size + pos %
+// block_size), and rejected slots, or positions with no block, get
+// PADDING_SLOT_ID = -1 ("Hidden State 管理": no cache write for them).
+//
 // Request b owns the fixed window of n_b + K - 1 slots starting at
 // in_start[b] + b*(K-1), so no scan is needed; G workgroups share a request's
 // window row-interleaved, each writing the metadata of its rows and copying
@@ -20,6 +25,15 @@
 #include "verify_kernels.hpp"
 
 namespace specv {
+
+// KV-cache slot of output slot position pos of request b (-1: none).
+__device__ __forceinline__ int64_t cache_slot(const ExpandParams& P, int b, int64_t pos, bool rejected) {
+  if (rejected || pos < 0) return -1;
+  const int64_t blk = pos / P.block_size;
+  if (blk >= P.max_blocks) return -1;
+  const int32_t phys = P.bt[(int64_t)b * P.bt_stride + blk];
+  return phys < 0 ? -1 : (int64_t)phys * P.block_size + pos % P.block_size;
+}
 
 constexpr int kCopyBatch = 8;  // 16-byte cells per lane loaded before any is stored
 
@@ -90,21 +104,27 @@ __global__ __launch_bounds__(kWG) void expand_kernel(ExpandParams P) {
   const int bonus = P.vtok ? P.vtok[(int64_t)b * (K + 1) + a] : P.bonus[b];
   for (int r = g + P.G * tid; r < Wb; r += P.G * kWG) {
     const int slot = o + r;
+    int64_t pos;
+    bool rejected;
     if (r < n) {
+      pos = P.pos[s + r] + 1;
+      rejected = r > a;
       P.hmap[s + r] = slot;
       P.out_ids[slot] = (r == a) ? bonus : P.ids[s + min(r + 1, n - 1)];
-      P.out_pos[slot] = P.pos[s + r] + 1;
-      P.rej[slot] = (uint8_t)(r > a);
+      P.rej[slot] = (uint8_t)rejected;
       P.msk[slot] = 0;
       if (r == a) P.nti[(int64_t)b * K] = slot;
     } else {
       const int m = r - n + 1;  // 1..K-1
+      pos = P.pos[s + a] + 1 + m;
+      rejected = false;
       P.out_ids[slot] = P.mask_id;
-      P.out_pos[slot] = P.pos[s + a] + 1 + m;
       P.rej[slot] = 0;
       P.msk[slot] = 1;
       P.nti[(int64_t)b * K + m] = slot;
     }
+    P.out_pos[slot] = pos;
+    if (P.slots) P.slots[slot] = cache_slot(P, b, pos, rejected);
   }
 }
 

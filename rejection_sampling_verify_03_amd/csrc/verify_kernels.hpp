@@ -52,6 +52,10 @@ struct ExpandParams {
   int32_t* hmap;
   int32_t* out_start;
   uint16_t* out_h;
+  const int32_t* bt;  // block table (slot mapping) or null
+  int64_t bt_stride;
+  int32_t max_blocks, block_size;
+  int64_t* slots;     // slot mapping out, or null
 };
 
 // phase_starts: bit k (1 <= k <= K) starts an early-exit phase at draft

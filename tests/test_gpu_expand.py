@@ -1,6 +1,6 @@
 """GPU P-EAGLE expansion through the C ABI against the CPU oracle: every output
 bit-exact (token ids, positions, masks, new-token indices, hidden map, start
-indices and the gathered hidden rows)."""
+indices, KV-cache slot mapping and the gathered hidden rows)."""
 import sys
 
 import numpy as np
@@ -31,18 +31,30 @@ def to_dev(e):
     return e
 
 
-def run_both(sv, e, with_hidden=True, accepted=None, in_start=None, hidden=None):
+def run_both(sv, e, with_hidden=True, accepted=None, in_start=None, hidden=None, block_table=None,
+             block_size=0):
     acc = e.accepted if accepted is None else accepted
     st = e.in_start if in_start is None else in_start
     th = (e.target_hidden if hidden is None else hidden) if with_hidden else None
     out = sv.expand(e.in_token_ids, e.in_positions, st, acc, e.bonus, e.K, e.mask_id, th,
-                    e.mask_hidden if with_hidden else None)
+                    e.mask_hidden if with_hidden else None, block_table=block_table, block_size=block_size)
     torch.cuda.synchronize()
     ref = oracle.expand(e.in_token_ids.cpu().numpy(), e.in_positions.cpu().numpy(), st.cpu().numpy(),
                         acc.cpu().numpy(), e.bonus.cpu().numpy(), e.K, e.mask_id,
                         workloads.bf16_bits(th) if with_hidden else None,
-                        workloads.bf16_bits(e.mask_hidden) if with_hidden else None)
+                        workloads.bf16_bits(e.mask_hidden) if with_hidden else None,
+                        block_table=None if block_table is None else block_table.cpu().numpy(),
+                        block_size=block_size)
     return out, ref
+
+
+def table_for(e, block_size, seed, unmapped_fraction=0.0, max_blocks=None):
+    """A block table covering every position of the batch (or max_blocks)."""
+    if max_blocks is None:
+        top = int(e.in_positions.max()) + e.K + 2
+        max_blocks = top // block_size + 1
+    return workloads.block_tables(e.B, max_blocks, seed=seed, device="cuda",
+                                  unmapped_fraction=unmapped_fraction)
 
 
 def assert_same(out, ref, with_hidden=True, valid_rows=None):
@@ -57,6 +69,8 @@ def assert_same(out, ref, with_hidden=True, valid_rows=None):
         np.testing.assert_array_equal(getattr(out, name).cpu().numpy()[mask], getattr(ref, name)[mask], name)
     hm_mask = ref.hidden_map != -7
     np.testing.assert_array_equal(out.hidden_map.cpu().numpy()[hm_mask], ref.hidden_map[hm_mask])
+    if ref.slot_mapping is not None:
+        np.testing.assert_array_equal(out.slot_mapping.cpu().numpy()[mask], ref.slot_mapping[mask], "slots")
     if with_hidden:
         got = workloads.bf16_bits(out.out_hidden)
         np.testing.assert_array_equal(got[mask], ref.out_hidden[mask])
@@ -72,6 +86,31 @@ def test_full_size_expand(sv):
         out, ref = run_both(sv, e)
         assert ref.n_bad == 0
         assert_same(out, ref)
+    # with the KV-cache slot mapping through a paged block table of 16 slots per block
+    out, ref = run_both(sv, e, block_table=table_for(e, 16, seed=7), block_size=16)
+    assert_same(out, ref)
+    sm = out.slot_mapping.cpu().numpy()
+    assert ((sm == -1) == out.rejected_mask.cpu().numpy().astype(bool)).all()
+
+
+def test_slot_mapping_edges(sv):
+    """Unmapped blocks, positions past the table, one slot per block, and a
+    block table inside a wider buffer."""
+    say("case: expand slot mapping edges")
+    e = workloads.expand_inputs(B=100, K=5, H=16, seed=11, device="cuda", max_offset=200)
+    for bs, frac, mb in [(16, 0.3, None), (1, 0.0, None), (4, 0.0, 30), (7, 0.2, 12)]:
+        bt = table_for(e, bs, seed=bs, unmapped_fraction=frac, max_blocks=mb)
+        out, ref = run_both(sv, e, block_table=bt, block_size=bs)
+        assert_same(out, ref)
+    wide = torch.full((e.B, 64), 5, dtype=torch.int32, device="cuda")
+    bt = table_for(e, 16, seed=3)
+    wide[:, :bt.shape[1]] = bt
+    out, ref = run_both(sv, e, block_table=wide[:, :bt.shape[1]], block_size=16)
+    assert_same(out, ref)
+    # no logical block at all: every slot -1
+    out, ref = run_both(sv, e, block_table=wide[:, :0], block_size=16)
+    assert_same(out, ref)
+    assert (out.slot_mapping.cpu().numpy()[ref.out_token_ids != -7] == -1).all()
 
 
 @pytest.mark.parametrize("K,H", [(1, 64), (2, 2880), (5, 100), (8, 7), (63, 16)])
@@ -144,3 +183,71 @@ def test_chained_after_verify(sv):
                         a, bonus, K, e.mask_id, workloads.bf16_bits(e.target_hidden),
                         workloads.bf16_bits(e.mask_hidden))
     assert_same(out, ref)
+
+
+def test_chained_step_graph_capture(sv):
+    """verify (early-exit phases) -> expand (bonus from the verify tokens, KV
+    slot mapping) chained on one stream with no host round trip, captured
+    into a HIP graph and replayed: every replay, with eager work and a reset
+    of the outputs between replays, must reproduce the eager outputs."""
+    say("case: chained verify -> expand, graph capture")
+    dev = torch.device("cuda")
+    vin = workloads.mixture_inputs("chain B64 K8 V32768", 64, 8, 32768, torch.bfloat16, 12, dev,
+                                   temps=(0.0, 0.6, 1.0), lam_lo=0.05, lam_hi=0.6)
+    B, K, V = vin.B, vin.K, vin.V
+    e = workloads.expand_inputs(B=B, K=K, H=256, seed=12, device="cuda")
+    bt = table_for(e, 16, seed=12)
+    acc = torch.empty(B, dtype=torch.int32, device=dev)
+    tok = torch.empty(B, K + 1, dtype=torch.int32, device=dev)
+    ws = sv.make_workspace(B, K, V, dev)
+    out = sv.expand_outputs(B, K, e.N_in, e.H, dev, with_slots=True)
+    va = sv.verify_args(vin.target, vin.draft, vin.draft_tokens, vin.temperature, acc, tok, None, ws,
+                        seed=21, step=3, phase_starts=0b100100)
+    xa = sv.expand_args(e.in_token_ids, e.in_positions, e.in_start, acc, None, K, e.mask_id, e.target_hidden,
+                        e.mask_hidden, out, verify_tokens=tok, block_table=bt, block_size=16)
+
+    def step(stream):
+        assert sv.spec_verify_launch(va, stream.cuda_stream) == sv.SPEC_OK
+        assert sv.spec_expand_launch(xa, stream.cuda_stream) == sv.SPEC_OK
+
+    names = ("out_token_ids", "out_positions", "rejected_mask", "masked_mask", "new_token_indices",
+             "hidden_map", "out_start", "out_hidden", "slot_mapping")
+
+    def snapshot():
+        return [acc.clone(), tok.clone()] + [getattr(out, n).clone() for n in names]
+
+    def reset():
+        acc.fill_(-5)
+        tok.fill_(-5)
+        for n in names:
+            getattr(out, n).zero_()
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step(s)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    eager = snapshot()
+    # the chained outputs against the oracle: the bonus is the verify's token at a
+    a = acc.cpu().numpy()
+    bonus = tok.cpu().numpy()[np.arange(B), a]
+    ref = oracle.expand(e.in_token_ids.cpu().numpy(), e.in_positions.cpu().numpy(), e.in_start.cpu().numpy(),
+                        a, bonus, K, e.mask_id, workloads.bf16_bits(e.target_hidden),
+                        workloads.bf16_bits(e.mask_hidden), block_table=bt.cpu().numpy(), block_size=16)
+    assert_same(out, ref)
+
+    g = torch.cuda.CUDAGraph()
+    reset()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        step(torch.cuda.current_stream())
+    for rep in range(4):
+        x = torch.randn(1 << 20, device=dev)
+        float(x.sum())  # eager work and a synchronisation between replays
+        reset()
+        g.replay()
+        torch.cuda.synchronize()
+        for i, (u, v) in enumerate(zip(snapshot(), eager)):
+            assert torch.equal(u, v), (rep, i)
+    say("  %d replays identical to the eager step" % 4)
