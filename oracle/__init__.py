@@ -62,6 +62,16 @@ class ExpandArgs(ctypes.Structure):
     ]
 
 
+class DraftArgs(ctypes.Structure):
+    _fields_ = [
+        ("B", ctypes.c_int32), ("K", ctypes.c_int32), ("V", ctypes.c_int32), ("N", ctypes.c_int32),
+        ("dtype", ctypes.c_int32), ("logits", ctypes.c_void_p), ("row_stride", ctypes.c_int64),
+        ("row_index", ctypes.c_void_p), ("temperature", ctypes.c_void_p),
+        ("seed", ctypes.c_uint64), ("step", ctypes.c_uint32), ("request_base", ctypes.c_uint32),
+        ("tokens", ctypes.c_void_p), ("trace", ctypes.c_void_p), ("mutation", ctypes.c_int32),
+    ]
+
+
 def lib():
     """Load (building first if absent) the oracle shared library."""
     global _lib
@@ -96,6 +106,10 @@ def lib():
         L.oracle_sampling_weights.restype = ctypes.c_int
         L.oracle_expand.argtypes = [ctypes.POINTER(ExpandArgs)]
         L.oracle_expand.restype = ctypes.c_int
+        L.oracle_draft_sample.argtypes = [ctypes.POINTER(DraftArgs)]
+        L.oracle_draft_sample.restype = ctypes.c_int
+        L.oracle_draft_uniform.argtypes = [ctypes.c_uint64, ctypes.c_uint32, ctypes.c_uint32, ctypes.c_uint32,
+                                           ctypes.c_void_p]
         _lib = L
     return _lib
 
@@ -312,3 +326,41 @@ def expand(in_token_ids, in_positions, in_start, accepted, bonus, K, mask_id,
         raise ValueError("oracle_expand rejected its arguments (%d)" % rc)
     r.n_bad = rc
     return r
+
+
+# ---------------------------------------------------------------- draft sampling
+class DraftResult:
+    def __init__(self, tokens, trace, n_bad):
+        self.tokens = tokens
+        self.trace = trace
+        self.n_bad = n_bad
+
+
+def draft_uniform(seed, step, request, position):
+    u = ctypes.c_double(0.0)
+    lib().oracle_draft_uniform(int(seed) & (2**64 - 1), int(step) & 0xFFFFFFFF, int(request), int(position),
+                               ctypes.byref(u))
+    return u.value
+
+
+def draft_sample(logits, row_index, temperature, seed=0, step=0, request_base=0, mutation=0):
+    """Draft tokens sampled at rows row_index [B, K] of logits [N, V] (float32,
+    or uint16 bf16 bit patterns).  Returns a DraftResult (tokens [B, K],
+    trace [B, K] = the uniform of each draw, n_bad)."""
+    lg, dt = _logit_buffer(logits)
+    if lg.ndim != 2:
+        raise ValueError("logits must be [N, V]")
+    ri = _c(row_index, np.int32)
+    B, K = ri.shape
+    T = _c(temperature, np.float32).reshape(B)
+    tok = np.zeros((B, K), np.int32)
+    trc = np.zeros((B, K), np.float64)
+    a = DraftArgs()
+    a.B, a.K, a.V, a.N, a.dtype = B, K, lg.shape[1], lg.shape[0], dt
+    a.logits, a.row_stride, a.row_index, a.temperature = _ptr(lg), lg.shape[1], _ptr(ri), _ptr(T)
+    a.seed, a.step, a.request_base = int(seed) & (2**64 - 1), int(step) & 0xFFFFFFFF, int(request_base)
+    a.tokens, a.trace, a.mutation = _ptr(tok), _ptr(trc), int(mutation)
+    rc = lib().oracle_draft_sample(ctypes.byref(a))
+    if rc < 0:
+        raise ValueError("oracle_draft_sample rejected its arguments")
+    return DraftResult(tok, trc, rc)

@@ -8,7 +8,7 @@ import os
 import subprocess
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-SOURCES = ["philox.c", "verify.c", "expand.c"]
+SOURCES = ["philox.c", "verify.c", "expand.c", "draft.c"]
 LIB = os.path.join(HERE, "libspecoracle.so")
 
 

@@ -19,7 +19,9 @@
  *  - "P-EAGLE: parallel speculative decoding in vLLM" page, sections
  *    "并行草稿生成的挑战", "Triton Kernel" and "Hidden State 管理": the expanded
  *    drafter batch (shifted copy, bonus insert, MASK slots, masks, new-token
- *    indices, hidden-state mapping) and the two-statement hidden-state fill.
+ *    indices, hidden-state mapping), the two-statement hidden-state fill and
+ *    the KV-cache slot mapping; the draft tokens sampled at the new-token
+ *    indices.
  *
  * Floating point is IEEE double throughout (logits are widened exactly from
  * fp32 / bf16).  Uniforms come from Philox4x32-10 (Salmon, Moraes, Dror, Shaw,
@@ -143,6 +145,33 @@ typedef struct {
  * request is invalid in that way and out_start is not written.  -1 on bad
  * arguments.  A decreasing in_start is outside the contract. */
 int oracle_expand(const oracle_expand_args* a);
+
+/* ------------------------------------------------------ draft sampling -- */
+/* The uniform of the draft draw at (request, position, step): Philox4x32-10
+ * counter {request, position, step, 1}, key {seed lo 32, seed hi 32}, word 0. */
+void oracle_draft_uniform(uint64_t seed, uint32_t step, uint32_t request, uint32_t position, double* u);
+
+typedef struct {
+  int32_t B, K, V, N;
+  int32_t dtype;                     /* 0 = fp32, 1 = bf16 (uint16 bits) */
+  const void* logits;                /* [N, V] drafter logits with the row stride below */
+  int64_t row_stride;                /* elements, >= V */
+  const int32_t* row_index;          /* [B, K]: row of position k of request b (new-token indices) */
+  const float* temperature;          /* [B]; 0 => greedy */
+  uint64_t seed;
+  uint32_t step;
+  uint32_t request_base;
+  int32_t* tokens;                   /* out [B, K] */
+  double* trace;                     /* nullable out [B, K]: the uniform of each draw */
+  int32_t mutation;                  /* 0 = the method; 1 = planted mistake for test power */
+} oracle_draft_args;
+
+/* Draft token k of request b: x ~ softmax(logits[row_index[b, k]] / T_b) by the
+ * inverse CDF with the uniform above (weights p, normaliser their sum); T = 0:
+ * lowest-index argmax.  A row index outside [0, N), a temperature < 0 / NaN /
+ * inf, or a row without a finite maximum gives token -1.  Returns the number
+ * of such positions, or -1 on bad arguments. */
+int oracle_draft_sample(const oracle_draft_args* a);
 
 #ifdef __cplusplus
 }
