@@ -210,6 +210,53 @@ typedef struct {
  * gather) as a single kernel. */
 int spec_expand_launch(const spec_expand_args* args, hipStream_t stream);
 
+/* ----------------------------------------------------------- draft sampling
+ *
+ * The next draft tokens, sampled from the drafter's logits at the new-token
+ * indices of an expansion ("P-EAGLE" page, section "Triton Kernel": the
+ * new-token indices are the rows at which the draft tokens are sampled; one
+ * drafter pass predicts all K, section "核心方法").  Token k of request b is
+ * drawn from q = softmax(logits[row_index[b, k]] / T_b) -- the distribution
+ * the next verification checks it against (explainer page, section
+ * "修正拒绝采样") -- by the inverse CDF in ascending vocabulary order with one
+ * uniform: Philox4x32-10 counter {b + request_base, k, step, 1} (a stream
+ * apart from the verification's, which uses word 3 = 0), key as for
+ * verification, word 0, mapped as (w >> 8) * 2^-24.  Temperature 0 takes the
+ * lowest-index argmax.
+ *
+ * Layout: logits [N, V] (row stride >= V elements), row_index [B, K] (for
+ * instance the new_token_indices of spec_expand_launch), temperature [B].
+ * A position whose row index is outside [0, N), a request whose temperature is
+ * negative, NaN or infinite, and a row without a finite maximum get token -1.
+ * Preconditions on the data (not checked): no NaN or +inf logit and
+ * |logit| / T < 2^100.
+ */
+typedef struct {
+  int32_t B;                   /* requests, >= 0 */
+  int32_t K;                   /* draft positions per request, >= 1 */
+  int32_t V;                   /* vocabulary size, >= 1 */
+  int32_t N;                   /* rows of the logits buffer, >= 0 */
+  int32_t dtype;               /* spec_dtype of the logits */
+  const void* logits;          /* device [N, V] drafter logits */
+  int64_t row_stride;          /* elements between rows, >= V */
+  const int32_t* row_index;    /* device [B, K]: logits row of position k of request b */
+  const float* temperature;    /* device [B]; 0 = greedy */
+  uint64_t seed;               /* Philox key */
+  uint32_t step;               /* Philox counter word 2 */
+  uint32_t request_base;       /* added to the request index in the counter */
+  int32_t* tokens;             /* device out [B, K] */
+  void* workspace;             /* device scratch, >= spec_draft_workspace_bytes(B, K, V), 16-B aligned */
+  size_t workspace_bytes;
+} spec_draft_args;
+
+/* Bytes of device workspace a draft sampling of this shape needs (0 for an
+ * invalid shape); stateless, no initialisation, reusable for any shape it is
+ * large enough for. */
+size_t spec_draft_workspace_bytes(int32_t B, int32_t K, int32_t V);
+
+/* Enqueue the draft sampling (two kernels). */
+int spec_draft_sample_launch(const spec_draft_args* args, hipStream_t stream);
+
 /* Human-readable name of a spec_status value (static storage). */
 const char* spec_status_string(int status);
 

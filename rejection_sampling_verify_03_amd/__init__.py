@@ -21,7 +21,8 @@ SPEC_F32, SPEC_BF16 = 0, 1
 SPEC_MAX_K = 63
 
 EXPORTED = ("spec_verify_workspace_bytes", "spec_verify_plan_phases", "spec_verify_launch",
-            "spec_expand_launch", "spec_status_string")
+            "spec_expand_launch", "spec_draft_workspace_bytes", "spec_draft_sample_launch",
+            "spec_status_string")
 
 
 class SpecVerifyArgs(ctypes.Structure):
@@ -55,6 +56,16 @@ class SpecExpandArgs(ctypes.Structure):
     ]
 
 
+class SpecDraftArgs(ctypes.Structure):
+    _fields_ = [
+        ("B", ctypes.c_int32), ("K", ctypes.c_int32), ("V", ctypes.c_int32), ("N", ctypes.c_int32),
+        ("dtype", ctypes.c_int32), ("logits", ctypes.c_void_p), ("row_stride", ctypes.c_int64),
+        ("row_index", ctypes.c_void_p), ("temperature", ctypes.c_void_p),
+        ("seed", ctypes.c_uint64), ("step", ctypes.c_uint32), ("request_base", ctypes.c_uint32),
+        ("tokens", ctypes.c_void_p), ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
+    ]
+
+
 def _load():
     # torch ships its own HIP runtime under the same SONAME as the system one;
     # loading torch first makes this library bind to that single runtime
@@ -74,6 +85,10 @@ def _load():
     L.spec_verify_launch.restype = ctypes.c_int
     L.spec_expand_launch.argtypes = [ctypes.POINTER(SpecExpandArgs), ctypes.c_void_p]
     L.spec_expand_launch.restype = ctypes.c_int
+    L.spec_draft_workspace_bytes.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32]
+    L.spec_draft_workspace_bytes.restype = ctypes.c_size_t
+    L.spec_draft_sample_launch.argtypes = [ctypes.POINTER(SpecDraftArgs), ctypes.c_void_p]
+    L.spec_draft_sample_launch.restype = ctypes.c_int
     L.spec_status_string.argtypes = [ctypes.c_int]
     L.spec_status_string.restype = ctypes.c_char_p
     return L
@@ -115,6 +130,14 @@ def spec_verify_launch(args, stream_ptr):
 
 def spec_expand_launch(args, stream_ptr):
     return int(lib.spec_expand_launch(ctypes.byref(args), stream_ptr))
+
+
+def spec_draft_workspace_bytes(B, K, V):
+    return int(lib.spec_draft_workspace_bytes(int(B), int(K), int(V)))
+
+
+def spec_draft_sample_launch(args, stream_ptr):
+    return int(lib.spec_draft_sample_launch(ctypes.byref(args), stream_ptr))
 
 
 def spec_status_string(status):
@@ -303,3 +326,42 @@ def expand(in_token_ids, in_positions, in_start, accepted, bonus, K, mask_id, ta
     if rc != SPEC_OK:
         raise SpecError(rc)
     return out
+
+
+# ------------------------------------------------------------ draft sampling
+def draft_args(logits, row_index, temperature, tokens, workspace, seed=0, step=0, request_base=0):
+    """Fill a SpecDraftArgs: logits [N, V] (unit column stride), row_index
+    [B, K] int32, temperature [B] float32, tokens [B, K] int32 out."""
+    torch = _torch()
+    _check_dev(logits, row_index, temperature, tokens, workspace)
+    if logits.dim() != 2 or logits.stride(-1) != 1:
+        raise ValueError("logits must be [N, V] with contiguous rows")
+    for t, dt in ((row_index, torch.int32), (temperature, torch.float32), (tokens, torch.int32)):
+        if t.dtype != dt or not t.is_contiguous():
+            raise ValueError("expected contiguous %s" % dt)
+    a = SpecDraftArgs()
+    B, K = row_index.shape
+    a.B, a.K, a.V, a.N, a.dtype = B, K, logits.shape[1], logits.shape[0], _logit_dtype(logits)
+    a.logits, a.row_stride = logits.data_ptr(), logits.stride(0)
+    a.row_index, a.temperature, a.tokens = row_index.data_ptr(), temperature.data_ptr(), tokens.data_ptr()
+    a.seed, a.step, a.request_base = int(seed) & (2 ** 64 - 1), int(step) & 0xFFFFFFFF, int(request_base)
+    a.workspace = workspace.data_ptr()
+    a.workspace_bytes = workspace.numel() * workspace.element_size()
+    return a
+
+
+def draft_sample(logits, row_index, temperature, seed=0, step=0, request_base=0, workspace=None, stream=None):
+    """Draft tokens [B, K] int32 sampled at rows row_index of logits, on
+    torch's current stream."""
+    torch = _torch()
+    B, K = row_index.shape
+    dev = logits.device
+    tokens = torch.empty(B, K, dtype=torch.int32, device=dev)
+    if workspace is None:
+        workspace = torch.empty(max(spec_draft_workspace_bytes(B, K, logits.shape[1]), 16), dtype=torch.uint8,
+                                device=dev)
+    a = draft_args(logits, row_index, temperature, tokens, workspace, seed, step, request_base)
+    rc = spec_draft_sample_launch(a, _stream_ptr(stream))
+    if rc != SPEC_OK:
+        raise SpecError(rc)
+    return tokens

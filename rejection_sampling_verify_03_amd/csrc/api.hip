@@ -56,9 +56,59 @@ int expand_check(const spec_expand_args* a) {
   return SPEC_OK;
 }
 
+size_t draft_ws_bytes(int32_t B, int32_t K, int32_t V) {
+  const int64_t nseg = ((int64_t)V + kSeg - 1) / kSeg;
+  return align256((size_t)B * K * nseg * sizeof(RowPartial));
+}
+
+int draft_check(const spec_draft_args* a) {
+  if (!a) return SPEC_EINVAL;
+  if (a->B < 0 || a->K < 1 || a->V < 1 || a->N < 0) return SPEC_EINVAL;
+  if (a->dtype != SPEC_F32 && a->dtype != SPEC_BF16) return SPEC_EDTYPE;
+  if (a->B == 0) return SPEC_OK;
+  if (!a->row_index || !a->temperature || !a->tokens || !a->workspace) return SPEC_EINVAL;
+  if (a->N > 0 && !a->logits) return SPEC_EINVAL;
+  if (a->row_stride < a->V) return SPEC_EINVAL;
+  const int64_t nseg = ((int64_t)a->V + kSeg - 1) / kSeg;
+  const int64_t C = (nseg + kDraftChunkSegs - 1) / kDraftChunkSegs;
+  if ((int64_t)a->B * a->K * C > INT32_MAX) return SPEC_EINVAL;
+  if (!aligned16(a->workspace)) return SPEC_EALIGN;
+  if (a->workspace_bytes < draft_ws_bytes(a->B, a->K, a->V)) return SPEC_EWORKSPACE;
+  return SPEC_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+size_t spec_draft_workspace_bytes(int32_t B, int32_t K, int32_t V) {
+  if (B < 0 || K < 1 || V < 1) return 0;
+  return draft_ws_bytes(B, K, V);
+}
+
+int spec_draft_sample_launch(const spec_draft_args* a, hipStream_t stream) {
+  const int rc = draft_check(a);
+  if (rc != SPEC_OK || a->B == 0) return rc;
+  const int es = a->dtype == SPEC_BF16 ? 2 : 4;
+  DraftParams P;
+  P.B = a->B;
+  P.K = a->K;
+  P.V = a->V;
+  P.N = a->N;
+  P.nseg = (int32_t)(((int64_t)a->V + kSeg - 1) / kSeg);
+  P.C = (P.nseg + kDraftChunkSegs - 1) / kDraftChunkSegs;
+  P.logits = static_cast<const char*>(a->logits);
+  P.row_stride = a->row_stride;
+  P.row_index = a->row_index;
+  P.temperature = a->temperature;
+  P.seed = a->seed;
+  P.step = a->step;
+  P.request_base = a->request_base;
+  P.tokens = a->tokens;
+  P.segp = static_cast<RowPartial*>(a->workspace);
+  const bool vec = aligned16(a->logits) && (a->row_stride * es) % 16 == 0;
+  return launch_draft(P, a->dtype, vec, stream) == hipSuccess ? SPEC_OK : SPEC_ELAUNCH;
+}
 
 uint64_t spec_verify_plan_phases(int32_t K, const double* survival, double sampled_fraction, double phase_cost) {
   if (K < 1 || K > SPEC_MAX_K || !survival) return 0;

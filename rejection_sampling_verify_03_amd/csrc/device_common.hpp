@@ -3,6 +3,7 @@
 // 64-lane wavefront / 256-thread workgroup reductions.
 #pragma once
 
+#include <float.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -172,6 +173,25 @@ __device__ __forceinline__ float load_one(const char* __restrict__ row, int64_t 
 // and M an integer-valued reference, so exp2(t) <= 1 for the row maximum.
 __device__ __forceinline__ float scaled_exp2(float x, float s_hi, float s_lo, float negM) {
   return __builtin_amdgcn_exp2f(__builtin_fmaf(x, s_hi, __builtin_fmaf(x, s_lo, negM)));
+}
+
+// log2(e) / T split as s_hi + s_lo with s_hi rounded toward zero and
+// s_lo >= FLT_MIN (keeps -inf * s = -inf in both fma terms).
+__device__ __forceinline__ void temperature_scale(float T, float& s_hi, float& s_lo) {
+  const double s = 1.4426950408889634074 / (double)T;
+  s_hi = __double2float_rz(s);
+  s_lo = fmaxf(__double2float_rn(s - (double)s_hi), FLT_MIN);
+}
+
+// A usable temperature: 0 (greedy) or positive and finite.
+__device__ __forceinline__ bool temperature_valid(float T) { return T >= 0.0f && T <= FLT_MAX; }
+
+// Sum of 2^(x * s - M) over a group of 8, pairwise in fp32.
+__device__ __forceinline__ float sum8_exp(const float x[8], float s_hi, float s_lo, float negM) {
+  float e[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) e[i] = scaled_exp2(x[i], s_hi, s_lo, negM);
+  return ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
 }
 
 // ---------------------------------------------------------- reductions --

@@ -45,20 +45,11 @@
 #include <limits.h>
 
 #include "device_common.hpp"
+#include "sampling.hpp"
 #include "verify_kernels.hpp"
 #include "verify_layout.hpp"
 
 namespace specv {
-
-// log2(e) / T split as s_hi + s_lo with s_hi rounded toward zero and
-// s_lo >= FLT_MIN (keeps -inf * s = -inf in both fma terms).
-__device__ __forceinline__ void temperature_scale(float T, float& s_hi, float& s_lo) {
-  const double s = 1.4426950408889634074 / (double)T;
-  s_hi = __double2float_rz(s);
-  s_lo = fmaxf(__double2float_rn(s - (double)s_hi), FLT_MIN);
-}
-
-__device__ __forceinline__ bool temperature_valid(float T) { return T >= 0.0f && T <= FLT_MAX; }
 
 template <int ES>
 __device__ __forceinline__ const char* row_ptr(const VerifyParams& P, int b, int r) {
@@ -74,13 +65,6 @@ __device__ __forceinline__ void raise_ref(float& M, double& S, float gm, float s
     S = ldexp(S, (int)fmaxf(M - gM, -2000.f));
     M = gM;
   }
-}
-
-__device__ __forceinline__ float sum8_exp(const float x[8], float s_hi, float s_lo, float negM) {
-  float e[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) e[i] = scaled_exp2(x[i], s_hi, s_lo, negM);
-  return ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
 }
 
 // ------------------------------------------------------------ chunk passes
@@ -453,17 +437,8 @@ __global__ __launch_bounds__(kWG) void verify_rowstats_kernel(VerifyParams P) {
 }
 
 // ------------------------------------------------------------ sampling weights
-// The draw samples from r = max(0, p - q) (or from p for the bonus).  With
-// e_p = 2^(x_p s - M_p), e_q = 2^(x_q s - M_q) and the normalisers S_p, S_q,
-// r = max(0, e_p - e_q * c) / S_p with c = S_p / S_q.  The weights are kept in
-// units of 1 / S_p (a common factor that cancels in the inverse CDF) and
-// computed in fp32 with c split as c_hi + c_lo: each fma rounds once,
-// relative to the result, so the residual keeps ~1e-7 relative accuracy even
-// where p and q nearly cancel.
-struct WeightCtx {
-  float s_hi, s_lo, negMp, negMq, c_hi, c_lo;
-};
-
+// The weight context of a decision record: scale, references and the split
+// residual constant c = S_p / S_q (see WeightCtx).
 __device__ __forceinline__ WeightCtx make_ctx(const ReqDesc& d) {
   WeightCtx w;
   w.s_hi = d.s_hi;
@@ -474,51 +449,6 @@ __device__ __forceinline__ WeightCtx make_ctx(const ReqDesc& d) {
   w.c_hi = (float)c;
   w.c_lo = (float)(c - (double)w.c_hi);
   return w;
-}
-
-// Weight of one logit pair: residual (res) or p, in units of 1 / S_p.
-__device__ __forceinline__ float pair_weight(const WeightCtx& w, float xp, float xq, bool res, float& ep) {
-  ep = scaled_exp2(xp, w.s_hi, w.s_lo, w.negMp);
-  if (!res) return ep;
-  const float eq = scaled_exp2(xq, w.s_hi, w.s_lo, w.negMq);
-  const float t = __builtin_fmaf(-eq, w.c_lo, __builtin_fmaf(-eq, w.c_hi, ep));
-  return fmaxf(t, 0.0f);
-}
-
-// 8 consecutive logits from e0 on, -inf past the row end e1.
-template <int ES, bool VEC>
-__device__ __forceinline__ void load_group_bounded(const char* row, int e0, int e1, float x[8]) {
-  if (e0 + 8 <= e1) {
-    load_group<ES, VEC>(row, e0, x);
-  } else {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) x[i] = (e0 + i < e1) ? load_one<ES>(row, e0 + i) : -INFINITY;
-  }
-}
-
-// A group of 8 logits from e0 on, -inf past the row end V (scalar loads for a
-// group that straddles the end).
-template <int ES, bool VEC>
-__device__ __forceinline__ RawGroup<ES, VEC> load_raw_bounded(const char* row, int e0, int V) {
-  if (e0 + 8 <= V) return load_raw<ES, VEC>(row, e0);
-  float x[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) x[i] = (e0 + i < V) ? load_one<ES>(row, e0 + i) : -INFINITY;
-  RawGroup<ES, VEC> r;
-  if constexpr (!VEC) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) r.x[i] = x[i];
-  } else if constexpr (ES == 2) {
-    uint32_t w[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      w[i] = (__float_as_uint(x[2 * i]) >> 16) | (__float_as_uint(x[2 * i + 1]) & 0xffff0000u);
-    r.v = u32x4{w[0], w[1], w[2], w[3]};
-  } else {
-    r.a = f32x4{x[0], x[1], x[2], x[3]};
-    r.b = f32x4{x[4], x[5], x[6], x[7]};
-  }
-  return r;
 }
 
 // One wave sums the weights of segment [s0, s0 + kSeg) (clipped to V): lane l
@@ -609,191 +539,7 @@ __global__ __launch_bounds__(64) void verify_segsum_kernel(VerifyParams P) {
 }
 
 // --------------------------------------------------------------------- draw
-constexpr int kWGD = 512;  // draw workgroup: 8 waves, one 512-logit block each
-static_assert(kWGD / 64 * 512 == kSeg, "a draw wave per 512-logit block of a segment");
-
-template <int NT>
-__device__ __forceinline__ int block_first_true(bool pred) {
-  constexpr int W = NT / 64;
-  __shared__ int first[W];
-  const uint64_t m = __ballot(pred);
-  const int w = threadIdx.x >> 6;
-  if ((threadIdx.x & 63) == 0) first[w] = m ? (int)__builtin_ctzll(m) + 64 * w : -1;
-  __syncthreads();
-  int r = -1;
-#pragma unroll
-  for (int i = W - 1; i >= 0; --i)
-    if (first[i] >= 0) r = first[i];
-  __syncthreads();
-  return r;
-}
-
-template <int NT>
-__device__ __forceinline__ int block_max_int(int v) {
-  constexpr int W = NT / 64;
-  __shared__ int mx[W];
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v = max(v, __shfl_xor(v, off, 64));
-  if ((threadIdx.x & 63) == 0) mx[threadIdx.x >> 6] = v;
-  __syncthreads();
-  int r = mx[0];
-#pragma unroll
-  for (int i = 1; i < W; ++i) r = max(r, mx[i]);
-  __syncthreads();
-  return r;
-}
-
-// Inside segment j: the first logit whose cumulative weight (from `base`)
-// exceeds `target`, or with `last_positive` the last logit of positive weight.
-// Wave w recomputes the weights of block w (512 logits); the crossing block
-// is found from the block totals in order, then the crossing lane and logit.
-template <int ES, bool VEC>
-__device__ int draw_in_segment(const VerifyParams& P, int b, const ReqDesc& d, bool res, int j, double base,
-                               double target, bool last_positive) {
-  constexpr int W = kWGD / 64;
-  __shared__ double blk_tot[W];
-  __shared__ int blk_last[W];
-  __shared__ int sh_w, sh_mode;
-  __shared__ double sh_base;
-  __shared__ int sh_pick;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const bool resmode = d.mode == kModeResidual;
-  const char* prow = row_ptr<ES>(P, b, d.a);
-  const char* qrow = resmode ? row_ptr<ES>(P, b, P.K + 1 + d.a) : prow;
-  const WeightCtx w = make_ctx(d);
-  const int e0 = j * kSeg + wave * 512 + 8 * lane;
-  float xp[8], xq[8];
-  if (e0 < P.V) {
-    load_group_bounded<ES, VEC>(prow, e0, P.V, xp);
-    if (resmode) load_group_bounded<ES, VEC>(qrow, e0, P.V, xq);
-  } else {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) xp[i] = -INFINITY;
-  }
-  if (!resmode || e0 >= P.V) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) xq[i] = resmode ? -INFINITY : 0.f;
-  }
-  double wt[8];
-  double ls = 0.0;
-  int lastpos = -1;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    float ep;
-    const float r = pair_weight(w, xp[i], xq[i], resmode, ep);
-    wt[i] = (double)(res ? r : ep);
-    ls += wt[i];
-    if (wt[i] > 0.0) lastpos = e0 + i;
-  }
-  double x = ls;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const double y = __shfl_up(x, off, 64);
-    if (lane >= off) x += y;
-  }
-  double xe = __shfl_up(x, 1, 64);
-  if (lane == 0) xe = 0.0;
-  const double wtotal = __shfl(x, 63, 64);
-  int wl = lastpos;
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) wl = max(wl, __shfl_xor(wl, off, 64));
-  if (lane == 0) {
-    blk_tot[wave] = wtotal;
-    blk_last[wave] = wl;
-  }
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    int wsel = -1, mode = 1;  // 0: search the block, 1: its last positive logit
-    double acc = base;
-    if (!last_positive) {
-      for (int i = 0; i < W; ++i) {
-        if (acc + blk_tot[i] > target) {
-          wsel = i;
-          mode = 0;
-          break;
-        }
-        acc += blk_tot[i];
-      }
-    }
-    if (wsel < 0)
-      for (int i = 0; i < W; ++i)
-        if (blk_last[i] >= 0) wsel = i;
-    sh_w = wsel;
-    sh_mode = mode;
-    sh_base = acc;
-    sh_pick = -1;
-  }
-  __syncthreads();
-  if (wave == sh_w) {
-    int pick = -1;
-    if (sh_mode == 0) {
-      const uint64_t m = __ballot(sh_base + x > target);
-      const int L = m ? (int)__builtin_ctzll(m) : 63;
-      if (lane == L) {
-        double run = sh_base + xe;
-        for (int i = 0; i < 8; ++i) {
-          run += wt[i];
-          if (wt[i] > 0.0 && target < run) {
-            pick = e0 + i;
-            break;
-          }
-        }
-        if (pick < 0) pick = lastpos;  // cumulative rounding: stay inside this lane
-      }
-      for (int off = 32; off >= 1; off >>= 1) pick = max(pick, __shfl_xor(pick, off, 64));
-      if (pick < 0) pick = blk_last[wave];
-    } else {
-      pick = blk_last[wave];
-    }
-    if (lane == 0) sh_pick = pick;
-  }
-  __syncthreads();
-  return sh_pick;
-}
-
-// Inclusive and exclusive scans of two doubles per thread over the workgroup in
-// one pass (fixed order); totals of both.  All threads must call it.
-template <int NT>
-__device__ __forceinline__ void block_scan_d2(double v0, double v1, double& incl0, double& excl0, double& tot0,
-                                              double& incl1, double& excl1, double& tot1) {
-  constexpr int W = NT / 64;
-  __shared__ double wt[2][W];
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  double x0 = v0, x1 = v1;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const double y0 = __shfl_up(x0, off, 64);
-    const double y1 = __shfl_up(x1, off, 64);
-    if (lane >= off) {
-      x0 += y0;
-      x1 += y1;
-    }
-  }
-  double e0 = __shfl_up(x0, 1, 64), e1 = __shfl_up(x1, 1, 64);
-  if (lane == 0) e0 = e1 = 0.0;
-  if (lane == 63) {
-    wt[0][w] = x0;
-    wt[1][w] = x1;
-  }
-  __syncthreads();
-  double b0 = 0.0, b1 = 0.0, t0 = 0.0, t1 = 0.0;
-#pragma unroll
-  for (int i = 0; i < W; ++i) {
-    if (i < w) {
-      b0 += wt[0][i];
-      b1 += wt[1][i];
-    }
-    t0 += wt[0][i];
-    t1 += wt[1][i];
-  }
-  incl0 = b0 + x0;
-  excl0 = b0 + e0;
-  tot0 = t0;
-  incl1 = b1 + x1;
-  excl1 = b1 + e1;
-  tot1 = t1;
-  __syncthreads();
-}
+constexpr int kWGD = kDrawThreads;
 
 template <int ES, bool VEC>
 __global__ __launch_bounds__(kWGD) void verify_draw_kernel(VerifyParams P) {
@@ -858,9 +604,15 @@ __global__ __launch_bounds__(kWGD) void verify_draw_kernel(VerifyParams P) {
       __syncthreads();
     }
   }
+  const bool resmode = d.mode == kModeResidual;
+  const char* prow = row_ptr<ES>(P, b, d.a);
+  const char* qrow = resmode ? row_ptr<ES>(P, b, P.K + 1 + d.a) : prow;
+  const WeightCtx w = make_ctx(d);
   int y = -1;  // no positive weight anywhere: only reachable outside the data contract
-  if (found >= 0) y = draw_in_segment<ES, VEC>(P, b, d, res, found, base, target, false);
-  else if (lastpos >= 0) y = draw_in_segment<ES, VEC>(P, b, d, res, lastpos, 0.0, 0.0, true);
+  if (found >= 0)
+    y = draw_in_segment<ES, VEC>(prow, qrow, P.V, w, resmode, res, 1.0, found, base, target, false);
+  else if (lastpos >= 0)
+    y = draw_in_segment<ES, VEC>(prow, qrow, P.V, w, resmode, res, 1.0, lastpos, 0.0, 0.0, true);
   if (tid == 0) P.out_tokens[(int64_t)b * (P.K + 1) + d.a] = y;
 }
 

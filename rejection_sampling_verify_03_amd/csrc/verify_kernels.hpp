@@ -58,10 +58,25 @@ struct ExpandParams {
   int64_t* slots;     // slot mapping out, or null
 };
 
+struct DraftParams {
+  int32_t B, K, V, N, nseg, C;  // C: chunks of kDraftChunkSegs segments per row
+  const char* logits;
+  int64_t row_stride;
+  const int32_t* row_index;
+  const float* temperature;
+  uint64_t seed;
+  uint32_t step, request_base;
+  int32_t* tokens;
+  RowPartial* segp;  // per (request, position, segment) statistics [B * K * nseg]
+};
+
+constexpr int kDraftChunkSegs = 8;  // segments per workgroup of the statistics pass
+
 // phase_starts: bit k (1 <= k <= K) starts an early-exit phase at draft
 // position k; 0 reads every row in one pass.
 hipError_t launch_verify(const VerifyParams& P, int dtype, bool vec, uint64_t phase_starts,
                          hipEvent_t phase_event, hipStream_t stream);
 hipError_t launch_expand(const ExpandParams& P, bool vec, hipStream_t stream);
+hipError_t launch_draft(const DraftParams& P, int dtype, bool vec, hipStream_t stream);
 
 }  // namespace specv

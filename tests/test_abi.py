@@ -43,7 +43,8 @@ def test_struct_layouts_match_the_header(sv, tmp_path):
     """Every field offset and struct size of the binding's ctypes mirrors
     equals what a C compiler makes of include/spec_verify.h."""
     lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "spec_verify.h"', 'int main(void) {']
-    for cname, py in (("spec_verify_args", sv.SpecVerifyArgs), ("spec_expand_args", sv.SpecExpandArgs)):
+    for cname, py in (("spec_verify_args", sv.SpecVerifyArgs), ("spec_expand_args", sv.SpecExpandArgs),
+                      ("spec_draft_args", sv.SpecDraftArgs)):
         lines.append('printf("%s size %%zu\\n", sizeof(%s));' % (cname, cname))
         for f, _ in py._fields_:
             lines.append('printf("%s %s %%zu\\n", offsetof(%s, %s));' % (cname, f, cname, f))
@@ -55,7 +56,8 @@ def test_struct_layouts_match_the_header(sv, tmp_path):
                    check=True)
     out = subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.split("\n")
     got = {tuple(l.split()[:2]): int(l.split()[2]) for l in out if l.strip()}
-    for cname, py in (("spec_verify_args", sv.SpecVerifyArgs), ("spec_expand_args", sv.SpecExpandArgs)):
+    for cname, py in (("spec_verify_args", sv.SpecVerifyArgs), ("spec_expand_args", sv.SpecExpandArgs),
+                      ("spec_draft_args", sv.SpecDraftArgs)):
         assert got[(cname, "size")] == ctypes.sizeof(py), cname
         for f, _ in py._fields_:
             assert got[(cname, f)] == getattr(py, f).offset, (cname, f)
@@ -160,3 +162,35 @@ def test_status_strings(sv):
     for code in (0, -1, -2, -3, -4, -5):
         assert sv.spec_status_string(code).startswith("SPEC_")
     assert "unknown" in sv.spec_status_string(42)
+
+
+def test_draft_argument_errors(sv):
+    fake = 0x10000  # never dereferenced: every call below fails validation first
+
+    def args():
+        a = sv.SpecDraftArgs()
+        a.B, a.K, a.V, a.N, a.dtype = 2, 3, 100, 8, sv.SPEC_BF16
+        a.logits, a.row_stride = fake, 100
+        a.row_index = a.temperature = a.tokens = a.workspace = fake
+        a.workspace_bytes = 0  # too small on purpose
+        return a
+
+    launch = lambda a: sv.spec_draft_sample_launch(a, None)
+    assert launch(args()) == sv.SPEC_EWORKSPACE
+    for field, value, want in [("K", 0, sv.SPEC_EINVAL), ("V", 0, sv.SPEC_EINVAL), ("B", -1, sv.SPEC_EINVAL),
+                               ("N", -1, sv.SPEC_EINVAL), ("dtype", 7, sv.SPEC_EDTYPE),
+                               ("row_stride", 99, sv.SPEC_EINVAL), ("row_index", None, sv.SPEC_EINVAL),
+                               ("temperature", None, sv.SPEC_EINVAL), ("tokens", None, sv.SPEC_EINVAL),
+                               ("logits", None, sv.SPEC_EINVAL), ("workspace", None, sv.SPEC_EINVAL),
+                               ("workspace", 0x10004, sv.SPEC_EALIGN)]:
+        a = args()
+        setattr(a, field, value)
+        assert launch(a) == want, (field, value)
+    a = args()
+    a.B = 0
+    assert launch(a) == sv.SPEC_OK
+    assert sv.lib.spec_draft_sample_launch(None, None) == sv.SPEC_EINVAL
+    # workspace: one 16-byte statistic per (request, position, 4096-logit segment), 256-byte rounded
+    assert sv.spec_draft_workspace_bytes(2, 3, 100) == 256
+    assert sv.spec_draft_workspace_bytes(256, 8, 151936) == 256 * 8 * 38 * 16
+    assert sv.spec_draft_workspace_bytes(1, 0, 10) == 0

@@ -253,6 +253,24 @@ def expand_inputs(B=512, K=8, H=HIDDEN_GPT_OSS_20B, vocab=GPT_OSS_VOCAB, seed=0,
         target_hidden=hidden, mask_hidden=mask_hidden)
 
 
+class DraftInputs:
+    def __init__(self, **kw):
+        self.__dict__.update(kw)
+
+
+def drafter_inputs(B, K, N, V, dtype, seed, device, temps=(0.0, 0.6, 1.0)):
+    """Drafter logits [N, V] (Zipf rows, as the target recipe), K row indices
+    per request drawn uniformly from [0, N) (the new-token indices stand-in),
+    and a temperature per request drawn uniformly from ``temps``."""
+    g = _gen(seed, device)
+    logits = zipf_logits(N, V, g, device).to(dtype)
+    row_index = torch.randint(0, N, (B, K), generator=g, device=device, dtype=torch.int64).to(torch.int32)
+    t = torch.tensor(temps, dtype=torch.float32, device=device)
+    temperature = t[torch.randint(0, len(temps), (B,), generator=g, device=device)]
+    return DraftInputs(B=B, K=K, N=N, V=V, logits=logits, row_index=row_index.contiguous(),
+                       temperature=temperature.contiguous())
+
+
 def block_tables(B, max_blocks, seed, device="cpu", unmapped_fraction=0.0):
     """A synthetic paged-KV block table [B, max_blocks] int32: every entry a
     distinct physical block (a random permutation of 0..B*max_blocks-1), and
