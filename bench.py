@@ -39,6 +39,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-draft-sampling", action="store_true",
+                    help="skip the separate measurement of draft-token sampling at the new-token indices")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="approximate CPU-seconds of oracle work for the CPU baseline")
     ap.add_argument("--early-exit", choices=("plan", "off"), default="plan",
@@ -74,6 +76,38 @@ def phased_logit_bytes(acc, temps, mask, K, V, es):
                 break
             total += (e - s) + ((min(e, K) - s) if t > 0 else 0)
     return total * V * es
+
+
+def draft_sampling(sv, torch, np, out, temperature, B, K, V, seed, dev, reps=50):
+    """Draft tokens sampled from drafter logits [N_out, V] bf16 (Zipf rows) at
+    the expansion's new-token indices, timed apart from the step with HIP
+    events; bytes = every sampled row once plus the one segment the draw
+    re-reads for a T > 0 position."""
+    import workloads
+    n_out = out.out_token_ids.shape[0]
+    g = workloads._gen(seed + 3, dev)
+    logits = workloads.zipf_logits(n_out, V, g, dev).to(torch.bfloat16)
+    tokens = torch.empty(B, K, dtype=torch.int32, device=dev)
+    ws = torch.empty(sv.spec_draft_workspace_bytes(B, K, V), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    args = [sv.draft_args(logits, out.new_token_indices, temperature, tokens, ws, seed=seed, step=i)
+            for i in range(reps)]
+    for a in args[:5]:
+        assert sv.spec_draft_sample_launch(a, stream.cuda_stream) == sv.SPEC_OK
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for a in args:
+        assert sv.spec_draft_sample_launch(a, stream.cuda_stream) == sv.SPEC_OK
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    n_sampled = int((temperature > 0).sum())
+    nbytes = B * K * V * 2 + n_sampled * K * 4096 * 2
+    del logits
+    return {"workload": "drafter logits [%d, %d] bf16, B=%d requests x K=%d new-token indices" % (n_out, V, B, K),
+            "ms": ms, "positions_per_s": B * K / (ms * 1e-3), "bytes": nbytes,
+            "GBps": nbytes / (ms * 1e-3) / 1e9, "frac_of_hbm_peak": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
 
 
 def sequential_logit_bytes(acc, temps, K, V, es):
@@ -309,6 +343,8 @@ def main():
         "emitted_tokens_per_s": float((acc_np + 1).sum()) / args.steps / (ms_per_step * 1e-3),
         "mean_accepted": float(acc_np.mean()),
     }
+    if not args.no_draft_sampling:
+        line["draft_sampling"] = draft_sampling(sv, torch, np, out, inp.temperature, B, K, V, args.seed, dev)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(inp, args.seed, args.cpu_seconds)
     print(json.dumps(line), flush=True)

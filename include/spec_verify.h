@@ -99,6 +99,12 @@ typedef struct {
                                   row-statistics stage (to time it apart from the rest) */
   uint64_t phase_starts;       /* early exit: bit k (1 <= k <= K) starts a new phase at draft
                                   position k; 0 = one pass over every row (see below) */
+  const int32_t* draft_row_index; /* device [B, K] or NULL: draft row k of request b is row
+                                  draft_row_index[b*K + k] of a [draft_rows, V] buffer at
+                                  draft_logits (row stride d_row_stride; d_req_stride unused),
+                                  e.g. the drafter's logits at the new-token indices */
+  int32_t draft_rows;          /* rows of that buffer; an entry outside [0, draft_rows) makes a
+                                  sampled request invalid */
 } spec_verify_args;
 
 /* Early exit (same explainer page, section "核心思想": a request stops at
@@ -131,7 +137,8 @@ uint64_t spec_verify_plan_phases(int32_t K, const double* survival, double sampl
 size_t spec_verify_workspace_bytes(int32_t B, int32_t K, int32_t V);
 
 /* Enqueue one verification step.  A request whose data is invalid (a draft
- * token outside [0, V), a temperature that is negative, NaN or infinite, or a
+ * token outside [0, V), a temperature that is negative, NaN or infinite, a
+ * draft row table entry of a sampled request outside [0, draft_rows), or a
  * row of a sampled request without a finite normaliser) gets
  * accepted_counts = -1, output_tokens all -1 and debug_probs 0. */
 int spec_verify_launch(const spec_verify_args* args, hipStream_t stream);

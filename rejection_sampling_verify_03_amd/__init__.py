@@ -35,6 +35,7 @@ class SpecVerifyArgs(ctypes.Structure):
         ("accepted_counts", ctypes.c_void_p), ("output_tokens", ctypes.c_void_p),
         ("debug_probs", ctypes.c_void_p), ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
         ("phase_event", ctypes.c_void_p), ("phase_starts", ctypes.c_uint64),
+        ("draft_row_index", ctypes.c_void_p), ("draft_rows", ctypes.c_int32),
     ]
 
 
@@ -184,8 +185,12 @@ def make_workspace(B, K, V, device="cuda"):
 
 
 def verify_args(target, draft, draft_tokens, temperature, accepted, tokens, debug, workspace,
-                seed=0, step=0, request_base=0, phase_event=None, phase_starts=0):
+                seed=0, step=0, request_base=0, phase_event=None, phase_starts=0, draft_row_index=None):
     """Fill a SpecVerifyArgs from tensors (no copies).
+
+    With draft_row_index [B, K] int32, draft is a 2-D [N, V] buffer (e.g. the
+    drafter's logits) and draft row k of request b is its row
+    draft_row_index[b, k].
 
     target [B or broadcast, K+1, V] and draft [B or broadcast, >=K, V] with a
     unit innermost stride; a request stride of 0 (expanded tensor) shares rows.
@@ -207,8 +212,19 @@ def verify_args(target, draft, draft_tokens, temperature, accepted, tokens, debu
     a.t_req_stride = target.stride(0) if target.shape[0] == B and B > 1 else 0
     a.t_row_stride = target.stride(1)
     a.draft_logits = draft.data_ptr()
-    a.d_req_stride = draft.stride(0) if draft.shape[0] == B and B > 1 else 0
-    a.d_row_stride = draft.stride(1)
+    if draft_row_index is not None:
+        _check_dev(draft_row_index)
+        if draft.dim() != 2:
+            raise ValueError("with a draft row table the draft logits are [N, V]")
+        if draft_row_index.dtype != _torch().int32 or not draft_row_index.is_contiguous() or \
+                tuple(draft_row_index.shape) != (B, K):
+            raise ValueError("draft_row_index must be contiguous int32 [B, K]")
+        a.d_req_stride, a.d_row_stride = 0, draft.stride(0)
+        a.draft_row_index, a.draft_rows = draft_row_index.data_ptr(), draft.shape[0]
+    else:
+        a.d_req_stride = draft.stride(0) if draft.shape[0] == B and B > 1 else 0
+        a.d_row_stride = draft.stride(1)
+        a.draft_row_index, a.draft_rows = None, 0
     a.draft_tokens = draft_tokens.data_ptr()
     a.temperature = temperature.data_ptr()
     a.seed, a.step, a.request_base = int(seed) & (2 ** 64 - 1), int(step) & 0xFFFFFFFF, int(request_base)
@@ -223,7 +239,7 @@ def verify_args(target, draft, draft_tokens, temperature, accepted, tokens, debu
 
 
 def verify(target, draft, draft_tokens, temperature, seed=0, step=0, request_base=0, debug=False,
-           workspace=None, stream=None, phase_starts=0):
+           workspace=None, stream=None, phase_starts=0, draft_row_index=None):
     """One verification step on torch's current stream.  Returns
     (accepted_counts [B] int32, output_tokens [B, K+1] int32, debug_probs
     [B, K, 2] float32 or None)."""
@@ -236,7 +252,7 @@ def verify(target, draft, draft_tokens, temperature, seed=0, step=0, request_bas
     dbg = torch.empty(B, K, 2, dtype=torch.float32, device=dev) if debug else None
     ws = workspace if workspace is not None else make_workspace(B, K, V, dev)
     a = verify_args(target, draft, draft_tokens, temperature, accepted, tokens, dbg, ws, seed, step,
-                    request_base, phase_starts=phase_starts)
+                    request_base, phase_starts=phase_starts, draft_row_index=draft_row_index)
     rc = spec_verify_launch(a, _stream_ptr(stream))
     if rc != SPEC_OK:
         raise SpecError(rc)

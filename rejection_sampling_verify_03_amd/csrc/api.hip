@@ -25,7 +25,9 @@ int verify_check(const spec_verify_args* a) {
     return SPEC_EINVAL;
   if (a->t_row_stride < a->V || a->d_row_stride < a->V) return SPEC_EINVAL;
   if (a->t_req_stride != 0 && a->t_req_stride < (int64_t)(a->K + 1) * a->t_row_stride) return SPEC_EINVAL;
-  if (a->d_req_stride != 0 && a->d_req_stride < (int64_t)a->K * a->d_row_stride) return SPEC_EINVAL;
+  if (!a->draft_row_index && a->d_req_stride != 0 && a->d_req_stride < (int64_t)a->K * a->d_row_stride)
+    return SPEC_EINVAL;
+  if (a->draft_row_index && a->draft_rows < 0) return SPEC_EINVAL;
   const Layout L = make_layout(a->B, a->K, a->V);
   if ((int64_t)a->B * L.R * L.C1 > INT32_MAX || (int64_t)a->B * L.nseg > INT32_MAX) return SPEC_EINVAL;
   if (!aligned16(a->workspace)) return SPEC_EALIGN;
@@ -159,6 +161,8 @@ int spec_verify_launch(const spec_verify_args* a, hipStream_t stream) {
   P.draft = static_cast<const char*>(a->draft_logits);
   P.d_req = a->d_req_stride;
   P.d_row = a->d_row_stride;
+  P.dridx = a->draft_row_index;
+  P.draft_rows = a->draft_row_index ? a->draft_rows : 0;
   P.tokens = a->draft_tokens;
   P.temperature = a->temperature;
   P.seed = a->seed;
@@ -173,7 +177,7 @@ int spec_verify_launch(const spec_verify_args* a, hipStream_t stream) {
   P.seg = reinterpret_cast<double*>(ws + L.off_seg);
   const bool vec = aligned16(a->target_logits) && aligned16(a->draft_logits) &&
                    (a->t_row_stride * es) % 16 == 0 && (a->t_req_stride * es) % 16 == 0 &&
-                   (a->d_row_stride * es) % 16 == 0 && (a->d_req_stride * es) % 16 == 0;
+                   (a->d_row_stride * es) % 16 == 0 && (a->draft_row_index || (a->d_req_stride * es) % 16 == 0);
   P.state = reinterpret_cast<int32_t*>(ws + L.off_state);
   P.ph_lo = P.ph_nt = P.ph_nd = P.ph_check = 0;
   P.last_lo = P.phased = 0;

@@ -51,10 +51,31 @@
 
 namespace specv {
 
+// Element offset of draft row k of request b from the draft base: through
+// the row table when one is given (entry di), else by the strides.
+__device__ __forceinline__ int64_t draft_off(const VerifyParams& P, int b, int k, int di) {
+  return P.dridx ? (int64_t)di * P.d_row : (int64_t)b * P.d_req + (int64_t)k * P.d_row;
+}
+
+// Row r of request b: target rows 0..K, then draft rows K+1..2K (di: the
+// draft row table's entry for it, when there is a table).
 template <int ES>
-__device__ __forceinline__ const char* row_ptr(const VerifyParams& P, int b, int r) {
+__device__ __forceinline__ const char* row_ptr(const VerifyParams& P, int b, int r, int di = 0) {
   if (r <= P.K) return P.target + ((int64_t)b * P.t_req + (int64_t)r * P.t_row) * ES;
-  return P.draft + ((int64_t)b * P.d_req + (int64_t)(r - P.K - 1) * P.d_row) * ES;
+  return P.draft + draft_off(P, b, r - P.K - 1, di) * ES;
+}
+
+// The draft row table's entry for position k (k clamped into [0, K); 0
+// without a table), loaded unconditionally so it can be issued with other
+// loads; and whether it names a row of the buffer.
+__device__ __forceinline__ int draft_entry(const VerifyParams& P, int b, int k) {
+  const int32_t* t = P.dridx ? P.dridx : P.tokens;  // any readable [B, K] int32 array
+  const int v = t[(int64_t)b * P.K + min(max(k, 0), P.K - 1)];
+  return P.dridx ? v : 0;
+}
+
+__device__ __forceinline__ bool draft_entry_ok(const VerifyParams& P, int di) {
+  return !P.dridx || (uint32_t)di < (uint32_t)P.draft_rows;
 }
 
 // Raise the reference exponent of a lane's running (M, S) to cover a new
@@ -189,6 +210,7 @@ __device__ __forceinline__ VI block_argmax(VI v) {
 // tested position, zero for the positions from hi on when the request stopped
 // before hi (their rows are never read) and zero everywhere for invalid data.
 struct DecideShared {
+  int64_t qoff[SPEC_MAX_K];     // draft row offsets of the positions
   float m[2 * SPEC_MAX_K + 1];
   double s[2 * SPEC_MAX_K + 1];
   float z[2 * SPEC_MAX_K + 1];  // logit of the row at its position's draft token
@@ -257,8 +279,13 @@ __device__ int decide_tests(const VerifyParams& P, int b, int lo, int hi, int th
   RowPartial q[kPartBatch];
   if (row_thread) load_partials(rp, 0, P.C1, q);
 
+  const int dix = draft_entry(P, b, tid);
   const bool greedy = (T == 0.0f);
   bool mybad = invalid || !temperature_valid(T) || (tid < K && (x < 0 || x >= P.V));
+  if (!greedy && tid < K) {
+    mybad |= !draft_entry_ok(P, dix);  // a sampled request reads every draft row
+    sh.qoff[tid] = draft_off(P, b, tid, dix);
+  }
   if (row_thread && (!greedy || tid < nt)) {
     MS ms{0.f, 0.0};
     VI vi{0.f, 0};
@@ -357,7 +384,8 @@ __device__ void decide(const VerifyParams& P, int b, bool write, ReqDesc& D) {
       d.a = a;
       d.mode = (bad || greedy) ? kModeNone : (a < K ? kModeResidual : kModeBonus);
       d.s_hi = d.s_lo = 0.f;
-      d.mp = d.sp = d.mq = d.sq = d.u = d.pad = 0.0;
+      d.mp = d.sp = d.mq = d.sq = d.u = 0.0;
+      d.qoff = 0;
       if (d.mode != kModeNone) {
         temperature_scale(T, d.s_hi, d.s_lo);
         d.mp = (double)sh.m[a];
@@ -365,6 +393,7 @@ __device__ void decide(const VerifyParams& P, int b, bool write, ReqDesc& D) {
         if (a < K) {
           d.mq = (double)sh.m[K + 1 + a];
           d.sq = sh.s[K + 1 + a];
+          d.qoff = sh.qoff[a];
         }
         const uint32_t k0 = (uint32_t)(P.seed & 0xffffffffu), k1 = (uint32_t)(P.seed >> 32);
         d.u = unit_uniform(philox4x32_10((uint32_t)b + P.request_base, (uint32_t)a, P.step, 0u, k0, k1).w[1]);
@@ -403,15 +432,17 @@ __global__ __launch_bounds__(kWG) void verify_rowstats_kernel(VerifyParams P) {
   const float T = P.temperature[b];
   const int st = P.state[b];
   const int xt = P.tokens[(int64_t)b * P.K + min(k, P.K - 1)];
+  const int di = draft_entry(P, b, k);
   const bool greedy = (T == 0.0f);
   // skip: draft rows of greedy requests (never read), requests that stopped in
-  // an earlier phase, and rows of a request whose draft token at this
-  // position is out of range (the request is invalid; no statistic is used)
+  // an earlier phase, and rows of a request whose draft token or draft row
+  // entry at this position is out of range (the request is invalid; no
+  // statistic is used)
   const bool skip = (greedy & (r > P.K)) | ((P.ph_check != 0) & (st != kStateAlive)) |
-                    ((k < P.K) & ((uint32_t)xt >= (uint32_t)P.V));
+                    ((k < P.K) & ((uint32_t)xt >= (uint32_t)P.V)) | ((r > P.K) & !draft_entry_ok(P, di));
   if (skip) return;
   const int x = k < P.K ? xt : -1;
-  const char* row = row_ptr<ES>(P, b, r);
+  const char* row = row_ptr<ES>(P, b, r, di);
   const int e0 = c * P.chunk1;
   const int e1 = min(P.V, e0 + P.chunk1);
   RowPartial part;
@@ -526,7 +557,7 @@ __global__ __launch_bounds__(64) void verify_segsum_kernel(VerifyParams P) {
   if (!desc_samples(d, P.K)) return;
   const bool res = d.mode == kModeResidual;
   const char* prow = row_ptr<ES>(P, b, d.a);
-  const char* qrow = res ? row_ptr<ES>(P, b, P.K + 1 + d.a) : prow;
+  const char* qrow = res ? P.draft + d.qoff * ES : prow;
   const WeightCtx w = make_ctx(d);
   double rs, ps;
   if (res) segment_sums<ES, VEC, true>(prow, qrow, w, j * kSeg, P.V, rs, ps);
@@ -606,7 +637,7 @@ __global__ __launch_bounds__(kWGD) void verify_draw_kernel(VerifyParams P) {
   }
   const bool resmode = d.mode == kModeResidual;
   const char* prow = row_ptr<ES>(P, b, d.a);
-  const char* qrow = resmode ? row_ptr<ES>(P, b, P.K + 1 + d.a) : prow;
+  const char* qrow = resmode ? P.draft + d.qoff * ES : prow;
   const WeightCtx w = make_ctx(d);
   int y = -1;  // no positive weight anywhere: only reachable outside the data contract
   if (found >= 0)

@@ -15,6 +15,8 @@ struct VerifyParams {
   int64_t t_req, t_row;
   const char* draft;
   int64_t d_req, d_row;
+  const int32_t* dridx;  // draft row table [B, K] (rows of a [draft_rows, V] buffer) or null
+  int32_t draft_rows;
   const int32_t* tokens;
   const float* temperature;
   uint64_t seed;

@@ -32,7 +32,7 @@ struct ReqDesc {  // decision of one request, read by the draw
   double mp, sp;  // reference exponent and normaliser of p at row a
   double mq, sq;  // same for q (residual mode)
   double u;       // the sampling uniform of row a
-  double pad;
+  int64_t qoff;   // element offset of draft row a from the draft base (residual mode)
 };
 
 static_assert(sizeof(RowPartial) == 16, "RowPartial layout");

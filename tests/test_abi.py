@@ -110,6 +110,13 @@ def test_verify_argument_errors(sv):
         a = _valid_verify_args(sv)
         a.phase_starts = mask
         assert launch(a) == want, mask
+    # a draft row table: its row count must not be negative, and the request stride is unused
+    a = _valid_verify_args(sv)
+    a.draft_row_index, a.draft_rows = 0x10000, -1
+    assert launch(a) == sv.SPEC_EINVAL
+    a = _valid_verify_args(sv)
+    a.draft_row_index, a.draft_rows, a.d_req_stride = 0x10000, 10, 5
+    assert launch(a) == sv.SPEC_EWORKSPACE
     # request stride 0 (shared rows) is accepted by validation
     a = _valid_verify_args(sv)
     a.t_req_stride = a.d_req_stride = 0

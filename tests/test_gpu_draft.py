@@ -15,7 +15,7 @@ import torch
 
 import oracle
 import workloads
-from parity import WINDOW
+from parity import WINDOW, Report, compare
 from stats_helpers import chi2_pvalue, softmax_rows
 
 pytestmark = pytest.mark.gpu
@@ -159,3 +159,73 @@ def test_chained_after_expand_full_size(sv):
         ex += e_
         nf += len(near)
     say("  64 positions: %d exact, %d near-threshold" % (ex, nf))
+
+
+def test_verify_reads_drafter_rows_in_place(sv):
+    """A verification whose draft rows come from a [N, V] drafter buffer
+    through a row table gives the bits of the same verification on the
+    gathered [B, K, V] draft tensor, in one pass and in early-exit phases; an
+    out-of-range entry invalidates a sampled request only."""
+    say("case: verify with a draft row table")
+    B, K, V, N = 24, 5, 40000, 200
+    dev = torch.device("cuda")
+    vin = workloads.mixture_inputs("table B24 K5 V40000", B, K, V, torch.bfloat16, 13, dev,
+                                   temps=(0.0, 0.6, 1.0), lam_lo=0.05, lam_hi=0.6)
+    g = workloads._gen(14, "cuda")
+    perm = torch.randperm(N, generator=g, device=dev)[:B * K].reshape(B, K).to(torch.int32).contiguous()
+    buf = workloads.zipf_logits(N, V, g, "cuda").to(torch.bfloat16)
+    buf[perm.reshape(-1).long()] = vin.draft[:, :K].reshape(B * K, V)
+    for mask in (0, 0b100100):
+        one = sv.verify(vin.target, vin.draft, vin.draft_tokens, vin.temperature, seed=3, step=1, debug=True,
+                        phase_starts=mask)
+        tab = sv.verify(vin.target, buf, vin.draft_tokens, vin.temperature, seed=3, step=1, debug=True,
+                        phase_starts=mask, draft_row_index=perm)
+        for u, v in zip(one, tab):
+            assert torch.equal(u, v), mask
+    bad = perm.clone()
+    bad[0, 2] = N
+    bad[1, 0] = -3
+    acc, tok, _ = sv.verify(vin.target, buf, vin.draft_tokens, vin.temperature, seed=3, step=1,
+                            draft_row_index=bad)
+    acc0, tok0, _ = sv.verify(vin.target, vin.draft, vin.draft_tokens, vin.temperature, seed=3, step=1)
+    T = vin.temperature.cpu().numpy()
+    for b in (0, 1):
+        if T[b] > 0:
+            assert acc[b] == -1 and (tok[b] == -1).all()
+        else:  # greedy requests read no draft rows
+            assert acc[b] == acc0[b] and torch.equal(tok[b], tok0[b])
+    assert torch.equal(acc[2:], acc0[2:]) and torch.equal(tok[2:], tok0[2:])
+
+
+def test_peagle_loop_on_device(sv):
+    """One P-EAGLE round on device with no host round trip: expansion ->
+    draft tokens sampled from the drafter logits at its new-token indices ->
+    the next verification reading those drafter rows in place and checking
+    the sampled tokens; the verification is checked against the oracle on the
+    gathered rows."""
+    say("case: P-EAGLE loop: expand -> draft sample -> verify")
+    B, K, V = 32, 5, 32768
+    dev = torch.device("cuda")
+    e = workloads.expand_inputs(B=B, K=K, H=16, seed=21, device="cuda", vocab=V)
+    out = sv.expand(e.in_token_ids, e.in_positions, e.in_start, e.accepted, e.bonus, K, e.mask_id)
+    nti = out.new_token_indices
+    g = workloads._gen(22, "cuda")
+    drafter = workloads.zipf_logits(e.N_out, V, g, "cuda").to(torch.bfloat16)
+    T = torch.tensor([0.0, 0.6, 1.0], device=dev)[torch.randint(0, 3, (B,), generator=g, device=dev)]
+    x = sv.draft_sample(drafter, nti, T, seed=30, step=7)
+    # target rows: the drafter's rows perturbed (a stand-in for the target model)
+    target = (drafter[nti.reshape(-1).long()].float().reshape(B, K, V) +
+              0.7 * torch.randn(B, K, V, generator=g, device=dev))
+    target = torch.cat([target, workloads.zipf_logits(B, V, g, "cuda").reshape(B, 1, V)], dim=1)
+    target = target.to(torch.bfloat16).contiguous()
+    acc, tok, dbg = sv.verify(target, drafter, x, T, seed=30, step=8, debug=True, draft_row_index=nti)
+    torch.cuda.synchronize()
+    gathered = drafter[nti.reshape(-1).long()].reshape(B, K, V)
+    rep = Report()
+    compare(workloads.logits_numpy(target), workloads.logits_numpy(gathered), x.cpu().numpy(), T.cpu().numpy(),
+            acc.cpu().numpy(), tok.cpu().numpy(), dbg.cpu().numpy(), seed=30, step=8, report=rep)
+    say("  ", rep.summary())
+    assert rep.ok(), rep.failures[:5]
+    a = acc.cpu().numpy()
+    say("  accepted per request: mean %.2f" % a.mean())
+    assert (a >= 0).all()
