@@ -41,7 +41,7 @@ class VerifyArgs(ctypes.Structure):
         ("uniforms", ctypes.c_void_p),
         ("accepted", ctypes.c_void_p), ("out_tokens", ctypes.c_void_p),
         ("debug_probs", ctypes.c_void_p), ("trace", ctypes.c_void_p),
-        ("mutation", ctypes.c_int32), ("nthreads", ctypes.c_int32),
+        ("mutation", ctypes.c_int32), ("nthreads", ctypes.c_int32), ("num_drafts", ctypes.c_void_p),
     ]
 
 
@@ -202,7 +202,7 @@ class VerifyResult:
 
 
 def _verify_struct(target, draft, draft_tokens, temperature, seed, step, request_base,
-                   uniforms, mutation, nthreads, keep):
+                   uniforms, mutation, nthreads, keep, num_drafts=None):
     t, dt = _logit_buffer(target)
     d, dd = _logit_buffer(draft)
     if dt != dd:
@@ -226,23 +226,30 @@ def _verify_struct(target, draft, draft_tokens, temperature, seed, step, request
     a.seed, a.step, a.request_base = int(seed) & (2**64 - 1), int(step) & 0xFFFFFFFF, int(request_base)
     a.uniforms = _ptr(u)
     a.mutation, a.nthreads = int(mutation), int(nthreads)
+    if num_drafts is not None:
+        nd = _c(num_drafts, np.int32).reshape(B)
+        keep.append(nd)
+        a.num_drafts = _ptr(nd)
+    else:
+        a.num_drafts = None
     return a, B, K, V
 
 
 def verify(target, draft, draft_tokens, temperature, seed=0, step=0, request_base=0,
-           uniforms=None, debug=True, trace=True, mutation=0, nthreads=0):
+           uniforms=None, debug=True, trace=True, mutation=0, nthreads=0, num_drafts=None):
     """Run the oracle verification.
 
     target: [B, K+1, V] float32 logits, or uint16 bf16 bit patterns; a leading
     dimension of 1 shares the rows across all B requests (B from draft_tokens).
     draft:  [B or 1, >=K, V] same dtype.  draft_tokens: [B, K] int.  temperature: [B].
     uniforms: optional [B, K+1, 2] override of the Philox draws.
+    num_drafts: optional [B] ragged draft counts K_b <= K (bonus at row K_b).
     Returns a VerifyResult (accepted [B], tokens [B, K+1], debug_probs [B, K, 2],
     trace [B, K+1, 3] = (u_accept, threshold, u_sample), n_bad).
     """
     keep = []
     a, B, K, V = _verify_struct(target, draft, draft_tokens, temperature, seed, step, request_base,
-                                uniforms, mutation, nthreads, keep)
+                                uniforms, mutation, nthreads, keep, num_drafts)
     acc = np.zeros(B, np.int32)
     tok = np.zeros((B, K + 1), np.int32)
     dbg = np.zeros((B, K, 2), np.float32) if debug else None
@@ -254,11 +261,11 @@ def verify(target, draft, draft_tokens, temperature, seed=0, step=0, request_bas
     return VerifyResult(acc, tok, dbg, trc, rc)
 
 
-def sampling_weights(target, draft, draft_tokens, temperature, b, j, mutation=0):
+def sampling_weights(target, draft, draft_tokens, temperature, b, j, mutation=0, num_drafts=None):
     """The weights (and their sum) the oracle samples from at row j of request b."""
     keep = []
     a, B, K, V = _verify_struct(target, draft, draft_tokens, temperature, 0, 0, 0, None,
-                                mutation, 1, keep)
+                                mutation, 1, keep, num_drafts)
     w = np.zeros(V, np.float64)
     W = ctypes.c_double(0.0)
     rc = lib().oracle_sampling_weights(ctypes.byref(a), int(b), int(j), _ptr(w), ctypes.byref(W))

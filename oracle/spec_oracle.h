@@ -91,10 +91,13 @@ typedef struct {
   double* trace;                     /* nullable out [B, K+1, 3]: u_accept, threshold, u_sample */
   int32_t mutation;                  /* 0 = the method; 1, 2 = planted mistakes for test power */
   int32_t nthreads;                  /* OpenMP threads over requests (<=0: library default) */
+  const int32_t* num_drafts;         /* nullable [B]: drafts K_b <= K of request b (ragged K);
+                                        positions k >= K_b do not exist, the bonus is at row K_b */
 } oracle_verify_args;
 
 /* Returns the number of requests rejected as invalid data (bad token id,
- * temperature < 0 / NaN / inf, row without a finite maximum); their outputs
+ * temperature < 0 / NaN / inf, K_b outside [0, K], row without a finite
+ * maximum); their outputs
  * are accepted = -1 and out_tokens all -1.  Returns -1 on bad arguments. */
 int oracle_verify(const oracle_verify_args* a);
 

@@ -166,19 +166,25 @@ static int row_has_finite_max(const void* row, int dtype, int V) {
   return 0;
 }
 
-/* Data checks made before any decision: every token id in range, a usable
- * temperature, and for sampled requests a finite maximum in every row the
- * parallel formulation reads (target rows 0..K, draft rows 0..K-1). */
+/* Drafts of request b: K, or its entry of the ragged table. */
+static int drafts_of(const oracle_verify_args* a, int b) { return a->num_drafts ? a->num_drafts[b] : a->K; }
+
+/* Data checks made before any decision: a draft count in [0, K], every token
+ * id in range, a usable temperature, and for sampled requests a finite
+ * maximum in every row the parallel formulation reads (target rows 0..K_b,
+ * draft rows 0..K_b-1). */
 static int request_valid(const oracle_verify_args* a, int b) {
+  const int Kb = drafts_of(a, b);
+  if (Kb < 0 || Kb > a->K) return 0;
   const int32_t* x = a->draft_tokens + (int64_t)b * a->K;
-  for (int k = 0; k < a->K; ++k)
+  for (int k = 0; k < Kb; ++k)
     if (x[k] < 0 || x[k] >= a->V) return 0;
   float T = a->temperature[b];
   if (!(T >= 0.0f) || isinf(T)) return 0;
   if (T > 0.0f) {
-    for (int k = 0; k <= a->K; ++k)
+    for (int k = 0; k <= Kb; ++k)
       if (!row_has_finite_max(trow(a, b, k), a->dtype, a->V)) return 0;
-    for (int k = 0; k < a->K; ++k)
+    for (int k = 0; k < Kb; ++k)
       if (!row_has_finite_max(drow(a, b, k), a->dtype, a->V)) return 0;
   }
   return 1;
@@ -188,7 +194,7 @@ static void sampling_weights(const oracle_verify_args* a, int b, int j, double* 
                              double* w, double* W) {
   double T = (double)a->temperature[b];
   oracle_softmax(trow(a, b, j), a->dtype, a->V, T, p);
-  if (j == a->K || a->mutation == 1) {
+  if (j == drafts_of(a, b) || a->mutation == 1) {
     /* the bonus row samples from p itself (mutation 1 plants the mistake of
      * resampling from p instead of the residual) */
     double S = 0.0;
@@ -204,7 +210,8 @@ static void sampling_weights(const oracle_verify_args* a, int b, int j, double* 
 }
 
 static int verify_one(const oracle_verify_args* a, int b, double* p, double* q, double* w) {
-  const int K = a->K, V = a->V;
+  int K = a->K;
+  const int V = a->V;
   const int32_t* x = a->draft_tokens + (int64_t)b * K;
   int32_t* out = a->out_tokens + (int64_t)b * (K + 1);
   double* tr = a->trace ? a->trace + (int64_t)b * (K + 1) * 3 : NULL;
@@ -219,6 +226,7 @@ static int verify_one(const oracle_verify_args* a, int b, double* p, double* q, 
     return 1;
   }
   const double T = (double)a->temperature[b];
+  K = drafts_of(a, b); /* positions k >= K_b do not exist; the bonus row is K_b */
 
   if (T == 0.0) { /* greedy */
     for (int k = 0; k < K; ++k) {
@@ -239,8 +247,8 @@ static int verify_one(const oracle_verify_args* a, int b, double* p, double* q, 
     for (int k = 0; k < K; ++k) {
       oracle_softmax(trow(a, b, k), a->dtype, V, T, p);
       oracle_softmax(drow(a, b, k), a->dtype, V, T, q);
-      a->debug_probs[((int64_t)b * K + k) * 2 + 0] = (float)p[x[k]];
-      a->debug_probs[((int64_t)b * K + k) * 2 + 1] = (float)q[x[k]];
+      a->debug_probs[((int64_t)b * a->K + k) * 2 + 0] = (float)p[x[k]];
+      a->debug_probs[((int64_t)b * a->K + k) * 2 + 1] = (float)q[x[k]];
     }
   }
 
@@ -325,7 +333,7 @@ int oracle_verify(const oracle_verify_args* a) {
 
 int oracle_sampling_weights(const oracle_verify_args* a, int b, int j, double* w, double* W) {
   if (!args_ok(a) || b < 0 || b >= a->B || j < 0 || j > a->K) return -1;
-  if (!request_valid(a, b) || !(a->temperature[b] > 0.0f)) return -1;
+  if (!request_valid(a, b) || !(a->temperature[b] > 0.0f) || j > drafts_of(a, b)) return -1;
   double* p = (double*)malloc(sizeof(double) * (size_t)a->V);
   double* q = (double*)malloc(sizeof(double) * (size_t)a->V);
   sampling_weights(a, b, j, p, q, w, W);
