@@ -105,6 +105,10 @@ typedef struct {
                                   e.g. the drafter's logits at the new-token indices */
   int32_t draft_rows;          /* rows of that buffer; an entry outside [0, draft_rows) makes a
                                   sampled request invalid */
+  const int32_t* num_drafts;   /* device [B] or NULL: ragged draft counts K_b in [0, K]; positions
+                                  k >= K_b do not exist (their tokens and rows are never read), a
+                                  request that accepts all K_b drafts takes the bonus from target
+                                  row K_b; a count outside [0, K] makes the request invalid */
 } spec_verify_args;
 
 /* Early exit (same explainer page, section "核心思想": a request stops at
@@ -138,8 +142,9 @@ size_t spec_verify_workspace_bytes(int32_t B, int32_t K, int32_t V);
 
 /* Enqueue one verification step.  A request whose data is invalid (a draft
  * token outside [0, V), a temperature that is negative, NaN or infinite, a
- * draft row table entry of a sampled request outside [0, draft_rows), or a
- * row of a sampled request without a finite normaliser) gets
+ * draft row table entry of a sampled request outside [0, draft_rows), a draft
+ * count outside [0, K], or a row of a sampled request without a finite
+ * normaliser) gets
  * accepted_counts = -1, output_tokens all -1 and debug_probs 0. */
 int spec_verify_launch(const spec_verify_args* args, hipStream_t stream);
 

@@ -332,7 +332,10 @@ int oracle_verify(const oracle_verify_args* a) {
 }
 
 int oracle_sampling_weights(const oracle_verify_args* a, int b, int j, double* w, double* W) {
-  if (!args_ok(a) || b < 0 || b >= a->B || j < 0 || j > a->K) return -1;
+  /* inputs only: this call writes no verification outputs */
+  if (!a || a->B < 1 || a->K < 1 || a->V < 1 || (a->dtype != 0 && a->dtype != 1)) return -1;
+  if (!a->target || !a->draft || !a->draft_tokens || !a->temperature || !w || !W) return -1;
+  if (b < 0 || b >= a->B || j < 0 || j > a->K) return -1;
   if (!request_valid(a, b) || !(a->temperature[b] > 0.0f) || j > drafts_of(a, b)) return -1;
   double* p = (double*)malloc(sizeof(double) * (size_t)a->V);
   double* q = (double*)malloc(sizeof(double) * (size_t)a->V);

@@ -36,6 +36,7 @@ class SpecVerifyArgs(ctypes.Structure):
         ("debug_probs", ctypes.c_void_p), ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
         ("phase_event", ctypes.c_void_p), ("phase_starts", ctypes.c_uint64),
         ("draft_row_index", ctypes.c_void_p), ("draft_rows", ctypes.c_int32),
+        ("num_drafts", ctypes.c_void_p),
     ]
 
 
@@ -185,7 +186,8 @@ def make_workspace(B, K, V, device="cuda"):
 
 
 def verify_args(target, draft, draft_tokens, temperature, accepted, tokens, debug, workspace,
-                seed=0, step=0, request_base=0, phase_event=None, phase_starts=0, draft_row_index=None):
+                seed=0, step=0, request_base=0, phase_event=None, phase_starts=0, draft_row_index=None,
+                num_drafts=None):
     """Fill a SpecVerifyArgs from tensors (no copies).
 
     With draft_row_index [B, K] int32, draft is a 2-D [N, V] buffer (e.g. the
@@ -235,11 +237,18 @@ def verify_args(target, draft, draft_tokens, temperature, accepted, tokens, debu
     a.workspace_bytes = workspace.numel() * workspace.element_size()
     a.phase_event = phase_event
     a.phase_starts = int(phase_starts)
+    if num_drafts is not None:
+        _check_dev(num_drafts)
+        if num_drafts.dtype != _torch().int32 or not num_drafts.is_contiguous() or num_drafts.numel() != B:
+            raise ValueError("num_drafts must be contiguous int32 [B]")
+        a.num_drafts = num_drafts.data_ptr()
+    else:
+        a.num_drafts = None
     return a
 
 
 def verify(target, draft, draft_tokens, temperature, seed=0, step=0, request_base=0, debug=False,
-           workspace=None, stream=None, phase_starts=0, draft_row_index=None):
+           workspace=None, stream=None, phase_starts=0, draft_row_index=None, num_drafts=None):
     """One verification step on torch's current stream.  Returns
     (accepted_counts [B] int32, output_tokens [B, K+1] int32, debug_probs
     [B, K, 2] float32 or None)."""
@@ -252,7 +261,8 @@ def verify(target, draft, draft_tokens, temperature, seed=0, step=0, request_bas
     dbg = torch.empty(B, K, 2, dtype=torch.float32, device=dev) if debug else None
     ws = workspace if workspace is not None else make_workspace(B, K, V, dev)
     a = verify_args(target, draft, draft_tokens, temperature, accepted, tokens, dbg, ws, seed, step,
-                    request_base, phase_starts=phase_starts, draft_row_index=draft_row_index)
+                    request_base, phase_starts=phase_starts, draft_row_index=draft_row_index,
+                    num_drafts=num_drafts)
     rc = spec_verify_launch(a, _stream_ptr(stream))
     if rc != SPEC_OK:
         raise SpecError(rc)

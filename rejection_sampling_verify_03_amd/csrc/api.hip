@@ -162,6 +162,7 @@ int spec_verify_launch(const spec_verify_args* a, hipStream_t stream) {
   P.d_req = a->d_req_stride;
   P.d_row = a->d_row_stride;
   P.dridx = a->draft_row_index;
+  P.num_drafts = a->num_drafts;
   P.draft_rows = a->draft_row_index ? a->draft_rows : 0;
   P.tokens = a->draft_tokens;
   P.temperature = a->temperature;

@@ -78,6 +78,16 @@ __device__ __forceinline__ bool draft_entry_ok(const VerifyParams& P, int di) {
   return !P.dridx || (uint32_t)di < (uint32_t)P.draft_rows;
 }
 
+// Drafts K_b of request b (ragged counts, else K), loaded unconditionally so
+// it can be issued with other loads; -1 for a count outside [0, K] (the
+// request is invalid).
+__device__ __forceinline__ int drafts_of(const VerifyParams& P, int b) {
+  const int32_t* t = P.num_drafts ? P.num_drafts : reinterpret_cast<const int32_t*>(P.temperature);
+  const int v = t[b];
+  const int kb = P.num_drafts ? v : P.K;
+  return (kb >= 0 && kb <= P.K) ? kb : -1;
+}
+
 // Raise the reference exponent of a lane's running (M, S) to cover a new
 // group maximum gm (the rescale is an exact power of two).
 __device__ __forceinline__ void raise_ref(float& M, double& S, float gm, float s_hi) {
@@ -216,6 +226,7 @@ struct DecideShared {
   float z[2 * SPEC_MAX_K + 1];  // logit of the row at its position's draft token
   int g[SPEC_MAX_K + 1];
   int a;
+  int kb;  // drafts of the request
 };
 
 // Merge the chunk partials of one row in chunk order, the first batch of 8
@@ -268,6 +279,7 @@ __device__ int decide_tests(const VerifyParams& P, int b, int lo, int hi, int th
   // rows too, ignored for a greedy request).
   const int st = P.state[b];
   const float T = P.temperature[b];
+  const int kb_ = drafts_of(P, b);
   const int x = P.tokens[(int64_t)b * K + min(tid, K - 1)];
   const int nt = thi - lo;
   const int nd = min(thi, K) - lo;
@@ -281,12 +293,16 @@ __device__ int decide_tests(const VerifyParams& P, int b, int lo, int hi, int th
 
   const int dix = draft_entry(P, b, tid);
   const bool greedy = (T == 0.0f);
-  bool mybad = invalid || !temperature_valid(T) || (tid < K && (x < 0 || x >= P.V));
-  if (!greedy && tid < K) {
+  // positions k >= K_b do not exist: no token, no draft row, no test; target
+  // rows up to K_b (the bonus row) exist
+  const int kb = max(kb_, 0);
+  bool mybad = invalid || kb_ < 0 || !temperature_valid(T) || (tid < kb && (x < 0 || x >= P.V));
+  if (!greedy && tid < kb) {
     mybad |= !draft_entry_ok(P, dix);  // a sampled request reads every draft row
     sh.qoff[tid] = draft_off(P, b, tid, dix);
   }
-  if (row_thread && (!greedy || tid < nt)) {
+  const bool row_exists = tid < nt ? k <= kb : k < kb;
+  if (row_thread && row_exists && (!greedy || tid < nt)) {
     MS ms{0.f, 0.0};
     VI vi{0.f, 0};
     float z;
@@ -294,7 +310,7 @@ __device__ int decide_tests(const VerifyParams& P, int b, int lo, int hi, int th
       merge_row<ES, true>(P, rp, q, -1, ms, vi, z);
       sh.g[r] = vi.i;
     } else {
-      merge_row<ES, false>(P, rp, q, k < K ? xr : -1, ms, vi, z);
+      merge_row<ES, false>(P, rp, q, k < kb ? xr : -1, ms, vi, z);
       sh.m[r] = ms.m;
       sh.s[r] = ms.s;
       sh.z[r] = z;
@@ -306,7 +322,7 @@ __device__ int decide_tests(const VerifyParams& P, int b, int lo, int hi, int th
   if (tid < 64) {  // wave 0: one lane per draft position
     bool acc = tid < lo;
     float dp = 0.f, dq = 0.f;
-    if (test && tid >= lo && tid < hi && !bad) {
+    if (test && tid >= lo && tid < min(hi, kb) && !bad) {
       if (greedy) {
         acc = (x == sh.g[tid]);
       } else {
@@ -324,7 +340,8 @@ __device__ int decide_tests(const VerifyParams& P, int b, int lo, int hi, int th
       }
     }
     const uint64_t mask = __ballot(acc);
-    const int a = bad ? -1 : (test ? (int)__builtin_ctzll(~mask) : known);  // lanes >= hi fail: a <= hi
+    // lanes >= min(hi, K_b) fail: a <= min(hi, K_b)
+    const int a = bad ? -1 : (test ? (int)__builtin_ctzll(~mask) : known);
     if (debug && P.debug && tid < K) {
       float* d = P.debug + ((int64_t)b * K + tid) * 2;
       if (bad || (tid >= hi && a < hi)) {
@@ -335,7 +352,10 @@ __device__ int decide_tests(const VerifyParams& P, int b, int lo, int hi, int th
         d[1] = dq;
       }
     }
-    if (tid == 0) sh.a = a;
+    if (tid == 0) {
+      sh.a = a;
+      sh.kb = kb;
+    }
   }
   __syncthreads();
   return sh.a;
@@ -382,7 +402,7 @@ __device__ void decide(const VerifyParams& P, int b, bool write, ReqDesc& D) {
     if (tid == 0) {
       ReqDesc d;
       d.a = a;
-      d.mode = (bad || greedy) ? kModeNone : (a < K ? kModeResidual : kModeBonus);
+      d.mode = (bad || greedy) ? kModeNone : (a < sh.kb ? kModeResidual : kModeBonus);
       d.s_hi = d.s_lo = 0.f;
       d.mp = d.sp = d.mq = d.sq = d.u = 0.0;
       d.qoff = 0;
@@ -390,7 +410,7 @@ __device__ void decide(const VerifyParams& P, int b, bool write, ReqDesc& D) {
         temperature_scale(T, d.s_hi, d.s_lo);
         d.mp = (double)sh.m[a];
         d.sp = sh.s[a];
-        if (a < K) {
+        if (a < sh.kb) {
           d.mq = (double)sh.m[K + 1 + a];
           d.sq = sh.s[K + 1 + a];
           d.qoff = sh.qoff[a];
@@ -433,15 +453,18 @@ __global__ __launch_bounds__(kWG) void verify_rowstats_kernel(VerifyParams P) {
   const int st = P.state[b];
   const int xt = P.tokens[(int64_t)b * P.K + min(k, P.K - 1)];
   const int di = draft_entry(P, b, k);
+  const int kb = drafts_of(P, b);
   const bool greedy = (T == 0.0f);
   // skip: draft rows of greedy requests (never read), requests that stopped in
-  // an earlier phase, and rows of a request whose draft token or draft row
-  // entry at this position is out of range (the request is invalid; no
-  // statistic is used)
+  // an earlier phase, rows past the request's drafts (target row > K_b, draft
+  // row >= K_b: they do not exist), and rows of a request whose draft count,
+  // draft token or draft row entry is out of range (the request is invalid;
+  // no statistic is used)
   const bool skip = (greedy & (r > P.K)) | ((P.ph_check != 0) & (st != kStateAlive)) |
-                    ((k < P.K) & ((uint32_t)xt >= (uint32_t)P.V)) | ((r > P.K) & !draft_entry_ok(P, di));
+                    ((k < kb) & ((uint32_t)xt >= (uint32_t)P.V)) | ((r > P.K) & !draft_entry_ok(P, di)) |
+                    (kb < 0) | ((r <= P.K) & (k > kb)) | ((r > P.K) & (k >= kb));
   if (skip) return;
-  const int x = k < P.K ? xt : -1;
+  const int x = k < kb ? xt : -1;
   const char* row = row_ptr<ES>(P, b, r, di);
   const int e0 = c * P.chunk1;
   const int e1 = min(P.V, e0 + P.chunk1);
@@ -542,7 +565,9 @@ __global__ __launch_bounds__(kWG) void verify_decide_kernel(VerifyParams P) {
 
 // A decision record that calls for a draw (anything else samples nothing).
 __device__ __forceinline__ bool desc_samples(const ReqDesc& d, int K) {
-  return (d.mode == kModeResidual && d.a >= 0 && d.a < K) || (d.mode == kModeBonus && d.a == K);
+  // residual at a rejected position a < K_b <= K; bonus at row a = K_b <= K
+  return (d.mode == kModeResidual || d.mode == kModeBonus) && d.a >= 0 && d.a <= K &&
+         (d.mode == kModeBonus || d.a < K);
 }
 
 // The sums of one 4096-logit segment of one request's sampling row(s): one

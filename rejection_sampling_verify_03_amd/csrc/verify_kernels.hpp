@@ -17,6 +17,7 @@ struct VerifyParams {
   int64_t d_req, d_row;
   const int32_t* dridx;  // draft row table [B, K] (rows of a [draft_rows, V] buffer) or null
   int32_t draft_rows;
+  const int32_t* num_drafts;  // ragged draft counts [B] or null (all K)
   const int32_t* tokens;
   const float* temperature;
   uint64_t seed;

@@ -34,8 +34,8 @@ class Report:
                 % (self.requests, self.exact, len(self.near), len(self.failures), self.max_prob_err))
 
 
-def _sampling_margin(tl, dl, x, T, b_local, j, u, y_g, y_o):
-    w, W = oracle.sampling_weights(tl, dl, x, T, b_local, j)
+def _sampling_margin(tl, dl, x, T, b_local, j, u, y_g, y_o, num_drafts=None):
+    w, W = oracle.sampling_weights(tl, dl, x, T, b_local, j, num_drafts=num_drafts)
     F = np.cumsum(w) / W
     lo, hi = min(y_g, y_o), max(y_g, y_o)
     if lo < 0:
@@ -44,13 +44,13 @@ def _sampling_margin(tl, dl, x, T, b_local, j, u, y_g, y_o):
 
 
 def compare(tl, dl, x, T, acc_g, tok_g, dbg_g=None, seed=0, step=0, request_base=0, report=None,
-            check_debug=True):
+            check_debug=True, num_drafts=None):
     """Compare GPU outputs for a batch with the oracle run on the same host
     inputs (tl, dl: oracle-format logits [B, K+1, V]; x [B, K]; T [B]).
     request_base is the global index of row 0 of this batch."""
     rep = report if report is not None else Report()
     res = oracle.verify(tl, dl, x, T, seed=seed, step=step, request_base=request_base,
-                        debug=dbg_g is not None and check_debug, trace=True)
+                        debug=dbg_g is not None and check_debug, trace=True, num_drafts=num_drafts)
     B, K1 = res.tokens.shape
     K = K1 - 1
     acc_g = np.asarray(acc_g)
@@ -77,7 +77,8 @@ def compare(tl, dl, x, T, acc_g, tok_g, dbg_g=None, seed=0, step=0, request_base
             u = res.trace[b, k, 2]
             margin = _sampling_margin(tl[b:b + 1] if tl.shape[0] > 1 else tl,
                                       dl[b:b + 1] if dl.shape[0] > 1 else dl,
-                                      x[b:b + 1], T[b:b + 1], 0, k, u, int(tg[k]), int(to[k]))
+                                      x[b:b + 1], T[b:b + 1], 0, k, u, int(tg[k]), int(to[k]),
+                                      None if num_drafts is None else np.asarray(num_drafts)[b:b + 1])
             kind = "sample@%d" % k
         if margin < WINDOW:
             rep.near.append((gb, kind, margin))
