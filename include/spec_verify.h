@@ -222,6 +222,16 @@ typedef struct {
  * gather) as a single kernel. */
 int spec_expand_launch(const spec_expand_args* args, hipStream_t stream);
 
+/* Enqueue only the hidden-row gather of an expansion.  The hidden rows depend
+ * on in_start, target_hidden and mask_hidden alone -- not on the accepted
+ * counts -- so this may run on another stream while the verification that
+ * produces the counts is still running; spec_expand_launch with
+ * out_hidden = NULL then writes the metadata.  Reads in_start, target_hidden,
+ * hidden_row_stride, mask_hidden, B, K, H, N_in; writes out_hidden for every
+ * request whose window is valid (n_b >= 1 inside [0, N_in], in_start[0] = 0,
+ * in_start[B] = N_in), whatever its accepted count. */
+int spec_expand_hidden_launch(const spec_expand_args* args, hipStream_t stream);
+
 /* ----------------------------------------------------------- draft sampling
  *
  * The next draft tokens, sampled from the drafter's logits at the new-token

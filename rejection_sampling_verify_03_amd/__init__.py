@@ -21,7 +21,8 @@ SPEC_F32, SPEC_BF16 = 0, 1
 SPEC_MAX_K = 63
 
 EXPORTED = ("spec_verify_workspace_bytes", "spec_verify_plan_phases", "spec_verify_launch",
-            "spec_expand_launch", "spec_draft_workspace_bytes", "spec_draft_sample_launch",
+            "spec_expand_launch", "spec_expand_hidden_launch", "spec_draft_workspace_bytes",
+            "spec_draft_sample_launch",
             "spec_status_string")
 
 
@@ -87,6 +88,8 @@ def _load():
     L.spec_verify_launch.restype = ctypes.c_int
     L.spec_expand_launch.argtypes = [ctypes.POINTER(SpecExpandArgs), ctypes.c_void_p]
     L.spec_expand_launch.restype = ctypes.c_int
+    L.spec_expand_hidden_launch.argtypes = [ctypes.POINTER(SpecExpandArgs), ctypes.c_void_p]
+    L.spec_expand_hidden_launch.restype = ctypes.c_int
     L.spec_draft_workspace_bytes.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32]
     L.spec_draft_workspace_bytes.restype = ctypes.c_size_t
     L.spec_draft_sample_launch.argtypes = [ctypes.POINTER(SpecDraftArgs), ctypes.c_void_p]
@@ -132,6 +135,10 @@ def spec_verify_launch(args, stream_ptr):
 
 def spec_expand_launch(args, stream_ptr):
     return int(lib.spec_expand_launch(ctypes.byref(args), stream_ptr))
+
+
+def spec_expand_hidden_launch(args, stream_ptr):
+    return int(lib.spec_expand_hidden_launch(ctypes.byref(args), stream_ptr))
 
 
 def spec_draft_workspace_bytes(B, K, V):

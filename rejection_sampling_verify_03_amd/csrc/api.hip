@@ -188,10 +188,9 @@ int spec_verify_launch(const spec_verify_args* a, hipStream_t stream) {
              : SPEC_ELAUNCH;
 }
 
-int spec_expand_launch(const spec_expand_args* a, hipStream_t stream) {
-  const int rc = expand_check(a);
-  if (rc != SPEC_OK || a->B == 0) return rc;
+static int expand_launch(const spec_expand_args* a, bool hidden_only, hipStream_t stream) {
   ExpandParams P;
+  P.hidden_only = hidden_only ? 1 : 0;
   P.B = a->B;
   P.K = a->K;
   P.H = a->H;
@@ -231,6 +230,23 @@ int spec_expand_launch(const spec_expand_args* a, hipStream_t stream) {
   const bool vec = (a->H % 8) == 0 && (a->hidden_row_stride % 8) == 0 && aligned16(a->target_hidden) &&
                    aligned16(a->mask_hidden) && aligned16(a->out_hidden);
   return launch_expand(P, vec, stream) == hipSuccess ? SPEC_OK : SPEC_ELAUNCH;
+}
+
+int spec_expand_launch(const spec_expand_args* a, hipStream_t stream) {
+  const int rc = expand_check(a);
+  if (rc != SPEC_OK || a->B == 0) return rc;
+  return expand_launch(a, false, stream);
+}
+
+int spec_expand_hidden_launch(const spec_expand_args* a, hipStream_t stream) {
+  if (!a) return SPEC_EINVAL;
+  if (a->B < 0 || a->K < 1 || a->H < 0 || a->N_in < 0) return SPEC_EINVAL;
+  if ((int64_t)a->N_in + (int64_t)a->B * (a->K - 1) > INT32_MAX) return SPEC_EINVAL;
+  if (a->B == 0 || a->H == 0) return SPEC_OK;
+  if (!a->in_start || !a->out_hidden || !a->mask_hidden || (a->N_in > 0 && !a->target_hidden))
+    return SPEC_EINVAL;
+  if (a->hidden_row_stride < a->H) return SPEC_EINVAL;
+  return expand_launch(a, true, stream);
 }
 
 const char* spec_status_string(int status) {

@@ -17,6 +17,10 @@
 // block_size), and rejected slots, or positions with no block, get
 // PADDING_SLOT_ID = -1 ("Hidden State 管理": no cache write for them).
 //
+// The hidden rows depend only on the windows (not on the accepted counts), so
+// they can also be gathered alone, on another stream, while the verification
+// that produces the counts is still running (spec_expand_hidden_launch).
+//
 // Request b owns the fixed window of n_b + K - 1 slots starting at
 // in_start[b] + b*(K-1), so no scan is needed; G workgroups share a request's
 // window row-interleaved, each writing the metadata of its rows and copying
@@ -47,15 +51,17 @@ __global__ __launch_bounds__(kWG) void expand_kernel(ExpandParams P) {
   const int s = P.in_start[b];
   const int s1 = P.in_start[b + 1];
   const int n = s1 - s;
-  const int a = P.acc[b];
+  const int a = P.hidden_only ? 0 : P.acc[b];
   const int o = s + b * (K - 1);
   const int a_max = P.vtok ? min(n - 1, K) : n - 1;
-  if (gvalid && g == 0 && tid == 0) {
+  if (gvalid && g == 0 && tid == 0 && !P.hidden_only) {
     P.out_start[b] = o;
     if (b == P.B - 1) P.out_start[P.B] = P.N_in + P.B * (K - 1);
   }
-  const bool valid = gvalid && n >= 1 && s >= 0 && s1 <= P.N_in && a >= 0 && a <= a_max;
+  const bool window_ok = gvalid && n >= 1 && s >= 0 && s1 <= P.N_in;
+  const bool valid = window_ok && (P.hidden_only || (a >= 0 && a <= a_max));
   if (!valid) {
+    if (P.hidden_only) return;
     if (g == 0)
       for (int m = tid; m < K; m += kWG) P.nti[(int64_t)b * K + m] = -1;
     return;
@@ -99,6 +105,8 @@ __global__ __launch_bounds__(kWG) void expand_kernel(ExpandParams P) {
       }
     }
   }
+
+  if (P.hidden_only) return;
 
   // metadata: one thread per slot r of this workgroup's rows g, g+G, ...
   const int bonus = P.vtok ? P.vtok[(int64_t)b * (K + 1) + a] : P.bonus[b];

@@ -59,6 +59,7 @@ struct ExpandParams {
   int64_t bt_stride;
   int32_t max_blocks, block_size;
   int64_t* slots;     // slot mapping out, or null
+  int32_t hidden_only;  // gather the hidden rows only (no metadata, accepted counts unread)
 };
 
 struct DraftParams {

@@ -171,6 +171,24 @@ def test_status_strings(sv):
     assert "unknown" in sv.spec_status_string(42)
 
 
+def test_expand_hidden_argument_errors(sv):
+    fake = 0x10000
+    a = sv.SpecExpandArgs()
+    a.B, a.K, a.H, a.N_in = 2, 3, 8, 8
+    a.in_start = a.target_hidden = a.mask_hidden = a.out_hidden = fake
+    a.hidden_row_stride = 8
+    launch = lambda a: sv.spec_expand_hidden_launch(a, None)
+    for field, value in [("K", 0), ("B", -1), ("H", -1), ("N_in", -1), ("in_start", None), ("out_hidden", None),
+                         ("mask_hidden", None), ("target_hidden", None), ("hidden_row_stride", 7)]:
+        b = sv.SpecExpandArgs.from_buffer_copy(a)
+        setattr(b, field, value)
+        assert launch(b) == sv.SPEC_EINVAL, field
+    b = sv.SpecExpandArgs.from_buffer_copy(a)
+    b.H = 0  # nothing to gather
+    assert launch(b) == sv.SPEC_OK
+    assert sv.lib.spec_expand_hidden_launch(None, None) == sv.SPEC_EINVAL
+
+
 def test_draft_argument_errors(sv):
     fake = 0x10000  # never dereferenced: every call below fails validation first
 

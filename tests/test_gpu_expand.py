@@ -251,3 +251,46 @@ def test_chained_step_graph_capture(sv):
         for i, (u, v) in enumerate(zip(snapshot(), eager)):
             assert torch.equal(u, v), (rep, i)
     say("  %d replays identical to the eager step" % 4)
+
+
+def test_hidden_gather_apart_on_a_second_stream(sv):
+    """The hidden rows gathered alone (spec_expand_hidden_launch) on a second
+    stream while the verification runs, then the metadata on the first:
+    the same bits as the fused expansion after the verification."""
+    say("case: expand hidden rows on a second stream")
+    dev = torch.device("cuda")
+    vin = workloads.mixture_inputs("overlap B64 K8 V32768", 64, 8, 32768, torch.bfloat16, 15, dev,
+                                   temps=(0.0, 1.0), lam_lo=0.05, lam_hi=0.6)
+    B, K = vin.B, vin.K
+    e = workloads.expand_inputs(B=B, K=K, H=2880, seed=15, device="cuda")
+    acc = torch.empty(B, dtype=torch.int32, device=dev)
+    tok = torch.empty(B, K + 1, dtype=torch.int32, device=dev)
+    ws = sv.make_workspace(B, K, vin.V, dev)
+    ev = torch.cuda.Event()
+    ev.record()  # create the event
+    va = sv.verify_args(vin.target, vin.draft, vin.draft_tokens, vin.temperature, acc, tok, None, ws, seed=5,
+                        phase_event=ev.cuda_event, phase_starts=0b100100)
+    fused = sv.expand_outputs(B, K, e.N_in, e.H, dev)
+    split = sv.expand_outputs(B, K, e.N_in, e.H, dev)
+    for o in (fused, split):
+        o.out_hidden.fill_(7)
+    xf = sv.expand_args(e.in_token_ids, e.in_positions, e.in_start, acc, None, K, e.mask_id, e.target_hidden,
+                        e.mask_hidden, fused, verify_tokens=tok)
+    xs = sv.expand_args(e.in_token_ids, e.in_positions, e.in_start, acc, None, K, e.mask_id, e.target_hidden,
+                        e.mask_hidden, split, verify_tokens=tok)
+    main = torch.cuda.current_stream()
+    side = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    assert sv.spec_verify_launch(va, main.cuda_stream) == sv.SPEC_OK
+    side.wait_event(ev)  # after the row statistics: overlaps the sampling stage
+    assert sv.spec_expand_hidden_launch(xs, side.cuda_stream) == sv.SPEC_OK
+    meta = sv.expand_args(e.in_token_ids, e.in_positions, e.in_start, acc, None, K, e.mask_id, e.target_hidden,
+                          e.mask_hidden, sv.ExpandOutputs(**{**split.__dict__, "out_hidden": None}),
+                          verify_tokens=tok)
+    assert sv.spec_expand_launch(meta, main.cuda_stream) == sv.SPEC_OK
+    main.wait_stream(side)
+    assert sv.spec_expand_launch(xf, main.cuda_stream) == sv.SPEC_OK
+    torch.cuda.synchronize()
+    for name in ("out_token_ids", "out_positions", "rejected_mask", "masked_mask", "new_token_indices",
+                 "hidden_map", "out_start", "out_hidden"):
+        assert torch.equal(getattr(fused, name), getattr(split, name)), name
