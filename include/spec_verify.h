@@ -279,6 +279,60 @@ size_t spec_draft_workspace_bytes(int32_t B, int32_t K, int32_t V);
 /* Enqueue the draft sampling (two kernels). */
 int spec_draft_sample_launch(const spec_draft_args* args, hipStream_t stream);
 
+/* ---------------------------------------------------- vocab-sharded verify
+ *
+ * The verification of spec_verify_launch (same method, same uniforms, K
+ * drafts for every request, one pass) with the vocabulary split over G
+ * shards, each holding only its slice [v0, v0 + Vs) of every target and draft
+ * row -- as a tensor-parallel target holds its logits (the MineDraft reading
+ * notes verify with TP = 4).  Each quantity the method needs is a sum or a
+ * maximum over the vocabulary, so shards exchange reductions, never logits:
+ *   1. spec_shard_stats_launch on every shard writes its slot g of `records`;
+ *      then every shard needs all G slots (an all-gather of
+ *      G * B * (2K+1) * 32 bytes);
+ *   2. spec_shard_decide_launch on every shard merges the records in shard
+ *      order -- every shard takes the same decisions and writes the same
+ *      accepted_counts and output_tokens, except the sampled token, left -1
+ *      -- and writes its slot g of `masses` (its slice's residual and p
+ *      masses); then every shard needs all G slots (all-gather of G * B * 16
+ *      bytes);
+ *   3. spec_shard_draw_launch on every shard: the shard whose slice holds the
+ *      inverse-CDF crossing writes the sampled token (a global id) into its
+ *      output_tokens; the others leave -1, so an element-wise maximum over
+ *      the shards' output_tokens (the third exchange) completes them.
+ * On one GPU the exchanges are the shared `records` and `masses` arrays.
+ * Results equal spec_verify_launch's up to the order of the floating-point
+ * merges (a decision may differ only within rounding of its threshold).
+ * Invalid data is reported as by spec_verify_launch (the draft tokens are
+ * global ids in [0, V)).
+ */
+typedef struct {
+  int32_t B, K, V;             /* requests, drafts (1..SPEC_MAX_K), full vocabulary */
+  int32_t dtype;               /* spec_dtype */
+  int32_t G, g;                /* shards, and this shard (0 <= g < G) */
+  int32_t v0, Vs;              /* this shard's slice of the vocabulary: [v0, v0 + Vs), Vs >= 1 */
+  const void* target_logits;   /* device: element (b, r, j) = target logit of token v0 + j at row r */
+  int64_t t_req_stride, t_row_stride;  /* elements; row stride >= Vs; request stride 0 = shared */
+  const void* draft_logits;    /* device: the same for the draft rows 0..K-1 */
+  int64_t d_req_stride, d_row_stride;
+  const int32_t* draft_tokens; /* device [B, K], global token ids */
+  const float* temperature;    /* device [B] */
+  uint64_t seed;
+  uint32_t step, request_base;
+  void* records;               /* device [G, B, 2K+1] records of 32 bytes (slot g written by stats) */
+  double* masses;              /* device [G, B, 2] (slot g written by decide) */
+  int32_t* accepted_counts;    /* device out [B] */
+  int32_t* output_tokens;      /* device out [B, K+1] */
+  void* workspace;             /* device, >= spec_shard_workspace_bytes(B, K, Vs), 16-byte aligned; the
+                                  same workspace must serve decide and draw of one shard */
+  size_t workspace_bytes;
+} spec_shard_args;
+
+size_t spec_shard_workspace_bytes(int32_t B, int32_t K, int32_t Vs);
+int spec_shard_stats_launch(const spec_shard_args* args, hipStream_t stream);
+int spec_shard_decide_launch(const spec_shard_args* args, hipStream_t stream);
+int spec_shard_draw_launch(const spec_shard_args* args, hipStream_t stream);
+
 /* Human-readable name of a spec_status value (static storage). */
 const char* spec_status_string(int status);
 

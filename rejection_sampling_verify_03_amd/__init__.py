@@ -22,7 +22,8 @@ SPEC_MAX_K = 63
 
 EXPORTED = ("spec_verify_workspace_bytes", "spec_verify_plan_phases", "spec_verify_launch",
             "spec_expand_launch", "spec_expand_hidden_launch", "spec_draft_workspace_bytes",
-            "spec_draft_sample_launch",
+            "spec_draft_sample_launch", "spec_shard_workspace_bytes", "spec_shard_stats_launch",
+            "spec_shard_decide_launch", "spec_shard_draw_launch",
             "spec_status_string")
 
 
@@ -69,6 +70,20 @@ class SpecDraftArgs(ctypes.Structure):
     ]
 
 
+class SpecShardArgs(ctypes.Structure):
+    _fields_ = [
+        ("B", ctypes.c_int32), ("K", ctypes.c_int32), ("V", ctypes.c_int32), ("dtype", ctypes.c_int32),
+        ("G", ctypes.c_int32), ("g", ctypes.c_int32), ("v0", ctypes.c_int32), ("Vs", ctypes.c_int32),
+        ("target_logits", ctypes.c_void_p), ("t_req_stride", ctypes.c_int64), ("t_row_stride", ctypes.c_int64),
+        ("draft_logits", ctypes.c_void_p), ("d_req_stride", ctypes.c_int64), ("d_row_stride", ctypes.c_int64),
+        ("draft_tokens", ctypes.c_void_p), ("temperature", ctypes.c_void_p),
+        ("seed", ctypes.c_uint64), ("step", ctypes.c_uint32), ("request_base", ctypes.c_uint32),
+        ("records", ctypes.c_void_p), ("masses", ctypes.c_void_p),
+        ("accepted_counts", ctypes.c_void_p), ("output_tokens", ctypes.c_void_p),
+        ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
+    ]
+
+
 def _load():
     # torch ships its own HIP runtime under the same SONAME as the system one;
     # loading torch first makes this library bind to that single runtime
@@ -94,6 +109,11 @@ def _load():
     L.spec_draft_workspace_bytes.restype = ctypes.c_size_t
     L.spec_draft_sample_launch.argtypes = [ctypes.POINTER(SpecDraftArgs), ctypes.c_void_p]
     L.spec_draft_sample_launch.restype = ctypes.c_int
+    L.spec_shard_workspace_bytes.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32]
+    L.spec_shard_workspace_bytes.restype = ctypes.c_size_t
+    for name in ("spec_shard_stats_launch", "spec_shard_decide_launch", "spec_shard_draw_launch"):
+        getattr(L, name).argtypes = [ctypes.POINTER(SpecShardArgs), ctypes.c_void_p]
+        getattr(L, name).restype = ctypes.c_int
     L.spec_status_string.argtypes = [ctypes.c_int]
     L.spec_status_string.restype = ctypes.c_char_p
     return L
@@ -147,6 +167,22 @@ def spec_draft_workspace_bytes(B, K, V):
 
 def spec_draft_sample_launch(args, stream_ptr):
     return int(lib.spec_draft_sample_launch(ctypes.byref(args), stream_ptr))
+
+
+def spec_shard_workspace_bytes(B, K, Vs):
+    return int(lib.spec_shard_workspace_bytes(int(B), int(K), int(Vs)))
+
+
+def spec_shard_stats_launch(args, stream_ptr):
+    return int(lib.spec_shard_stats_launch(ctypes.byref(args), stream_ptr))
+
+
+def spec_shard_decide_launch(args, stream_ptr):
+    return int(lib.spec_shard_decide_launch(ctypes.byref(args), stream_ptr))
+
+
+def spec_shard_draw_launch(args, stream_ptr):
+    return int(lib.spec_shard_draw_launch(ctypes.byref(args), stream_ptr))
 
 
 def spec_status_string(status):
@@ -398,3 +434,56 @@ def draft_sample(logits, row_index, temperature, seed=0, step=0, request_base=0,
     if rc != SPEC_OK:
         raise SpecError(rc)
     return tokens
+
+
+# ---------------------------------------------------- vocab-sharded verify
+SHARD_RECORD_BYTES = 32
+
+
+def verify_sharded(target, draft, draft_tokens, temperature, G, seed=0, step=0, request_base=0, bounds=None,
+                   stream=None):
+    """The verification with the vocabulary split over G shards, each stage of
+    each shard launched through the C ABI on one GPU; the exchanges between
+    shards are the shared record and mass arrays, and the last one (the
+    sampled token, -1 on every shard but its owner) an element-wise maximum.
+    bounds: G+1 slice boundaries (default: as equal as possible).  Returns
+    (accepted [B], output_tokens [B, K+1], per-shard accepted counts [G, B])."""
+    torch = _torch()
+    B, K = draft_tokens.shape
+    V = target.shape[-1]
+    dev = target.device
+    if bounds is None:
+        bounds = [(V * h) // G for h in range(G + 1)]
+    if len(bounds) != G + 1 or bounds[0] != 0 or bounds[-1] != V:
+        raise ValueError("bounds must run from 0 to V in G steps")
+    R = 2 * K + 1
+    records = torch.empty(G * B * R * SHARD_RECORD_BYTES, dtype=torch.uint8, device=dev)
+    masses = torch.empty(G * B * 2, dtype=torch.float64, device=dev)
+    acc = torch.empty(G, B, dtype=torch.int32, device=dev)
+    tok = torch.empty(G, B, K + 1, dtype=torch.int32, device=dev)
+    sp = _stream_ptr(stream)
+    shards = []
+    for h in range(G):
+        v0, v1 = bounds[h], bounds[h + 1]
+        ws = torch.empty(max(spec_shard_workspace_bytes(B, K, v1 - v0), 16), dtype=torch.uint8, device=dev)
+        t, d = target[..., v0:v1], draft[..., v0:v1]
+        a = SpecShardArgs()
+        a.B, a.K, a.V, a.dtype, a.G, a.g, a.v0, a.Vs = B, K, V, _logit_dtype(target), G, h, v0, v1 - v0
+        a.target_logits = t.data_ptr()
+        a.t_req_stride = target.stride(0) if target.shape[0] == B and B > 1 else 0
+        a.t_row_stride = target.stride(1)
+        a.draft_logits = d.data_ptr()
+        a.d_req_stride = draft.stride(0) if draft.shape[0] == B and B > 1 else 0
+        a.d_row_stride = draft.stride(1)
+        a.draft_tokens, a.temperature = draft_tokens.data_ptr(), temperature.data_ptr()
+        a.seed, a.step, a.request_base = int(seed) & (2 ** 64 - 1), int(step) & 0xFFFFFFFF, int(request_base)
+        a.records, a.masses = records.data_ptr(), masses.data_ptr()
+        a.accepted_counts, a.output_tokens = acc[h].data_ptr(), tok[h].data_ptr()
+        a.workspace, a.workspace_bytes = ws.data_ptr(), ws.numel()
+        shards.append((a, ws))
+    for launch in (spec_shard_stats_launch, spec_shard_decide_launch, spec_shard_draw_launch):
+        for a, _ in shards:
+            rc = launch(a, sp)
+            if rc != SPEC_OK:
+                raise SpecError(rc)
+    return acc[0].clone(), tok.max(dim=0).values, acc

@@ -11,7 +11,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
-SOURCES = ["verify.hip", "expand.hip", "draft.hip", "api.hip"]
+SOURCES = ["verify.hip", "expand.hip", "draft.hip", "shard.hip", "api.hip"]
 LIB = os.path.join(HERE, "libspecverify.so")
 ARCH = os.environ.get("SPEC_OFFLOAD_ARCH", "gfx950")
 

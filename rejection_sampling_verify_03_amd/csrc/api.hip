@@ -79,9 +79,95 @@ int draft_check(const spec_draft_args* a) {
   return SPEC_OK;
 }
 
+size_t shard_ws_bytes(int32_t B, int32_t Vs) {
+  const int64_t nseg = ((int64_t)Vs + kSeg - 1) / kSeg;
+  return align256((size_t)B * sizeof(ReqDesc)) + align256((size_t)B * nseg * 2 * sizeof(double));
+}
+
+int shard_check(const spec_shard_args* a) {
+  if (!a) return SPEC_EINVAL;
+  if (a->B < 0 || a->K < 1 || a->K > SPEC_MAX_K || a->V < 1) return SPEC_EINVAL;
+  if (a->dtype != SPEC_F32 && a->dtype != SPEC_BF16) return SPEC_EDTYPE;
+  if (a->G < 1 || a->g < 0 || a->g >= a->G) return SPEC_EINVAL;
+  if (a->Vs < 1 || a->v0 < 0 || (int64_t)a->v0 + a->Vs > a->V) return SPEC_EINVAL;
+  if (a->B == 0) return SPEC_OK;
+  if (!a->target_logits || !a->draft_logits || !a->draft_tokens || !a->temperature || !a->records ||
+      !a->masses || !a->accepted_counts || !a->output_tokens || !a->workspace)
+    return SPEC_EINVAL;
+  if (a->t_row_stride < a->Vs || a->d_row_stride < a->Vs) return SPEC_EINVAL;
+  if (a->t_req_stride != 0 && a->t_req_stride < (int64_t)(a->K + 1) * a->t_row_stride) return SPEC_EINVAL;
+  if (a->d_req_stride != 0 && a->d_req_stride < (int64_t)a->K * a->d_row_stride) return SPEC_EINVAL;
+  if ((int64_t)a->B * (2 * a->K + 1) > INT32_MAX) return SPEC_EINVAL;
+  if (!aligned16(a->workspace)) return SPEC_EALIGN;
+  if (a->workspace_bytes < shard_ws_bytes(a->B, a->Vs)) return SPEC_EWORKSPACE;
+  return SPEC_OK;
+}
+
+ShardParams shard_params(const spec_shard_args* a) {
+  ShardParams P;
+  P.B = a->B;
+  P.K = a->K;
+  P.V = a->V;
+  P.R = 2 * a->K + 1;
+  P.G = a->G;
+  P.g = a->g;
+  P.v0 = a->v0;
+  P.Vs = a->Vs;
+  P.nseg = (int32_t)(((int64_t)a->Vs + kSeg - 1) / kSeg);
+  P.target = static_cast<const char*>(a->target_logits);
+  P.t_req = a->t_req_stride;
+  P.t_row = a->t_row_stride;
+  P.draft = static_cast<const char*>(a->draft_logits);
+  P.d_req = a->d_req_stride;
+  P.d_row = a->d_row_stride;
+  P.tokens = a->draft_tokens;
+  P.temperature = a->temperature;
+  P.seed = a->seed;
+  P.step = a->step;
+  P.request_base = a->request_base;
+  P.recs = static_cast<ShardRec*>(a->records);
+  P.masses = a->masses;
+  P.accepted = a->accepted_counts;
+  P.out_tokens = a->output_tokens;
+  char* ws = static_cast<char*>(a->workspace);
+  P.desc = reinterpret_cast<ReqDesc*>(ws);
+  P.seg = reinterpret_cast<double*>(ws + align256((size_t)a->B * sizeof(ReqDesc)));
+  return P;
+}
+
+bool shard_vec(const spec_shard_args* a) {
+  const int es = a->dtype == SPEC_BF16 ? 2 : 4;
+  return aligned16(a->target_logits) && aligned16(a->draft_logits) && (a->t_row_stride * es) % 16 == 0 &&
+         (a->t_req_stride * es) % 16 == 0 && (a->d_row_stride * es) % 16 == 0 && (a->d_req_stride * es) % 16 == 0;
+}
+
 }  // namespace
 
 extern "C" {
+
+size_t spec_shard_workspace_bytes(int32_t B, int32_t K, int32_t Vs) {
+  if (B < 0 || K < 1 || K > SPEC_MAX_K || Vs < 1) return 0;
+  return shard_ws_bytes(B, Vs);
+}
+
+int spec_shard_stats_launch(const spec_shard_args* a, hipStream_t stream) {
+  const int rc = shard_check(a);
+  if (rc != SPEC_OK || a->B == 0) return rc;
+  return launch_shard_stats(shard_params(a), a->dtype, shard_vec(a), stream) == hipSuccess ? SPEC_OK : SPEC_ELAUNCH;
+}
+
+int spec_shard_decide_launch(const spec_shard_args* a, hipStream_t stream) {
+  const int rc = shard_check(a);
+  if (rc != SPEC_OK || a->B == 0) return rc;
+  return launch_shard_decide(shard_params(a), a->dtype, shard_vec(a), stream) == hipSuccess ? SPEC_OK
+                                                                                            : SPEC_ELAUNCH;
+}
+
+int spec_shard_draw_launch(const spec_shard_args* a, hipStream_t stream) {
+  const int rc = shard_check(a);
+  if (rc != SPEC_OK || a->B == 0) return rc;
+  return launch_shard_draw(shard_params(a), a->dtype, shard_vec(a), stream) == hipSuccess ? SPEC_OK : SPEC_ELAUNCH;
+}
 
 size_t spec_draft_workspace_bytes(int32_t B, int32_t K, int32_t V) {
   if (B < 0 || K < 1 || V < 1) return 0;

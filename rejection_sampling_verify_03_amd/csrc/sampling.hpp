@@ -251,4 +251,54 @@ __device__ __forceinline__ void block_scan_d2(double v0, double v1, double& incl
   __syncthreads();
 }
 
+// One wave sums the weights of segment [s0, s0 + kSeg) (clipped to V): lane l
+// takes groups l, l+64, ... so that every load of the wave is one contiguous
+// kilobyte, and a whole part of the segment (both rows) is loaded before any
+// of it is used.  Returns (residual sum, p sum) in every lane.
+template <int ES, bool VEC, bool RES>
+__device__ __forceinline__ void segment_sums(const char* prow, const char* qrow, const WeightCtx& w, int s0,
+                                             int V, double& rsum, double& psum) {
+  constexpr int H = (ES == 2 && VEC) ? kSegGroups : kSegGroups / 2;  // groups per part
+  constexpr int NH = kSegGroups / H;
+  const int lane = threadIdx.x & 63;
+  const bool full = s0 + kSeg <= V;
+  rsum = 0.0;
+  psum = 0.0;
+#pragma unroll 1
+  for (int h = 0; h < NH; ++h) {
+    RawGroup<ES, VEC> rp[H], rq[H];
+#pragma unroll
+    for (int g = 0; g < H; ++g) {
+      const int e = s0 + ((h * H + g) * 64 + lane) * 8;
+      if (full) {
+        rp[g] = load_raw<ES, VEC>(prow, e);
+        if (RES) rq[g] = load_raw<ES, VEC>(qrow, e);
+      } else if (e < V) {
+        rp[g] = load_raw_bounded<ES, VEC>(prow, e, V);
+        if (RES) rq[g] = load_raw_bounded<ES, VEC>(qrow, e, V);
+      } else {
+        rp[g] = neg_inf_group<ES, VEC>();
+        if (RES) rq[g] = neg_inf_group<ES, VEC>();
+      }
+    }
+#pragma unroll
+    for (int g = 0; g < H; ++g) {
+      float xp[8], xq[8];
+      unpack_group<ES, VEC>(rp[g], xp);
+      if (RES) unpack_group<ES, VEC>(rq[g], xq);
+      float r8 = 0.f, p8 = 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        float ep;
+        r8 += pair_weight(w, xp[i], RES ? xq[i] : 0.f, RES, ep);
+        p8 += ep;
+      }
+      rsum += (double)r8;
+      psum += (double)p8;
+    }
+  }
+  rsum = wave_sum_d(rsum);
+  psum = wave_sum_d(psum);
+}
+
 }  // namespace specv

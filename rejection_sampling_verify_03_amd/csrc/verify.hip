@@ -45,6 +45,7 @@
 #include <limits.h>
 
 #include "device_common.hpp"
+#include "rowpass.hpp"
 #include "sampling.hpp"
 #include "verify_kernels.hpp"
 #include "verify_layout.hpp"
@@ -86,124 +87,6 @@ __device__ __forceinline__ int drafts_of(const VerifyParams& P, int b) {
   const int v = t[b];
   const int kb = P.num_drafts ? v : P.K;
   return (kb >= 0 && kb <= P.K) ? kb : -1;
-}
-
-// Raise the reference exponent of a lane's running (M, S) to cover a new
-// group maximum gm (the rescale is an exact power of two).
-__device__ __forceinline__ void raise_ref(float& M, double& S, float gm, float s_hi) {
-  const float gM = ceilf(gm * s_hi);
-  if (gM > M) {
-    S = ldexp(S, (int)fmaxf(M - gM, -2000.f));
-    M = gM;
-  }
-}
-
-// ------------------------------------------------------------ chunk passes
-// Each thread takes groups tid, tid + 256, ...; the main loop issues U
-// unconditional 16-byte loads per lane before using any of them, the
-// remainder loop takes one group at a time, and the (< 8) trailing logits of a
-// row whose length is not a multiple of 8 go to thread 0.
-template <int ES, bool VEC>
-__device__ __forceinline__ MS chunk_stats(const char* __restrict__ row, int e0, int e1, float s_hi,
-                                          float s_lo) {
-  constexpr int U = (ES == 2) ? 8 : 4;  // 128 bytes in flight per lane per iteration
-  const int nfull = (e1 - e0) >> 3;
-  float M = -INFINITY;
-  double S = 0.0;
-  int g = threadIdx.x;
-  for (; g + (U - 1) * kWG < nfull; g += kWG * U) {
-    float x[U][8];
-#pragma unroll
-    for (int u = 0; u < U; ++u) load_group<ES, VEC>(row, (int64_t)e0 + 8 * (int64_t)(g + u * kWG), x[u]);
-    float gm = -INFINITY;
-#pragma unroll
-    for (int u = 0; u < U; ++u)
-#pragma unroll
-      for (int i = 0; i < 8; ++i) gm = fmaxf(gm, x[u][i]);
-    raise_ref(M, S, gm, s_hi);
-    const float negM = -fmaxf(M, -1e30f);
-    float acc = 0.f;
-#pragma unroll
-    for (int u = 0; u < U; ++u) acc += sum8_exp(x[u], s_hi, s_lo, negM);
-    S += (double)acc;
-  }
-  for (; g < nfull; g += kWG) {
-    float x[8];
-    load_group<ES, VEC>(row, (int64_t)e0 + 8 * (int64_t)g, x);
-    float gm = x[0];
-#pragma unroll
-    for (int i = 1; i < 8; ++i) gm = fmaxf(gm, x[i]);
-    raise_ref(M, S, gm, s_hi);
-    S += (double)sum8_exp(x, s_hi, s_lo, -fmaxf(M, -1e30f));
-  }
-  const int t0 = e0 + 8 * nfull;
-  if (t0 < e1 && threadIdx.x == 0) {
-    for (int e = t0; e < e1; ++e) {
-      const float x = load_one<ES>(row, e);
-      raise_ref(M, S, x, s_hi);
-      S += (double)scaled_exp2(x, s_hi, s_lo, -fmaxf(M, -1e30f));
-    }
-  }
-  return MS{M, S};
-}
-
-template <int ES, bool VEC>
-__device__ __forceinline__ VI chunk_argmax(const char* __restrict__ row, int e0, int e1) {
-  constexpr int U = (ES == 2) ? 8 : 4;
-  const int nfull = (e1 - e0) >> 3;
-  VI best{-INFINITY, INT_MAX};
-  int g = threadIdx.x;
-  for (; g + (U - 1) * kWG < nfull; g += kWG * U) {
-    float x[U][8];
-#pragma unroll
-    for (int u = 0; u < U; ++u) load_group<ES, VEC>(row, (int64_t)e0 + 8 * (int64_t)(g + u * kWG), x[u]);
-#pragma unroll
-    for (int u = 0; u < U; ++u)
-#pragma unroll
-      for (int i = 0; i < 8; ++i) best = vi_pick(best, VI{x[u][i], e0 + 8 * (g + u * kWG) + i});
-  }
-  for (; g < nfull; g += kWG) {
-    float x[8];
-    load_group<ES, VEC>(row, (int64_t)e0 + 8 * (int64_t)g, x);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) best = vi_pick(best, VI{x[i], e0 + 8 * g + i});
-  }
-  const int t0 = e0 + 8 * nfull;
-  if (t0 < e1 && threadIdx.x == 0)
-    for (int e = t0; e < e1; ++e) best = vi_pick(best, VI{load_one<ES>(row, e), e});
-  return best;
-}
-
-__device__ __forceinline__ MS block_merge_ms(MS v) {
-  __shared__ float sm[kWaves];
-  __shared__ double ss[kWaves];
-  v = wave_merge_ms(v);
-  const int w = threadIdx.x >> 6;
-  if ((threadIdx.x & 63) == 0) {
-    sm[w] = v.m;
-    ss[w] = v.s;
-  }
-  __syncthreads();
-  MS r{sm[0], ss[0]};
-#pragma unroll
-  for (int i = 1; i < kWaves; ++i) r = ms_merge(r, MS{sm[i], ss[i]});
-  return r;
-}
-
-__device__ __forceinline__ VI block_argmax(VI v) {
-  __shared__ float sv[kWaves];
-  __shared__ int si[kWaves];
-  v = wave_argmax(v);
-  const int w = threadIdx.x >> 6;
-  if ((threadIdx.x & 63) == 0) {
-    sv[w] = v.v;
-    si[w] = v.i;
-  }
-  __syncthreads();
-  VI r{sv[0], si[0]};
-#pragma unroll
-  for (int i = 1; i < kWaves; ++i) r = vi_pick(r, VI{sv[i], si[i]});
-  return r;
 }
 
 // ------------------------------------------------------------- decision
@@ -503,56 +386,6 @@ __device__ __forceinline__ WeightCtx make_ctx(const ReqDesc& d) {
   w.c_hi = (float)c;
   w.c_lo = (float)(c - (double)w.c_hi);
   return w;
-}
-
-// One wave sums the weights of segment [s0, s0 + kSeg) (clipped to V): lane l
-// takes groups l, l+64, ... so that every load of the wave is one contiguous
-// kilobyte, and a whole part of the segment (both rows) is loaded before any
-// of it is used.  Returns (residual sum, p sum) in every lane.
-template <int ES, bool VEC, bool RES>
-__device__ __forceinline__ void segment_sums(const char* prow, const char* qrow, const WeightCtx& w, int s0,
-                                             int V, double& rsum, double& psum) {
-  constexpr int H = (ES == 2 && VEC) ? kSegGroups : kSegGroups / 2;  // groups per part
-  constexpr int NH = kSegGroups / H;
-  const int lane = threadIdx.x & 63;
-  const bool full = s0 + kSeg <= V;
-  rsum = 0.0;
-  psum = 0.0;
-#pragma unroll 1
-  for (int h = 0; h < NH; ++h) {
-    RawGroup<ES, VEC> rp[H], rq[H];
-#pragma unroll
-    for (int g = 0; g < H; ++g) {
-      const int e = s0 + ((h * H + g) * 64 + lane) * 8;
-      if (full) {
-        rp[g] = load_raw<ES, VEC>(prow, e);
-        if (RES) rq[g] = load_raw<ES, VEC>(qrow, e);
-      } else if (e < V) {
-        rp[g] = load_raw_bounded<ES, VEC>(prow, e, V);
-        if (RES) rq[g] = load_raw_bounded<ES, VEC>(qrow, e, V);
-      } else {
-        rp[g] = neg_inf_group<ES, VEC>();
-        if (RES) rq[g] = neg_inf_group<ES, VEC>();
-      }
-    }
-#pragma unroll
-    for (int g = 0; g < H; ++g) {
-      float xp[8], xq[8];
-      unpack_group<ES, VEC>(rp[g], xp);
-      if (RES) unpack_group<ES, VEC>(rq[g], xq);
-      float r8 = 0.f, p8 = 0.f;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        float ep;
-        r8 += pair_weight(w, xp[i], RES ? xq[i] : 0.f, RES, ep);
-        p8 += ep;
-      }
-      rsum += (double)r8;
-      psum += (double)p8;
-    }
-  }
-  rsum = wave_sum_d(rsum);
-  psum = wave_sum_d(psum);
 }
 
 // The final decision of every request: outputs (all but the token the draw

@@ -76,6 +76,40 @@ struct DraftParams {
 
 constexpr int kDraftChunkSegs = 8;  // segments per workgroup of the statistics pass
 
+// Vocab-sharded verification: one shard's statistics of one row of its vocab
+// slice (exchanged between shards).
+struct ShardRec {
+  float m;        // integer-valued reference (sampled) or max logit (greedy)
+  int32_t idx;    // argmax as a global token id (greedy)
+  double s;       // sum of 2^(x * s - m) over the slice (sampled)
+  float z;        // logit at the position's draft token, when the slice holds it
+  int32_t has_z;
+  int64_t pad;
+};
+static_assert(sizeof(ShardRec) == 32, "ShardRec layout");
+
+struct ShardParams {
+  int32_t B, K, V, R, G, g, v0, Vs, nseg;  // nseg: 4096-logit segments of the slice
+  const char* target;
+  int64_t t_req, t_row;
+  const char* draft;
+  int64_t d_req, d_row;
+  const int32_t* tokens;
+  const float* temperature;
+  uint64_t seed;
+  uint32_t step, request_base;
+  ShardRec* recs;    // [G, B, R]
+  double* masses;    // [G, B, 2]: residual and p masses of each shard's slice
+  int32_t* accepted;
+  int32_t* out_tokens;
+  ReqDesc* desc;     // [B] (this shard's workspace)
+  double* seg;       // [B, nseg, 2] (this shard's workspace)
+};
+
+hipError_t launch_shard_stats(const ShardParams& P, int dtype, bool vec, hipStream_t stream);
+hipError_t launch_shard_decide(const ShardParams& P, int dtype, bool vec, hipStream_t stream);
+hipError_t launch_shard_draw(const ShardParams& P, int dtype, bool vec, hipStream_t stream);
+
 // phase_starts: bit k (1 <= k <= K) starts an early-exit phase at draft
 // position k; 0 reads every row in one pass.
 hipError_t launch_verify(const VerifyParams& P, int dtype, bool vec, uint64_t phase_starts,

@@ -44,7 +44,7 @@ def test_struct_layouts_match_the_header(sv, tmp_path):
     equals what a C compiler makes of include/spec_verify.h."""
     lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "spec_verify.h"', 'int main(void) {']
     for cname, py in (("spec_verify_args", sv.SpecVerifyArgs), ("spec_expand_args", sv.SpecExpandArgs),
-                      ("spec_draft_args", sv.SpecDraftArgs)):
+                      ("spec_draft_args", sv.SpecDraftArgs), ("spec_shard_args", sv.SpecShardArgs)):
         lines.append('printf("%s size %%zu\\n", sizeof(%s));' % (cname, cname))
         for f, _ in py._fields_:
             lines.append('printf("%s %s %%zu\\n", offsetof(%s, %s));' % (cname, f, cname, f))
@@ -57,7 +57,7 @@ def test_struct_layouts_match_the_header(sv, tmp_path):
     out = subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.split("\n")
     got = {tuple(l.split()[:2]): int(l.split()[2]) for l in out if l.strip()}
     for cname, py in (("spec_verify_args", sv.SpecVerifyArgs), ("spec_expand_args", sv.SpecExpandArgs),
-                      ("spec_draft_args", sv.SpecDraftArgs)):
+                      ("spec_draft_args", sv.SpecDraftArgs), ("spec_shard_args", sv.SpecShardArgs)):
         assert got[(cname, "size")] == ctypes.sizeof(py), cname
         for f, _ in py._fields_:
             assert got[(cname, f)] == getattr(py, f).offset, (cname, f)
@@ -219,3 +219,30 @@ def test_draft_argument_errors(sv):
     assert sv.spec_draft_workspace_bytes(2, 3, 100) == 256
     assert sv.spec_draft_workspace_bytes(256, 8, 151936) == 256 * 8 * 38 * 16
     assert sv.spec_draft_workspace_bytes(1, 0, 10) == 0
+
+
+def test_shard_argument_errors(sv):
+    fake = 0x10000
+
+    def args():
+        a = sv.SpecShardArgs()
+        a.B, a.K, a.V, a.dtype, a.G, a.g, a.v0, a.Vs = 2, 3, 100, sv.SPEC_BF16, 2, 1, 50, 50
+        a.target_logits, a.t_req_stride, a.t_row_stride = fake, 400, 100
+        a.draft_logits, a.d_req_stride, a.d_row_stride = fake, 400, 100
+        a.draft_tokens = a.temperature = a.records = a.masses = fake
+        a.accepted_counts = a.output_tokens = a.workspace = fake
+        a.workspace_bytes = 0
+        return a
+
+    for launch in (sv.spec_shard_stats_launch, sv.spec_shard_decide_launch, sv.spec_shard_draw_launch):
+        assert launch(args(), None) == sv.SPEC_EWORKSPACE
+        for field, value, want in [("G", 0, sv.SPEC_EINVAL), ("g", 2, sv.SPEC_EINVAL), ("g", -1, sv.SPEC_EINVAL),
+                                   ("Vs", 0, sv.SPEC_EINVAL), ("v0", 51, sv.SPEC_EINVAL), ("v0", -1, sv.SPEC_EINVAL),
+                                   ("K", 64, sv.SPEC_EINVAL), ("dtype", 3, sv.SPEC_EDTYPE),
+                                   ("t_row_stride", 49, sv.SPEC_EINVAL), ("records", None, sv.SPEC_EINVAL),
+                                   ("masses", None, sv.SPEC_EINVAL), ("workspace", 0x10008, sv.SPEC_EALIGN)]:
+            a = args()
+            setattr(a, field, value)
+            assert launch(a, None) == want, (launch, field, value)
+    assert sv.spec_shard_workspace_bytes(2, 3, 50) == 256 + 256
+    assert sv.spec_shard_workspace_bytes(256, 8, 37984) == 256 * 64 + 256 * 10 * 16
