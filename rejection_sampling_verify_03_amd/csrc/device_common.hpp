@@ -234,6 +234,64 @@ __device__ __forceinline__ double wave_sum_d(double v) {
   return v;
 }
 
+// ----------------------------------------------- DPP lane movement (wave64) --
+// Cross-lane moves through the VALU's data-parallel-primitive path instead of
+// the LDS permute unit: a few cycles each rather than an LDS round trip.
+// Controls (gfx9 encoding): row_shr:n = 0x110 + n within each 16-lane row,
+// row_bcast:15 = 0x142 (lane 15 of a row to the whole next row) and
+// row_bcast:31 = 0x143 (lane 31 to rows 2 and 3).  A lane whose source is
+// outside its row, or whose row is not in ROW_MASK, receives `fill`.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ int dpp_i(int x, int fill) {
+  return __builtin_amdgcn_update_dpp(fill, x, CTRL, ROW_MASK, 0xf, false);
+}
+
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ double dpp_d0(double x) {  // fill 0.0
+  const uint64_t b = (uint64_t)__double_as_longlong(x);
+  const uint32_t lo = (uint32_t)dpp_i<CTRL, ROW_MASK>((int)(uint32_t)b, 0);
+  const uint32_t hi = (uint32_t)dpp_i<CTRL, ROW_MASK>((int)(uint32_t)(b >> 32), 0);
+  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+
+// Inclusive prefix sum over the 64 lanes in a fixed order: within 16-lane
+// rows by doubling shifts, then the row totals carried across rows.
+__device__ __forceinline__ double wave_scan_d(double x) {
+  x += dpp_d0<0x111, 0xf>(x);
+  x += dpp_d0<0x112, 0xf>(x);
+  x += dpp_d0<0x114, 0xf>(x);
+  x += dpp_d0<0x118, 0xf>(x);
+  x += dpp_d0<0x142, 0xa>(x);
+  x += dpp_d0<0x143, 0xc>(x);
+  return x;
+}
+
+// The value of lane l (l the same in every lane).
+__device__ __forceinline__ int lane_i(int x, int l) { return __builtin_amdgcn_readlane(x, l); }
+
+__device__ __forceinline__ float lane_f(float x, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), l));
+}
+
+__device__ __forceinline__ double lane_d(double x, int l) {
+  const uint64_t b = (uint64_t)__double_as_longlong(x);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)b, l);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(b >> 32), l);
+  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+
+// Maximum over the 64 lanes, the same in every lane.
+__device__ __forceinline__ float wave_max_f(float x) {
+  const int ninf = __float_as_int(-INFINITY);
+  x = fmaxf(x, __int_as_float(dpp_i<0x111, 0xf>(__float_as_int(x), ninf)));
+  x = fmaxf(x, __int_as_float(dpp_i<0x112, 0xf>(__float_as_int(x), ninf)));
+  x = fmaxf(x, __int_as_float(dpp_i<0x114, 0xf>(__float_as_int(x), ninf)));
+  x = fmaxf(x, __int_as_float(dpp_i<0x118, 0xf>(__float_as_int(x), ninf)));
+  x = fmaxf(x, __int_as_float(dpp_i<0x142, 0xa>(__float_as_int(x), ninf)));
+  x = fmaxf(x, __int_as_float(dpp_i<0x143, 0xc>(__float_as_int(x), ninf)));
+  return lane_f(x, 63);
+}
+
 // (value, index) with larger value first, lower index on ties.
 struct VI {
   float v;

@@ -20,11 +20,15 @@
 //      segment maximum, rounded up, in units of the scale s = log2(e) / T),
 //      or to (max, lowest argmax) at temperature 0.
 //
-//  draft_draw      one 512-thread workgroup per (request, position): brings
-//      the segment sums to the row's largest reference M* by exact
-//      power-of-two scaling, scans them in order for the crossing of u * W,
-//      and finds the token inside that one segment, recomputing its weights
-//      scaled by the same power of two.
+//  draft_draw      one wave64 workgroup per (request, position): brings the
+//      segment sums to the row's largest reference M* by exact power-of-two
+//      scaling, scans them in order for the crossing of u * W, and finds the
+//      token inside that one segment, recomputing its weights scaled by the
+//      same power of two (groups of 8 logits scanned 64 at a time, one per
+//      lane, in vocabulary order).  The wave is one chain of dependent
+//      steps, so the segment records load with the row index, the segment's
+//      64 logits per lane load together, and lanes exchange values through
+//      DPP moves and readlane rather than LDS permutes.
 #include <limits.h>
 
 #include "device_common.hpp"
@@ -107,119 +111,146 @@ __global__ __launch_bounds__(kWG) void draft_segstats_kernel(DraftParams P) {
   }
 }
 
-template <int NT>
-__device__ __forceinline__ float block_max_f(float v) {
-  constexpr int W = NT / 64;
-  __shared__ float mx[W];
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
-  if ((threadIdx.x & 63) == 0) mx[threadIdx.x >> 6] = v;
-  __syncthreads();
-  float r = mx[0];
-#pragma unroll
-  for (int i = 1; i < W; ++i) r = fmaxf(r, mx[i]);
-  __syncthreads();
-  return r;
-}
-
-template <int NT>
-__device__ __forceinline__ VI block_argmax_vi(VI v) {
-  constexpr int W = NT / 64;
-  __shared__ float sv[W];
-  __shared__ int si[W];
-  v = wave_argmax(v);
-  if ((threadIdx.x & 63) == 0) {
-    sv[threadIdx.x >> 6] = v.v;
-    si[threadIdx.x >> 6] = v.i;
-  }
-  __syncthreads();
-  VI r{sv[0], si[0]};
-#pragma unroll
-  for (int i = 1; i < W; ++i) r = vi_pick(r, VI{sv[i], si[i]});
-  __syncthreads();
-  return r;
-}
-
 // Segment j's sum in units of 2^M* (exact power-of-two scaling).
 __device__ __forceinline__ double scaled_seg(const RowPartial& p, float Mstar) {
   return ldexp(p.s, (int)fmaxf(p.m - Mstar, -2000.f));
 }
 
+// One wave per (request, position): the crossing segment from a scan of the
+// segment sums, then the token inside it -- lane l takes the groups of 8
+// logits l, l + 64, ... of the segment, so that each round of 64 groups is one
+// contiguous wave load; the rounds are scanned in vocabulary order and the
+// crossing lane walks its own 8 logits.  The whole search is one chain of
+// dependent steps per wave, so every load of a step is issued before any of
+// its results is used, and lanes exchange values through DPP and readlane.
 template <int ES, bool VEC>
-__global__ __launch_bounds__(kDrawThreads) void draft_draw_kernel(DraftParams P) {
-  constexpr int NT = kDrawThreads;
+__global__ __launch_bounds__(64) void draft_draw_kernel(DraftParams P) {
   const int i = blockIdx.x;
   const int b = i / P.K, k = i % P.K;
-  const int tid = threadIdx.x;
+  const int lane = threadIdx.x;
   const int row = P.row_index[i];
   const float T = P.temperature[b];
-  if (!draft_row_valid(P, row, T)) {
-    if (tid == 0) P.tokens[i] = -1;
-    return;
-  }
+  // the records of segments 0..63 stay in registers, one per lane; loaded
+  // together with the row index (an invalid row's records are never used)
   const RowPartial* sp = P.segp + (int64_t)i * P.nseg;
   const int nseg = P.nseg;
-  if (T == 0.0f) {
-    VI best{-INFINITY, INT_MAX};
-    for (int j = tid; j < nseg; j += NT) best = vi_pick(best, VI{sp[j].m, sp[j].idx});
-    best = block_argmax_vi<NT>(best);
-    if (tid == 0) P.tokens[i] = best.i;
+  RowPartial r0{-INFINITY, INT_MAX, 0.0};
+  if (lane < nseg) r0 = sp[lane];
+  if (!draft_row_valid(P, row, T)) {
+    if (lane == 0) P.tokens[i] = -1;
     return;
   }
-  float mloc = -INFINITY;
-  for (int j = tid; j < nseg; j += NT) mloc = fmaxf(mloc, sp[j].m);
-  const float Mstar = block_max_f<NT>(mloc);
+  if (T == 0.0f) {
+    VI best{r0.m, r0.idx};
+    for (int j = lane + 64; j < nseg; j += 64) best = vi_pick(best, VI{sp[j].m, sp[j].idx});
+    best = wave_argmax(best);
+    if (lane == 0) P.tokens[i] = best.i;
+    return;
+  }
+  float Mstar = r0.m;
+  for (int j = lane + 64; j < nseg; j += 64) Mstar = fmaxf(Mstar, sp[j].m);
+  Mstar = wave_max_f(Mstar);
   if (!(fabsf(Mstar) <= FLT_MAX)) {  // no finite logit in the row
-    if (tid == 0) P.tokens[i] = -1;
+    if (lane == 0) P.tokens[i] = -1;
     return;
   }
   const uint32_t k0 = (uint32_t)(P.seed & 0xffffffffu), k1 = (uint32_t)(P.seed >> 32);
   const double u = unit_uniform(philox4x32_10((uint32_t)b + P.request_base, (uint32_t)k, P.step, 1u, k0, k1).w[0]);
-  // totals, then the crossing of u * W in a fixed-order scan over the segments
-  __shared__ double sh_base;
-  double W = 0.0;
-  for (int j0 = 0; j0 < nseg; j0 += NT) {
-    const int j = j0 + tid;
-    double incl, excl, tot, i2, e2, t2;
-    block_scan_d2<NT>(j < nseg ? scaled_seg(sp[j], Mstar) : 0.0, 0.0, incl, excl, tot, i2, e2, t2);
-    W += tot;
+  // total W, then the crossing of u * W, in one fixed-order scan over the
+  // segments (64 at a time)
+  const double v0 = lane < nseg ? scaled_seg(r0, Mstar) : 0.0;
+  const double x0 = wave_scan_d(v0);
+  double W = lane_d(x0, 63);
+  for (int j0 = 64; j0 < nseg; j0 += 64) {
+    const int j = j0 + lane;
+    W += lane_d(wave_scan_d(j < nseg ? scaled_seg(sp[j], Mstar) : 0.0), 63);
   }
   const double target = u * W;
-  int found = -1, lastpos = -1;
+  int found = -1, lastseg = -1;
   double base = 0.0, carry = 0.0;
-  for (int j0 = 0; j0 < nseg && found < 0; j0 += NT) {
-    const int j = j0 + tid;
-    const double v = j < nseg ? scaled_seg(sp[j], Mstar) : 0.0;
-    double incl, excl, tot, i2, e2, t2;
-    block_scan_d2<NT>(v, 0.0, incl, excl, tot, i2, e2, t2);
-    const int f = block_first_true<NT>(j < nseg && carry + incl > target);
-    lastpos = max(lastpos, block_max_int<NT>(v > 0.0 ? j : -1));
-    if (f >= 0 && tid == f) sh_base = carry + excl;
-    __syncthreads();
-    if (f >= 0) {
-      found = j0 + f;
-      base = sh_base;
+  for (int j0 = 0; j0 < nseg && found < 0; j0 += 64) {
+    const int j = j0 + lane;
+    double v = v0, x = x0;
+    if (j0 > 0) {
+      v = j < nseg ? scaled_seg(sp[j], Mstar) : 0.0;
+      x = wave_scan_d(v);
     }
-    carry += tot;
-    __syncthreads();
+    const uint64_t m = __ballot(j < nseg && carry + x > target);
+    const uint64_t pos = __ballot(v > 0.0);
+    if (pos) lastseg = j0 + 63 - __builtin_clzll(pos);
+    if (m) {
+      const int f = __builtin_ctzll(m);
+      found = j0 + f;
+      base = carry + lane_d(x - v, f);
+    }
+    carry += lane_d(x, 63);
   }
-  const int js = found >= 0 ? found : lastpos;
+  const bool last_positive = found < 0;
+  const int js = last_positive ? lastseg : found;
   int y = -1;  // no positive weight anywhere: only reachable outside the data contract
   if (js >= 0) {
-    const float mj = sp[js].m;
-    WeightCtx w;
-    w.s_hi = 0.f;
-    w.s_lo = 0.f;
-    temperature_scale(T, w.s_hi, w.s_lo);
-    w.negMp = -mj;
-    w.negMq = 0.f;
-    w.c_hi = w.c_lo = 0.f;
-    const double scale = ldexp(1.0, (int)fmaxf(mj - Mstar, -2000.f));
     const char* lg = P.logits + (int64_t)row * P.row_stride * ES;
-    y = draw_in_segment<ES, VEC>(lg, lg, P.V, w, false, false, scale, js, found >= 0 ? base : 0.0,
-                                 found >= 0 ? target : 0.0, found < 0);
+    const int s0 = js * kSeg;
+    // all 64 logits of the lane in flight at once; a segment cut by the row
+    // end reads clamped addresses and masks them
+    float xs[kSegGroups][8];
+    if (s0 + kSeg <= P.V) {
+#pragma unroll
+      for (int g = 0; g < kSegGroups; ++g) load_group<ES, VEC>(lg, s0 + (g * 64 + lane) * 8, xs[g]);
+    } else {
+#pragma unroll
+      for (int g = 0; g < kSegGroups; ++g)
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          const int e = s0 + (g * 64 + lane) * 8 + q;
+          const float v = load_one<ES>(lg, min(e, P.V - 1));
+          xs[g][q] = e < P.V ? v : -INFINITY;
+        }
+    }
+    float s_hi, s_lo;
+    temperature_scale(T, s_hi, s_lo);
+    const float mj = js < 64 ? lane_f(r0.m, js) : sp[js].m;
+    const float negM = -mj;
+    const double scale = ldexp(1.0, (int)fmaxf(mj - Mstar, -2000.f));
+    // groups in vocabulary order: 64 per round (one per lane), scanned in order
+    double carry = base;
+    int pick = -1, lpos = -1;
+#pragma unroll
+    for (int g = 0; g < kSegGroups; ++g) {
+      const int e = s0 + (g * 64 + lane) * 8;
+      double w[8], wg = 0.0;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        w[q] = (double)scaled_exp2(xs[g][q], s_hi, s_lo, negM) * scale;
+        wg += w[q];
+        if (w[q] > 0.0) lpos = e + q;
+      }
+      const double x = wave_scan_d(wg);
+      const double tot = lane_d(x, 63);
+      if (!last_positive && pick < 0 && carry + tot > target) {
+        const uint64_t m = __ballot(carry + x > target);
+        const int L = m ? __builtin_ctzll(m) : 63;
+        double run = carry + (x - wg);
+        int pl = -1;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          run += w[q];
+          if (pl < 0 && w[q] > 0.0 && target < run) pl = e + q;
+        }
+        if (pl < 0) pl = lpos >= e ? lpos : -1;  // cumulative rounding: stay inside this group
+        pick = lane_i(pl, L);
+      }
+      carry += tot;
+    }
+    if (pick < 0) {  // the last positive logit of the segment
+      int lp = lpos;
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) lp = max(lp, __shfl_xor(lp, off, 64));
+      pick = lp;
+    }
+    y = pick;
   }
-  if (tid == 0) P.tokens[i] = y;
+  if (lane == 0) P.tokens[i] = y;
 }
 
 template <int ES, bool VEC>
@@ -228,7 +259,7 @@ static hipError_t launch_draft_typed(const DraftParams& P, hipStream_t stream) {
   hipLaunchKernelGGL((draft_segstats_kernel<ES, VEC>), dim3((unsigned)g1), dim3(kWG), 0, stream, P);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((draft_draw_kernel<ES, VEC>), dim3((unsigned)(P.B * P.K)), dim3(kDrawThreads), 0, stream, P);
+  hipLaunchKernelGGL((draft_draw_kernel<ES, VEC>), dim3((unsigned)(P.B * P.K)), dim3(64), 0, stream, P);
   return hipGetLastError();
 }
 
