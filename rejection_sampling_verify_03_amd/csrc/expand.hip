@@ -68,20 +68,29 @@ __global__ __launch_bounds__(kWG) void expand_kernel(ExpandParams P) {
   }
   const int Wb = n + K - 1;  // slots of this request's window
 
+  // The hidden copy and the metadata are independent, and the metadata is a
+  // chain of dependent loads (the bonus token after the accepted count, the
+  // block table after the position), so with both to do the last wave writes
+  // the metadata while the other waves copy.
+  const bool do_meta = !P.hidden_only;
+  const bool do_copy = P.out_h != nullptr && g < Wb;
+  const int meta_first = (do_meta && P.out_h != nullptr) ? kWG - 64 : 0;  // metadata threads from here on
+  const int copy_threads = do_meta ? meta_first : kWG;
+
   // hidden rows g, g+G, ... of the window: slot o+r takes input row s+r
   // (r < n) or the MASK placeholder; loads of a batch are all issued before
   // its stores, and the output is written once (non-temporal stores)
-  if (P.out_h != nullptr && g < Wb) {
+  if (do_copy && tid < copy_threads) {
     const int nr = (Wb - g + P.G - 1) / P.G;
     if constexpr (VEC) {
       const int ncols = P.H >> 3;
       const int cells = nr * ncols;
-      for (int c0 = tid; c0 < cells; c0 += kWG * kCopyBatch) {
+      for (int c0 = tid; c0 < cells; c0 += copy_threads * kCopyBatch) {
         u32x4 v[kCopyBatch];
         int64_t dst[kCopyBatch];
 #pragma unroll
         for (int u = 0; u < kCopyBatch; ++u) {
-          const int c = c0 + u * kWG;
+          const int c = c0 + u * copy_threads;
           dst[u] = -1;
           if (c < cells) {
             const int rl = c / ncols, col = c - rl * ncols;
@@ -97,7 +106,7 @@ __global__ __launch_bounds__(kWG) void expand_kernel(ExpandParams P) {
       }
     } else {
       const int cells = nr * P.H;
-      for (int c = tid; c < cells; c += kWG) {
+      for (int c = tid; c < cells; c += copy_threads) {
         const int rl = c / P.H, col = c - rl * P.H;
         const int r = g + P.G * rl;
         const uint16_t* src = r < n ? P.th + (int64_t)(s + r) * P.th_stride : P.mh;
@@ -106,11 +115,12 @@ __global__ __launch_bounds__(kWG) void expand_kernel(ExpandParams P) {
     }
   }
 
-  if (P.hidden_only) return;
+  if (!do_meta || tid < meta_first) return;
 
   // metadata: one thread per slot r of this workgroup's rows g, g+G, ...
+  const int mt = tid - meta_first, meta_threads = kWG - meta_first;
   const int bonus = P.vtok ? P.vtok[(int64_t)b * (K + 1) + a] : P.bonus[b];
-  for (int r = g + P.G * tid; r < Wb; r += P.G * kWG) {
+  for (int r = g + P.G * mt; r < Wb; r += P.G * meta_threads) {
     const int slot = o + r;
     int64_t pos;
     bool rejected;
