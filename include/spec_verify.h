@@ -135,9 +135,10 @@ typedef struct {
 uint64_t spec_verify_plan_phases(int32_t K, const double* survival, double sampled_fraction, double phase_cost);
 
 /* Bytes of device workspace a verification of this shape needs (0 for an
- * invalid shape).  The workspace carries nothing from one call to the next:
- * it needs no initialisation and may be reused for any shape it is large
- * enough for.  Calls that overlap on one workspace race. */
+ * invalid shape).  The workspace carries nothing from one call to the next
+ * (but the invalid-request count that spec_workspace_error reads): it needs
+ * no initialisation and may be reused for any shape it is large enough for.
+ * Calls that overlap on one workspace race. */
 size_t spec_verify_workspace_bytes(int32_t B, int32_t K, int32_t V);
 
 /* Enqueue one verification step.  A request whose data is invalid (a draft
@@ -147,6 +148,15 @@ size_t spec_verify_workspace_bytes(int32_t B, int32_t K, int32_t V);
  * normaliser) gets
  * accepted_counts = -1, output_tokens all -1 and debug_probs 0. */
 int spec_verify_launch(const spec_verify_args* args, hipStream_t stream);
+
+/* The data errors of the last verification enqueued on this workspace: waits
+ * for `stream` (so it is not for graph capture or a tight loop), then returns
+ * the number of requests that verification found invalid (the ones with
+ * accepted_counts = -1; 0 when every request was valid).  The count lives in
+ * the first 4 bytes of the workspace and is cleared by each verification with
+ * B >= 1.  Returns SPEC_EINVAL for a NULL workspace and SPEC_ELAUNCH if the
+ * stream reports an error or the copy fails. */
+int spec_workspace_error(const void* workspace, hipStream_t stream);
 
 /* ---------------------------------------------------------------- expansion
  *

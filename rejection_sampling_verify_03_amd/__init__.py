@@ -24,7 +24,7 @@ EXPORTED = ("spec_verify_workspace_bytes", "spec_verify_plan_phases", "spec_veri
             "spec_expand_launch", "spec_expand_hidden_launch", "spec_draft_workspace_bytes",
             "spec_draft_sample_launch", "spec_shard_workspace_bytes", "spec_shard_stats_launch",
             "spec_shard_decide_launch", "spec_shard_draw_launch",
-            "spec_status_string")
+            "spec_workspace_error", "spec_status_string")
 
 
 class SpecVerifyArgs(ctypes.Structure):
@@ -101,6 +101,8 @@ def _load():
     L.spec_verify_plan_phases.restype = ctypes.c_uint64
     L.spec_verify_launch.argtypes = [ctypes.POINTER(SpecVerifyArgs), ctypes.c_void_p]
     L.spec_verify_launch.restype = ctypes.c_int
+    L.spec_workspace_error.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+    L.spec_workspace_error.restype = ctypes.c_int
     L.spec_expand_launch.argtypes = [ctypes.POINTER(SpecExpandArgs), ctypes.c_void_p]
     L.spec_expand_launch.restype = ctypes.c_int
     L.spec_expand_hidden_launch.argtypes = [ctypes.POINTER(SpecExpandArgs), ctypes.c_void_p]
@@ -151,6 +153,13 @@ def survival_from_accepted(accepted, K):
 def spec_verify_launch(args, stream_ptr):
     """args: a SpecVerifyArgs; stream_ptr: hipStream_t as an int (0 = null stream)."""
     return int(lib.spec_verify_launch(ctypes.byref(args), stream_ptr))
+
+
+def spec_workspace_error(workspace, stream_ptr=0):
+    """Invalid requests of the last verification on this workspace (a device
+    tensor or pointer); waits for the stream.  Negative: a spec_status."""
+    ptr = workspace.data_ptr() if hasattr(workspace, "data_ptr") else workspace
+    return int(lib.spec_workspace_error(ptr, stream_ptr))
 
 
 def spec_expand_launch(args, stream_ptr):

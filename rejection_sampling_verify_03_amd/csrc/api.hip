@@ -265,6 +265,7 @@ int spec_verify_launch(const spec_verify_args* a, hipStream_t stream) {
   const bool vec = aligned16(a->target_logits) && aligned16(a->draft_logits) &&
                    (a->t_row_stride * es) % 16 == 0 && (a->t_req_stride * es) % 16 == 0 &&
                    (a->d_row_stride * es) % 16 == 0 && (a->draft_row_index || (a->d_req_stride * es) % 16 == 0);
+  P.err = reinterpret_cast<int32_t*>(ws + L.off_err);
   P.state = reinterpret_cast<int32_t*>(ws + L.off_state);
   P.ph_lo = P.ph_nt = P.ph_nd = P.ph_check = 0;
   P.last_lo = P.phased = 0;
@@ -333,6 +334,14 @@ int spec_expand_hidden_launch(const spec_expand_args* a, hipStream_t stream) {
     return SPEC_EINVAL;
   if (a->hidden_row_stride < a->H) return SPEC_EINVAL;
   return expand_launch(a, true, stream);
+}
+
+int spec_workspace_error(const void* workspace, hipStream_t stream) {
+  if (workspace == nullptr) return SPEC_EINVAL;
+  if (hipStreamSynchronize(stream) != hipSuccess) return SPEC_ELAUNCH;
+  int32_t n = 0;
+  if (hipMemcpy(&n, workspace, sizeof(n), hipMemcpyDeviceToHost) != hipSuccess) return SPEC_ELAUNCH;
+  return n;
 }
 
 const char* spec_status_string(int status) {

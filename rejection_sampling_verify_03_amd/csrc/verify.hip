@@ -280,7 +280,10 @@ __device__ void decide(const VerifyParams& P, int b, bool write, ReqDesc& D) {
         else tok = greedy ? sh.g[a] : -1;  // sampled: written by the draw
         if (!(j == a && !greedy && !bad)) out[j] = tok;
       }
-      if (tid == 0) P.accepted[b] = a;
+      if (tid == 0) {
+        P.accepted[b] = a;
+        if (bad) atomicAdd(P.err, 1);
+      }
     }
     if (tid == 0) {
       ReqDesc d;
@@ -343,6 +346,7 @@ __global__ __launch_bounds__(kWG) void verify_rowstats_kernel(VerifyParams P) {
   // row >= K_b: they do not exist), and rows of a request whose draft count,
   // draft token or draft row entry is out of range (the request is invalid;
   // no statistic is used)
+  if (blockIdx.x == 0 && threadIdx.x == 0 && P.ph_lo == 0) *P.err = 0;  // counted by the final decision
   const bool skip = (greedy & (r > P.K)) | ((P.ph_check != 0) & (st != kStateAlive)) |
                     ((k < kb) & ((uint32_t)xt >= (uint32_t)P.V)) | ((r > P.K) & !draft_entry_ok(P, di)) |
                     (kb < 0) | ((r <= P.K) & (k > kb)) | ((r > P.K) & (k >= kb));

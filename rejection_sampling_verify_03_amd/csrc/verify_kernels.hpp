@@ -28,6 +28,7 @@ struct VerifyParams {
   RowPartial* rowp;
   ReqDesc* desc;
   double* seg;
+  int32_t* err;    // count of invalid requests of this verification
   int32_t* state;  // per-request state between early-exit phases
   // rows of one early-exit phase: target rows [ph_lo, ph_lo + ph_nt), draft
   // rows [ph_lo, ph_lo + ph_nd); ph_check: skip requests no longer alive

@@ -50,7 +50,9 @@ struct Layout {
   int32_t R;           // rows per request the row pass may read: K+1 target + K draft
   int32_t C1, chunk1;  // row-pass chunks per row and their length
   int32_t nseg;        // segments per row
-  size_t off_rowp, off_desc, off_seg, off_state, total;
+  // the invalid-request count sits at byte 0 of the workspace (read by
+  // spec_workspace_error without knowing the shape)
+  size_t off_err, off_rowp, off_desc, off_seg, off_state, total;
 };
 
 __host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -71,6 +73,8 @@ __host__ __device__ inline Layout make_layout(int32_t B, int32_t K, int32_t V) {
   chunking(V, kRowChunkTarget, L.C1, L.chunk1);
   L.nseg = (int32_t)(((int64_t)V + kSeg - 1) / kSeg);
   size_t off = 0;
+  L.off_err = off;
+  off = align256(off + sizeof(int32_t));
   L.off_rowp = off;
   off = align256(off + (size_t)B * L.R * L.C1 * sizeof(RowPartial));
   L.off_desc = off;

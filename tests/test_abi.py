@@ -171,6 +171,11 @@ def test_status_strings(sv):
     assert "unknown" in sv.spec_status_string(42)
 
 
+def test_workspace_error_rejects_a_null_workspace(sv):
+    # rejected before any HIP call, so this runs without a GPU
+    assert sv.spec_workspace_error(0, 0) == sv.SPEC_EINVAL
+
+
 def test_expand_hidden_argument_errors(sv):
     fake = 0x10000
     a = sv.SpecExpandArgs()

@@ -219,6 +219,24 @@ def test_invalid_requests(sv):
     assert rep.ok(), rep.failures
 
 
+def test_workspace_error_counts_invalid_requests(sv):
+    say("case: workspace error word")
+    inp = workloads.noisy_draft_inputs("bad", 6, 3, 64, torch.float32, 2, "cuda", "gauss")
+    ws = sv.make_workspace(6, 3, 64)
+    ws.fill_(0x5A)  # a stale count is cleared by the verification
+    run(sv, inp.target, inp.draft, inp.draft_tokens, inp.temperature, ws=ws)
+    assert sv.spec_workspace_error(ws) == 0
+    x = inp.draft_tokens.clone()
+    T = inp.temperature.clone()
+    x[1, 2] = 64
+    T[4] = -1.0
+    acc, _, _ = run(sv, inp.target, inp.draft, x, T, ws=ws)
+    assert sv.spec_workspace_error(ws) == 2 == int((acc == -1).sum())
+    # phased rows: the count comes from the final decision all the same
+    sv.verify(inp.target, inp.draft, x, T, workspace=ws, phase_starts=0b10)
+    assert sv.spec_workspace_error(ws, torch.cuda.current_stream().cuda_stream) == 2
+
+
 def test_determinism_and_workspace_reuse(sv):
     say("case: determinism / workspace reuse")
     big = workloads.mixture_inputs("reuse", 16, 6, 40000, torch.bfloat16, 11, "cuda", temps=(0.0, 1.0),
