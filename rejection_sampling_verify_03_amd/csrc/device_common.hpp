@@ -5,6 +5,7 @@
 
 #include <float.h>
 #include <hip/hip_runtime.h>
+#include <limits.h>
 #include <stdint.h>
 
 namespace specv {
@@ -125,6 +126,18 @@ __device__ __forceinline__ void unpack_group(const RawGroup<ES, VEC>& r, float x
   } else {
     x[0] = r.a.x; x[1] = r.a.y; x[2] = r.a.z; x[3] = r.a.w;
     x[4] = r.b.x; x[5] = r.b.y; x[6] = r.b.z; x[7] = r.b.w;
+  }
+}
+
+// An empty register-to-register step the compiler cannot see through: a
+// group widened twice from its loaded registers stays loaded-size in between
+// (the compiler would otherwise keep the first widening alive).
+template <int ES, bool VEC>
+__device__ __forceinline__ void opaque_group(RawGroup<ES, VEC>& r) {
+  if constexpr (VEC && ES == 2) {
+    asm volatile("" : "+v"(r.v));
+  } else if constexpr (VEC) {
+    asm volatile("" : "+v"(r.a), "+v"(r.b));
   }
 }
 
@@ -292,6 +305,10 @@ __device__ __forceinline__ float wave_max_f(float x) {
   return lane_f(x, 63);
 }
 
+// Sum over the 64 lanes in a fixed order (the last lane of the inclusive
+// scan), the same in every lane.
+__device__ __forceinline__ double wave_total_d(double x) { return lane_d(wave_scan_d(x), 63); }
+
 // (value, index) with larger value first, lower index on ties.
 struct VI {
   float v;
@@ -301,6 +318,25 @@ struct VI {
 __device__ __forceinline__ VI vi_pick(VI a, VI b) {
   const bool take_b = (b.v > a.v) || (b.v == a.v && b.i < a.i);
   return take_b ? b : a;
+}
+
+// wave_argmax through DPP: prefix maxima across the rows, lane 63's read out.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ VI dpp_vi(VI v) {
+  VI o;
+  o.v = __int_as_float(dpp_i<CTRL, ROW_MASK>(__float_as_int(v.v), __float_as_int(-INFINITY)));
+  o.i = dpp_i<CTRL, ROW_MASK>(v.i, INT_MAX);
+  return o;
+}
+
+__device__ __forceinline__ VI wave_argmax_dpp(VI v) {
+  v = vi_pick(v, dpp_vi<0x111, 0xf>(v));
+  v = vi_pick(v, dpp_vi<0x112, 0xf>(v));
+  v = vi_pick(v, dpp_vi<0x114, 0xf>(v));
+  v = vi_pick(v, dpp_vi<0x118, 0xf>(v));
+  v = vi_pick(v, dpp_vi<0x142, 0xa>(v));
+  v = vi_pick(v, dpp_vi<0x143, 0xc>(v));
+  return VI{lane_f(v.v, 63), lane_i(v.i, 63)};
 }
 
 __device__ __forceinline__ VI wave_argmax(VI v) {

@@ -79,7 +79,7 @@ __global__ __launch_bounds__(kWG) void draft_segstats_kernel(DraftParams P) {
         for (int q = 0; q < 8; ++q)
           if (e + q < P.V) best = vi_pick(best, VI{x[q], e + q});
       }
-      best = wave_argmax(best);
+      best = wave_argmax_dpp(best);
       part.m = best.v;
       part.idx = best.i;
       part.s = 0.0;
@@ -92,20 +92,20 @@ __global__ __launch_bounds__(kWG) void draft_segstats_kernel(DraftParams P) {
 #pragma unroll
         for (int q = 0; q < 8; ++q) gm = fmaxf(gm, x[q]);
       }
-#pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) gm = fmaxf(gm, __shfl_xor(gm, off, 64));
+      gm = wave_max_f(gm);
       const float M = ceilf(gm * s_hi);  // -inf for a segment without a finite logit
       const float negM = -fmaxf(M, -1e30f);
       double S = 0.0;
 #pragma unroll
       for (int g = 0; g < kSegGroups; ++g) {
+        opaque_group<ES, VEC>(rg[g]);
         float x[8];
         unpack_group<ES, VEC>(rg[g], x);
         S += (double)sum8_exp(x, s_hi, s_lo, negM);
       }
       part.m = M;
       part.idx = 0;
-      part.s = wave_sum_d(S);
+      part.s = wave_total_d(S);
     }
     if (lane == 0) P.segp[(int64_t)i * P.nseg + j] = part;
   }
