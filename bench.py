@@ -4,9 +4,11 @@ A step = one verification of the headline batch (B=256 requests, K=8 drafts,
 V=151936 bf16 logits, temperatures drawn from {0, 0.6, 1}, mixture drafts)
 followed by the P-EAGLE expansion of the same batch (hidden width 2880, the
 bonus read from the verification's output tokens, KV-cache slot mapping
-through a 16-slot-per-block table), both through the C ABI on torch's current
-stream.  Inputs are generated once on the GPU and stay resident
-in HBM; each timed step uses a new Philox step counter.
+through a 16-slot-per-block table), enqueued through the C ABI on torch's
+current stream as one chained call (spec_verify_expand_launch: the expansion
+runs inside the verification's sampling stage; --separate-expand enqueues it
+as its own call).  Inputs are generated once on the GPU and stay resident in
+HBM; each timed step uses a new Philox step counter.
 
 By default the verification reads its rows in early-exit phases (rows of a
 phase only for requests whose earlier drafts were all accepted), cut by the
@@ -39,6 +41,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--separate-expand", action="store_true",
+                    help="enqueue the expansion as its own call after the verification instead of the chained "
+                         "call that runs it inside the verification's sampling stage")
     ap.add_argument("--overlap", action="store_true",
                     help="gather the expansion's hidden rows on a second stream while the verification's sampling "
                          "stage runs (measured slower: the gather competes with the segment sums for HBM)")
@@ -254,6 +259,7 @@ def main():
     # records phase_event there), overlapping the verification's sampling stage; the metadata follows the
     # verification on the main stream, and the step ends when both are done.
     overlap = args.overlap
+    chained = not (args.overlap or args.separate_expand)
     side = torch.cuda.Stream()
     meta_out = sv.ExpandOutputs(**{**out.__dict__, "out_hidden": None})
     meta_args = sv.expand_args(in_ids, in_pos, in_start, accepted, None, K, mask_id, hidden, mask_hidden, meta_out,
@@ -261,12 +267,26 @@ def main():
     untimed_phase = torch.cuda.Event()
     untimed_phase.record(stream)
 
+    # the argument block is built once, as a serving loop would keep it; each step sets its step counter,
+    # phase cut and event (rebuilding it in Python every step costs host time the GPU can wait on)
+    va = sv.verify_args(inp.target, inp.draft, inp.draft_tokens, inp.temperature, accepted, tokens, None, ws,
+                        seed=args.seed, step=0, phase_event=untimed_phase.cuda_event, phase_starts=0)
+
     def step(i, events=None):
         ph = events[1] if events else untimed_phase
-        va = sv.verify_args(inp.target, inp.draft, inp.draft_tokens, inp.temperature, accepted, tokens, None,
-                            ws, seed=args.seed, step=i, phase_event=ph.cuda_event, phase_starts=plan["mask"])
+        va.step = i & 0xFFFFFFFF
+        va.phase_event = ph.cuda_event
+        va.phase_starts = plan["mask"]
         if events:
             events[0].record(stream)
+        if chained:  # one call: the expansion runs inside the verification's sampling stage
+            rc = sv.spec_verify_expand_launch(va, ex_args, sptr)
+            if rc != sv.SPEC_OK:
+                raise sv.SpecError(rc)
+            if events:
+                events[2].record(stream)
+                events[3].record(stream)
+            return
         rc = sv.spec_verify_launch(va, sptr)
         if rc != sv.SPEC_OK:
             raise sv.SpecError(rc)
@@ -351,7 +371,9 @@ def main():
         "config": {"workload": "headline verify B=256 K=8 V=151936 bf16, T in {0,0.6,1}, mixture drafts "
                                "+ P-EAGLE expand H=2880 with KV slot mapping, chained on the verify outputs",
                    "B": B, "K": K, "V": V, "H": H, "sampled_requests": int((temps > 0).sum()),
-                   "hidden_gather": "second stream, overlapping the sampling stage" if overlap else "in the expand kernel"},
+                   "expansion": ("chained call: hidden rows and metadata inside the verification's sampling stage"
+                                 if chained else "hidden rows on a second stream, overlapping the sampling stage"
+                                 if overlap else "its own kernel after the verification")},
         "roofline": {"kernel": "verify_rowstats", "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                      "traffic": measured_traffic(mask),
@@ -359,11 +381,13 @@ def main():
                      "sequential_min_bytes": seq_bytes},
         "early_exit": {"phase_starts": mask, "phases": [0] + [k for k in range(1, K + 1) if (mask >> k) & 1],
                        **{k: v for k, v in plan.items() if k != "mask"}},
-        "kernels_ms": {"verify_row_stage": k1_ms, "verify_decide_and_draw": float(k2.mean()),
-                       ("expand_metadata_and_join" if overlap else "expand"): float(ke.mean()),
+        "kernels_ms": {"verify_row_stage": k1_ms,
+                       ("sampling_stage_with_expansion" if chained else "verify_decide_and_draw"): float(k2.mean()),
+                       **({} if chained else {("expand_metadata_and_join" if overlap else "expand"): float(ke.mean())}),
                        "verify_row_stage_p10_p90": [float(np.percentile(k1, 10)), float(np.percentile(k1, 90))]},
-        "verify_GBps_algorithmic": (read_bytes + vbytes - one_pass_bytes) / ((k1.mean() + k2.mean()) * 1e-3) / 1e9,
-        "expand_GBps_algorithmic": None if overlap else ebytes / (ke.mean() * 1e-3) / 1e9,
+        "verify_GBps_algorithmic": None if chained else
+        (read_bytes + vbytes - one_pass_bytes) / ((k1.mean() + k2.mean()) * 1e-3) / 1e9,
+        "expand_GBps_algorithmic": None if (overlap or chained) else ebytes / (ke.mean() * 1e-3) / 1e9,
         "emitted_tokens_per_s": float((acc_np + 1).sum()) / args.steps / (ms_per_step * 1e-3),
         "mean_accepted": float(acc_np.mean()),
     }

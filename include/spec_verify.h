@@ -242,6 +242,19 @@ int spec_expand_launch(const spec_expand_args* args, hipStream_t stream);
  * in_start[B] = N_in), whatever its accepted count. */
 int spec_expand_hidden_launch(const spec_expand_args* args, hipStream_t stream);
 
+/* One verification step and the expansion of its outputs, enqueued as one
+ * chained call: `v` as for spec_verify_launch and `e` as for
+ * spec_expand_launch, with e->accepted_counts == v->accepted_counts and
+ * e->verify_output_tokens == v->output_tokens (the expansion of this very
+ * verification; e->bonus_tokens NULL) and the same B and K.  The results are
+ * those of spec_verify_launch followed by spec_expand_launch; the expansion's
+ * work runs inside the verification's sampling stage (its hidden rows and the
+ * metadata after the decision, a sampled request's bonus id with the draw),
+ * so no expansion kernel of its own is launched.  Argument errors of either
+ * part, or arrays that do not chain as above, return SPEC_EINVAL (or the
+ * part's own status) before anything is enqueued. */
+int spec_verify_expand_launch(const spec_verify_args* v, const spec_expand_args* e, hipStream_t stream);
+
 /* ----------------------------------------------------------- draft sampling
  *
  * The next draft tokens, sampled from the drafter's logits at the new-token

@@ -21,7 +21,8 @@ SPEC_F32, SPEC_BF16 = 0, 1
 SPEC_MAX_K = 63
 
 EXPORTED = ("spec_verify_workspace_bytes", "spec_verify_plan_phases", "spec_verify_launch",
-            "spec_expand_launch", "spec_expand_hidden_launch", "spec_draft_workspace_bytes",
+            "spec_expand_launch", "spec_expand_hidden_launch", "spec_verify_expand_launch",
+            "spec_draft_workspace_bytes",
             "spec_draft_sample_launch", "spec_shard_workspace_bytes", "spec_shard_stats_launch",
             "spec_shard_decide_launch", "spec_shard_draw_launch",
             "spec_workspace_error", "spec_status_string")
@@ -105,6 +106,9 @@ def _load():
     L.spec_workspace_error.restype = ctypes.c_int
     L.spec_expand_launch.argtypes = [ctypes.POINTER(SpecExpandArgs), ctypes.c_void_p]
     L.spec_expand_launch.restype = ctypes.c_int
+    L.spec_verify_expand_launch.argtypes = [ctypes.POINTER(SpecVerifyArgs), ctypes.POINTER(SpecExpandArgs),
+                                            ctypes.c_void_p]
+    L.spec_verify_expand_launch.restype = ctypes.c_int
     L.spec_expand_hidden_launch.argtypes = [ctypes.POINTER(SpecExpandArgs), ctypes.c_void_p]
     L.spec_expand_hidden_launch.restype = ctypes.c_int
     L.spec_draft_workspace_bytes.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32]
@@ -164,6 +168,11 @@ def spec_workspace_error(workspace, stream_ptr=0):
 
 def spec_expand_launch(args, stream_ptr):
     return int(lib.spec_expand_launch(ctypes.byref(args), stream_ptr))
+
+
+def spec_verify_expand_launch(verify_args_, expand_args_, stream_ptr):
+    """The verification and the expansion of its outputs as one chained call."""
+    return int(lib.spec_verify_expand_launch(ctypes.byref(verify_args_), ctypes.byref(expand_args_), stream_ptr))
 
 
 def spec_expand_hidden_launch(args, stream_ptr):

@@ -228,9 +228,9 @@ size_t spec_verify_workspace_bytes(int32_t B, int32_t K, int32_t V) {
   return make_layout(B, K, V).total;
 }
 
-int spec_verify_launch(const spec_verify_args* a, hipStream_t stream) {
-  const int rc = verify_check(a);
-  if (rc != SPEC_OK || a->B == 0) return rc;
+// The kernel parameters of a checked verification (B >= 1); vec: 16-byte
+// row loads are possible.
+static VerifyParams verify_params(const spec_verify_args* a, bool& vec) {
   const Layout L = make_layout(a->B, a->K, a->V);
   const int es = a->dtype == SPEC_BF16 ? 2 : 4;
   VerifyParams P;
@@ -262,20 +262,36 @@ int spec_verify_launch(const spec_verify_args* a, hipStream_t stream) {
   P.rowp = reinterpret_cast<RowPartial*>(ws + L.off_rowp);
   P.desc = reinterpret_cast<ReqDesc*>(ws + L.off_desc);
   P.seg = reinterpret_cast<double*>(ws + L.off_seg);
-  const bool vec = aligned16(a->target_logits) && aligned16(a->draft_logits) &&
-                   (a->t_row_stride * es) % 16 == 0 && (a->t_req_stride * es) % 16 == 0 &&
-                   (a->d_row_stride * es) % 16 == 0 && (a->draft_row_index || (a->d_req_stride * es) % 16 == 0);
+  vec = aligned16(a->target_logits) && aligned16(a->draft_logits) && (a->t_row_stride * es) % 16 == 0 &&
+        (a->t_req_stride * es) % 16 == 0 && (a->d_row_stride * es) % 16 == 0 &&
+        (a->draft_row_index || (a->d_req_stride * es) % 16 == 0);
   P.err = reinterpret_cast<int32_t*>(ws + L.off_err);
   P.state = reinterpret_cast<int32_t*>(ws + L.off_state);
   P.ph_lo = P.ph_nt = P.ph_nd = P.ph_check = 0;
   P.last_lo = P.phased = 0;
+  P.ex_on = 0;
+  P.ex_G = 1;
+  return P;
+}
+
+static int verify_enqueue(const VerifyParams& P, const spec_verify_args* a, bool vec, hipStream_t stream) {
   return launch_verify(P, a->dtype, vec, a->phase_starts, static_cast<hipEvent_t>(a->phase_event), stream) ==
                  hipSuccess
              ? SPEC_OK
              : SPEC_ELAUNCH;
 }
 
-static int expand_launch(const spec_expand_args* a, bool hidden_only, hipStream_t stream) {
+int spec_verify_launch(const spec_verify_args* a, hipStream_t stream) {
+  const int rc = verify_check(a);
+  if (rc != SPEC_OK || a->B == 0) return rc;
+  bool vec;
+  const VerifyParams P = verify_params(a, vec);
+  return verify_enqueue(P, a, vec, stream);
+}
+
+// The kernel parameters of a checked expansion (B >= 1), G workgroups per
+// request window.
+static ExpandParams expand_params(const spec_expand_args* a, bool hidden_only, int64_t rows_per_wg) {
   ExpandParams P;
   P.hidden_only = hidden_only ? 1 : 0;
   P.B = a->B;
@@ -283,11 +299,11 @@ static int expand_launch(const spec_expand_args* a, bool hidden_only, hipStream_
   P.H = a->H;
   P.N_in = a->N_in;
   P.mask_id = a->mask_token_id;
-  // about kExpandRowsPerWG output rows per workgroup on average; a request's
+  // about rows_per_wg output rows per workgroup on average; a request's
   // window is shared by G workgroups row-interleaved
   const int64_t n_out = (int64_t)a->N_in + (int64_t)a->B * (a->K - 1);
   const int64_t avg_window = (n_out + a->B - 1) / a->B;
-  int64_t G = (avg_window + kExpandRowsPerWG - 1) / kExpandRowsPerWG;
+  int64_t G = (avg_window + rows_per_wg - 1) / rows_per_wg;
   if (G < 1) G = 1;
   if (G > 64) G = 64;
   if ((int64_t)a->B * G > INT32_MAX) G = 1;
@@ -314,9 +330,14 @@ static int expand_launch(const spec_expand_args* a, bool hidden_only, hipStream_
   P.bt_stride = a->bt_row_stride;
   P.max_blocks = a->slot_mapping ? a->max_blocks : 0;
   P.block_size = a->slot_mapping ? a->block_size : 1;
-  const bool vec = (a->H % 8) == 0 && (a->hidden_row_stride % 8) == 0 && aligned16(a->target_hidden) &&
-                   aligned16(a->mask_hidden) && aligned16(a->out_hidden);
-  return launch_expand(P, vec, stream) == hipSuccess ? SPEC_OK : SPEC_ELAUNCH;
+  P.vec = (a->H % 8) == 0 && (a->hidden_row_stride % 8) == 0 && aligned16(a->target_hidden) &&
+          aligned16(a->mask_hidden) && aligned16(a->out_hidden);
+  return P;
+}
+
+static int expand_launch(const spec_expand_args* a, bool hidden_only, hipStream_t stream) {
+  const ExpandParams P = expand_params(a, hidden_only, kExpandRowsPerWG);
+  return launch_expand(P, P.vec != 0, stream) == hipSuccess ? SPEC_OK : SPEC_ELAUNCH;
 }
 
 int spec_expand_launch(const spec_expand_args* a, hipStream_t stream) {
@@ -334,6 +355,25 @@ int spec_expand_hidden_launch(const spec_expand_args* a, hipStream_t stream) {
     return SPEC_EINVAL;
   if (a->hidden_row_stride < a->H) return SPEC_EINVAL;
   return expand_launch(a, true, stream);
+}
+
+int spec_verify_expand_launch(const spec_verify_args* v, const spec_expand_args* e, hipStream_t stream) {
+  int rc = verify_check(v);
+  if (rc != SPEC_OK) return rc;
+  rc = expand_check(e);
+  if (rc != SPEC_OK) return rc;
+  // the expansion reads this verification's outputs: same batch, the counts
+  // and the bonus source are the verification's own output arrays
+  if (e->B != v->B || e->K != v->K) return SPEC_EINVAL;
+  if (v->B == 0) return SPEC_OK;
+  if (e->accepted_counts != v->accepted_counts || e->verify_output_tokens != v->output_tokens) return SPEC_EINVAL;
+  bool vec;
+  VerifyParams P = verify_params(v, vec);
+  P.ex = expand_params(e, false, 1);  // one output row per wave on average
+  P.ex_on = 1;
+  P.ex_G = P.ex.G;
+  if ((int64_t)P.B * P.nseg + (int64_t)P.B * P.ex_G > INT32_MAX) return SPEC_EINVAL;
+  return verify_enqueue(P, v, vec, stream);
 }
 
 int spec_workspace_error(const void* workspace, hipStream_t stream) {

@@ -26,124 +26,31 @@
 // window row-interleaved, each writing the metadata of its rows and copying
 // its hidden rows with 16-byte loads and stores.
 #include "device_common.hpp"
+#include "expand_device.hpp"
 #include "verify_kernels.hpp"
 
 namespace specv {
-
-// KV-cache slot of output slot position pos of request b (-1: none).
-__device__ __forceinline__ int64_t cache_slot(const ExpandParams& P, int b, int64_t pos, bool rejected) {
-  if (rejected || pos < 0) return -1;
-  const int64_t blk = pos / P.block_size;
-  if (blk >= P.max_blocks) return -1;
-  const int32_t phys = P.bt[(int64_t)b * P.bt_stride + blk];
-  return phys < 0 ? -1 : (int64_t)phys * P.block_size + pos % P.block_size;
-}
-
-constexpr int kCopyBatch = 8;  // 16-byte cells per lane loaded before any is stored
 
 template <bool VEC>
 __global__ __launch_bounds__(kWG) void expand_kernel(ExpandParams P) {
   const int b = blockIdx.x / P.G;
   const int g = blockIdx.x % P.G;
-  const int K = P.K;
   const int tid = threadIdx.x;
-  const bool gvalid = P.in_start[0] == 0 && P.in_start[P.B] == P.N_in;
-  const int s = P.in_start[b];
-  const int s1 = P.in_start[b + 1];
-  const int n = s1 - s;
-  const int a = P.hidden_only ? 0 : P.acc[b];
-  const int o = s + b * (K - 1);
-  const int a_max = P.vtok ? min(n - 1, K) : n - 1;
-  if (gvalid && g == 0 && tid == 0 && !P.hidden_only) {
-    P.out_start[b] = o;
-    if (b == P.B - 1) P.out_start[P.B] = P.N_in + P.B * (K - 1);
-  }
-  const bool window_ok = gvalid && n >= 1 && s >= 0 && s1 <= P.N_in;
-  const bool valid = window_ok && (P.hidden_only || (a >= 0 && a <= a_max));
-  if (!valid) {
-    if (P.hidden_only) return;
-    if (g == 0)
-      for (int m = tid; m < K; m += kWG) P.nti[(int64_t)b * K + m] = -1;
+  const ExpandWindow w = expand_window(P, b);
+  if (g == 0 && tid == 0) expand_out_start(P, b, w);
+  if (!w.valid) {
+    if (!P.hidden_only && g == 0) expand_invalid(P, b, tid, kWG);
     return;
   }
-  const int Wb = n + K - 1;  // slots of this request's window
-
   // The hidden copy and the metadata are independent, and the metadata is a
   // chain of dependent loads (the bonus token after the accepted count, the
   // block table after the position), so with both to do the last wave writes
   // the metadata while the other waves copy.
   const bool do_meta = !P.hidden_only;
-  const bool do_copy = P.out_h != nullptr && g < Wb;
   const int meta_first = (do_meta && P.out_h != nullptr) ? kWG - 64 : 0;  // metadata threads from here on
   const int copy_threads = do_meta ? meta_first : kWG;
-
-  // hidden rows g, g+G, ... of the window: slot o+r takes input row s+r
-  // (r < n) or the MASK placeholder; loads of a batch are all issued before
-  // its stores, and the output is written once (non-temporal stores)
-  if (do_copy && tid < copy_threads) {
-    const int nr = (Wb - g + P.G - 1) / P.G;
-    if constexpr (VEC) {
-      const int ncols = P.H >> 3;
-      const int cells = nr * ncols;
-      for (int c0 = tid; c0 < cells; c0 += copy_threads * kCopyBatch) {
-        u32x4 v[kCopyBatch];
-        int64_t dst[kCopyBatch];
-#pragma unroll
-        for (int u = 0; u < kCopyBatch; ++u) {
-          const int c = c0 + u * copy_threads;
-          dst[u] = -1;
-          if (c < cells) {
-            const int rl = c / ncols, col = c - rl * ncols;
-            const int r = g + P.G * rl;
-            const uint16_t* src = r < n ? P.th + (int64_t)(s + r) * P.th_stride : P.mh;
-            v[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src) + col);
-            dst[u] = (int64_t)(o + r) * ncols + col;
-          }
-        }
-#pragma unroll
-        for (int u = 0; u < kCopyBatch; ++u)
-          if (dst[u] >= 0) __builtin_nontemporal_store(v[u], reinterpret_cast<u32x4*>(P.out_h) + dst[u]);
-      }
-    } else {
-      const int cells = nr * P.H;
-      for (int c = tid; c < cells; c += copy_threads) {
-        const int rl = c / P.H, col = c - rl * P.H;
-        const int r = g + P.G * rl;
-        const uint16_t* src = r < n ? P.th + (int64_t)(s + r) * P.th_stride : P.mh;
-        P.out_h[(int64_t)(o + r) * P.H + col] = src[col];
-      }
-    }
-  }
-
-  if (!do_meta || tid < meta_first) return;
-
-  // metadata: one thread per slot r of this workgroup's rows g, g+G, ...
-  const int mt = tid - meta_first, meta_threads = kWG - meta_first;
-  const int bonus = P.vtok ? P.vtok[(int64_t)b * (K + 1) + a] : P.bonus[b];
-  for (int r = g + P.G * mt; r < Wb; r += P.G * meta_threads) {
-    const int slot = o + r;
-    int64_t pos;
-    bool rejected;
-    if (r < n) {
-      pos = P.pos[s + r] + 1;
-      rejected = r > a;
-      P.hmap[s + r] = slot;
-      P.out_ids[slot] = (r == a) ? bonus : P.ids[s + min(r + 1, n - 1)];
-      P.rej[slot] = (uint8_t)rejected;
-      P.msk[slot] = 0;
-      if (r == a) P.nti[(int64_t)b * K] = slot;
-    } else {
-      const int m = r - n + 1;  // 1..K-1
-      pos = P.pos[s + a] + 1 + m;
-      rejected = false;
-      P.out_ids[slot] = P.mask_id;
-      P.rej[slot] = 0;
-      P.msk[slot] = 1;
-      P.nti[(int64_t)b * K + m] = slot;
-    }
-    P.out_pos[slot] = pos;
-    if (P.slots) P.slots[slot] = cache_slot(P, b, pos, rejected);
-  }
+  if (P.out_h != nullptr && tid < copy_threads) expand_copy_rows<VEC>(P, w, g, P.G, tid, copy_threads);
+  if (do_meta && tid >= meta_first) expand_meta_rows(P, b, w, g, P.G, tid - meta_first, kWG - meta_first, false);
 }
 
 hipError_t launch_expand(const ExpandParams& P, bool vec, hipStream_t stream) {

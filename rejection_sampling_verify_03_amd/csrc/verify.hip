@@ -45,6 +45,7 @@
 #include <limits.h>
 
 #include "device_common.hpp"
+#include "expand_device.hpp"
 #include "rowpass.hpp"
 #include "sampling.hpp"
 #include "verify_kernels.hpp"
@@ -411,8 +412,33 @@ __device__ __forceinline__ bool desc_samples(const ReqDesc& d, int K) {
 // wave64 workgroup per (request, segment), so that the hardware dispatcher
 // balances the sampled requests' segments over the compute units (the
 // requests that sample nothing exit after reading their decision record).
+// The workgroups past B * nseg expand the verification's outputs (a chained
+// expansion): hidden rows and metadata of rows g, g + ex_G, ... of request
+// b's window, after the decision (accepted counts and greedy tokens are
+// written); a sampled request's bonus id is left to the draw, which samples it.
+__device__ __forceinline__ void chained_expand(const VerifyParams& P, int t) {
+  const ExpandParams& E = P.ex;
+  const int b = t / P.ex_G, g = t % P.ex_G;
+  const int tid = threadIdx.x;
+  const ExpandWindow w = expand_window(E, b);
+  if (g == 0 && tid == 0) expand_out_start(E, b, w);
+  if (!w.valid) {
+    if (g == 0) expand_invalid(E, b, tid, 64);
+    return;
+  }
+  if (E.out_h != nullptr) {
+    if (E.vec) expand_copy_rows<true>(E, w, g, P.ex_G, tid, 64);
+    else expand_copy_rows<false>(E, w, g, P.ex_G, tid, 64);
+  }
+  expand_meta_rows(E, b, w, g, P.ex_G, tid, 64, desc_samples(P.desc[b], P.K));
+}
+
 template <int ES, bool VEC>
 __global__ __launch_bounds__(64) void verify_segsum_kernel(VerifyParams P) {
+  if ((int64_t)blockIdx.x >= (int64_t)P.B * P.nseg) {
+    chained_expand(P, (int)(blockIdx.x - P.B * P.nseg));
+    return;
+  }
   const int j = blockIdx.x % P.nseg;
   const int b = blockIdx.x / P.nseg;
   const ReqDesc d = P.desc[b];
@@ -506,7 +532,13 @@ __global__ __launch_bounds__(kWGD) void verify_draw_kernel(VerifyParams P) {
     y = draw_in_segment<ES, VEC>(prow, qrow, P.V, w, resmode, res, 1.0, found, base, target, false);
   else if (lastpos >= 0)
     y = draw_in_segment<ES, VEC>(prow, qrow, P.V, w, resmode, res, 1.0, lastpos, 0.0, 0.0, true);
-  if (tid == 0) P.out_tokens[(int64_t)b * (P.K + 1) + d.a] = y;
+  if (tid == 0) {
+    P.out_tokens[(int64_t)b * (P.K + 1) + d.a] = y;
+    if (P.ex_on) {  // the chained expansion's bonus id
+      const ExpandWindow w = expand_window(P.ex, b);
+      if (w.valid) P.ex.out_ids[w.o + d.a] = y;
+    }
+  }
 }
 
 // --------------------------------------------------------------- launch
@@ -542,7 +574,7 @@ static hipError_t launch_typed(VerifyParams P, uint64_t phase_starts, hipEvent_t
   hipLaunchKernelGGL((verify_decide_kernel<ES>), dim3((unsigned)P.B), dim3(kWG), 0, stream, P);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int64_t g2 = (int64_t)P.B * P.nseg;
+  const int64_t g2 = (int64_t)P.B * P.nseg + (P.ex_on ? (int64_t)P.B * P.ex_G : 0);
   hipLaunchKernelGGL((verify_segsum_kernel<ES, VEC>), dim3((unsigned)g2), dim3(64), 0, stream, P);
   e = hipGetLastError();
   if (e != hipSuccess) return e;

@@ -9,6 +9,33 @@
 
 namespace specv {
 
+struct ExpandParams {
+  int32_t B, K, H, N_in, G, mask_id;
+  const int32_t* ids;
+  const int64_t* pos;
+  const int32_t* in_start;
+  const int32_t* acc;
+  const int32_t* bonus;
+  const int32_t* vtok;  // verification output tokens [B, K+1] (bonus source) or null
+  const uint16_t* th;
+  int64_t th_stride;
+  const uint16_t* mh;
+  int32_t* out_ids;
+  int64_t* out_pos;
+  uint8_t* rej;
+  uint8_t* msk;
+  int32_t* nti;
+  int32_t* hmap;
+  int32_t* out_start;
+  uint16_t* out_h;
+  const int32_t* bt;  // block table (slot mapping) or null
+  int64_t bt_stride;
+  int32_t max_blocks, block_size;
+  int64_t* slots;     // slot mapping out, or null
+  int32_t hidden_only;  // gather the hidden rows only (no metadata, accepted counts unread)
+  int32_t vec;          // 16-byte hidden-row copies (H % 8 == 0 and aligned rows)
+};
+
 struct VerifyParams {
   int32_t B, K, V, R, C1, chunk1, nseg;
   const char* target;
@@ -35,33 +62,12 @@ struct VerifyParams {
   int32_t ph_lo, ph_nt, ph_nd, ph_check;
   // start of the last phase when the rows were read in several phases, else 0
   int32_t last_lo, phased;
+  // a chained expansion of this verification's outputs, folded into its
+  // sampling stage (ex_on): ex_G workgroups per request window
+  ExpandParams ex;
+  int32_t ex_on, ex_G;
 };
 
-struct ExpandParams {
-  int32_t B, K, H, N_in, G, mask_id;
-  const int32_t* ids;
-  const int64_t* pos;
-  const int32_t* in_start;
-  const int32_t* acc;
-  const int32_t* bonus;
-  const int32_t* vtok;  // verification output tokens [B, K+1] (bonus source) or null
-  const uint16_t* th;
-  int64_t th_stride;
-  const uint16_t* mh;
-  int32_t* out_ids;
-  int64_t* out_pos;
-  uint8_t* rej;
-  uint8_t* msk;
-  int32_t* nti;
-  int32_t* hmap;
-  int32_t* out_start;
-  uint16_t* out_h;
-  const int32_t* bt;  // block table (slot mapping) or null
-  int64_t bt_stride;
-  int32_t max_blocks, block_size;
-  int64_t* slots;     // slot mapping out, or null
-  int32_t hidden_only;  // gather the hidden rows only (no metadata, accepted counts unread)
-};
 
 struct DraftParams {
   int32_t B, K, V, N, nseg, C;  // C: chunks of kDraftChunkSegs segments per row

@@ -165,6 +165,45 @@ def test_expand_argument_errors(sv):
     assert launch(a) == sv.SPEC_OK
 
 
+def test_verify_expand_argument_errors(sv):
+    fake = 0x10000  # never dereferenced: every call below fails validation first
+    v = _valid_verify_args(sv)
+    v.workspace_bytes = 1 << 40  # passes the size check; no call below gets to the launch
+
+    def expand_for(v):
+        a = sv.SpecExpandArgs()
+        a.B, a.K, a.H, a.N_in = v.B, v.K, 8, v.B * (v.K + 1)
+        for f in ("in_token_ids", "in_positions", "in_start", "out_token_ids", "out_positions", "rejected_mask",
+                  "masked_mask", "new_token_indices", "hidden_map", "out_start"):
+            setattr(a, f, fake)
+        a.accepted_counts, a.verify_output_tokens = v.accepted_counts, v.output_tokens
+        a.out_hidden = None
+        return a
+
+    launch = lambda v, e: sv.lib.spec_verify_expand_launch(ctypes.byref(v), ctypes.byref(e), None)
+    small = _valid_verify_args(sv)
+    assert launch(small, expand_for(small)) == sv.SPEC_EWORKSPACE  # the verification's own status
+    e = expand_for(v)
+    e.K = v.K + 1
+    assert launch(v, e) == sv.SPEC_EINVAL
+    e = expand_for(v)
+    e.B, e.N_in = v.B + 1, (v.B + 1) * (v.K + 1)
+    assert launch(v, e) == sv.SPEC_EINVAL
+    e = expand_for(v)
+    e.accepted_counts = fake + 64  # not the verification's counts
+    assert launch(v, e) == sv.SPEC_EINVAL
+    e = expand_for(v)
+    e.verify_output_tokens, e.bonus_tokens = None, fake  # bonus not from the verification
+    assert launch(v, e) == sv.SPEC_EINVAL
+    e = expand_for(v)
+    e.out_start = None  # the expansion's own argument error
+    assert launch(v, e) == sv.SPEC_EINVAL
+    v0, e0 = _valid_verify_args(sv), expand_for(v)
+    v0.B = e0.B = 0
+    assert launch(v0, e0) == sv.SPEC_OK
+    assert sv.lib.spec_verify_expand_launch(None, None, None) == sv.SPEC_EINVAL
+
+
 def test_status_strings(sv):
     for code in (0, -1, -2, -3, -4, -5):
         assert sv.spec_status_string(code).startswith("SPEC_")

@@ -294,3 +294,116 @@ def test_hidden_gather_apart_on_a_second_stream(sv):
     for name in ("out_token_ids", "out_positions", "rejected_mask", "masked_mask", "new_token_indices",
                  "hidden_map", "out_start", "out_hidden"):
         assert torch.equal(getattr(fused, name), getattr(split, name)), name
+
+
+EXPAND_NAMES = ("out_token_ids", "out_positions", "rejected_mask", "masked_mask", "new_token_indices",
+                "hidden_map", "out_start", "out_hidden", "slot_mapping")
+
+
+def _chained_case(sv, name, B, K, V, H, seed, temps, phase_starts, spoil=None, num_drafts=None, strided=False):
+    """spec_verify_expand_launch against spec_verify_launch followed by
+    spec_expand_launch on the same inputs: every output bit for bit."""
+    dev = torch.device("cuda")
+    vin = workloads.mixture_inputs(name, B, K, V, torch.bfloat16, seed, dev, temps=temps, lam_lo=0.05, lam_hi=0.6)
+    x = vin.draft_tokens.clone()
+    if spoil is not None:
+        spoil(x)
+    e = workloads.expand_inputs(B=B, K=K, H=H, seed=seed, device="cuda")
+    hidden = e.target_hidden
+    if strided:  # a row stride wider than H
+        wide = torch.zeros(e.N_in, H + 8, dtype=torch.bfloat16, device=dev)
+        wide[:, :H] = hidden
+        hidden = wide[:, :H]
+    bt = table_for(e, 16, seed=seed, unmapped_fraction=0.1)
+    res = []
+    for fused in (False, True):
+        acc = torch.full((B,), -7, dtype=torch.int32, device=dev)
+        tok = torch.full((B, K + 1), -7, dtype=torch.int32, device=dev)
+        ws = sv.make_workspace(B, K, V, dev)
+        out = sv.expand_outputs(B, K, e.N_in, H, dev, with_slots=True)
+        for n in EXPAND_NAMES:
+            getattr(out, n).fill_(3)
+        va = sv.verify_args(vin.target, vin.draft, x, vin.temperature, acc, tok, None, ws, seed=seed, step=2,
+                            phase_starts=phase_starts, num_drafts=num_drafts)
+        xa = sv.expand_args(e.in_token_ids, e.in_positions, e.in_start, acc, None, K, e.mask_id, hidden,
+                            e.mask_hidden, out, verify_tokens=tok, block_table=bt, block_size=16)
+        st = torch.cuda.current_stream().cuda_stream
+        if fused:
+            assert sv.spec_verify_expand_launch(va, xa, st) == sv.SPEC_OK
+        else:
+            assert sv.spec_verify_launch(va, st) == sv.SPEC_OK
+            assert sv.spec_expand_launch(xa, st) == sv.SPEC_OK
+        torch.cuda.synchronize()
+        res.append([acc, tok] + [getattr(out, n) for n in EXPAND_NAMES])
+    for i, (u, v) in enumerate(zip(*res)):
+        assert torch.equal(u, v), (name, i)
+    return res[1]
+
+
+def test_verify_expand_chained_call(sv):
+    say("case: spec_verify_expand_launch == verify then expand")
+    # one pass and early-exit phases, greedy and sampled requests, the KV
+    # slot mapping with unmapped blocks, headline-sized rows
+    _chained_case(sv, "chain one pass", 48, 8, 151936, 2880, 31, (0.0, 0.6, 1.0), 0)
+    _chained_case(sv, "chain phased", 48, 8, 151936, 2880, 32, (0.0, 0.6, 1.0), 0b100100)
+    # all sampled (every bonus id comes from the draw), all greedy
+    _chained_case(sv, "chain sampled", 16, 5, 32768, 256, 33, (1.0,), 0b1000)
+    _chained_case(sv, "chain greedy", 16, 5, 32768, 256, 34, (0.0,), 0)
+    # invalid draft tokens: accepted -1, the expansion marks the request invalid
+    def spoil(x):
+        x[1, 0] = -3
+        x[4, 2] = 1 << 20
+    acc = _chained_case(sv, "chain invalid", 8, 4, 4096, 64, 35, (0.0, 1.0), 0, spoil=spoil)[0]
+    assert acc[1].item() == -1 and acc[4].item() == -1
+    # ragged draft counts, a strided hidden tensor (scalar copy path), an odd H
+    nd = torch.tensor([4, 0, 2, 4, 1, 3, 4, 2], dtype=torch.int32, device="cuda")
+    _chained_case(sv, "chain ragged", 8, 4, 4096, 64, 36, (0.0, 1.0), 0b100, num_drafts=nd, strided=True)
+    _chained_case(sv, "chain odd H", 8, 4, 4096, 61, 37, (1.0,), 0)
+
+
+def test_verify_expand_chained_call_graph_capture(sv):
+    say("case: spec_verify_expand_launch captured in a graph")
+    dev = torch.device("cuda")
+    B, K, V, H = 32, 8, 32768, 256
+    vin = workloads.mixture_inputs("chain graph", B, K, V, torch.bfloat16, 41, dev, temps=(0.0, 0.6, 1.0),
+                                   lam_lo=0.05, lam_hi=0.6)
+    e = workloads.expand_inputs(B=B, K=K, H=H, seed=41, device="cuda")
+    bt = table_for(e, 16, seed=41)
+    acc = torch.empty(B, dtype=torch.int32, device=dev)
+    tok = torch.empty(B, K + 1, dtype=torch.int32, device=dev)
+    ws = sv.make_workspace(B, K, V, dev)
+    out = sv.expand_outputs(B, K, e.N_in, H, dev, with_slots=True)
+    va = sv.verify_args(vin.target, vin.draft, vin.draft_tokens, vin.temperature, acc, tok, None, ws, seed=9,
+                        step=1, phase_starts=0b100100)
+    xa = sv.expand_args(e.in_token_ids, e.in_positions, e.in_start, acc, None, K, e.mask_id, e.target_hidden,
+                        e.mask_hidden, out, verify_tokens=tok, block_table=bt, block_size=16)
+
+    def snapshot():
+        return [acc.clone(), tok.clone()] + [getattr(out, n).clone() for n in EXPAND_NAMES]
+
+    def reset():
+        acc.fill_(-5)
+        tok.fill_(-5)
+        for n in EXPAND_NAMES:
+            getattr(out, n).zero_()
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        assert sv.spec_verify_expand_launch(va, xa, s.cuda_stream) == sv.SPEC_OK
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    eager = snapshot()
+    g = torch.cuda.CUDAGraph()
+    reset()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        assert sv.spec_verify_expand_launch(va, xa, torch.cuda.current_stream().cuda_stream) == sv.SPEC_OK
+    for rep in range(3):
+        x = torch.randn(1 << 20, device=dev)
+        float(x.sum())
+        reset()
+        g.replay()
+        torch.cuda.synchronize()
+        for i, (u, v) in enumerate(zip(snapshot(), eager)):
+            assert torch.equal(u, v), (rep, i)
