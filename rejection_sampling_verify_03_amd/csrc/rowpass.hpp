@@ -22,48 +22,14 @@ __device__ __forceinline__ void raise_ref(float& M, double& S, float gm, float s
 
 // ------------------------------------------------------------ chunk passes
 // Each thread takes groups tid, tid + 256, ...: U of them per batch (U
-// 16-byte loads per lane in flight before any is used).  The last batch of a
-// chunk that is not a multiple of U * 256 groups loads clamped addresses (a
-// lane's first group again) and masks what lies past the chunk, so that its
-// loads are still issued together; the (< 8) trailing logits of a row whose
-// length is not a multiple of 8 go to thread 0.
+// 16-byte loads per lane in flight before any is used).  One loop body serves
+// every batch: groups past the chunk (in its last batch) load the lane's
+// first group again and are left out of the reduction, so a short last batch
+// still issues its loads together and the loop keeps one register set.  The
+// (< 8) trailing logits of a row whose length is not a multiple of 8 go to
+// thread 0.
 template <int ES>
 constexpr int batch_groups() { return ES == 2 ? 8 : 4; }  // 128 bytes per lane
-
-// The U groups g, g + 256, ... of a batch; with MASKED, groups from nfull on
-// read group g and come back as -inf.
-template <int ES, bool VEC, bool MASKED>
-__device__ __forceinline__ void load_batch(const char* __restrict__ row, int e0, int g, int nfull,
-                                           float x[batch_groups<ES>()][8]) {
-  constexpr int U = batch_groups<ES>();
-#pragma unroll
-  for (int u = 0; u < U; ++u) {
-    const int gu = g + u * kWG;
-    const int gl = (!MASKED || gu < nfull) ? gu : g;
-    load_group<ES, VEC>(row, (int64_t)e0 + 8 * (int64_t)gl, x[u]);
-    if (MASKED) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) x[u][i] = gu < nfull ? x[u][i] : -INFINITY;
-    }
-  }
-}
-
-template <int ES>
-__device__ __forceinline__ void stats_batch(const float x[batch_groups<ES>()][8], float s_hi, float s_lo, float& M,
-                                            double& S) {
-  constexpr int U = batch_groups<ES>();
-  float gm = -INFINITY;
-#pragma unroll
-  for (int u = 0; u < U; ++u)
-#pragma unroll
-    for (int i = 0; i < 8; ++i) gm = fmaxf(gm, x[u][i]);
-  raise_ref(M, S, gm, s_hi);
-  const float negM = -fmaxf(M, -1e30f);
-  float acc = 0.f;
-#pragma unroll
-  for (int u = 0; u < U; ++u) acc += sum8_exp(x[u], s_hi, s_lo, negM);
-  S += (double)acc;
-}
 
 template <int ES, bool VEC>
 __device__ __forceinline__ MS chunk_stats(const char* __restrict__ row, int e0, int e1, float s_hi,
@@ -72,16 +38,30 @@ __device__ __forceinline__ MS chunk_stats(const char* __restrict__ row, int e0, 
   const int nfull = (e1 - e0) >> 3;
   float M = -INFINITY;
   double S = 0.0;
-  int g = threadIdx.x;
-  for (; g + (U - 1) * kWG < nfull; g += kWG * U) {
+  for (int g = threadIdx.x; g < nfull; g += kWG * U) {
     float x[U][8];
-    load_batch<ES, VEC, false>(row, e0, g, nfull, x);
-    stats_batch<ES>(x, s_hi, s_lo, M, S);
-  }
-  if (g < nfull) {
-    float x[U][8];
-    load_batch<ES, VEC, true>(row, e0, g, nfull, x);
-    stats_batch<ES>(x, s_hi, s_lo, M, S);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int gu = g + u * kWG;
+      load_group<ES, VEC>(row, (int64_t)e0 + 8 * (int64_t)(gu < nfull ? gu : g), x[u]);
+    }
+    float gm = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      float m = x[u][0];
+#pragma unroll
+      for (int i = 1; i < 8; ++i) m = fmaxf(m, x[u][i]);
+      if (g + u * kWG < nfull) gm = fmaxf(gm, m);
+    }
+    raise_ref(M, S, gm, s_hi);
+    const float negM = -fmaxf(M, -1e30f);
+    float acc = 0.f;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const float e = sum8_exp(x[u], s_hi, s_lo, negM);
+      acc += g + u * kWG < nfull ? e : 0.f;
+    }
+    S += (double)acc;
   }
   const int t0 = e0 + 8 * nfull;
   if (t0 < e1 && threadIdx.x == 0) {
@@ -94,28 +74,37 @@ __device__ __forceinline__ MS chunk_stats(const char* __restrict__ row, int e0, 
   return MS{M, S};
 }
 
-// The groups past the chunk of a masked batch repeat the lane's first group
-// (same values, same indices), which cannot change the lowest-index argmax.
+// Full batches of U groups, then the remaining groups as one masked batch.
 template <int ES, bool VEC>
 __device__ __forceinline__ VI chunk_argmax(const char* __restrict__ row, int e0, int e1) {
   constexpr int U = batch_groups<ES>();
   const int nfull = (e1 - e0) >> 3;
   VI best{-INFINITY, INT_MAX};
   int g = threadIdx.x;
-  for (; g < nfull; g += kWG * U) {
+  for (; g + (U - 1) * kWG < nfull; g += kWG * U) {
+    float x[U][8];
+#pragma unroll
+    for (int u = 0; u < U; ++u) load_group<ES, VEC>(row, (int64_t)e0 + 8 * (int64_t)(g + u * kWG), x[u]);
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) best = vi_pick(best, VI{x[u][i], e0 + 8 * (g + u * kWG) + i});
+  }
+  if (g < nfull) {
+    // the remaining groups as one batch: a group past the chunk reads the
+    // lane's first group again and counts as -inf at its own (larger) index,
+    // which never wins against the lane's lower indices
     float x[U][8];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int gu = g + u * kWG;
-      const int gl = gu < nfull ? gu : g;
-      load_group<ES, VEC>(row, (int64_t)e0 + 8 * (int64_t)gl, x[u]);
+      load_group<ES, VEC>(row, (int64_t)e0 + 8 * (int64_t)(gu < nfull ? gu : g), x[u]);
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int gu = g + u * kWG;
-      const int gl = gu < nfull ? gu : g;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) best = vi_pick(best, VI{x[u][i], e0 + 8 * gl + i});
+      for (int i = 0; i < 8; ++i) best = vi_pick(best, VI{gu < nfull ? x[u][i] : -INFINITY, e0 + 8 * gu + i});
     }
   }
   const int t0 = e0 + 8 * nfull;

@@ -471,6 +471,10 @@ __global__ __launch_bounds__(kWGD) void verify_draw_kernel(VerifyParams P) {
   const bool in0 = tid < nseg;
   const double r0 = in0 ? seg[2 * tid + 0] : 0.0;
   const double p0 = in0 ? seg[2 * tid + 1] : 0.0;
+  // a chained expansion's window, for the bonus id written at the end: its
+  // loads go out with the others instead of after the draw
+  ExpandWindow xw{};
+  if (P.ex_on && tid == 0) xw = expand_window(P.ex, b);
   if (!desc_samples(d, P.K)) return;  // greedy or invalid: nothing to sample
   __shared__ double sh_base;
   int found = -1, lastpos = -1;
@@ -534,10 +538,7 @@ __global__ __launch_bounds__(kWGD) void verify_draw_kernel(VerifyParams P) {
     y = draw_in_segment<ES, VEC>(prow, qrow, P.V, w, resmode, res, 1.0, lastpos, 0.0, 0.0, true);
   if (tid == 0) {
     P.out_tokens[(int64_t)b * (P.K + 1) + d.a] = y;
-    if (P.ex_on) {  // the chained expansion's bonus id
-      const ExpandWindow w = expand_window(P.ex, b);
-      if (w.valid) P.ex.out_ids[w.o + d.a] = y;
-    }
+    if (P.ex_on && xw.valid) P.ex.out_ids[xw.o + d.a] = y;  // the chained expansion's bonus id
   }
 }
 
