@@ -305,6 +305,21 @@ __device__ __forceinline__ float wave_max_f(float x) {
   return lane_f(x, 63);
 }
 
+// The value of lane l - 1 in lane l (the whole wave shifted by one lane,
+// wave_shr:1 = 0x138), 0 in lane 0: with an inclusive scan, the exclusive one.
+__device__ __forceinline__ double wave_shr1_d(double x) { return dpp_d0<0x138, 0xf>(x); }
+
+// Maximum over the 64 lanes, the same in every lane.
+__device__ __forceinline__ int wave_max_i(int x) {
+  x = max(x, dpp_i<0x111, 0xf>(x, INT_MIN));
+  x = max(x, dpp_i<0x112, 0xf>(x, INT_MIN));
+  x = max(x, dpp_i<0x114, 0xf>(x, INT_MIN));
+  x = max(x, dpp_i<0x118, 0xf>(x, INT_MIN));
+  x = max(x, dpp_i<0x142, 0xa>(x, INT_MIN));
+  x = max(x, dpp_i<0x143, 0xc>(x, INT_MIN));
+  return lane_i(x, 63);
+}
+
 // Sum over the 64 lanes in a fixed order (the last lane of the inclusive
 // scan), the same in every lane.
 __device__ __forceinline__ double wave_total_d(double x) { return lane_d(wave_scan_d(x), 63); }

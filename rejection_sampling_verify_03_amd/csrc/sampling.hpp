@@ -141,18 +141,10 @@ __device__ int draw_in_segment(const char* prow, const char* qrow, int V, const 
     ls += wt[i];
     if (wt[i] > 0.0) lastpos = e0 + i;
   }
-  double x = ls;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const double y = __shfl_up(x, off, 64);
-    if (lane >= off) x += y;
-  }
-  double xe = __shfl_up(x, 1, 64);
-  if (lane == 0) xe = 0.0;
-  const double wtotal = __shfl(x, 63, 64);
-  int wl = lastpos;
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) wl = max(wl, __shfl_xor(wl, off, 64));
+  const double x = wave_scan_d(ls);  // DPP: fixed order, no LDS round trips
+  const double xe = wave_shr1_d(x);
+  const double wtotal = lane_d(x, 63);
+  const int wl = wave_max_i(lastpos);
   if (lane == 0) {
     blk_tot[wave] = wtotal;
     blk_last[wave] = wl;
@@ -196,7 +188,7 @@ __device__ int draw_in_segment(const char* prow, const char* qrow, int V, const 
         }
         if (pick < 0) pick = lastpos;  // cumulative rounding: stay inside this lane
       }
-      for (int off = 32; off >= 1; off >>= 1) pick = max(pick, __shfl_xor(pick, off, 64));
+      pick = lane_i(pick, L);
       if (pick < 0) pick = blk_last[wave];
     } else {
       pick = blk_last[wave];

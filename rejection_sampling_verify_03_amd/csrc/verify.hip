@@ -480,21 +480,36 @@ __global__ __launch_bounds__(kWGD) void verify_draw_kernel(VerifyParams P) {
   int found = -1, lastpos = -1;
   double base = 0.0, target;
   bool res;
-  if (nseg <= kWGD) {
-    // one pass: scans of both weight kinds, then the crossing of u' * W
-    double ir, er, tr, ip, ep, tp;
-    block_scan_d2<kWGD>(r0, p0, ir, er, tr, ip, ep, tp);
-    res = d.mode == kModeResidual && tr > 0.0;  // else the weights fall back to p
-    target = d.u * (res ? tr : tp);
-    const double incl = res ? ir : ip, excl = res ? er : ep, v = res ? r0 : p0;
-    const int f = block_first_true<kWGD>(in0 && incl > target);
-    lastpos = block_max_int<kWGD>(v > 0.0 ? tid : -1);
-    if (f >= 0 && tid == f) sh_base = excl;
-    __syncthreads();
-    if (f >= 0) {
-      found = f;
-      base = sh_base;
+  if (nseg <= 64) {
+    // one wave scans both weight kinds and finds the crossing of u' * W; the
+    // other waves take the result from LDS
+    __shared__ double sh_target;
+    __shared__ int sh_found, sh_last, sh_res;
+    if (tid < 64) {
+      const double ir = wave_scan_d(r0), ip = wave_scan_d(p0);
+      const double tr = lane_d(ir, 63), tp = lane_d(ip, 63);
+      const bool rs = d.mode == kModeResidual && tr > 0.0;  // else the weights fall back to p
+      const double tg = d.u * (rs ? tr : tp);
+      const double incl = rs ? ir : ip, v = rs ? r0 : p0;
+      const uint64_t m = __ballot(in0 && incl > tg);
+      const uint64_t pos = __ballot(v > 0.0);
+      const int f = m ? (int)__builtin_ctzll(m) : -1;
+      const double ex = wave_shr1_d(incl);          // exclusive prefix of every lane
+      const double bf = f >= 0 ? lane_d(ex, f) : 0.0;  // the crossing segment's start (whole wave)
+      if (tid == 0) {
+        sh_res = rs;
+        sh_target = tg;
+        sh_found = f;
+        sh_last = pos ? 63 - (int)__builtin_clzll(pos) : -1;
+        sh_base = bf;
+      }
     }
+    __syncthreads();
+    res = sh_res != 0;
+    target = sh_target;
+    found = sh_found;
+    lastpos = sh_last;
+    base = sh_base;
   } else {
     // totals of both weight kinds, a fixed-order batched scan over the segments
     double carry_r = 0.0, carry_p = 0.0;
