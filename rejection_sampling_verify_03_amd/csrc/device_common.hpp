@@ -324,6 +324,27 @@ __device__ __forceinline__ int wave_max_i(int x) {
 // scan), the same in every lane.
 __device__ __forceinline__ double wave_total_d(double x) { return lane_d(wave_scan_d(x), 63); }
 
+// wave_merge_ms through DPP: prefix merges across the rows (empty lanes
+// enter as (-inf, 0)), lane 63's read out; every lane ends with the same value.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ MS dpp_ms(MS v) {
+  MS o;
+  o.m = __int_as_float(dpp_i<CTRL, ROW_MASK>(__float_as_int(v.m), __float_as_int(-INFINITY)));
+  o.s = dpp_d0<CTRL, ROW_MASK>(v.s);
+  return o;
+}
+
+__device__ __forceinline__ MS wave_merge_ms_dpp(MS v) {
+  v = ms_merge(v, dpp_ms<0x111, 0xf>(v));
+  v = ms_merge(v, dpp_ms<0x112, 0xf>(v));
+  v = ms_merge(v, dpp_ms<0x114, 0xf>(v));
+  v = ms_merge(v, dpp_ms<0x118, 0xf>(v));
+  v = ms_merge(v, dpp_ms<0x142, 0xa>(v));
+  v = ms_merge(v, dpp_ms<0x143, 0xc>(v));
+  return MS{lane_f(v.m, 63), lane_d(v.s, 63)};
+}
+
+
 // (value, index) with larger value first, lower index on ties.
 struct VI {
   float v;

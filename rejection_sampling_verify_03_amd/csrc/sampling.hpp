@@ -289,8 +289,8 @@ __device__ __forceinline__ void segment_sums(const char* prow, const char* qrow,
       psum += (double)p8;
     }
   }
-  rsum = wave_sum_d(rsum);
-  psum = wave_sum_d(psum);
+  rsum = wave_total_d(rsum);  // DPP, fixed order
+  psum = wave_total_d(psum);
 }
 
 }  // namespace specv
