@@ -15,12 +15,12 @@ phase only for requests whose earlier drafts were all accepted), cut by the
 library's planner from the acceptance curve of 8 untimed one-pass steps; the
 outputs are identical to one pass (--early-exit off).
 
-Prints one JSON line: verified draft positions per second (B*K per step),
-the roofline of the dominant stage (the row statistics of verification: its
-row-pass kernels and, with phases, the decisions between them), timed with
-HIP events on the launch stream against the logit bytes the timed steps
-read, and the CPU oracle timed on the host's cores over whole steps of the
-same batch.
+Prints one JSON line: verified draft positions per second (B*K per step,
+wall clock over the timed steps), the roofline of the dominant stage (the row
+statistics of verification: its row-pass kernels and, with phases, the
+decisions between them), timed with HIP events on the launch stream on every
+--event-every-th timed step against the logit bytes those steps read, and the
+CPU oracle timed on the host's cores over whole steps of the same batch.
 """
 import argparse
 import json
@@ -41,6 +41,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--event-every", type=int, default=8,
+                    help="record the HIP events that time the stages on every N-th timed step only (each event "
+                         "record costs GPU time of its own; 1 = every step)")
     ap.add_argument("--separate-expand", action="store_true",
                     help="enqueue the expansion as its own call after the verification instead of the chained "
                          "call that runs it inside the verification's sampling stage")
@@ -245,8 +248,9 @@ def main():
     ex_args = sv.expand_args(in_ids, in_pos, in_start, accepted, None, K, mask_id, hidden, mask_hidden, out,
                              verify_tokens=tokens, block_table=block_table, block_size=block_size)
 
-    n_events = args.steps
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(n_events)]
+    every = max(1, args.event_every)
+    timed_with_events = [i for i in range(args.steps) if i % every == 0]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in timed_with_events]
     for e4 in ev:  # create the underlying HIP events
         for e in e4:
             e.record(stream)
@@ -275,7 +279,8 @@ def main():
     def step(i, events=None):
         ph = events[1] if events else untimed_phase
         va.step = i & 0xFFFFFFFF
-        va.phase_event = ph.cuda_event
+        # the phase event only where it is used: a timed stage, or the second stream's start
+        va.phase_event = ph.cuda_event if (events or overlap) else None
         va.phase_starts = plan["mask"]
         if events:
             events[0].record(stream)
@@ -325,7 +330,7 @@ def main():
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(i, ev[i])
+        step(i, ev[i // every] if i % every == 0 else None)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / args.steps
@@ -346,8 +351,9 @@ def main():
     for i in range(args.steps):
         step(i)
         acc_steps.append(accepted.cpu().numpy().copy())
-    read_bytes = float(np.mean([phased_logit_bytes(a, temps, mask, K, V, 2) for a in acc_steps]))
-    seq_bytes = float(np.mean([sequential_logit_bytes(a, temps, K, V, 2) for a in acc_steps]))
+    # the bytes of the steps whose stages the events timed
+    read_bytes = float(np.mean([phased_logit_bytes(acc_steps[i], temps, mask, K, V, 2) for i in timed_with_events]))
+    seq_bytes = float(np.mean([sequential_logit_bytes(acc_steps[i], temps, K, V, 2) for i in timed_with_events]))
     vbytes = algorithmic_verify_bytes(B, K, V, 2, temps)
     one_pass_bytes = vbytes - (B * K * 4 + B * 4 + B * 4 + B * (K + 1) * 4)
     ebytes = algorithmic_expand_bytes(B, K, H, B * (K + 1))
@@ -381,7 +387,7 @@ def main():
                      "sequential_min_bytes": seq_bytes},
         "early_exit": {"phase_starts": mask, "phases": [0] + [k for k in range(1, K + 1) if (mask >> k) & 1],
                        **{k: v for k, v in plan.items() if k != "mask"}},
-        "kernels_ms": {"verify_row_stage": k1_ms,
+        "kernels_ms": {"timed_steps_with_events": len(timed_with_events), "verify_row_stage": k1_ms,
                        ("sampling_stage_with_expansion" if chained else "verify_decide_and_draw"): float(k2.mean()),
                        **({} if chained else {("expand_metadata_and_join" if overlap else "expand"): float(ke.mean())}),
                        "verify_row_stage_p10_p90": [float(np.percentile(k1, 10)), float(np.percentile(k1, 90))]},
