@@ -69,7 +69,8 @@ def run_case(sv, inp, seed=0, step=0, request_base=0):
 
 
 @pytest.mark.parametrize("dtype,V", [(torch.bfloat16, 70001), (torch.float32, 33000),
-                                     (torch.bfloat16, 4096 * 8 * 2 + 77)])
+                                     (torch.bfloat16, 4096 * 8 * 2 + 77),
+                                     (torch.bfloat16, 64 * 4096 + 40007)])  # > 64 segments per row
 def test_parity_mixed_temperatures(sv, dtype, V):
     """Several 8-segment chunks per row, a ragged last segment, shared rows."""
     say("case: draft sampling B12 K5 N40 V%d %s" % (V, dtype))

@@ -72,7 +72,8 @@ def test_tiny_fp32_many_steps(sv):
 
 
 @pytest.mark.parametrize("dtype,V", [(torch.bfloat16, 70001), (torch.float32, 33000),
-                                     (torch.bfloat16, 2 * 32768 + 512)])
+                                     (torch.bfloat16, 2 * 32768 + 512),
+                                     (torch.bfloat16, 64 * 4096 + 40007)])  # > 64 segments: the block scan path
 def test_multi_chunk_mixed_temperatures(sv, dtype, V):
     say("case: B12 K5 V%d %s mixed T" % (V, dtype))
     inp = workloads.mixture_inputs("mixed B12 K5 V%d" % V, 12, 5, V, dtype, 3, "cuda",
