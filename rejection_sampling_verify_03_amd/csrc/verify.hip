@@ -9,7 +9,8 @@
 //
 // Four kernels in stream order, no host round trip, and no communication
 // between workgroups of one kernel (each kernel boundary makes the previous
-// kernel's writes visible, so no atomics and no cache-maintenance fences):
+// kernel's writes visible, so no cache-maintenance fences; the one device
+// atomic counts invalid requests for the host to read after the stream):
 //
 //  verify_rowstats  one 256-thread workgroup per (request, row, chunk of ~32K
 //      logits) streams every row the parallel formulation needs exactly once
@@ -29,11 +30,14 @@
 //  verify_segsum    one wave64 workgroup per (request, 4096-logit segment)
 //      sums the residual weights max(0, p - q) and the weights of p over its
 //      segment of the sampling row(s) (p_a and q_a, or p_K for the bonus).
+//      With a chained expansion, more one-wave workgroups at the end of its
+//      grid expand this verification's outputs (hidden rows, metadata).
 //
 //  verify_draw      one 512-thread workgroup per sampled request scans the
-//      segment sums for the inverse-CDF crossing of u' * R, recomputes the
-//      weights of that one segment (one 512-logit block per wave) and finds
-//      the token with a wavefront scan.
+//      segment sums for the inverse-CDF crossing of u' * R (one wave, DPP),
+//      recomputes the weights of that one segment (one 512-logit block per
+//      wave) and finds the token with a wavefront scan; with a chained
+//      expansion it also writes the bonus id into the drafter batch.
 //
 // Early exit (a request stops at its first rejection, same page, section
 // "核心思想"): the caller may cut the positions 0..K into phases.  The row
