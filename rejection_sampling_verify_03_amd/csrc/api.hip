@@ -1,6 +1,7 @@
 // api.hip -- the C ABI: host-side argument validation, workspace sizing and
 // kernel launches.  Every check here runs before anything is enqueued, and no
-// entry point synchronises the stream or allocates memory.
+// launch entry point synchronises the stream or allocates memory (the host
+// query spec_workspace_error waits for the stream it is given).
 #include <stdint.h>
 
 #include "spec_verify.h"

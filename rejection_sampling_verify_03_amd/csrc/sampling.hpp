@@ -1,5 +1,6 @@
 // sampling.hpp -- device pieces shared by the samplers (the verification's
-// draw and the draft-token draw): the per-logit sampling weights, bounded
+// draw and segment sums, their vocab-sharded forms, and the draft-token
+// statistics pass's bounded loads): the per-logit sampling weights, bounded
 // group loads, workgroup scans and searches, and the search for the
 // inverse-CDF crossing inside one 4096-logit segment.
 #pragma once
