@@ -72,6 +72,12 @@ def algorithmic_verify_bytes(B, K, V, es, temps):
     return logits + B * K * 4 + B * 4 + B * 4 + B * (K + 1) * 4
 
 
+def one_pass_logit_bytes(B, K, V, es, temps):
+    """Logit bytes of the row pass without early exit: every target row 0..K
+    and the draft rows 0..K-1 of sampled requests."""
+    return B * (K + 1) * V * es + int((temps > 0).sum()) * K * V * es
+
+
 def phased_logit_bytes(acc, temps, mask, K, V, es):
     """Logit bytes the row stage reads under the phase cut `mask` (0 = one
     pass) for one step with accepted counts `acc`: a request reads the rows of
@@ -345,6 +351,27 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
+    # the row pass as one launch over every row (no early exit), timed the same way on a few more
+    # steps: the kernel's own streaming rate, beside the planned stage above
+    one_pass = None
+    if plan["mask"] != 0:
+        saved_mask = plan["mask"]
+        plan["mask"] = 0
+        for i in range(5):
+            step(3_000_000 + i)
+        ev1 = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(24)]
+        for e4 in ev1:  # create the underlying HIP events
+            for e in e4:
+                e.record(stream)
+        torch.cuda.synchronize()
+        for i, e4 in enumerate(ev1):
+            step(4_000_000 + i, e4)
+        torch.cuda.synchronize()
+        k1o = float(np.mean([e[0].elapsed_time(e[1]) for e in ev1]))
+        plan["mask"] = saved_mask
+        gbs = one_pass_logit_bytes(B, K, V, 2, temps) / (k1o * 1e-3) / 1e9
+        one_pass = {"ms": k1o, "achieved": gbs, "frac": gbs / HBM_PEAK_GBS, "steps": len(ev1)}
+
     # the timed steps again, untimed (outputs depend only on seed and step), for the rows each one read
     mask = plan["mask"]
     acc_steps = []
@@ -384,7 +411,7 @@ def main():
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                      "traffic": measured_traffic(mask),
                      "algorithmic_bytes": read_bytes, "one_pass_bytes": one_pass_bytes,
-                     "sequential_min_bytes": seq_bytes},
+                     "sequential_min_bytes": seq_bytes, "one_pass_row_kernel": one_pass},
         "early_exit": {"phase_starts": mask, "phases": [0] + [k for k in range(1, K + 1) if (mask >> k) & 1],
                        **{k: v for k, v in plan.items() if k != "mask"}},
         "kernels_ms": {"timed_steps_with_events": len(timed_with_events), "verify_row_stage": k1_ms,
