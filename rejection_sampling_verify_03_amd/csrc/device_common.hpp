@@ -225,27 +225,6 @@ __device__ __forceinline__ MS ms_merge(MS a, MS b) {
   return r;
 }
 
-__device__ __forceinline__ double shfl_xor_d(double v, int lane_mask) {
-  return __shfl_xor(v, lane_mask, 64);
-}
-
-// Butterfly over the 64 lanes; every lane ends with the same value.
-__device__ __forceinline__ MS wave_merge_ms(MS v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    MS o;
-    o.m = __shfl_xor(v.m, off, 64);
-    o.s = shfl_xor_d(v.s, off);
-    v = ms_merge(v, o);
-  }
-  return v;
-}
-
-__device__ __forceinline__ double wave_sum_d(double v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v += shfl_xor_d(v, off);
-  return v;
-}
 
 // ----------------------------------------------- DPP lane movement (wave64) --
 // Cross-lane moves through the VALU's data-parallel-primitive path instead of
@@ -324,8 +303,9 @@ __device__ __forceinline__ int wave_max_i(int x) {
 // scan), the same in every lane.
 __device__ __forceinline__ double wave_total_d(double x) { return lane_d(wave_scan_d(x), 63); }
 
-// wave_merge_ms through DPP: prefix merges across the rows (empty lanes
-// enter as (-inf, 0)), lane 63's read out; every lane ends with the same value.
+// The (M, S) merge of the 64 lanes through DPP: prefix merges across the rows
+// (empty lanes enter as (-inf, 0)), lane 63's read out; every lane ends with
+// the same value.
 template <int CTRL, int ROW_MASK>
 __device__ __forceinline__ MS dpp_ms(MS v) {
   MS o;
@@ -334,7 +314,7 @@ __device__ __forceinline__ MS dpp_ms(MS v) {
   return o;
 }
 
-__device__ __forceinline__ MS wave_merge_ms_dpp(MS v) {
+__device__ __forceinline__ MS wave_merge_ms(MS v) {
   v = ms_merge(v, dpp_ms<0x111, 0xf>(v));
   v = ms_merge(v, dpp_ms<0x112, 0xf>(v));
   v = ms_merge(v, dpp_ms<0x114, 0xf>(v));
@@ -356,7 +336,8 @@ __device__ __forceinline__ VI vi_pick(VI a, VI b) {
   return take_b ? b : a;
 }
 
-// wave_argmax through DPP: prefix maxima across the rows, lane 63's read out.
+// The lowest-index argmax of the 64 lanes through DPP: prefix picks across the
+// rows, lane 63's read out; every lane ends with the same value.
 template <int CTRL, int ROW_MASK>
 __device__ __forceinline__ VI dpp_vi(VI v) {
   VI o;
@@ -365,7 +346,7 @@ __device__ __forceinline__ VI dpp_vi(VI v) {
   return o;
 }
 
-__device__ __forceinline__ VI wave_argmax_dpp(VI v) {
+__device__ __forceinline__ VI wave_argmax(VI v) {
   v = vi_pick(v, dpp_vi<0x111, 0xf>(v));
   v = vi_pick(v, dpp_vi<0x112, 0xf>(v));
   v = vi_pick(v, dpp_vi<0x114, 0xf>(v));
@@ -375,15 +356,5 @@ __device__ __forceinline__ VI wave_argmax_dpp(VI v) {
   return VI{lane_f(v.v, 63), lane_i(v.i, 63)};
 }
 
-__device__ __forceinline__ VI wave_argmax(VI v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    VI o;
-    o.v = __shfl_xor(v.v, off, 64);
-    o.i = __shfl_xor(v.i, off, 64);
-    v = vi_pick(v, o);
-  }
-  return v;
-}
 
 }  // namespace specv

@@ -79,7 +79,7 @@ __global__ __launch_bounds__(kWG) void draft_segstats_kernel(DraftParams P) {
         for (int q = 0; q < 8; ++q)
           if (e + q < P.V) best = vi_pick(best, VI{x[q], e + q});
       }
-      best = wave_argmax_dpp(best);
+      best = wave_argmax(best);
       part.m = best.v;
       part.idx = best.i;
       part.s = 0.0;
@@ -243,10 +243,7 @@ __global__ __launch_bounds__(64) void draft_draw_kernel(DraftParams P) {
       carry += tot;
     }
     if (pick < 0) {  // the last positive logit of the segment
-      int lp = lpos;
-#pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) lp = max(lp, __shfl_xor(lp, off, 64));
-      pick = lp;
+      pick = wave_max_i(lpos);
     }
     y = pick;
   }

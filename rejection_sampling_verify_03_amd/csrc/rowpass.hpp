@@ -116,7 +116,7 @@ __device__ __forceinline__ VI chunk_argmax(const char* __restrict__ row, int e0,
 __device__ __forceinline__ MS block_merge_ms(MS v) {
   __shared__ float sm[kWaves];
   __shared__ double ss[kWaves];
-  v = wave_merge_ms_dpp(v);
+  v = wave_merge_ms(v);
   const int w = threadIdx.x >> 6;
   if ((threadIdx.x & 63) == 0) {
     sm[w] = v.m;
@@ -132,7 +132,7 @@ __device__ __forceinline__ MS block_merge_ms(MS v) {
 __device__ __forceinline__ VI block_argmax(VI v) {
   __shared__ float sv[kWaves];
   __shared__ int si[kWaves];
-  v = wave_argmax_dpp(v);
+  v = wave_argmax(v);
   const int w = threadIdx.x >> 6;
   if ((threadIdx.x & 63) == 0) {
     sv[w] = v.v;

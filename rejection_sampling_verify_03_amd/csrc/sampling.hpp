@@ -89,8 +89,7 @@ template <int NT>
 __device__ __forceinline__ int block_max_int(int v) {
   constexpr int W = NT / 64;
   __shared__ int mx[W];
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v = max(v, __shfl_xor(v, off, 64));
+  v = wave_max_i(v);
   if ((threadIdx.x & 63) == 0) mx[threadIdx.x >> 6] = v;
   __syncthreads();
   int r = mx[0];
@@ -208,18 +207,8 @@ __device__ __forceinline__ void block_scan_d2(double v0, double v1, double& incl
   constexpr int W = NT / 64;
   __shared__ double wt[2][W];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  double x0 = v0, x1 = v1;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const double y0 = __shfl_up(x0, off, 64);
-    const double y1 = __shfl_up(x1, off, 64);
-    if (lane >= off) {
-      x0 += y0;
-      x1 += y1;
-    }
-  }
-  double e0 = __shfl_up(x0, 1, 64), e1 = __shfl_up(x1, 1, 64);
-  if (lane == 0) e0 = e1 = 0.0;
+  const double x0 = wave_scan_d(v0), x1 = wave_scan_d(v1);  // DPP, fixed order
+  const double e0 = wave_shr1_d(x0), e1 = wave_shr1_d(x1);
   if (lane == 63) {
     wt[0][w] = x0;
     wt[1][w] = x1;
