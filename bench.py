@@ -57,6 +57,9 @@ def parse():
     ap.add_argument("--early-exit", choices=("plan", "off"), default="plan",
                     help="plan: read rows in phases planned from the acceptance of the warmup steps; "
                          "off: one pass over every row")
+    ap.add_argument("--phase-starts", type=int, default=None,
+                    help="with --early-exit plan: use this phase mask (bit k starts a phase at draft position k) "
+                         "instead of the one planned from the acceptance curve")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the timed steps, copy 1 GiB device to device once (a plain copy kernel of known "
                          "size, to scale hardware byte counters)")
@@ -134,11 +137,14 @@ def sequential_logit_bytes(acc, temps, K, V, es):
     return rows * V * es
 
 
-# Planner inputs: one extra phase costs its decision kernel and two launch gaps
-# (~8 us measured), priced against the time to stream one row of every request
-# at a nominal 6.8 TB/s (the row pass's measured one-pass rate), so that the
-# plan depends only on the acceptance curve, not on timing noise.
-PHASE_BOUNDARY_US = 8.0
+# Planner inputs: one extra phase costs its decision kernel, two launch gaps and
+# the ramp-up and tail of one more row-pass kernel. Fitted to the row stages of
+# forced cuts at the headline batch (one, two and three phases), that is
+# 11-12.6 us per boundary beyond the bytes the phase saves at the nominal rate;
+# it is priced against the time to stream one row of every request at a nominal
+# 6.8 TB/s (the row pass's measured one-pass rate), so that the plan depends
+# only on the acceptance curve, not on timing noise.
+PHASE_BOUNDARY_US = 12.0
 NOMINAL_ROW_GBS = 6800.0
 PLAN_STEPS = 8  # one-pass steps whose accepted counts give the survival curve
 
@@ -329,6 +335,9 @@ def main():
         surv = sv.survival_from_accepted(accs, K)
         row_us = B * V * 2 / (NOMINAL_ROW_GBS * 1e3)
         plan["mask"] = sv.spec_verify_plan_phases(K, surv, sampled_fraction, PHASE_BOUNDARY_US / row_us)
+        if args.phase_starts is not None:
+            plan["planned_mask"] = plan["mask"]
+            plan["mask"] = args.phase_starts
         plan["survival"] = [round(v, 4) for v in surv]
         plan["phase_cost_rows"] = round(PHASE_BOUNDARY_US / row_us, 4)
     for i in range(args.warmup):
