@@ -54,18 +54,23 @@ __global__ __launch_bounds__(kWG) void draft_segstats_kernel(DraftParams P) {
   const bool greedy = T == 0.0f;
   float s_hi = 0.f, s_lo = 0.f;
   if (!greedy) temperature_scale(T, s_hi, s_lo);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // the wave index through readfirstlane, so that the segment bounds and the
+  // full-segment test below are scalar (uniform branches around the loads)
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int j1 = min(P.nseg, (c + 1) * kDraftChunkSegs);
   for (int j = c * kDraftChunkSegs + wave; j < j1; j += kWaves) {
     const int s0 = j * kSeg;
     const bool full = s0 + kSeg <= P.V;
     RawGroup<ES, VEC> rg[kSegGroups];
+    if (full) {  // eight loads in a row, none under a branch
 #pragma unroll
-    for (int g = 0; g < kSegGroups; ++g) {
-      const int e = s0 + (g * 64 + lane) * 8;
-      if (full) rg[g] = load_raw<ES, VEC>(lg, e);
-      else if (e < P.V) rg[g] = load_raw_bounded<ES, VEC>(lg, e, P.V);
-      else rg[g] = neg_inf_group<ES, VEC>();
+      for (int g = 0; g < kSegGroups; ++g) rg[g] = load_raw<ES, VEC>(lg, s0 + (g * 64 + lane) * 8);
+    } else {
+#pragma unroll
+      for (int g = 0; g < kSegGroups; ++g) {
+        const int e = s0 + (g * 64 + lane) * 8;
+        rg[g] = e < P.V ? load_raw_bounded<ES, VEC>(lg, e, P.V) : neg_inf_group<ES, VEC>();
+      }
     }
     RowPartial part;
     if (greedy) {

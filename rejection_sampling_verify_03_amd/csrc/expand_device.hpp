@@ -68,7 +68,10 @@ constexpr int kCopyBatch = 8;  // 16-byte cells per lane loaded before any is st
 // The hidden rows g, g + G, ... of request window w, copied by `nthreads`
 // threads (tid in [0, nthreads)): slot o + r takes input row s + r (r < n)
 // or the MASK placeholder; loads of a batch are all issued before its stores,
-// and the output is written once (non-temporal stores).
+// and the output is written once (non-temporal stores).  A lane past the last
+// cell reloads the last cell and stores nothing: with every load of a batch
+// unconditional the compiler can wait for each load by its own count, where
+// loads under a branch made it drain the whole queue before every store.
 template <bool VEC>
 __device__ __forceinline__ void expand_copy_rows(const ExpandParams& P, const ExpandWindow& w, int g, int G, int tid,
                                                  int nthreads) {
@@ -83,14 +86,12 @@ __device__ __forceinline__ void expand_copy_rows(const ExpandParams& P, const Ex
 #pragma unroll
       for (int u = 0; u < kCopyBatch; ++u) {
         const int c = c0 + u * nthreads;
-        dst[u] = -1;
-        if (c < cells) {
-          const int rl = c / ncols, col = c - rl * ncols;
-          const int r = g + G * rl;
-          const uint16_t* src = r < w.n ? P.th + (int64_t)(w.s + r) * P.th_stride : P.mh;
-          v[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src) + col);
-          dst[u] = (int64_t)(w.o + r) * ncols + col;
-        }
+        const int cl = min(c, cells - 1);
+        const int rl = cl / ncols, col = cl - rl * ncols;
+        const int r = g + G * rl;
+        const uint16_t* src = r < w.n ? P.th + (int64_t)(w.s + r) * P.th_stride : P.mh;
+        v[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src) + col);
+        dst[u] = c < cells ? (int64_t)(w.o + r) * ncols + col : -1;
       }
 #pragma unroll
       for (int u = 0; u < kCopyBatch; ++u)

@@ -177,7 +177,7 @@ __global__ __launch_bounds__(kWG) void shard_decide_kernel(ShardParams P) {
   w.c_hi = (float)c;
   w.c_lo = (float)(c - (double)w.c_hi);
   double* seg = P.seg + (int64_t)b * P.nseg * 2;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // scalar segment bounds
   for (int j = wave; j < P.nseg; j += kWaves) {
     double rs, ps;
     if (res) segment_sums<ES, VEC, true>(prow, qrow, w, j * kSeg, P.Vs, rs, ps);

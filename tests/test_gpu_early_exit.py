@@ -142,22 +142,30 @@ def test_invalid_requests_phased(sv):
 
 
 def test_headline_planned(sv):
-    """B=256, K=8, V=151936 bf16 as benchmarked: the plan from the measured
-    survival curve of one step, then 3 steps bit-identical to one pass and 24
-    requests against the oracle."""
-    say("case: early exit, headline B256 K8 V151936 with a measured plan")
+    """B=256, K=8, V=151936 bf16 as benchmarked: plans from the measured
+    survival curve of one step at two boundary prices (the decision kernel
+    alone, and the price the benchmark plans with), each 3 steps
+    bit-identical to one pass and 24 requests against the oracle."""
+    import bench
+    say("case: early exit, headline B256 K8 V151936 with measured plans")
     inp = workloads.verify_headline(seed=0, device="cuda")
-    K = inp.K
+    B, K, V = inp.B, inp.K, inp.V
     acc, _, _ = sv.verify(inp.target, inp.draft, inp.draft_tokens, inp.temperature, seed=0, step=100)
     surv = sv.survival_from_accepted(acc.cpu().numpy(), K)
     f = float((inp.temperature > 0).float().mean())
-    mask = sv.spec_verify_plan_phases(K, surv, f, 0.7)
-    say("  survival", [round(s, 3) for s in surv], "plan", bin(mask))
-    assert mask != 0
-    for step in range(3):
-        acc, tok = one_vs_phased(sv, inp, mask, step=step)
-    rng = np.random.default_rng(2)
-    oracle_check(inp, acc, tok, 0, 2, idx=sorted(rng.choice(inp.B, 24, replace=False)))
+    row_us = B * V * 2 / (bench.NOMINAL_ROW_GBS * 1e3)
+    masks = []
+    for cost in (0.7, bench.PHASE_BOUNDARY_US / row_us):
+        mask = sv.spec_verify_plan_phases(K, surv, f, cost)
+        say("  survival", [round(s, 3) for s in surv], "cost", round(cost, 3), "plan", bin(mask))
+        assert mask != 0
+        if mask not in masks:
+            masks.append(mask)
+    for i, mask in enumerate(masks):
+        for step in range(3):
+            acc, tok = one_vs_phased(sv, inp, mask, step=step)
+        rng = np.random.default_rng(2 + i)
+        oracle_check(inp, acc, tok, 0, 2, idx=sorted(rng.choice(inp.B, 24, replace=False)))
 
 
 def test_gptoss_vocab_planned_full_parity(sv):

@@ -346,6 +346,8 @@ def test_verify_expand_chained_call(sv):
     # slot mapping with unmapped blocks, headline-sized rows
     _chained_case(sv, "chain one pass", 48, 8, 151936, 2880, 31, (0.0, 0.6, 1.0), 0)
     _chained_case(sv, "chain phased", 48, 8, 151936, 2880, 32, (0.0, 0.6, 1.0), 0b100100)
+    # the benchmarked step: B=256, K=8, V=151936, H=2880, phases {0..2 | 3..8}
+    _chained_case(sv, "chain headline", 256, 8, 151936, 2880, 38, (0.0, 0.6, 1.0), 0b1000)
     # all sampled (every bonus id comes from the draw), all greedy
     _chained_case(sv, "chain sampled", 16, 5, 32768, 256, 33, (1.0,), 0b1000)
     _chained_case(sv, "chain greedy", 16, 5, 32768, 256, 34, (0.0,), 0)
