@@ -215,9 +215,24 @@ def cpu_baseline(inp, seed, cpu_seconds):
         if time.process_time() - cpu0 >= cpu_seconds or steps >= 50:
             break
     B, K = x.shape
+    used = time.process_time() - cpu0
+    # the same oracle on one core, over blocks of 16 requests of the same
+    # batch (request_base keeps each request's uniforms those of the step)
+    one_wall = 0.0
+    one_req = 0
+    cpu1 = time.process_time()
+    while one_req < B and time.process_time() - cpu1 < cpu_seconds / 4:
+        r1 = min(B, one_req + 16)
+        t0 = time.perf_counter()
+        oracle.verify(tl[one_req:r1], dl[one_req:r1], x[one_req:r1], T[one_req:r1], seed=seed, step=0,
+                      request_base=one_req, debug=False, trace=False, nthreads=1)
+        one_wall += time.perf_counter() - t0
+        one_req = r1
     return {"value": steps * B * K / wall, "unit": "positions/s", "cores": threads, "kind": "oracle",
             "sample": "%d whole step(s) of the headline batch (B=%d, K=%d, V=%d), %.1f CPU-s"
-                      % (steps, B, K, tl.shape[-1], time.process_time() - cpu0)}
+                      % (steps, B, K, tl.shape[-1], used),
+            "single_core": {"value": one_req * K / one_wall, "unit": "positions/s", "cores": 1,
+                            "sample": "requests 0..%d of step 0 of the same batch" % (one_req - 1)}}
 
 
 def main():
