@@ -42,27 +42,21 @@ __device__ __forceinline__ bool draft_row_valid(const DraftParams& P, int row, f
   return row >= 0 && row < P.N && temperature_valid(T);
 }
 
-template <int ES, bool VEC>
-__global__ __launch_bounds__(kWG) void draft_segstats_kernel(DraftParams P) {
-  const int c = blockIdx.x % P.C;
-  const int i = blockIdx.x / P.C;  // (request, position)
-  const int b = i / P.K;
-  const int row = P.row_index[i];
-  const float T = P.temperature[b];
-  if (!draft_row_valid(P, row, T)) return;  // the draw reports -1
-  const char* lg = P.logits + (int64_t)row * P.row_stride * ES;
-  const bool greedy = T == 0.0f;
-  float s_hi = 0.f, s_lo = 0.f;
-  if (!greedy) temperature_scale(T, s_hi, s_lo);
-  // the wave index through readfirstlane, so that the segment bounds and the
-  // full-segment test below are scalar (uniform branches around the loads)
-  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int j1 = min(P.nseg, (c + 1) * kDraftChunkSegs);
-  for (int j = c * kDraftChunkSegs + wave; j < j1; j += kWaves) {
+// The segments j = j0, j0 + kWaves, ... below j1 of one row, one wave each:
+// lane l loads groups l, l+64, ... (one contiguous kilobyte per wave load)
+// and the wave writes the segment's record.  GREEDY: (max, lowest argmax);
+// else S * 2^M in one pass -- each lane sums its 64 logits against its own
+// reference ceil(lane max * s) and the wave merges the (M, S) pairs by exact
+// powers of two, so M is ceil(segment max * s) (-inf for a segment without a
+// finite logit).  The two kinds are separate loops so that each keeps its
+// own register set.
+template <int ES, bool VEC, bool GREEDY>
+__device__ __forceinline__ void segment_records(const DraftParams& P, const char* lg, RowPartial* out, int j0,
+                                                int j1, int lane, float s_hi, float s_lo) {
+  for (int j = j0; j < j1; j += kWaves) {
     const int s0 = j * kSeg;
-    const bool full = s0 + kSeg <= P.V;
     RawGroup<ES, VEC> rg[kSegGroups];
-    if (full) {  // eight loads in a row, none under a branch
+    if (s0 + kSeg <= P.V) {  // a full segment: eight loads in a row, none under a branch
 #pragma unroll
       for (int g = 0; g < kSegGroups; ++g) rg[g] = load_raw<ES, VEC>(lg, s0 + (g * 64 + lane) * 8);
     } else {
@@ -73,10 +67,11 @@ __global__ __launch_bounds__(kWG) void draft_segstats_kernel(DraftParams P) {
       }
     }
     RowPartial part;
-    if (greedy) {
+    if constexpr (GREEDY) {
       VI best{-INFINITY, INT_MAX};
 #pragma unroll
       for (int g = 0; g < kSegGroups; ++g) {
+        opaque_group<ES, VEC>(rg[g]);  // widened one group at a time
         float x[8];
         unpack_group<ES, VEC>(rg[g], x);
         const int e = s0 + (g * 64 + lane) * 8;
@@ -89,30 +84,49 @@ __global__ __launch_bounds__(kWG) void draft_segstats_kernel(DraftParams P) {
       part.idx = best.i;
       part.s = 0.0;
     } else {
+      float x[kSegGroups][8];
       float gm = -INFINITY;
 #pragma unroll
       for (int g = 0; g < kSegGroups; ++g) {
-        float x[8];
-        unpack_group<ES, VEC>(rg[g], x);
+        unpack_group<ES, VEC>(rg[g], x[g]);
 #pragma unroll
-        for (int q = 0; q < 8; ++q) gm = fmaxf(gm, x[q]);
+        for (int q = 0; q < 8; ++q) gm = fmaxf(gm, x[g][q]);
       }
-      gm = wave_max_f(gm);
-      const float M = ceilf(gm * s_hi);  // -inf for a segment without a finite logit
-      const float negM = -fmaxf(M, -1e30f);
+      const float Ml = ceilf(gm * s_hi);
+      const float negM = -fmaxf(Ml, -1e30f);
       double S = 0.0;
 #pragma unroll
-      for (int g = 0; g < kSegGroups; ++g) {
-        opaque_group<ES, VEC>(rg[g]);
-        float x[8];
-        unpack_group<ES, VEC>(rg[g], x);
-        S += (double)sum8_exp(x, s_hi, s_lo, negM);
-      }
-      part.m = M;
+      for (int g = 0; g < kSegGroups; ++g) S += (double)sum8_exp(x[g], s_hi, s_lo, negM);
+      const MS ms = wave_merge_ms(MS{Ml, S});
+      part.m = ms.m;
       part.idx = 0;
-      part.s = wave_total_d(S);
+      part.s = ms.s;
     }
-    if (lane == 0) P.segp[(int64_t)i * P.nseg + j] = part;
+    if (lane == 0) out[j] = part;
+  }
+}
+
+template <int ES, bool VEC>
+__global__ __launch_bounds__(kWG) void draft_segstats_kernel(DraftParams P) {
+  const int c = blockIdx.x % P.C;
+  const int i = blockIdx.x / P.C;  // (request, position)
+  const int b = i / P.K;
+  const int row = P.row_index[i];
+  const float T = P.temperature[b];
+  if (!draft_row_valid(P, row, T)) return;  // the draw reports -1
+  const char* lg = P.logits + (int64_t)row * P.row_stride * ES;
+  // the wave index through readfirstlane, so that the segment bounds and the
+  // full-segment test are scalar (uniform branches around the loads)
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int j0 = c * kDraftChunkSegs + wave;
+  const int j1 = min(P.nseg, (c + 1) * kDraftChunkSegs);
+  RowPartial* out = P.segp + (int64_t)i * P.nseg;
+  if (T == 0.0f) {
+    segment_records<ES, VEC, true>(P, lg, out, j0, j1, lane, 0.f, 0.f);
+  } else {
+    float s_hi, s_lo;
+    temperature_scale(T, s_hi, s_lo);
+    segment_records<ES, VEC, false>(P, lg, out, j0, j1, lane, s_hi, s_lo);
   }
 }
 
