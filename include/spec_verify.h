@@ -44,6 +44,10 @@ typedef enum { SPEC_F32 = 0, SPEC_BF16 = 1 } spec_dtype;
 /* Largest number of drafts per request (one 64-lane wavefront ballot). */
 #define SPEC_MAX_K 63
 
+/* Largest vocabulary (2^31 - 2^16): every index into a row, padded to whole
+ * 4096-logit segments, stays within 32 bits.  Larger V is SPEC_EINVAL. */
+#define SPEC_MAX_V 2147418112
+
 /* ------------------------------------------------------------- verification
  *
  * Defined by the explainer page on speculative decoding, section "修正拒绝采样"
@@ -77,7 +81,7 @@ typedef enum { SPEC_F32 = 0, SPEC_BF16 = 1 } spec_dtype;
 typedef struct {
   int32_t B;                   /* requests, >= 0 */
   int32_t K;                   /* drafts per request, 1..SPEC_MAX_K */
-  int32_t V;                   /* vocabulary size, >= 1 */
+  int32_t V;                   /* vocabulary size, 1..SPEC_MAX_V */
   int32_t dtype;               /* spec_dtype of both logits tensors */
   const void* target_logits;   /* device [B, K+1, V] */
   int64_t t_req_stride;        /* elements between requests (0 = shared), else >= (K+1)*t_row_stride */
@@ -279,7 +283,7 @@ int spec_verify_expand_launch(const spec_verify_args* v, const spec_expand_args*
 typedef struct {
   int32_t B;                   /* requests, >= 0 */
   int32_t K;                   /* draft positions per request, >= 1 */
-  int32_t V;                   /* vocabulary size, >= 1 */
+  int32_t V;                   /* vocabulary size, 1..SPEC_MAX_V */
   int32_t N;                   /* rows of the logits buffer, >= 0 */
   int32_t dtype;               /* spec_dtype of the logits */
   const void* logits;          /* device [N, V] drafter logits */
@@ -330,7 +334,7 @@ int spec_draft_sample_launch(const spec_draft_args* args, hipStream_t stream);
  * global ids in [0, V)).
  */
 typedef struct {
-  int32_t B, K, V;             /* requests, drafts (1..SPEC_MAX_K), full vocabulary */
+  int32_t B, K, V;             /* requests, drafts (1..SPEC_MAX_K), full vocabulary (1..SPEC_MAX_V) */
   int32_t dtype;               /* spec_dtype */
   int32_t G, g;                /* shards, and this shard (0 <= g < G) */
   int32_t v0, Vs;              /* this shard's slice of the vocabulary: [v0, v0 + Vs), Vs >= 1 */

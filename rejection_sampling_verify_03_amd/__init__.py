@@ -19,6 +19,7 @@ LIB_PATH = os.path.join(HERE, "libspecverify.so")
 SPEC_OK, SPEC_EINVAL, SPEC_EDTYPE, SPEC_EALIGN, SPEC_EWORKSPACE, SPEC_ELAUNCH = 0, -1, -2, -3, -4, -5
 SPEC_F32, SPEC_BF16 = 0, 1
 SPEC_MAX_K = 63
+SPEC_MAX_V = 2147418112  # 2^31 - 2^16
 
 EXPORTED = ("spec_verify_workspace_bytes", "spec_verify_plan_phases", "spec_verify_launch",
             "spec_expand_launch", "spec_expand_hidden_launch", "spec_verify_expand_launch",

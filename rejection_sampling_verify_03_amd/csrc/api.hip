@@ -18,7 +18,7 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 int verify_check(const spec_verify_args* a) {
   if (!a) return SPEC_EINVAL;
-  if (a->B < 0 || a->K < 1 || a->K > SPEC_MAX_K || a->V < 1) return SPEC_EINVAL;
+  if (a->B < 0 || a->K < 1 || a->K > SPEC_MAX_K || a->V < 1 || a->V > SPEC_MAX_V) return SPEC_EINVAL;
   if (a->dtype != SPEC_F32 && a->dtype != SPEC_BF16) return SPEC_EDTYPE;
   if (a->B == 0) return SPEC_OK;
   if (!a->target_logits || !a->draft_logits || !a->draft_tokens || !a->temperature ||
@@ -66,7 +66,7 @@ size_t draft_ws_bytes(int32_t B, int32_t K, int32_t V) {
 
 int draft_check(const spec_draft_args* a) {
   if (!a) return SPEC_EINVAL;
-  if (a->B < 0 || a->K < 1 || a->V < 1 || a->N < 0) return SPEC_EINVAL;
+  if (a->B < 0 || a->K < 1 || a->V < 1 || a->V > SPEC_MAX_V || a->N < 0) return SPEC_EINVAL;
   if (a->dtype != SPEC_F32 && a->dtype != SPEC_BF16) return SPEC_EDTYPE;
   if (a->B == 0) return SPEC_OK;
   if (!a->row_index || !a->temperature || !a->tokens || !a->workspace) return SPEC_EINVAL;
@@ -87,7 +87,7 @@ size_t shard_ws_bytes(int32_t B, int32_t Vs) {
 
 int shard_check(const spec_shard_args* a) {
   if (!a) return SPEC_EINVAL;
-  if (a->B < 0 || a->K < 1 || a->K > SPEC_MAX_K || a->V < 1) return SPEC_EINVAL;
+  if (a->B < 0 || a->K < 1 || a->K > SPEC_MAX_K || a->V < 1 || a->V > SPEC_MAX_V) return SPEC_EINVAL;
   if (a->dtype != SPEC_F32 && a->dtype != SPEC_BF16) return SPEC_EDTYPE;
   if (a->G < 1 || a->g < 0 || a->g >= a->G) return SPEC_EINVAL;
   if (a->Vs < 1 || a->v0 < 0 || (int64_t)a->v0 + a->Vs > a->V) return SPEC_EINVAL;
@@ -147,7 +147,7 @@ bool shard_vec(const spec_shard_args* a) {
 extern "C" {
 
 size_t spec_shard_workspace_bytes(int32_t B, int32_t K, int32_t Vs) {
-  if (B < 0 || K < 1 || K > SPEC_MAX_K || Vs < 1) return 0;
+  if (B < 0 || K < 1 || K > SPEC_MAX_K || Vs < 1 || Vs > SPEC_MAX_V) return 0;
   return shard_ws_bytes(B, Vs);
 }
 
@@ -171,7 +171,7 @@ int spec_shard_draw_launch(const spec_shard_args* a, hipStream_t stream) {
 }
 
 size_t spec_draft_workspace_bytes(int32_t B, int32_t K, int32_t V) {
-  if (B < 0 || K < 1 || V < 1) return 0;
+  if (B < 0 || K < 1 || V < 1 || V > SPEC_MAX_V) return 0;
   return draft_ws_bytes(B, K, V);
 }
 
@@ -225,7 +225,7 @@ uint64_t spec_verify_plan_phases(int32_t K, const double* survival, double sampl
 }
 
 size_t spec_verify_workspace_bytes(int32_t B, int32_t K, int32_t V) {
-  if (B < 0 || K < 1 || K > SPEC_MAX_K || V < 1) return 0;
+  if (B < 0 || K < 1 || K > SPEC_MAX_K || V < 1 || V > SPEC_MAX_V) return 0;
   return make_layout(B, K, V).total;
 }
 

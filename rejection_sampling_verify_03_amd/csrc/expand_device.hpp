@@ -76,32 +76,37 @@ template <bool VEC>
 __device__ __forceinline__ void expand_copy_rows(const ExpandParams& P, const ExpandWindow& w, int g, int G, int tid,
                                                  int nthreads) {
   if (g >= w.W) return;
-  const int nr = (w.W - g + G - 1) / G;
+  const int nr = (int)(((int64_t)w.W - g + G - 1) / G);  // rows g, g + G, ... of the window
   if constexpr (VEC) {
     const int ncols = P.H >> 3;
-    const int cells = nr * ncols;
-    for (int c0 = tid; c0 < cells; c0 += nthreads * kCopyBatch) {
-      u32x4 v[kCopyBatch];
-      int64_t dst[kCopyBatch];
+    // cells are counted in 32 bits, in passes of at most 2^30 cells
+    const int pass_rows = max(1, (1 << 30) / max(ncols, 1));
+    for (int r0 = 0; r0 < nr; r0 += pass_rows) {
+      const int cells = min(nr - r0, pass_rows) * ncols;
+      for (int c0 = tid; c0 < cells; c0 += nthreads * kCopyBatch) {
+        u32x4 v[kCopyBatch];
+        int64_t dst[kCopyBatch];
 #pragma unroll
-      for (int u = 0; u < kCopyBatch; ++u) {
-        const int c = c0 + u * nthreads;
-        const int cl = min(c, cells - 1);
-        const int rl = cl / ncols, col = cl - rl * ncols;
-        const int r = g + G * rl;
-        const uint16_t* src = r < w.n ? P.th + (int64_t)(w.s + r) * P.th_stride : P.mh;
-        v[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src) + col);
-        dst[u] = c < cells ? (int64_t)(w.o + r) * ncols + col : -1;
+        for (int u = 0; u < kCopyBatch; ++u) {
+          const int c = c0 + u * nthreads;
+          const int cl = min(c, cells - 1);
+          const int rl = cl / ncols, col = cl - rl * ncols;
+          const int r = g + G * (r0 + rl);
+          const uint16_t* src = r < w.n ? P.th + (int64_t)(w.s + r) * P.th_stride : P.mh;
+          v[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src) + col);
+          dst[u] = c < cells ? (int64_t)(w.o + r) * ncols + col : -1;
+        }
+#pragma unroll
+        for (int u = 0; u < kCopyBatch; ++u)
+          if (dst[u] >= 0) __builtin_nontemporal_store(v[u], reinterpret_cast<u32x4*>(P.out_h) + dst[u]);
       }
-#pragma unroll
-      for (int u = 0; u < kCopyBatch; ++u)
-        if (dst[u] >= 0) __builtin_nontemporal_store(v[u], reinterpret_cast<u32x4*>(P.out_h) + dst[u]);
     }
   } else {
-    const int cells = nr * P.H;
-    for (int c = tid; c < cells; c += nthreads) {
-      const int rl = c / P.H, col = c - rl * P.H;
-      const int r = g + G * rl;
+    const int64_t cells = (int64_t)nr * P.H;
+    for (int64_t c = tid; c < cells; c += nthreads) {
+      const int64_t rl = c / P.H;
+      const int col = (int)(c - rl * P.H);
+      const int r = g + G * (int)rl;
       const uint16_t* src = r < w.n ? P.th + (int64_t)(w.s + r) * P.th_stride : P.mh;
       P.out_h[(int64_t)(w.o + r) * P.H + col] = src[col];
     }
@@ -116,7 +121,8 @@ __device__ __forceinline__ void expand_meta_rows(const ExpandParams& P, int b, c
   const int K = P.K;
   const int a = w.a;
   const int bonus = bonus_later ? 0 : (P.vtok ? P.vtok[(int64_t)b * (K + 1) + a] : P.bonus[b]);
-  for (int r = g + G * tid; r < w.W; r += G * nthreads) {
+  for (int64_t rr = g + (int64_t)G * tid; rr < w.W; rr += (int64_t)G * nthreads) {
+    const int r = (int)rr;
     const int slot = w.o + r;
     int64_t pos;
     bool rejected;

@@ -68,6 +68,8 @@ def test_workspace_sizing(sv):
     assert sv.spec_verify_workspace_bytes(4, 0, 10) == 0
     assert sv.spec_verify_workspace_bytes(4, 64, 10) == 0
     assert sv.spec_verify_workspace_bytes(4, 4, 0) == 0
+    assert sv.spec_verify_workspace_bytes(4, 4, sv.SPEC_MAX_V + 1) == 0
+    assert sv.spec_verify_workspace_bytes(1, 1, sv.SPEC_MAX_V) > 0
     small = sv.spec_verify_workspace_bytes(4, 4, 1024)
     big = sv.spec_verify_workspace_bytes(256, 8, 151936)
     assert 0 < small < big
@@ -96,6 +98,7 @@ def test_verify_argument_errors(sv):
     assert launch(a) == sv.SPEC_EWORKSPACE
     for field, value, want in [("K", 0, sv.SPEC_EINVAL), ("K", 64, sv.SPEC_EINVAL), ("V", 0, sv.SPEC_EINVAL),
                                ("B", -1, sv.SPEC_EINVAL), ("dtype", 5, sv.SPEC_EDTYPE),
+                               ("V", sv.SPEC_MAX_V + 1, sv.SPEC_EINVAL),
                                ("t_row_stride", 63, sv.SPEC_EINVAL), ("d_row_stride", 10, sv.SPEC_EINVAL),
                                ("t_req_stride", 64, sv.SPEC_EINVAL), ("d_req_stride", 5, sv.SPEC_EINVAL),
                                ("target_logits", None, sv.SPEC_EINVAL), ("draft_tokens", None, sv.SPEC_EINVAL),
@@ -247,6 +250,7 @@ def test_draft_argument_errors(sv):
     launch = lambda a: sv.spec_draft_sample_launch(a, None)
     assert launch(args()) == sv.SPEC_EWORKSPACE
     for field, value, want in [("K", 0, sv.SPEC_EINVAL), ("V", 0, sv.SPEC_EINVAL), ("B", -1, sv.SPEC_EINVAL),
+                               ("V", sv.SPEC_MAX_V + 1, sv.SPEC_EINVAL),
                                ("N", -1, sv.SPEC_EINVAL), ("dtype", 7, sv.SPEC_EDTYPE),
                                ("row_stride", 99, sv.SPEC_EINVAL), ("row_index", None, sv.SPEC_EINVAL),
                                ("temperature", None, sv.SPEC_EINVAL), ("tokens", None, sv.SPEC_EINVAL),
@@ -263,6 +267,7 @@ def test_draft_argument_errors(sv):
     assert sv.spec_draft_workspace_bytes(2, 3, 100) == 256
     assert sv.spec_draft_workspace_bytes(256, 8, 151936) == 256 * 8 * 38 * 16
     assert sv.spec_draft_workspace_bytes(1, 0, 10) == 0
+    assert sv.spec_draft_workspace_bytes(1, 1, sv.SPEC_MAX_V + 1) == 0
 
 
 def test_shard_argument_errors(sv):
@@ -283,10 +288,12 @@ def test_shard_argument_errors(sv):
         for field, value, want in [("G", 0, sv.SPEC_EINVAL), ("g", 2, sv.SPEC_EINVAL), ("g", -1, sv.SPEC_EINVAL),
                                    ("Vs", 0, sv.SPEC_EINVAL), ("v0", 51, sv.SPEC_EINVAL), ("v0", -1, sv.SPEC_EINVAL),
                                    ("K", 64, sv.SPEC_EINVAL), ("dtype", 3, sv.SPEC_EDTYPE),
+                                   ("V", sv.SPEC_MAX_V + 1, sv.SPEC_EINVAL),
                                    ("t_row_stride", 49, sv.SPEC_EINVAL), ("records", None, sv.SPEC_EINVAL),
                                    ("masses", None, sv.SPEC_EINVAL), ("workspace", 0x10008, sv.SPEC_EALIGN)]:
             a = args()
             setattr(a, field, value)
             assert launch(a, None) == want, (launch, field, value)
     assert sv.spec_shard_workspace_bytes(2, 3, 50) == 256 + 256
+    assert sv.spec_shard_workspace_bytes(1, 1, sv.SPEC_MAX_V + 1) == 0
     assert sv.spec_shard_workspace_bytes(256, 8, 37984) == 256 * 64 + 256 * 10 * 16
