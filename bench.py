@@ -52,6 +52,8 @@ def parse():
                          "stage runs (measured slower: the gather competes with the segment sums for HBM)")
     ap.add_argument("--no-draft-sampling", action="store_true",
                     help="skip the separate measurement of draft-token sampling at the new-token indices")
+    ap.add_argument("--no-shard-share", action="store_true",
+                    help="skip the separate measurement of one GPU's share of a 4-way vocab-sharded verification")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="approximate CPU-seconds of oracle work for the CPU baseline")
     ap.add_argument("--early-exit", choices=("plan", "off"), default="plan",
@@ -126,6 +128,40 @@ def draft_sampling(sv, torch, np, out, temperature, B, K, V, seed, dev, reps=50)
     nbytes = B * K * V * 2 + n_sampled * K * 4096 * 2
     del logits
     return {"workload": "drafter logits [%d, %d] bf16, B=%d requests x K=%d new-token indices" % (n_out, V, B, K),
+            "ms": ms, "positions_per_s": B * K / (ms * 1e-3), "bytes": nbytes,
+            "GBps": nbytes / (ms * 1e-3) / 1e9, "frac_of_hbm_peak": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+
+
+def shard_share(sv, torch, inp, seed, G=4, reps=50):
+    """One GPU's share of a tensor-parallel verification of the headline batch
+    over G vocabulary shards: shard 0's three stages (statistics over its
+    slice, decisions from every shard's records, draw) on its slice, timed
+    with HIP events after one run of every shard has filled the exchanged
+    records and masses (the same step each rep, so the work is the same).
+    Bytes: the slice of every target row 0..K and of the draft rows 0..K-1 of
+    sampled requests, once."""
+    B, K, V = inp.B, inp.K, inp.V
+    st = sv.shard_setup(inp.target, inp.draft, inp.draft_tokens, inp.temperature, G, seed=seed, step=0)
+    st.run()
+    stream = torch.cuda.current_stream()
+
+    def share():
+        for stage in range(3):
+            st.launch(stage, 0)
+
+    for _ in range(5):
+        share()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(reps):
+        share()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    Vs = st.shards[0][0].Vs
+    nbytes = one_pass_logit_bytes(B, K, Vs, 2, inp.temperature.cpu().numpy())
+    return {"workload": "shard 0 of %d: logits [%d, %d, %d..%d) bf16 of the headline batch" % (G, B, K + 1, 0, Vs),
             "ms": ms, "positions_per_s": B * K / (ms * 1e-3), "bytes": nbytes,
             "GBps": nbytes / (ms * 1e-3) / 1e9, "frac_of_hbm_peak": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
 
@@ -450,6 +486,8 @@ def main():
     }
     if not args.no_draft_sampling:
         line["draft_sampling"] = draft_sampling(sv, torch, np, out, inp.temperature, B, K, V, args.seed, dev)
+    if not args.no_shard_share:
+        line["shard_share_tp4"] = shard_share(sv, torch, inp, args.seed)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(inp, args.seed, args.cpu_seconds)
     print(json.dumps(line), flush=True)

@@ -459,14 +459,36 @@ def draft_sample(logits, row_index, temperature, seed=0, step=0, request_base=0,
 SHARD_RECORD_BYTES = 32
 
 
-def verify_sharded(target, draft, draft_tokens, temperature, G, seed=0, step=0, request_base=0, bounds=None,
-                   stream=None):
-    """The verification with the vocabulary split over G shards, each stage of
-    each shard launched through the C ABI on one GPU; the exchanges between
-    shards are the shared record and mass arrays, and the last one (the
-    sampled token, -1 on every shard but its owner) an element-wise maximum.
-    bounds: G+1 slice boundaries (default: as equal as possible).  Returns
-    (accepted [B], output_tokens [B, K+1], per-shard accepted counts [G, B])."""
+class ShardSetup:
+    """Argument blocks of the G shards of one vocab-sharded verification and
+    the arrays they exchange (records, masses) and write (per-shard accepted
+    counts [G, B], output tokens [G, B, K+1])."""
+
+    def __init__(self, shards, records, masses, acc, tok, stream_ptr):
+        self.shards, self.records, self.masses = shards, records, masses
+        self.acc, self.tok, self.stream_ptr = acc, tok, stream_ptr
+
+    def launch(self, stage, h):
+        """Enqueue stage 0 (statistics), 1 (decisions) or 2 (draw) of shard h."""
+        launch = (spec_shard_stats_launch, spec_shard_decide_launch, spec_shard_draw_launch)[stage]
+        rc = launch(self.shards[h][0], self.stream_ptr)
+        if rc != SPEC_OK:
+            raise SpecError(rc)
+
+    def run(self):
+        """Every stage of every shard, in stage order (the exchanges between
+        stages are the shared arrays)."""
+        for stage in range(3):
+            for h in range(len(self.shards)):
+                self.launch(stage, h)
+
+
+def shard_setup(target, draft, draft_tokens, temperature, G, seed=0, step=0, request_base=0, bounds=None,
+                stream=None):
+    """The argument blocks of a verification with the vocabulary split over G
+    shards (bounds: G+1 slice boundaries, default as equal as possible), each
+    shard reading only its slice of the logits, with their workspaces and
+    exchange arrays allocated here."""
     torch = _torch()
     B, K = draft_tokens.shape
     V = target.shape[-1]
@@ -480,7 +502,6 @@ def verify_sharded(target, draft, draft_tokens, temperature, G, seed=0, step=0, 
     masses = torch.empty(G * B * 2, dtype=torch.float64, device=dev)
     acc = torch.empty(G, B, dtype=torch.int32, device=dev)
     tok = torch.empty(G, B, K + 1, dtype=torch.int32, device=dev)
-    sp = _stream_ptr(stream)
     shards = []
     for h in range(G):
         v0, v1 = bounds[h], bounds[h + 1]
@@ -500,9 +521,18 @@ def verify_sharded(target, draft, draft_tokens, temperature, G, seed=0, step=0, 
         a.accepted_counts, a.output_tokens = acc[h].data_ptr(), tok[h].data_ptr()
         a.workspace, a.workspace_bytes = ws.data_ptr(), ws.numel()
         shards.append((a, ws))
-    for launch in (spec_shard_stats_launch, spec_shard_decide_launch, spec_shard_draw_launch):
-        for a, _ in shards:
-            rc = launch(a, sp)
-            if rc != SPEC_OK:
-                raise SpecError(rc)
-    return acc[0].clone(), tok.max(dim=0).values, acc
+    return ShardSetup(shards, records, masses, acc, tok, _stream_ptr(stream))
+
+
+def verify_sharded(target, draft, draft_tokens, temperature, G, seed=0, step=0, request_base=0, bounds=None,
+                   stream=None):
+    """The verification with the vocabulary split over G shards, each stage of
+    each shard launched through the C ABI on one GPU; the exchanges between
+    shards are the shared record and mass arrays, and the last one (the
+    sampled token, -1 on every shard but its owner) an element-wise maximum.
+    bounds: G+1 slice boundaries (default: as equal as possible).  Returns
+    (accepted [B], output_tokens [B, K+1], per-shard accepted counts [G, B])."""
+    st = shard_setup(target, draft, draft_tokens, temperature, G, seed=seed, step=step, request_base=request_base,
+                     bounds=bounds, stream=stream)
+    st.run()
+    return st.acc[0].clone(), st.tok.max(dim=0).values, st.acc

@@ -72,8 +72,14 @@ __global__ __launch_bounds__(kWG) void shard_stats_kernel(ShardParams P) {
   if (threadIdx.x == 0) P.recs[((int64_t)P.g * P.B + b) * P.R + r] = rec;
 }
 
+// The decision workgroup is 16 waves, so that each of a slice's segments
+// (10 at a quarter of a 151936-token vocabulary) gets a wave of its own and
+// the sampling row's segment sums take one round of loads.
+constexpr int kDecideWG = 1024;
+constexpr int kDecideWaves = kDecideWG / 64;
+
 template <int ES, bool VEC>
-__global__ __launch_bounds__(kWG) void shard_decide_kernel(ShardParams P) {
+__global__ __launch_bounds__(kDecideWG) void shard_decide_kernel(ShardParams P) {
   __shared__ float sm[2 * SPEC_MAX_K + 1];
   __shared__ double ss[2 * SPEC_MAX_K + 1];
   __shared__ float sz[2 * SPEC_MAX_K + 1];
@@ -178,7 +184,7 @@ __global__ __launch_bounds__(kWG) void shard_decide_kernel(ShardParams P) {
   w.c_lo = (float)(c - (double)w.c_hi);
   double* seg = P.seg + (int64_t)b * P.nseg * 2;
   const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // scalar segment bounds
-  for (int j = wave; j < P.nseg; j += kWaves) {
+  for (int j = wave; j < P.nseg; j += kDecideWaves) {
     double rs, ps;
     if (res) segment_sums<ES, VEC, true>(prow, qrow, w, j * kSeg, P.Vs, rs, ps);
     else segment_sums<ES, VEC, false>(prow, qrow, w, j * kSeg, P.Vs, rs, ps);
@@ -295,7 +301,7 @@ hipError_t launch_shard_stats(const ShardParams& P, int dtype, bool vec, hipStre
 }
 
 hipError_t launch_shard_decide(const ShardParams& P, int dtype, bool vec, hipStream_t stream) {
-  SHARD_DISPATCH(shard_decide_kernel, (unsigned)P.B, kWG);
+  SHARD_DISPATCH(shard_decide_kernel, (unsigned)P.B, kDecideWG);
 }
 
 hipError_t launch_shard_draw(const ShardParams& P, int dtype, bool vec, hipStream_t stream) {
