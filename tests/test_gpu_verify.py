@@ -303,6 +303,30 @@ def _sampled_parity(sv, inp, idx, seed, step, acc, tok, dbg, rep):
                 request_base=b, report=rep)
 
 
+@pytest.mark.parametrize("iseed", [1, 2])
+def test_headline_every_request(sv, iseed):
+    """The headline recipe (B=256, K=8, V=151936 bf16) on fresh inputs: every
+    request of the batch against the oracle under two Philox streams, each
+    run both in one pass and with the benchmarked early-exit cut
+    {0..2 | 3..8} (bit-identical)."""
+    say("case: headline B256 K8 V151936, every request, inputs seed %d" % iseed)
+    inp = workloads.verify_headline(seed=iseed, device="cuda")
+    tl, dl = workloads.logits_numpy(inp.target), workloads.logits_numpy(inp.draft)
+    x, T = inp.draft_tokens.cpu().numpy(), inp.temperature.cpu().numpy()
+    rep = Report()
+    for seed, step in ((iseed, 0), (2 ** 40 + iseed, 77)):
+        a1, t1, d1 = sv.verify(inp.target, inp.draft, inp.draft_tokens, inp.temperature, seed=seed, step=step,
+                               debug=True)
+        a2, t2, _ = sv.verify(inp.target, inp.draft, inp.draft_tokens, inp.temperature, seed=seed, step=step,
+                              debug=True, phase_starts=0b1000)
+        torch.cuda.synchronize()
+        assert torch.equal(a1, a2) and torch.equal(t1, t2), (seed, step)
+        compare(tl, dl, x, T, a1.cpu().numpy(), t1.cpu().numpy(), d1.cpu().numpy(), seed=seed, step=step,
+                report=rep)
+    say(rep.summary())
+    assert rep.ok(), rep.failures[:5]
+
+
 def test_headline_full_size_sampled(sv):
     """B=256, K=8, V=151936 bf16, temperatures {0, 0.6, 1}, mixture drafts:
     the whole batch in one launch (as benchmarked), 40 requests checked
