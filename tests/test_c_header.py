@@ -1,0 +1,40 @@
+"""The C ABI from C: a C99 program includes include/spec_verify.h (with
+-Wall -Wextra -Werror), links the built library and runs the host-side
+calls (workspace sizing, the phase planner, argument errors, status
+strings); each result must equal the one the Python binding gets."""
+import os
+import shutil
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def sv():
+    import rejection_sampling_verify_03_amd as m
+    return m
+
+
+def test_c_program_against_the_header(sv, tmp_path):
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    lib = sv.LIB_PATH
+    exe = tmp_path / "abi_host_calls"
+    subprocess.run([cc, "-std=c99", "-Wall", "-Wextra", "-Werror", "-I", os.path.join(ROOT, "include"),
+                    os.path.join(ROOT, "tests", "c", "abi_host_calls.c"), "-o", str(exe), lib,
+                    "-Wl,-rpath," + os.path.dirname(lib)], check=True)
+    out = subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout
+    got = dict(line.split(" ", 1) for line in out.strip().splitlines())
+    surv = [1.0, 0.8145, 0.7026, 0.6206, 0.5498, 0.501, 0.4668, 0.4395, 0.3989]
+    assert int(got["verify_workspace"]) == sv.spec_verify_workspace_bytes(256, 8, 151936) > 0
+    assert int(got["verify_workspace_bad"]) == 0
+    assert int(got["draft_workspace"]) == sv.spec_draft_workspace_bytes(256, 8, 151936) > 0
+    assert int(got["shard_workspace"]) == sv.spec_shard_workspace_bytes(256, 8, 37984) > 0
+    assert int(got["plan"]) == sv.spec_verify_plan_phases(8, surv, 2.0 / 3.0, 1.05) != 0
+    assert int(got["plan_null"]) == 0
+    for key in ("verify_null", "verify_bad", "expand_bad", "chained_bad", "draft_bad", "shard_bad"):
+        assert int(got[key]) == sv.SPEC_EINVAL, key
+    assert got["status"] == sv.lib.spec_status_string(sv.SPEC_EWORKSPACE).decode()
