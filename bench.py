@@ -274,7 +274,7 @@ def cpu_baseline(inp, seed, cpu_seconds):
 def main():
     args = parse()
     if args.gpus != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (request sharding is "
+        print("bench.py measures one GPU: the library has no multi-GPU path (request sharding is "
               "described in the design notes); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
     import numpy as np
