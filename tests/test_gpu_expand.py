@@ -300,11 +300,12 @@ EXPAND_NAMES = ("out_token_ids", "out_positions", "rejected_mask", "masked_mask"
                 "hidden_map", "out_start", "out_hidden", "slot_mapping")
 
 
-def _chained_case(sv, name, B, K, V, H, seed, temps, phase_starts, spoil=None, num_drafts=None, strided=False):
+def _chained_case(sv, name, B, K, V, H, seed, temps, phase_starts, spoil=None, num_drafts=None, strided=False,
+                  dtype=torch.bfloat16):
     """spec_verify_expand_launch against spec_verify_launch followed by
     spec_expand_launch on the same inputs: every output bit for bit."""
     dev = torch.device("cuda")
-    vin = workloads.mixture_inputs(name, B, K, V, torch.bfloat16, seed, dev, temps=temps, lam_lo=0.05, lam_hi=0.6)
+    vin = workloads.mixture_inputs(name, B, K, V, dtype, seed, dev, temps=temps, lam_lo=0.05, lam_hi=0.6)
     x = vin.draft_tokens.clone()
     if spoil is not None:
         spoil(x)
@@ -361,6 +362,10 @@ def test_verify_expand_chained_call(sv):
     nd = torch.tensor([4, 0, 2, 4, 1, 3, 4, 2], dtype=torch.int32, device="cuda")
     _chained_case(sv, "chain ragged", 8, 4, 4096, 64, 36, (0.0, 1.0), 0b100, num_drafts=nd, strided=True)
     _chained_case(sv, "chain odd H", 8, 4, 4096, 61, 37, (1.0,), 0)
+    # fp32 logits (the 4-byte segment-sum kernel with the expansion appended)
+    _chained_case(sv, "chain fp32", 12, 5, 10000, 128, 39, (0.0, 0.7, 1.0), 0b100, dtype=torch.float32)
+    # K = 63 (windows of n_b + 62 slots) with an irregular cut
+    _chained_case(sv, "chain K63", 6, 63, 4096, 64, 40, (0.0, 1.0), (1 << 10) | (1 << 40))
 
 
 def test_verify_expand_chained_call_graph_capture(sv):
