@@ -20,7 +20,10 @@ wall clock over the timed steps), the roofline of the dominant stage (the row
 statistics of verification: its row-pass kernels and, with phases, the
 decisions between them), timed with HIP events on the launch stream on every
 --event-every-th timed step against the logit bytes those steps read, and the
-CPU oracle timed on the host's cores over whole steps of the same batch.
+CPU oracle timed on the host's cores over whole steps of the same batch (and
+on one core).  Two side measurements, outside the timed steps: draft-token
+sampling at the step's new-token indices (draft_sampling) and one GPU's share
+of a 4-way vocab-sharded verification of the same batch (shard_share_tp4).
 """
 import argparse
 import json
