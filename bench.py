@@ -138,7 +138,8 @@ def draft_sampling(sv, torch, np, out, temperature, B, K, V, seed, dev, reps=50)
 def shard_share(sv, torch, inp, seed, G=4, reps=50):
     """One GPU's share of a tensor-parallel verification of the headline batch
     over G vocabulary shards: shard 0's three stages (statistics over its
-    slice, decisions from every shard's records, draw) on its slice, timed
+    slice, decisions from every shard's records, draw) on its slice, held as
+    a contiguous tensor as a tensor-parallel GPU would hold it, timed
     with HIP events after one run of every shard has filled the exchanged
     records and masses (the same step each rep, so the work is the same).
     Bytes: the slice of every target row 0..K and of the draft rows 0..K-1 of
@@ -147,6 +148,13 @@ def shard_share(sv, torch, inp, seed, G=4, reps=50):
     st = sv.shard_setup(inp.target, inp.draft, inp.draft_tokens, inp.temperature, G, seed=seed, step=0)
     st.run()
     stream = torch.cuda.current_stream()
+    # a tensor-parallel GPU holds its slice as a tensor of its own: shard 0
+    # reads contiguous copies [B, K+1, Vs] (the same values as the view)
+    a0 = st.shards[0][0]
+    t0 = inp.target[..., a0.v0:a0.v0 + a0.Vs].contiguous()
+    d0 = inp.draft[..., a0.v0:a0.v0 + a0.Vs].contiguous()
+    a0.target_logits, a0.t_req_stride, a0.t_row_stride = t0.data_ptr(), t0.stride(0), t0.stride(1)
+    a0.draft_logits, a0.d_req_stride, a0.d_row_stride = d0.data_ptr(), d0.stride(0), d0.stride(1)
 
     def share():
         for stage in range(3):
@@ -164,7 +172,8 @@ def shard_share(sv, torch, inp, seed, G=4, reps=50):
     ms = e0.elapsed_time(e1) / reps
     Vs = st.shards[0][0].Vs
     nbytes = one_pass_logit_bytes(B, K, Vs, 2, inp.temperature.cpu().numpy())
-    return {"workload": "shard 0 of %d: logits [%d, %d, %d..%d) bf16 of the headline batch" % (G, B, K + 1, 0, Vs),
+    del t0, d0
+    return {"workload": "shard 0 of %d: its slice [%d, %d, %d] bf16 of the headline batch, contiguous" % (G, B, K + 1, Vs),
             "ms": ms, "positions_per_s": B * K / (ms * 1e-3), "bytes": nbytes,
             "GBps": nbytes / (ms * 1e-3) / 1e9, "frac_of_hbm_peak": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
 
