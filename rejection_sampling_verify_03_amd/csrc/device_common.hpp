@@ -184,8 +184,12 @@ __device__ __forceinline__ float load_one(const char* __restrict__ row, int64_t 
 // Logits enter as t = x * s - M with s = log2(e) / T split into s_hi (fp32,
 // rounded toward zero) + s_lo (>= FLT_MIN, so -inf logits stay -inf and give 0)
 // and M an integer-valued reference, so exp2(t) <= 1 for the row maximum.
+// The large terms cancel first: x * s_hi - M is exact before its one rounding,
+// which is relative to the small result t, and the correction x * s_lo is
+// added to that.  (Adding x * s_lo to -M first would round at the ulp of M,
+// an error in t that grows with |logit| / T.)
 __device__ __forceinline__ float scaled_exp2(float x, float s_hi, float s_lo, float negM) {
-  return __builtin_amdgcn_exp2f(__builtin_fmaf(x, s_hi, __builtin_fmaf(x, s_lo, negM)));
+  return __builtin_amdgcn_exp2f(__builtin_fmaf(x, s_lo, __builtin_fmaf(x, s_hi, negM)));
 }
 
 // log2(e) / T split as s_hi + s_lo with s_hi rounded toward zero and

@@ -79,6 +79,18 @@ def test_parity_mixed_temperatures(sv, dtype, V):
         run_case(sv, inp, seed=11, step=step, request_base=5)
 
 
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("offset", [0.0, 40.0])
+def test_large_logits_low_temperature(sv, dtype, offset):
+    """Drafter rows shifted by +40 at temperatures 0.1 and 0.3: the sampled
+    law does not change under a shift, and neither may the tokens."""
+    say("case: draft sampling, logits + %g, T in {0.1, 0.3}, %s" % (offset, dtype))
+    inp = workloads.drafter_inputs(12, 5, 30, 40000, dtype, seed=13, device="cuda", temps=(0.1, 0.3),
+                                   offset=offset)
+    for step in range(2):
+        run_case(sv, inp, seed=7, step=step)
+
+
 @pytest.mark.parametrize("dtype,V", [(torch.bfloat16, 20003), (torch.float32, 1023), (torch.bfloat16, 9),
                                      (torch.float32, 1)])
 def test_scalar_path_and_tiny_rows(sv, dtype, V):

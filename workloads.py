@@ -114,9 +114,11 @@ def _draw_tokens(draft, temperature, K, g):
 
 
 def noisy_draft_inputs(name, B, K, V, dtype, seed, device, recipe, target_std=2.0, draft_noise=0.5,
-                       temperature=1.0):
+                       temperature=1.0, temps=None, offset=0.0):
     """Target rows from ``recipe`` ("gauss": i.i.d. N(0, target_std); "zipf"),
-    draft rows = target + N(0, draft_noise), a single temperature."""
+    draft rows = target + N(0, draft_noise), both shifted by ``offset`` (a
+    shift leaves every softmax unchanged); a single temperature, or one per
+    request drawn uniformly from ``temps``."""
     g = _gen(seed, device)
     if recipe == "gauss":
         t = target_std * torch.randn(B * (K + 1), V, generator=g, device=device)
@@ -125,10 +127,14 @@ def noisy_draft_inputs(name, B, K, V, dtype, seed, device, recipe, target_std=2.
     else:
         raise ValueError(recipe)
     d = t + draft_noise * torch.randn(B * (K + 1), V, generator=g, device=device)
-    target = t.reshape(B, K + 1, V).to(dtype)
-    draft = d.reshape(B, K + 1, V).to(dtype)
+    target = (t + offset).reshape(B, K + 1, V).to(dtype)
+    draft = (d + offset).reshape(B, K + 1, V).to(dtype)
     del t, d
-    temp = torch.full((B,), float(temperature), dtype=torch.float32, device=device)
+    if temps is None:
+        temp = torch.full((B,), float(temperature), dtype=torch.float32, device=device)
+    else:
+        tt = torch.tensor(temps, dtype=torch.float32, device=device)
+        temp = tt[torch.randint(0, len(temps), (B,), generator=g, device=device)].contiguous()
     x = _draw_tokens(draft, temp, K, g)
     return VerifyInputs(name, target, draft, x, temp, seed)
 
@@ -253,17 +259,42 @@ def expand_inputs(B=512, K=8, H=HIDDEN_GPT_OSS_20B, vocab=GPT_OSS_VOCAB, seed=0,
         target_hidden=hidden, mask_hidden=mask_hidden)
 
 
+def step_expand_inputs(inp, H=HIDDEN_GPT_OSS_20B, seed=0, block_size=16, max_offset=16384):
+    """The expansion batch of one verification step of ``inp`` (a
+    VerifyInputs on a device): per request the K+1 verified slots [last
+    token, x_0..x_{K-1}] with the last token uniform in [0, V), int64
+    positions off_b + j with off_b uniform in [0, max_offset), bf16 N(0, 1)
+    hidden rows of width H and mask row, MASK id = the GPT-OSS vocabulary
+    size, and a paged-KV block table of ``block_size``-slot blocks covering
+    every position the expansion can produce."""
+    dev = inp.target.device
+    B, K, V = inp.B, inp.K, inp.V
+    g = _gen(seed + 1, dev)
+    last = torch.randint(0, V, (B, 1), generator=g, device=dev, dtype=torch.int32)
+    in_ids = torch.cat([last, inp.draft_tokens], dim=1).reshape(-1).contiguous()
+    off = torch.randint(0, max_offset, (B, 1), generator=g, device=dev, dtype=torch.int64)
+    in_pos = (off + torch.arange(K + 1, device=dev)).reshape(-1).contiguous()
+    in_start = (torch.arange(B + 1, device=dev, dtype=torch.int32) * (K + 1)).contiguous()
+    hidden = torch.randn(B * (K + 1), H, generator=g, device=dev).to(torch.bfloat16)
+    mask_hidden = torch.randn(H, generator=g, device=dev).to(torch.bfloat16)
+    table = block_tables(B, (max_offset + 2 * K + 2) // block_size + 1, seed=seed + 2, device=dev)
+    return ExpandInputs(B=B, K=K, H=H, N_in=B * (K + 1), N_out=B * (2 * K), in_token_ids=in_ids,
+                        in_positions=in_pos, in_start=in_start, target_hidden=hidden, mask_hidden=mask_hidden,
+                        mask_id=GPT_OSS_VOCAB, block_table=table, block_size=block_size)
+
+
 class DraftInputs:
     def __init__(self, **kw):
         self.__dict__.update(kw)
 
 
-def drafter_inputs(B, K, N, V, dtype, seed, device, temps=(0.0, 0.6, 1.0)):
-    """Drafter logits [N, V] (Zipf rows, as the target recipe), K row indices
-    per request drawn uniformly from [0, N) (the new-token indices stand-in),
-    and a temperature per request drawn uniformly from ``temps``."""
+def drafter_inputs(B, K, N, V, dtype, seed, device, temps=(0.0, 0.6, 1.0), offset=0.0):
+    """Drafter logits [N, V] (Zipf rows, as the target recipe, shifted by
+    ``offset``), K row indices per request drawn uniformly from [0, N) (the
+    new-token indices stand-in), and a temperature per request drawn uniformly
+    from ``temps``."""
     g = _gen(seed, device)
-    logits = zipf_logits(N, V, g, device).to(dtype)
+    logits = (zipf_logits(N, V, g, device) + offset).to(dtype)
     row_index = torch.randint(0, N, (B, K), generator=g, device=device, dtype=torch.int64).to(torch.int32)
     t = torch.tensor(temps, dtype=torch.float32, device=device)
     temperature = t[torch.randint(0, len(temps), (B,), generator=g, device=device)]
