@@ -110,6 +110,10 @@ def lib():
         L.oracle_draft_sample.restype = ctypes.c_int
         L.oracle_draft_uniform.argtypes = [ctypes.c_uint64, ctypes.c_uint32, ctypes.c_uint32, ctypes.c_uint32,
                                            ctypes.c_void_p]
+        L.oracle_draft_uniforms_many.argtypes = [ctypes.c_uint64, ctypes.c_uint32, ctypes.c_void_p,
+                                                 ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
+        L.oracle_verify_uniforms_many.argtypes = [ctypes.c_uint64, ctypes.c_uint32, ctypes.c_void_p,
+                                                  ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]
         _lib = L
     return _lib
 
@@ -348,6 +352,32 @@ def draft_uniform(seed, step, request, position):
     lib().oracle_draft_uniform(int(seed) & (2**64 - 1), int(step) & 0xFFFFFFFF, int(request), int(position),
                                ctypes.byref(u))
     return u.value
+
+
+def draft_uniforms(seed, step, requests, positions):
+    """draft_uniform for arrays of (global request, position) pairs."""
+    r = _c(np.asarray(requests, dtype=np.int64) & 0xFFFFFFFF, np.uint32)
+    k = _c(np.asarray(positions, dtype=np.int64) & 0xFFFFFFFF, np.uint32)
+    if r.shape != k.shape:
+        raise ValueError("requests and positions must have one shape")
+    u = np.zeros(r.shape, np.float64)
+    lib().oracle_draft_uniforms_many(int(seed) & (2**64 - 1), int(step) & 0xFFFFFFFF, _ptr(r), _ptr(k), r.size,
+                                     _ptr(u))
+    return u
+
+
+def verify_uniforms(seed, step, requests, rows):
+    """The verification's two uniforms (accept test, sampling draw) of each
+    (global request, row) pair: arrays (u_accept, u_sample)."""
+    r = _c(np.asarray(requests, dtype=np.int64) & 0xFFFFFFFF, np.uint32)
+    k = _c(np.asarray(rows, dtype=np.int64) & 0xFFFFFFFF, np.uint32)
+    if r.shape != k.shape:
+        raise ValueError("requests and rows must have one shape")
+    ua = np.zeros(r.shape, np.float64)
+    us = np.zeros(r.shape, np.float64)
+    lib().oracle_verify_uniforms_many(int(seed) & (2**64 - 1), int(step) & 0xFFFFFFFF, _ptr(r), _ptr(k), r.size,
+                                      _ptr(ua), _ptr(us))
+    return ua, us
 
 
 def draft_sample(logits, row_index, temperature, seed=0, step=0, request_base=0, mutation=0):

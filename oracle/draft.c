@@ -34,6 +34,11 @@ void oracle_draft_uniform(uint64_t seed, uint32_t step, uint32_t request, uint32
   *u = oracle_uniform(out[0]);
 }
 
+void oracle_draft_uniforms_many(uint64_t seed, uint32_t step, const uint32_t* requests,
+                                const uint32_t* positions, int64_t n, double* u) {
+  for (int64_t i = 0; i < n; ++i) oracle_draft_uniform(seed, step, requests[i], positions[i], &u[i]);
+}
+
 int oracle_draft_sample(const oracle_draft_args* a) {
   if (!a || a->B < 0 || a->K < 1 || a->V < 1 || a->N < 0 || (a->dtype != 0 && a->dtype != 1)) return -1;
   if (a->B > 0 && (!a->logits || !a->row_index || !a->temperature || !a->tokens)) return -1;

@@ -56,3 +56,9 @@ void oracle_verify_uniforms(uint64_t seed, uint32_t step, uint32_t request, uint
   if (u_accept) *u_accept = oracle_uniform(out[0]);
   if (u_sample) *u_sample = oracle_uniform(out[1]);
 }
+
+void oracle_verify_uniforms_many(uint64_t seed, uint32_t step, const uint32_t* requests, const uint32_t* rows,
+                                 int64_t n, double* u_accept, double* u_sample) {
+  for (int64_t i = 0; i < n; ++i)
+    oracle_verify_uniforms(seed, step, requests[i], rows[i], &u_accept[i], &u_sample[i]);
+}

@@ -47,6 +47,10 @@ double oracle_uniform(uint32_t w);
  * {r, k, step, 0}, key {seed lo 32, seed hi 32}. */
 void oracle_verify_uniforms(uint64_t seed, uint32_t step, uint32_t request, uint32_t row,
                             double* u_accept, double* u_sample);
+/* The same for n (request, row) pairs: oracle_verify_uniforms(seed, step,
+ * requests[i], rows[i], &u_accept[i], &u_sample[i]) for each i. */
+void oracle_verify_uniforms_many(uint64_t seed, uint32_t step, const uint32_t* requests, const uint32_t* rows,
+                                 int64_t n, double* u_accept, double* u_sample);
 
 /* ------------------------------------------------------ decision primitives */
 /* Accept rule: u < min(1, p_x / q_x); q_x == 0 => accept iff p_x > 0. */
@@ -153,6 +157,9 @@ int oracle_expand(const oracle_expand_args* a);
 /* The uniform of the draft draw at (request, position, step): Philox4x32-10
  * counter {request, position, step, 1}, key {seed lo 32, seed hi 32}, word 0. */
 void oracle_draft_uniform(uint64_t seed, uint32_t step, uint32_t request, uint32_t position, double* u);
+/* The same for n (request, position) pairs. */
+void oracle_draft_uniforms_many(uint64_t seed, uint32_t step, const uint32_t* requests,
+                                const uint32_t* positions, int64_t n, double* u);
 
 typedef struct {
   int32_t B, K, V, N;

@@ -414,3 +414,66 @@ def test_verify_expand_chained_call_graph_capture(sv):
         torch.cuda.synchronize()
         for i, (u, v) in enumerate(zip(snapshot(), eager)):
             assert torch.equal(u, v), (rep, i)
+
+
+@pytest.mark.parametrize("iseed", [0, 5])
+def test_benchmarked_call_against_oracle(sv, iseed):
+    """The benchmarked step at its own shape: one spec_verify_expand_launch
+    over the headline batch (B=256, K=8, V=151936 bf16, T in {0, 0.6, 1},
+    mixture drafts) and its expansion (H=2880, the bonus read from the
+    verification's tokens, KV slot mapping through a 16-slot block table),
+    rows read in the early-exit phases {0..2 | 3..8}; checked against
+    oracle.verify followed by oracle.expand on the oracle's own outputs:
+    every request, every expansion array and every hidden row."""
+    from parity import Report, compare
+    dev = torch.device("cuda")
+    inp = workloads.verify_headline(seed=iseed, device=dev)
+    e = workloads.step_expand_inputs(inp, seed=iseed)
+    B, K, V, H = inp.B, inp.K, inp.V, e.H
+    tl, dl = workloads.logits_numpy(inp.target), workloads.logits_numpy(inp.draft)
+    x, T = inp.draft_tokens.cpu().numpy(), inp.temperature.cpu().numpy()
+    hid, mhid = workloads.bf16_bits(e.target_hidden), workloads.bf16_bits(e.mask_hidden)
+    host = {n: getattr(e, n).cpu().numpy() for n in ("in_token_ids", "in_positions", "in_start", "block_table")}
+    acc = torch.empty(B, dtype=torch.int32, device=dev)
+    tok = torch.empty(B, K + 1, dtype=torch.int32, device=dev)
+    ws = sv.make_workspace(B, K, V, dev)
+    out = sv.expand_outputs(B, K, e.N_in, H, dev, with_slots=True)
+    for seed, step in ((iseed, 0), ((1 << 40) + iseed, 77)):
+        say("case: benchmarked call B256 K8 V151936 H2880, inputs %d, seed %d step %d" % (iseed, seed, step))
+        for n in EXPAND_NAMES:
+            getattr(out, n).fill_(3)
+        va = sv.verify_args(inp.target, inp.draft, inp.draft_tokens, inp.temperature, acc, tok, None, ws,
+                            seed=seed, step=step, phase_starts=0b1000)
+        xa = sv.expand_args(e.in_token_ids, e.in_positions, e.in_start, acc, None, K, e.mask_id, e.target_hidden,
+                            e.mask_hidden, out, verify_tokens=tok, block_table=e.block_table,
+                            block_size=e.block_size)
+        assert sv.spec_verify_expand_launch(va, xa, torch.cuda.current_stream().cuda_stream) == sv.SPEC_OK
+        torch.cuda.synchronize()
+        a_g, t_g = acc.cpu().numpy(), tok.cpu().numpy()
+        rep = compare(tl, dl, x, T, a_g, t_g, None, seed=seed, step=step, report=Report())
+        say("  verification:", rep.summary())
+        assert rep.ok(), rep.failures[:5]
+        res = oracle.verify(tl, dl, x, T, seed=seed, step=step, debug=False, trace=False)
+        a_o = res.accepted
+        ref = oracle.expand(host["in_token_ids"], host["in_positions"], host["in_start"], a_o,
+                            res.tokens[np.arange(B), a_o], K, e.mask_id, hid, mhid,
+                            block_table=host["block_table"], block_size=e.block_size)
+        # requests whose verification differs only at a counted near-threshold
+        # decision legitimately expand differently: leave their windows out
+        same = (a_g == a_o) & (t_g == res.tokens).all(axis=1)
+        win = 2 * K  # every window holds n_b + K - 1 = 2K slots
+        slot_ok = np.repeat(same, win)
+        in_ok = np.repeat(same, K + 1)
+        for n in EXPAND_NAMES:
+            g = getattr(out, n)
+            g = workloads.bf16_bits(g) if n == "out_hidden" else g.cpu().numpy()
+            r = getattr(ref, n)
+            if n == "new_token_indices":
+                g, r = g[same], r[same]
+            elif n == "hidden_map":
+                g, r = g[in_ok], r[in_ok]
+            elif n != "out_start":
+                g, r = g[slot_ok], r[slot_ok]
+            assert np.array_equal(g, r), (n, iseed, seed, step)
+        say("  expansion: every array bit-exact on %d of %d windows" % (int(same.sum()), B))
+        assert same.sum() >= B - len(rep.near)

@@ -5,6 +5,7 @@ import os
 import numpy as np
 
 import oracle
+import philox_cases
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -57,3 +58,24 @@ def test_counter_layout_of_verification_draws():
     r = oracle.verify(t, d, [[3]], [1.0], seed=seed, step=step, request_base=req)
     assert r.accepted[0] == 0 and r.tokens[0, 0] == 0
     assert r.trace[0, 0, 0] == ua.value and r.trace[0, 0, 2] == us.value
+
+
+def test_device_stream_cases_match_the_oracle():
+    """The closed forms the device-versus-oracle stream test expects
+    (philox_cases) are the oracle's own outputs on those inputs: draft tokens
+    over equal logits, and verification over uniform target rows with
+    restricted draft rows, ragged counts and wrapping request indices."""
+    for seed, step, base in ((0, 0, 0), ((1 << 64) - 1, 0xFFFFFFFF, 0xFFFFFFFF - 20), (1 << 32, 99, 7)):
+        want = philox_cases.draft_expected(seed, step, base, 40, 9, 4096)
+        r = oracle.draft_sample(np.zeros((1, 4096), np.float32), np.zeros((40, 9), np.int32),
+                                np.ones(40, np.float32), seed=seed, step=step, request_base=base)
+        assert np.array_equal(r.tokens, want)
+    rng = np.random.default_rng(5)
+    for seed, step, base in ((3, 1, 0), (0xFEDCBA9876543210, 1 << 31, 0xFFFFFFFF - 30)):
+        c = philox_cases.VerifyCase(rng, 60, 63, 1024)
+        want_a, want_y, _ = c.expected(seed, step, base)
+        draft = c.drows[c.ridx]  # the row table gathered into [B, K, V]
+        r = oracle.verify(c.target, draft, c.x, np.ones(c.B, np.float32), seed=seed, step=step,
+                          request_base=base, num_drafts=c.kb, debug=False, trace=False)
+        assert np.array_equal(r.accepted, want_a)
+        assert np.array_equal(r.tokens[np.arange(c.B), want_a], want_y)
