@@ -138,6 +138,18 @@ typedef struct {
  * inputs). */
 uint64_t spec_verify_plan_phases(int32_t K, const double* survival, double sampled_fraction, double phase_cost);
 
+/* The price of one phase boundary on MI355X for a batch of this shape, in the
+ * unit spec_verify_plan_phases takes (the time to read one row of every
+ * request, B * V logits of `dtype`, at the row pass's streaming rate of
+ * 6.8 TB/s).  A boundary costs its decision kernel, two launch gaps and the
+ * ramp-up and tail of one more row-pass kernel: 12 us measured at B = 256
+ * and B = 1024, plus up to 7.7 us more when one row of every request is less
+ * than one dispatch round of the row pass (B * chunks per row below the
+ * 1280 workgroups 256 compute units hold at once), fitted to B = 64
+ * (V = 201088) where a boundary costs ~17 us.  Returns -1 for an invalid
+ * shape (which spec_verify_plan_phases turns into the one-pass plan). */
+double spec_verify_phase_cost(int32_t B, int32_t K, int32_t V, int32_t dtype);
+
 /* Bytes of device workspace a verification of this shape needs (0 for an
  * invalid shape).  The workspace carries nothing from one call to the next
  * (but the invalid-request count that spec_workspace_error reads): it needs

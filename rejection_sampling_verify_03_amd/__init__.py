@@ -21,7 +21,8 @@ SPEC_F32, SPEC_BF16 = 0, 1
 SPEC_MAX_K = 63
 SPEC_MAX_V = 2147418112  # 2^31 - 2^16
 
-EXPORTED = ("spec_verify_workspace_bytes", "spec_verify_plan_phases", "spec_verify_launch",
+EXPORTED = ("spec_verify_workspace_bytes", "spec_verify_plan_phases", "spec_verify_phase_cost",
+            "spec_verify_launch",
             "spec_expand_launch", "spec_expand_hidden_launch", "spec_verify_expand_launch",
             "spec_draft_workspace_bytes",
             "spec_draft_sample_launch", "spec_shard_workspace_bytes", "spec_shard_stats_launch",
@@ -101,6 +102,8 @@ def _load():
     L.spec_verify_plan_phases.argtypes = [ctypes.c_int32, ctypes.POINTER(ctypes.c_double), ctypes.c_double,
                                           ctypes.c_double]
     L.spec_verify_plan_phases.restype = ctypes.c_uint64
+    L.spec_verify_phase_cost.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32]
+    L.spec_verify_phase_cost.restype = ctypes.c_double
     L.spec_verify_launch.argtypes = [ctypes.POINTER(SpecVerifyArgs), ctypes.c_void_p]
     L.spec_verify_launch.restype = ctypes.c_int
     L.spec_workspace_error.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
@@ -145,6 +148,18 @@ def spec_verify_plan_phases(K, survival, sampled_fraction, phase_cost):
     draft position k.  Returns the phase_starts bit mask (0 = one pass)."""
     arr = (ctypes.c_double * (int(K) + 1))(*[float(v) for v in survival])
     return int(lib.spec_verify_plan_phases(int(K), arr, float(sampled_fraction), float(phase_cost)))
+
+
+def spec_verify_phase_cost(B, K, V, dtype=SPEC_BF16):
+    """The price of one early-exit phase boundary for a batch of this shape,
+    in row-units (the planner's unit); -1 for an invalid shape."""
+    return float(lib.spec_verify_phase_cost(int(B), int(K), int(V), int(dtype)))
+
+
+def plan_phases(B, K, V, survival, sampled_fraction, dtype=SPEC_BF16):
+    """The phase_starts mask the planner picks for this batch shape and
+    acceptance curve, with the boundary priced by spec_verify_phase_cost."""
+    return spec_verify_plan_phases(K, survival, sampled_fraction, spec_verify_phase_cost(B, K, V, dtype))
 
 
 def survival_from_accepted(accepted, K):

@@ -224,6 +224,21 @@ uint64_t spec_verify_plan_phases(int32_t K, const double* survival, double sampl
   return mask;
 }
 
+double spec_verify_phase_cost(int32_t B, int32_t K, int32_t V, int32_t dtype) {
+  if (B < 1 || K < 1 || K > SPEC_MAX_K || V < 1 || V > SPEC_MAX_V) return -1.0;
+  if (dtype != SPEC_F32 && dtype != SPEC_BF16) return -1.0;
+  // measured on MI355X (see the header): the boundary's fixed cost, the extra
+  // when a phase's rows cannot fill the chip, the slots of the row pass
+  // (256 compute units x 5 resident 256-thread workgroups) and its rate
+  constexpr double kBoundaryUs = 12.0, kUnderfillUs = 7.7, kSlots = 256.0 * 5.0, kRowBytesPerUs = 6.8e6;
+  const Layout L = make_layout(1, K, V);
+  const double per_row_unit = (double)B * (double)L.C1;  // workgroups reading one row of every request
+  const double fill = per_row_unit < kSlots ? 1.0 - per_row_unit / kSlots : 0.0;
+  const double boundary_us = kBoundaryUs + kUnderfillUs * fill;
+  const double row_us = (double)B * (double)V * (dtype == SPEC_BF16 ? 2.0 : 4.0) / kRowBytesPerUs;
+  return boundary_us / row_us;
+}
+
 size_t spec_verify_workspace_bytes(int32_t B, int32_t K, int32_t V) {
   if (B < 0 || K < 1 || K > SPEC_MAX_K || V < 1 || V > SPEC_MAX_V) return 0;
   return make_layout(B, K, V).total;

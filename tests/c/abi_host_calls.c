@@ -17,6 +17,8 @@ int main(void) {
   printf("shard_workspace %zu\n", spec_shard_workspace_bytes(256, 8, 37984));
   printf("plan %llu\n", (unsigned long long)spec_verify_plan_phases(8, survival, 2.0 / 3.0, 1.05));
   printf("plan_null %llu\n", (unsigned long long)spec_verify_plan_phases(8, NULL, 0.5, 1.0));
+  printf("phase_cost %.17g\n", spec_verify_phase_cost(256, 8, 151936, SPEC_BF16));
+  printf("phase_cost_bad %.17g\n", spec_verify_phase_cost(0, 8, 151936, SPEC_BF16));
   printf("verify_null %d\n", spec_verify_launch(NULL, NULL));
   v.K = 0; /* invalid: rejected before anything is enqueued */
   printf("verify_bad %d\n", spec_verify_launch(&v, NULL));

@@ -35,6 +35,8 @@ def test_c_program_against_the_header(sv, tmp_path):
     assert int(got["shard_workspace"]) == sv.spec_shard_workspace_bytes(256, 8, 37984) > 0
     assert int(got["plan"]) == sv.spec_verify_plan_phases(8, surv, 2.0 / 3.0, 1.05) != 0
     assert int(got["plan_null"]) == 0
+    assert float(got["phase_cost"]) == sv.spec_verify_phase_cost(256, 8, 151936) > 0
+    assert float(got["phase_cost_bad"]) == -1.0
     for key in ("verify_null", "verify_bad", "expand_bad", "chained_bad", "draft_bad", "shard_bad"):
         assert int(got[key]) == sv.SPEC_EINVAL, key
     assert got["status"] == sv.lib.spec_status_string(sv.SPEC_EWORKSPACE).decode()

@@ -144,18 +144,17 @@ def test_invalid_requests_phased(sv):
 def test_headline_planned(sv):
     """B=256, K=8, V=151936 bf16 as benchmarked: plans from the measured
     survival curve of one step at two boundary prices (the decision kernel
-    alone, and the price the benchmark plans with), each 3 steps
-    bit-identical to one pass and 24 requests against the oracle."""
-    import bench
+    alone, and the price the library gives this batch shape, which the
+    benchmark plans with), each 3 steps bit-identical to one pass and 24
+    requests against the oracle."""
     say("case: early exit, headline B256 K8 V151936 with measured plans")
     inp = workloads.verify_headline(seed=0, device="cuda")
     B, K, V = inp.B, inp.K, inp.V
     acc, _, _ = sv.verify(inp.target, inp.draft, inp.draft_tokens, inp.temperature, seed=0, step=100)
     surv = sv.survival_from_accepted(acc.cpu().numpy(), K)
     f = float((inp.temperature > 0).float().mean())
-    row_us = B * V * 2 / (bench.NOMINAL_ROW_GBS * 1e3)
     masks = []
-    for cost in (0.7, bench.PHASE_BOUNDARY_US / row_us):
+    for cost in (0.7, sv.spec_verify_phase_cost(B, K, V, sv.SPEC_BF16)):
         mask = sv.spec_verify_plan_phases(K, surv, f, cost)
         say("  survival", [round(s, 3) for s in surv], "cost", round(cost, 3), "plan", bin(mask))
         assert mask != 0
