@@ -12,18 +12,27 @@ HBM; each timed step uses a new Philox step counter.
 
 By default the verification reads its rows in early-exit phases (rows of a
 phase only for requests whose earlier drafts were all accepted), cut by the
-library's planner from the acceptance curve of 8 untimed one-pass steps; the
+library's planner from the acceptance curve of 8 untimed one-pass steps with
+the phase boundary priced for the batch shape (spec_verify_phase_cost); the
 outputs are identical to one pass (--early-exit off).
 
 Prints one JSON line: verified draft positions per second (B*K per step,
-wall clock over the timed steps), the roofline of the dominant stage (the row
+wall clock over the timed steps); the roofline of the dominant stage (the row
 statistics of verification: its row-pass kernels and, with phases, the
 decisions between them), timed with HIP events on the launch stream on every
---event-every-th timed step against the logit bytes those steps read, and the
-CPU oracle timed on the host's cores over whole steps of the same batch (and
-on one core).  Two side measurements, outside the timed steps: draft-token
-sampling at the step's new-token indices (draft_sampling) and one GPU's share
-of a 4-way vocab-sharded verification of the same batch (shard_share_tp4).
+--event-every-th timed step (at least 10 of them), against the logit bytes
+those steps read under the plan, against the method's sequential minimum,
+and -- for the row pass as one launch over every row -- against the
+algorithmic bytes of the parallel formulation; and the CPU oracle timed on
+the host's cores over whole steps of the same batch (and on one core).
+
+Side measurements, outside the timed steps (each timed with HIP events):
+draft-token sampling at the step's new-token indices (draft_sampling), one
+GPU's share of a 4-way vocab-sharded verification of the same batch
+(shard_share_tp4), and the other workloads (configs): the GPT-OSS vocabulary
+batch (B=64, K=5, V=201088) and the expansion alone (B=512, K=8, H=2880),
+each rotating over input copies that together exceed the 256 MB Infinity
+Cache, and the large batch (B=1024, K=8, V=201088, acceptance ~0.8).
 """
 import argparse
 import json
@@ -44,9 +53,10 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--event-every", type=int, default=8,
+    ap.add_argument("--event-every", type=int, default=None,
                     help="record the HIP events that time the stages on every N-th timed step only (each event "
-                         "record costs GPU time of its own; 1 = every step)")
+                         "record costs GPU time of its own; 1 = every step); default: at most 8, and at least "
+                         "10 timed steps with events")
     ap.add_argument("--separate-expand", action="store_true",
                     help="enqueue the expansion as its own call after the verification instead of the chained "
                          "call that runs it inside the verification's sampling stage")
@@ -65,6 +75,10 @@ def parse():
     ap.add_argument("--phase-starts", type=int, default=None,
                     help="with --early-exit plan: use this phase mask (bit k starts a phase at draft position k) "
                          "instead of the one planned from the acceptance curve")
+    ap.add_argument("--only", choices=("all", "headline", "gptoss", "expand", "large"), default="all",
+                    help="run only the headline step, or only one of the side workloads (for profiling runs)")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the side workloads (GPT-OSS vocabulary batch, expansion alone, large batch)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the timed steps, copy 1 GiB device to device once (a plain copy kernel of known "
                          "size, to scale hardware byte counters)")
@@ -185,15 +199,7 @@ def sequential_logit_bytes(acc, temps, K, V, es):
     return rows * V * es
 
 
-# Planner inputs: one extra phase costs its decision kernel, two launch gaps and
-# the ramp-up and tail of one more row-pass kernel. Fitted to the row stages of
-# forced cuts at the headline batch (one, two and three phases), that is
-# 11-12.6 us per boundary beyond the bytes the phase saves at the nominal rate;
-# it is priced against the time to stream one row of every request at a nominal
-# 6.8 TB/s (the row pass's measured one-pass rate), so that the plan depends
-# only on the acceptance curve, not on timing noise.
-PHASE_BOUNDARY_US = 12.0
-NOMINAL_ROW_GBS = 6800.0
+NOMINAL_ROW_GBS = 6800.0  # the row pass's one-pass streaming rate (the planner's price unit)
 PLAN_STEPS = 8  # one-pass steps whose accepted counts give the survival curve
 
 
@@ -227,18 +233,189 @@ def rowpass_source_hash():
 
 def measured_traffic(phase_starts):
     """HBM bytes per step of the row-statistics stage under this phase plan,
-    from the committed counter summary, or None when there is none for the plan
-    or the row-pass sources changed since those counters were taken."""
+    from the committed counter summary, with the provenance: (bytes or None,
+    {"summary", "source_sha256", "matches_sources"}).  The bytes are None when
+    the summary holds none for the plan or the row-pass sources changed since
+    those counters were taken."""
     import re
+    src = rowpass_source_hash()
+    prov = {"summary": os.path.relpath(TRAFFIC_SUMMARY, ROOT), "source_sha256": src, "matches_sources": False}
     try:
         text = open(TRAFFIC_SUMMARY).read()
     except OSError:
-        return None
-    src = rowpass_source_hash()
+        return None, prov
     for m in re.finditer(r"traffic_bytes_per_step: (\d+) phase_starts: (\d+) source_sha256: ([0-9a-f]+)", text):
         if int(m.group(2)) == phase_starts and m.group(3) == src:
-            return int(m.group(1))
-    return None
+            prov["matches_sources"] = True
+            return int(m.group(1)), prov
+    return None, prov
+
+
+def event_steps(torch, stream, launch, n):
+    """Run launch(i, (start, stage_end, end) or None) for i < n twice: once
+    with only an event pair around the whole loop (the step time), then with
+    an event triple around every step (the stage times: row statistics, and
+    the rest).  Returns (ms per step, [stage ms], [rest ms])."""
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record(stream)
+    for i in range(n):
+        launch(i, None)
+    b.record(stream)
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n)]
+    for e3 in ev:  # create the underlying HIP events before the loop
+        for e in e3:
+            e.record(stream)
+    torch.cuda.synchronize()
+    for i in range(n):
+        launch(i, ev[i])
+    torch.cuda.synchronize()
+    return (a.elapsed_time(b) / n, [e[0].elapsed_time(e[1]) for e in ev], [e[1].elapsed_time(e[2]) for e in ev])
+
+
+def verify_config(sv, torch, np, name, copies, steps=20, seed=0):
+    """One verification per step of a side workload through spec_verify_launch,
+    rotating over `copies` (VerifyInputs with the same values in different
+    buffers, so that a step's rows are not left in the Infinity Cache by the
+    step before), rows read in the phases the planner picks for this shape
+    from 8 one-pass steps; the one-pass timing beside it."""
+    inp = copies[0]
+    B, K, V = inp.B, inp.K, inp.V
+    es = inp.bytes_per_logit()
+    dev = inp.target.device
+    temps = inp.temperature.cpu().numpy()
+    acc = torch.empty(B, dtype=torch.int32, device=dev)
+    tok = torch.empty(B, K + 1, dtype=torch.int32, device=dev)
+    ws = sv.make_workspace(B, K, V, dev)
+    stream = torch.cuda.current_stream()
+    args = [sv.verify_args(c.target, c.draft, c.draft_tokens, c.temperature, acc, tok, None, ws, seed=seed)
+            for c in copies]
+    mask = {"m": 0}
+
+    def launch(i, ev):
+        a = args[i % len(args)]
+        a.step = i & 0xFFFFFFFF
+        a.phase_starts = mask["m"]
+        a.phase_event = ev[1].cuda_event if ev else None
+        if ev:
+            ev[0].record(stream)
+        rc = sv.spec_verify_launch(a, stream.cuda_stream)
+        if rc != sv.SPEC_OK:
+            raise sv.SpecError(rc)
+        if ev:
+            ev[2].record(stream)
+
+    accs = []
+    for i in range(PLAN_STEPS):
+        launch(5_000_000 + i, None)
+        torch.cuda.synchronize()
+        accs.extend(acc.cpu().tolist())
+    surv = sv.survival_from_accepted(accs, K)
+    frac_sampled = float((temps > 0).mean())
+    cost = sv.spec_verify_phase_cost(B, K, V, sv.SPEC_BF16 if es == 2 else sv.SPEC_F32)
+    planned = sv.spec_verify_plan_phases(K, surv, frac_sampled, cost)
+    out = {"workload": name, "B": B, "K": K, "V": V, "dtype": "bf16" if es == 2 else "f32",
+           "input_copies": len(copies), "steps": steps}
+    res = {}
+    for m in sorted({0, planned}):
+        mask["m"] = m
+        for i in range(3):
+            launch(6_000_000 + i, None)
+        ms, k1, k2 = event_steps(torch, stream, launch, steps)
+        read = []
+        seq = []
+        for i in range(steps):  # outputs depend only on (seed, step): the rows each timed step read
+            launch(i, None)
+            a_np = acc.cpu().numpy()
+            read.append(phased_logit_bytes(a_np, temps, m, K, V, es))
+            seq.append(sequential_logit_bytes(a_np, temps, K, V, es))
+        stage = float(np.mean(k1))
+        res[m] = {"ms_per_step": ms, "row_stage_ms": stage, "row_stage_p10_p90": [float(np.percentile(k1, 10)),
+                                                                                   float(np.percentile(k1, 90))],
+                  "sampling_stage_ms": float(np.mean(k2)), "read_bytes": float(np.mean(read)),
+                  "seq_bytes": float(np.mean(seq)), "mean_accepted": float(acc.float().mean())}
+    alg = one_pass_logit_bytes(B, K, V, es, temps)
+    p = res[planned]
+    out.update({
+        "plan": {"phase_starts": planned, "phases": [0] + [k for k in range(1, K + 1) if (planned >> k) & 1],
+                 "survival": [round(v, 4) for v in surv], "phase_cost_rows": round(cost, 4)},
+        "ms_per_step": p["ms_per_step"], "positions_per_s": B * K / (p["ms_per_step"] * 1e-3),
+        "row_stage_ms": p["row_stage_ms"], "row_stage_p10_p90": p["row_stage_p10_p90"],
+        "algorithmic_bytes": alg, "plan_read_bytes": p["read_bytes"], "sequential_min_bytes": p["seq_bytes"],
+        "frac": p["read_bytes"] / (p["row_stage_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "frac_seq_min": p["seq_bytes"] / (p["row_stage_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "one_pass": {"ms_per_step": res[0]["ms_per_step"], "row_stage_ms": res[0]["row_stage_ms"],
+                     "frac": alg / (res[0]["row_stage_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS},
+        "plan_is_fastest": p["ms_per_step"] <= min(r["ms_per_step"] for r in res.values()),
+        "mean_accepted": p["mean_accepted"]})
+    return out
+
+
+def expand_config(sv, torch, B=512, K=8, H=2880, copies=8, steps=48, seed=0):
+    """spec_expand_launch alone on the expansion workload (B=512, K=8,
+    H=2880, accepted counts uniform in 0..K), rotating over `copies` input and
+    output buffers (~74 MB per copy); bytes: hidden rows read and written
+    once, the mask row, metadata in and out."""
+    import workloads
+    dev = torch.device("cuda")
+    e = workloads.expand_inputs(B=B, K=K, H=H, seed=seed, device=dev)
+    stream = torch.cuda.current_stream()
+    args = []
+    keep = []
+    for c in range(copies):
+        th = e.target_hidden.clone()
+        out = sv.expand_outputs(B, K, e.N_in, H, dev)
+        keep.append((th, out))
+        args.append(sv.expand_args(e.in_token_ids, e.in_positions, e.in_start, e.accepted, e.bonus, K, e.mask_id,
+                                   th, e.mask_hidden, out))
+
+    def launch(i, ev):
+        if ev:
+            ev[0].record(stream)
+        rc = sv.spec_expand_launch(args[i % copies], stream.cuda_stream)
+        if rc != sv.SPEC_OK:
+            raise sv.SpecError(rc)
+        if ev:
+            ev[1].record(stream)
+            ev[2].record(stream)
+
+    for i in range(copies):
+        launch(i, None)
+    ms, k1, _ = event_steps(torch, stream, launch, steps)
+    nbytes = algorithmic_expand_bytes(B, K, H, e.N_in) - (e.N_in + B * (K - 1)) * 12  # no slot mapping here
+    each = float(sum(k1) / len(k1))
+    return {"workload": "P-EAGLE expansion alone: B=%d, K=%d, H=%d bf16, accepted uniform in 0..K" % (B, K, H),
+            "input_copies": copies, "launches": steps, "ms_per_launch": ms, "ms_per_launch_events": each,
+            "algorithmic_bytes": nbytes, "GBps": nbytes / (ms * 1e-3) / 1e9,
+            "frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+
+
+def side_configs(sv, torch, np, only, seed):
+    import workloads
+    dev = torch.device("cuda")
+    out = {}
+    if only in ("all", "gptoss"):
+        base = workloads.verify_gptoss(seed=seed, device=dev)
+        copies = [base] + [workloads.VerifyInputs(base.name, base.target.clone(), base.draft.clone(),
+                                                  base.draft_tokens.clone(), base.temperature.clone(), seed)
+                           for _ in range(3)]
+        out["gptoss_vocab"] = verify_config(sv, torch, np, "GPT-OSS vocabulary: B=64, K=5, V=201088 bf16, Zipf "
+                                            "target, draft = target + N(0, 0.7), T = 1", copies, seed=seed)
+        del base, copies
+    if only in ("all", "expand"):
+        out["expand"] = expand_config(sv, torch, seed=seed)
+    if only in ("all", "large"):
+        beta = 0.8
+        lam = (1.0 - beta) / workloads.total_variation_noise(workloads.GPT_OSS_VOCAB, rows=16, seed=7, device=dev)
+        inp = workloads.verify_beta_sweep(lam, seed=8, device=dev)
+        r = verify_config(sv, torch, np, "large batch: B=1024, K=8, V=201088 bf16, T = 1, mixture drafts, "
+                          "lam = %.4f for acceptance ~%.1f" % (lam, beta), [inp], steps=12, seed=seed)
+        r["acceptance_target"] = beta
+        out["large_batch"] = r
+        del inp
+    torch.cuda.empty_cache()
+    return out
 
 
 def cpu_baseline(inp, seed, cpu_seconds):
@@ -283,47 +460,28 @@ def cpu_baseline(inp, seed, cpu_seconds):
                             "sample": "requests 0..%d of step 0 of the same batch" % (one_req - 1)}}
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print("bench.py measures one GPU: the library has no multi-GPU path (request sharding is "
-              "described in the design notes); run with --gpus 1", file=sys.stderr)
-        sys.exit(2)
-    import numpy as np
-    import torch
-
-    import rejection_sampling_verify_03_amd as sv
-    import workloads
-
+def headline(args, sv, torch, np, workloads):
+    """The timed steps of the headline workload; returns the JSON fields and
+    what the side measurements reuse (inputs, expansion outputs)."""
     dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
     inp = workloads.verify_headline(seed=args.seed, device=dev)
     B, K, V = inp.B, inp.K, inp.V
     H = workloads.HIDDEN_GPT_OSS_20B
-    # the verify batch feeding the expansion: per request [last token, x_0..x_{K-1}]
-    g = torch.Generator(device=dev).manual_seed(args.seed + 1)
-    last = torch.randint(0, V, (B, 1), generator=g, device=dev, dtype=torch.int32)
-    in_ids = torch.cat([last, inp.draft_tokens], dim=1).reshape(-1).contiguous()
-    off = torch.randint(0, 16384, (B, 1), generator=g, device=dev, dtype=torch.int64)
-    in_pos = (off + torch.arange(K + 1, device=dev)).reshape(-1).contiguous()
-    in_start = (torch.arange(B + 1, device=dev, dtype=torch.int32) * (K + 1)).contiguous()
-    hidden = torch.randn(B * (K + 1), H, generator=g, device=dev).to(torch.bfloat16)
-    mask_hidden = torch.randn(H, generator=g, device=dev).to(torch.bfloat16)
-    mask_id = workloads.GPT_OSS_VOCAB
-
+    # the verify batch feeding the expansion: per request [last token, x_0..x_{K-1}], and a paged
+    # KV cache of 16-slot blocks covering every position of the batch
+    ex = workloads.step_expand_inputs(inp, H=H, seed=args.seed)
     accepted = torch.empty(B, dtype=torch.int32, device=dev)
     tokens = torch.empty(B, K + 1, dtype=torch.int32, device=dev)
     ws = sv.make_workspace(B, K, V, dev)
-    out = sv.expand_outputs(B, K, B * (K + 1), H, dev, with_slots=True)
-    # paged KV cache of 16-slot blocks covering every position of the batch
-    block_size = 16
-    block_table = workloads.block_tables(B, (16384 + 2 * K + 2) // block_size + 1, seed=args.seed + 2, device=dev)
+    out = sv.expand_outputs(B, K, ex.N_in, H, dev, with_slots=True)
     stream = torch.cuda.current_stream()
     sptr = stream.cuda_stream
-    ex_args = sv.expand_args(in_ids, in_pos, in_start, accepted, None, K, mask_id, hidden, mask_hidden, out,
-                             verify_tokens=tokens, block_table=block_table, block_size=block_size)
+    ex_args = sv.expand_args(ex.in_token_ids, ex.in_positions, ex.in_start, accepted, None, K, ex.mask_id,
+                             ex.target_hidden, ex.mask_hidden, out, verify_tokens=tokens,
+                             block_table=ex.block_table, block_size=ex.block_size)
 
-    every = max(1, args.event_every)
+    # events on every `every`-th timed step: at least 10 of them (each event record costs GPU time of its own)
+    every = args.event_every if args.event_every else max(1, min(8, args.steps // 10))
     timed_with_events = [i for i in range(args.steps) if i % every == 0]
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in timed_with_events]
     for e4 in ev:  # create the underlying HIP events
@@ -341,8 +499,9 @@ def main():
     chained = not (args.overlap or args.separate_expand)
     side = torch.cuda.Stream()
     meta_out = sv.ExpandOutputs(**{**out.__dict__, "out_hidden": None})
-    meta_args = sv.expand_args(in_ids, in_pos, in_start, accepted, None, K, mask_id, hidden, mask_hidden, meta_out,
-                               verify_tokens=tokens, block_table=block_table, block_size=block_size)
+    meta_args = sv.expand_args(ex.in_token_ids, ex.in_positions, ex.in_start, accepted, None, K, ex.mask_id,
+                               ex.target_hidden, ex.mask_hidden, meta_out, verify_tokens=tokens,
+                               block_table=ex.block_table, block_size=ex.block_size)
     untimed_phase = torch.cuda.Event()
     untimed_phase.record(stream)
 
@@ -365,7 +524,6 @@ def main():
                 raise sv.SpecError(rc)
             if events:
                 events[2].record(stream)
-                events[3].record(stream)
             return
         rc = sv.spec_verify_launch(va, sptr)
         if rc != sv.SPEC_OK:
@@ -389,20 +547,21 @@ def main():
     sampled_fraction = float((temps > 0).mean())
     if args.early_exit == "plan":
         # the accepted counts of a few one-pass steps give the acceptance curve and the phase plan
-        # follows from it, as a serving loop would plan from its recent steps
+        # follows from it, as a serving loop would plan from its recent steps; the boundary is priced
+        # for this batch shape
         accs = []
         for i in range(PLAN_STEPS):
             step(2_000_000 + i)
             torch.cuda.synchronize()
             accs.extend(accepted.cpu().tolist())
         surv = sv.survival_from_accepted(accs, K)
-        row_us = B * V * 2 / (NOMINAL_ROW_GBS * 1e3)
-        plan["mask"] = sv.spec_verify_plan_phases(K, surv, sampled_fraction, PHASE_BOUNDARY_US / row_us)
+        cost = sv.spec_verify_phase_cost(B, K, V, sv.SPEC_BF16)
+        plan["mask"] = sv.spec_verify_plan_phases(K, surv, sampled_fraction, cost)
         if args.phase_starts is not None:
             plan["planned_mask"] = plan["mask"]
             plan["mask"] = args.phase_starts
         plan["survival"] = [round(v, 4) for v in surv]
-        plan["phase_cost_rows"] = round(PHASE_BOUNDARY_US / row_us, 4)
+        plan["phase_cost_rows"] = round(cost, 4)
     for i in range(args.warmup):
         step(1_000_000 + i)
     torch.cuda.synchronize()
@@ -414,7 +573,7 @@ def main():
     ms_per_step = wall * 1e3 / args.steps
     k1 = np.array([e[0].elapsed_time(e[1]) for e in ev])
     k2 = np.array([e[1].elapsed_time(e[2]) for e in ev])
-    ke = np.array([e[2].elapsed_time(e[3]) for e in ev])
+    ke = None if chained else np.array([e[2].elapsed_time(e[3]) for e in ev])
 
     if args.copy_calibration:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -423,26 +582,26 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    # the row pass as one launch over every row (no early exit), timed the same way on a few more
-    # steps: the kernel's own streaming rate, beside the planned stage above
-    one_pass = None
-    if plan["mask"] != 0:
-        saved_mask = plan["mask"]
-        plan["mask"] = 0
-        for i in range(5):
-            step(3_000_000 + i)
-        ev1 = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(24)]
-        for e4 in ev1:  # create the underlying HIP events
-            for e in e4:
-                e.record(stream)
-        torch.cuda.synchronize()
-        for i, e4 in enumerate(ev1):
-            step(4_000_000 + i, e4)
-        torch.cuda.synchronize()
-        k1o = float(np.mean([e[0].elapsed_time(e[1]) for e in ev1]))
-        plan["mask"] = saved_mask
-        gbs = one_pass_logit_bytes(B, K, V, 2, temps) / (k1o * 1e-3) / 1e9
-        one_pass = {"ms": k1o, "achieved": gbs, "frac": gbs / HBM_PEAK_GBS, "steps": len(ev1)}
+    # the row pass as one launch over every row (no early exit), timed the same way on 24 more
+    # steps: the kernel's own streaming rate against the parallel formulation's bytes
+    alg_bytes = one_pass_logit_bytes(B, K, V, 2, temps)
+    saved_mask = plan["mask"]
+    plan["mask"] = 0
+    for i in range(5):
+        step(3_000_000 + i)
+    ev1 = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(24)]
+    for e4 in ev1:  # create the underlying HIP events
+        for e in e4:
+            e.record(stream)
+    torch.cuda.synchronize()
+    for i, e4 in enumerate(ev1):
+        step(4_000_000 + i, e4)
+    torch.cuda.synchronize()
+    k1o = np.array([e[0].elapsed_time(e[1]) for e in ev1])
+    plan["mask"] = saved_mask
+    gbs = alg_bytes / (float(k1o.mean()) * 1e-3) / 1e9
+    one_pass = {"ms": float(k1o.mean()), "ms_median": float(np.median(k1o)), "achieved": gbs,
+                "frac": gbs / HBM_PEAK_GBS, "algorithmic_bytes": alg_bytes, "steps": len(ev1)}
 
     # the timed steps again, untimed (outputs depend only on seed and step), for the rows each one read
     mask = plan["mask"]
@@ -454,12 +613,12 @@ def main():
     read_bytes = float(np.mean([phased_logit_bytes(acc_steps[i], temps, mask, K, V, 2) for i in timed_with_events]))
     seq_bytes = float(np.mean([sequential_logit_bytes(acc_steps[i], temps, K, V, 2) for i in timed_with_events]))
     vbytes = algorithmic_verify_bytes(B, K, V, 2, temps)
-    one_pass_bytes = vbytes - (B * K * 4 + B * 4 + B * 4 + B * (K + 1) * 4)
     ebytes = algorithmic_expand_bytes(B, K, H, B * (K + 1))
     k1_ms = float(k1.mean())
     achieved = read_bytes / (k1_ms * 1e-3) / 1e9
     acc_np = np.concatenate(acc_steps)
     positions_per_s = B * K / (ms_per_step * 1e-3)
+    traffic, traffic_src = measured_traffic(mask)
     line = {
         "metric": "verified draft positions/sec + achieved HBM GB/s at B=256,K=8,V=151936 bf16",
         "value": positions_per_s,
@@ -479,27 +638,57 @@ def main():
                    "expansion": ("chained call: hidden rows and metadata inside the verification's sampling stage"
                                  if chained else "hidden rows on a second stream, overlapping the sampling stage"
                                  if overlap else "its own kernel after the verification")},
-        "roofline": {"kernel": "verify_rowstats", "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": measured_traffic(mask),
-                     "algorithmic_bytes": read_bytes, "one_pass_bytes": one_pass_bytes,
-                     "sequential_min_bytes": seq_bytes, "one_pass_row_kernel": one_pass},
+        # the dominant stage as run: achieved and frac on the logit bytes the planned phases read;
+        # frac_seq_min on the method's sequential minimum (rows 0..a only); the one-pass row kernel
+        # against the parallel formulation's algorithmic bytes
+        "roofline": {"kernel": "verify_rowstats", "stage": "row statistics (row-pass launches and phase decisions)",
+                     "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "frac_seq_min": seq_bytes / (k1_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                     "traffic": traffic, "traffic_from_profiles": traffic_src,
+                     "plan_read_bytes": read_bytes, "algorithmic_bytes": alg_bytes,
+                     "sequential_min_bytes": seq_bytes, "stage_ms": k1_ms, "one_pass_row_kernel": one_pass},
         "early_exit": {"phase_starts": mask, "phases": [0] + [k for k in range(1, K + 1) if (mask >> k) & 1],
                        **{k: v for k, v in plan.items() if k != "mask"}},
-        "kernels_ms": {"timed_steps_with_events": len(timed_with_events), "verify_row_stage": k1_ms,
+        "kernels_ms": {"timed_steps_with_events": len(timed_with_events), "event_every": every,
+                       "verify_row_stage": k1_ms,
                        ("sampling_stage_with_expansion" if chained else "verify_decide_and_draw"): float(k2.mean()),
                        **({} if chained else {("expand_metadata_and_join" if overlap else "expand"): float(ke.mean())}),
                        "verify_row_stage_p10_p90": [float(np.percentile(k1, 10)), float(np.percentile(k1, 90))]},
         "verify_GBps_algorithmic": None if chained else
-        (read_bytes + vbytes - one_pass_bytes) / ((k1.mean() + k2.mean()) * 1e-3) / 1e9,
+        (read_bytes + vbytes - alg_bytes) / ((k1.mean() + k2.mean()) * 1e-3) / 1e9,
         "expand_GBps_algorithmic": None if (overlap or chained) else ebytes / (ke.mean() * 1e-3) / 1e9,
         "emitted_tokens_per_s": float((acc_np + 1).sum()) / args.steps / (ms_per_step * 1e-3),
         "mean_accepted": float(acc_np.mean()),
     }
+    return line, inp, out
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: the library has no multi-GPU path (request sharding is "
+              "described in the design notes); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import rejection_sampling_verify_03_amd as sv
+    import workloads
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    if args.only not in ("all", "headline"):
+        print(json.dumps({"only": args.only, "configs": side_configs(sv, torch, np, args.only, args.seed)}),
+              flush=True)
+        return
+    line, inp, out = headline(args, sv, torch, np, workloads)
+    B, K, V = inp.B, inp.K, inp.V
     if not args.no_draft_sampling:
         line["draft_sampling"] = draft_sampling(sv, torch, np, out, inp.temperature, B, K, V, args.seed, dev)
     if not args.no_shard_share:
         line["shard_share_tp4"] = shard_share(sv, torch, inp, args.seed)
+    if not args.no_configs and args.only == "all":
+        line["configs"] = side_configs(sv, torch, np, "all", args.seed)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(inp, args.seed, args.cpu_seconds)
     print(json.dumps(line), flush=True)
