@@ -165,6 +165,24 @@ size_t spec_verify_workspace_bytes(int32_t B, int32_t K, int32_t V);
  * accepted_counts = -1, output_tokens all -1 and debug_probs 0. */
 int spec_verify_launch(const spec_verify_args* args, hipStream_t stream);
 
+/* For callers that cannot allocate device memory -- code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation: the same
+ * verification as spec_verify_launch (same checks, kernels and outputs),
+ * with args->workspace and args->workspace_bytes ignored.  Its workspace is a
+ * SPEC_NOALLOC_SCRATCH_BYTES array of device memory inside the library, one
+ * per GPU, held from the first call on that GPU until the process ends; the
+ * call allocates nothing.  The stream must belong to the current device
+ * (else SPEC_EINVAL).  A shape whose spec_verify_workspace_bytes exceeds
+ * SPEC_NOALLOC_SCRATCH_BYTES returns SPEC_EWORKSPACE before anything is
+ * enqueued (8 MiB holds B = 1024, K = 8, V = 201088 nearly three times over).
+ * Every call on one GPU shares that GPU's array: calls that may overlap on
+ * that GPU (other streams, or graphs replayed concurrently) race and must be
+ * ordered by the caller.  Invalid requests are reported in the outputs
+ * (accepted_counts = -1); their count is not readable through
+ * spec_workspace_error. */
+#define SPEC_NOALLOC_SCRATCH_BYTES (8u << 20)
+int spec_verify_launch_noalloc(const spec_verify_args* args, hipStream_t stream);
+
 /* The data errors of the last verification enqueued on this workspace: waits
  * for `stream` (so it is not for graph capture or a tight loop), then returns
  * the number of requests that verification found invalid (the ones with

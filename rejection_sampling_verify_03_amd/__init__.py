@@ -20,9 +20,10 @@ SPEC_OK, SPEC_EINVAL, SPEC_EDTYPE, SPEC_EALIGN, SPEC_EWORKSPACE, SPEC_ELAUNCH = 
 SPEC_F32, SPEC_BF16 = 0, 1
 SPEC_MAX_K = 63
 SPEC_MAX_V = 2147418112  # 2^31 - 2^16
+SPEC_NOALLOC_SCRATCH_BYTES = 8 << 20
 
 EXPORTED = ("spec_verify_workspace_bytes", "spec_verify_plan_phases", "spec_verify_phase_cost",
-            "spec_verify_launch",
+            "spec_verify_launch", "spec_verify_launch_noalloc",
             "spec_expand_launch", "spec_expand_hidden_launch", "spec_verify_expand_launch",
             "spec_draft_workspace_bytes",
             "spec_draft_sample_launch", "spec_shard_workspace_bytes", "spec_shard_stats_launch",
@@ -106,6 +107,8 @@ def _load():
     L.spec_verify_phase_cost.restype = ctypes.c_double
     L.spec_verify_launch.argtypes = [ctypes.POINTER(SpecVerifyArgs), ctypes.c_void_p]
     L.spec_verify_launch.restype = ctypes.c_int
+    L.spec_verify_launch_noalloc.argtypes = [ctypes.POINTER(SpecVerifyArgs), ctypes.c_void_p]
+    L.spec_verify_launch_noalloc.restype = ctypes.c_int
     L.spec_workspace_error.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
     L.spec_workspace_error.restype = ctypes.c_int
     L.spec_expand_launch.argtypes = [ctypes.POINTER(SpecExpandArgs), ctypes.c_void_p]
@@ -173,6 +176,12 @@ def survival_from_accepted(accepted, K):
 def spec_verify_launch(args, stream_ptr):
     """args: a SpecVerifyArgs; stream_ptr: hipStream_t as an int (0 = null stream)."""
     return int(lib.spec_verify_launch(ctypes.byref(args), stream_ptr))
+
+
+def spec_verify_launch_noalloc(args, stream_ptr):
+    """The same verification with the library's own per-GPU scratch array as
+    its workspace (args.workspace ignored); allocates nothing."""
+    return int(lib.spec_verify_launch_noalloc(ctypes.byref(args), stream_ptr))
 
 
 def spec_workspace_error(workspace, stream_ptr=0):
@@ -310,8 +319,9 @@ def verify_args(target, draft, draft_tokens, temperature, accepted, tokens, debu
     a.accepted_counts = accepted.data_ptr()
     a.output_tokens = tokens.data_ptr()
     a.debug_probs = debug.data_ptr() if debug is not None else None
-    a.workspace = workspace.data_ptr()
-    a.workspace_bytes = workspace.numel() * workspace.element_size()
+    # workspace None: for spec_verify_launch_noalloc, which brings its own
+    a.workspace = workspace.data_ptr() if workspace is not None else None
+    a.workspace_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     a.phase_event = phase_event
     a.phase_starts = int(phase_starts)
     if num_drafts is not None:

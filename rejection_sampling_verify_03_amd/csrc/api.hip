@@ -4,17 +4,50 @@
 // query spec_workspace_error waits for the stream it is given).
 #include <stdint.h>
 
+#include <mutex>
+
 #include "spec_verify.h"
 #include "verify_kernels.hpp"
 #include "verify_layout.hpp"
 
 using namespace specv;
 
+// The workspace of spec_verify_launch_noalloc: one copy of this array per GPU
+// the library runs on, held until the process ends.  Host code never passes
+// its name to a kernel (on the host it is only a stand-in for the symbol): it
+// uses the device address hipGetSymbolAddress gives for the current device.
+static __device__ __align__(256) unsigned char scratch[SPEC_NOALLOC_SCRATCH_BYTES];
+
 namespace {
 
 constexpr int64_t kExpandRowsPerWG = 4;
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Device address of `scratch` per device, looked up on the first call made
+// with that device current (a lookup, not an allocation).
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices] = {};
+
+int scratch_address(hipStream_t stream, void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return SPEC_ELAUNCH;
+  if (stream != nullptr) {  // the lookup is for the current device: the stream must be on it
+    hipDevice_t sdev = -1;
+    if (hipStreamGetDevice(stream, &sdev) != hipSuccess) return SPEC_ELAUNCH;
+    if (sdev != dev) return SPEC_EINVAL;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch[dev] == nullptr) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress((void**)&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr)
+      return SPEC_ELAUNCH;
+    g_scratch[dev] = ptr;
+  }
+  *out = g_scratch[dev];
+  return SPEC_OK;
+}
 
 int verify_check(const spec_verify_args* a) {
   if (!a) return SPEC_EINVAL;
@@ -303,6 +336,26 @@ int spec_verify_launch(const spec_verify_args* a, hipStream_t stream) {
   bool vec;
   const VerifyParams P = verify_params(a, vec);
   return verify_enqueue(P, a, vec, stream);
+}
+
+int spec_verify_launch_noalloc(const spec_verify_args* a, hipStream_t stream) {
+  if (!a) return SPEC_EINVAL;
+  if (a->B < 0 || a->K < 1 || a->K > SPEC_MAX_K || a->V < 1 || a->V > SPEC_MAX_V) return SPEC_EINVAL;
+  if (a->B == 0) return verify_check(a);  // nothing to enqueue (a bad dtype is still reported)
+  if (make_layout(a->B, a->K, a->V).total > (size_t)SPEC_NOALLOC_SCRATCH_BYTES) return SPEC_EWORKSPACE;
+  void* ws = nullptr;
+  const int rs = scratch_address(stream, &ws);
+  if (rs != SPEC_OK) return rs;
+  // the same checks and kernels as spec_verify_launch, with this device's
+  // scratch array as the workspace
+  spec_verify_args b = *a;
+  b.workspace = ws;
+  b.workspace_bytes = SPEC_NOALLOC_SCRATCH_BYTES;
+  const int rc = verify_check(&b);
+  if (rc != SPEC_OK) return rc;
+  bool vec;
+  const VerifyParams P = verify_params(&b, vec);
+  return verify_enqueue(P, &b, vec, stream);
 }
 
 // The kernel parameters of a checked expansion (B >= 1), G workgroups per

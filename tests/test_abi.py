@@ -297,3 +297,19 @@ def test_shard_argument_errors(sv):
     assert sv.spec_shard_workspace_bytes(2, 3, 50) == 256 + 256
     assert sv.spec_shard_workspace_bytes(1, 1, sv.SPEC_MAX_V + 1) == 0
     assert sv.spec_shard_workspace_bytes(256, 8, 37984) == 256 * 64 + 256 * 10 * 16
+
+
+def test_noalloc_argument_errors(sv):
+    """The allocation-free entry point refuses bad shapes, and shapes whose
+    workspace exceeds its scratch array, on the host before anything runs."""
+    assert sv.lib.spec_verify_launch_noalloc(None, None) == sv.SPEC_EINVAL
+    a = sv.SpecVerifyArgs()
+    a.B, a.K, a.V, a.dtype = 4, 0, 100, sv.SPEC_BF16
+    assert sv.spec_verify_launch_noalloc(a, 0) == sv.SPEC_EINVAL
+    a.K = 8
+    a.B, a.V = 4096, 201088
+    assert sv.spec_verify_workspace_bytes(4096, 8, 201088) > sv.SPEC_NOALLOC_SCRATCH_BYTES
+    assert sv.spec_verify_launch_noalloc(a, 0) == sv.SPEC_EWORKSPACE
+    a.B = 0
+    a.dtype = 7
+    assert sv.spec_verify_launch_noalloc(a, 0) == sv.SPEC_EDTYPE
