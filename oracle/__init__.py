@@ -14,8 +14,8 @@ Pinning status of each function (what fixes it other than itself):
     disjoint supports, one-hot targets, greedy argmax ties, V=1, K=1).
   * ``expand``: the invariants the P-EAGLE page fixes (mask partition,
     injective mapping, counts, positions, start indices), a hand-worked
-    fixture, and the page's own two hidden-state statements run in torch on the
-    CPU.  The order of slots inside a request's window is a reading of the page
+    fixture, and the hidden-state fill written out row by row from the page's
+    description.  The order of slots inside a request's window is a reading of the page
     and is pinned only by those invariants and the hand-worked fixture.
 """
 import ctypes
@@ -24,7 +24,9 @@ import os
 import numpy as np
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-_LIB_PATH = os.path.join(HERE, "libspecoracle.so")
+# SPEC_ORACLE_LIB names another build of the same sources (e.g. one with
+# sanitizers, see build.py); default: the in-tree build
+_LIB_PATH = os.environ.get("SPEC_ORACLE_LIB") or os.path.join(HERE, "libspecoracle.so")
 _lib = None
 
 F32, BF16 = 0, 1

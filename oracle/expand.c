@@ -14,9 +14,9 @@
  *    target, fills the extra slots with the MASK id, and emits the
  *    rejected-token mask, the masked-token mask, the new-token indices used to
  *    sample draft tokens, and the hidden-state mapping.
- *  - "Hidden State 管理": the hidden rows are filled by two statements,
- *    hidden[mapping] = target_hidden, then the masked rows take the learned
- *    placeholder; valid tokens get their normal KV-cache slot and rejected
+ *  - "Hidden State 管理": the hidden rows are filled in two steps, the
+ *    target rows scattered to their mapped slots, then the masked rows take
+ *    the learned placeholder; valid tokens get their normal KV-cache slot and rejected
  *    tokens the padding slot -1, so that no cache entry is written for them.
  *  - "核心方法" step 2: the drafter input at a position pairs the token of the
  *    next position with the hidden state of this one (inputs shifted by one).
