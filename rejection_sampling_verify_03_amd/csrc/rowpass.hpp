@@ -25,7 +25,10 @@ __device__ __forceinline__ void raise_ref(float& M, double& S, float gm, float s
 // 16-byte loads per lane in flight before any is used).  One loop body serves
 // every batch: groups past the chunk (in its last batch) load the lane's
 // first group again and are left out of the reduction, so a short last batch
-// still issues its loads together and the loop keeps one register set.  The
+// still issues its loads together and the loop keeps one register set; the
+// arithmetic of groups that no lane of the wave needs is skipped (a
+// wave-uniform branch), which in a pass bound by its own arithmetic as much
+// as by memory is what a short last batch costs.  The
 // (< 8) trailing logits of a row whose length is not a multiple of 8 go to
 // thread 0.
 template <int ES>
@@ -39,6 +42,10 @@ __device__ __forceinline__ MS chunk_stats(const char* __restrict__ row, int e0, 
   float M = -INFINITY;
   double S = 0.0;
   for (int g = threadIdx.x; g < nfull; g += kWG * U) {
+    // groups u < nu are needed by some lane of the wave (its first active lane
+    // holds the lowest group): the rest are skipped with a wave-uniform branch
+    const int g0 = __builtin_amdgcn_readfirstlane(g);
+    const int nu = (nfull - g0 + kWG - 1) / kWG;
     float x[U][8];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -48,18 +55,22 @@ __device__ __forceinline__ MS chunk_stats(const char* __restrict__ row, int e0, 
     float gm = -INFINITY;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      float m = x[u][0];
+      if (u < nu) {
+        float m = x[u][0];
 #pragma unroll
-      for (int i = 1; i < 8; ++i) m = fmaxf(m, x[u][i]);
-      if (g + u * kWG < nfull) gm = fmaxf(gm, m);
+        for (int i = 1; i < 8; ++i) m = fmaxf(m, x[u][i]);
+        if (g + u * kWG < nfull) gm = fmaxf(gm, m);
+      }
     }
     raise_ref(M, S, gm, s_hi);
     const float negM = -fmaxf(M, -1e30f);
     float acc = 0.f;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const float e = sum8_exp(x[u], s_hi, s_lo, negM);
-      acc += g + u * kWG < nfull ? e : 0.f;
+      if (u < nu) {
+        const float e = sum8_exp(x[u], s_hi, s_lo, negM);
+        acc += g + u * kWG < nfull ? e : 0.f;
+      }
     }
     S += (double)acc;
   }
