@@ -385,10 +385,30 @@ def expand_config(sv, torch, B=512, K=8, H=2880, copies=8, steps=48, seed=0):
     ms, k1, _ = event_steps(torch, stream, launch, steps)
     nbytes = algorithmic_expand_bytes(B, K, H, e.N_in) - (e.N_in + B * (K - 1)) * 12  # no slot mapping here
     each = float(sum(k1) / len(k1))
+
+    # the practical ceiling of this copy-shaped traffic: a plain device-to-device copy of the output's
+    # hidden bytes (torch's copy kernel, the same rotation), timed the same way
+    def copy(i, ev):
+        if ev:
+            ev[0].record(stream)
+        keep[i % copies][1].out_hidden.copy_(keep[(i + 1) % copies][1].out_hidden)
+        if ev:
+            ev[1].record(stream)
+            ev[2].record(stream)
+
+    for i in range(copies):
+        copy(i, None)
+    cms, _, _ = event_steps(torch, stream, copy, steps)
+    cbytes = 2 * keep[0][1].out_hidden.numel() * 2
     return {"workload": "P-EAGLE expansion alone: B=%d, K=%d, H=%d bf16, accepted uniform in 0..K" % (B, K, H),
             "input_copies": copies, "launches": steps, "ms_per_launch": ms, "ms_per_launch_events": each,
             "algorithmic_bytes": nbytes, "GBps": nbytes / (ms * 1e-3) / 1e9,
-            "frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+            "frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "write_GBps": (e.N_in + B * (K - 1)) * H * 2 / (ms * 1e-3) / 1e9,
+            "device_copy": {"what": "torch copy_ of the [%d, %d] bf16 output hidden rows (read and write once)"
+                                    % tuple(keep[0][1].out_hidden.shape), "ms": cms, "bytes": cbytes,
+                            "GBps": cbytes / (cms * 1e-3) / 1e9,
+                            "write_GBps": cbytes / 2 / (cms * 1e-3) / 1e9}}
 
 
 def side_configs(sv, torch, np, only, seed):
@@ -458,6 +478,16 @@ def cpu_baseline(inp, seed, cpu_seconds):
                       % (steps, B, K, tl.shape[-1], used),
             "single_core": {"value": one_req * K / one_wall, "unit": "positions/s", "cores": 1,
                             "sample": "requests 0..%d of step 0 of the same batch" % (one_req - 1)}}
+
+
+def copy_calibration(torch, dev):
+    """One 1 GiB device-to-device copy (a plain copy kernel of known size, to
+    scale hardware byte counters)."""
+    src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
 
 
 def headline(args, sv, torch, np, workloads):
@@ -576,11 +606,7 @@ def headline(args, sv, torch, np, workloads):
     ke = None if chained else np.array([e[2].elapsed_time(e[3]) for e in ev])
 
     if args.copy_calibration:
-        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
-        dst = torch.empty_like(src)
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
+        copy_calibration(torch, dev)
 
     # the row pass as one launch over every row (no early exit), timed the same way on 24 more
     # steps: the kernel's own streaming rate against the parallel formulation's bytes
@@ -678,8 +704,10 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     if args.only not in ("all", "headline"):
-        print(json.dumps({"only": args.only, "configs": side_configs(sv, torch, np, args.only, args.seed)}),
-              flush=True)
+        configs = side_configs(sv, torch, np, args.only, args.seed)
+        if args.copy_calibration:
+            copy_calibration(torch, dev)
+        print(json.dumps({"only": args.only, "configs": configs}), flush=True)
         return
     line, inp, out = headline(args, sv, torch, np, workloads)
     B, K, V = inp.B, inp.K, inp.V
