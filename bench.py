@@ -149,18 +149,22 @@ def draft_sampling(sv, torch, np, out, temperature, B, K, V, seed, dev, reps=50)
             "GBps": nbytes / (ms * 1e-3) / 1e9, "frac_of_hbm_peak": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
 
 
-def shard_share(sv, torch, inp, seed, G=4, reps=50):
+def shard_share(sv, torch, inp, seed, G=4, reps=50, phase_starts=0):
     """One GPU's share of a tensor-parallel verification of the headline batch
-    over G vocabulary shards: shard 0's three stages (statistics over its
-    slice, decisions from every shard's records, draw) on its slice, held as
-    a contiguous tensor as a tensor-parallel GPU would hold it, timed
-    with HIP events after one run of every shard has filled the exchanged
-    records and masses (the same step each rep, so the work is the same).
-    Bytes: the slice of every target row 0..K and of the draft rows 0..K-1 of
-    sampled requests, once."""
+    over G vocabulary shards: shard 0's stages (statistics over its slice --
+    per early-exit phase, with the phase's accept tests between phases --,
+    decisions from every shard's records, draw) on its slice, held as a
+    contiguous tensor as a tensor-parallel GPU would hold it, timed with HIP
+    events after one run of every shard has filled the exchanged records and
+    masses (the same step each rep, so the work is the same).  Bytes: the
+    slice of every row the plan reads, once."""
+    import numpy as np
     B, K, V = inp.B, inp.K, inp.V
-    st = sv.shard_setup(inp.target, inp.draft, inp.draft_tokens, inp.temperature, G, seed=seed, step=0)
+    st = sv.shard_setup(inp.target, inp.draft, inp.draft_tokens, inp.temperature, G, seed=seed, step=0,
+                        phase_starts=phase_starts)
     st.run()
+    torch.cuda.synchronize()
+    acc = st.acc[0].cpu().numpy()
     stream = torch.cuda.current_stream()
     # a tensor-parallel GPU holds its slice as a tensor of its own: shard 0
     # reads contiguous copies [B, K+1, Vs] (the same values as the view)
@@ -169,10 +173,11 @@ def shard_share(sv, torch, inp, seed, G=4, reps=50):
     d0 = inp.draft[..., a0.v0:a0.v0 + a0.Vs].contiguous()
     a0.target_logits, a0.t_req_stride, a0.t_row_stride = t0.data_ptr(), t0.stride(0), t0.stride(1)
     a0.draft_logits, a0.d_req_stride, a0.d_row_stride = d0.data_ptr(), d0.stride(0), d0.stride(1)
+    sched = st.schedule()
 
     def share():
-        for stage in range(3):
-            st.launch(stage, 0)
+        for stage, p in sched:
+            st.launch(stage, 0, p)
 
     for _ in range(5):
         share()
@@ -184,12 +189,15 @@ def shard_share(sv, torch, inp, seed, G=4, reps=50):
     e1.record(stream)
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / reps
-    Vs = st.shards[0][0].Vs
-    nbytes = one_pass_logit_bytes(B, K, Vs, 2, inp.temperature.cpu().numpy())
+    Vs = a0.Vs
+    temps = inp.temperature.cpu().numpy()
+    nbytes = phased_logit_bytes(acc, temps, phase_starts, K, Vs, 2)
     del t0, d0
-    return {"workload": "shard 0 of %d: its slice [%d, %d, %d] bf16 of the headline batch, contiguous" % (G, B, K + 1, Vs),
-            "ms": ms, "positions_per_s": B * K / (ms * 1e-3), "bytes": nbytes,
-            "GBps": nbytes / (ms * 1e-3) / 1e9, "frac_of_hbm_peak": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+    return {"workload": "shard 0 of %d: its slice [%d, %d, %d] bf16 of the headline batch, contiguous%s"
+                        % (G, B, K + 1, Vs, ", early-exit phases %#x" % phase_starts if phase_starts else ""),
+            "launches": len(sched), "ms": ms, "positions_per_s": B * K / (ms * 1e-3), "bytes": nbytes,
+            "GBps": nbytes / (ms * 1e-3) / 1e9, "frac_of_hbm_peak": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "one_pass_bytes": one_pass_logit_bytes(B, K, Vs, 2, temps)}
 
 
 def sequential_logit_bytes(acc, temps, K, V, es):
@@ -714,7 +722,19 @@ def main():
     if not args.no_draft_sampling:
         line["draft_sampling"] = draft_sampling(sv, torch, np, out, inp.temperature, B, K, V, args.seed, dev)
     if not args.no_shard_share:
-        line["shard_share_tp4"] = shard_share(sv, torch, inp, args.seed)
+        # the slice's own plan: the headline's acceptance curve, the boundary priced for a
+        # [B, K+1, V/4] slice; the headline's cut timed beside it
+        G = 4
+        Vs = V // G
+        cost = sv.spec_verify_phase_cost(B, K, Vs, sv.SPEC_BF16)
+        surv = line["early_exit"].get("survival")
+        frac_sampled = line["config"]["sampled_requests"] / B
+        smask = sv.spec_verify_plan_phases(K, surv, frac_sampled, cost) if surv else 0
+        line["shard_share_tp4"] = shard_share(sv, torch, inp, args.seed, G=G, phase_starts=smask)
+        line["shard_share_tp4"]["plan"] = {"phase_starts": smask, "phase_cost_rows": round(cost, 4)}
+        hmask = line["early_exit"]["phase_starts"]
+        if hmask and hmask != smask:
+            line["shard_share_tp4_headline_cut"] = shard_share(sv, torch, inp, args.seed, G=G, phase_starts=hmask)
     if not args.no_configs and args.only == "all":
         line["configs"] = side_configs(sv, torch, np, "all", args.seed)
     if not args.no_cpu_baseline:

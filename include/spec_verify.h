@@ -362,6 +362,20 @@ int spec_draft_sample_launch(const spec_draft_args* args, hipStream_t stream);
  * merges (a decision may differ only within rounding of its threshold).
  * Invalid data is reported as by spec_verify_launch (the draft tokens are
  * global ids in [0, V)).
+ *
+ * Ragged draft counts (num_drafts), a draft row table (draft_row_index into
+ * a buffer of draft rows, each shard holding its slice of them) and early
+ * exit (phase_starts) mean what they mean for spec_verify_launch.  With
+ * phase_starts != 0 the positions 0..K are cut into phases p = 0, 1, ...
+ * at its set bits, and step 1 becomes, for each phase p in order: every
+ * shard runs spec_shard_stats_launch with args->phase = p (records of that
+ * phase's rows, only for requests still alive), the records are exchanged,
+ * and -- unless p is the last phase -- every shard runs
+ * spec_shard_phase_launch with args->phase = p (that phase's accept tests;
+ * each shard keeps the same per-request state in its workspace).  Steps 2
+ * and 3 follow as above.  The outputs are identical to the one-pass sharded
+ * verification (phase_starts = 0, one statistics launch with phase 0); a row
+ * of a phase after the one where a request stopped is never read.
  */
 typedef struct {
   int32_t B, K, V;             /* requests, drafts (1..SPEC_MAX_K), full vocabulary (1..SPEC_MAX_V) */
@@ -381,12 +395,23 @@ typedef struct {
   int32_t* accepted_counts;    /* device out [B] */
   int32_t* output_tokens;      /* device out [B, K+1] */
   void* workspace;             /* device, >= spec_shard_workspace_bytes(B, K, Vs), 16-byte aligned; the
-                                  same workspace must serve decide and draw of one shard */
+                                  same workspace must serve every stage of one shard */
   size_t workspace_bytes;
+  const int32_t* num_drafts;   /* device [B] or NULL: ragged draft counts K_b in [0, K] */
+  const int32_t* draft_row_index; /* device [B, K] or NULL: draft row k of request b is row
+                                  draft_row_index[b*K + k] of a [draft_rows, Vs] slice buffer at
+                                  draft_logits (row stride d_row_stride; d_req_stride unused) */
+  int32_t draft_rows;          /* rows of that buffer (entries outside [0, draft_rows) make a
+                                  sampled request invalid) */
+  uint64_t phase_starts;       /* early exit: bit k (1 <= k <= K) starts a phase at position k; 0 = one pass */
+  int32_t phase;               /* the phase a statistics or phase-decision launch covers, 0-based */
 } spec_shard_args;
 
 size_t spec_shard_workspace_bytes(int32_t B, int32_t K, int32_t Vs);
 int spec_shard_stats_launch(const spec_shard_args* args, hipStream_t stream);
+/* The accept tests of phase args->phase (not the last phase) from every
+ * shard's records of its rows: updates this shard's per-request state. */
+int spec_shard_phase_launch(const spec_shard_args* args, hipStream_t stream);
 int spec_shard_decide_launch(const spec_shard_args* args, hipStream_t stream);
 int spec_shard_draw_launch(const spec_shard_args* args, hipStream_t stream);
 

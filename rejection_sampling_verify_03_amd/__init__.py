@@ -27,7 +27,7 @@ EXPORTED = ("spec_verify_workspace_bytes", "spec_verify_plan_phases", "spec_veri
             "spec_expand_launch", "spec_expand_hidden_launch", "spec_verify_expand_launch",
             "spec_draft_workspace_bytes",
             "spec_draft_sample_launch", "spec_shard_workspace_bytes", "spec_shard_stats_launch",
-            "spec_shard_decide_launch", "spec_shard_draw_launch",
+            "spec_shard_phase_launch", "spec_shard_decide_launch", "spec_shard_draw_launch",
             "spec_workspace_error", "spec_status_string")
 
 
@@ -85,6 +85,8 @@ class SpecShardArgs(ctypes.Structure):
         ("records", ctypes.c_void_p), ("masses", ctypes.c_void_p),
         ("accepted_counts", ctypes.c_void_p), ("output_tokens", ctypes.c_void_p),
         ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
+        ("num_drafts", ctypes.c_void_p), ("draft_row_index", ctypes.c_void_p), ("draft_rows", ctypes.c_int32),
+        ("phase_starts", ctypes.c_uint64), ("phase", ctypes.c_int32),
     ]
 
 
@@ -124,7 +126,8 @@ def _load():
     L.spec_draft_sample_launch.restype = ctypes.c_int
     L.spec_shard_workspace_bytes.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32]
     L.spec_shard_workspace_bytes.restype = ctypes.c_size_t
-    for name in ("spec_shard_stats_launch", "spec_shard_decide_launch", "spec_shard_draw_launch"):
+    for name in ("spec_shard_stats_launch", "spec_shard_phase_launch", "spec_shard_decide_launch",
+                 "spec_shard_draw_launch"):
         getattr(L, name).argtypes = [ctypes.POINTER(SpecShardArgs), ctypes.c_void_p]
         getattr(L, name).restype = ctypes.c_int
     L.spec_status_string.argtypes = [ctypes.c_int]
@@ -218,6 +221,10 @@ def spec_shard_workspace_bytes(B, K, Vs):
 
 def spec_shard_stats_launch(args, stream_ptr):
     return int(lib.spec_shard_stats_launch(ctypes.byref(args), stream_ptr))
+
+
+def spec_shard_phase_launch(args, stream_ptr):
+    return int(lib.spec_shard_phase_launch(ctypes.byref(args), stream_ptr))
 
 
 def spec_shard_decide_launch(args, stream_ptr):
@@ -484,36 +491,59 @@ def draft_sample(logits, row_index, temperature, seed=0, step=0, request_base=0,
 SHARD_RECORD_BYTES = 32
 
 
+def phase_count(K, phase_starts):
+    """Phases of a phase_starts cut of positions 0..K (1 for one pass)."""
+    return 1 + sum(1 for k in range(1, int(K) + 1) if (int(phase_starts) >> k) & 1)
+
+
 class ShardSetup:
     """Argument blocks of the G shards of one vocab-sharded verification and
     the arrays they exchange (records, masses) and write (per-shard accepted
     counts [G, B], output tokens [G, B, K+1])."""
 
-    def __init__(self, shards, records, masses, acc, tok, stream_ptr):
+    def __init__(self, shards, records, masses, acc, tok, stream_ptr, phases=1):
         self.shards, self.records, self.masses = shards, records, masses
         self.acc, self.tok, self.stream_ptr = acc, tok, stream_ptr
+        self.phases = phases
 
-    def launch(self, stage, h):
-        """Enqueue stage 0 (statistics), 1 (decisions) or 2 (draw) of shard h."""
-        launch = (spec_shard_stats_launch, spec_shard_decide_launch, spec_shard_draw_launch)[stage]
-        rc = launch(self.shards[h][0], self.stream_ptr)
+    def launch(self, stage, h, phase=0):
+        """Enqueue stage 0 (statistics of a phase), 1 (decisions), 2 (draw)
+        or 3 (the accept tests of a phase before the last) of shard h."""
+        launch = (spec_shard_stats_launch, spec_shard_decide_launch, spec_shard_draw_launch,
+                  spec_shard_phase_launch)[stage]
+        a = self.shards[h][0]
+        a.phase = int(phase)
+        rc = launch(a, self.stream_ptr)
         if rc != SPEC_OK:
             raise SpecError(rc)
+
+    def schedule(self):
+        """The (stage, phase) launches of one verification in order; each is
+        run on every shard before the next (an exchange between them)."""
+        out = []
+        for p in range(self.phases):
+            out.append((0, p))
+            if p + 1 < self.phases:
+                out.append((3, p))
+        return out + [(1, 0), (2, 0)]
 
     def run(self):
         """Every stage of every shard, in stage order (the exchanges between
         stages are the shared arrays)."""
-        for stage in range(3):
+        for stage, p in self.schedule():
             for h in range(len(self.shards)):
-                self.launch(stage, h)
+                self.launch(stage, h, p)
 
 
 def shard_setup(target, draft, draft_tokens, temperature, G, seed=0, step=0, request_base=0, bounds=None,
-                stream=None):
+                stream=None, phase_starts=0, num_drafts=None, draft_row_index=None):
     """The argument blocks of a verification with the vocabulary split over G
     shards (bounds: G+1 slice boundaries, default as equal as possible), each
     shard reading only its slice of the logits, with their workspaces and
-    exchange arrays allocated here."""
+    exchange arrays allocated here.  With draft_row_index [B, K] int32, draft
+    is a 2-D [N, V] buffer of draft rows (each shard reads its slice of
+    them); num_drafts [B] int32: ragged draft counts; phase_starts: early
+    exit as for verify()."""
     torch = _torch()
     B, K = draft_tokens.shape
     V = target.shape[-1]
@@ -545,12 +575,19 @@ def shard_setup(target, draft, draft_tokens, temperature, G, seed=0, step=0, req
         a.records, a.masses = records.data_ptr(), masses.data_ptr()
         a.accepted_counts, a.output_tokens = acc[h].data_ptr(), tok[h].data_ptr()
         a.workspace, a.workspace_bytes = ws.data_ptr(), ws.numel()
+        if draft_row_index is not None:
+            a.d_req_stride, a.d_row_stride = 0, draft.stride(0)
+            a.draft_row_index, a.draft_rows = draft_row_index.data_ptr(), draft.shape[0]
+        else:
+            a.draft_row_index, a.draft_rows = None, 0
+        a.num_drafts = num_drafts.data_ptr() if num_drafts is not None else None
+        a.phase_starts, a.phase = int(phase_starts), 0
         shards.append((a, ws))
-    return ShardSetup(shards, records, masses, acc, tok, _stream_ptr(stream))
+    return ShardSetup(shards, records, masses, acc, tok, _stream_ptr(stream), phase_count(K, phase_starts))
 
 
 def verify_sharded(target, draft, draft_tokens, temperature, G, seed=0, step=0, request_base=0, bounds=None,
-                   stream=None):
+                   stream=None, phase_starts=0, num_drafts=None, draft_row_index=None):
     """The verification with the vocabulary split over G shards, each stage of
     each shard launched through the C ABI on one GPU; the exchanges between
     shards are the shared record and mass arrays, and the last one (the
@@ -558,6 +595,7 @@ def verify_sharded(target, draft, draft_tokens, temperature, G, seed=0, step=0, 
     bounds: G+1 slice boundaries (default: as equal as possible).  Returns
     (accepted [B], output_tokens [B, K+1], per-shard accepted counts [G, B])."""
     st = shard_setup(target, draft, draft_tokens, temperature, G, seed=seed, step=step, request_base=request_base,
-                     bounds=bounds, stream=stream)
+                     bounds=bounds, stream=stream, phase_starts=phase_starts, num_drafts=num_drafts,
+                     draft_row_index=draft_row_index)
     st.run()
     return st.acc[0].clone(), st.tok.max(dim=0).values, st.acc

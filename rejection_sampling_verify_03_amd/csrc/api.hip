@@ -115,7 +115,32 @@ int draft_check(const spec_draft_args* a) {
 
 size_t shard_ws_bytes(int32_t B, int32_t Vs) {
   const int64_t nseg = ((int64_t)Vs + kSeg - 1) / kSeg;
-  return align256((size_t)B * sizeof(ReqDesc)) + align256((size_t)B * nseg * 2 * sizeof(double));
+  return align256((size_t)B * sizeof(ReqDesc)) + align256((size_t)B * nseg * 2 * sizeof(double)) +
+         align256((size_t)B * sizeof(int32_t));
+}
+
+// Phase p of a cut (bit k of `starts` starts a phase at position k; 0 = one
+// phase): positions [lo, hi) with hi = K + 1 for the last; the number of
+// phases and the start of the last.
+struct PhaseRange {
+  int lo, hi, count, last_lo;
+};
+
+PhaseRange phase_range(uint64_t starts, int K, int p) {
+  PhaseRange r{0, K + 1, 0, 0};
+  int lo = 0;
+  for (int j = 0; lo <= K; ++j) {
+    int hi = lo + 1;
+    while (hi <= K && !((starts >> hi) & 1u)) ++hi;
+    if (j == p) {
+      r.lo = lo;
+      r.hi = hi;
+    }
+    r.count = j + 1;
+    r.last_lo = lo;
+    lo = hi;
+  }
+  return r;
 }
 
 int shard_check(const spec_shard_args* a) {
@@ -130,8 +155,13 @@ int shard_check(const spec_shard_args* a) {
     return SPEC_EINVAL;
   if (a->t_row_stride < a->Vs || a->d_row_stride < a->Vs) return SPEC_EINVAL;
   if (a->t_req_stride != 0 && a->t_req_stride < (int64_t)(a->K + 1) * a->t_row_stride) return SPEC_EINVAL;
-  if (a->d_req_stride != 0 && a->d_req_stride < (int64_t)a->K * a->d_row_stride) return SPEC_EINVAL;
+  if (!a->draft_row_index && a->d_req_stride != 0 && a->d_req_stride < (int64_t)a->K * a->d_row_stride)
+    return SPEC_EINVAL;
+  if (a->draft_row_index && a->draft_rows < 0) return SPEC_EINVAL;
   if ((int64_t)a->B * (2 * a->K + 1) > INT32_MAX) return SPEC_EINVAL;
+  if (a->phase_starts & 1u) return SPEC_EINVAL;  // position 0 always starts the first phase
+  if (a->K < 63 && (a->phase_starts >> (a->K + 1)) != 0) return SPEC_EINVAL;
+  if (a->phase < 0 || a->phase >= phase_range(a->phase_starts, a->K, 0).count) return SPEC_EINVAL;
   if (!aligned16(a->workspace)) return SPEC_EALIGN;
   if (a->workspace_bytes < shard_ws_bytes(a->B, a->Vs)) return SPEC_EWORKSPACE;
   return SPEC_OK;
@@ -165,14 +195,27 @@ ShardParams shard_params(const spec_shard_args* a) {
   P.out_tokens = a->output_tokens;
   char* ws = static_cast<char*>(a->workspace);
   P.desc = reinterpret_cast<ReqDesc*>(ws);
-  P.seg = reinterpret_cast<double*>(ws + align256((size_t)a->B * sizeof(ReqDesc)));
+  const size_t off_seg = align256((size_t)a->B * sizeof(ReqDesc));
+  P.seg = reinterpret_cast<double*>(ws + off_seg);
+  P.state = reinterpret_cast<int32_t*>(ws + off_seg + align256((size_t)a->B * P.nseg * 2 * sizeof(double)));
+  P.dridx = a->draft_row_index;
+  P.draft_rows = a->draft_row_index ? a->draft_rows : 0;
+  P.num_drafts = a->num_drafts;
+  const PhaseRange ph = phase_range(a->phase_starts, a->K, a->phase);
+  P.ph_lo = ph.lo;
+  P.ph_nt = ph.hi - ph.lo;
+  P.ph_nd = (ph.hi < a->K ? ph.hi : a->K) - ph.lo;
+  P.ph_check = a->phase > 0;
+  P.phased = ph.count > 1;
+  P.last_lo = ph.last_lo;
   return P;
 }
 
 bool shard_vec(const spec_shard_args* a) {
   const int es = a->dtype == SPEC_BF16 ? 2 : 4;
   return aligned16(a->target_logits) && aligned16(a->draft_logits) && (a->t_row_stride * es) % 16 == 0 &&
-         (a->t_req_stride * es) % 16 == 0 && (a->d_row_stride * es) % 16 == 0 && (a->d_req_stride * es) % 16 == 0;
+         (a->t_req_stride * es) % 16 == 0 && (a->d_row_stride * es) % 16 == 0 &&
+         (a->draft_row_index || (a->d_req_stride * es) % 16 == 0);
 }
 
 }  // namespace
@@ -188,6 +231,15 @@ int spec_shard_stats_launch(const spec_shard_args* a, hipStream_t stream) {
   const int rc = shard_check(a);
   if (rc != SPEC_OK || a->B == 0) return rc;
   return launch_shard_stats(shard_params(a), a->dtype, shard_vec(a), stream) == hipSuccess ? SPEC_OK : SPEC_ELAUNCH;
+}
+
+int spec_shard_phase_launch(const spec_shard_args* a, hipStream_t stream) {
+  if (!a || a->K < 1 || a->K > SPEC_MAX_K) return SPEC_EINVAL;
+  if (a->phase >= phase_range(a->phase_starts, a->K, 0).count - 1) return SPEC_EINVAL;  // not the last phase
+  const int rc = shard_check(a);
+  if (rc != SPEC_OK) return rc;
+  if (a->B == 0) return SPEC_OK;
+  return launch_shard_phase(shard_params(a), a->dtype, shard_vec(a), stream) == hipSuccess ? SPEC_OK : SPEC_ELAUNCH;
 }
 
 int spec_shard_decide_launch(const spec_shard_args* a, hipStream_t stream) {

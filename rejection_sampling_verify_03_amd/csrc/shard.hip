@@ -15,6 +15,9 @@
 //      writes the same outputs; then sums the residual (and p) weights of its
 //      slice of the sampling row(s) per 4096-logit segment -> one (R_g, P_g)
 //      pair per request; the pairs are exchanged.
+//  shard_phase   (early exit only) between phases, per request on every
+//      shard: the phase's accept tests from every shard's records of its
+//      rows, leaving the same per-request state on every shard.
 //  shard_draw    per request: the totals over shards, in shard order, give
 //      u' * W and the shard holding the crossing; that shard alone finds the
 //      token in its slice (segment scan, then one segment) and writes it as a
@@ -31,19 +34,65 @@
 
 namespace specv {
 
-template <int ES>
-__device__ __forceinline__ const char* shard_row(const ShardParams& P, int b, int r) {
-  if (r <= P.K) return P.target + ((int64_t)b * P.t_req + (int64_t)r * P.t_row) * ES;
-  return P.draft + ((int64_t)b * P.d_req + (int64_t)(r - P.K - 1) * P.d_row) * ES;
+// Drafts K_b of request b (ragged counts, else K), loaded unconditionally so
+// it can be issued with other loads; -1 for a count outside [0, K].
+__device__ __forceinline__ int shard_drafts_of(const ShardParams& P, int b) {
+  const int32_t* t = P.num_drafts ? P.num_drafts : reinterpret_cast<const int32_t*>(P.temperature);
+  const int v = t[b];
+  const int kb = P.num_drafts ? v : P.K;
+  return (kb >= 0 && kb <= P.K) ? kb : -1;
 }
 
+// The draft row table's entry for position k (clamped into [0, K); 0 without
+// a table), loaded unconditionally; and whether it names a row of the buffer.
+__device__ __forceinline__ int shard_draft_entry(const ShardParams& P, int b, int k) {
+  const int32_t* t = P.dridx ? P.dridx : P.tokens;
+  const int v = t[(int64_t)b * P.K + min(max(k, 0), P.K - 1)];
+  return P.dridx ? v : 0;
+}
+
+__device__ __forceinline__ bool shard_entry_ok(const ShardParams& P, int di) {
+  return !P.dridx || (uint32_t)di < (uint32_t)P.draft_rows;
+}
+
+// Element offset of draft row k of request b's slice from the draft base.
+__device__ __forceinline__ int64_t shard_draft_off(const ShardParams& P, int b, int k, int di) {
+  return P.dridx ? (int64_t)di * P.d_row : (int64_t)b * P.d_req + (int64_t)k * P.d_row;
+}
+
+// Row r of request b's slice: target rows 0..K, then draft rows K+1..2K.
+template <int ES>
+__device__ __forceinline__ const char* shard_row(const ShardParams& P, int b, int r, int di = 0) {
+  if (r <= P.K) return P.target + ((int64_t)b * P.t_req + (int64_t)r * P.t_row) * ES;
+  return P.draft + shard_draft_off(P, b, r - P.K - 1, di) * ES;
+}
+
+// Statistics of the rows of one phase (every row in one pass): one
+// workgroup per (request, row) reduces this shard's slice of the row.  Rows
+// that are not read write no record: draft rows of greedy requests, rows of
+// requests that stopped in an earlier phase, rows past a request's drafts,
+// and rows of a request whose draft count, token or row entry is out of
+// range (such a request is invalid; no record of it is used).
 template <int ES, bool VEC>
 __global__ __launch_bounds__(kWG) void shard_stats_kernel(ShardParams P) {
-  const int b = blockIdx.x / P.R, r = blockIdx.x % P.R;
+  const int nr = P.ph_nt + P.ph_nd;
+  const int b = blockIdx.x / nr, lr = blockIdx.x % nr;
+  const int r = lr < P.ph_nt ? P.ph_lo + lr : P.K + 1 + P.ph_lo + (lr - P.ph_nt);
   const int k = r <= P.K ? r : r - P.K - 1;
+  // independent loads, issued together (the state of a first phase is stale
+  // and ignored; position K has no token)
   const float T = P.temperature[b];
-  const int x = P.tokens[(int64_t)b * P.K + min(k, P.K - 1)];
+  const int st = P.state[b];
+  const int xt = P.tokens[(int64_t)b * P.K + min(k, P.K - 1)];
+  const int di = shard_draft_entry(P, b, k);
+  const int kb = shard_drafts_of(P, b);
   const bool greedy = T == 0.0f;
+  const bool bad_t = !temperature_valid(T);
+  const bool skip = bad_t | (greedy & (r > P.K)) | ((P.ph_check != 0) & (st != kStateAlive)) |
+                    ((k < kb) & ((uint32_t)xt >= (uint32_t)P.V)) | ((r > P.K) & !shard_entry_ok(P, di)) |
+                    (kb < 0) | ((r <= P.K) & (k > kb)) | ((r > P.K) & (k >= kb));
+  if (skip) return;
+  const int x = k < kb ? xt : -1;
   ShardRec rec;
   rec.m = -INFINITY;
   rec.idx = INT_MAX;
@@ -51,25 +100,131 @@ __global__ __launch_bounds__(kWG) void shard_stats_kernel(ShardParams P) {
   rec.z = 0.f;
   rec.has_z = 0;
   rec.pad = 0;
-  if (temperature_valid(T) && !(greedy && r > P.K)) {  // greedy requests read no draft rows
-    const char* row = shard_row<ES>(P, b, r);
-    if (greedy) {
-      const VI v = block_argmax(chunk_argmax<ES, VEC>(row, 0, P.Vs));
-      rec.m = v.v;
-      rec.idx = v.i + P.v0;
-    } else {
-      float s_hi, s_lo;
-      temperature_scale(T, s_hi, s_lo);
-      const MS v = block_merge_ms(chunk_stats<ES, VEC>(row, 0, P.Vs, s_hi, s_lo));
-      rec.m = v.m;
-      rec.s = v.s;
-      if (k < P.K && x >= P.v0 && x - P.v0 < P.Vs) {
-        rec.z = load_one<ES>(row, x - P.v0);
-        rec.has_z = 1;
-      }
+  const char* row = shard_row<ES>(P, b, r, di);
+  if (greedy) {
+    const VI v = block_argmax(chunk_argmax<ES, VEC>(row, 0, P.Vs));
+    rec.m = v.v;
+    rec.idx = v.i + P.v0;
+  } else {
+    float s_hi, s_lo;
+    temperature_scale(T, s_hi, s_lo);
+    const MS v = block_merge_ms(chunk_stats<ES, VEC>(row, 0, P.Vs, s_hi, s_lo));
+    rec.m = v.m;
+    rec.s = v.s;
+    if (x >= P.v0 && x - P.v0 < P.Vs) {
+      rec.z = load_one<ES>(row, x - P.v0);
+      rec.has_z = 1;
     }
   }
   if (threadIdx.x == 0) P.recs[((int64_t)P.g * P.B + b) * P.R + r] = rec;
+}
+
+struct ShardShared {
+  int64_t qoff[SPEC_MAX_K];     // draft row offsets of the positions
+  float m[2 * SPEC_MAX_K + 1];
+  double s[2 * SPEC_MAX_K + 1];
+  float z[2 * SPEC_MAX_K + 1];  // logit of the row at its position's draft token
+  int g[SPEC_MAX_K + 1];
+  int a;
+  int kb;
+};
+
+constexpr int kNotAliveShard = -3;  // shard_tests: the request stopped in an earlier phase
+
+// The accept tests of request b over draft positions [lo, hi) from every
+// shard's records, in the order of the unsharded decision: merges (in shard
+// order) the records of target rows [lo, thi) and, for a sampled request,
+// draft rows [lo, min(thi, K)); with known >= 0 no test runs and a = known.
+// Returns, in every thread, a in [lo, hi] or -1 for invalid data (every
+// draft token, the temperature, the draft count and the row entries are
+// checked whatever the range); with check_state, kNotAliveShard for a
+// request that stopped earlier.  All threads of the workgroup call it.
+__device__ int shard_tests(const ShardParams& P, int b, int lo, int hi, int thi, int known, bool invalid,
+                           bool check_state, ShardShared& sh) {
+  const int K = P.K;
+  const int tid = threadIdx.x;
+  const bool test = known < 0;
+  const int st = P.state[b];
+  const float T = P.temperature[b];
+  const int kb_ = shard_drafts_of(P, b);
+  const int x = P.tokens[(int64_t)b * K + min(tid, K - 1)];
+  const int nt = thi - lo;
+  const int nd = min(thi, K) - lo;
+  const bool row_thread = tid < nt + nd && !invalid;
+  const int r = tid < nt ? lo + tid : K + 1 + lo + (tid - nt);
+  const int k = tid < nt ? r : r - K - 1;
+  const int dix = shard_draft_entry(P, b, tid);
+  const bool greedy = T == 0.0f;
+  const int kb = max(kb_, 0);
+  bool mybad = invalid || kb_ < 0 || !temperature_valid(T) || (tid < kb && (x < 0 || x >= P.V));
+  if (!greedy && tid < kb) {
+    mybad |= !shard_entry_ok(P, dix);  // a sampled request reads every draft row
+    sh.qoff[tid] = shard_draft_off(P, b, tid, dix);
+  }
+  const bool row_exists = tid < nt ? k <= kb : k < kb;
+  if (row_thread && row_exists && (!greedy || tid < nt) && temperature_valid(T)) {
+    const ShardRec* rr = P.recs + (int64_t)b * P.R + r;
+    const int64_t stride = (int64_t)P.B * P.R;
+    if (greedy) {
+      VI best{rr[0].m, rr[0].idx};
+      for (int h = 1; h < P.G; ++h) best = vi_pick(best, VI{rr[h * stride].m, rr[h * stride].idx});
+      sh.g[r] = best.i;
+    } else {
+      MS acc{rr[0].m, rr[0].s};
+      float z = rr[0].z;
+      for (int h = 1; h < P.G; ++h) {
+        const ShardRec q = rr[h * stride];
+        acc = ms_merge(acc, MS{q.m, q.s});
+        if (q.has_z) z = q.z;
+      }
+      sh.m[r] = acc.m;
+      sh.s[r] = acc.s;
+      sh.z[r] = z;
+      mybad |= !(acc.s > 0.0 && acc.s <= DBL_MAX && fabsf(acc.m) <= FLT_MAX);
+    }
+  }
+  const bool bad = __syncthreads_or(mybad) != 0;
+  if (check_state && st != kStateAlive) return kNotAliveShard;  // its records here were never written
+  if (tid < 64) {  // wave 0: one lane per draft position
+    bool acc = tid < lo;
+    if (test && tid >= lo && tid < min(hi, kb) && !bad) {
+      if (greedy) {
+        acc = x == sh.g[tid];
+      } else {
+        float s_hi, s_lo;
+        temperature_scale(T, s_hi, s_lo);
+        const double s_eff = (double)s_hi + (double)s_lo;
+        const double p = exp2((double)sh.z[tid] * s_eff - (double)sh.m[tid]) / sh.s[tid];
+        const double q = exp2((double)sh.z[K + 1 + tid] * s_eff - (double)sh.m[K + 1 + tid]) / sh.s[K + 1 + tid];
+        const double thr = q > 0.0 ? fmin(1.0, p / q) : (p > 0.0 ? 1.0 : 0.0);
+        const uint32_t k0 = (uint32_t)(P.seed & 0xffffffffu), k1 = (uint32_t)(P.seed >> 32);
+        acc = unit_uniform(philox4x32_10((uint32_t)b + P.request_base, (uint32_t)tid, P.step, 0u, k0, k1).w[0]) < thr;
+      }
+    }
+    const uint64_t mask = __ballot(acc);
+    // lanes >= min(hi, K_b) fail: a <= min(hi, K_b)
+    const int a = bad ? -1 : (test ? (int)__builtin_ctzll(~mask) : known);
+    if (tid == 0) {
+      sh.a = a;
+      sh.kb = kb;
+    }
+  }
+  __syncthreads();
+  return sh.a;
+}
+
+// Between early-exit phases: the accept tests of the phase's positions
+// [ph_lo, ph_lo + ph_nd) for every request still alive, from every shard's
+// records of the phase; one workgroup per request updates the state (every
+// shard computes the same).
+template <int ES>
+__global__ __launch_bounds__(kWG) void shard_phase_kernel(ShardParams P) {
+  __shared__ ShardShared sh;
+  const int b = blockIdx.x;
+  const int lo = P.ph_lo, hi = P.ph_lo + P.ph_nd;
+  const int a = shard_tests(P, b, lo, hi, hi, -1, false, P.ph_check != 0, sh);
+  if (a == kNotAliveShard) return;
+  if (threadIdx.x == 0) P.state[b] = a < 0 ? kStateInvalid : (a < hi ? a : kStateAlive);
 }
 
 // The decision workgroup is 16 waves, so that each of a slice's segments
@@ -80,84 +235,54 @@ constexpr int kDecideWaves = kDecideWG / 64;
 
 template <int ES, bool VEC>
 __global__ __launch_bounds__(kDecideWG) void shard_decide_kernel(ShardParams P) {
-  __shared__ float sm[2 * SPEC_MAX_K + 1];
-  __shared__ double ss[2 * SPEC_MAX_K + 1];
-  __shared__ float sz[2 * SPEC_MAX_K + 1];
-  __shared__ int sg[SPEC_MAX_K + 1];
+  __shared__ ShardShared sh;
   __shared__ ReqDesc D;
   const int b = blockIdx.x, K = P.K, tid = threadIdx.x;
-  const float T = P.temperature[b];
-  const bool greedy = T == 0.0f;
-  const int x = P.tokens[(int64_t)b * K + min(tid, K - 1)];
-  bool mybad = !temperature_valid(T) || (tid < K && (x < 0 || x >= P.V));
-  const int nrows = greedy ? K + 1 : P.R;
-  if (tid < nrows && temperature_valid(T)) {
-    // the G records of row tid, merged in shard order
-    const ShardRec* rr = P.recs + (int64_t)b * P.R + tid;
-    const int64_t stride = (int64_t)P.B * P.R;
-    if (greedy) {
-      VI best{rr[0].m, rr[0].idx};
-      for (int h = 1; h < P.G; ++h) best = vi_pick(best, VI{rr[h * stride].m, rr[h * stride].idx});
-      sg[tid] = best.i;
+  int lo = 0, known = -1;
+  bool invalid = false;
+  if (P.phased) {  // rows were read in phases: the request may have stopped earlier
+    const int st = P.state[b];
+    invalid = st == kStateInvalid;
+    if (st >= 0) {
+      known = st;
+      lo = st;
     } else {
-      MS acc{rr[0].m, rr[0].s};
-      float z = rr[0].z;
-      for (int h = 1; h < P.G; ++h) {
-        const ShardRec q = rr[h * stride];
-        acc = ms_merge(acc, MS{q.m, q.s});
-        if (q.has_z) z = q.z;
-      }
-      sm[tid] = acc.m;
-      ss[tid] = acc.s;
-      sz[tid] = z;
-      mybad |= !(acc.s > 0.0 && acc.s <= DBL_MAX && fabsf(acc.m) <= FLT_MAX);
+      lo = P.last_lo;
     }
   }
-  const bool bad = __syncthreads_or(mybad) != 0;
-  float s_hi = 0.f, s_lo = 0.f;
-  if (!greedy && !bad) temperature_scale(T, s_hi, s_lo);
-  const uint32_t k0 = (uint32_t)(P.seed & 0xffffffffu), k1 = (uint32_t)(P.seed >> 32);
-  const uint32_t req = (uint32_t)b + P.request_base;
-  if (tid < 64) {  // wave 0: one lane per draft position
-    bool acc = false;
-    if (tid < K && !bad) {
-      if (greedy) {
-        acc = x == sg[tid];
-      } else {
-        const double s_eff = (double)s_hi + (double)s_lo;
-        const double p = exp2((double)sz[tid] * s_eff - (double)sm[tid]) / ss[tid];
-        const double q = exp2((double)sz[K + 1 + tid] * s_eff - (double)sm[K + 1 + tid]) / ss[K + 1 + tid];
-        const double thr = q > 0.0 ? fmin(1.0, p / q) : (p > 0.0 ? 1.0 : 0.0);
-        acc = unit_uniform(philox4x32_10(req, (uint32_t)tid, P.step, 0u, k0, k1).w[0]) < thr;
-      }
-    }
-    const uint64_t mask = __ballot(acc);
-    const int a = bad ? -1 : (int)__builtin_ctzll(~mask);
+  const int thi = known >= 0 ? known + 1 : K + 1;
+  const int a = shard_tests(P, b, lo, K, thi, known, invalid, false, sh);
+  const float T = P.temperature[b];
+  const bool greedy = T == 0.0f;
+  const bool bad = a < 0;
+  if (tid < 64) {
     int32_t* out = P.out_tokens + (int64_t)b * (K + 1);
     for (int j = tid; j <= K; j += 64) {  // K <= 63: one pass
       int tok;
       if (bad || j > a) tok = -1;
       else if (j < a) tok = P.tokens[(int64_t)b * K + j];
-      else tok = greedy ? sg[a] : -1;  // sampled: the owning shard's draw writes it
+      else tok = greedy ? sh.g[a] : -1;  // sampled: the owning shard's draw writes it
       out[j] = tok;
     }
     if (tid == 0) {
       P.accepted[b] = a;
       ReqDesc d;
       d.a = a;
-      d.mode = (bad || greedy) ? kModeNone : (a < K ? kModeResidual : kModeBonus);
-      d.s_hi = s_hi;
-      d.s_lo = s_lo;
+      d.mode = (bad || greedy) ? kModeNone : (a < sh.kb ? kModeResidual : kModeBonus);
+      d.s_hi = d.s_lo = 0.f;
       d.mp = d.sp = d.mq = d.sq = d.u = 0.0;
       d.qoff = 0;
       if (d.mode != kModeNone) {
-        d.mp = (double)sm[a];
-        d.sp = ss[a];
-        if (a < K) {
-          d.mq = (double)sm[K + 1 + a];
-          d.sq = ss[K + 1 + a];
+        temperature_scale(T, d.s_hi, d.s_lo);
+        d.mp = (double)sh.m[a];
+        d.sp = sh.s[a];
+        if (a < sh.kb) {
+          d.mq = (double)sh.m[K + 1 + a];
+          d.sq = sh.s[K + 1 + a];
+          d.qoff = sh.qoff[a];
         }
-        d.u = unit_uniform(philox4x32_10(req, (uint32_t)a, P.step, 0u, k0, k1).w[1]);
+        const uint32_t k0 = (uint32_t)(P.seed & 0xffffffffu), k1 = (uint32_t)(P.seed >> 32);
+        d.u = unit_uniform(philox4x32_10((uint32_t)b + P.request_base, (uint32_t)a, P.step, 0u, k0, k1).w[1]);
       }
       D = d;
       P.desc[b] = d;
@@ -173,7 +298,7 @@ __global__ __launch_bounds__(kDecideWG) void shard_decide_kernel(ShardParams P) 
   // per segment, in units of 1 / S_p of the whole row
   const bool res = D.mode == kModeResidual;
   const char* prow = shard_row<ES>(P, b, D.a);
-  const char* qrow = res ? shard_row<ES>(P, b, K + 1 + D.a) : prow;
+  const char* qrow = res ? P.draft + D.qoff * ES : prow;
   WeightCtx w;
   w.s_hi = D.s_hi;
   w.s_lo = D.s_lo;
@@ -267,7 +392,7 @@ __global__ __launch_bounds__(kDrawThreads) void shard_draw_kernel(ShardParams P)
   }
   const bool resmode = d.mode == kModeResidual;
   const char* prow = shard_row<ES>(P, b, d.a);
-  const char* qrow = resmode ? shard_row<ES>(P, b, P.K + 1 + d.a) : prow;
+  const char* qrow = resmode ? P.draft + d.qoff * ES : prow;
   WeightCtx w;
   w.s_hi = d.s_hi;
   w.s_lo = d.s_lo;
@@ -297,7 +422,14 @@ __global__ __launch_bounds__(kDrawThreads) void shard_draw_kernel(ShardParams P)
   } while (0)
 
 hipError_t launch_shard_stats(const ShardParams& P, int dtype, bool vec, hipStream_t stream) {
-  SHARD_DISPATCH(shard_stats_kernel, (unsigned)(P.B * P.R), kWG);
+  SHARD_DISPATCH(shard_stats_kernel, (unsigned)(P.B * (P.ph_nt + P.ph_nd)), kWG);
+}
+
+hipError_t launch_shard_phase(const ShardParams& P, int dtype, bool vec, hipStream_t stream) {
+  (void)vec;
+  if (dtype == SPEC_BF16) hipLaunchKernelGGL((shard_phase_kernel<2>), dim3((unsigned)P.B), dim3(kWG), 0, stream, P);
+  else hipLaunchKernelGGL((shard_phase_kernel<4>), dim3((unsigned)P.B), dim3(kWG), 0, stream, P);
+  return hipGetLastError();
 }
 
 hipError_t launch_shard_decide(const ShardParams& P, int dtype, bool vec, hipStream_t stream) {

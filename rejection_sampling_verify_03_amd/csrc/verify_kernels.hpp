@@ -111,9 +111,21 @@ struct ShardParams {
   int32_t* out_tokens;
   ReqDesc* desc;     // [B] (this shard's workspace)
   double* seg;       // [B, nseg, 2] (this shard's workspace)
+  int32_t* state;    // [B] request state between early-exit phases (this shard's workspace)
+  const int32_t* dridx;       // draft row table [B, K] (rows of a [draft_rows, Vs] slice buffer) or null
+  int32_t draft_rows;
+  const int32_t* num_drafts;  // ragged draft counts [B] or null (all K)
+  // rows of the phase a statistics or phase-decision launch covers: target
+  // rows [ph_lo, ph_lo + ph_nt), draft rows [ph_lo, ph_lo + ph_nd); ph_check:
+  // a later phase (skip requests no longer alive)
+  int32_t ph_lo, ph_nt, ph_nd, ph_check;
+  // the final decision: rows were read in phases (phased), the last phase
+  // starting at position last_lo
+  int32_t phased, last_lo;
 };
 
 hipError_t launch_shard_stats(const ShardParams& P, int dtype, bool vec, hipStream_t stream);
+hipError_t launch_shard_phase(const ShardParams& P, int dtype, bool vec, hipStream_t stream);
 hipError_t launch_shard_decide(const ShardParams& P, int dtype, bool vec, hipStream_t stream);
 hipError_t launch_shard_draw(const ShardParams& P, int dtype, bool vec, hipStream_t stream);
 

@@ -283,20 +283,39 @@ def test_shard_argument_errors(sv):
         a.workspace_bytes = 0
         return a
 
-    for launch in (sv.spec_shard_stats_launch, sv.spec_shard_decide_launch, sv.spec_shard_draw_launch):
+    for launch in (sv.spec_shard_stats_launch, sv.spec_shard_decide_launch, sv.spec_shard_draw_launch,
+                   sv.spec_shard_phase_launch):
+        if launch is sv.spec_shard_phase_launch:  # needs a phase that is not the last
+            a = args()
+            a.phase_starts = 1 << 2
+            assert launch(a, None) == sv.SPEC_EWORKSPACE
+            a.phase = 1
+            assert launch(a, None) == sv.SPEC_EINVAL
+            a.phase_starts = 0
+            a.phase = 0
+            assert launch(a, None) == sv.SPEC_EINVAL
+            continue
         assert launch(args(), None) == sv.SPEC_EWORKSPACE
         for field, value, want in [("G", 0, sv.SPEC_EINVAL), ("g", 2, sv.SPEC_EINVAL), ("g", -1, sv.SPEC_EINVAL),
                                    ("Vs", 0, sv.SPEC_EINVAL), ("v0", 51, sv.SPEC_EINVAL), ("v0", -1, sv.SPEC_EINVAL),
                                    ("K", 64, sv.SPEC_EINVAL), ("dtype", 3, sv.SPEC_EDTYPE),
                                    ("V", sv.SPEC_MAX_V + 1, sv.SPEC_EINVAL),
                                    ("t_row_stride", 49, sv.SPEC_EINVAL), ("records", None, sv.SPEC_EINVAL),
-                                   ("masses", None, sv.SPEC_EINVAL), ("workspace", 0x10008, sv.SPEC_EALIGN)]:
+                                   ("masses", None, sv.SPEC_EINVAL), ("workspace", 0x10008, sv.SPEC_EALIGN),
+                                   ("phase_starts", 1, sv.SPEC_EINVAL), ("phase_starts", 1 << 4, sv.SPEC_EINVAL),
+                                   ("phase", 1, sv.SPEC_EINVAL), ("phase", -1, sv.SPEC_EINVAL),
+                                   ("draft_rows", -1, sv.SPEC_EWORKSPACE)]:
             a = args()
             setattr(a, field, value)
             assert launch(a, None) == want, (launch, field, value)
-    assert sv.spec_shard_workspace_bytes(2, 3, 50) == 256 + 256
+    # a draft row table with a negative row count
+    a = args()
+    a.draft_row_index, a.draft_rows = fake, -1
+    assert sv.spec_shard_stats_launch(a, None) == sv.SPEC_EINVAL
+    # decision records, segment sums and the request state between phases
+    assert sv.spec_shard_workspace_bytes(2, 3, 50) == 256 + 256 + 256
     assert sv.spec_shard_workspace_bytes(1, 1, sv.SPEC_MAX_V + 1) == 0
-    assert sv.spec_shard_workspace_bytes(256, 8, 37984) == 256 * 64 + 256 * 10 * 16
+    assert sv.spec_shard_workspace_bytes(256, 8, 37984) == 256 * 64 + 256 * 10 * 16 + 256 * 4
 
 
 def test_noalloc_argument_errors(sv):

@@ -93,3 +93,81 @@ def test_headline_sharded_tp4(sv):
     same = ((a1 == acc) & (t1 == tok).all(dim=1)).float().mean().item()
     say("  %.4f of requests identical to the unsharded launch" % same)
     assert same > 0.98
+
+
+def _row_table_inputs(inp, seed):
+    """The draft rows of `inp` scattered into a larger [N, V] buffer (the
+    drafter's rows at the new-token indices) and the [B, K] table naming
+    them."""
+    B, K, V = inp.B, inp.K, inp.V
+    g = torch.Generator(device="cuda").manual_seed(seed)
+    N = B * K + 7
+    perm = torch.randperm(N, generator=g, device="cuda")[:B * K]
+    buf = torch.zeros(N, V, dtype=inp.draft.dtype, device="cuda")
+    buf[perm] = inp.draft[:, :K].reshape(B * K, V)
+    return buf, perm.reshape(B, K).to(torch.int32).contiguous()
+
+
+@pytest.mark.parametrize("G", [2, 3])
+def test_sharded_phases_ragged_row_table(sv, G):
+    """Early exit, ragged draft counts and a draft row table in the sharded
+    form: bit-identical to the sharded one pass under every cut (the same
+    records and merges), every shard taking the same decisions, and every
+    request against the oracle."""
+    say("case: vocab-sharded verify G=%d with phases, ragged counts and a draft row table" % G)
+    B, K, V = 16, 6, 40000
+    inp = workloads.mixture_inputs("shard ext", B, K, V, torch.bfloat16, 12 + G, "cuda", temps=(0.0, 0.6, 1.0),
+                                   lam_lo=0.05, lam_hi=0.6)
+    nd = torch.tensor([6, 0, 3, 6, 1, 5, 2, 6, 4, 6, 0, 6, 3, 5, 6, 1], dtype=torch.int32, device="cuda")
+    buf, ridx = _row_table_inputs(inp, G)
+    tl, dl = workloads.logits_numpy(inp.target), workloads.logits_numpy(inp.draft)
+    x, T = inp.draft_tokens.cpu().numpy(), inp.temperature.cpu().numpy()
+    for step in range(2):
+        ref = None
+        for mask in (0, 0b100100, 0b10, 0b1111110):
+            acc, tok, per = sv.verify_sharded(inp.target, buf, inp.draft_tokens, inp.temperature, G, seed=7,
+                                              step=step, phase_starts=mask, num_drafts=nd, draft_row_index=ridx)
+            torch.cuda.synchronize()
+            per = per.cpu().numpy()
+            assert (per == per[0]).all(), ("shards disagree", mask)
+            if ref is None:
+                ref = (acc.clone(), tok.clone())
+            else:
+                assert torch.equal(ref[0], acc) and torch.equal(ref[1], tok), ("cut differs from one pass", mask)
+        rep = compare(tl, dl, x, T, ref[0].cpu().numpy(), ref[1].cpu().numpy(), None, seed=7, step=step,
+                      report=Report(), num_drafts=nd.cpu().numpy())
+        say("  step %d: %s" % (step, rep.summary()))
+        assert rep.ok(), rep.failures[:5]
+        assert (ref[0].cpu().numpy() <= nd.cpu().numpy()).all()
+
+
+def test_sharded_extensions_invalid_data(sv):
+    say("case: vocab-sharded verify, invalid draft counts and row entries, phased")
+    B, K, V = 6, 3, 3000
+    inp = workloads.mixture_inputs("shard bad", B, K, V, torch.float32, 5, "cuda", temps=(0.6, 1.0),
+                                   lam_lo=0.1, lam_hi=0.5)
+    buf, ridx = _row_table_inputs(inp, 1)
+    nd = torch.tensor([3, 4, 2, 3, -1, 3], dtype=torch.int32, device="cuda")  # 4 > K and -1: invalid
+    ridx = ridx.clone()
+    ridx[2, 1] = buf.shape[0]      # outside the buffer: request 2 reads draft row 1 -> invalid
+    ridx[5, 2] = -3
+    for mask in (0, 0b100):
+        acc, tok, per = sv.verify_sharded(inp.target, buf, inp.draft_tokens, inp.temperature, 2,
+                                          phase_starts=mask, num_drafts=nd, draft_row_index=ridx)
+        acc, tok = acc.cpu().numpy(), tok.cpu().numpy()
+        for b in (1, 2, 4, 5):
+            assert acc[b] == -1 and (tok[b] == -1).all(), (mask, b)
+        assert acc[0] >= 0 and acc[3] >= 0, mask
+
+
+def test_headline_sharded_tp4_phased(sv):
+    """B=256, K=8, V=151936 bf16 over 4 shards with the benchmarked cut
+    {0..2 | 3..8}: identical to the sharded one pass."""
+    say("case: vocab-sharded verify, headline over 4 shards, phased")
+    inp = workloads.verify_headline(seed=3, device="cuda")
+    a0, t0, _ = sv.verify_sharded(inp.target, inp.draft, inp.draft_tokens, inp.temperature, 4, seed=1)
+    a1, t1, per = sv.verify_sharded(inp.target, inp.draft, inp.draft_tokens, inp.temperature, 4, seed=1,
+                                    phase_starts=0b1000)
+    torch.cuda.synchronize()
+    assert torch.equal(a0, a1) and torch.equal(t0, t1)
+    assert (per == per[0]).all()
