@@ -29,7 +29,9 @@ the host's cores over whole steps of the same batch (and on one core).
 Side measurements, outside the timed steps (each timed with HIP events):
 draft-token sampling at the step's new-token indices (draft_sampling), one
 GPU's share of a 4-way vocab-sharded verification of the same batch
-(shard_share_tp4), and the other workloads (configs): the GPT-OSS vocabulary
+(shard_share_tp4), a whole P-EAGLE round -- draft sampling, then the chained
+verification and expansion -- with and without the sampler's row statistics
+handed to the verification (peagle_round), and the other workloads (configs): the GPT-OSS vocabulary
 batch (B=64, K=5, V=201088) and the expansion alone (B=512, K=8, H=2880),
 each rotating over input copies that together exceed the 256 MB Infinity
 Cache, and the large batch (B=1024, K=8, V=201088, acceptance ~0.8).
@@ -419,6 +421,86 @@ def expand_config(sv, torch, B=512, K=8, H=2880, copies=8, steps=48, seed=0):
                             "write_GBps": cbytes / 2 / (cms * 1e-3) / 1e9}}
 
 
+def peagle_round(sv, torch, np, inp, seed, steps=20):
+    """One P-EAGLE round at the headline shape, timed two ways: draft-token
+    sampling at the new-token indices of an expanded batch (from drafter rows
+    holding the headline's mixture drafts, so the acceptance is the
+    headline's), then the chained verification of those tokens against those
+    rows (read in place through the row table) with the expansion of its
+    outputs.  "rows": the verification's row pass reads the drafter rows;
+    "stats": the sampler hands its row statistics to the verification, whose
+    row pass then reads the target rows only.  Each way plans its early-exit
+    cut with the shape-priced planner from 8 one-pass rounds."""
+    import workloads
+    B, K, V = inp.B, inp.K, inp.V
+    dev = inp.target.device
+    ex = workloads.step_expand_inputs(inp, seed=seed)
+    acc = torch.empty(B, dtype=torch.int32, device=dev)
+    tok = torch.empty(B, K + 1, dtype=torch.int32, device=dev)
+    ws = sv.make_workspace(B, K, V, dev)
+    out = sv.expand_outputs(B, K, ex.N_in, ex.H, dev, with_slots=True)
+    # the new-token indices of one expansion, and drafter rows there holding the mixture drafts
+    first = sv.expand(ex.in_token_ids, ex.in_positions, ex.in_start, torch.zeros(B, dtype=torch.int32, device=dev),
+                      inp.draft_tokens[:, 0].contiguous(), K, ex.mask_id)
+    nti = first.new_token_indices.clone()
+    drafter = torch.zeros(ex.N_out, V, dtype=inp.draft.dtype, device=dev)
+    drafter[nti.reshape(-1).long()] = inp.draft[:, :K].reshape(B * K, V)
+    x = torch.empty(B, K, dtype=torch.int32, device=dev)
+    stats = sv.draft_stats_buffer(B, K, dev)
+    dws = torch.empty(sv.spec_draft_workspace_bytes(B, K, V), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    sptr = stream.cuda_stream
+    xa = sv.expand_args(ex.in_token_ids, ex.in_positions, ex.in_start, acc, None, K, ex.mask_id, ex.target_hidden,
+                        ex.mask_hidden, out, verify_tokens=tok, block_table=ex.block_table, block_size=ex.block_size)
+    temps = inp.temperature.cpu().numpy()
+    res = {}
+    for way in ("rows", "stats"):
+        da = sv.draft_args(drafter, nti, inp.temperature, x, dws, seed=seed + 9,
+                           stats_out=stats if way == "stats" else None)
+        va = sv.verify_args(inp.target, drafter, x, inp.temperature, acc, tok, None, ws, seed=seed,
+                            draft_row_index=nti, draft_stats=stats if way == "stats" else None)
+        mask = {"m": 0}
+
+        def launch(i, ev):
+            da.step = va.step = i & 0xFFFFFFFF
+            va.phase_starts = mask["m"]
+            va.phase_event = ev[1].cuda_event if ev else None
+            if ev:
+                ev[0].record(stream)
+            rc = sv.spec_draft_sample_launch(da, sptr)
+            if rc == sv.SPEC_OK:
+                rc = sv.spec_verify_expand_launch(va, xa, sptr)
+            if rc != sv.SPEC_OK:
+                raise sv.SpecError(rc)
+            if ev:
+                ev[2].record(stream)
+
+        accs = []
+        for i in range(PLAN_STEPS):
+            launch(7_000_000 + i, None)
+            torch.cuda.synchronize()
+            accs.extend(acc.cpu().tolist())
+        surv = sv.survival_from_accepted(accs, K)
+        f = 0.0 if way == "stats" else float((temps > 0).mean())  # draft rows the row pass reads
+        mask["m"] = sv.spec_verify_plan_phases(K, surv, f, sv.spec_verify_phase_cost(B, K, V, sv.SPEC_BF16))
+        for i in range(3):
+            launch(8_000_000 + i, None)
+        ms, _, _ = event_steps(torch, stream, launch, steps)
+        read = []
+        for i in range(steps):
+            launch(i, None)
+            a_np = acc.cpu().numpy()
+            t_eff = temps if way == "rows" else np.zeros_like(temps)
+            read.append(phased_logit_bytes(a_np, t_eff, mask["m"], K, V, 2))
+        res[way] = {"phase_starts": mask["m"], "ms_per_round": ms, "positions_per_s": B * K / (ms * 1e-3),
+                    "row_stage_read_bytes": float(np.mean(read)), "mean_accepted": float(acc.float().mean())}
+    del drafter
+    return {"workload": "P-EAGLE round at the headline shape: draft sampling at the new-token indices "
+                        "([%d, %d] bf16 drafter rows), then the chained verify + expand (H=%d)" % (ex.N_out, V, ex.H),
+            "rows": res["rows"], "stats": res["stats"],
+            "speedup": res["rows"]["ms_per_round"] / res["stats"]["ms_per_round"]}
+
+
 def side_configs(sv, torch, np, only, seed):
     import workloads
     dev = torch.device("cuda")
@@ -736,6 +818,7 @@ def main():
         if hmask and hmask != smask:
             line["shard_share_tp4_headline_cut"] = shard_share(sv, torch, inp, args.seed, G=G, phase_starts=hmask)
     if not args.no_configs and args.only == "all":
+        line["peagle_round"] = peagle_round(sv, torch, np, inp, args.seed)
         line["configs"] = side_configs(sv, torch, np, "all", args.seed)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(inp, args.seed, args.cpu_seconds)

@@ -113,6 +113,10 @@ typedef struct {
                                   k >= K_b do not exist (their tokens and rows are never read), a
                                   request that accepts all K_b drafts takes the bonus from target
                                   row K_b; a count outside [0, K] makes the request invalid */
+  const void* draft_stats;     /* device [B, K] records of 16 bytes, or NULL: the statistics of the
+                                  draft rows as spec_draft_sample_launch wrote them (stats_out) when
+                                  it drew draft_tokens from these rows at these temperatures; the
+                                  row statistics then read no draft row (see below) */
 } spec_verify_args;
 
 /* Early exit (same explainer page, section "核心思想": a request stops at
@@ -125,6 +129,21 @@ typedef struct {
  * one-pass result.  Differences: debug_probs of positions in phases after
  * the one where a request stopped are 0 (their rows are never read), and a
  * row without a finite normaliser in such a phase is not detected. */
+
+/* Draft statistics (same explainer page, section "修正拒绝采样": the
+ * accept test needs q only at the drafted token, and its normaliser).  In
+ * the P-EAGLE round the draft tokens are drawn from the drafter's rows by
+ * spec_draft_sample_launch, which reduces every such row to its normaliser
+ * on the way; with draft_stats those records stand in for the row pass over
+ * the draft rows, so the row statistics read the target rows only.  A
+ * sampled request's q row is still read where the request stops (the
+ * residual's weights).  The outputs follow the same method and uniforms;
+ * they can differ from reading the rows only where a decision sits within
+ * rounding of its threshold (the two reductions round differently).  A
+ * record without a finite normaliser makes a sampled request invalid.
+ * Records of greedy requests are not read.  Preconditions: record [b, k]
+ * was written for token draft_tokens[b, k] of draft row k of request b at
+ * temperature[b]. */
 
 /* A phase plan for phase_starts: minimises the expected rows read plus
  * phase_cost per extra phase, over every way of cutting 0..K into phases,
@@ -326,6 +345,12 @@ typedef struct {
   int32_t* tokens;             /* device out [B, K] */
   void* workspace;             /* device scratch, >= spec_draft_workspace_bytes(B, K, V), 16-B aligned */
   size_t workspace_bytes;
+  void* stats_out;             /* device out [B, K] records of 16 bytes, or NULL: for a position drawn
+                                  at T > 0, the row's normaliser S * 2^M of sum_v 2^(x_v * log2(e) / T)
+                                  (float M, integer-valued, at byte 0; double S at byte 8) and the
+                                  drawn token's logit as stored (bf16 bits zero-extended, or fp32
+                                  bits; 4 bytes at byte 4) -- what spec_verify_args.draft_stats
+                                  takes; zeros for T = 0 and for positions given token -1 */
 } spec_draft_args;
 
 /* Bytes of device workspace a draft sampling of this shape needs (0 for an

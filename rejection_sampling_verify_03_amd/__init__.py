@@ -42,7 +42,7 @@ class SpecVerifyArgs(ctypes.Structure):
         ("debug_probs", ctypes.c_void_p), ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
         ("phase_event", ctypes.c_void_p), ("phase_starts", ctypes.c_uint64),
         ("draft_row_index", ctypes.c_void_p), ("draft_rows", ctypes.c_int32),
-        ("num_drafts", ctypes.c_void_p),
+        ("num_drafts", ctypes.c_void_p), ("draft_stats", ctypes.c_void_p),
     ]
 
 
@@ -71,7 +71,11 @@ class SpecDraftArgs(ctypes.Structure):
         ("row_index", ctypes.c_void_p), ("temperature", ctypes.c_void_p),
         ("seed", ctypes.c_uint64), ("step", ctypes.c_uint32), ("request_base", ctypes.c_uint32),
         ("tokens", ctypes.c_void_p), ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
+        ("stats_out", ctypes.c_void_p),
     ]
+
+
+DRAFT_STATS_BYTES = 16  # one record per (request, position)
 
 
 class SpecShardArgs(ctypes.Structure):
@@ -280,7 +284,7 @@ def make_workspace(B, K, V, device="cuda"):
 
 def verify_args(target, draft, draft_tokens, temperature, accepted, tokens, debug, workspace,
                 seed=0, step=0, request_base=0, phase_event=None, phase_starts=0, draft_row_index=None,
-                num_drafts=None):
+                num_drafts=None, draft_stats=None):
     """Fill a SpecVerifyArgs from tensors (no copies).
 
     With draft_row_index [B, K] int32, draft is a 2-D [N, V] buffer (e.g. the
@@ -338,11 +342,18 @@ def verify_args(target, draft, draft_tokens, temperature, accepted, tokens, debu
         a.num_drafts = num_drafts.data_ptr()
     else:
         a.num_drafts = None
+    if draft_stats is not None:
+        _check_dev(draft_stats)
+        if draft_stats.numel() * draft_stats.element_size() < B * K * DRAFT_STATS_BYTES:
+            raise ValueError("draft_stats must hold [B, K] records of %d bytes" % DRAFT_STATS_BYTES)
+        a.draft_stats = draft_stats.data_ptr()
+    else:
+        a.draft_stats = None
     return a
 
 
 def verify(target, draft, draft_tokens, temperature, seed=0, step=0, request_base=0, debug=False,
-           workspace=None, stream=None, phase_starts=0, draft_row_index=None, num_drafts=None):
+           workspace=None, stream=None, phase_starts=0, draft_row_index=None, num_drafts=None, draft_stats=None):
     """One verification step on torch's current stream.  Returns
     (accepted_counts [B] int32, output_tokens [B, K+1] int32, debug_probs
     [B, K, 2] float32 or None)."""
@@ -356,7 +367,7 @@ def verify(target, draft, draft_tokens, temperature, seed=0, step=0, request_bas
     ws = workspace if workspace is not None else make_workspace(B, K, V, dev)
     a = verify_args(target, draft, draft_tokens, temperature, accepted, tokens, dbg, ws, seed, step,
                     request_base, phase_starts=phase_starts, draft_row_index=draft_row_index,
-                    num_drafts=num_drafts)
+                    num_drafts=num_drafts, draft_stats=draft_stats)
     rc = spec_verify_launch(a, _stream_ptr(stream))
     if rc != SPEC_OK:
         raise SpecError(rc)
@@ -449,7 +460,7 @@ def expand(in_token_ids, in_positions, in_start, accepted, bonus, K, mask_id, ta
 
 
 # ------------------------------------------------------------ draft sampling
-def draft_args(logits, row_index, temperature, tokens, workspace, seed=0, step=0, request_base=0):
+def draft_args(logits, row_index, temperature, tokens, workspace, seed=0, step=0, request_base=0, stats_out=None):
     """Fill a SpecDraftArgs: logits [N, V] (unit column stride), row_index
     [B, K] int32, temperature [B] float32, tokens [B, K] int32 out."""
     torch = _torch()
@@ -467,12 +478,26 @@ def draft_args(logits, row_index, temperature, tokens, workspace, seed=0, step=0
     a.seed, a.step, a.request_base = int(seed) & (2 ** 64 - 1), int(step) & 0xFFFFFFFF, int(request_base)
     a.workspace = workspace.data_ptr()
     a.workspace_bytes = workspace.numel() * workspace.element_size()
+    if stats_out is not None:
+        _check_dev(stats_out)
+        if stats_out.numel() * stats_out.element_size() < B * K * DRAFT_STATS_BYTES:
+            raise ValueError("stats_out must hold [B, K] records of %d bytes" % DRAFT_STATS_BYTES)
+        a.stats_out = stats_out.data_ptr()
+    else:
+        a.stats_out = None
     return a
 
 
-def draft_sample(logits, row_index, temperature, seed=0, step=0, request_base=0, workspace=None, stream=None):
+def draft_stats_buffer(B, K, device="cuda"):
+    """Device memory for the [B, K] draft statistics records."""
+    return _torch().empty(B * K * DRAFT_STATS_BYTES, dtype=_torch().uint8, device=device)
+
+
+def draft_sample(logits, row_index, temperature, seed=0, step=0, request_base=0, workspace=None, stream=None,
+                 stats_out=None):
     """Draft tokens [B, K] int32 sampled at rows row_index of logits, on
-    torch's current stream."""
+    torch's current stream (and, with stats_out, the rows' statistics for
+    the verification of these tokens)."""
     torch = _torch()
     B, K = row_index.shape
     dev = logits.device
@@ -480,7 +505,7 @@ def draft_sample(logits, row_index, temperature, seed=0, step=0, request_base=0,
     if workspace is None:
         workspace = torch.empty(max(spec_draft_workspace_bytes(B, K, logits.shape[1]), 16), dtype=torch.uint8,
                                 device=dev)
-    a = draft_args(logits, row_index, temperature, tokens, workspace, seed, step, request_base)
+    a = draft_args(logits, row_index, temperature, tokens, workspace, seed, step, request_base, stats_out)
     rc = spec_draft_sample_launch(a, _stream_ptr(stream))
     if rc != SPEC_OK:
         raise SpecError(rc)

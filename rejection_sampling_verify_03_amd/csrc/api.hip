@@ -280,6 +280,7 @@ int spec_draft_sample_launch(const spec_draft_args* a, hipStream_t stream) {
   P.request_base = a->request_base;
   P.tokens = a->tokens;
   P.segp = static_cast<RowPartial*>(a->workspace);
+  P.stats = static_cast<RowPartial*>(a->stats_out);
   const bool vec = aligned16(a->logits) && (a->row_stride * es) % 16 == 0;
   return launch_draft(P, a->dtype, vec, stream) == hipSuccess ? SPEC_OK : SPEC_ELAUNCH;
 }
@@ -350,6 +351,7 @@ static VerifyParams verify_params(const spec_verify_args* a, bool& vec) {
   P.d_row = a->d_row_stride;
   P.dridx = a->draft_row_index;
   P.num_drafts = a->num_drafts;
+  P.dstats = static_cast<const RowPartial*>(a->draft_stats);
   P.draft_rows = a->draft_row_index ? a->draft_rows : 0;
   P.tokens = a->draft_tokens;
   P.temperature = a->temperature;
@@ -368,7 +370,7 @@ static VerifyParams verify_params(const spec_verify_args* a, bool& vec) {
         (a->draft_row_index || (a->d_req_stride * es) % 16 == 0);
   P.err = reinterpret_cast<int32_t*>(ws + L.off_err);
   P.state = reinterpret_cast<int32_t*>(ws + L.off_state);
-  P.ph_lo = P.ph_nt = P.ph_nd = P.ph_check = 0;
+  P.ph_lo = P.ph_nt = P.ph_nd = P.ph_rd = P.ph_check = 0;
   P.last_lo = P.phased = 0;
   P.ex_on = 0;
   P.ex_G = 1;

@@ -28,7 +28,9 @@
 //      lane, in vocabulary order).  The wave is one chain of dependent
 //      steps, so the segment records load with the row index, the segment's
 //      64 logits per lane load together, and lanes exchange values through
-//      DPP moves and readlane rather than LDS permutes.
+//      DPP moves and readlane rather than LDS permutes.  On request it also
+//      writes the row's normaliser W * 2^M* and the drawn token's logit: the
+//      statistics the next verification takes instead of reading the row.
 #include <limits.h>
 
 #include "device_common.hpp"
@@ -155,22 +157,32 @@ __global__ __launch_bounds__(64) void draft_draw_kernel(DraftParams P) {
   const int nseg = P.nseg;
   RowPartial r0{-INFINITY, INT_MAX, 0.0};
   if (lane < nseg) r0 = sp[lane];
+  const RowPartial none{0.f, 0, 0.0};  // the statistics record of a position drawn at T = 0 or given -1
   if (!draft_row_valid(P, row, T)) {
-    if (lane == 0) P.tokens[i] = -1;
+    if (lane == 0) {
+      P.tokens[i] = -1;
+      if (P.stats) P.stats[i] = none;
+    }
     return;
   }
   if (T == 0.0f) {
     VI best{r0.m, r0.idx};
     for (int j = lane + 64; j < nseg; j += 64) best = vi_pick(best, VI{sp[j].m, sp[j].idx});
     best = wave_argmax(best);
-    if (lane == 0) P.tokens[i] = best.i;
+    if (lane == 0) {
+      P.tokens[i] = best.i;
+      if (P.stats) P.stats[i] = none;
+    }
     return;
   }
   float Mstar = r0.m;
   for (int j = lane + 64; j < nseg; j += 64) Mstar = fmaxf(Mstar, sp[j].m);
   Mstar = wave_max_f(Mstar);
   if (!(fabsf(Mstar) <= FLT_MAX)) {  // no finite logit in the row
-    if (lane == 0) P.tokens[i] = -1;
+    if (lane == 0) {
+      P.tokens[i] = -1;
+      if (P.stats) P.stats[i] = none;
+    }
     return;
   }
   const uint32_t k0 = (uint32_t)(P.seed & 0xffffffffu), k1 = (uint32_t)(P.seed >> 32);
@@ -266,7 +278,20 @@ __global__ __launch_bounds__(64) void draft_draw_kernel(DraftParams P) {
     }
     y = pick;
   }
-  if (lane == 0) P.tokens[i] = y;
+  if (lane == 0) {
+    P.tokens[i] = y;
+    // the row's normaliser W * 2^M* and the drawn logit, for a verification
+    // of this token against this row (the draft row statistics it takes)
+    if (P.stats) {
+      RowPartial rec = none;
+      if (y >= 0) {
+        rec.m = Mstar;
+        rec.idx = (int32_t)load_bits<ES>(P.logits + (int64_t)row * P.row_stride * ES, y);
+        rec.s = W;
+      }
+      P.stats[i] = rec;
+    }
+  }
 }
 
 template <int ES, bool VEC>

@@ -176,8 +176,13 @@ __device__ int decide_tests(const VerifyParams& P, int b, int lo, int hi, int th
   const int k = tid < nt ? r : r - K - 1;  // position of the row
   const RowPartial* rp = P.rowp + ((int64_t)b * P.R + (row_thread ? r : 0)) * P.C1;
   const int xr = P.tokens[(int64_t)b * K + min(k, K - 1)];
+  // with draft statistics a draft row is its sampler's record, not partials
+  const bool stat_row = P.dstats != nullptr && tid >= nt;
   RowPartial q[kPartBatch];
-  if (row_thread) load_partials(rp, 0, P.C1, q);
+  if (row_thread) {
+    if (stat_row) q[0] = P.dstats[(int64_t)b * K + min(k, K - 1)];
+    else load_partials(rp, 0, P.C1, q);
+  }
 
   const int dix = draft_entry(P, b, tid);
   const bool greedy = (T == 0.0f);
@@ -198,7 +203,12 @@ __device__ int decide_tests(const VerifyParams& P, int b, int lo, int hi, int th
       merge_row<ES, true>(P, rp, q, -1, ms, vi, z);
       sh.g[r] = vi.i;
     } else {
-      merge_row<ES, false>(P, rp, q, k < kb ? xr : -1, ms, vi, z);
+      if (stat_row) {
+        ms = MS{q[0].m, q[0].s};
+        z = bits_to_logit<ES>((uint32_t)q[0].idx);
+      } else {
+        merge_row<ES, false>(P, rp, q, k < kb ? xr : -1, ms, vi, z);
+      }
       sh.m[r] = ms.m;
       sh.s[r] = ms.s;
       sh.z[r] = z;
@@ -331,7 +341,7 @@ __global__ __launch_bounds__(kWG) void verify_phase_kernel(VerifyParams P) {
 
 template <int ES, bool VEC>
 __global__ __launch_bounds__(kWG) void verify_rowstats_kernel(VerifyParams P) {
-  const int nr = P.ph_nt + P.ph_nd;
+  const int nr = P.ph_nt + P.ph_rd;
   const int c = blockIdx.x % P.C1;
   const int lr = (blockIdx.x / P.C1) % nr;
   const int b = blockIdx.x / (P.C1 * nr);
@@ -573,8 +583,9 @@ static hipError_t launch_typed(VerifyParams P, uint64_t phase_starts, hipEvent_t
     P.ph_lo = lo;
     P.ph_nt = hi - lo;
     P.ph_nd = min(hi, K) - lo;
+    P.ph_rd = P.dstats ? 0 : P.ph_nd;  // with draft statistics the draft rows are not read here
     P.ph_check = j > 0;
-    const int64_t g1 = (int64_t)P.B * (P.ph_nt + P.ph_nd) * P.C1;
+    const int64_t g1 = (int64_t)P.B * (P.ph_nt + P.ph_rd) * P.C1;
     hipLaunchKernelGGL((verify_rowstats_kernel<ES, VEC>), dim3((unsigned)g1), dim3(kWG), 0, stream, P);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

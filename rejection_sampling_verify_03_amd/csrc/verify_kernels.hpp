@@ -45,6 +45,7 @@ struct VerifyParams {
   const int32_t* dridx;  // draft row table [B, K] (rows of a [draft_rows, V] buffer) or null
   int32_t draft_rows;
   const int32_t* num_drafts;  // ragged draft counts [B] or null (all K)
+  const RowPartial* dstats;   // draft row statistics [B, K] from the draft sampler, or null
   const int32_t* tokens;
   const float* temperature;
   uint64_t seed;
@@ -58,8 +59,9 @@ struct VerifyParams {
   int32_t* err;    // count of invalid requests of this verification
   int32_t* state;  // per-request state between early-exit phases
   // rows of one early-exit phase: target rows [ph_lo, ph_lo + ph_nt), draft
-  // rows [ph_lo, ph_lo + ph_nd); ph_check: skip requests no longer alive
-  int32_t ph_lo, ph_nt, ph_nd, ph_check;
+  // rows [ph_lo, ph_lo + ph_nd), of which the row pass reads the first ph_rd
+  // (none with draft statistics); ph_check: skip requests no longer alive
+  int32_t ph_lo, ph_nt, ph_nd, ph_rd, ph_check;
   // start of the last phase when the rows were read in several phases, else 0
   int32_t last_lo, phased;
   // a chained expansion of this verification's outputs, folded into its
@@ -79,6 +81,7 @@ struct DraftParams {
   uint32_t step, request_base;
   int32_t* tokens;
   RowPartial* segp;  // per (request, position, segment) statistics [B * K * nseg]
+  RowPartial* stats; // per (request, position): the row's normaliser and the drawn logit, or null
 };
 
 constexpr int kDraftChunkSegs = 8;  // segments per workgroup of the statistics pass

@@ -242,3 +242,94 @@ def test_peagle_loop_on_device(sv):
     a = acc.cpu().numpy()
     say("  accepted per request: mean %.2f" % a.mean())
     assert (a >= 0).all()
+
+
+def _drafter_buffer(vin, seed):
+    """The draft rows of `vin` placed at random rows of a larger drafter
+    buffer [N, V] (as the drafter's logits at the new-token indices)."""
+    B, K, V = vin.B, vin.K, vin.V
+    g = torch.Generator(device="cuda").manual_seed(seed)
+    N = B * K + 11
+    perm = torch.randperm(N, generator=g, device="cuda")[:B * K]
+    buf = torch.zeros(N, V, dtype=vin.draft.dtype, device="cuda")
+    buf[perm] = vin.draft[:, :K].reshape(B * K, V)
+    return buf, perm.reshape(B, K).to(torch.int32).contiguous()
+
+
+@pytest.mark.parametrize("dtype,V", [(torch.bfloat16, 50000), (torch.float32, 33000), (torch.bfloat16, 151936)])
+def test_verify_with_draft_stats(sv, dtype, V):
+    """The P-EAGLE round with the sampler's row statistics handed to the
+    verification: draft tokens drawn from drafter rows (with stats_out),
+    then their verification against those rows reading the statistics
+    instead of the rows -- every request against the oracle (bar of
+    parity.py, debug probabilities included), phased bit-identical to one
+    pass, and the same outputs as reading the rows but where a decision
+    sits within rounding of its threshold."""
+    from parity import Report, compare
+    say("case: verification from the sampler's draft statistics, V%d %s" % (V, dtype))
+    B, K = 24, 6
+    vin = workloads.mixture_inputs("stats", B, K, V, dtype, V % 89, "cuda", temps=(0.0, 0.6, 1.0),
+                                   lam_lo=0.05, lam_hi=0.6)
+    buf, ridx = _drafter_buffer(vin, 3)
+    tl, dl = workloads.logits_numpy(vin.target), workloads.logits_numpy(vin.draft)
+    T = vin.temperature
+    rep = Report()
+    same = 0
+    for step in range(3):
+        stats = sv.draft_stats_buffer(B, K)
+        x = sv.draft_sample(buf, ridx, T, seed=3, step=step, stats_out=stats)
+        a1, t1, d1 = sv.verify(vin.target, buf, x, T, seed=5, step=step, draft_row_index=ridx, draft_stats=stats,
+                               debug=True)
+        a2, t2, _ = sv.verify(vin.target, buf, x, T, seed=5, step=step, draft_row_index=ridx, draft_stats=stats,
+                              phase_starts=0b100100)
+        a3, t3, _ = sv.verify(vin.target, buf, x, T, seed=5, step=step, draft_row_index=ridx)
+        torch.cuda.synchronize()
+        assert torch.equal(a1, a2) and torch.equal(t1, t2), step
+        same += int(((a1 == a3) & (t1 == t3).all(dim=1)).sum())
+        compare(tl, dl, x.cpu().numpy(), T.cpu().numpy(), a1.cpu().numpy(), t1.cpu().numpy(), d1.cpu().numpy(),
+                seed=5, step=step, report=rep)
+    say("  %s; %d of %d request-steps identical to reading the rows" % (rep.summary(), same, 3 * B))
+    assert rep.ok(), rep.failures[:5]
+    assert same >= 3 * B - len(rep.near) - 1
+
+
+def test_draft_stats_records(sv):
+    """The records themselves: for a sampled position the normaliser of the
+    row at the request's temperature in (M, S) form and the drawn token's
+    logit; zeros for greedy positions and for positions given -1; a record
+    without a finite normaliser makes the verification's request invalid."""
+    say("case: draft statistics records")
+    B, K, V = 6, 3, 5000
+    vin = workloads.mixture_inputs("stats rec", B, K, V, torch.float32, 8, "cuda", temps=(0.0, 0.7, 1.3),
+                                   lam_lo=0.1, lam_hi=0.5)
+    buf, ridx = _drafter_buffer(vin, 4)
+    ridx_bad = ridx.clone()
+    ridx_bad[0, 2] = buf.shape[0] + 5  # outside the buffer: token -1, zero record
+    stats = sv.draft_stats_buffer(B, K)
+    x = sv.draft_sample(buf, ridx_bad, vin.temperature, seed=1, stats_out=stats)
+    torch.cuda.synchronize()
+    raw = stats.cpu().numpy().reshape(B, K, 16)
+    m = raw[:, :, 0:4].copy().view(np.float32)[..., 0]
+    zb = raw[:, :, 4:8].copy().view(np.uint32)[..., 0]
+    s = raw[:, :, 8:16].copy().view(np.float64)[..., 0]
+    T = vin.temperature.cpu().numpy()
+    lg = buf.cpu().numpy().astype(np.float64)
+    xs = x.cpu().numpy()
+    for b in range(B):
+        for k in range(K):
+            if T[b] == 0.0 or xs[b, k] < 0:
+                assert m[b, k] == 0 and zb[b, k] == 0 and s[b, k] == 0, (b, k)
+                continue
+            row = lg[ridx_bad[b, k].item()]
+            want = np.sum(np.exp2(row * (np.log2(np.e) / T[b]) - m[b, k]))
+            assert abs(s[b, k] / want - 1) < 1e-6, (b, k)
+            assert np.float32(zb[b, k].view(np.float32)) == np.float32(row[xs[b, k]]), (b, k)
+    assert xs[0, 2] == -1
+    # a record without a finite normaliser: that sampled request is invalid
+    bad = stats.clone()
+    sampled = [b for b in range(B) if T[b] > 0 and (xs[b] >= 0).all()]
+    vb = sampled[0]
+    bad.view(B, K, 16)[vb, 1, 8:16] = 0
+    a, t, _ = sv.verify(vin.target, buf, x, vin.temperature, draft_row_index=ridx_bad, draft_stats=bad)
+    a = a.cpu().numpy()
+    assert a[vb] == -1
