@@ -34,7 +34,7 @@ typedef enum {
   SPEC_OK = 0,
   SPEC_EINVAL = -1,     /* null pointer, size or stride out of range */
   SPEC_EDTYPE = -2,     /* unknown logits dtype */
-  SPEC_EALIGN = -3,     /* workspace not 16-byte aligned */
+  SPEC_EALIGN = -3,     /* workspace (or a statistics record array) not 16-byte aligned */
   SPEC_EWORKSPACE = -4, /* workspace smaller than spec_verify_workspace_bytes() */
   SPEC_ELAUNCH = -5     /* the HIP runtime refused a launch */
 } spec_status;
@@ -113,7 +113,7 @@ typedef struct {
                                   k >= K_b do not exist (their tokens and rows are never read), a
                                   request that accepts all K_b drafts takes the bonus from target
                                   row K_b; a count outside [0, K] makes the request invalid */
-  const void* draft_stats;     /* device [B, K] records of 16 bytes, or NULL: the statistics of the
+  const void* draft_stats;     /* device [B, K] records of 16 bytes (16-byte aligned), or NULL: the statistics of the
                                   draft rows as spec_draft_sample_launch wrote them (stats_out) when
                                   it drew draft_tokens from these rows at these temperatures; the
                                   row statistics then read no draft row (see below) */
@@ -345,7 +345,7 @@ typedef struct {
   int32_t* tokens;             /* device out [B, K] */
   void* workspace;             /* device scratch, >= spec_draft_workspace_bytes(B, K, V), 16-B aligned */
   size_t workspace_bytes;
-  void* stats_out;             /* device out [B, K] records of 16 bytes, or NULL: for a position drawn
+  void* stats_out;             /* device out [B, K] records of 16 bytes (16-byte aligned), or NULL: for a position drawn
                                   at T > 0, the row's normaliser S * 2^M of sum_v 2^(x_v * log2(e) / T)
                                   (float M, integer-valued, at byte 0; double S at byte 8) and the
                                   drawn token's logit as stored (bf16 bits zero-extended, or fp32

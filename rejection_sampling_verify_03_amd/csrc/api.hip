@@ -64,7 +64,7 @@ int verify_check(const spec_verify_args* a) {
   if (a->draft_row_index && a->draft_rows < 0) return SPEC_EINVAL;
   const Layout L = make_layout(a->B, a->K, a->V);
   if ((int64_t)a->B * L.R * L.C1 > INT32_MAX || (int64_t)a->B * L.nseg > INT32_MAX) return SPEC_EINVAL;
-  if (!aligned16(a->workspace)) return SPEC_EALIGN;
+  if (!aligned16(a->workspace) || (a->draft_stats && !aligned16(a->draft_stats))) return SPEC_EALIGN;
   if (a->phase_starts & 1u) return SPEC_EINVAL;  // position 0 always starts the first phase
   if (a->K < 63 && (a->phase_starts >> (a->K + 1)) != 0) return SPEC_EINVAL;
   if (a->workspace_bytes < L.total) return SPEC_EWORKSPACE;
@@ -108,7 +108,7 @@ int draft_check(const spec_draft_args* a) {
   const int64_t nseg = ((int64_t)a->V + kSeg - 1) / kSeg;
   const int64_t C = (nseg + kDraftChunkSegs - 1) / kDraftChunkSegs;
   if ((int64_t)a->B * a->K * C > INT32_MAX) return SPEC_EINVAL;
-  if (!aligned16(a->workspace)) return SPEC_EALIGN;
+  if (!aligned16(a->workspace) || (a->stats_out && !aligned16(a->stats_out))) return SPEC_EALIGN;
   if (a->workspace_bytes < draft_ws_bytes(a->B, a->K, a->V)) return SPEC_EWORKSPACE;
   return SPEC_OK;
 }
@@ -512,7 +512,7 @@ const char* spec_status_string(int status) {
     case SPEC_OK: return "SPEC_OK";
     case SPEC_EINVAL: return "SPEC_EINVAL: invalid argument (null pointer, size or stride out of range)";
     case SPEC_EDTYPE: return "SPEC_EDTYPE: unknown logits dtype";
-    case SPEC_EALIGN: return "SPEC_EALIGN: workspace not 16-byte aligned";
+    case SPEC_EALIGN: return "SPEC_EALIGN: workspace or statistics records not 16-byte aligned";
     case SPEC_EWORKSPACE: return "SPEC_EWORKSPACE: workspace too small";
     case SPEC_ELAUNCH: return "SPEC_ELAUNCH: kernel launch failed";
     default: return "unknown spec_status";

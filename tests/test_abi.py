@@ -103,7 +103,8 @@ def test_verify_argument_errors(sv):
                                ("t_req_stride", 64, sv.SPEC_EINVAL), ("d_req_stride", 5, sv.SPEC_EINVAL),
                                ("target_logits", None, sv.SPEC_EINVAL), ("draft_tokens", None, sv.SPEC_EINVAL),
                                ("temperature", None, sv.SPEC_EINVAL), ("workspace", None, sv.SPEC_EINVAL),
-                               ("output_tokens", None, sv.SPEC_EINVAL), ("workspace", 0x10008, sv.SPEC_EALIGN)]:
+                               ("output_tokens", None, sv.SPEC_EINVAL), ("workspace", 0x10008, sv.SPEC_EALIGN),
+                               ("draft_stats", 0x10008, sv.SPEC_EALIGN), ("draft_stats", 0x10010, sv.SPEC_EWORKSPACE)]:
         a = _valid_verify_args(sv)
         setattr(a, field, value)
         assert launch(a) == want, (field, value)
@@ -255,7 +256,8 @@ def test_draft_argument_errors(sv):
                                ("row_stride", 99, sv.SPEC_EINVAL), ("row_index", None, sv.SPEC_EINVAL),
                                ("temperature", None, sv.SPEC_EINVAL), ("tokens", None, sv.SPEC_EINVAL),
                                ("logits", None, sv.SPEC_EINVAL), ("workspace", None, sv.SPEC_EINVAL),
-                               ("workspace", 0x10004, sv.SPEC_EALIGN)]:
+                               ("workspace", 0x10004, sv.SPEC_EALIGN), ("stats_out", 0x10004, sv.SPEC_EALIGN),
+                               ("stats_out", 0x10010, sv.SPEC_EWORKSPACE)]:
         a = args()
         setattr(a, field, value)
         assert launch(a) == want, (field, value)
