@@ -73,3 +73,41 @@ def test_noalloc_refuses_shapes_beyond_its_array(sv):
     assert sv.spec_verify_launch_noalloc(a, torch.cuda.current_stream().cuda_stream) == sv.SPEC_EWORKSPACE
     torch.cuda.synchronize()
     assert (acc == -7).all() and (tok == -7).all()  # nothing was enqueued
+
+
+def test_noalloc_under_graph_capture(sv):
+    """The caller it is for: a verification captured in a HIP graph with no
+    allocation inside the capture (the workspace is the library's own array)
+    and replayed four times, with eager work and an output reset between the
+    replays; every replay equals the eager call, phased and one pass."""
+    say("case: no-alloc verify captured in a graph")
+    inp = workloads.mixture_inputs("graph", 32, 8, 32768, torch.bfloat16, 21, "cuda", temps=(0.0, 0.6, 1.0),
+                                   lam_lo=0.05, lam_hi=0.6)
+    B, K = 32, 8
+    for cut in (0, 0b100100):
+        acc = torch.empty(B, dtype=torch.int32, device="cuda")
+        tok = torch.empty(B, K + 1, dtype=torch.int32, device="cuda")
+        a = sv.verify_args(inp.target, inp.draft, inp.draft_tokens, inp.temperature, acc, tok, None, None,
+                           seed=4, step=9, phase_starts=cut)
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            assert sv.spec_verify_launch_noalloc(a, s.cuda_stream) == sv.SPEC_OK
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        eager = (acc.clone(), tok.clone())
+        g = torch.cuda.CUDAGraph()
+        acc.fill_(-5)
+        tok.fill_(-5)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g):
+            assert sv.spec_verify_launch_noalloc(a, torch.cuda.current_stream().cuda_stream) == sv.SPEC_OK
+        for rep in range(4):
+            x = torch.randn(1 << 20, device="cuda")
+            float(x.sum())
+            acc.fill_(-5)
+            tok.fill_(-5)
+            g.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(acc, eager[0]) and torch.equal(tok, eager[1]), (cut, rep)
+        say("  cut %#x: 4 replays identical to the eager call" % cut)
