@@ -23,7 +23,10 @@
  * iff p(x) > 0; the same temperature divides both logits; argmax ties go to
  * the lowest index; a residual that sums to exactly zero falls back to p; the
  * inverse CDF runs in ascending vocabulary order over the weights with their
- * own sum as normaliser.
+ * own sum as normaliser; a sampled request whose rows at a position it
+ * reaches (target and draft row of a tested position, the target row of the
+ * bonus) lack a finite maximum is invalid, and rows after its stop are never
+ * looked at.
  *
  * Everything is computed in double, sequentially, with no blocking or
  * reordering beyond the definitions above.
@@ -169,10 +172,9 @@ static int row_has_finite_max(const void* row, int dtype, int V) {
 /* Drafts of request b: K, or its entry of the ragged table. */
 static int drafts_of(const oracle_verify_args* a, int b) { return a->num_drafts ? a->num_drafts[b] : a->K; }
 
-/* Data checks made before any decision: a draft count in [0, K], every token
- * id in range, a usable temperature, and for sampled requests a finite
- * maximum in every row the parallel formulation reads (target rows 0..K_b,
- * draft rows 0..K_b-1). */
+/* Data checks made before any decision, on the inputs alone: a draft count
+ * in [0, K], every token id in range and a usable temperature.  The rows are
+ * checked as the method reaches them (rows_usable). */
 static int request_valid(const oracle_verify_args* a, int b) {
   const int Kb = drafts_of(a, b);
   if (Kb < 0 || Kb > a->K) return 0;
@@ -181,13 +183,17 @@ static int request_valid(const oracle_verify_args* a, int b) {
     if (x[k] < 0 || x[k] >= a->V) return 0;
   float T = a->temperature[b];
   if (!(T >= 0.0f) || isinf(T)) return 0;
-  if (T > 0.0f) {
-    for (int k = 0; k <= Kb; ++k)
-      if (!row_has_finite_max(trow(a, b, k), a->dtype, a->V)) return 0;
-    for (int k = 0; k < Kb; ++k)
-      if (!row_has_finite_max(drow(a, b, k), a->dtype, a->V)) return 0;
-  }
   return 1;
+}
+
+/* The rows a sampled request reads at position k (explainer page, section
+ * "核心思想": the verification walks the positions in order and stops at the
+ * first rejection, so a row after the stop is never read): target row k, and
+ * draft row k when k < K_b (k = K_b is the bonus row, target only).  Each
+ * needs a finite maximum for its softmax to exist. */
+static int rows_usable(const oracle_verify_args* a, int b, int k, int Kb) {
+  if (!row_has_finite_max(trow(a, b, k), a->dtype, a->V)) return 0;
+  return k == Kb || row_has_finite_max(drow(a, b, k), a->dtype, a->V);
 }
 
 static void sampling_weights(const oracle_verify_args* a, int b, int j, double* p, double* q,
@@ -209,6 +215,18 @@ static void sampling_weights(const oracle_verify_args* a, int b, int j, double* 
   oracle_residual(p, q, a->V, w, W);
 }
 
+/* Request b's data is invalid: accepted = -1, every output token -1, debug 0. */
+static int invalid_request(const oracle_verify_args* a, int b) {
+  int32_t* out = a->out_tokens + (int64_t)b * (a->K + 1);
+  for (int k = 0; k <= a->K; ++k) out[k] = -1;
+  if (a->debug_probs)
+    for (int i = 0; i < 2 * a->K; ++i) a->debug_probs[(int64_t)b * a->K * 2 + i] = 0.0f;
+  if (a->trace)
+    for (int i = 0; i < (a->K + 1) * 3; ++i) a->trace[(int64_t)b * (a->K + 1) * 3 + i] = NAN;
+  a->accepted[b] = -1;
+  return 1;
+}
+
 static int verify_one(const oracle_verify_args* a, int b, double* p, double* q, double* w) {
   int K = a->K;
   const int V = a->V;
@@ -221,10 +239,7 @@ static int verify_one(const oracle_verify_args* a, int b, double* p, double* q, 
   if (a->debug_probs)
     for (int i = 0; i < 2 * K; ++i) a->debug_probs[(int64_t)b * K * 2 + i] = 0.0f;
 
-  if (!request_valid(a, b)) {
-    a->accepted[b] = -1;
-    return 1;
-  }
+  if (!request_valid(a, b)) return invalid_request(a, b);
   const double T = (double)a->temperature[b];
   K = drafts_of(a, b); /* positions k >= K_b do not exist; the bonus row is K_b */
 
@@ -244,7 +259,10 @@ static int verify_one(const oracle_verify_args* a, int b, double* p, double* q, 
   }
 
   if (a->debug_probs) {
+    /* every position's p_k(x_k), q_k(x_k), the parallel formulation's view
+     * (0 where a row has no finite maximum) */
     for (int k = 0; k < K; ++k) {
+      if (!rows_usable(a, b, k, K)) continue;
       oracle_softmax(trow(a, b, k), a->dtype, V, T, p);
       oracle_softmax(drow(a, b, k), a->dtype, V, T, q);
       a->debug_probs[((int64_t)b * a->K + k) * 2 + 0] = (float)p[x[k]];
@@ -253,6 +271,7 @@ static int verify_one(const oracle_verify_args* a, int b, double* p, double* q, 
   }
 
   for (int k = 0; k < K; ++k) {
+    if (!rows_usable(a, b, k, K)) return invalid_request(a, b);
     oracle_softmax(trow(a, b, k), a->dtype, V, T, p);
     oracle_softmax(drow(a, b, k), a->dtype, V, T, q);
     double ua, us;
@@ -288,6 +307,7 @@ static int verify_one(const oracle_verify_args* a, int b, double* p, double* q, 
   }
 
   /* all K drafts accepted: the bonus token is sampled from p at row K */
+  if (!rows_usable(a, b, K, K)) return invalid_request(a, b);
   oracle_softmax(trow(a, b, K), a->dtype, V, T, p);
   double ua, us, W = 0.0;
   uniforms_for(a, b, K, &ua, &us);
@@ -337,6 +357,7 @@ int oracle_sampling_weights(const oracle_verify_args* a, int b, int j, double* w
   if (!a->target || !a->draft || !a->draft_tokens || !a->temperature || !w || !W) return -1;
   if (b < 0 || b >= a->B || j < 0 || j > a->K) return -1;
   if (!request_valid(a, b) || !(a->temperature[b] > 0.0f) || j > drafts_of(a, b)) return -1;
+  if (!rows_usable(a, b, j, drafts_of(a, b))) return -1;
   double* p = (double*)malloc(sizeof(double) * (size_t)a->V);
   double* q = (double*)malloc(sizeof(double) * (size_t)a->V);
   sampling_weights(a, b, j, p, q, w, W);

@@ -121,12 +121,49 @@ def test_invalid_requests_are_flagged():
     x[1, 2] = V          # token out of range
     x[2, 0] = -1         # negative token
     T[3] = -1.0          # negative temperature
-    t[4, 1, :] = -np.inf  # a row with no finite maximum (sampled request)
+    t[4, 0, :] = -np.inf  # a row every sampled request reads, with no finite maximum
     r = oracle.verify(t, t, x, T)
     assert r.n_bad == 4
     assert r.accepted[0] == K
     for b in range(1, 5):
-        assert r.accepted[b] == -1 and (r.tokens[b] == -1).all()
+        assert r.accepted[b] == -1 and (r.tokens[b] == -1).all() and (r.debug_probs[b] == 0).all()
+
+
+def test_rows_after_the_stop_are_never_read():
+    """The verification walks the positions in order and stops at the first
+    rejection (explainer page, section "核心思想"), so a row past the stop
+    has no say, while a row at the stop, or the bonus row, does.  Position 0
+    rejects with certainty (the draft token lies outside the target's
+    support), so the rows of positions 1..K may be anything; the residual is
+    then p_0 itself.  When every draft is accepted (identical rows) the bonus
+    row K_b is read."""
+    rng = np.random.default_rng(11)
+    B, K, V = 6, 3, 12
+    t = np.full((B, K + 1, V), -np.inf, np.float32)
+    d = np.full((B, K + 1, V), -np.inf, np.float32)
+    t[:, 0, :6] = rng.standard_normal((B, 6))
+    d[:, 0, 6:] = rng.standard_normal((B, 6))
+    x = rng.integers(6, V, (B, K)).astype(np.int32)  # p_0(x_0) = 0: rejected
+    T = np.full(B, 0.8, np.float32)
+    t[1, 2, 3] = np.nan  # a NaN past the stop
+    t[2, 0, :] = -np.inf  # no finite maximum at the stop: invalid
+    d[3, 0, :] = -np.inf  # the draft row at the stop: invalid
+    r = oracle.verify(t, d, x, T, seed=5)
+    assert list(r.accepted) == [0, 0, -1, -1, 0, 0]
+    for b in (0, 1, 4, 5):
+        assert 0 <= r.tokens[b, 0] < 6 and (r.tokens[b, 1:] == -1).all()
+        assert r.debug_probs[b, 0, 0] == 0.0 and r.debug_probs[b, 0, 1] > 0.0  # p_0(x_0) = 0 < q_0(x_0)
+        assert (r.debug_probs[b, 1:] == 0).all()  # positions whose rows have no finite maximum
+    assert (r.tokens[2] == -1).all() and (r.tokens[3] == -1).all()
+    # identical rows accept everything; the bonus row K_b must be usable
+    u = rng.standard_normal((B, K + 1, V)).astype(np.float32)
+    xs = rng.integers(0, V, (B, K)).astype(np.int32)
+    nd = np.array([3, 3, 2, 2, 0, 0], np.int32)
+    u[1, 3, :] = -np.inf  # request 1's bonus row (K_b = 3)
+    u[3, 3, :] = -np.inf  # past request 3's bonus row (K_b = 2): never read
+    u[5, 0, :] = -np.inf  # request 5's bonus row (K_b = 0)
+    r = oracle.verify(u, u, xs, np.ones(B, np.float32), seed=6, num_drafts=nd)
+    assert list(r.accepted) == [3, -1, 2, 2, 0, -1]
 
 
 def test_request_base_reproduces_a_shard():
