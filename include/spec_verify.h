@@ -41,6 +41,10 @@ typedef enum {
 
 typedef enum { SPEC_F32 = 0, SPEC_BF16 = 1 } spec_dtype;
 
+/* spec_verify_args.phase_starts value selecting the dynamic early exit (the
+ * row pass takes the decisions as it goes; see "Early exit" below). */
+#define SPEC_PHASES_DYNAMIC 1ull
+
 /* Largest number of drafts per request (one 64-lane wavefront ballot). */
 #define SPEC_MAX_K 63
 
@@ -76,7 +80,8 @@ typedef enum { SPEC_F32 = 0, SPEC_BF16 = 1 } spec_dtype;
  * Preconditions on the data (not checked): logits are not NaN or +inf and
  * |logit| / T_b < 2^100; every row of a sampled request has a finite maximum
  * (violations are detected where they make a row's normaliser non-finite or
- * zero, and reported as a data error).
+ * zero, and reported as a data error when the request reaches that row: the
+ * target and draft row of a position it tests, or its bonus row).
  */
 typedef struct {
   int32_t B;                   /* requests, >= 0 */
@@ -102,7 +107,8 @@ typedef struct {
   void* phase_event;           /* hipEvent_t or NULL: recorded on `stream` right after the
                                   row-statistics stage (to time it apart from the rest) */
   uint64_t phase_starts;       /* early exit: bit k (1 <= k <= K) starts a new phase at draft
-                                  position k; 0 = one pass over every row (see below) */
+                                  position k; 0 = one pass over every row;
+                                  SPEC_PHASES_DYNAMIC = decisions inside the row pass (see below) */
   const int32_t* draft_row_index; /* device [B, K] or NULL: draft row k of request b is row
                                   draft_row_index[b*K + k] of a [draft_rows, V] buffer at
                                   draft_logits (row stride d_row_stride; d_req_stride unused),
@@ -125,10 +131,18 @@ typedef struct {
  * the rows of a phase (target rows k and, for sampled requests, draft rows k
  * of its positions) are read only for requests whose drafts before the phase
  * were all accepted, and a small kernel between phases runs the phase's
- * accept tests.  accepted_counts and output_tokens are identical to the
- * one-pass result.  Differences: debug_probs of positions in phases after
- * the one where a request stopped are 0 (their rows are never read), and a
- * row without a finite normaliser in such a phase is not detected. */
+ * accept tests.  With phase_starts == SPEC_PHASES_DYNAMIC there is one row
+ * pass, ordered by position, and workgroups inside it run the accept tests
+ * of each request as the records of its rows come in, so that the rows of a
+ * request past its stop are mostly never read; no plan is needed, and how
+ * many rows are skipped depends on timing, not the outputs: the final
+ * decision recomputes every test from the rows read, and a request's rows up
+ * to its stop are always read.  In every mode accepted_counts and
+ * output_tokens are identical to the one-pass result (a row without a finite
+ * normaliser counts only at or before the position where the request stops,
+ * in every mode).  debug_probs: positions in phases after the one where a
+ * request stopped are 0 (their rows are never read); with the dynamic exit
+ * every position past the stop is 0. */
 
 /* Draft statistics (same explainer page, section "修正拒绝采样": the
  * accept test needs q only at the drafted token, and its normaliser).  In
@@ -170,18 +184,23 @@ uint64_t spec_verify_plan_phases(int32_t K, const double* survival, double sampl
 double spec_verify_phase_cost(int32_t B, int32_t K, int32_t V, int32_t dtype);
 
 /* Bytes of device workspace a verification of this shape needs (0 for an
- * invalid shape).  The workspace carries nothing from one call to the next
- * (but the invalid-request count that spec_workspace_error reads): it needs
- * no initialisation and may be reused for any shape it is large enough for.
- * Calls that overlap on one workspace race. */
+ * invalid shape).  The workspace needs no initialisation and may be reused
+ * for any shape it is large enough for; calls that overlap on one workspace
+ * race.  What it carries from one call to the next: the invalid-request count
+ * that spec_workspace_error reads, and a launch counter with per-request
+ * words of the dynamic early exit, which tag what a launch wrote so that it
+ * is told apart from anything older.  Leftover bytes can only make that mode
+ * read more rows, never change an output (a request's rows up to its stop
+ * are read unless a leftover word matches this launch's 56-bit tag, and the
+ * final decision reports a request invalid if that happened). */
 size_t spec_verify_workspace_bytes(int32_t B, int32_t K, int32_t V);
 
 /* Enqueue one verification step.  A request whose data is invalid (a draft
  * token outside [0, V), a temperature that is negative, NaN or infinite, a
  * draft row table entry of a sampled request outside [0, draft_rows), a draft
- * count outside [0, K], or a row of a sampled request without a finite
- * normaliser) gets
- * accepted_counts = -1, output_tokens all -1 and debug_probs 0. */
+ * count outside [0, K], or, at a position the request reaches, a row of a
+ * sampled request without a finite normaliser) gets accepted_counts = -1,
+ * output_tokens all -1 and debug_probs 0. */
 int spec_verify_launch(const spec_verify_args* args, hipStream_t stream);
 
 /* For callers that cannot allocate device memory -- code under HIP graph
@@ -193,7 +212,7 @@ int spec_verify_launch(const spec_verify_args* args, hipStream_t stream);
  * call allocates nothing.  The stream must belong to the current device
  * (else SPEC_EINVAL).  A shape whose spec_verify_workspace_bytes exceeds
  * SPEC_NOALLOC_SCRATCH_BYTES returns SPEC_EWORKSPACE before anything is
- * enqueued (8 MiB holds B = 1024, K = 8, V = 201088 nearly three times over).
+ * enqueued (8 MiB holds B = 1024, K = 8, V = 201088: 6.4 MiB).
  * Every call on one GPU shares that GPU's array: calls that may overlap on
  * that GPU (other streams, or graphs replayed concurrently) race and must be
  * ordered by the caller.  Invalid requests are reported in the outputs

@@ -21,6 +21,7 @@ SPEC_F32, SPEC_BF16 = 0, 1
 SPEC_MAX_K = 63
 SPEC_MAX_V = 2147418112  # 2^31 - 2^16
 SPEC_NOALLOC_SCRATCH_BYTES = 8 << 20
+SPEC_PHASES_DYNAMIC = 1  # phase_starts value: decisions inside the row pass (dynamic early exit)
 
 EXPORTED = ("spec_verify_workspace_bytes", "spec_verify_plan_phases", "spec_verify_phase_cost",
             "spec_verify_launch", "spec_verify_launch_noalloc",

@@ -65,8 +65,10 @@ int verify_check(const spec_verify_args* a) {
   const Layout L = make_layout(a->B, a->K, a->V);
   if ((int64_t)a->B * L.R * L.C1 > INT32_MAX || (int64_t)a->B * L.nseg > INT32_MAX) return SPEC_EINVAL;
   if (!aligned16(a->workspace) || (a->draft_stats && !aligned16(a->draft_stats))) return SPEC_EALIGN;
-  if (a->phase_starts & 1u) return SPEC_EINVAL;  // position 0 always starts the first phase
+  // position 0 always starts the first phase; bit 0 alone: dynamic early exit
+  if ((a->phase_starts & 1u) && a->phase_starts != SPEC_PHASES_DYNAMIC) return SPEC_EINVAL;
   if (a->K < 63 && (a->phase_starts >> (a->K + 1)) != 0) return SPEC_EINVAL;
+  if ((int64_t)a->B * (L.R * L.C1 + a->K + 1) > INT32_MAX) return SPEC_EINVAL;  // the dynamic pass's grid
   if (a->workspace_bytes < L.total) return SPEC_EWORKSPACE;
   return SPEC_OK;
 }
@@ -370,6 +372,12 @@ static VerifyParams verify_params(const spec_verify_args* a, bool& vec) {
         (a->draft_row_index || (a->d_req_stride * es) % 16 == 0);
   P.err = reinterpret_cast<int32_t*>(ws + L.off_err);
   P.state = reinterpret_cast<int32_t*>(ws + L.off_state);
+  P.epoch = reinterpret_cast<uint64_t*>(ws + L.off_epoch);
+  P.dstate = reinterpret_cast<uint64_t*>(ws + L.off_dstate);
+  P.trec = reinterpret_cast<TaggedPartial*>(ws + L.off_trec);
+  P.dyn = a->phase_starts == SPEC_PHASES_DYNAMIC;
+  // a request's decider slot sits this many request groups after its chunks
+  P.dyn_shift = (int32_t)min((int64_t)a->B - 1, (int64_t)a->B * kDynShiftNum / kDynShiftDen);
   P.ph_lo = P.ph_nt = P.ph_nd = P.ph_rd = P.ph_check = 0;
   P.last_lo = P.phased = 0;
   P.ex_on = 0;

@@ -26,6 +26,7 @@
 #include <float.h>
 #include <limits.h>
 
+#include "decision.hpp"
 #include "device_common.hpp"
 #include "rowpass.hpp"
 #include "sampling.hpp"
@@ -125,6 +126,7 @@ struct ShardShared {
   double s[2 * SPEC_MAX_K + 1];
   float z[2 * SPEC_MAX_K + 1];  // logit of the row at its position's draft token
   int g[SPEC_MAX_K + 1];
+  unsigned char bad[2 * SPEC_MAX_K + 1];  // a merged sampled row without a usable normaliser
   int a;
   int kb;
 };
@@ -137,8 +139,9 @@ constexpr int kNotAliveShard = -3;  // shard_tests: the request stopped in an ea
 // draft rows [lo, min(thi, K)); with known >= 0 no test runs and a = known.
 // Returns, in every thread, a in [lo, hi] or -1 for invalid data (every
 // draft token, the temperature, the draft count and the row entries are
-// checked whatever the range); with check_state, kNotAliveShard for a
-// request that stopped earlier.  All threads of the workgroup call it.
+// checked whatever the range; a row without a usable normaliser counts where
+// the request stops, as in stop_position); with check_state, kNotAliveShard
+// for a request that stopped earlier.  All threads of the workgroup call it.
 __device__ int shard_tests(const ShardParams& P, int b, int lo, int hi, int thi, int known, bool invalid,
                            bool check_state, ShardShared& sh) {
   const int K = P.K;
@@ -156,9 +159,9 @@ __device__ int shard_tests(const ShardParams& P, int b, int lo, int hi, int thi,
   const int dix = shard_draft_entry(P, b, tid);
   const bool greedy = T == 0.0f;
   const int kb = max(kb_, 0);
-  bool mybad = invalid || kb_ < 0 || !temperature_valid(T) || (tid < kb && (x < 0 || x >= P.V));
+  bool inbad = invalid || kb_ < 0 || !temperature_valid(T) || (tid < kb && (x < 0 || x >= P.V));
   if (!greedy && tid < kb) {
-    mybad |= !shard_entry_ok(P, dix);  // a sampled request reads every draft row
+    inbad |= !shard_entry_ok(P, dix);  // a sampled request reads every draft row
     sh.qoff[tid] = shard_draft_off(P, b, tid, dix);
   }
   const bool row_exists = tid < nt ? k <= kb : k < kb;
@@ -180,30 +183,27 @@ __device__ int shard_tests(const ShardParams& P, int b, int lo, int hi, int thi,
       sh.m[r] = acc.m;
       sh.s[r] = acc.s;
       sh.z[r] = z;
-      mybad |= !(acc.s > 0.0 && acc.s <= DBL_MAX && fabsf(acc.m) <= FLT_MAX);
+      sh.bad[r] = !row_usable(acc.m, acc.s);
     }
   }
-  const bool bad = __syncthreads_or(mybad) != 0;
+  const bool anybad = __syncthreads_or(inbad) != 0;
   if (check_state && st != kStateAlive) return kNotAliveShard;  // its records here were never written
   if (tid < 64) {  // wave 0: one lane per draft position
+    const bool merged = !greedy && tid >= lo && tid < thi && tid < kb;
+    const bool rowbad = merged && (sh.bad[tid] || sh.bad[K + 1 + tid]);
+    const bool bonusbad = !greedy && kb >= lo && kb < thi && sh.bad[kb];
     bool acc = tid < lo;
-    if (test && tid >= lo && tid < min(hi, kb) && !bad) {
+    if (test && tid >= lo && tid < min(hi, kb) && !anybad && !rowbad) {
       if (greedy) {
         acc = x == sh.g[tid];
       } else {
-        float s_hi, s_lo;
-        temperature_scale(T, s_hi, s_lo);
-        const double s_eff = (double)s_hi + (double)s_lo;
-        const double p = exp2((double)sh.z[tid] * s_eff - (double)sh.m[tid]) / sh.s[tid];
-        const double q = exp2((double)sh.z[K + 1 + tid] * s_eff - (double)sh.m[K + 1 + tid]) / sh.s[K + 1 + tid];
-        const double thr = q > 0.0 ? fmin(1.0, p / q) : (p > 0.0 ? 1.0 : 0.0);
-        const uint32_t k0 = (uint32_t)(P.seed & 0xffffffffu), k1 = (uint32_t)(P.seed >> 32);
-        acc = unit_uniform(philox4x32_10((uint32_t)b + P.request_base, (uint32_t)tid, P.step, 0u, k0, k1).w[0]) < thr;
+        float dp, dq;
+        acc = accept_test(T, sh.z[tid], sh.m[tid], sh.s[tid], sh.z[K + 1 + tid], sh.m[K + 1 + tid],
+                          sh.s[K + 1 + tid], P.seed, (uint32_t)b + P.request_base, (uint32_t)tid, P.step, dp, dq);
       }
     }
-    const uint64_t mask = __ballot(acc);
     // lanes >= min(hi, K_b) fail: a <= min(hi, K_b)
-    const int a = bad ? -1 : (test ? (int)__builtin_ctzll(~mask) : known);
+    const int a = stop_position(test, lo, hi, thi, known, kb, acc, rowbad, bonusbad, anybad);
     if (tid == 0) {
       sh.a = a;
       sh.kb = kb;

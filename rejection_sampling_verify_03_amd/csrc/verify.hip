@@ -48,6 +48,7 @@
 #include <float.h>
 #include <limits.h>
 
+#include "decision.hpp"
 #include "device_common.hpp"
 #include "expand_device.hpp"
 #include "rowpass.hpp"
@@ -94,6 +95,33 @@ __device__ __forceinline__ int drafts_of(const VerifyParams& P, int b) {
   return (kb >= 0 && kb <= P.K) ? kb : -1;
 }
 
+// State words of the dynamic early exit (see verify_rowstats_dyn_kernel):
+// (launch tag << 8) | (2 n + f).
+constexpr uint64_t kTagMask = (1ull << 56) - 1;
+
+__device__ __forceinline__ uint64_t dstate_word(uint64_t E, int n, int f) {
+  return ((E & kTagMask) << 8) | (uint64_t)(2 * n + f);
+}
+
+// (n, f) of a state word in launch E; (0, 0) for a word of another launch or
+// one no decision can write (n > K, or a stop at n >= K).
+__device__ __forceinline__ void dstate_read(uint64_t w, uint64_t E, int K, int& n, int& f) {
+  const int key = (w >> 8) == (E & kTagMask) ? (int)(w & 0xffu) : 0;
+  n = key >> 1;
+  f = key & 1;
+  if (n > K || (f && n >= K)) n = f = 0;
+}
+
+// Agent-scope accesses: coherent between workgroups of one launch, whatever
+// their XCD (no cache maintenance, no ordering between different words).
+__device__ __forceinline__ uint64_t load_coherent(const uint64_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ void store_coherent(uint64_t* p, uint64_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // ------------------------------------------------------------- decision
 // The accept tests of request b over draft positions [lo, hi) (positions
 // before lo passed in earlier phases), computed by the whole workgroup.
@@ -101,18 +129,23 @@ __device__ __forceinline__ int drafts_of(const VerifyParams& P, int b) {
 // draft rows [lo, min(thi, K)) into `sh`; thi >= hi.  With known >= 0 no test
 // runs and a = known (its rows lo = known, thi = known + 1 are merged for the
 // draw).  Returns, in every thread, a in [lo, hi] (hi: every test in range
-// passed) or -1 for invalid data.  Every draft token and the temperature are
-// checked whatever the range, so invalid tokens are caught by the first
-// decision of a request.  With check_state, a request whose state is not
-// alive returns kNotAlive and writes nothing.  With `debug`, writes p_k(x_k), q_k(x_k) of every
-// tested position, zero for the positions from hi on when the request stopped
-// before hi (their rows are never read) and zero everywhere for invalid data.
+// passed) or -1 for invalid data (stop_position: the inputs, or a row without
+// a usable normaliser where the request stops; rows past the stop do not
+// count).  Every draft token and the temperature are checked whatever the
+// range, so invalid tokens are caught by the first decision of a request.
+// With check_state, a request whose state is not alive returns kNotAlive and
+// writes nothing.  With `debug`, writes p_k(x_k), q_k(x_k) of every tested
+// position, and zero for: the positions from hi on when the request stopped
+// before hi (their rows are never read), with zero_after the positions past
+// the stop, positions whose rows have no usable normaliser, and every
+// position of an invalid request.
 struct DecideShared {
   int64_t qoff[SPEC_MAX_K];     // draft row offsets of the positions
   float m[2 * SPEC_MAX_K + 1];
   double s[2 * SPEC_MAX_K + 1];
   float z[2 * SPEC_MAX_K + 1];  // logit of the row at its position's draft token
   int g[SPEC_MAX_K + 1];
+  unsigned char bad[2 * SPEC_MAX_K + 1];  // a merged sampled row without a usable normaliser
   int a;
   int kb;  // drafts of the request
 };
@@ -157,7 +190,7 @@ constexpr int kNotAlive = -3;  // decide_tests: the request stopped in an earlie
 
 template <int ES>
 __device__ int decide_tests(const VerifyParams& P, int b, int lo, int hi, int thi, int known, bool invalid,
-                            bool debug, bool check_state, DecideShared& sh) {
+                            bool debug, bool check_state, DecideShared& sh, bool zero_after = false) {
   const int K = P.K;
   const int tid = threadIdx.x;
   const bool test = known < 0;
@@ -189,9 +222,9 @@ __device__ int decide_tests(const VerifyParams& P, int b, int lo, int hi, int th
   // positions k >= K_b do not exist: no token, no draft row, no test; target
   // rows up to K_b (the bonus row) exist
   const int kb = max(kb_, 0);
-  bool mybad = invalid || kb_ < 0 || !temperature_valid(T) || (tid < kb && (x < 0 || x >= P.V));
+  bool inbad = invalid || kb_ < 0 || !temperature_valid(T) || (tid < kb && (x < 0 || x >= P.V));
   if (!greedy && tid < kb) {
-    mybad |= !draft_entry_ok(P, dix);  // a sampled request reads every draft row
+    inbad |= !draft_entry_ok(P, dix);  // a sampled request reads every draft row
     sh.qoff[tid] = draft_off(P, b, tid, dix);
   }
   const bool row_exists = tid < nt ? k <= kb : k < kb;
@@ -212,37 +245,30 @@ __device__ int decide_tests(const VerifyParams& P, int b, int lo, int hi, int th
       sh.m[r] = ms.m;
       sh.s[r] = ms.s;
       sh.z[r] = z;
-      mybad |= !(ms.s > 0.0 && ms.s <= DBL_MAX && fabsf(ms.m) <= FLT_MAX);
+      sh.bad[r] = !row_usable(ms.m, ms.s);
     }
   }
-  const bool bad = __syncthreads_or(mybad) != 0;
+  const bool anybad = __syncthreads_or(inbad) != 0;
   if (check_state && st != kStateAlive) return kNotAlive;  // its partials here were never written
   if (tid < 64) {  // wave 0: one lane per draft position
+    // rows of position tid merged here (sampled): target row and draft row
+    const bool merged = !greedy && tid >= lo && tid < thi && tid < kb;
+    const bool rowbad = merged && (sh.bad[tid] || sh.bad[K + 1 + tid]);
+    const bool bonusbad = !greedy && kb >= lo && kb < thi && sh.bad[kb];
     bool acc = tid < lo;
     float dp = 0.f, dq = 0.f;
-    if (test && tid >= lo && tid < min(hi, kb) && !bad) {
-      if (greedy) {
+    if (test && tid >= lo && tid < min(hi, kb) && !anybad && !rowbad) {
+      if (greedy)
         acc = (x == sh.g[tid]);
-      } else {
-        float s_hi, s_lo;
-        temperature_scale(T, s_hi, s_lo);
-        const double s_eff = (double)s_hi + (double)s_lo;
-        const double p = exp2((double)sh.z[tid] * s_eff - (double)sh.m[tid]) / sh.s[tid];
-        const double q = exp2((double)sh.z[K + 1 + tid] * s_eff - (double)sh.m[K + 1 + tid]) / sh.s[K + 1 + tid];
-        const double thr = q > 0.0 ? fmin(1.0, p / q) : (p > 0.0 ? 1.0 : 0.0);
-        const uint32_t k0 = (uint32_t)(P.seed & 0xffffffffu), k1 = (uint32_t)(P.seed >> 32);
-        const Philox4 rr = philox4x32_10((uint32_t)b + P.request_base, (uint32_t)tid, P.step, 0u, k0, k1);
-        acc = unit_uniform(rr.w[0]) < thr;
-        dp = (float)p;
-        dq = (float)q;
-      }
+      else
+        acc = accept_test(T, sh.z[tid], sh.m[tid], sh.s[tid], sh.z[K + 1 + tid], sh.m[K + 1 + tid],
+                          sh.s[K + 1 + tid], P.seed, (uint32_t)b + P.request_base, (uint32_t)tid, P.step, dp, dq);
     }
-    const uint64_t mask = __ballot(acc);
     // lanes >= min(hi, K_b) fail: a <= min(hi, K_b)
-    const int a = bad ? -1 : (test ? (int)__builtin_ctzll(~mask) : known);
+    const int a = stop_position(test, lo, hi, thi, known, kb, acc, rowbad, bonusbad, anybad);
     if (debug && P.debug && tid < K) {
       float* d = P.debug + ((int64_t)b * K + tid) * 2;
-      if (bad || (tid >= hi && a < hi)) {
+      if (a < 0 || (tid >= hi && a < hi) || (zero_after && tid > a) || (rowbad && tid >= lo && tid < hi)) {
         d[0] = 0.f;
         d[1] = 0.f;
       } else if (test && tid >= lo && tid < hi) {
@@ -259,29 +285,15 @@ __device__ int decide_tests(const VerifyParams& P, int b, int lo, int hi, int th
   return sh.a;
 }
 
-// The decision of request b at the sampling stage, computed by the whole
-// workgroup into `D` (shared).  With `write`, the request's outputs (all but
-// the token the draw samples), its debug rows and its decision record are
-// written too.
+// The outputs and decision record of request b once its stop a = sh.a is
+// known (all threads of the workgroup call it): with `write`, the outputs (all
+// but the token the draw samples) and the decision record; `D` (shared) gets
+// the record either way.
 template <int ES>
-__device__ void decide(const VerifyParams& P, int b, bool write, ReqDesc& D) {
-  __shared__ DecideShared sh;
+__device__ void decide_finish(const VerifyParams& P, int b, bool write, ReqDesc& D, const DecideShared& sh) {
   const int K = P.K;
   const int tid = threadIdx.x;
-  int lo = 0, known = -1;
-  bool invalid = false;
-  if (P.phased) {  // rows were read in phases: the request may have stopped earlier
-    const int st = P.state[b];
-    invalid = st == kStateInvalid;
-    if (st >= 0) {
-      known = st;
-      lo = st;
-    } else {
-      lo = P.last_lo;
-    }
-  }
-  const int thi = known >= 0 ? known + 1 : K + 1;
-  const int a = decide_tests<ES>(P, b, lo, K, thi, known, invalid, write, false, sh);
+  const int a = sh.a;
   const float T = P.temperature[b];
   const bool greedy = (T == 0.0f);
   const bool bad = a < 0;
@@ -295,6 +307,11 @@ __device__ void decide(const VerifyParams& P, int b, bool write, ReqDesc& D) {
         else tok = greedy ? sh.g[a] : -1;  // sampled: written by the draw
         if (!(j == a && !greedy && !bad)) out[j] = tok;
       }
+      if (bad && P.debug)  // invalid: no probability is reported
+        for (int j = tid; j < K; j += 64) {
+          P.debug[((int64_t)b * K + j) * 2 + 0] = 0.f;
+          P.debug[((int64_t)b * K + j) * 2 + 1] = 0.f;
+        }
       if (tid == 0) {
         P.accepted[b] = a;
         if (bad) atomicAdd(P.err, 1);
@@ -324,6 +341,47 @@ __device__ void decide(const VerifyParams& P, int b, bool write, ReqDesc& D) {
     }
   }
   __syncthreads();
+}
+
+// The decision of request b at the sampling stage, computed by the whole
+// workgroup into `D` (shared).  With `write`, the request's outputs (all but
+// the token the draw samples), its debug rows and its decision record are
+// written too.
+template <int ES>
+__device__ void decide(const VerifyParams& P, int b, bool write, ReqDesc& D) {
+  __shared__ DecideShared sh;
+  const int K = P.K;
+  int lo = 0, known = -1;
+  bool invalid = false;
+  if (P.dyn) {  // decisions inside the row pass: every test again, from the partials
+    const uint64_t E = *P.epoch;
+    int n, f;
+    dstate_read(P.dstate[b], E, K, n, f);
+    // with f the rows past n may not have been read: test [0, n] only
+    const int a = decide_tests<ES>(P, b, 0, f ? n + 1 : K, f ? n + 1 : K + 1, -1, false, write, false, sh, true);
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      // position n passed after all: the state word was not written in this launch
+      sh.a = (f && a > n) ? -1 : a;
+      if (write) P.dstate[b] = dstate_word(E + 1, 0, 0);  // the next launch starts from nothing
+    }
+    __syncthreads();
+    decide_finish<ES>(P, b, write, D, sh);
+    return;
+  }
+  if (P.phased) {  // rows were read in phases: the request may have stopped earlier
+    const int st = P.state[b];
+    invalid = st == kStateInvalid;
+    if (st >= 0) {
+      known = st;
+      lo = st;
+    } else {
+      lo = P.last_lo;
+    }
+  }
+  const int thi = known >= 0 ? known + 1 : K + 1;
+  decide_tests<ES>(P, b, lo, K, thi, known, invalid, write, false, sh);
+  decide_finish<ES>(P, b, write, D, sh);
 }
 
 // Between early-exit phases: the accept tests of the phase's positions
@@ -390,6 +448,228 @@ __global__ __launch_bounds__(kWG) void verify_rowstats_kernel(VerifyParams P) {
     part.s = v.s;
   }
   if (threadIdx.x == 0) P.rowp[((int64_t)b * P.R + r) * P.C1 + c] = part;
+}
+
+// ------------------------------------------------------ dynamic early exit
+// The row pass with the decisions inside it (same page, section "核心思想":
+// a request stops at its first rejection).  The grid is position-major:
+// block J holds, for every request in order, the chunks of its target row J
+// and (sampled, without draft statistics) draft row J, plus one decider slot.
+// The decider slot after request g's chunks serves request d = g - dyn_shift
+// (mod B): it tests, from the records of this launch, the positions of d from
+// the first one not yet known to pass up to J (J - 1 when d's chunks of J come
+// after it), in order, and stops at the first position whose records are not
+// all there yet, that fails its test, or whose rows have no usable
+// normaliser.  The result goes into d's state word with an atomic maximum, so
+// it only ever moves forward: (n, 0) positions before n known to pass, (n, 1)
+// the request stops at n.  A chunk workgroup of position k > n of a stopped
+// request exits at once.  Nothing waits for anything: a decision that finds
+// its records incomplete is left to a later decider slot, and a late one only
+// costs the rows read meanwhile.  The final decision recomputes every test
+// from the plain partials after the launch, so the outputs never depend on
+// which rows the deciders let the pass skip.
+struct DynShared {
+  uint64_t sw;  // the request's state word as the decider read it
+  float m[kWG];
+  int32_t idx[kWG];
+  double s[kWG];
+  unsigned char ok[kWG];
+  // merged rows, (position - n0) * rows + row kind
+  float rm[2 * 64];
+  double rs[2 * 64];
+  float rz[2 * 64];
+  int32_t rg[2 * 64];
+  unsigned char rok[2 * 64];
+};
+
+// The decider slot of request d at block J: one round of loads (the state
+// word, the request's scalars and every record of a window of positions
+// ending at the last one it may test), then the merges and tests, then one
+// atomic maximum that nothing waits for.
+template <int ES>
+__device__ void dyn_decider(const VerifyParams& P, int J, int g, uint64_t E, DynShared& ds) {
+  const int B = P.B, K = P.K, C1 = P.C1;
+  int d = g - P.dyn_shift, j = J;
+  if (d < 0) {
+    d += B;
+    j = J - 1;
+  }
+  const int per = 2 * C1;  // records of a position: its target row and its draft row
+  if (j < 0 || per > kWG) return;  // a position's records must fit one round
+  const int top = min(j, K - 1);          // the last position that may be tested
+  const int w = min(top + 1, kWG / per);  // the window [p0, top] of loaded positions
+  const int p0 = top - w + 1;
+  const int t = threadIdx.x;
+  const float T = P.temperature[d];
+  const int kb = drafts_of(P, d);
+  if (t == 0) ds.sw = load_coherent(P.dstate + d);  // one value for the whole workgroup
+  if (t < w * per) {
+    const int p = p0 + t / per, rr = (t / C1) % 2, c = t % C1;
+    const int r = rr == 0 ? p : K + 1 + p;
+    const uint64_t* wp = P.trec[((int64_t)d * P.R + r) * C1 + c].w;
+    const uint64_t w0 = load_coherent(wp), w1 = load_coherent(wp + 1), w2 = load_coherent(wp + 2),
+                   w3 = load_coherent(wp + 3);
+    const uint32_t tag = (uint32_t)E;
+    ds.ok[t] = (uint32_t)(w0 >> 32) == tag && (uint32_t)(w1 >> 32) == tag && (uint32_t)(w2 >> 32) == tag &&
+               (uint32_t)(w3 >> 32) == tag;
+    ds.m[t] = __uint_as_float((uint32_t)w0);
+    ds.idx[t] = (int32_t)(uint32_t)w1;
+    ds.s[t] = __longlong_as_double((long long)((w3 << 32) | (w2 & 0xffffffffull)));
+  }
+  __syncthreads();
+  int n0, f;
+  dstate_read(ds.sw, E, K, n0, f);
+  const int hi = min(top, kb - 1);  // the last position to test
+  // nothing to decide: stopped already, invalid scalars, no position in
+  // range, or the first open position outside the window
+  if (f || kb < 0 || !temperature_valid(T) || hi < n0 || n0 < p0) return;
+  const bool greedy = T == 0.0f;
+  if (t < 2 * w) {  // one thread per row of the window: merge its chunks in chunk order
+    const int p = p0 + t / 2, rr = t % 2;
+    const int base = (t / 2) * per + rr * C1;
+    const int x = P.tokens[(int64_t)d * K + p];
+    const bool xin = x >= 0 && x < P.V;
+    const int cx = xin ? x / P.chunk1 : -1;
+    bool ok = xin;
+    MS ms{ds.m[base], ds.s[base]};
+    VI vi{ds.m[base], ds.idx[base]};
+    float z = cx == 0 ? bits_to_logit<ES>((uint32_t)ds.idx[base]) : 0.f;
+    for (int c = 0; c < C1; ++c) {
+      ok = ok && ds.ok[base + c];
+      if (c == 0) continue;
+      if (greedy) {
+        vi = vi_pick(vi, VI{ds.m[base + c], ds.idx[base + c]});
+      } else {
+        ms = ms_merge(ms, MS{ds.m[base + c], ds.s[base + c]});
+        if (c == cx) z = bits_to_logit<ES>((uint32_t)ds.idx[base + c]);
+      }
+    }
+    ds.rm[t] = ms.m;
+    ds.rs[t] = ms.s;
+    ds.rz[t] = z;
+    ds.rg[t] = vi.i;
+    ds.rok[t] = ok;
+  }
+  __syncthreads();
+  if (t < 64) {  // wave 0: lane l tests position n0 + l
+    const int p = n0 + t;
+    const int np = hi - n0 + 1;
+    const bool in = t < np;
+    const int i = in ? 2 * (p - p0) : 0;  // its target row in the window (draft row: i + 1)
+    const bool need_q = !greedy && !P.dstats;
+    const bool complete = in && ds.rok[i] && (!need_q || ds.rok[i + 1]);
+    const int x = in ? P.tokens[(int64_t)d * K + p] : 0;
+    bool stop = false;  // the request stops here: its test failed, or its rows are unusable
+    if (complete) {
+      if (greedy) {
+        stop = x != ds.rg[i];
+      } else {
+        float mq, zq;
+        double sq;
+        if (P.dstats) {
+          const RowPartial q = P.dstats[(int64_t)d * K + p];
+          mq = q.m;
+          sq = q.s;
+          zq = bits_to_logit<ES>((uint32_t)q.idx);
+        } else {
+          mq = ds.rm[i + 1];
+          sq = ds.rs[i + 1];
+          zq = ds.rz[i + 1];
+        }
+        float dp, dq;
+        stop = !row_usable(ds.rm[i], ds.rs[i]) || !row_usable(mq, sq) ||
+               !accept_test(T, ds.rz[i], ds.rm[i], ds.rs[i], zq, mq, sq, P.seed, (uint32_t)d + P.request_base,
+                            (uint32_t)p, P.step, dp, dq);
+      }
+    }
+    const uint64_t go = __ballot(complete && !stop);
+    const uint64_t done = __ballot(complete);
+    const int first = (int)__builtin_ctzll(~go);  // <= np
+    if (t == 0) {
+      const int n = n0 + first;
+      const int fl = (first < np && ((done >> first) & 1u)) ? 1 : 0;
+      if (2 * n + fl > 2 * n0 + f)
+        __hip_atomic_fetch_max(P.dstate + d, (unsigned long long)dstate_word(E, n, fl), __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+}
+
+// Chunk c of row r of request b: its partial into rowp and, tagged with the
+// launch, into trec (one word per lane of the first four).
+template <int ES, bool VEC>
+__device__ __forceinline__ void dyn_chunk(const VerifyParams& P, int b, int r, int c, int x, bool greedy, float T,
+                                          int di, uint64_t E) {
+  const char* row = row_ptr<ES>(P, b, r, di);
+  const int e0 = c * P.chunk1;
+  const int e1 = min(P.V, e0 + P.chunk1);
+  RowPartial part;
+  if (greedy) {
+    const VI v = block_argmax(chunk_argmax<ES, VEC>(row, e0, e1));
+    part.m = v.v;
+    part.idx = v.i;
+    part.s = 0.0;
+  } else {
+    const bool has_x = x >= e0 && x < e1;
+    const uint32_t zbits = load_bits<ES>(row, min(max(x, e0), e1 - 1));
+    float s_hi, s_lo;
+    temperature_scale(T, s_hi, s_lo);
+    const MS v = block_merge_ms(chunk_stats<ES, VEC>(row, e0, e1, s_hi, s_lo));
+    part.m = v.m;
+    part.idx = has_x ? (int32_t)zbits : 0;
+    part.s = v.s;
+  }
+  const int64_t at = ((int64_t)b * P.R + r) * P.C1 + c;
+  if (threadIdx.x == 0) P.rowp[at] = part;
+  if (threadIdx.x < 4) {
+    const uint64_t sb = (uint64_t)__double_as_longlong(part.s);
+    const uint32_t pay = threadIdx.x == 0   ? __float_as_uint(part.m)
+                         : threadIdx.x == 1 ? (uint32_t)part.idx
+                         : threadIdx.x == 2 ? (uint32_t)sb
+                                            : (uint32_t)(sb >> 32);
+    store_coherent(&P.trec[at].w[threadIdx.x], ((uint64_t)(uint32_t)E << 32) | pay);
+  }
+}
+
+// Block J: per request, the chunks of its target row J and (sampled, J <
+// K_b, without draft statistics) of its draft row J, one workgroup each, then
+// its decider slot.
+template <int ES, bool VEC>
+__global__ __launch_bounds__(kWG) void verify_rowstats_dyn_kernel(VerifyParams P) {
+  __shared__ DynShared ds;
+  const int K = P.K, C1 = P.C1;
+  const int wm = (P.dstats ? 1 : 2) * C1 + 1, wl = C1 + 1;
+  const int64_t span = (int64_t)P.B * wm;
+  const int64_t bid = blockIdx.x;
+  const int J = (int)min(bid / span, (int64_t)K);
+  const int64_t rem = bid - (int64_t)J * span;
+  const int W = J < K ? wm : wl;
+  // the roles inside a group rotate with the group, so that no role keeps to
+  // one XCD when W is a multiple of the 8 the hardware deals workgroups to
+  const int g = (int)(rem / W), sl = (int)((rem % W + g) % W);
+  const uint64_t E = *P.epoch;
+  if (sl == W - 1) {
+    dyn_decider<ES>(P, J, g, E, ds);
+    return;
+  }
+  const int b = g, k = J, c = sl % C1;
+  const bool draft_row = sl >= C1;
+  const int r = draft_row ? K + 1 + k : k;
+  const uint64_t sw = load_coherent(P.dstate + b);
+  const float T = P.temperature[b];
+  const int xt = P.tokens[(int64_t)b * K + min(k, K - 1)];
+  const int di = draft_entry(P, b, k);
+  const int kb = drafts_of(P, b);
+  const bool greedy = (T == 0.0f);
+  if (bid == 0 && threadIdx.x == 0) *P.err = 0;  // counted by the final decision
+  int n, f;
+  dstate_read(sw, E, K, n, f);
+  // skip as the phased pass does, and every row past a known stop
+  const bool skip = (greedy & draft_row) | ((f != 0) & (n < k)) | ((k < kb) & ((uint32_t)xt >= (uint32_t)P.V)) |
+                    (draft_row & !draft_entry_ok(P, di)) | (kb < 0) | (!draft_row & (k > kb)) |
+                    (draft_row & (k >= kb));
+  if (skip) return;
+  dyn_chunk<ES, VEC>(P, b, r, c, k < kb ? xt : -1, greedy, T, di, E);
 }
 
 // ------------------------------------------------------------ sampling weights
@@ -480,6 +760,9 @@ __global__ __launch_bounds__(kWGD) void verify_draw_kernel(VerifyParams P) {
   const int tid = threadIdx.x;
   const int nseg = P.nseg;
   const double* seg = P.seg + (int64_t)b * P.nseg * 2;
+  // the last kernel of the verification advances the launch counter (the
+  // row pass and the decision of this launch have read it)
+  if (b == 0 && tid == 0) *P.epoch = *P.epoch + 1;
   // the decision record and the first block of segment sums are loaded together
   const ReqDesc d = P.desc[b];
   const bool in0 = tid < nseg;
@@ -576,7 +859,18 @@ template <int ES, bool VEC>
 static hipError_t launch_typed(VerifyParams P, uint64_t phase_starts, hipEvent_t phase_event,
                                hipStream_t stream) {
   const int K = P.K;
-  int lo = 0;
+  int lo = P.dyn ? K + 1 : 0;
+  if (P.dyn) {  // one row pass with its decider slots
+    P.ph_lo = 0;
+    P.ph_nt = K + 1;
+    P.ph_nd = K;
+    P.ph_rd = P.dstats ? 0 : K;
+    P.ph_check = P.phased = P.last_lo = 0;
+    const int64_t g1 = (int64_t)K * P.B * ((P.dstats ? 1 : 2) * P.C1 + 1) + (int64_t)P.B * (P.C1 + 1);
+    hipLaunchKernelGGL((verify_rowstats_dyn_kernel<ES, VEC>), dim3((unsigned)g1), dim3(kWG), 0, stream, P);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   for (int j = 0; lo <= K; ++j) {  // phases [lo, hi), the last one ends past target row K
     int hi = lo + 1;
     while (hi <= K && !((phase_starts >> hi) & 1u)) ++hi;

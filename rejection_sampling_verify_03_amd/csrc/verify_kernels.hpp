@@ -64,12 +64,28 @@ struct VerifyParams {
   int32_t ph_lo, ph_nt, ph_nd, ph_rd, ph_check;
   // start of the last phase when the rows were read in several phases, else 0
   int32_t last_lo, phased;
+  // dynamic early exit (dyn): decisions taken inside the row pass as its
+  // chunks finish.  epoch: the launch counter (its low 32 bits tag the
+  // records of this launch); dstate [B]: per request (tag << 8) | (2 n + f),
+  // positions before n known accepted and, with f, position n stops the
+  // request; trec: tagged copies of rowp; dyn_shift: request groups between a
+  // request's chunks of a position and its decider slot
+  uint64_t* epoch;
+  uint64_t* dstate;
+  TaggedPartial* trec;
+  int32_t dyn, dyn_shift;
   // a chained expansion of this verification's outputs, folded into its
   // sampling stage (ex_on): ex_G workgroups per request window
   ExpandParams ex;
   int32_t ex_on, ex_G;
 };
 
+
+// Decider slots of the dynamic early exit: a request's slot comes
+// kDynShiftNum / kDynShiftDen of a position's request groups after its chunks
+// of that position (late enough that most of the chunks have finished, early
+// enough that the decision lands before its chunks of the next position).
+constexpr int64_t kDynShiftNum = 3, kDynShiftDen = 10;
 
 struct DraftParams {
   int32_t B, K, V, N, nseg, C;  // C: chunks of kDraftChunkSegs segments per row

@@ -35,7 +35,19 @@ struct ReqDesc {  // decision of one request, read by the draw
   int64_t qoff;   // element offset of draft row a from the draft base (residual mode)
 };
 
+// A chunk's RowPartial as read by workgroups of the same row-pass launch
+// (dynamic early exit): four 64-bit words, each stored by one single-copy
+// atomic store and each carrying the launch's 32-bit tag in its high half
+// (payload in the low half: m's bits, idx, the low and the high half of s's
+// bits).  A reader that finds the tag in all four words has the whole record
+// of this launch; anything else (a record still being written, or left by an
+// earlier launch) it treats as not yet there.
+struct TaggedPartial {
+  uint64_t w[4];
+};
+
 static_assert(sizeof(RowPartial) == 16, "RowPartial layout");
+static_assert(sizeof(TaggedPartial) == 32, "TaggedPartial layout");
 static_assert(sizeof(ReqDesc) == 64, "ReqDesc layout");
 
 enum { kModeNone = 0, kModeResidual = 1, kModeBonus = 2 };
@@ -51,8 +63,9 @@ struct Layout {
   int32_t C1, chunk1;  // row-pass chunks per row and their length
   int32_t nseg;        // segments per row
   // the invalid-request count sits at byte 0 of the workspace (read by
-  // spec_workspace_error without knowing the shape)
-  size_t off_err, off_rowp, off_desc, off_seg, off_state, total;
+  // spec_workspace_error without knowing the shape), the launch counter of
+  // the dynamic early exit at byte 8
+  size_t off_err, off_epoch, off_rowp, off_desc, off_seg, off_state, off_dstate, off_trec, total;
 };
 
 __host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -74,7 +87,8 @@ __host__ __device__ inline Layout make_layout(int32_t B, int32_t K, int32_t V) {
   L.nseg = (int32_t)(((int64_t)V + kSeg - 1) / kSeg);
   size_t off = 0;
   L.off_err = off;
-  off = align256(off + sizeof(int32_t));
+  L.off_epoch = off + 8;
+  off = align256(off + 16);
   L.off_rowp = off;
   off = align256(off + (size_t)B * L.R * L.C1 * sizeof(RowPartial));
   L.off_desc = off;
@@ -83,6 +97,10 @@ __host__ __device__ inline Layout make_layout(int32_t B, int32_t K, int32_t V) {
   off = align256(off + (size_t)B * L.nseg * 2 * sizeof(double));
   L.off_state = off;
   off = align256(off + (size_t)B * sizeof(int32_t));
+  L.off_dstate = off;
+  off = align256(off + (size_t)B * sizeof(uint64_t));
+  L.off_trec = off;
+  off = align256(off + (size_t)B * L.R * L.C1 * sizeof(TaggedPartial));
   L.total = off;
   return L;
 }

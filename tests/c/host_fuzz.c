@@ -103,7 +103,7 @@ int main(void) {
   if (spec_verify_launch(&w, NULL) != SPEC_EALIGN) return fail("verify_align", 0, 0);
   w = v; w.dtype = 9;
   if (spec_verify_launch(&w, NULL) != SPEC_EDTYPE) return fail("verify_dtype", 0, 0);
-  w = v; w.phase_starts = 1;
+  w = v; w.phase_starts = 3; /* bit 0 (the dynamic exit) with a cut */
   w.workspace_bytes = (size_t)1 << 40;
   if (spec_verify_launch(&w, NULL) != SPEC_EINVAL) return fail("verify_phase_bit0", 0, 0);
   w.phase_starts = (uint64_t)1 << 5;

@@ -108,9 +108,11 @@ def test_verify_argument_errors(sv):
         a = _valid_verify_args(sv)
         setattr(a, field, value)
         assert launch(a) == want, (field, value)
-    # early-exit phases: bit 0 or a bit above K is rejected (K = 3 here); bits 1..K pass validation
-    for mask, want in [(1, sv.SPEC_EINVAL), (1 << 4, sv.SPEC_EINVAL), (1 << 63, sv.SPEC_EINVAL),
-                       ((1 << 1) | (1 << 3), sv.SPEC_EWORKSPACE)]:
+    # early-exit phases: bit 0 with another bit, or a bit above K, is rejected (K = 3 here); bits
+    # 1..K pass validation, and so does bit 0 alone (the dynamic early exit)
+    for mask, want in [(3, sv.SPEC_EINVAL), (1 | (1 << 2), sv.SPEC_EINVAL), (1 << 4, sv.SPEC_EINVAL),
+                       (1 << 63, sv.SPEC_EINVAL), ((1 << 1) | (1 << 3), sv.SPEC_EWORKSPACE),
+                       (sv.SPEC_PHASES_DYNAMIC, sv.SPEC_EWORKSPACE)]:
         a = _valid_verify_args(sv)
         a.phase_starts = mask
         assert launch(a) == want, mask

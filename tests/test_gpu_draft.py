@@ -188,7 +188,7 @@ def test_verify_reads_drafter_rows_in_place(sv):
     perm = torch.randperm(N, generator=g, device=dev)[:B * K].reshape(B, K).to(torch.int32).contiguous()
     buf = workloads.zipf_logits(N, V, g, "cuda").to(torch.bfloat16)
     buf[perm.reshape(-1).long()] = vin.draft[:, :K].reshape(B * K, V)
-    for mask in (0, 0b100100):
+    for mask in (0, 0b100100, sv.SPEC_PHASES_DYNAMIC):
         one = sv.verify(vin.target, vin.draft, vin.draft_tokens, vin.temperature, seed=3, step=1, debug=True,
                         phase_starts=mask)
         tab = sv.verify(vin.target, buf, vin.draft_tokens, vin.temperature, seed=3, step=1, debug=True,
@@ -262,8 +262,8 @@ def test_verify_with_draft_stats(sv, dtype, V):
     verification: draft tokens drawn from drafter rows (with stats_out),
     then their verification against those rows reading the statistics
     instead of the rows -- every request against the oracle (bar of
-    parity.py, debug probabilities included), phased bit-identical to one
-    pass, and the same outputs as reading the rows but where a decision
+    parity.py, debug probabilities included), phased and with the dynamic
+    exit bit-identical to one pass, and the same outputs as reading the rows but where a decision
     sits within rounding of its threshold."""
     from parity import Report, compare
     say("case: verification from the sampler's draft statistics, V%d %s" % (V, dtype))
@@ -283,8 +283,11 @@ def test_verify_with_draft_stats(sv, dtype, V):
         a2, t2, _ = sv.verify(vin.target, buf, x, T, seed=5, step=step, draft_row_index=ridx, draft_stats=stats,
                               phase_starts=0b100100)
         a3, t3, _ = sv.verify(vin.target, buf, x, T, seed=5, step=step, draft_row_index=ridx)
+        a4, t4, _ = sv.verify(vin.target, buf, x, T, seed=5, step=step, draft_row_index=ridx, draft_stats=stats,
+                              phase_starts=sv.SPEC_PHASES_DYNAMIC)
         torch.cuda.synchronize()
         assert torch.equal(a1, a2) and torch.equal(t1, t2), step
+        assert torch.equal(a1, a4) and torch.equal(t1, t4), step
         same += int(((a1 == a3) & (t1 == t3).all(dim=1)).sum())
         compare(tl, dl, x.cpu().numpy(), T.cpu().numpy(), a1.cpu().numpy(), t1.cpu().numpy(), d1.cpu().numpy(),
                 seed=5, step=step, report=rep)

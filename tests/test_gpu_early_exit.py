@@ -1,11 +1,12 @@
 """Early-exit verification on the GPU (rows read in phases, only for requests
-still alive) through the C ABI.
+still alive, or in one pass whose workgroups decide as the rows come in)
+through the C ABI.
 
-For every case and phase plan the accepted counts and output tokens must be
-bit-identical to the one-pass launch on the same inputs, the debug
-probabilities must equal the one-pass ones on every position whose phase was
-read and be 0 past the phase where the request stopped, and the outputs must
-meet the oracle bar of ``parity.py``.
+For every case and phase plan, and for the dynamic exit (DYN), the accepted
+counts and output tokens must be bit-identical to the one-pass launch on the
+same inputs, the debug probabilities must equal the one-pass ones on every
+position whose phase was read (dynamic: every position up to the stop) and
+be 0 past it, and the outputs must meet the oracle bar of ``parity.py``.
 """
 import sys
 
@@ -31,9 +32,15 @@ def say(*a):
     sys.stdout.flush()
 
 
+DYN = 1  # phase_starts of the dynamic early exit (SPEC_PHASES_DYNAMIC)
+
+
 def phase_end(a, mask, K):
-    """End (exclusive) of the phase holding position a under the cut `mask`."""
+    """End (exclusive) of the phase holding position a under the cut `mask`
+    (the dynamic exit reports positions up to the stop)."""
     e = a + 1
+    if mask == DYN:
+        return e
     while e <= K and not (mask >> e) & 1:
         e += 1
     return e
@@ -82,12 +89,12 @@ def oracle_check(inp, acc, tok, seed, step, idx=None):
 
 def test_every_plan_tiny(sv):
     """B=4, K=4, V=1024 fp32: all 16 cuts of the positions, 8 steps each."""
-    say("case: early exit, every plan, B4 K4 V1024 fp32")
+    say("case: early exit, every plan and the dynamic exit, B4 K4 V1024 fp32")
     inp = workloads.verify_tiny(seed=0, device="cuda")
-    for mask in all_masks(inp.K):
+    for mask in all_masks(inp.K) + [DYN]:
         for step in range(8):
             acc, tok = one_vs_phased(sv, inp, mask, seed=1, step=step)
-            if mask == 0b11110 and step < 2:
+            if mask in (0b11110, DYN) and step < 2:
                 oracle_check(inp, acc, tok, 1, step)
 
 
@@ -96,7 +103,7 @@ def test_plans_multi_chunk_mixed_temperatures(sv, dtype, V):
     say("case: early exit B12 K5 V%d %s mixed T" % (V, dtype))
     inp = workloads.mixture_inputs("mixed B12 K5 V%d" % V, 12, 5, V, dtype, 3, "cuda",
                                    temps=(0.0, 0.6, 1.0), lam_lo=0.05, lam_hi=0.6)
-    for mask in [1 << 1, 1 << 3, 1 << 5, 0b111110, 0b101010]:
+    for mask in [1 << 1, 1 << 3, 1 << 5, 0b111110, 0b101010, DYN]:
         for step in range(2):
             acc, tok = one_vs_phased(sv, inp, mask, seed=5, step=step)
             oracle_check(inp, acc, tok, 5, step)
@@ -106,14 +113,14 @@ def test_plans_scalar_path_and_K63(sv):
     say("case: early exit, scalar path and K=63")
     inp = workloads.noisy_draft_inputs("scalar V20003", 6, 4, 20003, torch.bfloat16, 1, "cuda", "gauss",
                                        target_std=2.0, draft_noise=0.5)
-    for mask in [0b11110, 0b00100]:
+    for mask in [0b11110, 0b00100, DYN]:
         acc, tok = one_vs_phased(sv, inp, mask, step=3)
         oracle_check(inp, acc, tok, 0, 3)
     inp = workloads.noisy_draft_inputs("K63", 3, 63, 256, torch.float32, 8, "cuda", "gauss",
                                        target_std=0.3, draft_noise=0.05)
     rng = np.random.default_rng(63)
     some = rng.choice(np.arange(1, 64), 9, replace=False)
-    masks = [(1 << 64) - 2, 1 << 1, 1 << 63, int(sum(1 << int(k) for k in some))]
+    masks = [(1 << 64) - 2, 1 << 1, 1 << 63, int(sum(1 << int(k) for k in some)), DYN]
     for mask in masks:
         for step in range(2):
             acc, tok = one_vs_phased(sv, inp, mask, step=step)
@@ -122,8 +129,8 @@ def test_plans_scalar_path_and_K63(sv):
 
 def test_invalid_requests_phased(sv):
     """Invalid tokens anywhere and invalid temperatures are caught by the first
-    decision; a row without a finite normaliser in a phase that is read is
-    caught there."""
+    decision; a row without a finite normaliser at a position every request
+    reaches is caught in every mode."""
     say("case: early exit, invalid request data")
     inp = workloads.noisy_draft_inputs("bad", 6, 3, 64, torch.float32, 2, "cuda", "gauss")
     x = inp.draft_tokens.clone()
@@ -134,11 +141,55 @@ def test_invalid_requests_phased(sv):
     T[3] = -1.0
     T[4] = float("nan")
     t[5, 0, :] = -float("inf")
-    for mask in [0b0010, 0b1110, 0b1000]:
+    for mask in [0b0010, 0b1110, 0b1000, DYN]:
         acc, tok = one_vs_phased(sv, inp, mask, x=x, T=T, target=t)
         assert acc[0] >= 0
         for b in range(1, 6):
             assert acc[b] == -1 and (tok[b] == -1).all(), (b, bin(mask))
+
+
+def test_rows_past_the_stop_do_not_count(sv):
+    """Position 0 rejects with certainty (the draft token lies outside the
+    target's support), so rows of later positions without a finite maximum,
+    or with a NaN, leave the request valid in every mode; the same row at
+    the stop, or the bonus row of a request that accepts everything, makes
+    it invalid (explainer page, section "核心思想": the positions are taken
+    in order and the first rejection ends the request).  Every mode equals
+    the oracle."""
+    say("case: rows past the stop, every mode")
+    B, K, V = 8, 4, 3000
+    g = torch.Generator().manual_seed(17)
+    t = torch.full((B, K + 1, V), -float("inf"))
+    d = torch.full((B, K + 1, V), -float("inf"))
+    t[:, 0, :1500] = torch.randn(B, 1500, generator=g)
+    d[:, 0, 1500:] = torch.randn(B, 1500, generator=g)
+    t[:, 1:, :] = torch.randn(B, K, V, generator=g)
+    d[:, 1:, :] = t[:, 1:, :]
+    x = torch.randint(1500, V, (B, K), generator=g, dtype=torch.int32)
+    T = torch.full((B,), 0.7)
+    t[1, 2, 7] = float("nan")          # past the stop
+    t[2, 3, :] = -float("inf")         # past the stop
+    d[3, 1, :] = -float("inf")         # past the stop
+    t[4, 0, :] = -float("inf")         # at the stop: invalid
+    d[5, 0, :] = -float("inf")         # at the stop: invalid
+    # requests 6 and 7 accept everything (identical rows everywhere)
+    t[6:, 0, :] = torch.randn(2, V, generator=g)
+    d[6:, 0, :] = t[6:, 0, :]
+    x[6:] = torch.randint(0, V, (2, K), generator=g, dtype=torch.int32)
+    t[7, K, :] = -float("inf")         # request 7's bonus row: invalid
+    inp = type("Inp", (), {})()
+    inp.target, inp.draft = t.cuda(), d.cuda()
+    inp.draft_tokens, inp.temperature = x.cuda(), T.cuda()
+    want = [0, 0, 0, 0, -1, -1, K, -1]
+    for mask in [0, 0b0100, 0b11110, DYN]:
+        a, tok, dbg = sv.verify(inp.target, inp.draft, inp.draft_tokens, inp.temperature, seed=3, step=1,
+                                debug=True, phase_starts=mask)
+        torch.cuda.synchronize()
+        a = a.cpu().numpy()
+        assert list(a) == want, (bin(mask), list(a))
+        rep = compare(workloads.logits_numpy(t), workloads.logits_numpy(d), x.numpy(), T.numpy(),
+                      a, tok.cpu().numpy(), dbg.cpu().numpy() if mask == 0 else None, seed=3, step=1)
+        assert rep.ok(), (bin(mask), rep.failures[:3])
 
 
 def test_headline_planned(sv):
@@ -160,6 +211,7 @@ def test_headline_planned(sv):
         assert mask != 0
         if mask not in masks:
             masks.append(mask)
+    masks.append(DYN)
     for i, mask in enumerate(masks):
         for step in range(3):
             acc, tok = one_vs_phased(sv, inp, mask, step=step)
@@ -174,3 +226,49 @@ def test_gptoss_vocab_planned_full_parity(sv):
     inp = workloads.verify_gptoss(seed=0, device="cuda")
     acc, tok = one_vs_phased(sv, inp, 0b111110, step=0)
     oracle_check(inp, acc, tok, 0, 0)
+    acc, tok = one_vs_phased(sv, inp, DYN, step=1)
+    oracle_check(inp, acc, tok, 0, 1)
+
+
+def test_dynamic_exit_graph_replays_on_new_inputs(sv):
+    """The dynamic exit captured in a HIP graph and replayed on new inputs
+    written into the captured buffers between replays: each replay equals an
+    eager one-pass launch on the same inputs.  (The records a launch writes
+    carry a tag that the launch counter in the workspace changes at every
+    launch, replays included; records of an earlier replay must not pass for
+    this one's.)"""
+    say("case: dynamic exit, graph replays on new inputs")
+    dev = torch.device("cuda")
+    B, K, V = 48, 6, 40000
+    vin = workloads.mixture_inputs("dyn graph", B, K, V, torch.bfloat16, 31, dev, temps=(0.0, 0.6, 1.0),
+                                   lam_lo=0.05, lam_hi=0.6)
+    tgt, dft, x, T = vin.target.clone(), vin.draft.clone(), vin.draft_tokens.clone(), vin.temperature.clone()
+    acc = torch.empty(B, dtype=torch.int32, device=dev)
+    tok = torch.empty(B, K + 1, dtype=torch.int32, device=dev)
+    ws = sv.make_workspace(B, K, V, dev)
+    a = sv.verify_args(tgt, dft, x, T, acc, tok, None, ws, seed=8, step=2, phase_starts=DYN)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        assert sv.spec_verify_launch(a, s.cuda_stream) == sv.SPEC_OK
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        assert sv.spec_verify_launch(a, torch.cuda.current_stream().cuda_stream) == sv.SPEC_OK
+    for rep in range(5):
+        nin = workloads.mixture_inputs("dyn graph %d" % rep, B, K, V, torch.bfloat16, 40 + rep, dev,
+                                       temps=(0.0, 0.6, 1.0), lam_lo=0.05, lam_hi=0.6)
+        tgt.copy_(nin.target)
+        dft.copy_(nin.draft)
+        x.copy_(nin.draft_tokens)
+        T.copy_(nin.temperature)
+        acc.fill_(-5)
+        tok.fill_(-5)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        a1, t1, _ = sv.verify(nin.target, nin.draft, nin.draft_tokens, nin.temperature, seed=8, step=2)
+        torch.cuda.synchronize()
+        assert torch.equal(acc, a1) and torch.equal(tok, t1), rep
+    say("  5 replays on new inputs equal to the eager one pass")

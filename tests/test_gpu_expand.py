@@ -185,8 +185,9 @@ def test_chained_after_verify(sv):
     assert_same(out, ref)
 
 
-def test_chained_step_graph_capture(sv):
-    """verify (early-exit phases) -> expand (bonus from the verify tokens, KV
+@pytest.mark.parametrize("phase_starts", [0b100100, 1])
+def test_chained_step_graph_capture(sv, phase_starts):
+    """verify (early-exit phases, or the dynamic exit) -> expand (bonus from the verify tokens, KV
     slot mapping) chained on one stream with no host round trip, captured
     into a HIP graph and replayed: every replay, with eager work and a reset
     of the outputs between replays, must reproduce the eager outputs."""
@@ -202,7 +203,7 @@ def test_chained_step_graph_capture(sv):
     ws = sv.make_workspace(B, K, V, dev)
     out = sv.expand_outputs(B, K, e.N_in, e.H, dev, with_slots=True)
     va = sv.verify_args(vin.target, vin.draft, vin.draft_tokens, vin.temperature, acc, tok, None, ws,
-                        seed=21, step=3, phase_starts=0b100100)
+                        seed=21, step=3, phase_starts=phase_starts)
     xa = sv.expand_args(e.in_token_ids, e.in_positions, e.in_start, acc, None, K, e.mask_id, e.target_hidden,
                         e.mask_hidden, out, verify_tokens=tok, block_table=bt, block_size=16)
 

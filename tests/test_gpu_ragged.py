@@ -59,7 +59,7 @@ def test_ragged_parity(sv, dtype, V):
     inp = workloads.mixture_inputs("ragged B16 K6 V%d" % V, 16, 6, V, dtype, 7, "cuda",
                                    temps=(0.0, 0.6, 1.0), lam_lo=0.05, lam_hi=0.5)
     kb, x = ragged(inp, 7)
-    for mask in (0, 0b0010100, 0b1111110):
+    for mask in (0, 0b0010100, 0b1111110, sv.SPEC_PHASES_DYNAMIC):
         for step in range(2):
             check(sv, inp, kb, x, 4, step, mask)
 
@@ -69,7 +69,7 @@ def test_full_counts_equal_no_table(sv):
     inp = workloads.mixture_inputs("full", 12, 5, 33000, torch.bfloat16, 2, "cuda", temps=(0.0, 1.0),
                                    lam_lo=0.1, lam_hi=0.5)
     full = torch.full((12,), 5, dtype=torch.int32, device="cuda")
-    for mask in (0, 0b100100):
+    for mask in (0, 0b100100, sv.SPEC_PHASES_DYNAMIC):
         a = sv.verify(inp.target, inp.draft, inp.draft_tokens, inp.temperature, seed=1, debug=True,
                       phase_starts=mask)
         b = sv.verify(inp.target, inp.draft, inp.draft_tokens, inp.temperature, seed=1, debug=True,
@@ -83,7 +83,7 @@ def test_invalid_counts(sv):
     inp = workloads.mixture_inputs("bad", 6, 4, 5000, torch.float32, 3, "cuda", temps=(0.0, 1.0),
                                    lam_lo=0.1, lam_hi=0.5)
     kb = torch.tensor([-1, 5, 0, 4, 2, 1], dtype=torch.int32, device="cuda")
-    for mask in (0, 0b00110):
+    for mask in (0, 0b00110, sv.SPEC_PHASES_DYNAMIC):
         acc, tok, _ = sv.verify(inp.target, inp.draft, inp.draft_tokens, inp.temperature, seed=2,
                                 phase_starts=mask, num_drafts=kb)
         acc, tok = acc.cpu().numpy(), tok.cpu().numpy()
@@ -93,8 +93,9 @@ def test_invalid_counts(sv):
 
 
 def test_headline_ragged_planned(sv):
-    """B=256, K=8, V=151936 bf16 with K_b uniform in 0..8 and the early-exit
-    plan of the benchmark; 24 requests against the oracle."""
+    """B=256, K=8, V=151936 bf16 with K_b uniform in 0..8, in one pass, with
+    an early-exit plan and with the dynamic exit; 24 requests against the
+    oracle."""
     say("case: ragged K headline B256 K8 V151936")
     inp = workloads.verify_headline(seed=1, device="cuda")
     kb, x = ragged(inp, 11)
@@ -103,3 +104,5 @@ def test_headline_ragged_planned(sv):
     a1, t1 = check(sv, inp, kb, x, 0, 0, 0, idx)
     a2, t2 = check(sv, inp, kb, x, 0, 0, 0b100100, idx)
     assert np.array_equal(a1, a2) and np.array_equal(t1, t2)
+    a3, t3 = check(sv, inp, kb, x, 0, 0, sv.SPEC_PHASES_DYNAMIC, idx)
+    assert np.array_equal(a1, a3) and np.array_equal(t1, t3)

@@ -80,6 +80,30 @@ def test_invalid_requests(sv):
         assert acc[b] == -1 and (tok[b] == -1).all()
 
 
+def test_rows_past_the_stop_sharded(sv):
+    """As unsharded: a row without a finite maximum, or with a NaN, past the
+    position where a request stops leaves it valid; at the stop, or in the
+    bonus row of a request that accepts everything, it makes it invalid
+    (explainer page, section "核心思想").  Two shards, one pass and phased."""
+    say("case: vocab-sharded verify, rows past the stop")
+    B, K, V = 6, 3, 4000
+    g = torch.Generator().manual_seed(23)
+    t = torch.randn(B, K + 1, V, generator=g)
+    d = t.clone()
+    t[:4, 0, 2000:] = -float("inf")  # requests 0..3: position 0 rejects (x_0 outside p_0's support)
+    d[:4, 0, :2000] = -float("inf")
+    x = torch.randint(0, V, (B, K), generator=g, dtype=torch.int32)
+    x[:4, 0] = torch.randint(2000, V, (4,), generator=g, dtype=torch.int32)
+    t[0, 2, 5] = float("nan")   # past the stop (slice 0)
+    d[1, 1, :] = -float("inf")  # past the stop
+    t[2, 0, :] = -float("inf")  # at the stop: invalid
+    t[5, K, :] = -float("inf")  # request 5 accepts everything: its bonus row is invalid
+    T = torch.full((B,), 0.9)
+    for mask in (0, 0b0100):
+        acc, tok, _ = sv.verify_sharded(t.cuda(), d.cuda(), x.cuda(), T.cuda(), 2, phase_starts=mask)
+        assert list(acc.cpu().numpy()) == [0, 0, -1, 0, K, -1], (bin(mask), acc.cpu().numpy())
+
+
 def test_headline_sharded_tp4(sv):
     """B=256, K=8, V=151936 bf16 over 4 shards (a TP = 4 target): 24 requests
     against the oracle, and the share identical to the unsharded launch."""

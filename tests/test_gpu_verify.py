@@ -228,7 +228,7 @@ def test_invalid_requests(sv):
     x[2, 0] = -5
     T[3] = -1.0
     T[4] = float("nan")
-    t[5, 1, :] = -float("inf")
+    t[5, 0, :] = -float("inf")  # a row every sampled request reads
     acc, tok, dbg = run(sv, t, inp.draft, x, T)
     assert acc[0] >= 0
     for b in range(1, 6):

@@ -53,7 +53,8 @@ def test_noalloc_matches_the_workspace_call(sv):
     say("case: no-alloc verify, headline batch then a smaller one (workspace %d of %d bytes)"
         % (need, sv.SPEC_NOALLOC_SCRATCH_BYTES))
     assert need <= sv.SPEC_NOALLOC_SCRATCH_BYTES
-    for inp, seed, step, cut in ((big, 1, 0, 0), (small, 2, 5, 0), (big, 3, 7, 0b1000), (small, 4, 1, 0b100)):
+    for inp, seed, step, cut in ((big, 1, 0, 0), (small, 2, 5, 0), (big, 3, 7, 0b1000), (small, 4, 1, 0b100),
+                                 (big, 5, 2, sv.SPEC_PHASES_DYNAMIC), (small, 6, 3, sv.SPEC_PHASES_DYNAMIC)):
         (a1, t1, d1), (a2, t2, d2) = both(sv, inp, seed, step, cut)
         assert torch.equal(a1, a2) and torch.equal(t1, t2) and torch.equal(d1, d2), (inp.name, seed, step, cut)
         assert (a1 >= 0).all()
@@ -84,7 +85,7 @@ def test_noalloc_under_graph_capture(sv):
     inp = workloads.mixture_inputs("graph", 32, 8, 32768, torch.bfloat16, 21, "cuda", temps=(0.0, 0.6, 1.0),
                                    lam_lo=0.05, lam_hi=0.6)
     B, K = 32, 8
-    for cut in (0, 0b100100):
+    for cut in (0, 0b100100, sv.SPEC_PHASES_DYNAMIC):
         acc = torch.empty(B, dtype=torch.int32, device="cuda")
         tok = torch.empty(B, K + 1, dtype=torch.int32, device="cuda")
         a = sv.verify_args(inp.target, inp.draft, inp.draft_tokens, inp.temperature, acc, tok, None, None,
