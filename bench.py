@@ -71,9 +71,10 @@ def parse():
                     help="skip the separate measurement of one GPU's share of a 4-way vocab-sharded verification")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="approximate CPU-seconds of oracle work for the CPU baseline")
-    ap.add_argument("--early-exit", choices=("plan", "off"), default="plan",
+    ap.add_argument("--early-exit", choices=("plan", "off", "dynamic"), default="plan",
                     help="plan: read rows in phases planned from the acceptance of the warmup steps; "
-                         "off: one pass over every row")
+                         "off: one pass over every row; dynamic: decisions inside the row pass (no plan; the "
+                         "rows read are not counted, so frac is left out)")
     ap.add_argument("--phase-starts", type=int, default=None,
                     help="with --early-exit plan: use this phase mask (bit k starts a phase at draft position k) "
                          "instead of the one planned from the acceptance curve")
@@ -328,7 +329,8 @@ def verify_config(sv, torch, np, name, copies, steps=20, seed=0):
     out = {"workload": name, "B": B, "K": K, "V": V, "dtype": "bf16" if es == 2 else "f32",
            "input_copies": len(copies), "steps": steps}
     res = {}
-    for m in sorted({0, planned}):
+    dyn = sv.SPEC_PHASES_DYNAMIC
+    for m in sorted({0, planned, dyn}):
         mask["m"] = m
         for i in range(3):
             launch(6_000_000 + i, None)
@@ -338,7 +340,8 @@ def verify_config(sv, torch, np, name, copies, steps=20, seed=0):
         for i in range(steps):  # outputs depend only on (seed, step): the rows each timed step read
             launch(i, None)
             a_np = acc.cpu().numpy()
-            read.append(phased_logit_bytes(a_np, temps, m, K, V, es))
+            # the dynamic exit's rows depend on timing: no exact count (the sequential minimum bounds it)
+            read.append(phased_logit_bytes(a_np, temps, m, K, V, es) if m != dyn else float("nan"))
             seq.append(sequential_logit_bytes(a_np, temps, K, V, es))
         stage = float(np.mean(k1))
         res[m] = {"ms_per_step": ms, "row_stage_ms": stage, "row_stage_p10_p90": [float(np.percentile(k1, 10)),
@@ -357,6 +360,9 @@ def verify_config(sv, torch, np, name, copies, steps=20, seed=0):
         "frac_seq_min": p["seq_bytes"] / (p["row_stage_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
         "one_pass": {"ms_per_step": res[0]["ms_per_step"], "row_stage_ms": res[0]["row_stage_ms"],
                      "frac": alg / (res[0]["row_stage_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS},
+        "dynamic": {"ms_per_step": res[dyn]["ms_per_step"], "row_stage_ms": res[dyn]["row_stage_ms"],
+                    "frac_seq_min": res[dyn]["seq_bytes"] / (res[dyn]["row_stage_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                    "positions_per_s": B * K / (res[dyn]["ms_per_step"] * 1e-3)},
         "plan_is_fastest": p["ms_per_step"] <= min(r["ms_per_step"] for r in res.values()),
         "mean_accepted": p["mean_accepted"]})
     return out
@@ -686,6 +692,8 @@ def headline(args, sv, torch, np, workloads):
             plan["mask"] = args.phase_starts
         plan["survival"] = [round(v, 4) for v in surv]
         plan["phase_cost_rows"] = round(cost, 4)
+    elif args.early_exit == "dynamic":
+        plan["mask"] = sv.SPEC_PHASES_DYNAMIC
     for i in range(args.warmup):
         step(1_000_000 + i)
     torch.cuda.synchronize()
@@ -732,6 +740,21 @@ def headline(args, sv, torch, np, workloads):
         step(4_000_000 + i, e4)
     torch.cuda.synchronize()
     k1o = np.array([e[0].elapsed_time(e[1]) for e in ev1])
+    # the dynamic early exit (decisions inside the row pass, no plan) on the step numbers of the timed
+    # steps with events, every event recorded
+    plan["mask"] = sv.SPEC_PHASES_DYNAMIC
+    for i in range(5):
+        step(7_000_000 + i)
+    evd = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in timed_with_events]
+    for e4 in evd:  # create the underlying HIP events
+        for e in e4:
+            e.record(stream)
+    torch.cuda.synchronize()
+    for i, e4 in zip(timed_with_events, evd):
+        step(i, e4)
+    torch.cuda.synchronize()
+    k1d = np.array([e[0].elapsed_time(e[1]) for e in evd])
+    k2d = np.array([e[1].elapsed_time(e[2]) for e in evd])
     plan["mask"] = saved_mask
     gbs = alg_bytes / (float(k1o.mean()) * 1e-3) / 1e9
     one_pass = {"ms": float(k1o.mean()), "ms_median": float(np.median(k1o)), "achieved": gbs,
@@ -744,8 +767,12 @@ def headline(args, sv, torch, np, workloads):
         step(i)
         acc_steps.append(accepted.cpu().numpy().copy())
     # the bytes of the steps whose stages the events timed
-    read_bytes = float(np.mean([phased_logit_bytes(acc_steps[i], temps, mask, K, V, 2) for i in timed_with_events]))
+    dyn_mode = mask == sv.SPEC_PHASES_DYNAMIC
     seq_bytes = float(np.mean([sequential_logit_bytes(acc_steps[i], temps, K, V, 2) for i in timed_with_events]))
+    # the dynamic exit's rows depend on timing and are not counted: its frac is taken on the
+    # sequential minimum, a lower bound of what it read
+    read_bytes = seq_bytes if dyn_mode else float(
+        np.mean([phased_logit_bytes(acc_steps[i], temps, mask, K, V, 2) for i in timed_with_events]))
     vbytes = algorithmic_verify_bytes(B, K, V, 2, temps)
     ebytes = algorithmic_expand_bytes(B, K, H, B * (K + 1))
     k1_ms = float(k1.mean())
@@ -779,10 +806,15 @@ def headline(args, sv, torch, np, workloads):
                      "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "frac_seq_min": seq_bytes / (k1_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
                      "traffic": traffic, "traffic_from_profiles": traffic_src,
-                     "plan_read_bytes": read_bytes, "algorithmic_bytes": alg_bytes,
+                     "plan_read_bytes": None if dyn_mode else read_bytes, "algorithmic_bytes": alg_bytes,
                      "sequential_min_bytes": seq_bytes, "stage_ms": k1_ms, "one_pass_row_kernel": one_pass},
         "early_exit": {"phase_starts": mask, "phases": [0] + [k for k in range(1, K + 1) if (mask >> k) & 1],
                        **{k: v for k, v in plan.items() if k != "mask"}},
+        # the same steps with the dynamic exit: row stage and sampling stage from events on every step
+        # (each event costs GPU time: compare with the plan's stages, not with ms_per_step)
+        "early_exit_dynamic": {"phase_starts": sv.SPEC_PHASES_DYNAMIC, "steps": len(evd),
+                               "row_stage_ms": float(k1d.mean()), "sampling_stage_ms": float(k2d.mean()),
+                               "frac_seq_min": seq_bytes / (float(k1d.mean()) * 1e-3) / 1e9 / HBM_PEAK_GBS},
         "kernels_ms": {"timed_steps_with_events": len(timed_with_events), "event_every": every,
                        "verify_row_stage": k1_ms, "later_stages_timed_on": "24 further steps of the same plan",
                        ("sampling_stage_with_expansion" if chained else "verify_decide_and_draw"): float(k2.mean()),
