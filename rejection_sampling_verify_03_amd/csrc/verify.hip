@@ -8,9 +8,10 @@
 // target argmax, emit the target argmax where the request stops).
 //
 // Four kernels in stream order, no host round trip, and no communication
-// between workgroups of one kernel (each kernel boundary makes the previous
-// kernel's writes visible, so no cache-maintenance fences; the one device
-// atomic counts invalid requests for the host to read after the stream):
+// between workgroups of one kernel but in the dynamic early exit below (each
+// kernel boundary makes the previous kernel's writes visible, so no
+// cache-maintenance fences; a device atomic counts invalid requests for the
+// host to read after the stream):
 //
 //  verify_rowstats  one 256-thread workgroup per (request, row, chunk of ~32K
 //      logits) streams every row the parallel formulation needs exactly once
@@ -44,7 +45,8 @@
 // pass then runs once per phase over the phase's rows, skipping requests that
 // already stopped, and verify_phase runs the phase's accept tests in between
 // (one workgroup per request), leaving a per-request state for the next
-// phase and for the final decision.
+// phase and for the final decision.  Or the row pass takes the decisions
+// itself as its rows come in (verify_rowstats_dyn_kernel), with no phases.
 #include <float.h>
 #include <limits.h>
 
