@@ -229,7 +229,8 @@ def algorithmic_expand_bytes(B, K, H, n_in):
 ROWPASS_SOURCES = ["rejection_sampling_verify_03_amd/csrc/verify.hip", "rejection_sampling_verify_03_amd/csrc/device_common.hpp",
                    "rejection_sampling_verify_03_amd/csrc/verify_layout.hpp",
                    "rejection_sampling_verify_03_amd/csrc/verify_kernels.hpp",
-                   "rejection_sampling_verify_03_amd/csrc/rowpass.hpp"]
+                   "rejection_sampling_verify_03_amd/csrc/rowpass.hpp",
+                   "rejection_sampling_verify_03_amd/csrc/decision.hpp"]
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "verify_rowstats_traffic.md")
 
 
