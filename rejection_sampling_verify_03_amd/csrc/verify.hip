@@ -472,6 +472,8 @@ __global__ __launch_bounds__(kWG) void verify_rowstats_kernel(VerifyParams P) {
 // which rows the deciders let the pass skip.
 struct DynShared {
   uint64_t sw;  // the request's state word as the decider read it
+  uint64_t swv[kWaves];  // the state word as each wave of a chunk workgroup read it
+  unsigned char skipv[kWaves];
   float m[kWG];
   int32_t idx[kWG];
   double s[kWG];
@@ -657,20 +659,33 @@ __global__ __launch_bounds__(kWG) void verify_rowstats_dyn_kernel(VerifyParams P
   const int b = g, k = J, c = sl % C1;
   const bool draft_row = sl >= C1;
   const int r = draft_row ? K + 1 + k : k;
+  // every wave reads the state word, and the waves then agree on the largest
+  // value any of them saw: a decision may land between two waves' reads, and
+  // the waves must agree on whether to skip (the block reduction below has
+  // barriers); the word only moves forward, so the largest is the newest
   const uint64_t sw = load_coherent(P.dstate + b);
   const float T = P.temperature[b];
   const int xt = P.tokens[(int64_t)b * K + min(k, K - 1)];
   const int di = draft_entry(P, b, k);
   const int kb = drafts_of(P, b);
   const bool greedy = (T == 0.0f);
+  // skip as the phased pass does (then, below, every row past a known stop)
+  const bool skip_rows = (greedy & draft_row) | ((k < kb) & ((uint32_t)xt >= (uint32_t)P.V)) |
+                         (draft_row & !draft_entry_ok(P, di)) | (kb < 0) | (!draft_row & (k > kb)) |
+                         (draft_row & (k >= kb));
+  if ((threadIdx.x & 63) == 0) {
+    ds.skipv[threadIdx.x >> 6] = skip_rows;  // first: its loads go out before the state word is awaited
+    ds.swv[threadIdx.x >> 6] = sw;
+  }
   if (bid == 0 && threadIdx.x == 0) *P.err = 0;  // counted by the final decision
+  __syncthreads();
+  if (skip_rows) return;  // the same in every wave: plain inputs
+  uint64_t swm = ds.swv[0];
+#pragma unroll
+  for (int w = 1; w < kWaves; ++w) swm = max(swm, ds.swv[w]);
   int n, f;
-  dstate_read(sw, E, K, n, f);
-  // skip as the phased pass does, and every row past a known stop
-  const bool skip = (greedy & draft_row) | ((f != 0) & (n < k)) | ((k < kb) & ((uint32_t)xt >= (uint32_t)P.V)) |
-                    (draft_row & !draft_entry_ok(P, di)) | (kb < 0) | (!draft_row & (k > kb)) |
-                    (draft_row & (k >= kb));
-  if (skip) return;
+  dstate_read(swm, E, K, n, f);
+  if ((f != 0) & (n < k)) return;
   dyn_chunk<ES, VEC>(P, b, r, c, k < kb ? xt : -1, greedy, T, di, E);
 }
 
