@@ -13,7 +13,8 @@ Checks (explainer page, section "一轮能赚多少": a round yields
     and the exact expectation;
   * beta_hat lands within 0.03 of its target;
   * steps 0 and 99 match the oracle on every request, and a planned
-    early-exit cut of the same steps is bit-identical to one pass.
+    early-exit cut and the dynamic exit of the same steps are bit-identical
+    to one pass.
 """
 import sys
 import time
@@ -99,8 +100,11 @@ def test_beta_sweep_closed_form(sv, beta):
             mask = sv.spec_verify_plan_phases(K, surv, 1.0, 0.2) or 0b1000
             acc2, tok2, _ = sv.verify(inp.target, inp.draft, x, inp.temperature, seed=3, step=s, workspace=ws,
                                       phase_starts=mask)
+            acc3, tok3, _ = sv.verify(inp.target, inp.draft, x, inp.temperature, seed=3, step=s, workspace=ws,
+                                      phase_starts=sv.SPEC_PHASES_DYNAMIC)
             torch.cuda.synchronize()
             assert torch.equal(acc, acc2) and torch.equal(tok, tok2), (s, mask)
+            assert torch.equal(acc, acc3) and torch.equal(tok, tok3), (s, "dynamic")
             if tl is None:
                 tl, dl = workloads.logits_numpy(inp.target), workloads.logits_numpy(inp.draft)
             rep = Report()
