@@ -272,3 +272,19 @@ def test_dynamic_exit_graph_replays_on_new_inputs(sv):
         torch.cuda.synchronize()
         assert torch.equal(acc, a1) and torch.equal(tok, t1), rep
     say("  5 replays on new inputs equal to the eager one pass")
+
+
+@pytest.mark.parametrize("B,K,V,dtype", [(1, 1, 9, torch.float32), (3, 2, 9, torch.bfloat16),
+                                         (2, 1, 4_300_000, torch.bfloat16), (5, 3, 302151, torch.bfloat16)])
+def test_dynamic_exit_edge_shapes(sv, B, K, V, dtype):
+    """The dynamic exit at the edges of its grid: one request, one draft, a
+    row of one chunk, rows of more chunks than a decider can load at once
+    (V = 4.3M: 132 chunks a row, so no decision is taken and every row is
+    read) and of ten; bit-identical to one pass, and against the oracle."""
+    say("case: dynamic exit B%d K%d V%d %s" % (B, K, V, dtype))
+    inp = workloads.mixture_inputs("dyn edge", B, K, V, dtype, 5 + K, "cuda", temps=(0.0, 0.7, 1.0),
+                                   lam_lo=0.05, lam_hi=0.6)
+    for step in range(3):
+        acc, tok = one_vs_phased(sv, inp, DYN, seed=2, step=step)
+        if V < 1_000_000 or step == 0:
+            oracle_check(inp, acc, tok, 2, step)
