@@ -642,15 +642,17 @@ template <int ES, bool VEC>
 __global__ __launch_bounds__(kWG) void verify_rowstats_dyn_kernel(VerifyParams P) {
   __shared__ DynShared ds;
   const int K = P.K, C1 = P.C1;
+  // 32-bit index arithmetic (the grid fits, checked on the host): it runs
+  // before the first load of every workgroup
   const int wm = (P.dstats ? 1 : 2) * C1 + 1, wl = C1 + 1;
-  const int64_t span = (int64_t)P.B * wm;
-  const int64_t bid = blockIdx.x;
-  const int J = (int)min(bid / span, (int64_t)K);
-  const int64_t rem = bid - (int64_t)J * span;
+  const int span = P.B * wm;
+  const int bid = (int)blockIdx.x;
+  const int J = min(bid / span, K);
+  const int rem = bid - J * span;
   const int W = J < K ? wm : wl;
   // the roles inside a group rotate with the group, so that no role keeps to
   // one XCD when W is a multiple of the 8 the hardware deals workgroups to
-  const int g = (int)(rem / W), sl = (int)((rem % W + g) % W);
+  const int g = rem / W, sl = (rem - g * W + g) % W;
   const uint64_t E = *P.epoch;
   if (sl == W - 1) {
     dyn_decider<ES>(P, J, g, E, ds);
