@@ -288,3 +288,38 @@ def test_dynamic_exit_edge_shapes(sv, B, K, V, dtype):
         acc, tok = one_vs_phased(sv, inp, DYN, seed=2, step=step)
         if V < 1_000_000 or step == 0:
             oracle_check(inp, acc, tok, 2, step)
+
+
+def test_dynamic_exit_random_shapes(sv):
+    """Twenty seeded random shapes (B, K, V, dtype, temperatures, ragged
+    counts or not, seed and step): the dynamic exit bit-identical to one pass
+    on every output, debug probabilities up to each stop included."""
+    say("case: dynamic exit, random shapes")
+    rng = np.random.default_rng(2026)
+    for it in range(20):
+        B = int(rng.integers(1, 300))
+        K = int(rng.integers(1, 12))
+        V = int(rng.choice([37, 1000, 4096, 33000, 70001, 151936]))
+        dtype = torch.bfloat16 if rng.random() < 0.7 else torch.float32
+        temps = (0.0, 0.6, 1.0) if rng.random() < 0.7 else (1.0,)
+        inp = workloads.mixture_inputs("rand %d" % it, B, K, V, dtype, 100 + it, "cuda", temps=temps,
+                                       lam_lo=0.05, lam_hi=0.7)
+        kw = {}
+        if rng.random() < 0.4:
+            kb = torch.from_numpy(rng.integers(0, K + 1, B).astype(np.int32)).cuda()
+            kw["num_drafts"] = kb
+        seed, step = int(rng.integers(0, 2**63)), int(rng.integers(0, 2**32))
+        a1, t1, d1 = sv.verify(inp.target, inp.draft, inp.draft_tokens, inp.temperature, seed=seed, step=step,
+                               debug=True, **kw)
+        a2, t2, d2 = sv.verify(inp.target, inp.draft, inp.draft_tokens, inp.temperature, seed=seed, step=step,
+                               debug=True, phase_starts=DYN, **kw)
+        torch.cuda.synchronize()
+        assert torch.equal(a1, a2) and torch.equal(t1, t2), (it, B, K, V, dtype)
+        a = a1.cpu().numpy()
+        d1, d2 = d1.cpu().numpy(), d2.cpu().numpy()
+        for b in range(B):
+            if a[b] >= 0:
+                n = min(int(a[b]) + 1, K)
+                assert np.array_equal(d1[b, :n], d2[b, :n]) and (d2[b, n:] == 0).all(), (it, b)
+        say("  %2d: B=%d K=%d V=%d %s ragged=%s accepted %s" % (it, B, K, V, str(dtype)[6:], "num_drafts" in kw,
+                                                           np.bincount(a[a >= 0], minlength=K + 1)))
