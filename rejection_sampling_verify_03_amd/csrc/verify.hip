@@ -681,7 +681,7 @@ __global__ __launch_bounds__(kWG) void verify_rowstats_dyn_kernel(VerifyParams P
   }
   if (bid == 0 && threadIdx.x == 0) *P.err = 0;  // counted by the final decision
   __syncthreads();
-  if (skip_rows) return;  // the same in every wave: plain inputs
+  if (ds.skipv[0]) return;  // the same in every wave: plain inputs
   uint64_t swm = ds.swv[0];
 #pragma unroll
   for (int w = 1; w < kWaves; ++w) swm = max(swm, ds.swv[w]);
