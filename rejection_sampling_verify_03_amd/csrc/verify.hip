@@ -401,10 +401,22 @@ __global__ __launch_bounds__(kWG) void verify_phase_kernel(VerifyParams P) {
 
 template <int ES, bool VEC>
 __global__ __launch_bounds__(kWG) void verify_rowstats_kernel(VerifyParams P) {
-  const int nr = P.ph_nt + P.ph_rd;
-  const int c = blockIdx.x % P.C1;
-  const int lr = (blockIdx.x / P.C1) % nr;
-  const int b = blockIdx.x / (P.C1 * nr);
+  // a 3D grid (chunk, row, request), in the order of the linear index, so
+  // that no integer division precedes the first load; batches past the
+  // grid's 65535 in z use the linear index instead (x then spans every
+  // workgroup, which a 3D grid's x only does for one row of one request, where
+  // both readings agree)
+  int c, lr, b;
+  if ((int)gridDim.x == P.C1) {
+    c = blockIdx.x;
+    lr = blockIdx.y;
+    b = blockIdx.z;
+  } else {
+    const int nr = P.ph_nt + P.ph_rd;
+    c = blockIdx.x % P.C1;
+    lr = (blockIdx.x / P.C1) % nr;
+    b = blockIdx.x / (P.C1 * nr);
+  }
   const int r = lr < P.ph_nt ? P.ph_lo + lr : P.K + 1 + P.ph_lo + (lr - P.ph_nt);
   const int k = lr < P.ph_nt ? r : r - P.K - 1;  // position of the row
   // three independent loads, unconditional and all feeding one branch so that
@@ -421,7 +433,8 @@ __global__ __launch_bounds__(kWG) void verify_rowstats_kernel(VerifyParams P) {
   // row >= K_b: they do not exist), and rows of a request whose draft count,
   // draft token or draft row entry is out of range (the request is invalid;
   // no statistic is used)
-  if (blockIdx.x == 0 && threadIdx.x == 0 && P.ph_lo == 0) *P.err = 0;  // counted by the final decision
+  if ((blockIdx.x | blockIdx.y | blockIdx.z) == 0 && threadIdx.x == 0 && P.ph_lo == 0)
+    *P.err = 0;  // counted by the final decision
   const bool skip = (greedy & (r > P.K)) | ((P.ph_check != 0) & (st != kStateAlive)) |
                     ((k < kb) & ((uint32_t)xt >= (uint32_t)P.V)) | ((r > P.K) & !draft_entry_ok(P, di)) |
                     (kb < 0) | ((r <= P.K) & (k > kb)) | ((r > P.K) & (k >= kb));
@@ -898,8 +911,10 @@ static hipError_t launch_typed(VerifyParams P, uint64_t phase_starts, hipEvent_t
     P.ph_nd = min(hi, K) - lo;
     P.ph_rd = P.dstats ? 0 : P.ph_nd;  // with draft statistics the draft rows are not read here
     P.ph_check = j > 0;
-    const int64_t g1 = (int64_t)P.B * (P.ph_nt + P.ph_rd) * P.C1;
-    hipLaunchKernelGGL((verify_rowstats_kernel<ES, VEC>), dim3((unsigned)g1), dim3(kWG), 0, stream, P);
+    const int nr = P.ph_nt + P.ph_rd;
+    const dim3 g1 = P.B <= 65535 ? dim3((unsigned)P.C1, (unsigned)nr, (unsigned)P.B)
+                                 : dim3((unsigned)((int64_t)P.B * nr * P.C1));
+    hipLaunchKernelGGL((verify_rowstats_kernel<ES, VEC>), g1, dim3(kWG), 0, stream, P);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (hi <= K) {
