@@ -485,13 +485,14 @@ __global__ __launch_bounds__(kWG) void verify_rowstats_kernel(VerifyParams P) {
 // which rows the deciders let the pass skip.
 struct DynShared {
   uint64_t sw;  // the request's state word as the decider read it
-  uint64_t swv[kWaves];  // the state word as each wave of a chunk workgroup read it
-  unsigned char skipv[kWaves];
+  uint64_t swv[kWaves];         // the state word as each wave of a chunk workgroup read it
+  unsigned char skipv[kWaves];  // a chunk workgroup's row skipped for its own reasons
+  // one record per thread of a decider: (position - p0) * 2 C1 + row kind * C1 + chunk
   float m[kWG];
   int32_t idx[kWG];
   double s[kWG];
-  unsigned char ok[kWG];
-  // merged rows, (position - n0) * rows + row kind
+  unsigned char ok[kWG];  // all four words carry this launch's tag
+  // merged rows of a decider's window: (position - p0) * 2 + row kind
   float rm[2 * 64];
   double rs[2 * 64];
   float rz[2 * 64];
