@@ -235,11 +235,18 @@ TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "verify_rowstats_traffic.md")
 
 
 def rowpass_source_hash():
+    """Hash of the row-pass sources as code: comments and whitespace are left
+    out, so that a reworded comment does not set the committed counters
+    aside."""
     import hashlib
+    import re
     h = hashlib.sha256()
     for f in ROWPASS_SOURCES:
-        with open(os.path.join(ROOT, f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, f), encoding="utf-8") as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)  # block comments
+        text = re.sub(r"//[^\n]*", " ", text)                # line comments
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 
