@@ -328,11 +328,22 @@ def test_draft_stats_records(sv):
             assert abs(s[b, k] / want - 1) < 1e-6, (b, k)
             assert np.float32(zb[b, k].view(np.float32)) == np.float32(row[xs[b, k]]), (b, k)
     assert xs[0, 2] == -1
-    # a record without a finite normaliser: that sampled request is invalid
-    bad = stats.clone()
+    # a record without a finite normaliser: the sampled request is invalid
+    # when it reaches that position (position 0 always is), and not when it
+    # stops before it
+    a0, t0, _ = sv.verify(vin.target, buf, x, vin.temperature, draft_row_index=ridx_bad, draft_stats=stats)
+    a0 = a0.cpu().numpy()
     sampled = [b for b in range(B) if T[b] > 0 and (xs[b] >= 0).all()]
     vb = sampled[0]
-    bad.view(B, K, 16)[vb, 1, 8:16] = 0
+    bad = stats.clone()
+    bad.view(B, K, 16)[vb, 0, 8:16] = 0
     a, t, _ = sv.verify(vin.target, buf, x, vin.temperature, draft_row_index=ridx_bad, draft_stats=bad)
     a = a.cpu().numpy()
     assert a[vb] == -1
+    past = [b for b in sampled if a0[b] < K - 1]
+    if past:
+        pb = past[0]
+        bad = stats.clone()
+        bad.view(B, K, 16)[pb, a0[pb] + 1, 8:16] = 0
+        a, t, _ = sv.verify(vin.target, buf, x, vin.temperature, draft_row_index=ridx_bad, draft_stats=bad)
+        assert a.cpu().numpy()[pb] == a0[pb] and torch.equal(t[pb], t0[pb]), pb
