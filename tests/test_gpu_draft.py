@@ -341,8 +341,10 @@ def test_draft_stats_records(sv):
     a = a.cpu().numpy()
     assert a[vb] == -1
     past = [b for b in sampled if a0[b] < K - 1]
+    assert past, "the seeded batch has a sampled request that stops before its last draft"
     if past:
         pb = past[0]
+        say("  request %d stops at %d; a bad record at %d leaves it as it was" % (pb, a0[pb], a0[pb] + 1))
         bad = stats.clone()
         bad.view(B, K, 16)[pb, a0[pb] + 1, 8:16] = 0
         a, t, _ = sv.verify(vin.target, buf, x, vin.temperature, draft_row_index=ridx_bad, draft_stats=bad)
