@@ -189,9 +189,11 @@ double spec_verify_phase_cost(int32_t B, int32_t K, int32_t V, int32_t dtype);
  * race.  What it carries from one call to the next: the invalid-request count
  * that spec_workspace_error reads, and a launch counter with per-request
  * words of the dynamic early exit, which tag what a launch wrote so that it
- * is told apart from anything older.  Leftover bytes can only make that mode
- * read more rows, never change an output (a request's rows up to its stop
- * are read unless a leftover word matches this launch's 56-bit tag, and the
+ * is told apart from anything older and from memory never written (zero bytes
+ * never carry a tag).  Leftover bytes can only make that mode read more
+ * rows, never change an output (a request's rows up to its stop are read
+ * unless leftover words match this launch's tags by chance: its 56-bit tag
+ * in a state word, or its 32-bit tag in all four words of a record; the
  * final decision reports a request invalid if that happened). */
 size_t spec_verify_workspace_bytes(int32_t B, int32_t K, int32_t V);
 

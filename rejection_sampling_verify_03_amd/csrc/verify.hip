@@ -114,6 +114,11 @@ __device__ __forceinline__ void dstate_read(uint64_t w, uint64_t E, int K, int& 
   if (n > K || (f && n >= K)) n = f = 0;
 }
 
+// The 32-bit tag of launch E in a record word: odd, so that zeroed memory (a
+// fresh workspace at launch counter 0, or the no-alloc array at load) never
+// passes for a record of any launch; consecutive launches differ.
+__device__ __forceinline__ uint32_t record_tag(uint64_t E) { return (uint32_t)(2 * E + 1); }
+
 // Agent-scope accesses: coherent between workgroups of one launch, whatever
 // their XCD (no cache maintenance, no ordering between different words).
 __device__ __forceinline__ uint64_t load_coherent(const uint64_t* p) {
@@ -527,7 +532,7 @@ __device__ void dyn_decider(const VerifyParams& P, int J, int g, uint64_t E, Dyn
     const uint64_t* wp = P.trec[((int64_t)d * P.R + r) * C1 + c].w;
     const uint64_t w0 = load_coherent(wp), w1 = load_coherent(wp + 1), w2 = load_coherent(wp + 2),
                    w3 = load_coherent(wp + 3);
-    const uint32_t tag = (uint32_t)E;
+    const uint32_t tag = record_tag(E);
     ds.ok[t] = (uint32_t)(w0 >> 32) == tag && (uint32_t)(w1 >> 32) == tag && (uint32_t)(w2 >> 32) == tag &&
                (uint32_t)(w3 >> 32) == tag;
     ds.m[t] = __uint_as_float((uint32_t)w0);
@@ -645,7 +650,7 @@ __device__ __forceinline__ void dyn_chunk(const VerifyParams& P, int b, int r, i
                          : threadIdx.x == 1 ? (uint32_t)part.idx
                          : threadIdx.x == 2 ? (uint32_t)sb
                                             : (uint32_t)(sb >> 32);
-    store_coherent(&P.trec[at].w[threadIdx.x], ((uint64_t)(uint32_t)E << 32) | pay);
+    store_coherent(&P.trec[at].w[threadIdx.x], ((uint64_t)record_tag(E) << 32) | pay);
   }
 }
 

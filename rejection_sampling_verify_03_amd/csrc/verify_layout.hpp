@@ -39,9 +39,10 @@ struct ReqDesc {  // decision of one request, read by the draw
 // (dynamic early exit): four 64-bit words, each stored by one single-copy
 // atomic store and each carrying the launch's 32-bit tag in its high half
 // (payload in the low half: m's bits, idx, the low and the high half of s's
-// bits).  A reader that finds the tag in all four words has the whole record
-// of this launch; anything else (a record still being written, or left by an
-// earlier launch) it treats as not yet there.
+// bits; the tag is odd, so zeroed memory never carries one).  A reader that
+// finds the tag in all four words has the whole record of this launch;
+// anything else (a record still being written, left by an earlier launch, or
+// memory never written) it treats as not yet there.
 struct TaggedPartial {
   uint64_t w[4];
 };

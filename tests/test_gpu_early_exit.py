@@ -323,3 +323,24 @@ def test_dynamic_exit_random_shapes(sv):
                 assert np.array_equal(d1[b, :n], d2[b, :n]) and (d2[b, n:] == 0).all(), (it, b)
         say("  %2d: B=%d K=%d V=%d %s ragged=%s accepted %s" % (it, B, K, V, str(dtype)[6:], "num_drafts" in kw,
                                                            np.bincount(a[a >= 0], minlength=K + 1)))
+
+
+def test_dynamic_exit_first_launch_on_zeroed_workspace(sv):
+    """The first launch on a workspace of zero bytes (a fresh allocation, or
+    the library's own no-alloc array at load) starts from launch counter 0:
+    the record words it has not written yet must not pass for this launch's,
+    so the outputs equal one pass."""
+    say("case: dynamic exit, first launch on a zeroed workspace")
+    dev = torch.device("cuda")
+    B, K, V = 192, 8, 151936
+    inp = workloads.mixture_inputs("dyn zero ws", B, K, V, torch.bfloat16, 77, dev, temps=(0.0, 0.6, 1.0),
+                                   lam_lo=0.05, lam_hi=0.5)
+    a1, t1, _ = sv.verify(inp.target, inp.draft, inp.draft_tokens, inp.temperature, seed=4, step=9)
+    for trial in range(3):
+        ws = torch.zeros(sv.spec_verify_workspace_bytes(B, K, V), dtype=torch.uint8, device=dev)
+        a2, t2, _ = sv.verify(inp.target, inp.draft, inp.draft_tokens, inp.temperature, seed=4, step=9,
+                              workspace=ws, phase_starts=DYN)
+        torch.cuda.synchronize()
+        assert (a2 >= 0).all(), (trial, int((a2 < 0).sum()))
+        assert torch.equal(a1, a2) and torch.equal(t1, t2), trial
+    say("  3 fresh zeroed workspaces: equal to one pass")
