@@ -32,7 +32,8 @@ typedef struct ihipStream_t* hipStream_t;
 
 typedef enum {
   SPEC_OK = 0,
-  SPEC_EINVAL = -1,     /* null pointer, size or stride out of range */
+  SPEC_EINVAL = -1,     /* null pointer, size or stride out of range (also a batch whose kernel
+                           grids would exceed one dispatch's 2^32 work-items) */
   SPEC_EDTYPE = -2,     /* unknown logits dtype */
   SPEC_EALIGN = -3,     /* workspace (or a statistics record array) not 16-byte aligned */
   SPEC_EWORKSPACE = -4, /* workspace smaller than spec_verify_workspace_bytes() */
@@ -202,7 +203,12 @@ size_t spec_verify_workspace_bytes(int32_t B, int32_t K, int32_t V);
  * draft row table entry of a sampled request outside [0, draft_rows), a draft
  * count outside [0, K], or, at a position the request reaches, a row of a
  * sampled request without a finite normaliser) gets accepted_counts = -1,
- * output_tokens all -1 and debug_probs 0. */
+ * output_tokens all -1 and debug_probs 0.  A batch whose kernel grids would
+ * exceed one dispatch (2^32 work-items per launch) returns SPEC_EINVAL before
+ * anything is enqueued: the draw needs B * 512 < 2^32, the segment sums
+ * B * ceil(V / 4096) * 64 < 2^32, and above B = 65535 the row pass needs
+ * B * (2K + 1) * ceil(V / 32768) * 256 < 2^32 (about B = 197K at K = 8,
+ * V = 151936); split larger batches over calls with request_base. */
 int spec_verify_launch(const spec_verify_args* args, hipStream_t stream);
 
 /* For callers that cannot allocate device memory -- code under HIP graph

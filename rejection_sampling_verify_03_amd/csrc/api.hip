@@ -49,6 +49,10 @@ int scratch_address(hipStream_t stream, void** out) {
   return SPEC_OK;
 }
 
+// Whether a grid of `blocks` workgroups of `threads` fits one dispatch
+// (2^32 work-items).
+static bool fits_dispatch(int64_t blocks, int64_t threads) { return blocks * threads <= (int64_t)UINT32_MAX; }
+
 int verify_check(const spec_verify_args* a) {
   if (!a) return SPEC_EINVAL;
   if (a->B < 0 || a->K < 1 || a->K > SPEC_MAX_K || a->V < 1 || a->V > SPEC_MAX_V) return SPEC_EINVAL;
@@ -69,6 +73,9 @@ int verify_check(const spec_verify_args* a) {
   if ((a->phase_starts & 1u) && a->phase_starts != SPEC_PHASES_DYNAMIC) return SPEC_EINVAL;
   if (a->K < 63 && (a->phase_starts >> (a->K + 1)) != 0) return SPEC_EINVAL;
   if ((int64_t)a->B * (L.R * L.C1 + a->K + 1) > INT32_MAX) return SPEC_EINVAL;  // the dynamic pass's grid
+  if (!verify_grids_fit(a->B, a->K, L.C1, L.nseg, a->phase_starts == SPEC_PHASES_DYNAMIC, a->draft_stats != nullptr,
+                        0))
+    return SPEC_EINVAL;
   if (a->workspace_bytes < L.total) return SPEC_EWORKSPACE;
   return SPEC_OK;
 }
@@ -78,6 +85,7 @@ int expand_check(const spec_expand_args* a) {
   if (a->B < 0 || a->K < 1 || a->H < 0 || a->N_in < 0) return SPEC_EINVAL;
   if ((int64_t)a->N_in + (int64_t)a->B * (a->K - 1) > INT32_MAX) return SPEC_EINVAL;
   if (a->B == 0) return SPEC_OK;
+  if (!fits_dispatch(a->B, 256)) return SPEC_EINVAL;  // one 256-thread workgroup per request at least
   if (!a->bonus_tokens == !a->verify_output_tokens) return SPEC_EINVAL;  // exactly one bonus source
   if (!a->in_start || !a->accepted_counts || !a->out_token_ids ||
       !a->out_positions || !a->rejected_mask || !a->masked_mask || !a->new_token_indices || !a->out_start)
@@ -110,6 +118,7 @@ int draft_check(const spec_draft_args* a) {
   const int64_t nseg = ((int64_t)a->V + kSeg - 1) / kSeg;
   const int64_t C = (nseg + kDraftChunkSegs - 1) / kDraftChunkSegs;
   if ((int64_t)a->B * a->K * C > INT32_MAX) return SPEC_EINVAL;
+  if (!fits_dispatch((int64_t)a->B * a->K * C, 256) || !fits_dispatch((int64_t)a->B * a->K, 64)) return SPEC_EINVAL;
   if (!aligned16(a->workspace) || (a->stats_out && !aligned16(a->stats_out))) return SPEC_EALIGN;
   if (a->workspace_bytes < draft_ws_bytes(a->B, a->K, a->V)) return SPEC_EWORKSPACE;
   return SPEC_OK;
@@ -161,6 +170,7 @@ int shard_check(const spec_shard_args* a) {
     return SPEC_EINVAL;
   if (a->draft_row_index && a->draft_rows < 0) return SPEC_EINVAL;
   if ((int64_t)a->B * (2 * a->K + 1) > INT32_MAX) return SPEC_EINVAL;
+  if (!fits_dispatch((int64_t)a->B * (2 * a->K + 1), 256) || !fits_dispatch(a->B, 1024)) return SPEC_EINVAL;
   if (a->phase_starts & 1u) return SPEC_EINVAL;  // position 0 always starts the first phase
   if (a->K < 63 && (a->phase_starts >> (a->K + 1)) != 0) return SPEC_EINVAL;
   if (a->phase < 0 || a->phase >= phase_range(a->phase_starts, a->K, 0).count) return SPEC_EINVAL;
@@ -437,7 +447,7 @@ static ExpandParams expand_params(const spec_expand_args* a, bool hidden_only, i
   int64_t G = (avg_window + rows_per_wg - 1) / rows_per_wg;
   if (G < 1) G = 1;
   if (G > 64) G = 64;
-  if ((int64_t)a->B * G > INT32_MAX) G = 1;
+  if ((int64_t)a->B * G > INT32_MAX || !fits_dispatch((int64_t)a->B * G, 256)) G = 1;
   P.G = (int32_t)G;
   P.ids = a->in_token_ids;
   P.pos = a->in_positions;
@@ -504,6 +514,8 @@ int spec_verify_expand_launch(const spec_verify_args* v, const spec_expand_args*
   P.ex_on = 1;
   P.ex_G = P.ex.G;
   if ((int64_t)P.B * P.nseg + (int64_t)P.B * P.ex_G > INT32_MAX) return SPEC_EINVAL;
+  if (!verify_grids_fit(P.B, P.K, P.C1, P.nseg, P.dyn != 0, P.dstats != nullptr, (int64_t)P.B * P.ex_G))
+    return SPEC_EINVAL;
   return verify_enqueue(P, v, vec, stream);
 }
 

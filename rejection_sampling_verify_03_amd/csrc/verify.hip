@@ -893,6 +893,21 @@ __global__ __launch_bounds__(kWGD) void verify_draw_kernel(VerifyParams P) {
 }
 
 // --------------------------------------------------------------- launch
+// Workgroups of the dynamic row pass: K position blocks of (draft rows read:
+// 2, else 1) x C1 chunks + a decider slot per request, then the bonus block.
+static int64_t dyn_blocks(int64_t B, int64_t K, int64_t C1, bool dstats) {
+  return K * B * ((dstats ? 1 : 2) * C1 + 1) + B * (C1 + 1);
+}
+
+bool verify_grids_fit(int32_t B, int32_t K, int32_t C1, int32_t nseg, bool dyn, bool dstats, int64_t ex_items) {
+  const int64_t kMax = UINT32_MAX;  // work-items of one dispatch
+  const int64_t rows = (int64_t)K + 1 + (dstats ? 0 : K);  // rows of the widest row-pass phase
+  if (B > 65535 && (int64_t)B * rows * C1 * kWG > kMax) return false;  // the linear row-pass grid
+  if (dyn && dyn_blocks(B, K, C1, dstats) * kWG > kMax) return false;
+  if (((int64_t)B * nseg + ex_items) * 64 > kMax) return false;  // segment sums (+ a chained expansion)
+  return (int64_t)B * kWGD <= kMax;  // the draw (the widest per-request launch)
+}
+
 template <int ES, bool VEC>
 static hipError_t launch_typed(VerifyParams P, uint64_t phase_starts, hipEvent_t phase_event,
                                hipStream_t stream) {
@@ -904,7 +919,7 @@ static hipError_t launch_typed(VerifyParams P, uint64_t phase_starts, hipEvent_t
     P.ph_nd = K;
     P.ph_rd = P.dstats ? 0 : K;
     P.ph_check = P.phased = P.last_lo = 0;
-    const int64_t g1 = (int64_t)K * P.B * ((P.dstats ? 1 : 2) * P.C1 + 1) + (int64_t)P.B * (P.C1 + 1);
+    const int64_t g1 = dyn_blocks(P.B, K, P.C1, P.dstats != nullptr);
     hipLaunchKernelGGL((verify_rowstats_dyn_kernel<ES, VEC>), dim3((unsigned)g1), dim3(kWG), 0, stream, P);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

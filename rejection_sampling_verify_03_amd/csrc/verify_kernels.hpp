@@ -152,6 +152,9 @@ hipError_t launch_shard_draw(const ShardParams& P, int dtype, bool vec, hipStrea
 // position k; 0 reads every row in one pass.
 hipError_t launch_verify(const VerifyParams& P, int dtype, bool vec, uint64_t phase_starts,
                          hipEvent_t phase_event, hipStream_t stream);
+// Whether every kernel grid of a verification of this shape fits one dispatch
+// (2^32 work-items); ex_items: the workgroups of a chained expansion.
+bool verify_grids_fit(int32_t B, int32_t K, int32_t C1, int32_t nseg, bool dyn, bool dstats, int64_t ex_items);
 hipError_t launch_expand(const ExpandParams& P, bool vec, hipStream_t stream);
 hipError_t launch_draft(const DraftParams& P, int dtype, bool vec, hipStream_t stream);
 

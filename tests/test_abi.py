@@ -127,6 +127,14 @@ def test_verify_argument_errors(sv):
     a = _valid_verify_args(sv)
     a.t_req_stride = a.d_req_stride = 0
     assert launch(a) == sv.SPEC_EWORKSPACE
+    # a batch whose grids exceed one dispatch (2^32 work-items): refused before anything is enqueued,
+    # with every other check passed (the workspace size included)
+    for B, K, V, dyn in [(1_000_000, 8, 151936, False), (9_000_000, 1, 8, False), (300_000, 8, 151936, True)]:
+        a = _valid_verify_args(sv, B=B, K=K, V=V)
+        a.workspace_bytes = sv.spec_verify_workspace_bytes(B, K, V)
+        a.phase_starts = sv.SPEC_PHASES_DYNAMIC if dyn else 0
+        assert a.workspace_bytes > 0
+        assert launch(a) == sv.SPEC_EINVAL, (B, K, V, dyn)
     # B = 0 is a no-op
     a = _valid_verify_args(sv)
     a.B = 0
@@ -165,6 +173,9 @@ def test_expand_argument_errors(sv):
     assert launch(a) == sv.SPEC_EINVAL
     a = args()
     a.B, a.N_in, a.K = 2, 2 ** 31 - 2, 3  # N_out overflows int32
+    assert launch(a) == sv.SPEC_EINVAL
+    a = args()
+    a.B, a.N_in, a.K = 20_000_000, 20_000_000, 1  # a workgroup per request: more work-items than one dispatch
     assert launch(a) == sv.SPEC_EINVAL
     a = args()
     a.B = 0
@@ -266,6 +277,11 @@ def test_draft_argument_errors(sv):
     a = args()
     a.B = 0
     assert launch(a) == sv.SPEC_OK
+    # more statistics work-items than one dispatch holds, every other check passed
+    a = args()
+    a.B, a.K, a.V, a.row_stride = 2_000_000, 8, 151936, 151936
+    a.workspace_bytes = sv.spec_draft_workspace_bytes(a.B, a.K, a.V)
+    assert launch(a) == sv.SPEC_EINVAL
     assert sv.lib.spec_draft_sample_launch(None, None) == sv.SPEC_EINVAL
     # workspace: one 16-byte statistic per (request, position, 4096-logit segment), 256-byte rounded
     assert sv.spec_draft_workspace_bytes(2, 3, 100) == 256
@@ -316,6 +332,12 @@ def test_shard_argument_errors(sv):
     a = args()
     a.draft_row_index, a.draft_rows = fake, -1
     assert sv.spec_shard_stats_launch(a, None) == sv.SPEC_EINVAL
+    # more statistics work-items than one dispatch holds, every other check passed
+    a = args()
+    a.B, a.K, a.t_req_stride, a.d_req_stride = 200_000, 63, 64 * 100, 64 * 100
+    a.workspace_bytes = sv.spec_shard_workspace_bytes(a.B, a.K, a.Vs)
+    for launch in (sv.spec_shard_stats_launch, sv.spec_shard_decide_launch, sv.spec_shard_draw_launch):
+        assert launch(a, None) == sv.SPEC_EINVAL
     # decision records, segment sums and the request state between phases
     assert sv.spec_shard_workspace_bytes(2, 3, 50) == 256 + 256 + 256
     assert sv.spec_shard_workspace_bytes(1, 1, sv.SPEC_MAX_V + 1) == 0
