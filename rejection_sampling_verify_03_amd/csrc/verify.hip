@@ -114,10 +114,14 @@ __device__ __forceinline__ void dstate_read(uint64_t w, uint64_t E, int K, int& 
   if (n > K || (f && n >= K)) n = f = 0;
 }
 
-// The 32-bit tag of launch E in a record word: odd, so that zeroed memory (a
-// fresh workspace at launch counter 0, or the no-alloc array at load) never
-// passes for a record of any launch; consecutive launches differ.
+// The 32-bit tags of launch E in the words of a record: words 0 and 1 carry
+// record_tag (odd, so that zeroed memory, such as a fresh workspace at launch
+// counter 0 or the no-alloc array at load, never passes for a record of any
+// launch), words 2 and 3 record_tag_hi, the counter's higher bits, so that
+// the four words together repeat only after 2^63 launches (the low tag alone
+// repeats every 2^31).
 __device__ __forceinline__ uint32_t record_tag(uint64_t E) { return (uint32_t)(2 * E + 1); }
+__device__ __forceinline__ uint32_t record_tag_hi(uint64_t E) { return (uint32_t)(E >> 31); }
 
 // Agent-scope accesses: coherent between workgroups of one launch, whatever
 // their XCD (no cache maintenance, no ordering between different words).
@@ -532,9 +536,9 @@ __device__ void dyn_decider(const VerifyParams& P, int J, int g, uint64_t E, Dyn
     const uint64_t* wp = P.trec[((int64_t)d * P.R + r) * C1 + c].w;
     const uint64_t w0 = load_coherent(wp), w1 = load_coherent(wp + 1), w2 = load_coherent(wp + 2),
                    w3 = load_coherent(wp + 3);
-    const uint32_t tag = record_tag(E);
-    ds.ok[t] = (uint32_t)(w0 >> 32) == tag && (uint32_t)(w1 >> 32) == tag && (uint32_t)(w2 >> 32) == tag &&
-               (uint32_t)(w3 >> 32) == tag;
+    const uint32_t tag = record_tag(E), tag_hi = record_tag_hi(E);
+    ds.ok[t] = (uint32_t)(w0 >> 32) == tag && (uint32_t)(w1 >> 32) == tag && (uint32_t)(w2 >> 32) == tag_hi &&
+               (uint32_t)(w3 >> 32) == tag_hi;
     ds.m[t] = __uint_as_float((uint32_t)w0);
     ds.idx[t] = (int32_t)(uint32_t)w1;
     ds.s[t] = __longlong_as_double((long long)((w3 << 32) | (w2 & 0xffffffffull)));
@@ -650,7 +654,8 @@ __device__ __forceinline__ void dyn_chunk(const VerifyParams& P, int b, int r, i
                          : threadIdx.x == 1 ? (uint32_t)part.idx
                          : threadIdx.x == 2 ? (uint32_t)sb
                                             : (uint32_t)(sb >> 32);
-    store_coherent(&P.trec[at].w[threadIdx.x], ((uint64_t)record_tag(E) << 32) | pay);
+    const uint32_t tag = threadIdx.x < 2 ? record_tag(E) : record_tag_hi(E);
+    store_coherent(&P.trec[at].w[threadIdx.x], ((uint64_t)tag << 32) | pay);
   }
 }
 

@@ -37,12 +37,14 @@ struct ReqDesc {  // decision of one request, read by the draw
 
 // A chunk's RowPartial as read by workgroups of the same row-pass launch
 // (dynamic early exit): four 64-bit words, each stored by one single-copy
-// atomic store and each carrying the launch's 32-bit tag in its high half
+// atomic store and each carrying a 32-bit tag of the launch in its high half
 // (payload in the low half: m's bits, idx, the low and the high half of s's
-// bits; the tag is odd, so zeroed memory never carries one).  A reader that
-// finds the tag in all four words has the whole record of this launch;
-// anything else (a record still being written, left by an earlier launch, or
-// memory never written) it treats as not yet there.
+// bits; words 0 and 1 carry an odd tag from the launch counter's low bits,
+// so zeroed memory never carries one, words 2 and 3 the counter's higher
+// bits).  A reader that finds the launch's tags in all four words has the
+// whole record of this launch; anything else (a record still being written,
+// left by an earlier launch, or memory never written) it treats as not yet
+// there.
 struct TaggedPartial {
   uint64_t w[4];
 };

@@ -344,3 +344,33 @@ def test_dynamic_exit_first_launch_on_zeroed_workspace(sv):
         assert (a2 >= 0).all(), (trial, int((a2 < 0).sum()))
         assert torch.equal(a1, a2) and torch.equal(t1, t2), trial
     say("  3 fresh zeroed workspaces: equal to one pass")
+
+
+def test_dynamic_exit_records_from_2_31_launches_ago_do_not_pass(sv):
+    """Records left in the workspace by a launch 2^31 launches back (the low
+    32 bits of their tag then read the same) must not pass for this launch's:
+    a dynamic launch at counter 5 leaves records of other inputs, the counter
+    is moved to 5 + 2^31, and the next dynamic launch on new inputs equals one
+    pass."""
+    say("case: dynamic exit, records of a launch 2^31 back")
+    dev = torch.device("cuda")
+    B, K, V = 192, 8, 151936
+    old = workloads.mixture_inputs("dyn stale", B, K, V, torch.bfloat16, 78, dev, temps=(0.6, 1.0),
+                                   lam_lo=0.05, lam_hi=0.5)
+    new = workloads.mixture_inputs("dyn fresh", B, K, V, torch.bfloat16, 79, dev, temps=(0.6, 1.0),
+                                   lam_lo=0.05, lam_hi=0.5)
+    a1, t1, _ = sv.verify(new.target, new.draft, new.draft_tokens, new.temperature, seed=4, step=9)
+    for trial in range(3):
+        ws = torch.zeros(sv.spec_verify_workspace_bytes(B, K, V), dtype=torch.uint8, device=dev)
+        counter = ws[8:16].view(torch.int64)
+        counter.fill_(5)
+        sv.verify(old.target, old.draft, old.draft_tokens, old.temperature, seed=1, step=3, workspace=ws,
+                  phase_starts=DYN)
+        torch.cuda.synchronize()
+        counter.fill_(5 + 2 ** 31)
+        a2, t2, _ = sv.verify(new.target, new.draft, new.draft_tokens, new.temperature, seed=4, step=9,
+                              workspace=ws, phase_starts=DYN)
+        torch.cuda.synchronize()
+        assert (a2 >= 0).all(), (trial, int((a2 < 0).sum()))
+        assert torch.equal(a1, a2) and torch.equal(t1, t2), trial
+    say("  3 workspaces with records of a launch 2^31 back: equal to one pass")
