@@ -107,13 +107,18 @@ __global__ __launch_bounds__(kWG) void shard_stats_kernel(ShardParams P) {
     rec.m = v.v;
     rec.idx = v.i + P.v0;
   } else {
+    // the logit at the position's draft token, when the slice holds it: loaded
+    // before the stream (clamped into the slice) so that nothing waits for it
+    // after
+    const bool has_x = x >= P.v0 && x - P.v0 < P.Vs;
+    const float zx = load_one<ES>(row, min(max(x - P.v0, 0), P.Vs - 1));
     float s_hi, s_lo;
     temperature_scale(T, s_hi, s_lo);
     const MS v = block_merge_ms(chunk_stats<ES, VEC>(row, 0, P.Vs, s_hi, s_lo));
     rec.m = v.m;
     rec.s = v.s;
-    if (x >= P.v0 && x - P.v0 < P.Vs) {
-      rec.z = load_one<ES>(row, x - P.v0);
+    if (has_x) {
+      rec.z = zx;
       rec.has_z = 1;
     }
   }
@@ -308,7 +313,35 @@ __global__ __launch_bounds__(kDecideWG) void shard_decide_kernel(ShardParams P) 
   w.c_hi = (float)c;
   w.c_lo = (float)(c - (double)w.c_hi);
   double* seg = P.seg + (int64_t)b * P.nseg * 2;
+  // each wave's running masses in segment order, kept in LDS for the total
+  __shared__ double wr[kDecideWaves], wp[kDecideWaves];
   const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // scalar segment bounds
+  if (P.nseg <= kDecideWaves) {
+    // one segment per wave (every slice up to 16 segments): its sums go to
+    // LDS as well, and thread 0 totals them in segment order from there
+    if (wave < P.nseg) {
+      double rs, ps;
+      if (res) segment_sums<ES, VEC, true>(prow, qrow, w, wave * kSeg, P.Vs, rs, ps);
+      else segment_sums<ES, VEC, false>(prow, qrow, w, wave * kSeg, P.Vs, rs, ps);
+      if (lane == 0) {
+        seg[2 * wave] = rs;
+        seg[2 * wave + 1] = ps;
+        wr[wave] = rs;
+        wp[wave] = ps;
+      }
+    }
+    __syncthreads();
+    if (tid == 0) {  // the slice's masses, summed in segment order
+      double R = 0.0, Pm = 0.0;
+      for (int j = 0; j < P.nseg; ++j) {
+        R += wr[j];
+        Pm += wp[j];
+      }
+      mass[0] = R;
+      mass[1] = Pm;
+    }
+    return;
+  }
   for (int j = wave; j < P.nseg; j += kDecideWaves) {
     double rs, ps;
     if (res) segment_sums<ES, VEC, true>(prow, qrow, w, j * kSeg, P.Vs, rs, ps);
