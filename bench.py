@@ -112,8 +112,10 @@ class TimingEvent:
         return ms.value
 
     def __del__(self):
-        if getattr(self, "h", None) and self.h.value:
-            self._hip.hipEventDestroy(self.h)
+        # at interpreter exit the runtime may already be gone: leave the event to it
+        if sys.is_finalizing() or not getattr(self, "h", None) or not self.h.value:
+            return
+        self._hip.hipEventDestroy(self.h)
 
 
 def parse():
