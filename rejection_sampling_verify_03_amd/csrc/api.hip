@@ -383,6 +383,9 @@ static VerifyParams verify_params(const spec_verify_args* a, bool& vec) {
   P.err = reinterpret_cast<int32_t*>(ws + L.off_err);
   P.state = reinterpret_cast<int32_t*>(ws + L.off_state);
   P.epoch = reinterpret_cast<uint64_t*>(ws + L.off_epoch);
+  // a workspace's launches are tagged by its counter plus this salt (an odd
+  // multiple of the address: different workspaces, different salts)
+  P.salt = (uint64_t)(uintptr_t)a->workspace * 0x9E3779B97F4A7C15ull;
   P.dstate = reinterpret_cast<uint64_t*>(ws + L.off_dstate);
   P.trec = reinterpret_cast<TaggedPartial*>(ws + L.off_trec);
   P.dyn = a->phase_starts == SPEC_PHASES_DYNAMIC;

@@ -114,14 +114,28 @@ __device__ __forceinline__ void dstate_read(uint64_t w, uint64_t E, int K, int& 
   if (n > K || (f && n >= K)) n = f = 0;
 }
 
-// The 32-bit tags of launch E in the words of a record: words 0 and 1 carry
-// record_tag (odd, so that zeroed memory, such as a fresh workspace at launch
-// counter 0 or the no-alloc array at load, never passes for a record of any
-// launch), words 2 and 3 record_tag_hi, the counter's higher bits, so that
-// the four words together repeat only after 2^63 launches (the low tag alone
-// repeats every 2^31).
+// The tag E of a launch: the workspace's launch counter (byte 8, advanced by
+// the last kernel of every launch) plus a salt taken from the workspace's
+// address.  The counter of a workspace that was never used holds whatever
+// the memory held, and two such workspaces -- say two allocations of one
+// allocator, each carved from memory a third one used before -- can hold the
+// same value while one's record area holds the other's records; the salt
+// keeps their launches apart.
+__device__ __forceinline__ uint64_t launch_tag(const VerifyParams& P) { return *P.epoch + P.salt; }
+
+// The 32-bit tags of launch E in the words of a record, each odd (so that
+// zeroed memory, such as a fresh workspace or the no-alloc array at load,
+// never passes for a record of any launch) and each different for any two
+// launches less than 2^31 apart, so that a decider that catches a record
+// half-written, its other words still from an earlier launch, sees the
+// difference in every word: words 0 and 1 carry record_tag (the low bits of
+// E), words 2 and 3 record_tag_b (the same with the higher bits E >> 31
+// folded in), so that the four words together repeat only after 2^63
+// launches.
 __device__ __forceinline__ uint32_t record_tag(uint64_t E) { return (uint32_t)(2 * E + 1); }
-__device__ __forceinline__ uint32_t record_tag_hi(uint64_t E) { return (uint32_t)(E >> 31); }
+__device__ __forceinline__ uint32_t record_tag_b(uint64_t E) {
+  return (uint32_t)(2 * E + 1) ^ ((uint32_t)(E >> 31) << 1);
+}
 
 // Agent-scope accesses: coherent between workgroups of one launch, whatever
 // their XCD (no cache maintenance, no ordering between different words).
@@ -365,7 +379,7 @@ __device__ void decide(const VerifyParams& P, int b, bool write, ReqDesc& D) {
   int lo = 0, known = -1;
   bool invalid = false;
   if (P.dyn) {  // decisions inside the row pass: every test again, from the partials
-    const uint64_t E = *P.epoch;
+    const uint64_t E = launch_tag(P);
     int n, f;
     dstate_read(P.dstate[b], E, K, n, f);
     // with f the rows past n may not have been read: test [0, n] only
@@ -536,9 +550,9 @@ __device__ void dyn_decider(const VerifyParams& P, int J, int g, uint64_t E, Dyn
     const uint64_t* wp = P.trec[((int64_t)d * P.R + r) * C1 + c].w;
     const uint64_t w0 = load_coherent(wp), w1 = load_coherent(wp + 1), w2 = load_coherent(wp + 2),
                    w3 = load_coherent(wp + 3);
-    const uint32_t tag = record_tag(E), tag_hi = record_tag_hi(E);
-    ds.ok[t] = (uint32_t)(w0 >> 32) == tag && (uint32_t)(w1 >> 32) == tag && (uint32_t)(w2 >> 32) == tag_hi &&
-               (uint32_t)(w3 >> 32) == tag_hi;
+    const uint32_t tag = record_tag(E), tag_b = record_tag_b(E);
+    ds.ok[t] = (uint32_t)(w0 >> 32) == tag && (uint32_t)(w1 >> 32) == tag && (uint32_t)(w2 >> 32) == tag_b &&
+               (uint32_t)(w3 >> 32) == tag_b;
     ds.m[t] = __uint_as_float((uint32_t)w0);
     ds.idx[t] = (int32_t)(uint32_t)w1;
     ds.s[t] = __longlong_as_double((long long)((w3 << 32) | (w2 & 0xffffffffull)));
@@ -654,7 +668,7 @@ __device__ __forceinline__ void dyn_chunk(const VerifyParams& P, int b, int r, i
                          : threadIdx.x == 1 ? (uint32_t)part.idx
                          : threadIdx.x == 2 ? (uint32_t)sb
                                             : (uint32_t)(sb >> 32);
-    const uint32_t tag = threadIdx.x < 2 ? record_tag(E) : record_tag_hi(E);
+    const uint32_t tag = threadIdx.x < 2 ? record_tag(E) : record_tag_b(E);
     store_coherent(&P.trec[at].w[threadIdx.x], ((uint64_t)tag << 32) | pay);
   }
 }
@@ -677,7 +691,7 @@ __global__ __launch_bounds__(kWG) void verify_rowstats_dyn_kernel(VerifyParams P
   // the roles inside a group rotate with the group, so that no role keeps to
   // one XCD when W is a multiple of the 8 the hardware deals workgroups to
   const int g = rem / W, sl = (rem - g * W + g) % W;
-  const uint64_t E = *P.epoch;
+  const uint64_t E = launch_tag(P);
   if (sl == W - 1) {
     dyn_decider<ES>(P, J, g, E, ds);
     return;

@@ -65,12 +65,14 @@ struct VerifyParams {
   // start of the last phase when the rows were read in several phases, else 0
   int32_t last_lo, phased;
   // dynamic early exit (dyn): decisions taken inside the row pass as its
-  // chunks finish.  epoch: the launch counter (its low 32 bits tag the
-  // records of this launch); dstate [B]: per request (tag << 8) | (2 n + f),
+  // chunks finish.  epoch: the launch counter, which with salt (from the
+  // workspace's address) gives the launch's tag E that its tagged records and
+  // state words carry; dstate [B]: per request (E << 8) | (2 n + f),
   // positions before n known accepted and, with f, position n stops the
   // request; trec: tagged copies of rowp; dyn_shift: request groups between a
   // request's chunks of a position and its decider slot
   uint64_t* epoch;
+  uint64_t salt;
   uint64_t* dstate;
   TaggedPartial* trec;
   int32_t dyn, dyn_shift;

@@ -39,12 +39,11 @@ struct ReqDesc {  // decision of one request, read by the draw
 // (dynamic early exit): four 64-bit words, each stored by one single-copy
 // atomic store and each carrying a 32-bit tag of the launch in its high half
 // (payload in the low half: m's bits, idx, the low and the high half of s's
-// bits; words 0 and 1 carry an odd tag from the launch counter's low bits,
-// so zeroed memory never carries one, words 2 and 3 the counter's higher
-// bits).  A reader that finds the launch's tags in all four words has the
-// whole record of this launch; anything else (a record still being written,
-// left by an earlier launch, or memory never written) it treats as not yet
-// there.
+// bits; every tag odd, so that zeroed memory never carries one, and each
+// word's different for any two launches less than 2^31 apart).  A reader
+// that finds the launch's tags in all four words has the whole record of
+// this launch; anything else (a record still being written, left by an
+// earlier launch, or memory never written) it treats as not yet there.
 struct TaggedPartial {
   uint64_t w[4];
 };

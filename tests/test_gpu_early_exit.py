@@ -374,3 +374,37 @@ def test_dynamic_exit_records_from_2_31_launches_ago_do_not_pass(sv):
         assert (a2 >= 0).all(), (trial, int((a2 < 0).sum()))
         assert torch.equal(a1, a2) and torch.equal(t1, t2), trial
     say("  3 workspaces with records of a launch 2^31 back: equal to one pass")
+
+
+def test_dynamic_exit_on_a_workspace_cut_from_another(sv):
+    """Two workspaces cut from one allocation 1536 bytes apart (as an
+    allocator hands out a freed block again after small output tensors took
+    its start), their launch counters holding the same leftover value: the
+    tagged records a dynamic exit on other inputs leaves in the first lie in
+    the second's record area, 48 records off, carrying the tag the second's
+    launch would expect if the tag were the counter alone.  The dynamic exit
+    on the second must equal one pass (the tag also depends on the
+    workspace's address)."""
+    say("case: dynamic exit on a workspace cut from another one's memory")
+    dev = torch.device("cuda")
+    B, K, V = 24, 6, 50000
+    inp = workloads.mixture_inputs("dyn carved ws", B, K, V, torch.bfloat16, 81, dev, temps=(0.0, 0.6, 1.0),
+                                   lam_lo=0.05, lam_hi=0.6)
+    old = workloads.mixture_inputs("dyn carved ws, other", B, K, V, torch.bfloat16, 82, dev,
+                                   temps=(0.0, 0.6, 1.0), lam_lo=0.05, lam_hi=0.6)
+    a1, t1, _ = sv.verify(inp.target, inp.draft, inp.draft_tokens, inp.temperature, seed=5, step=0)
+    n = sv.spec_verify_workspace_bytes(B, K, V)
+    for trial, counter0 in enumerate((7, 0x40297C9488840000, 2 ** 31 - 1)):
+        big = torch.zeros(n + 2 * 1536, dtype=torch.uint8, device=dev)
+        ws_a, ws_b = big[1536:1536 + n], big[3072:3072 + n]
+        ws_a[8:16].view(torch.int64).fill_(counter0)
+        sv.verify(old.target, old.draft, old.draft_tokens, old.temperature, seed=2, step=1, workspace=ws_a,
+                  phase_starts=DYN)
+        torch.cuda.synchronize()
+        ws_b[8:16].view(torch.int64).fill_(counter0)  # the same counter as the first launch ran at
+        a2, t2, _ = sv.verify(inp.target, inp.draft, inp.draft_tokens, inp.temperature, seed=5, step=0,
+                              workspace=ws_b, phase_starts=DYN)
+        torch.cuda.synchronize()
+        assert (a2 >= 0).all(), (trial, int((a2 < 0).sum()))
+        assert torch.equal(a1, a2) and torch.equal(t1, t2), trial
+    say("  3 counters: equal to one pass")
