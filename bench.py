@@ -612,6 +612,22 @@ def side_configs(sv, torch, np, only, seed):
     return out
 
 
+def host_cpu():
+    """The host's CPU model and core counts (logical cores, and those this
+    process may run on)."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    usable = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else None
+    return {"cpu_model": model, "logical_cores": os.cpu_count(), "usable_cores": usable}
+
+
 def cpu_baseline(inp, seed, cpu_seconds):
     """The oracle, as it stands, over whole steps of the headline batch on all
     host threads it is given (OMP_NUM_THREADS, else every core)."""
@@ -648,6 +664,7 @@ def cpu_baseline(inp, seed, cpu_seconds):
         one_wall += time.perf_counter() - t0
         one_req = r1
     return {"value": steps * B * K / wall, "unit": "positions/s", "cores": threads, "kind": "oracle",
+            "host": host_cpu(),
             "sample": "%d whole step(s) of the headline batch (B=%d, K=%d, V=%d), %.1f CPU-s"
                       % (steps, B, K, tl.shape[-1], used),
             "single_core": {"value": one_req * K / one_wall, "unit": "positions/s", "cores": 1,
