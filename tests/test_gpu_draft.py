@@ -81,11 +81,12 @@ def test_parity_mixed_temperatures(sv, dtype, V):
 
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
 @pytest.mark.parametrize("offset", [0.0, 40.0])
-def test_large_logits_low_temperature(sv, dtype, offset):
-    """Drafter rows shifted by +40 at temperatures 0.1 and 0.3: the sampled
+@pytest.mark.parametrize("temps", [(0.1, 0.3), (0.01, 0.03), (5.0, 20.0, 100.0)])
+def test_large_logits_low_temperature(sv, dtype, offset, temps):
+    """Drafter rows shifted by +40 at low and high temperatures: the sampled
     law does not change under a shift, and neither may the tokens."""
-    say("case: draft sampling, logits + %g, T in {0.1, 0.3}, %s" % (offset, dtype))
-    inp = workloads.drafter_inputs(12, 5, 30, 40000, dtype, seed=13, device="cuda", temps=(0.1, 0.3),
+    say("case: draft sampling, logits + %g, T in %s, %s" % (offset, temps, dtype))
+    inp = workloads.drafter_inputs(12, 5, 30, 40000, dtype, seed=13, device="cuda", temps=temps,
                                    offset=offset)
     for step in range(2):
         run_case(sv, inp, seed=7, step=step)

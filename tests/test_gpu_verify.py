@@ -201,20 +201,22 @@ def test_special_cases(sv):
 
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
 @pytest.mark.parametrize("offset", [0.0, 40.0])
-def test_large_logits_low_temperature(sv, dtype, offset):
-    """Logits shifted by +40 at temperatures 0.1 and 0.3 (|logit| / T up to
-    ~500): a shift leaves p and q unchanged, so the exponent arithmetic must
-    keep its accuracy whatever the logits' magnitude.  Every request against
-    the oracle, debug probabilities within the 1e-6 bar, over two chunks and
-    a ragged tail per row."""
-    say("case: logits + %g, T in {0.1, 0.3}, %s" % (offset, dtype))
+@pytest.mark.parametrize("temps", [(0.1, 0.3), (0.01, 0.03), (5.0, 20.0, 100.0)])
+def test_large_logits_low_temperature(sv, dtype, offset, temps):
+    """Logits shifted by +40 at low temperatures (|logit| / T up to ~5000 at
+    T = 0.01) and at high ones (nearly flat rows): a shift leaves p and q
+    unchanged, so the exponent arithmetic must keep its accuracy whatever the
+    logits' magnitude and the temperature.  Every request against the
+    oracle, debug probabilities within the 1e-6 bar, over two chunks and a
+    ragged tail per row."""
+    say("case: logits + %g, T in %s, %s" % (offset, temps, dtype))
     inp = workloads.noisy_draft_inputs("shift %g %s" % (offset, dtype), 16, 5, 40000, dtype, 21, "cuda",
-                                       "gauss", target_std=2.0, draft_noise=0.5, temps=(0.1, 0.3),
+                                       "gauss", target_std=2.0, draft_noise=0.5, temps=temps,
                                        offset=offset)
     check(sv, inp, seeds=(0, 3), steps=(0, 1))
     # Zipf rows (a long tail far below the maximum) at the same temperatures
     inp = workloads.noisy_draft_inputs("zipf shift %g %s" % (offset, dtype), 8, 4, 70001, dtype, 22, "cuda",
-                                       "zipf", draft_noise=0.7, temps=(0.1, 0.3), offset=offset)
+                                       "zipf", draft_noise=0.7, temps=temps, offset=offset)
     check(sv, inp, seeds=(1,), steps=(0, 1))
 
 
