@@ -92,6 +92,25 @@ def test_large_logits_low_temperature(sv, dtype, offset, temps):
         run_case(sv, inp, seed=7, step=step)
 
 
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("kind", ["random30", "block", "low_block"])
+def test_masked_drafter_rows(sv, kind, dtype):
+    """Drafter rows with a part of the vocabulary at -inf (V = 151936):
+    random30, the same random 30 % of every row; block, tokens
+    40000..109999 (whole segments and statistics chunks); low_block, tokens
+    0..59999.  Every position against the oracle."""
+    say("case: draft sampling, masked drafter rows %s %s" % (kind, dtype))
+    inp = workloads.drafter_inputs(12, 4, 30, 151936, dtype, seed=41, device="cuda", temps=(0.0, 0.6, 1.0))
+    g = torch.Generator(device="cuda").manual_seed(42)
+    if kind == "random30":
+        inp.logits[torch.rand(inp.logits.shape, generator=g, device="cuda") < 0.3] = float("-inf")
+    elif kind == "block":
+        inp.logits[:, 40000:110000] = float("-inf")
+    else:
+        inp.logits[:, 0:60000] = float("-inf")
+    run_case(sv, inp, seed=3, step=0)
+
+
 @pytest.mark.parametrize("dtype,V", [(torch.bfloat16, 20003), (torch.float32, 1023), (torch.bfloat16, 9),
                                      (torch.float32, 1)])
 def test_scalar_path_and_tiny_rows(sv, dtype, V):

@@ -366,3 +366,46 @@ def test_headline_full_size_sampled(sv):
     T = inp.temperature.cpu().numpy()
     say("accepted mean by T:", {float(t): float(acc[T == t].mean()) for t in np.unique(T)})
     assert (acc >= 0).all() and (acc <= 8).all()
+
+
+def masked_vocabulary(inp, kind, seed):
+    """Vocabulary masks as a serving stack applies them (banned tokens,
+    constrained decoding): logits set to -inf in place, then the draft tokens
+    drawn again from the masked draft rows.  random30: the same random 30 %
+    of each target and draft row; block: tokens 40000..109999 of every row,
+    which covers whole 32K row-pass chunks and whole 4096-logit segments;
+    disjoint_blocks: tokens 0..59999 of the target rows and 90000.. of the
+    draft rows, so that many drafted tokens have p(x) = 0."""
+    g = torch.Generator(device="cuda").manual_seed(seed)
+    ninf = float("-inf")
+    if kind == "random30":
+        m = torch.rand(inp.target.shape, generator=g, device="cuda") < 0.3
+        inp.target[m] = ninf
+        inp.draft[m] = ninf
+    elif kind == "block":
+        inp.target[:, :, 40000:110000] = ninf
+        inp.draft[:, :, 40000:110000] = ninf
+    else:
+        inp.target[:, :, 0:60000] = ninf
+        inp.draft[:, :, 90000:] = ninf
+    inp.draft_tokens = workloads.redraw_tokens(inp, seed + 1)
+    return inp
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("kind", ["random30", "block", "disjoint_blocks"])
+def test_masked_vocabulary(sv, kind, dtype):
+    """Rows with a part of the vocabulary at -inf at the headline vocabulary
+    (V = 151936; mixed temperatures 0, 0.6, 1): every request against the
+    oracle, and a planned cut and the dynamic exit equal to one pass."""
+    say("case: masked vocabulary %s %s" % (kind, dtype))
+    inp = workloads.noisy_draft_inputs("masked %s %s" % (kind, dtype), 24, 4, 151936, dtype, 31, "cuda", "zipf",
+                                       draft_noise=0.7, temps=(0.0, 0.6, 1.0))
+    inp = masked_vocabulary(inp, kind, 32)
+    check(sv, inp, seeds=(0, 1), steps=(0, 1))
+    a1, t1, _ = sv.verify(inp.target, inp.draft, inp.draft_tokens, inp.temperature, seed=0, step=0)
+    for ps in (0b100, sv.SPEC_PHASES_DYNAMIC):
+        a2, t2, _ = sv.verify(inp.target, inp.draft, inp.draft_tokens, inp.temperature, seed=0, step=0,
+                              phase_starts=ps)
+        torch.cuda.synchronize()
+        assert torch.equal(a1, a2) and torch.equal(t1, t2), ps
