@@ -196,6 +196,13 @@ __global__ __launch_bounds__(64) void draft_draw_kernel(DraftParams P) {
     const int j = j0 + lane;
     W += lane_d(wave_scan_d(j < nseg ? scaled_seg(sp[j], Mstar) : 0.0), 63);
   }
+  if (!(W > 0.0 && W <= DBL_MAX)) {  // a row without a finite normaliser (a NaN logit): as a bad row
+    if (lane == 0) {
+      P.tokens[i] = -1;
+      if (P.stats) P.stats[i] = none;
+    }
+    return;
+  }
   const double target = u * W;
   int found = -1, lastseg = -1;
   double base = 0.0, carry = 0.0;

@@ -137,11 +137,20 @@ def test_invalid_inputs(sv):
     T[2] = -1.0
     lg[5] = -float("inf")
     ri[3, :] = 5
-    tok = sv.draft_sample(lg, ri, T, seed=3).cpu().numpy()
+    # rows without a finite normaliser although their maximum is finite (a
+    # NaN logit) or with a +inf logit are bad rows too
+    lg[4, 17] = float("nan")
+    lg[3, 11] = float("inf")
+    ri[4, 0], ri[4, 1], ri[4, 2] = 4, 3, 0
+    stats = sv.draft_stats_buffer(5, 3)
+    tok = sv.draft_sample(lg, ri, T, seed=3, stats_out=stats).cpu().numpy()
     ref = oracle.draft_sample(lg.cpu().numpy(), ri.cpu().numpy(), T.cpu().numpy(), seed=3)
     assert tok[0, 1] == -1 and tok[0, 2] == -1 and tok[0, 0] >= 0
     assert (tok[1] == -1).all() and (tok[2] == -1).all() and (tok[3] == -1).all()
+    assert tok[4, 0] == -1 and tok[4, 1] == -1 and tok[4, 2] >= 0
     np.testing.assert_array_equal(tok, ref.tokens)
+    raw = stats.cpu().numpy().reshape(5, 3, 16)
+    assert (raw[4, 0] == 0).all() and (raw[4, 1] == 0).all()  # the records of bad rows are zero
     # no rows at all
     empty = torch.empty(0, 300, dtype=torch.float32, device="cuda")
     tok = sv.draft_sample(empty, ri, inp.temperature).cpu().numpy()
