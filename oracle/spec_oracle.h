@@ -65,7 +65,8 @@ int oracle_residual(const double* p, const double* q, int V, double* w, double* 
 /* softmax(logits / T) in double, max-subtracted; dtype 0 = fp32, 1 = bf16 bits.
  * Returns 0, or -1 if the row has no finite maximum or T is not > 0. */
 int oracle_softmax(const void* row, int dtype, int V, double T, double* out);
-/* Lowest index of the maximum logit (exact float compare). */
+/* Lowest index of the maximum logit (exact float compare), a NaN logit
+ * counting as -inf: a row with nothing above -inf gives 0. */
 int oracle_argmax(const void* row, int dtype, int V);
 
 /* Vectorised forms of the primitives for exhaustive enumeration tests:

@@ -21,12 +21,12 @@
  * step); word 0 of row k drives the accept test at k and word 1 the sampling
  * draw at k; the accept comparison is strict "<" as printed; q(x) = 0 accepts
  * iff p(x) > 0; the same temperature divides both logits; argmax ties go to
- * the lowest index; a residual that sums to exactly zero falls back to p; the
- * inverse CDF runs in ascending vocabulary order over the weights with their
- * own sum as normaliser; a sampled request whose rows at a position it
- * reaches (target and draft row of a tested position, the target row of the
- * bonus) lack a finite maximum is invalid, and rows after its stop are never
- * looked at.
+ * the lowest index and a NaN logit counts as -inf there; a residual that
+ * sums to exactly zero falls back to p; the inverse CDF runs in ascending
+ * vocabulary order over the weights with their own sum as normaliser; a
+ * sampled request whose rows at a position it reaches (target and draft row
+ * of a tested position, the target row of the bonus) lack a finite maximum
+ * is invalid, and rows after its stop are never looked at.
  *
  * Everything is computed in double, sequentially, with no blocking or
  * reordering beyond the definitions above.
@@ -67,11 +67,15 @@ int oracle_softmax(const void* row, int dtype, int V, double T, double* out) {
   return 0;
 }
 
+/* Lowest index of the largest logit, a NaN logit counting as -inf (the
+ * pages define the greedy token for numbers only; a NaN carries no
+ * preference), so a row with nothing above -inf gives index 0. */
 int oracle_argmax(const void* row, int dtype, int V) {
   int best = 0;
-  double bv = load_logit(row, dtype, 0);
-  for (int v = 1; v < V; ++v) {
+  double bv = -INFINITY;
+  for (int v = 0; v < V; ++v) {
     double x = load_logit(row, dtype, v);
+    if (isnan(x)) x = -INFINITY;
     if (x > bv) {
       bv = x;
       best = v;

@@ -340,6 +340,14 @@ __device__ __forceinline__ VI vi_pick(VI a, VI b) {
   return take_b ? b : a;
 }
 
+// The greedy argmax counts a NaN logit as -inf.  vi_pick never takes a NaN,
+// so a lane's scan over elements e0, e0 + 1, ... ends above -inf exactly when
+// the NaN-as--inf maximum is above -inf, and it then holds the right element;
+// otherwise every element it saw ties at -inf and the lowest, e0, wins.
+// Applied once per lane after its scan, so padding lanes and indices past
+// the row never come out of a merge.
+__device__ __forceinline__ VI vi_floor(VI v, int e0) { return v.v > -INFINITY ? v : VI{-INFINITY, e0}; }
+
 // The lowest-index argmax of the 64 lanes through DPP: prefix picks across the
 // rows, lane 63's read out; every lane ends with the same value.
 template <int CTRL, int ROW_MASK>

@@ -81,7 +81,7 @@ __device__ __forceinline__ void segment_records(const DraftParams& P, const char
         for (int q = 0; q < 8; ++q)
           if (e + q < P.V) best = vi_pick(best, VI{x[q], e + q});
       }
-      best = wave_argmax(best);
+      best = wave_argmax(vi_floor(best, s0));
       part.m = best.v;
       part.idx = best.i;
       part.s = 0.0;

@@ -121,7 +121,7 @@ __device__ __forceinline__ VI chunk_argmax(const char* __restrict__ row, int e0,
   const int t0 = e0 + 8 * nfull;
   if (t0 < e1 && threadIdx.x == 0)
     for (int e = t0; e < e1; ++e) best = vi_pick(best, VI{load_one<ES>(row, e), e});
-  return best;
+  return vi_floor(best, e0);
 }
 
 __device__ __forceinline__ MS block_merge_ms(MS v) {

@@ -111,6 +111,37 @@ def test_masked_drafter_rows(sv, kind, dtype):
     run_case(sv, inp, seed=3, step=0)
 
 
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_greedy_drafter_rows_with_nan(sv, dtype):
+    """Greedy draws (T = 0) from drafter rows holding NaN logits (V = 151936):
+    a NaN counts as -inf in the argmax, so an all-NaN row or a row with
+    nothing above -inf gives token 0 and a NaN ahead of the maximum does not
+    hide it.  Every position against the oracle."""
+    say("case: draft sampling, greedy drafter rows with NaN %s" % dtype)
+    N, V = 8, 151936
+    g = torch.Generator().manual_seed(43)
+    lg = torch.randn(N, V, generator=g)
+    nan, inf = float("nan"), float("inf")
+    lg[0] = nan                          # every logit NaN
+    lg[1, 0] = nan                       # NaN at index 0 ahead of the maximum
+    lg[2] = -inf
+    lg[2, 100000:] = nan                 # -inf, then NaN over whole segments
+    lg[3, :90000] = nan
+    lg[3, 90000:] = -inf
+    lg[3, 120001] = -7.0                 # the only number, behind NaN segments
+    lg[4, ::3] = nan                     # every third logit NaN
+    lg[5, 5] = nan
+    lg[5, 151935] = inf                  # +inf at the last index behind a NaN
+    lg = lg.to(dtype)
+    ri = torch.arange(N, dtype=torch.int32).reshape(4, 2)
+    T = torch.zeros(4)
+    tok = sv.draft_sample(lg.cuda(), ri.cuda(), T.cuda(), seed=1).cpu().numpy()
+    ref = oracle.draft_sample(workloads.logits_numpy(lg), ri.numpy(), T.numpy(), seed=1)
+    np.testing.assert_array_equal(tok, ref.tokens)
+    assert tok[0, 0] == 0 and tok[1, 0] == 0 and tok[1, 1] == 120001 and tok[2, 1] == V - 1
+    assert (tok >= 0).all() and (tok < V).all()
+
+
 @pytest.mark.parametrize("dtype,V", [(torch.bfloat16, 20003), (torch.float32, 1023), (torch.bfloat16, 9),
                                      (torch.float32, 1)])
 def test_scalar_path_and_tiny_rows(sv, dtype, V):

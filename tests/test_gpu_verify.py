@@ -409,3 +409,67 @@ def test_masked_vocabulary(sv, kind, dtype):
                               phase_starts=ps)
         torch.cuda.synchronize()
         assert torch.equal(a1, a2) and torch.equal(t1, t2), ps
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_greedy_rows_with_nan(sv, dtype):
+    """Greedy rows holding NaN logits (V = 70001, three statistics chunks):
+    a NaN counts as -inf in the argmax, so an all-NaN row or a row with
+    nothing above -inf gives token 0, and a NaN ahead of the maximum does not
+    hide it.  Every request against the oracle, one pass, the planned cut, the
+    dynamic exit and the vocabulary split over 2, 3 and 4 shards."""
+    import oracle
+    say("case: greedy rows with NaN %s" % dtype)
+    B, K, V = 12, 3, 70001
+    g = torch.Generator().manual_seed(21)
+    t = torch.randn(B, K + 1, V, generator=g)
+    d = t + 0.5 * torch.randn(B, K + 1, V, generator=g)
+    nan, inf = float("nan"), float("inf")
+    t[0, 0] = nan                                    # an all-NaN row, accepted (draft 0)
+    t[1, 1] = nan                                    # an all-NaN row, rejected: emits 0
+    t[2, 0, 0] = nan                                 # NaN at index 0 ahead of the maximum
+    t[3, K] = nan                                    # an all-NaN bonus row
+    t[4, 0] = -inf
+    t[4, 0, 40000:] = nan                            # -inf, then NaN over the last two chunks
+    t[5, 1, :40000] = nan
+    t[5, 1, 40000:] = -inf
+    t[5, 1, 50000] = -3.0                            # the only number, behind a NaN chunk
+    t[6, 2, :32768] = nan                            # a whole NaN chunk ahead of the maximum
+    t[7, 0, 10] = nan
+    t[7, 0, 65000] = inf                             # +inf behind a NaN
+    t[8, 1, ::2] = nan                               # every other logit NaN
+    T = torch.tensor([0.0] * 9 + [0.6, 1.0, 0.8])
+    tt, dd = t.to(dtype), d.to(dtype)
+    tl, dl = workloads.logits_numpy(tt), workloads.logits_numpy(dd)
+    x = np.array([[oracle.argmax(tl[b, k]) for k in range(K)] for b in range(B)], np.int32)
+    assert x[0, 0] == 0 and x[4, 0] == 0 and x[5, 1] == 50000 and x[7, 0] == 65000
+    x[1, 1] = 5                                      # the all-NaN row's argmax is 0: rejected there
+    x[6, 2] = (x[6, 2] + 1) % V
+    x[9:] = np.random.default_rng(22).integers(0, V, (3, K)).astype(np.int32)
+    Td = T.cuda()
+    tg, dg, xg = tt.cuda(), dd.cuda(), torch.from_numpy(x).cuda()
+    rep = Report()
+    outs = []
+    for ps in (0, 0b100, sv.SPEC_PHASES_DYNAMIC):
+        a, tok, dbg = sv.verify(tg, dg, xg, Td, seed=4, step=0, debug=ps == 0, phase_starts=ps)
+        torch.cuda.synchronize()
+        a, tok = a.cpu().numpy(), tok.cpu().numpy()
+        compare(tl, dl, x, T.numpy(), a, tok, None if dbg is None else dbg.cpu().numpy(), seed=4, step=0,
+                report=rep)
+        outs.append((a, tok))
+    for G in (2, 3, 4):
+        for ps in (0, 0b100):
+            a, tok, _ = sv.verify_sharded(tg, dg, xg, Td, G, seed=4, step=0, phase_starts=ps)
+            torch.cuda.synchronize()
+            a, tok = a.cpu().numpy(), tok.cpu().numpy()
+            compare(tl, dl, x, T.numpy(), a, tok, None, seed=4, step=0, report=rep)
+            outs.append((a, tok))
+    say(rep.summary())
+    assert rep.ok(), rep.failures[:5]
+    a, tok = outs[0]
+    assert list(a[:9]) == [K, 1, K, K, K, K, 2, K, K]
+    assert tok[1, 1] == 0 and tok[3, K] == 0 and tok[0, 0] == 0 and tok[5, 1] == 50000 and tok[7, 0] == 65000
+    assert (tok < V).all()
+    for a2, t2 in outs[1:]:
+        np.testing.assert_array_equal(a2, a)
+        np.testing.assert_array_equal(t2, tok)

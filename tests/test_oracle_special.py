@@ -98,6 +98,41 @@ def test_greedy_matches_argmax_definition():
         assert r.tokens[b, a] == g[b, a]
 
 
+def test_greedy_argmax_counts_nan_as_minus_inf():
+    """The greedy token when a row holds NaN logits: numpy's first-occurrence
+    argmax of the row with every NaN replaced by -inf, both dtypes."""
+    nan, inf = np.nan, np.inf
+    rows = [
+        [nan, 1.0, 2.0, 2.0],     # NaN first: the finite maximum, its lowest index
+        [nan, nan, nan, nan],     # every entry NaN: index 0
+        [nan, -inf, nan, -inf],   # nothing above -inf: index 0
+        [-inf, nan, -inf, -inf],  # ditto with -inf first
+        [1.0, nan, 3.0, nan],     # NaN between finite values
+        [nan, inf, nan, inf],     # +inf wins, lowest index
+        [-5.0, nan, -5.0, nan],   # ties below NaNs
+    ]
+    t = np.array(rows, np.float32)
+    want = np.argmax(np.where(np.isnan(t), -inf, t), axis=1)
+    assert list(want) == [2, 0, 0, 0, 2, 1, 0]
+    for b, row in enumerate(t):
+        assert oracle.argmax(row) == want[b]
+    # through verify: one greedy request per row, K = 0 (the bonus row only)
+    # and K = 1 with a draft that differs from the argmax
+    B, V = len(rows), 4
+    tl = np.repeat(t[:, None, :], 2, axis=1)
+    x = ((want + 1) % V).astype(np.int32)[:, None]
+    for dt in ("f32", "bf16"):
+        tt = tl if dt == "f32" else workloads.bf16_bits(__import__("torch").tensor(tl).bfloat16())
+        r = oracle.verify(tt, tt, x, np.zeros(B, np.float32))
+        assert (r.accepted == 0).all()
+        np.testing.assert_array_equal(r.tokens[:, 0], want)
+        r0 = oracle.verify(tt, tt, x, np.zeros(B, np.float32), num_drafts=np.zeros(B, np.int32))
+        np.testing.assert_array_equal(r0.tokens[:, 0], want)
+        # the draft sampler's greedy draw takes the same argmax
+        rd = oracle.draft_sample(tt[:, 0], np.arange(B, dtype=np.int32)[:, None], np.zeros(B, np.float32))
+        np.testing.assert_array_equal(rd.tokens[:, 0], want)
+
+
 def test_single_token_vocabulary_and_single_draft():
     r = oracle.verify(np.zeros((3, 3, 1), np.float32), np.zeros((3, 3, 1), np.float32),
                       np.zeros((3, 2), np.int32), np.array([1.0, 0.0, 0.5], np.float32))
