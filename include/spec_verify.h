@@ -221,13 +221,13 @@ int spec_verify_launch(const spec_verify_args* args, hipStream_t stream);
  * call allocates nothing.  The stream must belong to the current device
  * (else SPEC_EINVAL).  A shape whose spec_verify_workspace_bytes exceeds
  * SPEC_NOALLOC_SCRATCH_BYTES returns SPEC_EWORKSPACE before anything is
- * enqueued (8 MiB holds B = 1024, K = 8, V = 201088: 6.4 MiB).
+ * enqueued (16 MiB holds B = 1024, K = 8, V = 201088: 10.2 MiB).
  * Every call on one GPU shares that GPU's array: calls that may overlap on
  * that GPU (other streams, or graphs replayed concurrently) race and must be
  * ordered by the caller.  Invalid requests are reported in the outputs
  * (accepted_counts = -1); their count is not readable through
  * spec_workspace_error. */
-#define SPEC_NOALLOC_SCRATCH_BYTES (8u << 20)
+#define SPEC_NOALLOC_SCRATCH_BYTES (16u << 20)
 int spec_verify_launch_noalloc(const spec_verify_args* args, hipStream_t stream);
 
 /* The data errors of the last verification enqueued on this workspace: waits

@@ -20,7 +20,7 @@ SPEC_OK, SPEC_EINVAL, SPEC_EDTYPE, SPEC_EALIGN, SPEC_EWORKSPACE, SPEC_ELAUNCH = 
 SPEC_F32, SPEC_BF16 = 0, 1
 SPEC_MAX_K = 63
 SPEC_MAX_V = 2147418112  # 2^31 - 2^16
-SPEC_NOALLOC_SCRATCH_BYTES = 8 << 20
+SPEC_NOALLOC_SCRATCH_BYTES = 16 << 20
 SPEC_PHASES_DYNAMIC = 1  # phase_starts value: decisions inside the row pass (dynamic early exit)
 
 EXPORTED = ("spec_verify_workspace_bytes", "spec_verify_plan_phases", "spec_verify_phase_cost",

@@ -123,18 +123,28 @@ __device__ __forceinline__ void dstate_read(uint64_t w, uint64_t E, int K, int& 
 // keeps their launches apart.
 __device__ __forceinline__ uint64_t launch_tag(const VerifyParams& P) { return *P.epoch + P.salt; }
 
-// The 32-bit tags of launch E in the words of a record, each odd (so that
+// The 48-bit tags of launch E in the words of a record, each odd (so that
 // zeroed memory, such as a fresh workspace or the no-alloc array at load,
 // never passes for a record of any launch) and each different for any two
-// launches less than 2^31 apart, so that a decider that catches a record
-// half-written, its other words still from an earlier launch, sees the
-// difference in every word: words 0 and 1 carry record_tag (the low bits of
-// E), words 2 and 3 record_tag_b (the same with the higher bits E >> 31
-// folded in), so that the four words together repeat only after 2^63
-// launches.
-__device__ __forceinline__ uint32_t record_tag(uint64_t E) { return (uint32_t)(2 * E + 1); }
-__device__ __forceinline__ uint32_t record_tag_b(uint64_t E) {
-  return (uint32_t)(2 * E + 1) ^ ((uint32_t)(E >> 31) << 1);
+// launches less than 2^47 apart, so that a decider that catches a record
+// half-written, some words still from an earlier launch, sees the difference
+// in every such word: words 0-3 carry record_tag (the low bits of 2E + 1),
+// words 4-7 record_tag_b (the same with the higher bits E >> 47 folded in),
+// so that a record left whole by an earlier launch repeats all eight tags
+// only after 2^94 launches.  With 32-bit tags a record caught half-written
+// could pass for one whose other words a launch exactly 2^31 back had left.
+constexpr uint64_t kRecTagMask = (1ull << 48) - 1;
+__device__ __forceinline__ uint64_t record_tag(uint64_t E) { return (2 * E + 1) & kRecTagMask; }
+__device__ __forceinline__ uint64_t record_tag_b(uint64_t E) {
+  return ((2 * E + 1) ^ ((E >> 47) << 1)) & kRecTagMask;
+}
+
+// Word i of the tagged record of `part` in launch E.
+__device__ __forceinline__ uint64_t record_word(const RowPartial& part, int i, uint64_t E) {
+  const uint64_t lo = ((uint64_t)(uint32_t)part.idx << 32) | __float_as_uint(part.m);
+  const uint64_t hi = (uint64_t)__double_as_longlong(part.s);
+  const uint64_t pay = ((i < 4 ? lo : hi) >> (16 * (i & 3))) & 0xffffu;
+  return ((i < 4 ? record_tag(E) : record_tag_b(E)) << 16) | pay;
 }
 
 // Agent-scope accesses: coherent between workgroups of one launch, whatever
@@ -548,14 +558,23 @@ __device__ void dyn_decider(const VerifyParams& P, int J, int g, uint64_t E, Dyn
     const int p = p0 + t / per, rr = (t / C1) % 2, c = t % C1;
     const int r = rr == 0 ? p : K + 1 + p;
     const uint64_t* wp = P.trec[((int64_t)d * P.R + r) * C1 + c].w;
-    const uint64_t w0 = load_coherent(wp), w1 = load_coherent(wp + 1), w2 = load_coherent(wp + 2),
-                   w3 = load_coherent(wp + 3);
-    const uint32_t tag = record_tag(E), tag_b = record_tag_b(E);
-    ds.ok[t] = (uint32_t)(w0 >> 32) == tag && (uint32_t)(w1 >> 32) == tag && (uint32_t)(w2 >> 32) == tag_b &&
-               (uint32_t)(w3 >> 32) == tag_b;
-    ds.m[t] = __uint_as_float((uint32_t)w0);
-    ds.idx[t] = (int32_t)(uint32_t)w1;
-    ds.s[t] = __longlong_as_double((long long)((w3 << 32) | (w2 & 0xffffffffull)));
+    uint64_t wv[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) wv[i] = load_coherent(wp + i);
+    const uint64_t tag = record_tag(E), tag_b = record_tag_b(E);
+    bool ok = true;
+    uint64_t lo = 0, hi = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      ok = ok && (wv[i] >> 16) == (i < 4 ? tag : tag_b);
+      const uint64_t piece = (wv[i] & 0xffffu) << (16 * (i & 3));
+      if (i < 4) lo |= piece;
+      else hi |= piece;
+    }
+    ds.ok[t] = ok;
+    ds.m[t] = __uint_as_float((uint32_t)lo);
+    ds.idx[t] = (int32_t)(uint32_t)(lo >> 32);
+    ds.s[t] = __longlong_as_double((long long)hi);
   }
   __syncthreads();
   int n0, f;
@@ -637,7 +656,7 @@ __device__ void dyn_decider(const VerifyParams& P, int J, int g, uint64_t E, Dyn
 }
 
 // Chunk c of row r of request b: its partial into rowp and, tagged with the
-// launch, into trec (one word per lane of the first four).
+// launch, into trec (one word per lane of the first eight).
 template <int ES, bool VEC>
 __device__ __forceinline__ void dyn_chunk(const VerifyParams& P, int b, int r, int c, int x, bool greedy, float T,
                                           int di, uint64_t E) {
@@ -662,15 +681,7 @@ __device__ __forceinline__ void dyn_chunk(const VerifyParams& P, int b, int r, i
   }
   const int64_t at = ((int64_t)b * P.R + r) * P.C1 + c;
   if (threadIdx.x == 0) P.rowp[at] = part;
-  if (threadIdx.x < 4) {
-    const uint64_t sb = (uint64_t)__double_as_longlong(part.s);
-    const uint32_t pay = threadIdx.x == 0   ? __float_as_uint(part.m)
-                         : threadIdx.x == 1 ? (uint32_t)part.idx
-                         : threadIdx.x == 2 ? (uint32_t)sb
-                                            : (uint32_t)(sb >> 32);
-    const uint32_t tag = threadIdx.x < 2 ? record_tag(E) : record_tag_b(E);
-    store_coherent(&P.trec[at].w[threadIdx.x], ((uint64_t)tag << 32) | pay);
-  }
+  if (threadIdx.x < 8) store_coherent(&P.trec[at].w[threadIdx.x], record_word(part, threadIdx.x, E));
 }
 
 // Block J: per request, the chunks of its target row J and (sampled, J <

@@ -36,20 +36,21 @@ struct ReqDesc {  // decision of one request, read by the draw
 };
 
 // A chunk's RowPartial as read by workgroups of the same row-pass launch
-// (dynamic early exit): four 64-bit words, each stored by one single-copy
-// atomic store and each carrying a 32-bit tag of the launch in its high half
-// (payload in the low half: m's bits, idx, the low and the high half of s's
-// bits; every tag odd, so that zeroed memory never carries one, and each
-// word's different for any two launches less than 2^31 apart).  A reader
-// that finds the launch's tags in all four words has the whole record of
-// this launch; anything else (a record still being written, left by an
-// earlier launch, or memory never written) it treats as not yet there.
+// (dynamic early exit): eight 64-bit words, each stored by one single-copy
+// atomic store and each carrying a 48-bit tag of the launch in its high bits
+// and 16 bits of the record in its low bits (words 0-3: m's bits, then idx,
+// low half first; words 4-7: s's bits, lowest 16 first).  Every tag is odd,
+// so that zeroed memory never carries one, and each word's differs for any
+// two launches less than 2^47 apart.  A reader that finds the launch's tags
+// in all eight words has the whole record of this launch; anything else (a
+// record still being written, left by an earlier launch, or memory never
+// written) it treats as not yet there.
 struct TaggedPartial {
-  uint64_t w[4];
+  uint64_t w[8];
 };
 
 static_assert(sizeof(RowPartial) == 16, "RowPartial layout");
-static_assert(sizeof(TaggedPartial) == 32, "TaggedPartial layout");
+static_assert(sizeof(TaggedPartial) == 64, "TaggedPartial layout");
 static_assert(sizeof(ReqDesc) == 64, "ReqDesc layout");
 
 enum { kModeNone = 0, kModeResidual = 1, kModeBonus = 2 };

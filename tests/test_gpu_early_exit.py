@@ -381,7 +381,7 @@ def test_dynamic_exit_on_a_workspace_cut_from_another(sv):
     allocator hands out a freed block again after small output tensors took
     its start), their launch counters holding the same leftover value: the
     tagged records a dynamic exit on other inputs leaves in the first lie in
-    the second's record area, 48 records off, carrying the tag the second's
+    the second's record area, 24 records off, carrying the tag the second's
     launch would expect if the tag were the counter alone.  The dynamic exit
     on the second must equal one pass (the tag also depends on the
     workspace's address)."""
