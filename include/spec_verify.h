@@ -194,9 +194,10 @@ double spec_verify_phase_cost(int32_t B, int32_t K, int32_t V, int32_t dtype);
  * never carry a tag).  Leftover bytes can only make that mode read more
  * rows, never change an output (a request's rows up to its stop are read
  * unless leftover words match this launch's tags by chance: its 56-bit tag
- * in a state word, or its 32-bit tags in all four words of a record, which
- * together repeat only after 2^63 launches; the final decision reports a
- * request invalid if that happened). */
+ * in a state word, or its 48-bit tags in all eight words of a record, which
+ * repeat only after 2^94 launches, and in any one word only after 2^47, so
+ * that a record caught half-written is told apart too; the final decision
+ * reports a request invalid if that happened). */
 size_t spec_verify_workspace_bytes(int32_t B, int32_t K, int32_t V);
 
 /* Enqueue one verification step.  A request whose data is invalid (a draft

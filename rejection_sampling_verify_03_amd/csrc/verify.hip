@@ -524,7 +524,7 @@ struct DynShared {
   float m[kWG];
   int32_t idx[kWG];
   double s[kWG];
-  unsigned char ok[kWG];  // all four words carry this launch's tag
+  unsigned char ok[kWG];  // all eight words carry this launch's tags
   // merged rows of a decider's window: (position - p0) * 2 + row kind
   float rm[2 * 64];
   double rs[2 * 64];

@@ -347,11 +347,11 @@ def test_dynamic_exit_first_launch_on_zeroed_workspace(sv):
 
 
 def test_dynamic_exit_records_from_2_31_launches_ago_do_not_pass(sv):
-    """Records left in the workspace by a launch 2^31 launches back (the low
-    32 bits of their tag then read the same) must not pass for this launch's:
-    a dynamic launch at counter 5 leaves records of other inputs, the counter
-    is moved to 5 + 2^31, and the next dynamic launch on new inputs equals one
-    pass."""
+    """Records left in the workspace by a launch 2^31 launches back (where
+    32-bit tags of the low bits of the counter read the same) must not pass
+    for this launch's, whole or caught half-written: a dynamic launch at
+    counter 5 leaves records of other inputs, the counter is moved to
+    5 + 2^31, and the next dynamic launch on new inputs equals one pass."""
     say("case: dynamic exit, records of a launch 2^31 back")
     dev = torch.device("cuda")
     B, K, V = 192, 8, 151936
