@@ -78,11 +78,12 @@ typedef enum { SPEC_F32 = 0, SPEC_BF16 = 1 } spec_dtype;
  * row strides (request stride 0 shares one set of rows across all requests);
  * draft row K is never read, and draft rows are not read at all for T_b = 0.
  *
- * Preconditions on the data (not checked): logits are not NaN or +inf and
- * |logit| / T_b < 2^100; every row of a sampled request has a finite maximum
- * (violations are detected where they make a row's normaliser non-finite or
- * zero, and reported as a data error when the request reaches that row: the
- * target and draft row of a position it tests, or its bonus row).
+ * Data checked as the request reaches its rows (the target and draft row of
+ * a position it tests, or its bonus row): a row of a sampled request must
+ * have a finite maximum, no NaN or +inf logit, and its largest logit m must
+ * satisfy |ceil(m * s)| <= 2^24 with s = log2(e) / T_b (|m| / T_b up to about
+ * 1.16e7); a row that does not is a data error.  A greedy row may hold NaN
+ * (counted as -inf) and +inf logits.
  */
 typedef struct {
   int32_t B;                   /* requests, >= 0 */
@@ -201,11 +202,14 @@ double spec_verify_phase_cost(int32_t B, int32_t K, int32_t V, int32_t dtype);
 size_t spec_verify_workspace_bytes(int32_t B, int32_t K, int32_t V);
 
 /* Enqueue one verification step.  A request whose data is invalid (a draft
- * token outside [0, V), a temperature that is negative, NaN or infinite, a
- * draft row table entry of a sampled request outside [0, draft_rows), a draft
- * count outside [0, K], or, at a position the request reaches, a row of a
- * sampled request without a finite normaliser) gets accepted_counts = -1,
- * output_tokens all -1 and debug_probs 0.  A batch whose kernel grids would
+ * token outside [0, V), a temperature that is negative, NaN, infinite or
+ * positive below FLT_MIN, a draft row table entry of a sampled request
+ * outside [0, draft_rows), a draft count outside [0, K], or, at a position the
+ * request reaches, a row of a sampled request without a finite normaliser or
+ * whose largest logit m has |ceil(m * log2(e) / T)| above 2^24, the range in
+ * which the kernels hold a row's scaled maximum exactly in fp32: |m| / T up
+ * to about 1.16e7) gets accepted_counts = -1, output_tokens all -1 and
+ * debug_probs 0.  A batch whose kernel grids would
  * exceed one dispatch (2^32 work-items per launch) returns SPEC_EINVAL before
  * anything is enqueued: the draw needs B * 512 < 2^32, the segment sums
  * B * ceil(V / 4096) * 64 < 2^32, and above B = 65535 the row pass needs
@@ -354,9 +358,9 @@ int spec_verify_expand_launch(const spec_verify_args* v, const spec_expand_args*
  * Layout: logits [N, V] (row stride >= V elements), row_index [B, K] (for
  * instance the new_token_indices of spec_expand_launch), temperature [B].
  * A position whose row index is outside [0, N), a request whose temperature is
- * negative, NaN or infinite, and a row without a finite maximum get token -1.
- * Preconditions on the data (not checked): no NaN or +inf logit and
- * |logit| / T < 2^100.
+ * negative, NaN, infinite or positive below FLT_MIN, and (T > 0) a row
+ * without a finite normaliser (no finite logit, or a NaN or +inf one) or
+ * whose largest logit m has |ceil(m * log2(e) / T)| above 2^24 get token -1.
  */
 typedef struct {
   int32_t B;                   /* requests, >= 0 */

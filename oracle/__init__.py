@@ -97,6 +97,8 @@ def lib():
         L.oracle_softmax.restype = ctypes.c_int
         L.oracle_argmax.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int]
         L.oracle_argmax.restype = ctypes.c_int
+        L.oracle_scaled_max_in_range.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_float]
+        L.oracle_scaled_max_in_range.restype = ctypes.c_int
         L.oracle_accept_many.argtypes = [ctypes.c_double, ctypes.c_double, ctypes.c_void_p,
                                           ctypes.c_int64, ctypes.c_void_p]
         L.oracle_invcdf_many.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_double, ctypes.c_void_p,
@@ -195,6 +197,14 @@ def softmax(logits, T):
 def argmax(logits):
     row, dt = _logit_buffer(logits)
     return lib().oracle_argmax(_ptr(row), dt, row.shape[-1])
+
+
+def scaled_max_in_range(logits, T):
+    """True if the row's largest logit is finite and its scaled reference
+    ceil(max * log2(e) / T) is an exact fp32 integer (|ref| <= 2^24): the
+    range in which a sampled row's softmax is computed at all."""
+    row, dt = _logit_buffer(logits)
+    return bool(lib().oracle_scaled_max_in_range(_ptr(row), dt, row.shape[-1], float(T)))
 
 
 # ---------------------------------------------------------------------- verify

@@ -23,6 +23,7 @@
  */
 #include "spec_oracle.h"
 
+#include <float.h>
 #include <math.h>
 #include <stdlib.h>
 
@@ -53,7 +54,7 @@ int oracle_draft_sample(const oracle_draft_args* a) {
       const int32_t row = a->row_index[i];
       a->tokens[i] = -1;
       if (a->trace) a->trace[i] = NAN;
-      if (row < 0 || row >= a->N || !(T >= 0.0) || isinf(T)) {
+      if (row < 0 || row >= a->N || !(T >= 0.0) || isinf(T) || (T > 0.0 && T < FLT_MIN)) {
         ++bad;
         continue;
       }
@@ -63,7 +64,8 @@ int oracle_draft_sample(const oracle_draft_args* a) {
         continue;
       }
       /* mutation 1 plants the mistake of ignoring the temperature */
-      if (oracle_softmax(logits, a->dtype, a->V, a->mutation == 1 ? 1.0 : T, p) != 0) {
+      if (!oracle_scaled_max_in_range(logits, a->dtype, a->V, a->temperature[b]) ||
+          oracle_softmax(logits, a->dtype, a->V, a->mutation == 1 ? 1.0 : T, p) != 0) {
         ++bad;
         continue;
       }

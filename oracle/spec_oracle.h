@@ -65,6 +65,14 @@ int oracle_residual(const double* p, const double* q, int V, double* w, double* 
 /* softmax(logits / T) in double, max-subtracted; dtype 0 = fp32, 1 = bf16 bits.
  * Returns 0, or -1 if the row has no finite maximum or T is not > 0. */
 int oracle_softmax(const void* row, int dtype, int V, double T, double* out);
+/* 1 if the row's largest logit m is finite and its scaled reference
+ * ceil(m * s) -- s = log2(e) / T rounded toward zero to fp32, the product
+ * rounded to nearest in fp32 -- is an exact fp32 integer, |ref| <= 2^24;
+ * else 0.  The kernels hold a row's softmax as S * 2^ref with that fp32
+ * reference, exact only in this range; a sampled row outside it (|m| / T
+ * above about 1.16e7: a temperature tiny against the logits) counts as a row
+ * without a usable normaliser, on both sides. */
+int oracle_scaled_max_in_range(const void* row, int dtype, int V, float T);
 /* Lowest index of the maximum logit (exact float compare), a NaN logit
  * counting as -inf: a row with nothing above -inf gives 0. */
 int oracle_argmax(const void* row, int dtype, int V);
@@ -101,9 +109,10 @@ typedef struct {
 } oracle_verify_args;
 
 /* Returns the number of requests rejected as invalid data (bad token id,
- * temperature < 0 / NaN / inf, K_b outside [0, K], row without a finite
- * maximum); their outputs
- * are accepted = -1 and out_tokens all -1.  Returns -1 on bad arguments. */
+ * temperature < 0 / NaN / inf or below the smallest normal fp32 value but
+ * not 0, K_b outside [0, K], a row reached without a finite maximum or with
+ * its scaled maximum out of range); their outputs are accepted = -1 and
+ * out_tokens all -1.  Returns -1 on bad arguments. */
 int oracle_verify(const oracle_verify_args* a);
 
 /* The sampling weights of request b at row j (j < K: residual or its p
@@ -180,8 +189,9 @@ typedef struct {
 /* Draft token k of request b: x ~ softmax(logits[row_index[b, k]] / T_b) by the
  * inverse CDF with the uniform above (weights p, normaliser their sum); T = 0:
  * lowest-index argmax.  A row index outside [0, N), a temperature < 0 / NaN /
- * inf, or a row without a finite maximum gives token -1.  Returns the number
- * of such positions, or -1 on bad arguments. */
+ * inf or below the smallest normal fp32 value but not 0, or (T > 0) a row
+ * without a finite maximum or with its scaled maximum out of range gives
+ * token -1.  Returns the number of such positions, or -1 on bad arguments. */
 int oracle_draft_sample(const oracle_draft_args* a);
 
 #ifdef __cplusplus

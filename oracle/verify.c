@@ -25,14 +25,18 @@
  * sums to exactly zero falls back to p; the inverse CDF runs in ascending
  * vocabulary order over the weights with their own sum as normaliser; a
  * sampled request whose rows at a position it reaches (target and draft row
- * of a tested position, the target row of the bonus) lack a finite maximum
- * is invalid, and rows after its stop are never looked at.
+ * of a tested position, the target row of the bonus) lack a finite maximum,
+ * or whose scaled maximum lies beyond the fp32 range the kernels hold it in
+ * (oracle_scaled_max_in_range), is invalid, and rows after its stop are
+ * never looked at; a temperature between 0 and the smallest normal fp32
+ * value is invalid too.
  *
  * Everything is computed in double, sequentially, with no blocking or
  * reordering beyond the definitions above.
  */
 #include "spec_oracle.h"
 
+#include <float.h>
 #include <math.h>
 #include <stdlib.h>
 #include <string.h>
@@ -173,6 +177,28 @@ static int row_has_finite_max(const void* row, int dtype, int V) {
   return 0;
 }
 
+int oracle_scaled_max_in_range(const void* row, int dtype, int V, float T) {
+  double m = -INFINITY;
+  for (int v = 0; v < V; ++v) {
+    double x = load_logit(row, dtype, v);
+    if (x > m) m = x;
+  }
+  if (!isfinite(m)) return 0;
+  /* log2(e) / T rounded toward zero to fp32, then max * that in fp32
+   * (round to nearest), rounded up to an integer */
+  const double s = 1.4426950408889634074 / (double)T;
+  float s32 = (float)s;
+  if ((double)s32 > s) s32 = nextafterf(s32, 0.0f);
+  const float ref = ceilf((float)m * s32);
+  return fabsf(ref) <= 0x1p24f;
+}
+
+/* A row whose softmax at temperature T the method can use: a finite maximum,
+ * no NaN or +inf logit, and a scaled maximum in the fp32 range above. */
+static int row_usable_at(const void* row, int dtype, int V, float T) {
+  return row_has_finite_max(row, dtype, V) && oracle_scaled_max_in_range(row, dtype, V, T);
+}
+
 /* Drafts of request b: K, or its entry of the ragged table. */
 static int drafts_of(const oracle_verify_args* a, int b) { return a->num_drafts ? a->num_drafts[b] : a->K; }
 
@@ -186,7 +212,7 @@ static int request_valid(const oracle_verify_args* a, int b) {
   for (int k = 0; k < Kb; ++k)
     if (x[k] < 0 || x[k] >= a->V) return 0;
   float T = a->temperature[b];
-  if (!(T >= 0.0f) || isinf(T)) return 0;
+  if (!(T >= 0.0f) || isinf(T) || (T > 0.0f && T < FLT_MIN)) return 0;
   return 1;
 }
 
@@ -196,8 +222,9 @@ static int request_valid(const oracle_verify_args* a, int b) {
  * draft row k when k < K_b (k = K_b is the bonus row, target only).  Each
  * needs a finite maximum for its softmax to exist. */
 static int rows_usable(const oracle_verify_args* a, int b, int k, int Kb) {
-  if (!row_has_finite_max(trow(a, b, k), a->dtype, a->V)) return 0;
-  return k == Kb || row_has_finite_max(drow(a, b, k), a->dtype, a->V);
+  const float T = a->temperature[b];
+  if (!row_usable_at(trow(a, b, k), a->dtype, a->V, T)) return 0;
+  return k == Kb || row_usable_at(drow(a, b, k), a->dtype, a->V, T);
 }
 
 static void sampling_weights(const oracle_verify_args* a, int b, int j, double* p, double* q,

@@ -10,9 +10,12 @@
 namespace specv {
 
 // A row's statistics are usable when its normaliser is positive and finite
-// (its maximum was finite).
+// (its maximum was finite) and its reference m = ceil(max * s) is an exact
+// fp32 integer: beyond 2^24 the scaled logits near the maximum are no longer
+// held to within one unit of the reference, so the row is refused rather
+// than computed inexactly.
 __device__ __forceinline__ bool row_usable(float m, double s) {
-  return s > 0.0 && s <= DBL_MAX && fabsf(m) <= FLT_MAX;
+  return s > 0.0 && s <= DBL_MAX && fabsf(m) <= kMaxRef;
 }
 
 // The accept test at draft position k of request `req` (explainer page on

@@ -200,8 +200,13 @@ __device__ __forceinline__ void temperature_scale(float T, float& s_hi, float& s
   s_lo = fmaxf(__double2float_rn(s - (double)s_hi), FLT_MIN);
 }
 
-// A usable temperature: 0 (greedy) or positive and finite.
-__device__ __forceinline__ bool temperature_valid(float T) { return T >= 0.0f && T <= FLT_MAX; }
+// A usable temperature: 0 (greedy) or a positive finite normal fp32 value
+// (below FLT_MIN, log2(e) / T leaves the fp32 range of s_hi + s_lo).
+__device__ __forceinline__ bool temperature_valid(float T) { return T == 0.0f || (T >= FLT_MIN && T <= FLT_MAX); }
+
+// Largest |reference| a sampled row may have: ceil(max * s_hi) must be an
+// exact fp32 integer for the scaled exponents near the maximum to be exact.
+constexpr float kMaxRef = 0x1p24f;
 
 // Sum of 2^(x * s - M) over a group of 8, pairwise in fp32.
 __device__ __forceinline__ float sum8_exp(const float x[8], float s_hi, float s_lo, float negM) {

@@ -178,7 +178,7 @@ __global__ __launch_bounds__(64) void draft_draw_kernel(DraftParams P) {
   float Mstar = r0.m;
   for (int j = lane + 64; j < nseg; j += 64) Mstar = fmaxf(Mstar, sp[j].m);
   Mstar = wave_max_f(Mstar);
-  if (!(fabsf(Mstar) <= FLT_MAX)) {  // no finite logit in the row
+  if (!(fabsf(Mstar) <= kMaxRef)) {  // no finite logit in the row, or its scaled maximum out of range
     if (lane == 0) {
       P.tokens[i] = -1;
       if (P.stats) P.stats[i] = none;

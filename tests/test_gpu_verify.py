@@ -473,3 +473,69 @@ def test_greedy_rows_with_nan(sv, dtype):
     for a2, t2 in outs[1:]:
         np.testing.assert_array_equal(a2, a)
         np.testing.assert_array_equal(t2, tok)
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_temperature_tiny_against_the_logits(sv, dtype):
+    """A sampled row counts only while its largest logit m keeps
+    |m| * log2(e) / T within 2^24 (the exact fp32 integers the kernels hold
+    a row's scaled maximum in): temperatures 0.1 % inside that bound for all
+    of a request's rows, or 0.1 % outside it for its first target row (which
+    every walk reads), 1e-5 and 1e-4 against logits near 20, subnormal
+    temperatures (invalid), 3e38, and ordinary ones, at V = 70001.  Every
+    request against the oracle in one pass, a planned cut, the dynamic exit
+    and 2 and 3 shards, and the draft sampler on the first target rows."""
+    import oracle
+    say("case: temperatures tiny against the logits %s" % dtype)
+    B, K, V = 14, 3, 70001
+    g = torch.Generator().manual_seed(61)
+    t = 3 * torch.randn(B, K + 1, V, generator=g) + 15
+    d = t + 0.2 * torch.randn(B, K + 1, V, generator=g)
+    t[6:8] -= 40                                     # negative maxima
+    d[6:8] -= 40
+    t[[1, 3], 0] += 5                                # the first target row holds the largest |maximum|
+    t[7, 0] -= 5
+    tt, dd = t.to(dtype), d.to(dtype)
+    tl, dl = workloads.logits_numpy(tt), workloads.logits_numpy(dd)
+    tv, dv = tt.float().numpy(), dd.float().numpy()  # values (bf16 oracle rows are bit patterns)
+    rows_max = np.array([[abs(float(np.max(tv[b, k]))) for k in range(K + 1)] +
+                         [abs(float(np.max(dv[b, k]))) for k in range(K)] for b in range(B)])
+    mx, m0 = rows_max.max(axis=1), rows_max[:, 0]
+    assert (m0[[1, 3, 7]] == mx[[1, 3, 7]]).all()
+    f = np.log2(np.e) / 2.0 ** 24
+    T = np.array([mx[0] * f / 0.999, m0[1] * f / 1.001, mx[2] * f / 0.999, m0[3] * f / 1.001,
+                  1e-5, 1e-4, mx[6] * f / 0.999, m0[7] * f / 1.001, 1e-40, 3e38, 0.7, 1.0, 0.0, 2e-45],
+                 np.float32)
+    x = np.array([[oracle.argmax(dl[b, k]) for k in range(K)] for b in range(B)], np.int32)
+    x[2, 1] = (x[2, 1] + 7) % V                      # a rejection inside the range
+    Td = torch.from_numpy(T).cuda()
+    tg, dg, xg = tt.cuda(), dd.cuda(), torch.from_numpy(x).cuda()
+    ref = oracle.verify(tl, dl, x, T, seed=6, step=1)
+    assert (ref.accepted[[0, 2, 4, 5, 6, 9, 10, 11, 12]] >= 0).all()
+    assert (ref.accepted[[1, 3, 7, 8, 13]] == -1).all()
+    rep = Report()
+    outs = []
+    for ps in (0, 0b100, sv.SPEC_PHASES_DYNAMIC):
+        a, tok, dbg = sv.verify(tg, dg, xg, Td, seed=6, step=1, debug=ps == 0, phase_starts=ps)
+        torch.cuda.synchronize()
+        a, tok = a.cpu().numpy(), tok.cpu().numpy()
+        compare(tl, dl, x, T, a, tok, None if dbg is None else dbg.cpu().numpy(), seed=6, step=1, report=rep)
+        outs.append((a, tok))
+    for G in (2, 3):
+        a, tok, _ = sv.verify_sharded(tg, dg, xg, Td, G, seed=6, step=1)
+        torch.cuda.synchronize()
+        a, tok = a.cpu().numpy(), tok.cpu().numpy()
+        compare(tl, dl, x, T, a, tok, None, seed=6, step=1, report=rep)
+        outs.append((a, tok))
+    say(rep.summary())
+    assert rep.ok(), rep.failures[:5]
+    for a2, t2 in outs[1:]:
+        np.testing.assert_array_equal(a2, outs[0][0])
+        np.testing.assert_array_equal(t2, outs[0][1])
+    # the draft sampler on the first target rows at the same temperatures
+    lg = tt[:, 0].contiguous()
+    ri = torch.arange(B, dtype=torch.int32).reshape(B, 1)
+    tokd = sv.draft_sample(lg.cuda(), ri.cuda(), Td, seed=9).cpu().numpy()
+    refd = oracle.draft_sample(workloads.logits_numpy(lg), ri.numpy(), T, seed=9)
+    np.testing.assert_array_equal(tokd, refd.tokens)
+    assert (tokd[[1, 3, 7, 8, 13], 0] == -1).all() and (tokd[[0, 2, 4, 5, 6, 9, 10, 11, 12], 0] >= 0).all()

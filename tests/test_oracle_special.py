@@ -243,3 +243,43 @@ def test_softmax_matches_library_and_debug_probs(dtype):
             np.testing.assert_allclose(oracle.softmax(tl[b, k], float(T[b])), p, rtol=1e-13, atol=1e-300)
             assert r.debug_probs[b, k, 0] == np.float32(p[x[b, k]])
             assert r.debug_probs[b, k, 1] == np.float32(q[x[b, k]])
+
+
+def _boundary_temperature(m, factor):
+    """The temperature at which |m| * log2(e) / T = factor * 2^24, as fp32."""
+    return np.float32(abs(m) * np.log2(np.e) / (factor * 2.0 ** 24))
+
+
+def test_scaled_maximum_range_of_sampled_rows():
+    """A sampled row counts only while its largest logit m has
+    |m| * log2(e) / T within 2^24 (the fp32 reference of the kernels).
+    Pinned on either side of the bound with a 0.1 % margin, where rounding
+    cannot decide; a temperature between 0 and the smallest normal fp32 value
+    is invalid; and far inside the bound, at a temperature tiny against the
+    logit gaps, the draw is the argmax (the T -> 0 limit of softmax)."""
+    rng = np.random.default_rng(17)
+    V = 300
+    for m in (10.0, -10.0, 2000.0):
+        row = (m - 1.0 - rng.random(V)).astype(np.float32)
+        row[123] = m
+        t_in, t_out = _boundary_temperature(m, 0.999), _boundary_temperature(m, 1.001)
+        assert oracle.scaled_max_in_range(row, t_in) and not oracle.scaled_max_in_range(row, t_out)
+        assert oracle.scaled_max_in_range(row, 1.0)
+        # through verify (K = 1; the target row is the row above, draft rows
+        # equal, so the draft token 123 is accepted and the bonus row is read)
+        tl = np.stack([row, row])[None].repeat(3, axis=0)
+        x = np.full((3, 1), 123, np.int32)
+        T = np.array([t_in, t_out, 1e-40], np.float32)
+        r = oracle.verify(tl, tl, x, T, seed=1)
+        assert r.accepted[0] == 1 and r.tokens[0].tolist() == [123, 123]
+        assert r.accepted[1] == -1 and r.accepted[2] == -1 and (r.tokens[1:] == -1).all()
+        # the draft sampler on the same row
+        d = oracle.draft_sample(row[None], np.zeros((3, 1), np.int32), T, seed=2)
+        assert d.tokens[:, 0].tolist() == [123, -1, -1]
+    # a row with nothing finite stays out of range at any temperature
+    assert not oracle.scaled_max_in_range(np.full(5, -np.inf, np.float32), 1.0)
+    # bf16 rows: the bound on the bf16 value itself
+    import torch
+    rb = workloads.bf16_bits(torch.tensor([3.0, 96.0, -5.0]).bfloat16())
+    assert oracle.scaled_max_in_range(rb, _boundary_temperature(96.0, 0.999))
+    assert not oracle.scaled_max_in_range(rb, _boundary_temperature(96.0, 1.001))
