@@ -408,3 +408,40 @@ def test_dynamic_exit_on_a_workspace_cut_from_another(sv):
         assert (a2 >= 0).all(), (trial, int((a2 < 0).sum()))
         assert torch.equal(a1, a2) and torch.equal(t1, t2), trial
     say("  3 counters: equal to one pass")
+
+
+def test_concurrent_calls_on_two_streams(sv):
+    """Two halves of one batch verified at the same time on two streams, each
+    call with its own workspace (request_base keeping the halves' uniforms
+    those of the whole batch): one pass, a planned cut and the dynamic exit,
+    and the two halves under different modes at once.  The outputs equal the
+    whole batch verified in one call."""
+    say("case: concurrent verifications on two streams")
+    dev = torch.device("cuda")
+    B, K, V = 128, 8, 151936
+    inp = workloads.mixture_inputs("two streams", B, K, V, torch.bfloat16, 91, dev, temps=(0.0, 0.6, 1.0),
+                                   lam_lo=0.05, lam_hi=0.6)
+    a1, t1, _ = sv.verify(inp.target, inp.draft, inp.draft_tokens, inp.temperature, seed=3, step=4)
+    torch.cuda.synchronize()
+    h = B // 2
+    halves = [slice(0, h), slice(h, B)]
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    wss = [sv.make_workspace(h, K, V, dev) for _ in range(2)]
+    for modes in ((0, 0), (0b1000, 0b1000), (DYN, DYN), (DYN, 0b1000), (0, DYN)):
+        outs = []
+        for i, sl in enumerate(halves):
+            acc = torch.full((h,), -5, dtype=torch.int32, device=dev)
+            tok = torch.full((h, K + 1), -5, dtype=torch.int32, device=dev)
+            outs.append((acc, tok))
+            a = sv.verify_args(inp.target[sl], inp.draft[sl], inp.draft_tokens[sl], inp.temperature[sl], acc, tok,
+                               None, wss[i], seed=3, step=4, phase_starts=modes[i], request_base=sl.start)
+            streams[i].wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(streams[i]):
+                assert sv.spec_verify_launch(a, streams[i].cuda_stream) == sv.SPEC_OK
+        for s in streams:
+            torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        a2 = torch.cat([o[0] for o in outs])
+        t2 = torch.cat([o[1] for o in outs])
+        assert torch.equal(a1, a2) and torch.equal(t1, t2), modes
+        say("  modes %s: equal to the whole batch in one call" % (modes,))
