@@ -183,7 +183,9 @@ __device__ __forceinline__ float load_one(const char* __restrict__ row, int64_t 
 // ------------------------------------------------------ scaled exponentials --
 // Logits enter as t = x * s - M with s = log2(e) / T split into s_hi (fp32,
 // rounded toward zero) + s_lo (>= FLT_MIN, so -inf logits stay -inf and give 0)
-// and M an integer-valued reference, so exp2(t) <= 1 for the row maximum.
+// and M = ceil(max * s_hi) an integer-valued reference, so t <= 0 for the row
+// maximum up to the product's rounding and the s_lo term (t < 2 while
+// |M| <= 2^24, the range a sampled row must stay in).
 // The large terms cancel first: x * s_hi - M is exact before its one rounding,
 // which is relative to the small result t, and the correction x * s_lo is
 // added to that.  (Adding x * s_lo to -M first would round at the ulp of M,
