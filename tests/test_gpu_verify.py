@@ -539,3 +539,58 @@ def test_temperature_tiny_against_the_logits(sv, dtype):
     refd = oracle.draft_sample(workloads.logits_numpy(lg), ri.numpy(), T, seed=9)
     np.testing.assert_array_equal(tokd, refd.tokens)
     assert (tokd[[1, 3, 7, 8, 13], 0] == -1).all() and (tokd[[0, 2, 4, 5, 6, 9, 10, 11, 12], 0] >= 0).all()
+
+
+def test_largest_vocabulary(sv):
+    """V = SPEC_MAX_V (2^31 - 2^16, bf16: rows of 4.3 GB, byte offsets past
+    2^31): rows that are -inf except at 24 indices spread over the whole row
+    (past 2^30 and at its end among them), 16 requests sharing them, mixed
+    temperatures.  A -inf logit carries no weight anywhere in the method, and
+    the inverse CDF and the argmax keep vocabulary order, so the outputs must
+    be the oracle's on the rows cut down to those 24 indices, mapped back.
+    One pass, a planned cut and the dynamic exit, and the draft sampler on
+    the same rows."""
+    import oracle
+    say("case: the largest vocabulary, V = %d" % sv.SPEC_MAX_V)
+    B, K, V = 16, 1, sv.SPEC_MAX_V
+    rng = np.random.default_rng(71)
+    S = np.unique(np.concatenate([rng.integers(0, V, 16), [0, 5, 2**30 - 1, 2**30, 2**30 + 7, V - 4097, V - 2,
+                                                            V - 1]]))
+    n = len(S)
+    vt = (2.0 * rng.standard_normal((K + 1, n))).astype(np.float32)
+    vd = (vt[:K] + 0.7 * rng.standard_normal((K, n))).astype(np.float32)
+    vt[0, rng.random(n) < 0.2] = -np.inf           # some of the indices hold no target weight either
+    dev = torch.device("cuda")
+    idx = torch.from_numpy(S).to(dev)
+    t = torch.full((1, K + 1, V), float("-inf"), dtype=torch.bfloat16, device=dev)
+    d = torch.full((1, K, V), float("-inf"), dtype=torch.bfloat16, device=dev)
+    for k in range(K + 1):
+        t[0, k, idx] = torch.from_numpy(vt[k]).to(dev).bfloat16()
+    for k in range(K):
+        d[0, k, idx] = torch.from_numpy(vd[k]).to(dev).bfloat16()
+    # the cut-down rows as stored, shared by every request (leading dimension 1)
+    tcl = workloads.logits_numpy(t[0][:, idx].unsqueeze(0))
+    dcl = workloads.logits_numpy(d[0][:, idx].unsqueeze(0))
+    xc = rng.integers(0, n, (B, K)).astype(np.int32)
+    T = np.array([0.0, 0.0, 0.7, 1.0] * 4, np.float32)
+    xc[0, 0] = xc[1, 0] = oracle.argmax(tcl[0, 0])  # greedy requests whose draft is the target argmax
+    ref = oracle.verify(tcl, dcl, xc, T, seed=12, step=3, debug=False, trace=False)
+    assert (ref.accepted >= 0).all() and ref.accepted[0] == 1
+    want_tok = np.where(ref.tokens >= 0, S[np.maximum(ref.tokens, 0)], -1)
+    tg, dg = t.expand(B, K + 1, V), d.expand(B, K, V)
+    xg = torch.from_numpy(S[xc].astype(np.int32)).to(dev)
+    Tg = torch.from_numpy(T).to(dev)
+    for ps in (0, 0b10, sv.SPEC_PHASES_DYNAMIC):
+        a, tok, _ = sv.verify(tg, dg, xg, Tg, seed=12, step=3, phase_starts=ps)
+        torch.cuda.synchronize()
+        a, tok = a.cpu().numpy(), tok.cpu().numpy()
+        say("  phase_starts %#x: accepted %s" % (ps, a.tolist()))
+        np.testing.assert_array_equal(a, ref.accepted)
+        np.testing.assert_array_equal(tok, want_tok)
+    # the draft sampler on the two target rows, as a [2, V] drafter buffer
+    ri = torch.from_numpy(rng.integers(0, K + 1, (B, 3)).astype(np.int32)).to(dev)
+    tokd = sv.draft_sample(t[0], ri, Tg, seed=5, step=1).cpu().numpy()
+    refd = oracle.draft_sample(tcl[0], ri.cpu().numpy(), T, seed=5, step=1)
+    np.testing.assert_array_equal(tokd, np.where(refd.tokens >= 0, S[np.maximum(refd.tokens, 0)], -1))
+    del t, d, tg, dg
+    torch.cuda.empty_cache()
