@@ -594,3 +594,21 @@ def test_largest_vocabulary(sv):
     np.testing.assert_array_equal(tokd, np.where(refd.tokens >= 0, S[np.maximum(refd.tokens, 0)], -1))
     del t, d, tg, dg
     torch.cuda.empty_cache()
+
+
+def test_batch_past_the_3d_grid(sv):
+    """B = 70000 requests (past the 65535 the row pass's 3-D grid holds in z,
+    so its workgroups decode their request from the linear index), K = 3,
+    V = 300 fp32, mixed temperatures: every request against the oracle in
+    one pass, a planned cut and the dynamic exit."""
+    say("case: B = 70000 (linear row-pass grid)")
+    inp = workloads.noisy_draft_inputs("B70000", 70000, 3, 300, torch.float32, 73, "cuda", "gauss",
+                                       target_std=1.5, draft_noise=0.6, temps=(0.0, 0.6, 1.0))
+    tl, dl, x, T = host(inp)
+    for ps in (0, 0b100, sv.SPEC_PHASES_DYNAMIC):
+        acc, tok, _ = sv.verify(inp.target, inp.draft, inp.draft_tokens, inp.temperature, seed=9, step=2,
+                                phase_starts=ps)
+        torch.cuda.synchronize()
+        rep = compare(tl, dl, x, T, acc.cpu().numpy(), tok.cpu().numpy(), None, seed=9, step=2)
+        say("  phase_starts %#x:" % ps, rep.summary())
+        assert rep.ok(), rep.failures[:5]
