@@ -612,3 +612,23 @@ def test_batch_past_the_3d_grid(sv):
         rep = compare(tl, dl, x, T, acc.cpu().numpy(), tok.cpu().numpy(), None, seed=9, step=2)
         say("  phase_starts %#x:" % ps, rep.summary())
         assert rep.ok(), rep.failures[:5]
+
+
+@pytest.mark.parametrize("V", [5000, 70001])
+def test_largest_draft_count_every_mode(sv, V):
+    """K = SPEC_MAX_K = 63 (one wave64 ballot) with drafts close to the target
+    so that requests walk far, mixed temperatures: every request against the
+    oracle in one pass, a four-phase cut and the dynamic exit (whose decider
+    window covers 128 positions at V = 5000 and 42 at V = 70001)."""
+    say("case: K = 63, V = %d, every mode" % V)
+    inp = workloads.mixture_inputs("K63 V%d" % V, 24, sv.SPEC_MAX_K, V, torch.bfloat16, 75, "cuda",
+                                   temps=(0.0, 0.6, 1.0), lam_lo=0.01, lam_hi=0.08)
+    tl, dl, x, T = host(inp)
+    for ps in (0, (1 << 8) | (1 << 20) | (1 << 40), sv.SPEC_PHASES_DYNAMIC):
+        acc, tok, _ = sv.verify(inp.target, inp.draft, inp.draft_tokens, inp.temperature, seed=3, step=1,
+                                phase_starts=ps)
+        torch.cuda.synchronize()
+        a = acc.cpu().numpy()
+        rep = compare(tl, dl, x, T, a, tok.cpu().numpy(), None, seed=3, step=1)
+        say("  phase_starts %#x: mean accepted %.1f," % (ps, a.mean()), rep.summary())
+        assert rep.ok(), rep.failures[:5]
