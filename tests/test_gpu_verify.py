@@ -515,11 +515,14 @@ def test_temperature_tiny_against_the_logits(sv, dtype):
     assert (ref.accepted[[1, 3, 7, 8, 13]] == -1).all()
     rep = Report()
     outs = []
+    ws = sv.make_workspace(B, K, V)
     for ps in (0, 0b100, sv.SPEC_PHASES_DYNAMIC):
-        a, tok, dbg = sv.verify(tg, dg, xg, Td, seed=6, step=1, debug=ps == 0, phase_starts=ps)
+        a, tok, dbg = sv.verify(tg, dg, xg, Td, seed=6, step=1, debug=ps == 0, phase_starts=ps, workspace=ws)
         torch.cuda.synchronize()
         a, tok = a.cpu().numpy(), tok.cpu().numpy()
         compare(tl, dl, x, T, a, tok, None if dbg is None else dbg.cpu().numpy(), seed=6, step=1, report=rep)
+        # the out-of-range rows and subnormal temperatures are counted as data errors
+        assert sv.spec_workspace_error(ws) == int((a == -1).sum()) == 5, ps
         outs.append((a, tok))
     for G in (2, 3):
         a, tok, _ = sv.verify_sharded(tg, dg, xg, Td, G, seed=6, step=1)

@@ -272,7 +272,7 @@ def test_scaled_maximum_range_of_sampled_rows():
         T = np.array([t_in, t_out, 1e-40], np.float32)
         r = oracle.verify(tl, tl, x, T, seed=1)
         assert r.accepted[0] == 1 and r.tokens[0].tolist() == [123, 123]
-        assert r.accepted[1] == -1 and r.accepted[2] == -1 and (r.tokens[1:] == -1).all()
+        assert r.accepted[1] == -1 and r.accepted[2] == -1 and (r.tokens[1:] == -1).all() and r.n_bad == 2
         # the draft sampler on the same row
         d = oracle.draft_sample(row[None], np.zeros((3, 1), np.int32), T, seed=2)
         assert d.tokens[:, 0].tolist() == [123, -1, -1]
