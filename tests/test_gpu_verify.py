@@ -603,7 +603,7 @@ def test_batch_past_the_3d_grid(sv):
     """B = 70000 requests (past the 65535 the row pass's 3-D grid holds in z,
     so its workgroups decode their request from the linear index), K = 3,
     V = 300 fp32, mixed temperatures: every request against the oracle in
-    one pass, a planned cut and the dynamic exit."""
+    one pass, a planned cut, the dynamic exit and over 2 vocabulary shards."""
     say("case: B = 70000 (linear row-pass grid)")
     inp = workloads.noisy_draft_inputs("B70000", 70000, 3, 300, torch.float32, 73, "cuda", "gauss",
                                        target_std=1.5, draft_noise=0.6, temps=(0.0, 0.6, 1.0))
@@ -615,6 +615,12 @@ def test_batch_past_the_3d_grid(sv):
         rep = compare(tl, dl, x, T, acc.cpu().numpy(), tok.cpu().numpy(), None, seed=9, step=2)
         say("  phase_starts %#x:" % ps, rep.summary())
         assert rep.ok(), rep.failures[:5]
+    # the vocabulary split over 2 shards (linear grids of their own)
+    acc, tok, _ = sv.verify_sharded(inp.target, inp.draft, inp.draft_tokens, inp.temperature, 2, seed=9, step=2)
+    torch.cuda.synchronize()
+    rep = compare(tl, dl, x, T, acc.cpu().numpy(), tok.cpu().numpy(), None, seed=9, step=2)
+    say("  2 shards:", rep.summary())
+    assert rep.ok(), rep.failures[:5]
 
 
 @pytest.mark.parametrize("V", [5000, 70001])
