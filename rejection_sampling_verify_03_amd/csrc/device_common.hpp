@@ -204,7 +204,7 @@ __device__ __forceinline__ void temperature_scale(float T, float& s_hi, float& s
 
 // A usable temperature: 0 (greedy) or a positive finite normal fp32 value
 // (for subnormal T, log2(e) / T nears the top of the fp32 range and, below
-// about 4.2e-39, leaves it; any such row would be out of range anyway).
+// about 4.2e-39, leaves it).
 __device__ __forceinline__ bool temperature_valid(float T) { return T == 0.0f || (T >= FLT_MIN && T <= FLT_MAX); }
 
 // Largest |reference| a sampled row may have: ceil(max * s_hi) must be an
